@@ -1,0 +1,227 @@
+/*
+ * kivi.h -- C ABI of libkivi.so: KIVI asymmetric low-bit KV cache
+ * (keys per-channel, values per-token, min-max scale/zero, bf16 residual)
+ * and the decode-step attention that reads it, as HIP kernels for gfx950.
+ *
+ * Sources of the method (web pages):
+ *  [card]    "KIVI: A Tuning-Free Asymmetric 2bit Quantization for KV Cache"
+ *            (paper card) -- method paragraph: keys grouped along the channel
+ *            dimension, values per token, each with a group size, no tuning;
+ *            the channel/token split matches how attention reads memory.
+ *  [article] "KV cache quantization squeezes 5GB down to fit longer LLM
+ *            generations" -- asymmetry paragraph: outlier channels in keys,
+ *            asymmetric 2-bit quantization.
+ *  [record]  catalog record "kv-efficiency/kivi-2bit-llama3-8b-gqa-8k" --
+ *            "KV bytes basis" (grouped 2-bit history, group 32, bf16 residual
+ *            of the most recent R=128 tokens), "Methodology" (group size 32
+ *            and residual 128 for both 2- and 4-bit), "notes" (4-bit rate).
+ *
+ * Where the pages leave a step open, this header fixes one reading; every
+ * such reading is marked READING below.
+ *
+ * ------------------------------------------------------------------------
+ * Conventions shared by every entry point
+ * ------------------------------------------------------------------------
+ *  - Pointers named "device" must point to device memory of the current HIP
+ *    device; the caller allocates every buffer and keeps it alive until the
+ *    work enqueued on `stream` has finished.  The library never allocates,
+ *    never synchronises and keeps no global state apart from a thread-local
+ *    copy of the last HIP error.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *  - All arguments are validated on the host before anything is enqueued.
+ *    On any error nothing is enqueued and the counters in kivi_cache are
+ *    left unchanged.  No exception crosses the ABI.  KIVI_E_HIP is returned
+ *    when a launch fails; kivi_last_hip_error() then gives the hipError_t.
+ *  - Supported set (v1): bits in {2,4}; group == 32; head_dim == 128;
+ *    residual a multiple of group with 0 <= residual <= 4096;
+ *    1 <= q_per_kv <= 16; max_tokens a multiple of group;
+ *    batch, kv_heads >= 1.  Anything else: KIVI_E_UNSUPPORTED (or
+ *    KIVI_E_GEOMETRY for non-positive sizes).
+ *  - The whole batch moves in lockstep: one (n_q, n_res, res_start) triple
+ *    describes every sequence of the batch.
+ *  - Numbers: bf16 tensors are passed as uint16_t bit patterns.  Inputs must
+ *    be finite (NaN/Inf are not checked).
+ *
+ * ------------------------------------------------------------------------
+ * Symbols
+ * ------------------------------------------------------------------------
+ *  B = batch, H = kv_heads, QPK = q_per_kv, Hq = H*QPK, D = head_dim,
+ *  b = bits, L = 2^b - 1, G = group, R = residual, T = max_tokens,
+ *  NG = T / G, u = b*H + h  (a "unit" = one sequence and one kv head).
+ *  Query head hq = h*QPK + j reads kv head h (READING: consecutive query
+ *  heads share a kv head; the record gives only the head counts).
+ *
+ * ------------------------------------------------------------------------
+ * Quantiser (READING of "asymmetric min-max, fp scale/zero", [card] method,
+ * [article] asymmetry paragraph; the pages give no formula)
+ * ------------------------------------------------------------------------
+ *  For one group of G values x_i (bf16 widened exactly to fp32), every
+ *  operation in IEEE single precision, round-to-nearest-even, nothing fused:
+ *      mn = min x_i ; mx = max x_i
+ *      s   = (mx - mn) / L                      (correctly rounded divide)
+ *      inv = (s >= FLT_MIN) ? 1 / s : 0         (correctly rounded divide)
+ *      c_i = min(max(rint((x_i - mn) * inv), 0), L)
+ *      scale = s ; zero = mn ;  dequantised value = c_i * s + mn
+ *  A K group is G consecutive tokens of one channel (per-channel keys); a V
+ *  group is G consecutive channels of one token (per-token values).
+ *
+ * ------------------------------------------------------------------------
+ * Byte layout of the cache buffers (part of the contract: packed codes and
+ * scale/zero are compared byte for byte with an independent CPU oracle)
+ * ------------------------------------------------------------------------
+ *  k_codes  uint8 [B][H][T][D*b/8]   token row t holds channel c at byte
+ *           c*b/8, bits [(c*b)%8, (c*b)%8 + b)  (LSB first).
+ *  k_scale, k_zero  fp32 [B][H][NG][D]      (group g, channel c)
+ *  v_codes  uint8 [B][H][NG][G/8][D][b]     group g, octet o (tokens
+ *           8o..8o+7 of the group), channel c: b bytes holding the 8 codes
+ *           of that channel, token 8o+k at bits [k*b, k*b + b) (LSB first).
+ *  v_scale, v_zero  fp32 [B][H][NG][D/G][G] (group g, channel group j,
+ *           token i of the group)
+ *  k_res, v_res  bf16 [B][H][R+G][D]        residual ring of R+G slots.
+ *           Logical residual token i (0 = oldest) lives in slot
+ *           (res_start + i) mod (R+G).  res_start is always a multiple of G.
+ *  Packing runs along the contraction axis of the product that reads the
+ *  codes (channels for q.K^T, tokens for P.V), orthogonal to the group.
+ *
+ * ------------------------------------------------------------------------
+ * Cache state machine (READING of "the most recent R tokens stay in bf16
+ * until flushed into a new group", [record] KV bytes basis)
+ * ------------------------------------------------------------------------
+ *  prefill(S):  n_q = G*floor((S-R)/G) if S > R else 0;  n_res = S - n_q
+ *               (so R <= n_res < R+G once S >= R);  res_start = 0.
+ *  per decode step: append (n_res += 1) -> flush iff n_res == R+G (the G
+ *               oldest residual tokens become quantised group n_q/G) ->
+ *               attend over all n_q + n_res tokens.
+ *  Appending N tokens after prefill(S) leaves exactly the state (quantised
+ *  bytes and logical residual) that prefill(S+N) produces.
+ */
+#ifndef KIVI_H_
+#define KIVI_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KIVI_OK = 0,
+  KIVI_E_NULL = 1,           /* a required pointer is NULL                   */
+  KIVI_E_GEOMETRY = 2,       /* a size is zero/negative or inconsistent      */
+  KIVI_E_UNSUPPORTED = 3,    /* valid geometry outside the supported set     */
+  KIVI_E_SEQLEN = 4,         /* prefill seq_len < 1                          */
+  KIVI_E_CAPACITY = 5,       /* quantised history would exceed max_tokens    */
+  KIVI_E_RESIDUAL_FULL = 6,  /* append with n_res == R+G (flush first)       */
+  KIVI_E_WORKSPACE = 7,      /* decode workspace NULL or too small           */
+  KIVI_E_HIP = 8,            /* a HIP launch failed (see kivi_last_hip_error)*/
+  KIVI_E_STATE = 9           /* cache counters invalid (e.g. empty cache)    */
+} kivi_status;
+
+/* Problem statement: batch, kv heads, query heads per kv head (GQA),
+ * head_dim, bits, group size G, residual length R, and the capacity of the
+ * quantised history in tokens. */
+typedef struct {
+  int32_t batch;
+  int32_t kv_heads;
+  int32_t q_per_kv;
+  int32_t head_dim;
+  int32_t bits;
+  int32_t group;
+  int32_t residual;
+  int32_t max_tokens;
+} kivi_geom;
+
+/* The cache: eight caller-owned device buffers laid out as described above,
+ * plus three host-side counters that the calls below update. */
+typedef struct {
+  uint8_t  *k_codes;
+  float    *k_scale;
+  float    *k_zero;
+  uint8_t  *v_codes;
+  float    *v_scale;
+  float    *v_zero;
+  uint16_t *k_res;
+  uint16_t *v_res;
+  int32_t   n_q;        /* tokens in the quantised history (multiple of G) */
+  int32_t   n_res;      /* tokens in the residual ring                     */
+  int32_t   res_start;  /* ring slot of the oldest residual token          */
+} kivi_cache;
+
+/* Order of the eight sizes written by kivi_cache_layout. */
+enum {
+  KIVI_BUF_K_CODES = 0, KIVI_BUF_K_SCALE, KIVI_BUF_K_ZERO,
+  KIVI_BUF_V_CODES, KIVI_BUF_V_SCALE, KIVI_BUF_V_ZERO,
+  KIVI_BUF_K_RES, KIVI_BUF_V_RES, KIVI_NUM_BUFS
+};
+
+/* Byte sizes of the eight cache buffers for `geom`, in the order of the
+ * KIVI_BUF_* enum.  Host-only, touches no device.
+ * Errors: KIVI_E_NULL, KIVI_E_GEOMETRY, KIVI_E_UNSUPPORTED. */
+kivi_status kivi_cache_layout(const kivi_geom *geom, size_t bytes_out[8]);
+
+/* Bytes of decode workspace that kivi_decode_attention needs for `geom`
+ * (enough for any cache state of that geometry).  Host-only.
+ * Errors: KIVI_E_NULL, KIVI_E_GEOMETRY, KIVI_E_UNSUPPORTED. */
+kivi_status kivi_decode_workspace_size(const kivi_geom *geom, size_t *bytes_out);
+
+/* Prefill: quantise the first n_q tokens of k and v into the grouped
+ * history ([card] method: per-channel K, per-token V; [record] Methodology:
+ * G = 32) and copy the last n_res tokens, unchanged, into ring slots
+ * 0..n_res-1 ([record] KV bytes basis: bf16 residual of the most recent R).
+ * k, v: device bf16 [B][H][seq_len][D], read only.
+ * Resets the cache: sets n_q, n_res, res_start (= 0).
+ * Errors: KIVI_E_NULL, KIVI_E_GEOMETRY, KIVI_E_UNSUPPORTED,
+ *         KIVI_E_SEQLEN (seq_len < 1), KIVI_E_CAPACITY (n_q > max_tokens),
+ *         KIVI_E_HIP. */
+kivi_status kivi_quantize_prefill(const kivi_geom *geom, kivi_cache *cache,
+                                  const uint16_t *k, const uint16_t *v,
+                                  int32_t seq_len, void *stream);
+
+/* Append one decoded token per sequence and kv head to the residual ring:
+ * slot (res_start + n_res) mod (R+G); then n_res += 1.
+ * k_new, v_new: device bf16 [B][H][D].
+ * Errors: KIVI_E_NULL, KIVI_E_GEOMETRY, KIVI_E_UNSUPPORTED,
+ *         KIVI_E_RESIDUAL_FULL (n_res == R+G: flush first), KIVI_E_STATE,
+ *         KIVI_E_HIP. */
+kivi_status kivi_append_token(const kivi_geom *geom, kivi_cache *cache,
+                              const uint16_t *k_new, const uint16_t *v_new,
+                              void *stream);
+
+/* Flush: iff n_res == R+G, quantise the G oldest residual tokens into group
+ * n_q/G with the same quantiser as prefill, then n_q += G, n_res -= G,
+ * res_start = (res_start + G) mod (R+G), and *flushed = 1; otherwise do
+ * nothing and set *flushed = 0.  `flushed` is a host pointer (may be NULL).
+ * Errors: KIVI_E_NULL, KIVI_E_GEOMETRY, KIVI_E_UNSUPPORTED,
+ *         KIVI_E_CAPACITY (n_q + G > max_tokens), KIVI_E_STATE, KIVI_E_HIP. */
+kivi_status kivi_flush_residual(const kivi_geom *geom, kivi_cache *cache,
+                                int32_t *flushed, void *stream);
+
+/* Decode-step attention over the mixed cache ([card] method: the attention
+ * kernel reads per-channel K and per-token V; [record] KV bytes basis:
+ * grouped history plus bf16 residual).  For every query head hq of every
+ * sequence: score_t = softmax_scale * q . k_t over all n_q + n_res cached
+ * tokens (dequantised history and bf16 residual; no mask, no position
+ * handling), p = softmax(score), out = sum_t p_t v_t, accumulated in fp32.
+ * q:   device bf16 [B][Hq][D];  out: device fp32 [B][Hq][D] (written fully).
+ * ws:  device workspace of at least kivi_decode_workspace_size bytes; its
+ *      contents need no initialisation and are scratch after the call.
+ * Errors: KIVI_E_NULL, KIVI_E_GEOMETRY, KIVI_E_UNSUPPORTED, KIVI_E_STATE
+ *         (n_q + n_res == 0 or counters out of range), KIVI_E_WORKSPACE,
+ *         KIVI_E_HIP. */
+kivi_status kivi_decode_attention(const kivi_geom *geom, const kivi_cache *cache,
+                                  const uint16_t *q, float *out,
+                                  float softmax_scale, void *ws, size_t ws_bytes,
+                                  void *stream);
+
+/* Static description of a status code (never NULL). */
+const char *kivi_status_string(kivi_status status);
+
+/* hipError_t of the last failed HIP call made by this thread (0 if none). */
+int32_t kivi_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KIVI_H_ */
