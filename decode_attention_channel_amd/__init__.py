@@ -1,0 +1,8 @@
+"""KIVI asymmetric low-bit KV cache and decode attention for MI355X (gfx950).
+
+The product is libkivi.so (C ABI in include/kivi.h, HIP kernels in csrc/);
+``decode_attention_channel_amd.kivi`` is its thin ctypes binding.
+"""
+from . import kivi  # noqa: F401  (raises if libkivi.so is missing)
+from .kivi import (Cache, Geom, KiviError, Workspace, append_token, cache_layout,  # noqa: F401
+                   decode_attention, flush_residual, quantize_prefill, workspace_size)

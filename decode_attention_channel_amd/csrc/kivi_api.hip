@@ -1,0 +1,254 @@
+// kivi_api.hip -- the C ABI of libkivi.so (declared in include/kivi.h).
+//
+// Everything here runs on the host: argument validation (always before any
+// HIP call, so that an error enqueues nothing and leaves the cache counters
+// unchanged), buffer-size arithmetic, the choice of split-K partition for
+// decode attention, and the kernel launches.  The method steps themselves
+// are in quantize.hip (per-channel K / per-token V group quantiser, catalog
+// record kivi-2bit-llama3-8b-gqa-8k "KV bytes basis" residual handling) and
+// decode_attn.hip (decode attention over the mixed cache).
+#include <math.h>
+#include <stdlib.h>
+
+#include "kivi_internal.h"
+
+namespace {
+
+thread_local int32_t g_last_hip_error = 0;
+
+kivi_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return KIVI_OK;
+  g_last_hip_error = (int32_t)e;
+  return KIVI_E_HIP;
+}
+
+kivi_status check_geom(const kivi_geom *g) {
+  if (!g) return KIVI_E_NULL;
+  if (g->batch <= 0 || g->kv_heads <= 0 || g->q_per_kv <= 0 || g->head_dim <= 0 ||
+      g->bits <= 0 || g->group <= 0 || g->residual < 0 || g->max_tokens < 0)
+    return KIVI_E_GEOMETRY;
+  if (g->bits != 2 && g->bits != 4) return KIVI_E_UNSUPPORTED;
+  if (g->group != kivi::kGroup || g->head_dim != kivi::kHeadDim) return KIVI_E_UNSUPPORTED;
+  if (g->residual % g->group != 0 || g->residual > 4096) return KIVI_E_UNSUPPORTED;
+  if (g->q_per_kv > 16) return KIVI_E_UNSUPPORTED;
+  if (g->max_tokens % g->group != 0) return KIVI_E_UNSUPPORTED;
+  // keep every byte offset of every buffer inside 2^62
+  const double units = (double)g->batch * g->kv_heads;
+  if (units * ((double)g->max_tokens + g->residual + g->group) * g->head_dim * 8.0 > 4.0e18)
+    return KIVI_E_GEOMETRY;
+  return KIVI_OK;
+}
+
+kivi_status check_cache(const kivi_cache *c) {
+  if (!c) return KIVI_E_NULL;
+  if (!c->k_codes || !c->k_scale || !c->k_zero || !c->v_codes || !c->v_scale ||
+      !c->v_zero || !c->k_res || !c->v_res)
+    return KIVI_E_NULL;
+  return KIVI_OK;
+}
+
+kivi_status check_state(const kivi_geom *g, const kivi_cache *c) {
+  const int slots = g->residual + g->group;
+  if (c->n_q < 0 || c->n_q % g->group != 0 || c->n_q > g->max_tokens) return KIVI_E_STATE;
+  if (c->n_res < 0 || c->n_res > slots) return KIVI_E_STATE;
+  if (c->res_start < 0 || c->res_start >= slots || c->res_start % g->group != 0)
+    return KIVI_E_STATE;
+  return KIVI_OK;
+}
+
+long long units_of(const kivi_geom *g) { return (long long)g->batch * g->kv_heads; }
+
+int max_splits(const kivi_geom *g) {
+  const int ng = g->max_tokens / g->group;
+  return (ng + kivi::kMinGroupsPerSplit - 1) / kivi::kMinGroupsPerSplit + 1;
+}
+
+// Groups per quantised split.  Enough workgroups to cover the chip several
+// times over, each split a multiple of the 4 waves of a workgroup.  The
+// environment variable KIVI_GROUPS_PER_SPLIT overrides it (sweeps).
+int choose_gps(long long units, int n_groups) {
+  const char *env = getenv("KIVI_GROUPS_PER_SPLIT");
+  if (env) {
+    int v = atoi(env);
+    if (v >= kivi::kMinGroupsPerSplit) return v;
+  }
+  const long long target_wg = 2048;  // 256 CUs x 8
+  long long gps = (units * (long long)n_groups + target_wg - 1) / target_wg;
+  gps = (gps + 3) / 4 * 4;
+  if (gps < 8) gps = 8;
+  if (gps > 64) gps = 64;
+  return (int)gps;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *kivi_status_string(kivi_status s) {
+  switch (s) {
+    case KIVI_OK: return "ok";
+    case KIVI_E_NULL: return "a required pointer is NULL";
+    case KIVI_E_GEOMETRY: return "invalid geometry";
+    case KIVI_E_UNSUPPORTED: return "geometry outside the supported set";
+    case KIVI_E_SEQLEN: return "sequence length must be >= 1";
+    case KIVI_E_CAPACITY: return "quantised history would exceed max_tokens";
+    case KIVI_E_RESIDUAL_FULL: return "residual ring full: flush first";
+    case KIVI_E_WORKSPACE: return "decode workspace NULL or too small";
+    case KIVI_E_HIP: return "HIP error (see kivi_last_hip_error)";
+    case KIVI_E_STATE: return "cache counters invalid";
+  }
+  return "unknown status";
+}
+
+int32_t kivi_last_hip_error(void) { return g_last_hip_error; }
+
+kivi_status kivi_cache_layout(const kivi_geom *g, size_t bytes[8]) {
+  kivi_status st = check_geom(g);
+  if (st != KIVI_OK) return st;
+  if (!bytes) return KIVI_E_NULL;
+  const size_t U = (size_t)units_of(g), T = (size_t)g->max_tokens, D = (size_t)g->head_dim;
+  const size_t G = (size_t)g->group, NG = T / G, b = (size_t)g->bits;
+  const size_t slots = (size_t)(g->residual + g->group);
+  bytes[KIVI_BUF_K_CODES] = U * T * D * b / 8;
+  bytes[KIVI_BUF_K_SCALE] = U * NG * D * 4;
+  bytes[KIVI_BUF_K_ZERO] = U * NG * D * 4;
+  bytes[KIVI_BUF_V_CODES] = U * NG * (G / 8) * D * b;
+  bytes[KIVI_BUF_V_SCALE] = U * NG * (D / G) * G * 4;
+  bytes[KIVI_BUF_V_ZERO] = U * NG * (D / G) * G * 4;
+  bytes[KIVI_BUF_K_RES] = U * slots * D * 2;
+  bytes[KIVI_BUF_V_RES] = U * slots * D * 2;
+  return KIVI_OK;
+}
+
+kivi_status kivi_decode_workspace_size(const kivi_geom *g, size_t *bytes) {
+  kivi_status st = check_geom(g);
+  if (st != KIVI_OK) return st;
+  if (!bytes) return KIVI_E_NULL;
+  *bytes = (size_t)units_of(g) * (size_t)max_splits(g) * (size_t)g->q_per_kv *
+           (size_t)kivi::kPartStride * sizeof(float);
+  return KIVI_OK;
+}
+
+kivi_status kivi_quantize_prefill(const kivi_geom *g, kivi_cache *c, const uint16_t *k,
+                                  const uint16_t *v, int32_t seq_len, void *stream) {
+  kivi_status st = check_geom(g);
+  if (st != KIVI_OK) return st;
+  if ((st = check_cache(c)) != KIVI_OK) return st;
+  if (!k || !v) return KIVI_E_NULL;
+  if (seq_len < 1) return KIVI_E_SEQLEN;
+  const int G = g->group, R = g->residual, slots = R + G;
+  const int n_q = seq_len > R ? G * ((seq_len - R) / G) : 0;
+  const int r = seq_len - n_q;
+  if (n_q > g->max_tokens || r > slots) return KIVI_E_CAPACITY;
+  hipStream_t s = (hipStream_t)stream;
+  const int U = (int)units_of(g);
+  if (n_q > 0) {
+    kivi::QuantizeArgs a{};
+    a.src_k = k; a.src_v = v;
+    a.src_unit_stride = (long long)seq_len * g->head_dim;
+    a.src_tok0 = 0;
+    a.n_groups = n_q / G; a.n_units = U; a.dst_g0 = 0;
+    a.max_tokens = g->max_tokens; a.n_groups_cap = g->max_tokens / G;
+    a.k_codes = c->k_codes; a.k_scale = c->k_scale; a.k_zero = c->k_zero;
+    a.v_codes = c->v_codes; a.v_scale = c->v_scale; a.v_zero = c->v_zero;
+    if ((st = hip_status(kivi::launch_quantize(g->bits, a, s))) != KIVI_OK) return st;
+  }
+  if (r > 0) {
+    kivi::CopyRowsArgs a{};
+    a.src_k = k; a.src_v = v;
+    a.src_unit_stride = (long long)seq_len * g->head_dim;
+    a.src_tok0 = n_q;
+    a.dst_k = c->k_res; a.dst_v = c->v_res;
+    a.dst_unit_stride = (long long)slots * g->head_dim;
+    a.dst_row0 = 0; a.n_rows = r; a.n_units = U;
+    if ((st = hip_status(kivi::launch_copy_rows(a, s))) != KIVI_OK) return st;
+  }
+  c->n_q = n_q;
+  c->n_res = r;
+  c->res_start = 0;
+  return KIVI_OK;
+}
+
+kivi_status kivi_append_token(const kivi_geom *g, kivi_cache *c, const uint16_t *k_new,
+                              const uint16_t *v_new, void *stream) {
+  kivi_status st = check_geom(g);
+  if (st != KIVI_OK) return st;
+  if ((st = check_cache(c)) != KIVI_OK) return st;
+  if (!k_new || !v_new) return KIVI_E_NULL;
+  if ((st = check_state(g, c)) != KIVI_OK) return st;
+  const int slots = g->residual + g->group;
+  if (c->n_res == slots) return KIVI_E_RESIDUAL_FULL;
+  kivi::CopyRowsArgs a{};
+  a.src_k = k_new; a.src_v = v_new;
+  a.src_unit_stride = g->head_dim;
+  a.src_tok0 = 0;
+  a.dst_k = c->k_res; a.dst_v = c->v_res;
+  a.dst_unit_stride = (long long)slots * g->head_dim;
+  a.dst_row0 = (c->res_start + c->n_res) % slots;
+  a.n_rows = 1; a.n_units = (int)units_of(g);
+  if ((st = hip_status(kivi::launch_copy_rows(a, (hipStream_t)stream))) != KIVI_OK) return st;
+  c->n_res += 1;
+  return KIVI_OK;
+}
+
+kivi_status kivi_flush_residual(const kivi_geom *g, kivi_cache *c, int32_t *flushed,
+                                void *stream) {
+  kivi_status st = check_geom(g);
+  if (st != KIVI_OK) return st;
+  if ((st = check_cache(c)) != KIVI_OK) return st;
+  if ((st = check_state(g, c)) != KIVI_OK) return st;
+  const int G = g->group, slots = g->residual + G;
+  if (flushed) *flushed = 0;
+  if (c->n_res != slots) return KIVI_OK;
+  if (c->n_q + G > g->max_tokens) return KIVI_E_CAPACITY;
+  kivi::QuantizeArgs a{};
+  a.src_k = c->k_res; a.src_v = c->v_res;
+  a.src_unit_stride = (long long)slots * g->head_dim;
+  a.src_tok0 = c->res_start;   // a multiple of G: the G oldest tokens are contiguous
+  a.n_groups = 1; a.n_units = (int)units_of(g); a.dst_g0 = c->n_q / G;
+  a.max_tokens = g->max_tokens; a.n_groups_cap = g->max_tokens / G;
+  a.k_codes = c->k_codes; a.k_scale = c->k_scale; a.k_zero = c->k_zero;
+  a.v_codes = c->v_codes; a.v_scale = c->v_scale; a.v_zero = c->v_zero;
+  if ((st = hip_status(kivi::launch_quantize(g->bits, a, (hipStream_t)stream))) != KIVI_OK)
+    return st;
+  c->n_q += G;
+  c->n_res -= G;
+  c->res_start = (c->res_start + G) % slots;
+  if (flushed) *flushed = 1;
+  return KIVI_OK;
+}
+
+kivi_status kivi_decode_attention(const kivi_geom *g, const kivi_cache *c, const uint16_t *q,
+                                  float *out, float softmax_scale, void *ws, size_t ws_bytes,
+                                  void *stream) {
+  kivi_status st = check_geom(g);
+  if (st != KIVI_OK) return st;
+  if ((st = check_cache(c)) != KIVI_OK) return st;
+  if (!q || !out) return KIVI_E_NULL;
+  if ((st = check_state(g, c)) != KIVI_OK) return st;
+  if (c->n_q + c->n_res == 0) return KIVI_E_STATE;
+  size_t need = 0;
+  kivi_decode_workspace_size(g, &need);
+  if (!ws || ws_bytes < need) return KIVI_E_WORKSPACE;
+  if (!isfinite(softmax_scale)) return KIVI_E_GEOMETRY;
+
+  kivi::DecodeArgs a{};
+  a.k_codes = c->k_codes; a.k_scale = c->k_scale; a.k_zero = c->k_zero;
+  a.v_codes = c->v_codes; a.v_scale = c->v_scale; a.v_zero = c->v_zero;
+  a.k_res = c->k_res; a.v_res = c->v_res;
+  a.q = q; a.out = out; a.part = (float *)ws;
+  a.qscale = softmax_scale * 1.4426950408889634f;
+  a.kv_heads = g->kv_heads; a.qpk = g->q_per_kv; a.max_tokens = g->max_tokens;
+  a.n_groups_cap = g->max_tokens / g->group;
+  a.slots = g->residual + g->group;
+  a.n_units = (int)units_of(g);
+  a.n_groups = c->n_q / g->group;
+  a.n_res = c->n_res; a.res_start = c->res_start;
+  a.gps = choose_gps(units_of(g), a.n_groups);
+  a.n_split_q = (a.n_groups + a.gps - 1) / a.gps;
+  a.n_split = a.n_split_q + (c->n_res > 0 ? 1 : 0);
+  if (a.n_split > max_splits(g)) return KIVI_E_WORKSPACE;   // cannot happen: gps >= 4
+  return hip_status(kivi::launch_decode(g->bits, a, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,65 @@
+// kivi_internal.h -- declarations shared by the translation units of
+// libkivi.so (host API, quantise kernels, decode kernels).  Not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kivi.h"
+
+namespace kivi {
+
+constexpr int kHeadDim = 128;      // supported head_dim
+constexpr int kGroup = 32;         // supported group size G
+constexpr int kPartStride = 132;   // floats per split partial: m, l, pad, pad, o[128]
+constexpr int kMinGroupsPerSplit = 4;
+
+// One launch of the group quantiser: `n_groups` groups of G tokens for each
+// of `n_units` units.  Source token i of local group gl of unit u is row
+// (src_tok0 + gl*G + i) of a [rows][D] bf16 block starting at
+// src + u*src_unit_stride.  Destination group is dst_g0 + gl.
+struct QuantizeArgs {
+  const uint16_t *src_k, *src_v;
+  long long src_unit_stride;   // elements
+  int src_tok0;
+  int n_groups, n_units;
+  int dst_g0;
+  int max_tokens, n_groups_cap;  // T, NG
+  uint8_t *k_codes; float *k_scale, *k_zero;
+  uint8_t *v_codes; float *v_scale, *v_zero;
+};
+hipError_t launch_quantize(int bits, const QuantizeArgs &a, hipStream_t s);
+
+// Copy `n_rows` bf16 rows of D channels per unit (K and V) from
+// src + u*src_unit_stride + (src_tok0 + i)*D to dst + u*dst_unit_stride +
+// (dst_row0 + i)*D.
+struct CopyRowsArgs {
+  const uint16_t *src_k, *src_v;
+  long long src_unit_stride;
+  int src_tok0;
+  uint16_t *dst_k, *dst_v;
+  long long dst_unit_stride;
+  int dst_row0;
+  int n_rows, n_units;
+};
+hipError_t launch_copy_rows(const CopyRowsArgs &a, hipStream_t s);
+
+struct DecodeArgs {
+  const uint8_t *k_codes; const float *k_scale, *k_zero;
+  const uint8_t *v_codes; const float *v_scale, *v_zero;
+  const uint16_t *k_res, *v_res;
+  const uint16_t *q;
+  float *part;        // [units][n_split][QPK][kPartStride]
+  float *out;         // [B][Hq][D]
+  float qscale;       // softmax_scale * log2(e): scores come out in log2 units
+  int kv_heads, qpk, max_tokens, n_groups_cap, slots;
+  int n_units;
+  int n_groups;       // quantised groups in the cache (n_q / G)
+  int n_res, res_start;
+  int gps;            // groups per quantised split
+  int n_split_q;      // quantised splits per unit
+  int n_split;        // n_split_q + (n_res > 0)
+};
+hipError_t launch_decode(int bits, const DecodeArgs &a, hipStream_t s);
+
+}  // namespace kivi

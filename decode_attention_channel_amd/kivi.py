@@ -1,0 +1,234 @@
+"""ctypes binding of libkivi.so (include/kivi.h): argument marshalling only.
+
+Buffers are torch tensors on the current HIP device; the calls enqueue work
+on torch's current stream.  Every step of the method runs in the HIP kernels
+of libkivi.so.  There is no fallback: if the library is missing or fails to
+load, importing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import math
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkivi.so")
+
+STATUS = {
+    0: "KIVI_OK", 1: "KIVI_E_NULL", 2: "KIVI_E_GEOMETRY", 3: "KIVI_E_UNSUPPORTED",
+    4: "KIVI_E_SEQLEN", 5: "KIVI_E_CAPACITY", 6: "KIVI_E_RESIDUAL_FULL",
+    7: "KIVI_E_WORKSPACE", 8: "KIVI_E_HIP", 9: "KIVI_E_STATE",
+}
+EXPORTS = (
+    "kivi_cache_layout", "kivi_decode_workspace_size", "kivi_quantize_prefill",
+    "kivi_append_token", "kivi_flush_residual", "kivi_decode_attention",
+    "kivi_status_string", "kivi_last_hip_error",
+)
+BUFFERS = ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero", "k_res", "v_res")
+
+
+class KiviError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        name = STATUS.get(status, str(status))
+        msg = f"{where}: {name} ({_lib.kivi_status_string(status).decode()})"
+        if status == 8:
+            msg += f", hipError {_lib.kivi_last_hip_error()}"
+        super().__init__(msg)
+
+
+class _Geom(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "batch", "kv_heads", "q_per_kv", "head_dim", "bits", "group", "residual",
+        "max_tokens")]
+
+
+class _Cache(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in BUFFERS] + [
+        ("n_q", ctypes.c_int32), ("n_res", ctypes.c_int32), ("res_start", ctypes.c_int32)]
+
+
+def _load():
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is not built: run `python -m "
+                          "decode_attention_channel_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    G, C, P = ctypes.POINTER(_Geom), ctypes.POINTER(_Cache), ctypes.c_void_p
+    sz = ctypes.POINTER(ctypes.c_size_t)
+    lib.kivi_cache_layout.argtypes = [G, sz]
+    lib.kivi_decode_workspace_size.argtypes = [G, sz]
+    lib.kivi_quantize_prefill.argtypes = [G, C, P, P, ctypes.c_int32, P]
+    lib.kivi_append_token.argtypes = [G, C, P, P, P]
+    lib.kivi_flush_residual.argtypes = [G, C, ctypes.POINTER(ctypes.c_int32), P]
+    lib.kivi_decode_attention.argtypes = [G, C, P, P, ctypes.c_float, P, ctypes.c_size_t, P]
+    for f in ("kivi_cache_layout", "kivi_decode_workspace_size", "kivi_quantize_prefill",
+              "kivi_append_token", "kivi_flush_residual", "kivi_decode_attention"):
+        getattr(lib, f).restype = ctypes.c_int
+    lib.kivi_status_string.argtypes = [ctypes.c_int]
+    lib.kivi_status_string.restype = ctypes.c_char_p
+    lib.kivi_last_hip_error.restype = ctypes.c_int32
+    return lib
+
+
+_lib = _load()
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def raw_library():
+    return _lib
+
+
+@dataclasses.dataclass(frozen=True)
+class Geom:
+    batch: int
+    kv_heads: int
+    q_per_kv: int
+    head_dim: int = 128
+    bits: int = 2
+    group: int = 32
+    residual: int = 128
+    max_tokens: int = 0
+
+    def c(self) -> _Geom:
+        return _Geom(*dataclasses.astuple(self))
+
+    @property
+    def q_heads(self) -> int:
+        return self.kv_heads * self.q_per_kv
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise KiviError(status, where)
+
+
+def cache_layout(g: Geom) -> list[int]:
+    out = (ctypes.c_size_t * 8)()
+    _check(_lib.kivi_cache_layout(ctypes.byref(g.c()), out), "kivi_cache_layout")
+    return list(out)
+
+
+def workspace_size(g: Geom) -> int:
+    out = ctypes.c_size_t(0)
+    _check(_lib.kivi_decode_workspace_size(ctypes.byref(g.c()), ctypes.byref(out)),
+           "kivi_decode_workspace_size")
+    return out.value
+
+
+def _stream() -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t: torch.Tensor, dtype, shape=None, name="tensor") -> ctypes.c_void_p:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+class Cache:
+    """The eight cache buffers (torch tensors, shaped by the documented layout)
+    and the host-side counters."""
+
+    def __init__(self, g: Geom, device=None):
+        device = torch.device("cuda", torch.cuda.current_device()) if device is None else device
+        sizes = cache_layout(g)
+        B, H, T, D, b, G = g.batch, g.kv_heads, g.max_tokens, g.head_dim, g.bits, g.group
+        NG, S = T // G, g.residual + g.group
+        shapes = {
+            "k_codes": ((B, H, T, D * b // 8), torch.uint8),
+            "k_scale": ((B, H, NG, D), torch.float32),
+            "k_zero": ((B, H, NG, D), torch.float32),
+            "v_codes": ((B, H, NG, G // 8, D, b), torch.uint8),
+            "v_scale": ((B, H, NG, D // G, G), torch.float32),
+            "v_zero": ((B, H, NG, D // G, G), torch.float32),
+            "k_res": ((B, H, S, D), torch.bfloat16),
+            "v_res": ((B, H, S, D), torch.bfloat16),
+        }
+        self.geom = g
+        for (name, (shape, dt)), nbytes in zip(shapes.items(), sizes):
+            t = torch.empty(shape, dtype=dt, device=device)
+            assert t.numel() * t.element_size() == nbytes, name
+            setattr(self, name, t)
+        self._c = _Cache(*[ctypes.c_void_p(getattr(self, n).data_ptr()) for n in BUFFERS],
+                         0, 0, 0)
+
+    @property
+    def n_q(self) -> int:
+        return self._c.n_q
+
+    @property
+    def n_res(self) -> int:
+        return self._c.n_res
+
+    @property
+    def res_start(self) -> int:
+        return self._c.res_start
+
+    def set_counters(self, n_q: int, n_res: int, res_start: int):
+        self._c.n_q, self._c.n_res, self._c.res_start = n_q, n_res, res_start
+
+    def nbytes(self) -> int:
+        return sum(getattr(self, n).numel() * getattr(self, n).element_size() for n in BUFFERS)
+
+
+def quantize_prefill(g: Geom, c: Cache, k: torch.Tensor, v: torch.Tensor) -> None:
+    """k, v: bf16 [B][H][S][D] on the device."""
+    S = k.shape[2] if k.dim() == 4 else -1
+    shape = (g.batch, g.kv_heads, S, g.head_dim)
+    _check(_lib.kivi_quantize_prefill(ctypes.byref(g.c()), ctypes.byref(c._c),
+                                      _ptr(k, torch.bfloat16, shape, "k"),
+                                      _ptr(v, torch.bfloat16, shape, "v"), S, _stream()),
+           "kivi_quantize_prefill")
+
+
+def append_token(g: Geom, c: Cache, k_new: torch.Tensor, v_new: torch.Tensor) -> None:
+    shape = (g.batch, g.kv_heads, g.head_dim)
+    _check(_lib.kivi_append_token(ctypes.byref(g.c()), ctypes.byref(c._c),
+                                  _ptr(k_new, torch.bfloat16, shape, "k_new"),
+                                  _ptr(v_new, torch.bfloat16, shape, "v_new"), _stream()),
+           "kivi_append_token")
+
+
+def flush_residual(g: Geom, c: Cache) -> int:
+    flushed = ctypes.c_int32(0)
+    _check(_lib.kivi_flush_residual(ctypes.byref(g.c()), ctypes.byref(c._c),
+                                    ctypes.byref(flushed), _stream()), "kivi_flush_residual")
+    return flushed.value
+
+
+class Workspace:
+    """Device scratch for decode attention, sized for a geometry."""
+
+    def __init__(self, g: Geom, device=None):
+        device = torch.device("cuda", torch.cuda.current_device()) if device is None else device
+        self.nbytes = workspace_size(g)
+        self.buf = torch.empty(max(self.nbytes, 16), dtype=torch.uint8, device=device)
+
+
+def decode_attention(g: Geom, c: Cache, q: torch.Tensor, out: torch.Tensor | None = None,
+                     softmax_scale: float | None = None, ws: Workspace | None = None
+                     ) -> torch.Tensor:
+    """q: bf16 [B][H*QPK][D] -> fp32 [B][H*QPK][D]."""
+    shape = (g.batch, g.q_heads, g.head_dim)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = Workspace(g, q.device)
+    scale = 1.0 / math.sqrt(g.head_dim) if softmax_scale is None else float(softmax_scale)
+    _check(_lib.kivi_decode_attention(ctypes.byref(g.c()), ctypes.byref(c._c),
+                                      _ptr(q, torch.bfloat16, shape, "q"),
+                                      _ptr(out, torch.float32, shape, "out"), scale,
+                                      ctypes.c_void_p(ws.buf.data_ptr()), ws.nbytes, _stream()),
+           "kivi_decode_attention")
+    return out

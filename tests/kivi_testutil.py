@@ -1,0 +1,68 @@
+"""Helpers shared by the GPU tests: host copies of device caches, byte-exact
+comparison of the used part of a cache, and the attention error metric.
+
+The metric (a reading; the pages fix no error metric, the target names a
+maximum relative error of 1e-3 with fp32 accumulation): for every output row
+(one query head of one sequence), ||o - o_ref||_inf / ||o_ref||_inf, maximised
+over rows.  An element-wise relative error is meaningless for outputs that are
+averages of zero-mean values (some elements sit near zero)."""
+import numpy as np
+import torch
+
+import oracle
+
+ATTN_TOL = 1e-3
+
+
+def to_np(t: torch.Tensor) -> np.ndarray:
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def bits_to_dev(x: np.ndarray, device="cuda") -> torch.Tensor:
+    """uint16 bf16 bit patterns -> device bf16 tensor."""
+    return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(device)
+
+
+def host_cache(gc, og: oracle.Geom) -> oracle.Cache:
+    """Copy a device cache into an oracle.Cache (same documented layout)."""
+    hc = oracle.Cache(og)
+    for name in ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero", "k_res", "v_res"):
+        arr = getattr(hc, name)
+        arr[...] = to_np(getattr(gc, name)).reshape(arr.shape)
+    hc.n_q, hc.n_res, hc.res_start = gc.n_q, gc.n_res, gc.res_start
+    return hc
+
+
+def assert_same_cache(got: oracle.Cache, ref: oracle.Cache, units=None, ref_units=None):
+    """Byte-exact equality of the used part: quantised history (codes, scale,
+    zero) and the logical residual (ring slots in logical order)."""
+    assert (got.n_q, got.n_res) == (ref.n_q, ref.n_res)
+    g = got.geom
+    nq, ng, G = ref.n_q, ref.n_q // g.group, g.group
+    B, H = g.batch, g.kv_heads
+    units = [(b, h) for b in range(B) for h in range(H)] if units is None else units
+    ref_units = units if ref_units is None else ref_units
+    slots = g.residual + g.group
+    for (b, h), (rb, rh) in zip(units, ref_units):
+        msg = f"unit (b={b}, h={h})"
+        np.testing.assert_array_equal(got.k_codes[b, h, :nq], ref.k_codes[rb, rh, :nq], msg)
+        np.testing.assert_array_equal(got.v_codes[b, h, :ng], ref.v_codes[rb, rh, :ng], msg)
+        for name in ("k_scale", "k_zero", "v_scale", "v_zero"):
+            a = getattr(got, name)[b, h, :ng].view(np.uint32)
+            r = getattr(ref, name)[rb, rh, :ng].view(np.uint32)
+            np.testing.assert_array_equal(a, r, f"{msg} {name}")
+        go = [(got.res_start + i) % slots for i in range(got.n_res)]
+        ro = [(ref.res_start + i) % slots for i in range(ref.n_res)]
+        np.testing.assert_array_equal(got.k_res[b, h, go], ref.k_res[rb, rh, ro], msg)
+        np.testing.assert_array_equal(got.v_res[b, h, go], ref.v_res[rb, rh, ro], msg)
+
+
+def row_rel_err(out: np.ndarray, ref: np.ndarray) -> float:
+    out = out.reshape(-1, out.shape[-1]).astype(np.float64)
+    ref = ref.reshape(-1, ref.shape[-1]).astype(np.float64)
+    num = np.abs(out - ref).max(axis=1)
+    den = np.abs(ref).max(axis=1)
+    return float((num / den).max())

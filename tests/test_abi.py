@@ -1,0 +1,120 @@
+"""CPU checks of the C ABI: the library loads, exports every function that
+include/kivi.h declares, sizes its buffers as the header documents, and
+rejects invalid arguments on the host before touching any device (so these
+calls are safe without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+kivi = pytest.importorskip("decode_attention_channel_amd.kivi")
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "kivi.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kivi_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_function():
+    names = _declared()
+    assert len(names) == 8
+    lib = ctypes.CDLL(kivi.library_path())
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(kivi.EXPORTS)
+
+
+def _g(**kw):
+    base = dict(batch=2, kv_heads=3, q_per_kv=4, head_dim=128, bits=2, group=32, residual=128,
+                max_tokens=1024)
+    base.update(kw)
+    return kivi.Geom(**base)
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_layout_sizes(bits):
+    g = _g(bits=bits)
+    U, T, D, NG, S = 6, 1024, 128, 32, 160
+    assert kivi.cache_layout(g) == [U * T * D * bits // 8, U * NG * D * 4, U * NG * D * 4,
+                                    U * NG * 4 * D * bits, U * NG * 4 * 32 * 4,
+                                    U * NG * 4 * 32 * 4, U * S * D * 2, U * S * D * 2]
+    assert kivi.workspace_size(g) == U * (NG // 4 + 1) * 4 * 132 * 4
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=0), 2), (dict(kv_heads=-1), 2), (dict(bits=3), 3), (dict(bits=8), 3),
+    (dict(head_dim=64), 3), (dict(group=64), 3), (dict(residual=100), 3),
+    (dict(q_per_kv=17), 3), (dict(max_tokens=1000), 3), (dict(residual=-32), 2),
+])
+def test_geometry_rejected(kw, status):
+    with pytest.raises(kivi.KiviError) as e:
+        kivi.cache_layout(_g(**kw))
+    assert e.value.status == status
+
+
+def _cache_struct(n_q=0, n_res=0, res_start=0, null=None):
+    ptrs = [ctypes.c_void_p(0x1000 * (i + 1)) for i in range(8)]
+    if null is not None:
+        ptrs[null] = ctypes.c_void_p(0)
+    return kivi._Cache(*ptrs, n_q, n_res, res_start)
+
+
+def _call(fn, *args):
+    return getattr(kivi.raw_library(), fn)(*args)
+
+
+def test_host_validation_before_any_device_work():
+    g = _g().c()
+    fake = ctypes.c_void_p(0x2000)
+    P = ctypes.byref
+    # NULL geometry / cache / buffers / inputs
+    assert _call("kivi_quantize_prefill", None, P(_cache_struct()), fake, fake, 10, None) == 1
+    assert _call("kivi_quantize_prefill", P(g), None, fake, fake, 10, None) == 1
+    for i in range(8):
+        assert _call("kivi_quantize_prefill", P(g), P(_cache_struct(null=i)), fake, fake, 10,
+                     None) == 1
+    assert _call("kivi_quantize_prefill", P(g), P(_cache_struct()), None, fake, 10, None) == 1
+    # sequence length and capacity
+    assert _call("kivi_quantize_prefill", P(g), P(_cache_struct()), fake, fake, 0, None) == 4
+    c = _cache_struct()
+    assert _call("kivi_quantize_prefill", P(g), P(c), fake, fake, 1024 + 160, None) == 5
+    assert (c.n_q, c.n_res, c.res_start) == (0, 0, 0)
+    # append on a full ring, with counters left unchanged
+    c = _cache_struct(n_q=64, n_res=160, res_start=32)
+    assert _call("kivi_append_token", P(g), P(c), fake, fake, None) == 6
+    assert (c.n_q, c.n_res, c.res_start) == (64, 160, 32)
+    # flush: nothing to do (no device work) and history full
+    flushed = ctypes.c_int32(7)
+    c = _cache_struct(n_q=64, n_res=150)
+    assert _call("kivi_flush_residual", P(g), P(c), P(flushed), None) == 0
+    assert flushed.value == 0 and (c.n_q, c.n_res) == (64, 150)
+    c = _cache_struct(n_q=1024, n_res=160)
+    assert _call("kivi_flush_residual", P(g), P(c), P(flushed), None) == 5
+    # inconsistent counters
+    for bad in [dict(n_q=33), dict(n_q=-32), dict(n_res=161), dict(res_start=16),
+                dict(res_start=160), dict(n_q=1056)]:
+        c = _cache_struct(**bad)
+        assert _call("kivi_append_token", P(g), P(c), fake, fake, None) == 9, bad
+    # decode: empty cache, workspace, scale
+    ws_need = kivi.workspace_size(_g())
+    args = (fake, fake, ctypes.c_float(0.1))
+    assert _call("kivi_decode_attention", P(g), P(_cache_struct()), *args, fake, ws_need,
+                 None) == 9
+    c = _cache_struct(n_q=64, n_res=130)
+    assert _call("kivi_decode_attention", P(g), P(c), *args, fake, ws_need - 1, None) == 7
+    assert _call("kivi_decode_attention", P(g), P(c), *args, None, ws_need, None) == 7
+    assert _call("kivi_decode_attention", P(g), P(c), fake, fake, ctypes.c_float(float("nan")),
+                 fake, ws_need, None) == 2
+    assert _call("kivi_decode_attention", P(g), P(c), None, fake, ctypes.c_float(0.1), fake,
+                 ws_need, None) == 1
+
+
+def test_status_strings():
+    lib = kivi.raw_library()
+    for s in range(10):
+        assert lib.kivi_status_string(s)
+    assert lib.kivi_status_string(99) == b"unknown status"
+    assert lib.kivi_last_hip_error() == 0
