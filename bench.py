@@ -1,0 +1,274 @@
+"""Benchmark: KIVI decode step on one MI355X.
+
+Workload (Llama-3-8B GQA geometry of the catalog record kivi-2bit-llama3-8b-gqa-8k:
+32 layers, 8 kv heads, 32 query heads, head_dim 128, 8K context), batch 16,
+2-bit, G = 32, R = 128, seeded synthetic K/V/q with outlier key channels.
+
+* prefill leg: every layer's 8192-token K/V is quantised into its own cache
+  (per-layer launch timed with HIP events; reported as quantise Gelem/s and
+  HBM GB/s);
+* decode leg (the timed "step"): for each of the 32 layers, append one token
+  per sequence, flush a group when the residual is full, and run decode
+  attention over the whole mixed cache.  value = generated tokens/s
+  (batch / step time).  The 32 layer caches (4.5 GB) rotate, so the 256 MB
+  MALL cannot serve them;
+* roofline of the dominant kernel (decode attention, one launch per layer):
+  algorithmic bytes per launch / its HIP-event duration, against 8 TB/s;
+* cpu_baseline: the CPU oracle (plain C) on a bounded sample of the same
+  workload (two layers' worth of (sequence, kv head) units), threads over units.
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "KIVI decode-attention achieved HBM GB/s + tokens/sec; quantize Gelem/s"
+
+
+def attn_bytes(w, n_q, n_res):
+    """Algorithmic bytes of one decode-attention launch: the packed history
+    (codes + fp32 scale/zero), the bf16 residual, q (bf16) and out (fp32)."""
+    D, G, b = w.head_dim, w.group, w.bits
+    per_unit = n_q * (2 * D * b / 8 + 16 * D / G) + n_res * 4 * D
+    return w.batch * w.kv_heads * per_unit + w.batch * w.q_heads * D * (2 + 4)
+
+
+def prefill_bytes(w, S, n_q):
+    D, G, b = w.head_dim, w.group, w.bits
+    r = S - n_q
+    return w.batch * w.kv_heads * (4 * S * D + n_q * (2 * D * b / 8 + 16 * D / G) + 4 * r * D)
+
+
+def read_traffic(kernel_tag: str):
+    """HBM traffic per launch measured with rocprofv3 counters (committed
+    summary), valid only while the kernel source is unchanged."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{kernel_tag}_traffic.txt")
+    src = os.path.join(ROOT, "decode_attention_channel_amd", "csrc", "decode_attn.hip")
+    if not os.path.exists(path):
+        return None
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    vals = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            key, val = line.split(":", 1)
+            vals[key.strip()] = val.strip()
+    if vals.get("kernel_source_sha256_16") != sha:
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, seed, units_wanted=256):
+    import numpy as np
+
+    import oracle
+    import synth
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    og = oracle.Geom(1, 1, w.q_per_kv, bits=w.bits, max_tokens=w.seq_len)
+    per_layer = w.batch * w.kv_heads
+    jobs = []
+    for layer in range(math.ceil(units_wanted / per_layer)):
+        for bi in range(w.batch):
+            if len(jobs) >= units_wanted:
+                break
+            jobs.append((layer, bi))
+    # inputs: one sequence (all kv heads) at a time, same recipe as the GPU run
+    inputs = {}
+    for layer, bi in jobs:
+        k, v = synth.prefill_kv(w, seed + 7919 + 131 * bi, layer, batch=1)
+        q = synth.query(w, seed + 7919 + 131 * bi, layer, batch=1)
+        inputs[(layer, bi)] = (synth.bits_u16(k), synth.bits_u16(v), synth.bits_u16(q))
+    units = [(key, h) for key in inputs for h in range(w.kv_heads)][:units_wanted]
+    scale = 1.0 / math.sqrt(w.head_dim)
+
+    def prefill_one(item):
+        key, h = item
+        kb, vb, _ = inputs[key]
+        return oracle.prefill(og, kb[:, h:h + 1].copy(), vb[:, h:h + 1].copy())
+
+    with concurrent.futures.ThreadPoolExecutor(threads) as ex:
+        t0 = time.perf_counter()
+        caches = list(ex.map(prefill_one, units))
+        t_prefill = time.perf_counter() - t0
+
+        def attend_one(i):
+            (key, h), c = units[i], caches[i]
+            q = inputs[key][2][:, h * w.q_per_kv:(h + 1) * w.q_per_kv].copy()
+            return oracle.attention(c, q, scale)
+
+        t0 = time.perf_counter()
+        outs = list(ex.map(attend_one, range(len(units))))
+        t_attn = time.perf_counter() - t0
+    assert all(np.isfinite(o).all() for o in outs)
+    n = len(units)
+    n_q = caches[0].n_q
+    units_per_step = w.layers * w.batch * w.kv_heads
+    step_s = t_attn / n * units_per_step
+    return {
+        "value": w.batch / step_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+        "sample": (f"{n} (sequence, kv head) units at {w.seq_len} tokens ({n / per_layer:.0f} "
+                   f"layers' worth): oracle prefill + one decode-attention step per unit; "
+                   f"decode time scaled to {units_per_step} units per 32-layer step"),
+        "quantize_gelem_s": 2 * n * n_q * w.head_dim / t_prefill / 1e9,
+        "attn_wall_s": t_attn, "prefill_wall_s": t_prefill,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama3-8b-gqa-8k")
+    ap.add_argument("--layers", type=int, default=None)
+    ap.add_argument("--seed", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-steps", type=int, default=0,
+                    help="run only N decode steps after warmup, no reporting (profilers)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported on this build "
+              "(multi-GPU sharding is a design note only)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    from decode_attention_channel_amd import kivi
+
+    w = synth.WORKLOADS[args.workload]
+    layers = args.layers or w.layers
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    D, G, R = w.head_dim, w.group, w.residual
+    total_steps = args.warmup + (args.profile_steps or args.steps)
+    max_tokens = G * math.ceil((w.seq_len - R + total_steps + G) / G)
+    geom = kivi.Geom(w.batch, w.kv_heads, w.q_per_kv, bits=w.bits, max_tokens=max_tokens)
+
+    caches = [kivi.Cache(geom, dev) for _ in range(layers)]
+    ws = kivi.Workspace(geom, dev)
+    mall_flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+
+    # ---- prefill leg
+    pre_ms = []
+    n_q0 = None
+    for layer in range(layers):
+        k, v = synth.prefill_kv(w, args.seed, layer, device=dev)
+        mall_flush.zero_()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        kivi.quantize_prefill(geom, caches[layer], k, v)
+        e1.record()
+        torch.cuda.synchronize()
+        pre_ms.append(e0.elapsed_time(e1))
+        n_q0 = caches[layer].n_q
+        del k, v
+    del mall_flush
+    torch.cuda.empty_cache()
+    pre_t = sum(pre_ms) / 1e3
+    quant_gelem_s = 2 * w.batch * w.kv_heads * n_q0 * D * layers / pre_t / 1e9
+    pre_gbps = prefill_bytes(w, w.seq_len, n_q0) * layers / pre_t / 1e9
+
+    # ---- decode inputs (resident before timing)
+    qs = [synth.query(w, args.seed, layer, device=dev) for layer in range(layers)]
+    outs = [torch.empty(w.batch, w.q_heads, D, dtype=torch.float32, device=dev)
+            for _ in range(layers)]
+    new_tok = [[synth.new_token(w, args.seed, layer, step, device=dev) for layer in range(layers)]
+               for step in range(total_steps)]
+    steppers = [kivi.LayerStepper(geom, caches[layer], ws, qs[layer], outs[layer])
+                for layer in range(layers)]
+
+    def step(i, events=None, bytes_acc=None):
+        for layer in range(layers):
+            st = steppers[layer]
+            kn, vn = new_tok[i][layer]
+            st.append(kn, vn)
+            st.flush()
+            if events is not None:
+                bytes_acc.append(attn_bytes(w, st.cache.n_q, st.cache.n_res))
+                events[layer][0].record()
+            st.attend()
+            if events is not None:
+                events[layer][1].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    if args.profile_steps:
+        for i in range(args.warmup, total_steps):
+            step(i)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_steps": args.profile_steps}))
+        return
+
+    # step timing: no per-kernel events
+    n_timed = args.steps
+    half = n_timed // 2
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.warmup, args.warmup + half):
+        step(i)
+    torch.cuda.synchronize()
+    t_steps = time.perf_counter() - t0
+    # kernel timing: HIP events around every decode-attention launch, on the
+    # stream the library launches on; the GPU is held first so that the host
+    # enqueues far ahead and no launch waits for the host.
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(layers)] for _ in range(n_timed - half)]
+    bytes_acc = []
+    torch.cuda._sleep(200_000_000)
+    t1 = time.perf_counter()
+    for k_i, i in enumerate(range(args.warmup + half, args.warmup + n_timed)):
+        step(i, ev[k_i], bytes_acc)
+    torch.cuda.synchronize()
+    t_steps2 = time.perf_counter() - t1
+    kern_ms = [a.elapsed_time(b) for row in ev for (a, b) in row]
+    avg_kern_s = sum(kern_ms) / len(kern_ms) / 1e3
+    avg_bytes = sum(bytes_acc) / len(bytes_acc)
+    achieved = avg_bytes / avg_kern_s / 1e9
+
+    ms_per_step = t_steps / half * 1e3
+    tokens_s = w.batch / (t_steps / half)
+    res = {
+        "metric": METRIC, "value": tokens_s, "unit": "tokens/s", "n_gpus": 1,
+        "steps": n_timed, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "kv_heads": w.kv_heads,
+                   "q_heads": w.q_heads, "head_dim": D, "context": w.seq_len, "bits": w.bits,
+                   "group": G, "residual": R, "layers": layers,
+                   "step": "per layer: append + flush-if-full + decode attention"},
+        "attn_hbm_gbps": achieved,
+        "attn_kernel_us": avg_kern_s * 1e6,
+        "attn_tokens_s_kernel_only": w.batch / (avg_kern_s * layers),
+        "quantize_gelem_s": quant_gelem_s,
+        "quantize_hbm_gbps": pre_gbps,
+        "quantize_prefill_ms_per_layer": pre_t / layers * 1e3,
+        "ms_per_step_with_events": t_steps2 / (n_timed - half) * 1e3,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": read_traffic("decode_attn_llama3-8b-gqa-8k")},
+        "paper_context": "2.35x-3.47x decode throughput vs FP16 and 2.6x less peak memory "
+                         "(Llama-2-7B, one A100 80GB; not comparable, quoted as context)",
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, args.seed)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

@@ -16,6 +16,9 @@ FLAGS = [
     # no packed fp32 ops anywhere in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-result",
+    # MFMA accumulators in VGPRs: the kernels stay well inside 256 registers,
+    # and AGPR<->VGPR copies around the softmax rescale disappear
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
 
 

@@ -10,7 +10,8 @@
 // `gps` consecutive groups of 32 quantised tokens each (4 waves, one group per
 // wave at a time, each wave with its own online-softmax state, merged in LDS
 // at the end); split n_split_q takes the bf16 residual.  Each split writes
-// (m, l, o[128]) per query head; combine_kernel merges the splits.
+// (m, l, o[128]) per query head; the last workgroup of a unit to finish
+// merges that unit's splits into `out` (arrival counter in the workspace).
 //
 // Dequantisation is folded into the products, which is algebraically the
 // same as dequantise-then-dot:
@@ -120,6 +121,16 @@ __device__ __forceinline__ float xor_sum(float x, int m) { return x + __shfl_xor
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ float4 ld4(const float *p) { return *reinterpret_cast<const float4 *>(p); }
+
+// Split partials cross workgroups (and XCDs, whose L2 caches are not coherent
+// with each other), so they are written and read with agent-scope atomic
+// accesses, which are coherent without flushing or invalidating the L2.
+__device__ __forceinline__ void st_shared_agent(float *p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_shared_agent(const float *p) {
+  return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 __device__ __forceinline__ void ld8(const float *p, float (&x)[8]) {
   const float4 a = ld4(p), b = ld4(p + 4);
   x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
@@ -141,6 +152,7 @@ struct MergeSmem {
   float m[4][HMAX];
   float l[4][HMAX];
   float o[4][HMAX][D];
+  int last;
 };
 
 template <int HMAX>
@@ -160,22 +172,83 @@ __device__ void merge_and_store(MergeSmem<HMAX> &sm, const DecodeArgs &a, int u,
       l += f * sm.l[w][hh];
       o += f * sm.o[w][hh][c];
     }
-    part[hh * kPartStride + 4 + c] = o;
+    st_shared_agent(part + hh * kPartStride + 4 + c, o);
     if (c == 0) {
-      part[hh * kPartStride + 0] = M;
-      part[hh * kPartStride + 1] = l;
+      st_shared_agent(part + hh * kPartStride + 0, M);
+      st_shared_agent(part + hh * kPartStride + 1, l);
     }
   }
 }
 
+// ------------------------------------------------------------ combine -----
+// Called by every workgroup after it stored its partials.  Arrivals are
+// counted per unit; the last workgroup of the unit merges the n_split
+// partials of each of its query heads,
+//   M = max m_s,  out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s,
+// writes `out`, and re-arms the counter to zero for the next call.
+__device__ void finish_unit(const DecodeArgs &a, int u, int *s_last) {
+  // the barrier waits for this workgroup's partial stores (vmcnt) before the
+  // arrival is counted
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned prev =
+        __hip_atomic_fetch_add(a.counters + u, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *s_last = prev == (unsigned)(a.n_split - 1);
+  }
+  __syncthreads();
+  if (!*s_last) return;
+  const int qpk = a.qpk;
+  const long long stride = (long long)qpk * kPartStride;
+  constexpr int kBatch = 8;   // splits whose partials are loaded together
+  for (int idx = threadIdx.x; idx < qpk * D; idx += blockDim.x) {
+    const int hh = idx / D, c = idx % D;
+    const float *base = a.part + ((long long)u * a.n_split * qpk + hh) * kPartStride;
+    float M = kNegInf, l = 0.f, o = 0.f;
+    for (int s0 = 0; s0 < a.n_split; s0 += kBatch) {
+      float mb[kBatch], lb[kBatch], ob[kBatch];
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) {
+        const int sp = min(s0 + k, a.n_split - 1);
+        const float *pp = base + sp * stride;
+        mb[k] = s0 + k < a.n_split ? ld_shared_agent(pp) : kNegInf;
+        lb[k] = ld_shared_agent(pp + 1);
+        ob[k] = ld_shared_agent(pp + 4 + c);
+      }
+      float Mn = M;
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) Mn = fmaxf(Mn, mb[k]);
+      const float al = M == kNegInf ? 0.f : fast_exp2(M - Mn);
+      l *= al;
+      o *= al;
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) {
+        const float f = mb[k] == kNegInf ? 0.f : fast_exp2(mb[k] - Mn);
+        l += f * lb[k];
+        o += f * ob[k];
+      }
+      M = Mn;
+    }
+    a.out[((long long)u * qpk + hh) * D + c] = o / l;
+  }
+  if (threadIdx.x == 0)
+    __hip_atomic_store(a.counters + u, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // ------------------------------------------------------- residual split ---
-// The bf16 residual of one unit: one token per thread for q.k, then one
-// (head, channel pair) per thread for P.V, 256 tokens at a time.
+// The bf16 residual of one unit, 64 tokens at a time.  q.k: thread (token tt,
+// quarter qt) takes channels 32qt..32qt+31 of token tt for every head; the
+// four partial sums meet in LDS.  The chunk's V rows are staged in LDS with
+// coalesced loads, then P.V runs with one (head, channel pair) per thread.
+constexpr int kResChunk = 64;
+
 template <int HMAX>
 struct ResidSmem {
   float q[HMAX][D];
-  float s[HMAX][256];
+  float part[4][HMAX][kResChunk];
+  float p[HMAX][kResChunk];
+  uint32_t v[kResChunk][D / 2];
   float mx[HMAX];
+  int last;
 };
 
 template <int HMAX>
@@ -193,43 +266,53 @@ __device__ void residual_split(ResidSmem<HMAX> &sm, const DecodeArgs &a, int u, 
   for (int it = 0; it < ITEMS; ++it) { oacc[it][0] = oacc[it][1] = 0.f; lacc[it] = 0.f; }
 
   const long long ring = (long long)u * a.slots;
-  for (int t0 = 0; t0 < a.n_res; t0 += 256) {
-    const int cn = min(256, a.n_res - t0);
+  const int tt = tid & (kResChunk - 1), qt = tid >> 6;
+  for (int t0 = 0; t0 < a.n_res; t0 += kResChunk) {
+    const int cn = min(kResChunk, a.n_res - t0);
     __syncthreads();   // q staged / previous chunk consumed
-    if (tid < cn) {
-      const int slot = (a.res_start + t0 + tid) % a.slots;
-      const uint4 *krow = reinterpret_cast<const uint4 *>(a.k_res + (ring + slot) * D);
-      float s[HMAX];
+    // stage V rows: cn rows x 16 chunks of 16 bytes
+    for (int i = tid; i < cn * (D / 8); i += 256) {
+      const int r = i / (D / 8), c16 = i % (D / 8);
+      const int slot = (a.res_start + t0 + r) % a.slots;
+      reinterpret_cast<uint4 *>(sm.v[r])[c16] =
+          reinterpret_cast<const uint4 *>(a.v_res + (ring + slot) * D)[c16];
+    }
+    // partial scores over 32 channels
+    if (tt < cn) {
+      const int slot = (a.res_start + t0 + tt) % a.slots;
+      const uint4 *krow = reinterpret_cast<const uint4 *>(a.k_res + (ring + slot) * D + 32 * qt);
+      float kf[32];
 #pragma unroll
-      for (int hh = 0; hh < HMAX; ++hh) s[hh] = 0.f;
-      for (int c8 = 0; c8 < D / 8; ++c8) {
+      for (int c8 = 0; c8 < 4; ++c8) {
         const uint4 kv = krow[c8];
         const uint32_t w[4] = {kv.x, kv.y, kv.z, kv.w};
-        float kf[8];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          kf[2 * e] = __uint_as_float(w[e] << 16);
-          kf[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
-        }
-#pragma unroll
-        for (int hh = 0; hh < HMAX; ++hh) {
-          if (hh < qpk) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) s[hh] += sm.q[hh][8 * c8 + e] * kf[e];
-          }
+          kf[8 * c8 + 2 * e] = __uint_as_float(w[e] << 16);
+          kf[8 * c8 + 2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
         }
       }
 #pragma unroll
-      for (int hh = 0; hh < HMAX; ++hh)
-        if (hh < qpk) sm.s[hh][tid] = s[hh];
+      for (int hh = 0; hh < HMAX; ++hh) {
+        if (hh < qpk) {
+          float s = 0.f;
+#pragma unroll
+          for (int e = 0; e < 32; ++e) s += sm.q[hh][32 * qt + e] * kf[e];
+          sm.part[qt][hh][tt] = s;
+        }
+      }
+    }
+    __syncthreads();
+    for (int i = tid; i < qpk * kResChunk; i += 256) {
+      const int hh = i / kResChunk, t = i % kResChunk;
+      sm.p[hh][t] = sm.part[0][hh][t] + sm.part[1][hh][t] + sm.part[2][hh][t] + sm.part[3][hh][t];
     }
     __syncthreads();
     // chunk max per head: wave w reduces heads w, w+4, ...
     {
       const int w = tid >> 6, lane = tid & 63;
       for (int hh = w; hh < qpk; hh += 4) {
-        float mx = kNegInf;
-        for (int i = lane; i < cn; i += 64) mx = fmaxf(mx, sm.s[hh][i]);
+        float mx = lane < cn ? sm.p[hh][lane] : kNegInf;
 #pragma unroll
         for (int msk = 32; msk >= 1; msk >>= 1) mx = xor_max(mx, msk);
         if (lane == 0) sm.mx[hh] = mx;
@@ -247,9 +330,9 @@ __device__ void residual_split(ResidSmem<HMAX> &sm, const DecodeArgs &a, int u, 
         alpha[hh] = 0.f;
       }
     }
-    for (int i = tid; i < qpk * cn; i += 256) {
-      const int hh = i / cn, tt = i % cn;
-      sm.s[hh][tt] = fast_exp2(sm.s[hh][tt] - m_h[hh]);
+    for (int i = tid; i < qpk * kResChunk; i += 256) {
+      const int hh = i / kResChunk, t = i % kResChunk;
+      sm.p[hh][t] = t < cn ? fast_exp2(sm.p[hh][t] - m_h[hh]) : 0.f;
     }
     __syncthreads();
 #pragma unroll
@@ -262,13 +345,13 @@ __device__ void residual_split(ResidSmem<HMAX> &sm, const DecodeArgs &a, int u, 
         for (int x = 0; x < HMAX; ++x)
           if (x == hh) al = alpha[x];
         float o0 = oacc[it][0] * al, o1 = oacc[it][1] * al, l = lacc[it] * al;
-        for (int tt = 0; tt < cn; ++tt) {
-          const int slot = (a.res_start + t0 + tt) % a.slots;
-          const uint32_t vv = reinterpret_cast<const uint32_t *>(a.v_res + (ring + slot) * D)[cp];
-          const float p = sm.s[hh][tt];
-          o0 += p * __uint_as_float(vv << 16);
-          o1 += p * __uint_as_float(vv & 0xFFFF0000u);
-          l += p;
+#pragma unroll 8
+        for (int t = 0; t < cn; ++t) {
+          const uint32_t vv = sm.v[t][cp];
+          const float pr = sm.p[hh][t];
+          o0 += pr * __uint_as_float(vv << 16);
+          o1 += pr * __uint_as_float(vv & 0xFFFF0000u);
+          l += pr;
         }
         oacc[it][0] = o0; oacc[it][1] = o1; lacc[it] = l;
       }
@@ -284,27 +367,255 @@ __device__ void residual_split(ResidSmem<HMAX> &sm, const DecodeArgs &a, int u, 
 #pragma unroll
       for (int x = 0; x < HMAX; ++x)
         if (x == hh) mh = m_h[x];
-      reinterpret_cast<float2 *>(part + hh * kPartStride + 4)[cp] =
-          make_float2(oacc[it][0], oacc[it][1]);
+      st_shared_agent(part + hh * kPartStride + 4 + 2 * cp, oacc[it][0]);
+      st_shared_agent(part + hh * kPartStride + 5 + 2 * cp, oacc[it][1]);
       if (cp == 0) {
-        part[hh * kPartStride + 0] = mh;
-        part[hh * kPartStride + 1] = lacc[it];
+        st_shared_agent(part + hh * kPartStride + 0, mh);
+        st_shared_agent(part + hh * kPartStride + 1, lacc[it]);
       }
     }
   }
 }
 
 // ------------------------------------------------------ MFMA (GQA) path ---
+// ---- cross-lane sums / maxima without LDS round trips.  A wave is 4 rows of
+// 16 lanes; permlane16/32 swaps exchange row pairs, so x + swap(x) is the
+// sum over lanes l and l^16 (l^32) in every lane.
+__device__ __forceinline__ float sum_x16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_x32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_x16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_x32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+// sum over the 4 lanes n, n+-4, n+-8, n+-12 of each 16-lane row (DPP rotations)
+__device__ __forceinline__ float sum_row_stride4(float x) {
+  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x124, 0xF, 0xF, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x128, 0xF, 0xF, false));
+  return x;
+}
+
+typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4_t;
+typedef __attribute__((__vector_size__(2 * sizeof(unsigned)))) unsigned u32x2_t;
+
+// Buffer descriptor of a workgroup-uniform range (values forced into SGPRs, so
+// the loads need no per-lane descriptor loop).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  // readfirstlane returns int: go through uint32_t so that widening does not
+  // sign-extend the low address word into the high one
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)p);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>((hi << 32) | lo), (short)0,
+                                           (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+__device__ __forceinline__ void buf8f(__amdgpu_buffer_rsrc_t r, uint32_t vo, uint32_t so, float (&x)[8]) {
+  const u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(r, vo, so, 0);
+  const u32x4_t b = __builtin_amdgcn_raw_buffer_load_b128(r, vo + 16, so, 0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[i] = __uint_as_float(a[i]);
+    x[4 + i] = __uint_as_float(b[i]);
+  }
+}
+
+// Raw bytes of one group as one lane of the MFMA path needs them: K codes of
+// its two A-operand rows, V codes of its 8 channels x 8 tokens, and the
+// scale/zero values its q' and P.V roles read.
+template <int BITS>
+struct GroupRaw {
+  uint32_t kw[2][BITS];   // per tile: 32 channels of one token
+  uint32_t vw[2 * BITS];  // 8 channels x 8 tokens
+  float sk[8], zk[8], sv[8], zv[8];
+};
+
+// Per-unit buffer views and the lane-constant byte offsets of one lane; the
+// group enters only through scalar offsets (g * bytes per group).
+struct UnitView {
+  __amdgpu_buffer_rsrc_t kc, vc, ks, kz, vs, vz;
+  uint32_t o_k0, o_k1, o_v, o_km, o_vm;
+};
+
+template <int BITS>
+__device__ __forceinline__ UnitView make_view(const DecodeArgs &a, int u, int n, int gq, int cm) {
+  constexpr int KROW = D * BITS / 8;
+  constexpr int CB = 32 * BITS / 8;
+  const long long T = a.max_tokens, NG = a.n_groups_cap;
+  UnitView v;
+  const uint32_t code_bytes = (uint32_t)(T * KROW), meta_bytes = (uint32_t)(NG * D * 4);
+  v.kc = make_rsrc(a.k_codes + u * T * KROW, code_bytes);
+  v.vc = make_rsrc(a.v_codes + u * T * KROW, code_bytes);
+  v.ks = make_rsrc(a.k_scale + u * NG * D, meta_bytes);
+  v.kz = make_rsrc(a.k_zero + u * NG * D, meta_bytes);
+  v.vs = make_rsrc(a.v_scale + u * NG * D, meta_bytes);
+  v.vz = make_rsrc(a.v_zero + u * NG * D, meta_bytes);
+  const int kr0 = 8 * (n >> 2) + (n & 3);   // A-operand row n of tile 0 -> token; tile 1: +4
+  v.o_k0 = kr0 * KROW + gq * CB;
+  v.o_k1 = (kr0 + 4) * KROW + gq * CB;
+  v.o_v = (gq * D + 8 * n) * BITS;
+  v.o_km = (32 * gq + 8 * cm) * 4;
+  v.o_vm = ((n >> 2) * G + 8 * gq) * 4;
+  return v;
+}
+
+template <int BITS>
+__device__ __forceinline__ void load_group(GroupRaw<BITS> &r, const UnitView &v, int g) {
+  // group offsets are wave-uniform: keep them in SGPRs (scalar buffer offsets)
+  const uint32_t sc = __builtin_amdgcn_readfirstlane((uint32_t)g * (G * D * BITS / 8));
+  const uint32_t sm = __builtin_amdgcn_readfirstlane((uint32_t)g * (D * 4));
+  if constexpr (BITS == 2) {
+    const u32x2_t a = __builtin_amdgcn_raw_buffer_load_b64(v.kc, v.o_k0, sc, 0);
+    const u32x2_t b = __builtin_amdgcn_raw_buffer_load_b64(v.kc, v.o_k1, sc, 0);
+    r.kw[0][0] = a[0]; r.kw[0][1] = a[1];
+    r.kw[1][0] = b[0]; r.kw[1][1] = b[1];
+    const u32x4_t c = __builtin_amdgcn_raw_buffer_load_b128(v.vc, v.o_v, sc, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r.vw[i] = c[i];
+  } else {
+    const u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(v.kc, v.o_k0, sc, 0);
+    const u32x4_t b = __builtin_amdgcn_raw_buffer_load_b128(v.kc, v.o_k1, sc, 0);
+    const u32x4_t c = __builtin_amdgcn_raw_buffer_load_b128(v.vc, v.o_v, sc, 0);
+    const u32x4_t d = __builtin_amdgcn_raw_buffer_load_b128(v.vc, v.o_v + 16, sc, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      r.kw[0][i] = a[i]; r.kw[1][i] = b[i];
+      r.vw[i] = c[i]; r.vw[4 + i] = d[i];
+    }
+  }
+  buf8f(v.ks, v.o_km, sm, r.sk);
+  buf8f(v.kz, v.o_km, sm, r.zk);
+  buf8f(v.vs, v.o_vm, sm, r.sv);
+  buf8f(v.vz, v.o_vm, sm, r.zv);
+}
+
 template <int NHB>
 struct MfmaSmem {
   uint4 bq[4][NHB][2][4][4][4];   // [wave][head block][hi/lo][head][step][lane group]
 };
 
+// Online-softmax state of one wave (per head block): P.V accumulators in the
+// MFMA output layout, running max (log2 units), and per-lane partial sums of
+// p and of p * zero^V.
+template <int NHB>
+struct WaveState {
+  f32x4_t acc[NHB][8];
+  float m_run[NHB], l_run[NHB], z_run[NHB];
+};
+
+template <int BITS, int NHB>
+__device__ __forceinline__ void mfma_group(const GroupRaw<BITS> &cur, WaveState<NHB> &st,
+                                           MfmaSmem<NHB> &smf, const float (&qv)[NHB][8],
+                                           int wave, int n, int gq, int ch, int cm) {
+  // ---- A operands (exact codes)
+  Op8 ak[2][4];
+#pragma unroll
+  for (int tile = 0; tile < 2; ++tile) {
+    if constexpr (BITS == 2) {
+      unpack2(cur.kw[tile][0], ak[tile][0], ak[tile][1]);
+      unpack2(cur.kw[tile][1], ak[tile][2], ak[tile][3]);
+    } else {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) unpack4(cur.kw[tile][m], ak[tile][m]);
+    }
+  }
+  Op8 av[8];
+  if constexpr (BITS == 2) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) unpack2(cur.vw[d], av[2 * d], av[2 * d + 1]);
+  } else {
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) unpack4(cur.vw[mt], av[mt]);
+  }
+
+#pragma unroll
+  for (int hb = 0; hb < NHB; ++hb) {
+    // ---- cooperative q' = q * s^K (hi/lo) and beta = q . z^K
+    float beta = 0.f;
+    {
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int s = 0; s < 8; s += 2) {
+        split_bf16(qv[hb][s] * cur.sk[P8[s]], qv[hb][s + 1] * cur.sk[P8[s + 1]], hi[s / 2],
+                   lo[s / 2]);
+        beta += qv[hb][s] * cur.zk[P8[s]];
+        beta += qv[hb][s + 1] * cur.zk[P8[s + 1]];
+      }
+      smf.bq[wave][hb][0][ch][cm][gq] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+      smf.bq[wave][hb][1][ch][cm][gq] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    }
+    // every lane with (lane & 3) == head gets beta[head]
+    beta = sum_x32(sum_x16(sum_row_stride4(beta)));
+    __builtin_amdgcn_wave_barrier();
+
+    // ---- scores: columns n = 4x + head, x in {hi, lo, hi, lo}
+    f32x4_t sc[2] = {f32x4_t{beta, beta, beta, beta}, f32x4_t{beta, beta, beta, beta}};
+    if (n & 4) {   // lo columns: beta enters once, through the hi column
+      sc[0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      sc[1] = sc[0];
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      Op8 bq;
+      const uint4 x = smf.bq[wave][hb][(n >> 2) & 1][n & 3][m][gq];
+      bq.u[0] = x.x; bq.u[1] = x.y; bq.u[2] = x.z; bq.u[3] = x.w;
+#pragma unroll
+      for (int tile = 0; tile < 2; ++tile)
+        sc[tile] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak[tile][m].v, bq.v, sc[tile], 0, 0, 0);
+    }
+    // token 8gq + 4*tile + r  <->  p index 4*tile + r
+    float s8[8];
+#pragma unroll
+    for (int tile = 0; tile < 2; ++tile)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s8[4 * tile + r] = sc[tile][r] + dpp_ror4(sc[tile][r]);
+
+    // ---- online softmax (log2 domain), lazily rescaled
+    float mx = fmaxf(fmaxf(fmaxf(s8[0], s8[1]), fmaxf(s8[2], s8[3])),
+                     fmaxf(fmaxf(s8[4], s8[5]), fmaxf(s8[6], s8[7])));
+    mx = max_x32(max_x16(mx));
+    const bool need = mx > st.m_run[hb] + kRescaleSlack;
+    if (__any(need)) {
+      const float mnew = need ? mx : st.m_run[hb];
+      const float al = st.m_run[hb] == kNegInf ? 0.f : fast_exp2(st.m_run[hb] - mnew);
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) st.acc[hb][mt] *= al;
+      st.l_run[hb] *= al;
+      st.z_run[hb] *= al;
+      st.m_run[hb] = mnew;
+    }
+    float p[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      p[k] = fast_exp2(s8[k] - st.m_run[hb]);
+      st.l_run[hb] += p[k];
+      st.z_run[hb] += p[k] * cur.zv[k];
+    }
+    // ---- P.V: columns n = 4j + head; B slot s <-> token 8gq + P8[s]
+    Op8 bh, bl;
+#pragma unroll
+    for (int s = 0; s < 8; s += 2)
+      split_bf16(p[P8[s]] * cur.sv[P8[s]], p[P8[s + 1]] * cur.sv[P8[s + 1]], bh.u[s / 2],
+                 bl.u[s / 2]);
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+      st.acc[hb][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mt].v, bh.v, st.acc[hb][mt], 0, 0, 0);
+      st.acc[hb][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mt].v, bl.v, st.acc[hb][mt], 0, 0, 0);
+    }
+  }
+}
+
 template <int BITS, int NHB>
 __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int HMAX = 4 * NHB;
-  constexpr int KROW = D * BITS / 8;     // bytes per token row of K codes
-  constexpr int CB = 32 * BITS / 8;      // bytes of 32 channels
   __shared__ __align__(16) union {
     MfmaSmem<NHB> mf;
     MergeSmem<HMAX> mg;
@@ -314,9 +625,11 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   const int split = blockIdx.x, u = blockIdx.y;
   if (split >= a.n_split_q) {
     residual_split<HMAX>(sm.rs, a, u, split);
+    finish_unit(a, u, &sm.rs.last);
     return;
   }
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // wave index made visibly wave-uniform so that group offsets live in SGPRs
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int n = lane & 15, gq = lane >> 4;          // MFMA column / row, lane group
   const int ch = lane & 3, cm = (lane >> 2) & 3;    // cooperative q' role: head, step
   const int qpk = a.qpk;
@@ -345,156 +658,41 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     }
   }
 
-  f32x4_t acc[NHB][8];
-  float m_run[NHB], l_run[NHB], z_run[NHB];
+  WaveState<NHB> st;
 #pragma unroll
   for (int hb = 0; hb < NHB; ++hb) {
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) acc[hb][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    m_run[hb] = kNegInf; l_run[hb] = 0.f; z_run[hb] = 0.f;
+    for (int mt = 0; mt < 8; ++mt) st.acc[hb][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    st.m_run[hb] = kNegInf; st.l_run[hb] = 0.f; st.z_run[hb] = 0.f;
   }
 
   const int g_begin = split * a.gps;
   const int g_end = min(g_begin + a.gps, a.n_groups);
-  const int kr0 = 8 * (n >> 2) + (n & 3);   // A-operand row n of tile 0 -> token; tile 1: +4
-  const int jv = n >> 2;                      // V channel group of this column (P.V)
-  const int hv = n & 3;                       // head (within block) of this column
+  const UnitView view = make_view<BITS>(a, u, n, gq, cm);
 
-  for (int g = g_begin + wave; g < g_end; g += 4) {
-    const long long ug = (long long)u * a.n_groups_cap + g;
-    // ---- loads
-    const uint8_t *kb = a.k_codes + ((long long)u * a.max_tokens + (long long)g * G) * KROW + gq * CB;
-    const uint8_t *vb = a.v_codes + ((ug * (G / 8) + gq) * D + 8 * n) * BITS;
-    uint32_t kw[2][BITS];   // per tile: BITS words = 32 channels
-#pragma unroll
-    for (int tile = 0; tile < 2; ++tile) {
-      const uint8_t *p = kb + (kr0 + 4 * tile) * KROW;
-      if constexpr (BITS == 2) {
-        const uint2 x = *reinterpret_cast<const uint2 *>(p);
-        kw[tile][0] = x.x; kw[tile][1] = x.y;
-      } else {
-        const uint4 x = *reinterpret_cast<const uint4 *>(p);
-        kw[tile][0] = x.x; kw[tile][1] = x.y; kw[tile][2] = x.z; kw[tile][3] = x.w;
-      }
-    }
-    uint32_t vw[2 * BITS];   // 8 channels x 8 tokens
-    {
-      const uint4 x = *reinterpret_cast<const uint4 *>(vb);
-      vw[0] = x.x; vw[1] = x.y; vw[2] = x.z; vw[3] = x.w;
-      if constexpr (BITS == 4) {
-        const uint4 y = *reinterpret_cast<const uint4 *>(vb + 16);
-        vw[4] = y.x; vw[5] = y.y; vw[6] = y.z; vw[7] = y.w;
-      }
-    }
-    float sk[8], zk[8], sv[8], zv[8];
-    ld8(a.k_scale + ug * D + 32 * gq + 8 * cm, sk);
-    ld8(a.k_zero + ug * D + 32 * gq + 8 * cm, zk);
-    ld8(a.v_scale + (ug * (D / G) + jv) * G + 8 * gq, sv);
-    ld8(a.v_zero + (ug * (D / G) + jv) * G + 8 * gq, zv);
-
-    // ---- A operands (exact codes)
-    Op8 ak[2][4];
-#pragma unroll
-    for (int tile = 0; tile < 2; ++tile) {
-      if constexpr (BITS == 2) {
-        unpack2(kw[tile][0], ak[tile][0], ak[tile][1]);
-        unpack2(kw[tile][1], ak[tile][2], ak[tile][3]);
-      } else {
-#pragma unroll
-        for (int m = 0; m < 4; ++m) unpack4(kw[tile][m], ak[tile][m]);
-      }
-    }
-    Op8 av[8];
-    if constexpr (BITS == 2) {
-#pragma unroll
-      for (int d = 0; d < 4; ++d) unpack2(vw[d], av[2 * d], av[2 * d + 1]);
-    } else {
-#pragma unroll
-      for (int mt = 0; mt < 8; ++mt) unpack4(vw[mt], av[mt]);
-    }
-
-#pragma unroll
-    for (int hb = 0; hb < NHB; ++hb) {
-      // ---- cooperative q' = q * s^K (hi/lo) and beta = q . z^K
-      float beta = 0.f;
-      {
-        uint32_t hi[4], lo[4];
-#pragma unroll
-        for (int s = 0; s < 8; s += 2) {
-          split_bf16(qv[hb][s] * sk[P8[s]], qv[hb][s + 1] * sk[P8[s + 1]], hi[s / 2], lo[s / 2]);
-          beta += qv[hb][s] * zk[P8[s]];
-          beta += qv[hb][s + 1] * zk[P8[s + 1]];
-        }
-        sm.mf.bq[wave][hb][0][ch][cm][gq] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-        sm.mf.bq[wave][hb][1][ch][cm][gq] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-      }
-      beta = xor_sum(beta, 4);
-      beta = xor_sum(beta, 8);
-      beta = xor_sum(beta, 16);
-      beta = xor_sum(beta, 32);   // every lane with (lane & 3) == head holds beta[head]
-      __builtin_amdgcn_wave_barrier();
-
-      // ---- scores: columns n = 4x + head, x in {hi, lo, hi, lo}
-      f32x4_t sc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        Op8 bq;
-        const uint4 x = sm.mf.bq[wave][hb][(n >> 2) & 1][n & 3][m][gq];
-        bq.u[0] = x.x; bq.u[1] = x.y; bq.u[2] = x.z; bq.u[3] = x.w;
-#pragma unroll
-        for (int tile = 0; tile < 2; ++tile)
-          sc[tile] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak[tile][m].v, bq.v, sc[tile], 0, 0, 0);
-      }
-      // token 8gq + 4*tile + r  <->  p index 4*tile + r
-      float s8[8];
-#pragma unroll
-      for (int tile = 0; tile < 2; ++tile)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) s8[4 * tile + r] = sc[tile][r] + dpp_ror4(sc[tile][r]) + beta;
-
-      // ---- online softmax (log2 domain), lazily rescaled
-      float mx = s8[0];
-#pragma unroll
-      for (int k = 1; k < 8; ++k) mx = fmaxf(mx, s8[k]);
-      mx = xor_max(mx, 16);
-      mx = xor_max(mx, 32);
-      const bool need = mx > m_run[hb] + kRescaleSlack;
-      if (__any(need)) {
-        const float mnew = need ? mx : m_run[hb];
-        const float al = m_run[hb] == kNegInf ? 0.f : fast_exp2(m_run[hb] - mnew);
-#pragma unroll
-        for (int mt = 0; mt < 8; ++mt) acc[hb][mt] *= al;
-        l_run[hb] *= al;
-        z_run[hb] *= al;
-        m_run[hb] = mnew;
-      }
-      float p[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        p[k] = fast_exp2(s8[k] - m_run[hb]);
-        l_run[hb] += p[k];
-        z_run[hb] += p[k] * zv[k];
-      }
-      // ---- P.V: columns n = 4j + head; B slot s <-> token 8gq + P8[s]
-      Op8 bh, bl;
-#pragma unroll
-      for (int s = 0; s < 8; s += 2)
-        split_bf16(p[P8[s]] * sv[P8[s]], p[P8[s + 1]] * sv[P8[s + 1]], bh.u[s / 2], bl.u[s / 2]);
-#pragma unroll
-      for (int mt = 0; mt < 8; ++mt) {
-        acc[hb][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mt].v, bh.v, acc[hb][mt], 0, 0, 0);
-        acc[hb][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mt].v, bl.v, acc[hb][mt], 0, 0, 0);
-      }
-    }
+  // software pipeline, two register sets used in turn: the next group of this
+  // wave is in flight while the current one is computed
+  GroupRaw<BITS> r0, r1;
+  int g = g_begin + wave;
+  if (g < g_end) load_group<BITS>(r0, view, g);
+  while (g < g_end) {
+    if (g + 4 < g_end) load_group<BITS>(r1, view, g + 4);
+    mfma_group<BITS, NHB>(r0, st, sm.mf, qv, wave, n, gq, ch, cm);
+    g += 4;
+    if (g >= g_end) break;
+    if (g + 4 < g_end) load_group<BITS>(r0, view, g + 4);
+    mfma_group<BITS, NHB>(r1, st, sm.mf, qv, wave, n, gq, ch, cm);
+    g += 4;
   }
 
   // ---- per-wave totals, then the workgroup merge (the merge buffer aliases
   // the q' staging of the other waves: wait until every wave left the loop)
   __syncthreads();
+  const int jv = n >> 2, hv = n & 3;
 #pragma unroll
   for (int hb = 0; hb < NHB; ++hb) {
-    float l = xor_sum(xor_sum(l_run[hb], 16), 32);
-    float z = xor_sum(xor_sum(z_run[hb], 16), 32);
+    const float l = sum_x32(sum_x16(st.l_run[hb]));
+    const float z = sum_x32(sum_x16(st.z_run[hb]));
     // lane (n, gq) holds rows 4gq + r of M-tile mt = channel 32gq + 8r + mt,
     // for column n = 4j + head; the column is useful when j == gq.
     if (jv == gq) {
@@ -502,18 +700,19 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
       for (int r = 0; r < 4; ++r) {
         float o8[8];
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt) o8[mt] = acc[hb][mt][r] + z;
+        for (int mt = 0; mt < 8; ++mt) o8[mt] = st.acc[hb][mt][r] + z;
         float *dst = &sm.mg.o[wave][hb * 4 + hv][32 * gq + 8 * r];
         *reinterpret_cast<float4 *>(dst) = make_float4(o8[0], o8[1], o8[2], o8[3]);
         *reinterpret_cast<float4 *>(dst + 4) = make_float4(o8[4], o8[5], o8[6], o8[7]);
       }
     }
     if (gq == 0 && n < 4) {
-      sm.mg.m[wave][hb * 4 + n] = m_run[hb];
+      sm.mg.m[wave][hb * 4 + n] = st.m_run[hb];
       sm.mg.l[wave][hb * 4 + n] = l;
     }
   }
   merge_and_store<HMAX>(sm.mg, a, u, split);
+  finish_unit(a, u, &sm.mg.last);
 }
 
 // ------------------------------------------------------- VALU (MHA) path ---
@@ -535,6 +734,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
   const int split = blockIdx.x, u = blockIdx.y;
   if (split >= a.n_split_q) {
     residual_split<1>(sm.rs, a, u, split);
+    finish_unit(a, u, &sm.rs.last);
     return;
   }
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -720,27 +920,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
     sm.mg.l[wave][0] = l;
   }
   merge_and_store<1>(sm.mg, a, u, split);
-}
-
-// ---------------------------------------------------------- combine -----
-__global__ __launch_bounds__(128) void combine_kernel(DecodeArgs a) {
-  const int row = blockIdx.x, c = threadIdx.x;
-  const int hq_count = a.kv_heads * a.qpk;
-  const int b = row / hq_count, hq = row % hq_count;
-  const int h = hq / a.qpk, j = hq % a.qpk;
-  const long long u = (long long)b * a.kv_heads + h;
-  const float *base = a.part + (u * a.n_split * a.qpk + j) * kPartStride;
-  const long long stride = (long long)a.qpk * kPartStride;
-  float M = kNegInf;
-  for (int s = 0; s < a.n_split; ++s) M = fmaxf(M, base[s * stride]);
-  float l = 0.f, o = 0.f;
-  for (int s = 0; s < a.n_split; ++s) {
-    const float *p = base + s * stride;
-    const float f = p[0] == kNegInf ? 0.f : fast_exp2(p[0] - M);
-    l += f * p[1];
-    o += f * p[4 + c];
-  }
-  a.out[(long long)row * D + c] = o / l;
+  finish_unit(a, u, &sm.mg.last);
 }
 
 }  // namespace
@@ -766,9 +946,6 @@ hipError_t launch_decode(int bits, const DecodeArgs &a, hipStream_t s) {
   else
     KIVI_LAUNCH(4);
 #undef KIVI_LAUNCH
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(combine_kernel, dim3(a.n_units * a.qpk), dim3(128), 0, s, a);
   return hipGetLastError();
 }
 

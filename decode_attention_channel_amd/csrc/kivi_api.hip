@@ -31,6 +31,7 @@ kivi_status check_geom(const kivi_geom *g) {
   if (g->group != kivi::kGroup || g->head_dim != kivi::kHeadDim) return KIVI_E_UNSUPPORTED;
   if (g->residual % g->group != 0 || g->residual > 4096) return KIVI_E_UNSUPPORTED;
   if (g->q_per_kv > 16) return KIVI_E_UNSUPPORTED;
+  if ((long long)g->batch * g->kv_heads > 65535) return KIVI_E_UNSUPPORTED;   // grid.y
   if (g->max_tokens % g->group != 0) return KIVI_E_UNSUPPORTED;
   // keep every byte offset of every buffer inside 2^62
   const double units = (double)g->batch * g->kv_heads;
@@ -57,6 +58,12 @@ kivi_status check_state(const kivi_geom *g, const kivi_cache *c) {
 }
 
 long long units_of(const kivi_geom *g) { return (long long)g->batch * g->kv_heads; }
+
+// decode workspace: one arrival counter per unit (padded to 256 B), then the
+// split partials
+size_t counters_bytes(const kivi_geom *g) {
+  return ((size_t)units_of(g) * sizeof(unsigned) + 255) / 256 * 256;
+}
 
 int max_splits(const kivi_geom *g) {
   const int ng = g->max_tokens / g->group;
@@ -124,8 +131,8 @@ kivi_status kivi_decode_workspace_size(const kivi_geom *g, size_t *bytes) {
   kivi_status st = check_geom(g);
   if (st != KIVI_OK) return st;
   if (!bytes) return KIVI_E_NULL;
-  *bytes = (size_t)units_of(g) * (size_t)max_splits(g) * (size_t)g->q_per_kv *
-           (size_t)kivi::kPartStride * sizeof(float);
+  *bytes = counters_bytes(g) + (size_t)units_of(g) * (size_t)max_splits(g) *
+                                   (size_t)g->q_per_kv * (size_t)kivi::kPartStride * sizeof(float);
   return KIVI_OK;
 }
 
@@ -236,7 +243,9 @@ kivi_status kivi_decode_attention(const kivi_geom *g, const kivi_cache *c, const
   a.k_codes = c->k_codes; a.k_scale = c->k_scale; a.k_zero = c->k_zero;
   a.v_codes = c->v_codes; a.v_scale = c->v_scale; a.v_zero = c->v_zero;
   a.k_res = c->k_res; a.v_res = c->v_res;
-  a.q = q; a.out = out; a.part = (float *)ws;
+  a.q = q; a.out = out;
+  a.counters = (unsigned *)ws;
+  a.part = (float *)((char *)ws + counters_bytes(g));
   a.qscale = softmax_scale * 1.4426950408889634f;
   a.kv_heads = g->kv_heads; a.qpk = g->q_per_kv; a.max_tokens = g->max_tokens;
   a.n_groups_cap = g->max_tokens / g->group;

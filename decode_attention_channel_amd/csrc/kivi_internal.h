@@ -49,6 +49,7 @@ struct DecodeArgs {
   const uint8_t *v_codes; const float *v_scale, *v_zero;
   const uint16_t *k_res, *v_res;
   const uint16_t *q;
+  unsigned *counters; // [units] arrival counters, zero between calls
   float *part;        // [units][n_split][QPK][kPartStride]
   float *out;         // [B][Hq][D]
   float qscale;       // softmax_scale * log2(e): scores come out in log2 units

@@ -208,12 +208,13 @@ def flush_residual(g: Geom, c: Cache) -> int:
 
 
 class Workspace:
-    """Device scratch for decode attention, sized for a geometry."""
+    """Device workspace for decode attention, sized for a geometry and
+    zero-filled once (the calls leave its arrival counters at zero)."""
 
     def __init__(self, g: Geom, device=None):
         device = torch.device("cuda", torch.cuda.current_device()) if device is None else device
         self.nbytes = workspace_size(g)
-        self.buf = torch.empty(max(self.nbytes, 16), dtype=torch.uint8, device=device)
+        self.buf = torch.zeros(max(self.nbytes, 16), dtype=torch.uint8, device=device)
 
 
 def decode_attention(g: Geom, c: Cache, q: torch.Tensor, out: torch.Tensor | None = None,
@@ -232,3 +233,45 @@ def decode_attention(g: Geom, c: Cache, q: torch.Tensor, out: torch.Tensor | Non
                                       ctypes.c_void_p(ws.buf.data_ptr()), ws.nbytes, _stream()),
            "kivi_decode_attention")
     return out
+
+
+class LayerStepper:
+    """Pre-marshalled arguments of one layer's decode step (append, flush,
+    attend) for tight loops: the geometry, cache, workspace, q/out buffers,
+    softmax scale and stream (torch's current stream at construction) are
+    converted once; append() checks only the new token's tensors."""
+
+    def __init__(self, g: Geom, c: Cache, ws: Workspace, q: torch.Tensor, out: torch.Tensor,
+                 softmax_scale: float | None = None):
+        shape_q = (g.batch, g.q_heads, g.head_dim)
+        self.geom, self.cache = g, c
+        self._g = g.c()
+        self._gp, self._cp = ctypes.byref(self._g), ctypes.byref(c._c)
+        self._q = _ptr(q, torch.bfloat16, shape_q, "q")
+        self._out = _ptr(out, torch.float32, shape_q, "out")
+        self._keep = (q, out, ws)
+        self._ws, self._wsn = ctypes.c_void_p(ws.buf.data_ptr()), ws.nbytes
+        scale = 1.0 / math.sqrt(g.head_dim) if softmax_scale is None else float(softmax_scale)
+        self._scale = ctypes.c_float(scale)
+        self._stream = _stream()
+        self._flushed = ctypes.c_int32(0)
+        self._tok_shape = (g.batch, g.kv_heads, g.head_dim)
+
+    def append(self, k_new: torch.Tensor, v_new: torch.Tensor) -> None:
+        if (k_new.shape != self._tok_shape or v_new.shape != self._tok_shape or
+                k_new.dtype != torch.bfloat16 or v_new.dtype != torch.bfloat16 or
+                not k_new.is_contiguous() or not v_new.is_contiguous()):
+            raise ValueError("k_new / v_new must be contiguous bf16 [B][H][D]")
+        _check(_lib.kivi_append_token(self._gp, self._cp, ctypes.c_void_p(k_new.data_ptr()),
+                                      ctypes.c_void_p(v_new.data_ptr()), self._stream),
+               "kivi_append_token")
+
+    def flush(self) -> int:
+        _check(_lib.kivi_flush_residual(self._gp, self._cp, ctypes.byref(self._flushed),
+                                        self._stream), "kivi_flush_residual")
+        return self._flushed.value
+
+    def attend(self) -> None:
+        _check(_lib.kivi_decode_attention(self._gp, self._cp, self._q, self._out, self._scale,
+                                          self._ws, self._wsn, self._stream),
+               "kivi_decode_attention")

@@ -204,8 +204,11 @@ kivi_status kivi_flush_residual(const kivi_geom *geom, kivi_cache *cache,
  * tokens (dequantised history and bf16 residual; no mask, no position
  * handling), p = softmax(score), out = sum_t p_t v_t, accumulated in fp32.
  * q:   device bf16 [B][Hq][D];  out: device fp32 [B][Hq][D] (written fully).
- * ws:  device workspace of at least kivi_decode_workspace_size bytes; its
- *      contents need no initialisation and are scratch after the call.
+ * ws:  device workspace of at least kivi_decode_workspace_size bytes, filled
+ *      with zero bytes before its first use.  It holds one arrival counter per
+ *      (sequence, kv head) and the split-K partials; every call returns the
+ *      counters to zero, so a workspace is reusable by later calls ordered on
+ *      the same stream.  Calls that overlap in time on one workspace race.
  * Errors: KIVI_E_NULL, KIVI_E_GEOMETRY, KIVI_E_UNSUPPORTED, KIVI_E_STATE
  *         (n_q + n_res == 0 or counters out of range), KIVI_E_WORKSPACE,
  *         KIVI_E_HIP. */

@@ -41,7 +41,7 @@ def test_layout_sizes(bits):
     assert kivi.cache_layout(g) == [U * T * D * bits // 8, U * NG * D * 4, U * NG * D * 4,
                                     U * NG * 4 * D * bits, U * NG * 4 * 32 * 4,
                                     U * NG * 4 * 32 * 4, U * S * D * 2, U * S * D * 2]
-    assert kivi.workspace_size(g) == U * (NG // 4 + 1) * 4 * 132 * 4
+    assert kivi.workspace_size(g) == 256 + U * (NG // 4 + 1) * 4 * 132 * 4
 
 
 @pytest.mark.parametrize("kw,status", [
