@@ -1,0 +1,134 @@
+"""GPU parity at the full sizes of the workloads (the launch configuration
+that bench.py times), checked on sampled (sequence, kv head) units that the
+oracle recomputes one by one:
+
+* Llama-3-8B GQA, batch 16, 8 kv / 32 q heads, 8192 tokens, 2-bit: prefill
+  bytes and decode attention on sampled units;
+* Llama-2-7B-shaped MHA layer, batch 8, 32 heads, 4096 tokens, 2-bit:
+  prefill, then 128 decode steps (append, flush, attend) with 4 flushes;
+* long-context 4-bit GQA, batch 4, 8 kv / 32 q heads, 32768 tokens: prefill,
+  then 1024 streamed tokens with a flush every 32, attention checked along
+  the way;
+* Llama-2-13B-shaped MHA, 40 heads, 4096 tokens, at batch 8 (the memory-wall
+  sweep of that workload is a benchmark, not a test).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from kivi_testutil import ATTN_TOL, bits_to_dev, row_rel_err, to_np
+
+kivi = pytest.importorskip("decode_attention_channel_amd.kivi")
+
+pytestmark = pytest.mark.gpu
+
+
+def _unit_geoms(w, T):
+    return oracle.Geom(1, 1, w.q_per_kv, bits=w.bits, max_tokens=T)
+
+
+def _check_unit_cache(gc, oc1, b, h):
+    """Device cache unit (b, h) against a one-unit oracle cache."""
+    nq, ng = oc1.n_q, oc1.n_q // 32
+    assert (gc.n_q, gc.n_res) == (oc1.n_q, oc1.n_res)
+    np.testing.assert_array_equal(to_np(gc.k_codes[b, h, :nq]), oc1.k_codes[0, 0, :nq])
+    np.testing.assert_array_equal(to_np(gc.v_codes[b, h, :ng]), oc1.v_codes[0, 0, :ng])
+    for name in ("k_scale", "k_zero", "v_scale", "v_zero"):
+        np.testing.assert_array_equal(to_np(getattr(gc, name)[b, h, :ng]).view(np.uint32),
+                                      getattr(oc1, name)[0, 0, :ng].view(np.uint32), name)
+    slots = 160
+    go = [(gc.res_start + i) % slots for i in range(gc.n_res)]
+    ro = [(oc1.res_start + i) % slots for i in range(oc1.n_res)]
+    np.testing.assert_array_equal(to_np(gc.k_res[b, h])[go], oc1.k_res[0, 0, ro])
+    np.testing.assert_array_equal(to_np(gc.v_res[b, h])[go], oc1.v_res[0, 0, ro])
+
+
+def _check_unit_attention(out_np, oc1, q_bits, b, h, qpk, scale):
+    qrows = q_bits[b:b + 1, h * qpk:(h + 1) * qpk].copy()
+    ref = oracle.attention(oc1, qrows, scale)[0]
+    err = row_rel_err(out_np[b, h * qpk:(h + 1) * qpk], ref)
+    assert err <= ATTN_TOL, f"unit (b={b}, h={h}): row-relative error {err:.3e}"
+    return err
+
+
+def _sample_units(w, k, seed):
+    rng = np.random.default_rng(seed)
+    units = {(0, 0), (w.batch - 1, w.kv_heads - 1)}
+    while len(units) < k:
+        units.add((int(rng.integers(w.batch)), int(rng.integers(w.kv_heads))))
+    return sorted(units)
+
+
+@pytest.mark.parametrize("name", ["llama3-8b-gqa-8k", "llama2-13b-mha-wall"])
+def test_prefill_and_decode_full_size(name):
+    w = synth.WORKLOADS[name]
+    batch = 8 if name == "llama2-13b-mha-wall" else w.batch
+    print(f"workload {name} batch {batch}", flush=True)
+    k, v = synth.prefill_kv(w, 11, batch=batch)
+    q = synth.query(w, 11, batch=batch)
+    T = 32 * math.ceil((w.seq_len - 128 + 32) / 32)
+    g = kivi.Geom(batch, w.kv_heads, w.q_per_kv, bits=w.bits, max_tokens=T)
+    gc = kivi.Cache(g)
+    kivi.quantize_prefill(g, gc, k.cuda(), v.cuda())
+    out = torch.full((batch, w.q_heads, 128), float("nan"), device="cuda")
+    kivi.decode_attention(g, gc, q.cuda(), out=out)
+    torch.cuda.synchronize()
+    out_np = to_np(out)
+    assert np.isfinite(out_np).all()
+    kb, vb, qb = synth.bits_u16(k), synth.bits_u16(v), synth.bits_u16(q)
+    og = _unit_geoms(w, T)
+    scale = 1.0 / math.sqrt(128)
+    for b, h in _sample_units(synth.Workload(name, batch, w.kv_heads, w.q_per_kv, w.seq_len,
+                                             w.bits, 1, 3, 8.0), 4, 1):
+        oc1 = oracle.prefill(og, kb[b:b + 1, h:h + 1].copy(), vb[b:b + 1, h:h + 1].copy())
+        _check_unit_cache(gc, oc1, b, h)
+        _check_unit_attention(out_np, oc1, qb, b, h, w.q_per_kv, scale)
+
+
+@pytest.mark.parametrize("name,steps,check_every", [("llama2-7b-mha-4k", 128, 16),
+                                                    ("llama3-8b-gqa-32k-4bit", 1024, 128)])
+def test_streaming_decode_full_size(name, steps, check_every):
+    w = synth.WORKLOADS[name]
+    print(f"workload {name} steps {steps}", flush=True)
+    k, v = synth.prefill_kv(w, 21)
+    T = 32 * math.ceil((w.seq_len - 128 + steps + 32) / 32)
+    g = kivi.Geom(w.batch, w.kv_heads, w.q_per_kv, bits=w.bits, max_tokens=T)
+    gc = kivi.Cache(g)
+    kivi.quantize_prefill(g, gc, k.cuda(), v.cuda())
+    units = _sample_units(w, 3, 2)
+    og = _unit_geoms(w, T)
+    kb, vb = synth.bits_u16(k), synth.bits_u16(v)
+    ocs = {(b, h): oracle.prefill(og, kb[b:b + 1, h:h + 1].copy(), vb[b:b + 1, h:h + 1].copy())
+           for b, h in units}
+    del k, v, kb, vb
+    ws = kivi.Workspace(g)
+    out = torch.empty(w.batch, w.q_heads, 128, device="cuda")
+    scale = 1.0 / math.sqrt(128)
+    flushes = 0
+    for step in range(steps):
+        kn, vn = synth.new_token(w, 21, 0, step)
+        kivi.append_token(g, gc, kn.cuda(), vn.cuda())
+        f = kivi.flush_residual(g, gc)
+        flushes += f
+        knb, vnb = synth.bits_u16(kn), synth.bits_u16(vn)
+        for (b, h), oc1 in ocs.items():
+            oracle.append(oc1, knb[b:b + 1, h:h + 1].copy(), vnb[b:b + 1, h:h + 1].copy())
+            assert oracle.flush(oc1) == f
+        if step % check_every == check_every - 1 or step == steps - 1:
+            q = synth.query(w, 21, 0, step)
+            out.fill_(float("nan"))
+            kivi.decode_attention(g, gc, q.cuda(), out=out, ws=ws)
+            torch.cuda.synchronize()
+            out_np, qb = to_np(out), synth.bits_u16(q)
+            assert np.isfinite(out_np).all()
+            for (b, h), oc1 in ocs.items():
+                _check_unit_attention(out_np, oc1, qb, b, h, w.q_per_kv, scale)
+            print(f"step {step}: n_q {gc.n_q} n_res {gc.n_res} ok", flush=True)
+    assert flushes == steps // 32
+    torch.cuda.synchronize()
+    for (b, h), oc1 in ocs.items():
+        _check_unit_cache(gc, oc1, b, h)
