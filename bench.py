@@ -139,6 +139,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-steps", type=int, default=0,
                     help="run only N decode steps after warmup, no reporting (profilers)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy 5 times (scales HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported on this build "
@@ -150,9 +152,18 @@ def main():
     import synth
     from decode_attention_channel_amd import kivi
 
+    torch.cuda.set_device(0)
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": src.numel() * 4, "copy_bytes_written": dst.numel() * 4,
+                          "launches": 5}))
+        return
     w = synth.WORKLOADS[args.workload]
     layers = args.layers or w.layers
-    torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
     D, G, R = w.head_dim, w.group, w.residual
     total_steps = args.warmup + (args.profile_steps or args.steps)

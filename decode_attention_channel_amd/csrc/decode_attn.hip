@@ -500,6 +500,7 @@ __device__ __forceinline__ void load_group(GroupRaw<BITS> &r, const UnitView &v,
 template <int NHB>
 struct MfmaSmem {
   uint4 bq[4][NHB][2][4][4][4];   // [wave][head block][hi/lo][head][step][lane group]
+  uint16_t vres[4][G][D];          // [wave] one residual chunk of V rows (bf16)
 };
 
 // Online-softmax state of one wave (per head block): P.V accumulators in the
@@ -613,27 +614,141 @@ __device__ __forceinline__ void mfma_group(const GroupRaw<BITS> &cur, WaveState<
   }
 }
 
+// One residual chunk (32 ring slots, `valid` of them live) through the same
+// MFMA pipeline as a quantised group: q.K^T with the bf16 K rows as the A
+// operand and the raw query as B (hi columns; lo columns zero; the softmax
+// scale applied to the scores); P.V with the chunk's V rows transposed
+// through LDS as the A operand and p (hi/lo) as B for every channel block.
+template <int NHB>
+__device__ __forceinline__ void mfma_rchunk(const DecodeArgs &a, int u, int rc,
+                                            WaveState<NHB> &st, MfmaSmem<NHB> &smf, int wave,
+                                            int lane, int n, int gq) {
+  const int qpk = a.qpk;
+  const int t0 = G * rc, valid = min(G, a.n_res - t0);
+  const int slot0 = (a.res_start + t0) % a.slots;   // multiple of G: the chunk is contiguous
+  const long long ring = (long long)u * a.slots + slot0;
+  const uint16_t *krows = a.k_res + ring * D, *vrows = a.v_res + ring * D;
+
+  // stage V rows in LDS: lane -> (row lane/2, 64 channels); rows past `valid`
+  // (stale or never written slots) become zeros
+  {
+    const int row = lane >> 1, c0 = 64 * (lane & 1);
+    uint4 *dst = reinterpret_cast<uint4 *>(&smf.vres[wave][row][c0]);
+    const uint4 *src = reinterpret_cast<const uint4 *>(vrows + (long long)row * D + c0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dst[i] = row < valid ? src[i] : make_uint4(0u, 0u, 0u, 0u);
+  }
+  // A operands of q.K^T: K rows of the two tiles, natural channel order
+  const int kr0 = 8 * (n >> 2) + (n & 3);
+  Op8 ak[2][4];
+#pragma unroll
+  for (int tile = 0; tile < 2; ++tile) {
+    const uint4 *kp = reinterpret_cast<const uint4 *>(krows + (long long)(kr0 + 4 * tile) * D + 32 * gq);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const uint4 x = kp[m];
+      ak[tile][m].u[0] = x.x; ak[tile][m].u[1] = x.y; ak[tile][m].u[2] = x.z; ak[tile][m].u[3] = x.w;
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  // A operands of P.V: row i of M-tile mt = channel 8i + mt, k-slot s = token 8gq + s
+  Op8 av[8];
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) {
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2) {
+      const uint32_t lo = smf.vres[wave][8 * gq + 2 * s2][8 * n + mt];
+      const uint32_t hi = smf.vres[wave][8 * gq + 2 * s2 + 1][8 * n + mt];
+      av[mt].u[s2] = lo | (hi << 16);
+    }
+  }
+  const int b = u / a.kv_heads, h = u % a.kv_heads;
+#pragma unroll
+  for (int hb = 0; hb < NHB; ++hb) {
+    const int hh = hb * 4 + (n & 3);
+    const bool hi_col = (n & 4) == 0 && hh < qpk;
+    const uint4 *qp = reinterpret_cast<const uint4 *>(
+        a.q + ((long long)b * a.kv_heads * qpk + (long long)h * qpk + (hi_col ? hh : 0)) * D + 32 * gq);
+    f32x4_t sc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      Op8 bq;
+      const uint4 x = hi_col ? qp[m] : make_uint4(0u, 0u, 0u, 0u);
+      bq.u[0] = x.x; bq.u[1] = x.y; bq.u[2] = x.z; bq.u[3] = x.w;
+#pragma unroll
+      for (int tile = 0; tile < 2; ++tile)
+        sc[tile] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak[tile][m].v, bq.v, sc[tile], 0, 0, 0);
+    }
+    float s8[8];
+#pragma unroll
+    for (int tile = 0; tile < 2; ++tile)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float x = (sc[tile][r] + dpp_ror4(sc[tile][r])) * a.qscale;
+        s8[4 * tile + r] = 8 * gq + 4 * tile + r < valid ? x : kNegInf;
+      }
+    float mx = fmaxf(fmaxf(fmaxf(s8[0], s8[1]), fmaxf(s8[2], s8[3])),
+                     fmaxf(fmaxf(s8[4], s8[5]), fmaxf(s8[6], s8[7])));
+    mx = max_x32(max_x16(mx));
+    const bool need = mx > st.m_run[hb] + kRescaleSlack;
+    if (__any(need)) {
+      const float mnew = need ? mx : st.m_run[hb];
+      const float al = st.m_run[hb] == kNegInf ? 0.f : fast_exp2(st.m_run[hb] - mnew);
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) st.acc[hb][mt] *= al;
+      st.l_run[hb] *= al;
+      st.z_run[hb] *= al;
+      st.m_run[hb] = mnew;
+    }
+    float p[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      p[k] = fast_exp2(s8[k] - st.m_run[hb]);
+      st.l_run[hb] += p[k];
+    }
+    Op8 bh, bl;
+#pragma unroll
+    for (int k = 0; k < 8; k += 2) split_bf16(p[k], p[k + 1], bh.u[k / 2], bl.u[k / 2]);
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+      st.acc[hb][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mt].v, bh.v, st.acc[hb][mt], 0, 0, 0);
+      st.acc[hb][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mt].v, bl.v, st.acc[hb][mt], 0, 0, 0);
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+}
+
+// GQA decode attention.  Grid (wpu, unit): the `wpu` workgroups of a unit
+// split its work -- the quantised groups, then the residual in chunks of 32
+// tokens -- into equal byte shares, and each workgroup splits its share over
+// its 4 waves.  Item costs are in KiB: a group (codes + scale/zero) is
+// bits + 2, a residual chunk (32 bf16 K and V rows) is 16.
 template <int BITS, int NHB>
-__global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeArgs a) {
   constexpr int HMAX = 4 * NHB;
+  constexpr int CQ = BITS + 2, CR = 16;
   __shared__ __align__(16) union {
     MfmaSmem<NHB> mf;
     MergeSmem<HMAX> mg;
-    ResidSmem<HMAX> rs;
   } sm;
 
   const int split = blockIdx.x, u = blockIdx.y;
-  if (split >= a.n_split_q) {
-    residual_split<HMAX>(sm.rs, a, u, split);
-    finish_unit(a, u, &sm.rs.last);
-    return;
-  }
   // wave index made visibly wave-uniform so that group offsets live in SGPRs
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int n = lane & 15, gq = lane >> 4;          // MFMA column / row, lane group
   const int ch = lane & 3, cm = (lane >> 2) & 3;    // cooperative q' role: head, step
   const int qpk = a.qpk;
   const int b = u / a.kv_heads, h = u % a.kv_heads;
+
+  // this wave's byte share of the unit, and the items that start inside it
+  const int n_rc = (a.n_res + G - 1) / G;
+  const long long q0 = (long long)a.n_groups * CQ, total = q0 + (long long)n_rc * CR;
+  const long long wg_lo = total * split / a.n_split, wg_hi = total * (split + 1) / a.n_split;
+  const long long lo = wg_lo + (wg_hi - wg_lo) * wave / 4, hi = wg_lo + (wg_hi - wg_lo) * (wave + 1) / 4;
+  const int g_begin = (int)min((lo + CQ - 1) / CQ, (long long)a.n_groups);
+  const int g_end = (int)min((hi + CQ - 1) / CQ, (long long)a.n_groups);
+  const int r_begin = (int)min(max(lo - q0 + CR - 1, 0ll) / CR, (long long)n_rc);
+  const int r_end = (int)min(max(hi - q0 + CR - 1, 0ll) / CR, (long long)n_rc);
 
   // scaled query values in slot order for the cooperative role
   float qv[NHB][8];
@@ -666,27 +781,27 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     st.m_run[hb] = kNegInf; st.l_run[hb] = 0.f; st.z_run[hb] = 0.f;
   }
 
-  const int g_begin = split * a.gps;
-  const int g_end = min(g_begin + a.gps, a.n_groups);
-  const UnitView view = make_view<BITS>(a, u, n, gq, cm);
-
-  // software pipeline, two register sets used in turn: the next group of this
-  // wave is in flight while the current one is computed
-  GroupRaw<BITS> r0, r1;
-  int g = g_begin + wave;
-  if (g < g_end) load_group<BITS>(r0, view, g);
-  while (g < g_end) {
-    if (g + 4 < g_end) load_group<BITS>(r1, view, g + 4);
-    mfma_group<BITS, NHB>(r0, st, sm.mf, qv, wave, n, gq, ch, cm);
-    g += 4;
-    if (g >= g_end) break;
-    if (g + 4 < g_end) load_group<BITS>(r0, view, g + 4);
-    mfma_group<BITS, NHB>(r1, st, sm.mf, qv, wave, n, gq, ch, cm);
-    g += 4;
+  // quantised groups: software pipeline over two register sets, the next
+  // group in flight while the current one is computed
+  if (g_begin < g_end) {
+    const UnitView view = make_view<BITS>(a, u, n, gq, cm);
+    GroupRaw<BITS> r0, r1;
+    int g = g_begin;
+    load_group<BITS>(r0, view, g);
+    while (g < g_end) {
+      if (g + 1 < g_end) load_group<BITS>(r1, view, g + 1);
+      mfma_group<BITS, NHB>(r0, st, sm.mf, qv, wave, n, gq, ch, cm);
+      if (++g >= g_end) break;
+      if (g + 1 < g_end) load_group<BITS>(r0, view, g + 1);
+      mfma_group<BITS, NHB>(r1, st, sm.mf, qv, wave, n, gq, ch, cm);
+      ++g;
+    }
   }
+  // residual chunks
+  for (int rc = r_begin; rc < r_end; ++rc) mfma_rchunk<NHB>(a, u, rc, st, sm.mf, wave, lane, n, gq);
 
   // ---- per-wave totals, then the workgroup merge (the merge buffer aliases
-  // the q' staging of the other waves: wait until every wave left the loop)
+  // the staging areas of the other waves: wait until every wave is done)
   __syncthreads();
   const int jv = n >> 2, hv = n & 3;
 #pragma unroll
@@ -925,21 +1040,90 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
 
 }  // namespace
 
-hipError_t launch_decode(int bits, const DecodeArgs &a, hipStream_t s) {
-  const dim3 grid(a.n_split, a.n_units), block(256);
-  const int nhb = (a.qpk + 3) / 4;
-#define KIVI_LAUNCH(BITS)                                                                 \
-  do {                                                                                    \
-    if (a.qpk == 1)                                                                       \
-      hipLaunchKernelGGL((decode_valu_kernel<BITS>), grid, block, 0, s, a);               \
-    else if (nhb == 1)                                                                    \
-      hipLaunchKernelGGL((decode_mfma_kernel<BITS, 1>), grid, block, 0, s, a);            \
-    else if (nhb == 2)                                                                    \
-      hipLaunchKernelGGL((decode_mfma_kernel<BITS, 2>), grid, block, 0, s, a);            \
-    else if (nhb == 3)                                                                    \
-      hipLaunchKernelGGL((decode_mfma_kernel<BITS, 3>), grid, block, 0, s, a);            \
-    else                                                                                  \
-      hipLaunchKernelGGL((decode_mfma_kernel<BITS, 4>), grid, block, 0, s, a);            \
+namespace {
+
+template <int BITS, int NHB>
+void *gqa_kernel() {
+  return reinterpret_cast<void *>(&decode_gqa_kernel<BITS, NHB>);
+}
+
+// Resident workgroups of a GQA kernel variant on the current device
+// (occupancy x compute units), cached per device and variant.
+int resident_slots(int bits, int nhb) {
+  static int cache[16][2][4];   // 0 = not yet queried
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  const int d = dev & 15, bi = bits == 4 ? 1 : 0;
+  int v = __atomic_load_n(&cache[d][bi][nhb - 1], __ATOMIC_RELAXED);
+  if (v > 0) return v;
+  void *fn = nullptr;
+  switch ((bi << 2) | (nhb - 1)) {
+    case 0: fn = gqa_kernel<2, 1>(); break;
+    case 1: fn = gqa_kernel<2, 2>(); break;
+    case 2: fn = gqa_kernel<2, 3>(); break;
+    case 3: fn = gqa_kernel<2, 4>(); break;
+    case 4: fn = gqa_kernel<4, 1>(); break;
+    case 5: fn = gqa_kernel<4, 2>(); break;
+    case 6: fn = gqa_kernel<4, 3>(); break;
+    default: fn = gqa_kernel<4, 4>(); break;
+  }
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 256, 0) != hipSuccess || per_cu < 1)
+    per_cu = 1;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    cus = 256;
+  v = per_cu * cus;
+  __atomic_store_n(&cache[d][bi][nhb - 1], v, __ATOMIC_RELAXED);
+  return v;
+}
+
+// Workgroups per unit: the count that minimises (rounds of resident
+// workgroups) / (workgroups per unit), i.e. the finishing time of equal
+// shares, with at least two groups' worth of bytes per wave and no more
+// partials than the workspace holds.
+int choose_wpu(int bits, const DecodeArgs &a, int slots) {
+  const long long n_rc = (a.n_res + G - 1) / G;
+  const long long total = (long long)a.n_groups * (bits + 2) + n_rc * 16;
+  long long cap = total / (4 * 2 * (bits + 2));
+  if (cap < 1) cap = 1;
+  if (cap > a.n_split) cap = a.n_split;   // workspace capacity in partials per unit
+  if (cap > 256) cap = 256;
+  int best = 1;
+  double best_t = 1e30;
+  for (int w = 1; w <= cap; ++w) {
+    const long long rounds = ((long long)a.n_units * w + slots - 1) / slots;
+    const double t = (double)rounds / w;
+    if (t < best_t * 0.999) { best_t = t; best = w; }
+  }
+  return best;
+}
+
+}  // namespace
+
+hipError_t launch_decode(int bits, const DecodeArgs &a_in, hipStream_t s) {
+  const dim3 block(256);
+  if (a_in.qpk == 1) {
+    const dim3 grid(a_in.n_split, a_in.n_units);
+    if (bits == 2)
+      hipLaunchKernelGGL((decode_valu_kernel<2>), grid, block, 0, s, a_in);
+    else
+      hipLaunchKernelGGL((decode_valu_kernel<4>), grid, block, 0, s, a_in);
+    return hipGetLastError();
+  }
+  const int nhb = (a_in.qpk + 3) / 4;
+  DecodeArgs a = a_in;
+  a.n_split = choose_wpu(bits, a_in, resident_slots(bits, nhb));   // a_in.n_split: capacity
+  const dim3 grid(a.n_split, a.n_units);
+#define KIVI_LAUNCH(BITS)                                                                   \
+  do {                                                                                      \
+    if (nhb == 1)                                                                           \
+      hipLaunchKernelGGL((decode_gqa_kernel<BITS, 1>), grid, block, 0, s, a);              \
+    else if (nhb == 2)                                                                      \
+      hipLaunchKernelGGL((decode_gqa_kernel<BITS, 2>), grid, block, 0, s, a);              \
+    else if (nhb == 3)                                                                      \
+      hipLaunchKernelGGL((decode_gqa_kernel<BITS, 3>), grid, block, 0, s, a);              \
+    else                                                                                    \
+      hipLaunchKernelGGL((decode_gqa_kernel<BITS, 4>), grid, block, 0, s, a);              \
   } while (0)
   if (bits == 2)
     KIVI_LAUNCH(2);

@@ -253,10 +253,16 @@ kivi_status kivi_decode_attention(const kivi_geom *g, const kivi_cache *c, const
   a.n_units = (int)units_of(g);
   a.n_groups = c->n_q / g->group;
   a.n_res = c->n_res; a.res_start = c->res_start;
-  a.gps = choose_gps(units_of(g), a.n_groups);
-  a.n_split_q = (a.n_groups + a.gps - 1) / a.gps;
-  a.n_split = a.n_split_q + (c->n_res > 0 ? 1 : 0);
-  if (a.n_split > max_splits(g)) return KIVI_E_WORKSPACE;   // cannot happen: gps >= 4
+  if (g->q_per_kv == 1) {
+    // MHA: fixed-size splits of the quantised groups plus one residual split
+    a.gps = choose_gps(units_of(g), a.n_groups);
+    a.n_split_q = (a.n_groups + a.gps - 1) / a.gps;
+    a.n_split = a.n_split_q + (c->n_res > 0 ? 1 : 0);
+    if (a.n_split > max_splits(g)) return KIVI_E_WORKSPACE;   // cannot happen: gps >= 4
+  } else {
+    // GQA: the launcher picks the workgroups per unit; pass the capacity
+    a.n_split = max_splits(g);
+  }
   return hip_status(kivi::launch_decode(g->bits, a, (hipStream_t)stream));
 }
 
