@@ -435,14 +435,14 @@ template <int BITS>
 struct GroupRaw {
   uint32_t kw[2][BITS];   // per tile: 32 channels of one token
   uint32_t vw[2 * BITS];  // 8 channels x 8 tokens
-  float sk[8], zk[8], sv[8], zv[8];
+  uint32_t mw[4][2];      // this lane's 8 bytes of each of k_scale, k_zero, v_scale, v_zero
 };
 
 // Per-unit buffer views and the lane-constant byte offsets of one lane; the
 // group enters only through scalar offsets (g * bytes per group).
 struct UnitView {
   __amdgpu_buffer_rsrc_t kc, vc, ks, kz, vs, vz;
-  uint32_t o_k0, o_k1, o_v, o_km, o_vm;
+  uint32_t o_k0, o_k1, o_v, o_mu;
 };
 
 template <int BITS>
@@ -462,8 +462,7 @@ __device__ __forceinline__ UnitView make_view(const DecodeArgs &a, int u, int n,
   v.o_k0 = kr0 * KROW + gq * CB;
   v.o_k1 = (kr0 + 4) * KROW + gq * CB;
   v.o_v = (gq * D + 8 * n) * BITS;
-  v.o_km = (32 * gq + 8 * cm) * 4;
-  v.o_vm = ((n >> 2) * G + 8 * gq) * 4;
+  v.o_mu = (16 * gq + n) * 8;   // = 8 * lane
   return v;
 }
 
@@ -491,17 +490,32 @@ __device__ __forceinline__ void load_group(GroupRaw<BITS> &r, const UnitView &v,
       r.vw[i] = c[i]; r.vw[4 + i] = d[i];
     }
   }
-  buf8f(v.ks, v.o_km, sm, r.sk);
-  buf8f(v.kz, v.o_km, sm, r.zk);
-  buf8f(v.vs, v.o_vm, sm, r.sv);
-  buf8f(v.vz, v.o_vm, sm, r.zv);
+  // scale/zero: each lane loads 8 unique bytes of each 512-byte array; the
+  // values every role needs are re-read from LDS (mfma_group)
+  const __amdgpu_buffer_rsrc_t mr[4] = {v.ks, v.kz, v.vs, v.vz};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const u32x2_t x = __builtin_amdgcn_raw_buffer_load_b64(mr[i], v.o_mu, sm, 0);
+    r.mw[i][0] = x[0];
+    r.mw[i][1] = x[1];
+  }
 }
 
 template <int NHB>
 struct MfmaSmem {
-  uint4 bq[4][NHB][2][4][4][4];   // [wave][head block][hi/lo][head][step][lane group]
+  // q' operand chunks (8 bf16) per wave and head block, indexed by bq_index
+  uint4 bq[4][NHB][128];
+  float meta[4][4][D];             // [wave] the current group's k_scale, k_zero, v_scale, v_zero
   uint16_t vres[4][G][D];          // [wave] one residual chunk of V rows (bf16)
 };
+
+// LDS chunk of the q' operand for (hi/lo xx, head h, MFMA step m, lane group
+// gq).  The low 3 bits pick the 16-byte bank group; (xx + h + 2gq) mod 8
+// spreads both the stores (one xx at a time) and the loads (one m at a time)
+// evenly over the 8 bank groups.
+__device__ __forceinline__ int bq_index(int xx, int h, int m, int gq) {
+  return (m * 4 + h) * 8 + ((xx + h + 2 * gq) & 7);
+}
 
 // Online-softmax state of one wave (per head block): P.V accumulators in the
 // MFMA output layout, running max (log2 units), and per-lane partial sums of
@@ -513,9 +527,32 @@ struct WaveState {
 };
 
 template <int BITS, int NHB>
-__device__ __forceinline__ void mfma_group(const GroupRaw<BITS> &cur, WaveState<NHB> &st,
+__device__ __forceinline__ void mfma_group(const GroupRaw<BITS> &raw, WaveState<NHB> &st,
                                            MfmaSmem<NHB> &smf, const float (&qv)[NHB][8],
                                            int wave, int n, int gq, int ch, int cm) {
+  // scale/zero of this group: stage in LDS, read back what each role needs
+  {
+    const int lane = 16 * gq + n;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<uint2 *>(&smf.meta[wave][i][2 * lane]) = make_uint2(raw.mw[i][0], raw.mw[i][1]);
+  }
+  __builtin_amdgcn_wave_barrier();
+  struct {
+    const uint32_t (&kw)[2][BITS];
+    const uint32_t (&vw)[2 * BITS];
+    float sk[8], zk[8], sv[8], zv[8];
+  } cur{raw.kw, raw.vw, {}, {}, {}, {}};
+  {
+    const float *km = &smf.meta[wave][0][32 * gq + 8 * cm];
+    const float *kz = &smf.meta[wave][1][32 * gq + 8 * cm];
+    const float *vm = &smf.meta[wave][2][(n >> 2) * G + 8 * gq];
+    const float *vz = &smf.meta[wave][3][(n >> 2) * G + 8 * gq];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      cur.sk[i] = km[i]; cur.zk[i] = kz[i]; cur.sv[i] = vm[i]; cur.zv[i] = vz[i];
+    }
+  }
   // ---- A operands (exact codes)
   Op8 ak[2][4];
 #pragma unroll
@@ -550,8 +587,8 @@ __device__ __forceinline__ void mfma_group(const GroupRaw<BITS> &cur, WaveState<
         beta += qv[hb][s] * cur.zk[P8[s]];
         beta += qv[hb][s + 1] * cur.zk[P8[s + 1]];
       }
-      smf.bq[wave][hb][0][ch][cm][gq] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-      smf.bq[wave][hb][1][ch][cm][gq] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+      smf.bq[wave][hb][bq_index(0, ch, cm, gq)] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+      smf.bq[wave][hb][bq_index(1, ch, cm, gq)] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
     }
     // every lane with (lane & 3) == head gets beta[head]
     beta = sum_x32(sum_x16(sum_row_stride4(beta)));
@@ -566,7 +603,7 @@ __device__ __forceinline__ void mfma_group(const GroupRaw<BITS> &cur, WaveState<
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       Op8 bq;
-      const uint4 x = smf.bq[wave][hb][(n >> 2) & 1][n & 3][m][gq];
+      const uint4 x = smf.bq[wave][hb][bq_index((n >> 2) & 1, n & 3, m, gq)];
       bq.u[0] = x.x; bq.u[1] = x.y; bq.u[2] = x.z; bq.u[3] = x.w;
 #pragma unroll
       for (int tile = 0; tile < 2; ++tile)
@@ -781,20 +818,24 @@ __global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeArgs a) {
     st.m_run[hb] = kNegInf; st.l_run[hb] = 0.f; st.z_run[hb] = 0.f;
   }
 
-  // quantised groups: software pipeline over two register sets, the next
-  // group in flight while the current one is computed
+  // quantised groups: software pipeline over three register sets, the next
+  // two groups in flight while the current one is computed
   if (g_begin < g_end) {
     const UnitView view = make_view<BITS>(a, u, n, gq, cm);
-    GroupRaw<BITS> r0, r1;
+    GroupRaw<BITS> r0, r1, r2;
     int g = g_begin;
     load_group<BITS>(r0, view, g);
-    while (g < g_end) {
-      if (g + 1 < g_end) load_group<BITS>(r1, view, g + 1);
+    if (g + 1 < g_end) load_group<BITS>(r1, view, g + 1);
+    while (true) {
+      if (g + 2 < g_end) load_group<BITS>(r2, view, g + 2);
       mfma_group<BITS, NHB>(r0, st, sm.mf, qv, wave, n, gq, ch, cm);
       if (++g >= g_end) break;
-      if (g + 1 < g_end) load_group<BITS>(r0, view, g + 1);
+      if (g + 2 < g_end) load_group<BITS>(r0, view, g + 2);
       mfma_group<BITS, NHB>(r1, st, sm.mf, qv, wave, n, gq, ch, cm);
-      ++g;
+      if (++g >= g_end) break;
+      if (g + 2 < g_end) load_group<BITS>(r1, view, g + 2);
+      mfma_group<BITS, NHB>(r2, st, sm.mf, qv, wave, n, gq, ch, cm);
+      if (++g >= g_end) break;
     }
   }
   // residual chunks
