@@ -203,18 +203,13 @@ def main():
     steppers = [kivi.LayerStepper(geom, caches[layer], ws, qs[layer], outs[layer])
                 for layer in range(layers)]
 
-    def step(i, events=None, bytes_acc=None):
+    def step(i):
         for layer in range(layers):
             st = steppers[layer]
             kn, vn = new_tok[i][layer]
             st.append(kn, vn)
             st.flush()
-            if events is not None:
-                bytes_acc.append(attn_bytes(w, st.cache.n_q, st.cache.n_res))
-                events[layer][0].record()
             st.attend()
-            if events is not None:
-                events[layer][1].record()
 
     for i in range(args.warmup):
         step(i)
@@ -226,34 +221,38 @@ def main():
         print(json.dumps({"profile_steps": args.profile_steps}))
         return
 
-    # step timing: no per-kernel events
+    # step timing: exactly `steps` decode steps of all layers
     n_timed = args.steps
-    half = n_timed // 2
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.warmup, args.warmup + half):
+    for i in range(args.warmup, args.warmup + n_timed):
         step(i)
     torch.cuda.synchronize()
     t_steps = time.perf_counter() - t0
-    # kernel timing: HIP events around every decode-attention launch, on the
-    # stream the library launches on; the GPU is held first so that the host
-    # enqueues far ahead and no launch waits for the host.
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(layers)] for _ in range(n_timed - half)]
-    bytes_acc = []
-    torch.cuda._sleep(200_000_000)
-    t1 = time.perf_counter()
-    for k_i, i in enumerate(range(args.warmup + half, args.warmup + n_timed)):
-        step(i, ev[k_i], bytes_acc)
+
+    # kernel timing: the layers' decode-attention launches back to back on the
+    # final cache state, HIP events around each sweep on the stream the library
+    # launches on; the GPU is held first so that the host enqueues ahead and
+    # no launch waits for the host
+    bytes_per_launch = [attn_bytes(w, st.cache.n_q, st.cache.n_res) for st in steppers]
+    sweeps = 20
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(sweeps)]
     torch.cuda.synchronize()
-    t_steps2 = time.perf_counter() - t1
-    kern_ms = [a.elapsed_time(b) for row in ev for (a, b) in row]
-    avg_kern_s = sum(kern_ms) / len(kern_ms) / 1e3
-    avg_bytes = sum(bytes_acc) / len(bytes_acc)
+    torch.cuda._sleep(100_000_000)
+    for e0, e1 in ev:
+        e0.record()
+        for st in steppers:
+            st.attend()
+        e1.record()
+    torch.cuda.synchronize()
+    sweep_ms = [a.elapsed_time(b) for a, b in ev]
+    avg_kern_s = sum(sweep_ms) / len(sweep_ms) / layers / 1e3
+    avg_bytes = sum(bytes_per_launch) / len(bytes_per_launch)
     achieved = avg_bytes / avg_kern_s / 1e9
 
-    ms_per_step = t_steps / half * 1e3
-    tokens_s = w.batch / (t_steps / half)
+    ms_per_step = t_steps / n_timed * 1e3
+    tokens_s = w.batch / (t_steps / n_timed)
     res = {
         "metric": METRIC, "value": tokens_s, "unit": "tokens/s", "n_gpus": 1,
         "steps": n_timed, "warmup": args.warmup, "ms_per_step": ms_per_step,
@@ -264,12 +263,12 @@ def main():
                    "group": G, "residual": R, "layers": layers,
                    "step": "per layer: append + flush-if-full + decode attention"},
         "attn_hbm_gbps": achieved,
+        "attn_bytes_per_launch": avg_bytes,
         "attn_kernel_us": avg_kern_s * 1e6,
         "attn_tokens_s_kernel_only": w.batch / (avg_kern_s * layers),
         "quantize_gelem_s": quant_gelem_s,
         "quantize_hbm_gbps": pre_gbps,
         "quantize_prefill_ms_per_layer": pre_t / layers * 1e3,
-        "ms_per_step_with_events": t_steps2 / (n_timed - half) * 1e3,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": read_traffic("decode_attn_llama3-8b-gqa-8k")},
