@@ -7,13 +7,16 @@ Workload (Llama-3-8B GQA geometry of the catalog record kivi-2bit-llama3-8b-gqa-
 * prefill leg: every layer's 8192-token K/V is quantised into its own cache
   (per-layer launch timed with HIP events; reported as quantise Gelem/s and
   HBM GB/s);
-* decode leg (the timed "step"): for each of the 32 layers, append one token
-  per sequence, flush a group when the residual is full, and run decode
-  attention over the whole mixed cache.  value = generated tokens/s
-  (batch / step time).  The 32 layer caches (4.5 GB) rotate, so the 256 MB
-  MALL cannot serve them;
-* roofline of the dominant kernel (decode attention, one launch per layer):
-  algorithmic bytes per launch / its HIP-event duration, against 8 TB/s;
+* decode leg (the timed "step"): for each of the 32 layers, one
+  kivi_decode_step call -- append one token per sequence, flush a group when
+  the residual is full, and decode attention over the whole mixed cache, in
+  one launch (two on flush steps).  value = generated tokens/s (batch / step
+  time).  The same number of steps is then timed with the three separate
+  calls (append, flush, attend) for comparison.  The 32 layer caches (4.5 GB)
+  rotate, so the 256 MB MALL cannot serve them;
+* roofline of the dominant kernel (decode attention with the fused append,
+  one launch per layer): algorithmic bytes per launch / its duration from HIP
+  event pairs around each launch of 10 further decode steps, against 8 TB/s;
 * cpu_baseline: the CPU oracle (plain C) on a bounded sample of the same
   workload (two layers' worth of (sequence, kv head) units), threads over units.
 
@@ -36,11 +39,13 @@ HBM_PEAK_GBPS = 8000.0
 METRIC = "KIVI decode-attention achieved HBM GB/s + tokens/sec; quantize Gelem/s"
 
 
-def attn_bytes(w, n_q, n_res):
+def attn_bytes(w, n_q, n_res, fused_append=False):
     """Algorithmic bytes of one decode-attention launch: the packed history
-    (codes + fp32 scale/zero), the bf16 residual, q (bf16) and out (fp32)."""
+    (codes + fp32 scale/zero), the bf16 residual (the appended token included,
+    read from its input in a fused step), q (bf16) and out (fp32); a fused
+    step also writes the appended K and V rows into the ring."""
     D, G, b = w.head_dim, w.group, w.bits
-    per_unit = n_q * (2 * D * b / 8 + 16 * D / G) + n_res * 4 * D
+    per_unit = n_q * (2 * D * b / 8 + 16 * D / G) + n_res * 4 * D + (4 * D if fused_append else 0)
     return w.batch * w.kv_heads * per_unit + w.batch * w.q_heads * D * (2 + 4)
 
 
@@ -166,7 +171,8 @@ def main():
     layers = args.layers or w.layers
     dev = torch.device("cuda", 0)
     D, G, R = w.head_dim, w.group, w.residual
-    total_steps = args.warmup + (args.profile_steps or args.steps)
+    kernel_steps = 10   # extra fused steps with HIP events around every launch
+    total_steps = args.warmup + (args.profile_steps or 2 * args.steps + kernel_steps + 1)
     max_tokens = G * math.ceil((w.seq_len - R + total_steps + G) / G)
     geom = kivi.Geom(w.batch, w.kv_heads, w.q_per_kv, bits=w.bits, max_tokens=max_tokens)
 
@@ -205,6 +211,11 @@ def main():
 
     def step(i):
         for layer in range(layers):
+            kn, vn = new_tok[i][layer]
+            steppers[layer].step(kn, vn)
+
+    def step_separate(i):
+        for layer in range(layers):
             st = steppers[layer]
             kn, vn = new_tok[i][layer]
             st.append(kn, vn)
@@ -229,26 +240,44 @@ def main():
         step(i)
     torch.cuda.synchronize()
     t_steps = time.perf_counter() - t0
+    # the same number of steps through the three separate calls
+    t0 = time.perf_counter()
+    for i in range(args.warmup + n_timed, args.warmup + 2 * n_timed):
+        step_separate(i)
+    torch.cuda.synchronize()
+    t_steps_sep = time.perf_counter() - t0
 
-    # kernel timing: the layers' decode-attention launches back to back on the
-    # final cache state, HIP events around each sweep on the stream the library
-    # launches on; the GPU is held first so that the host enqueues ahead and
-    # no launch waits for the host
-    bytes_per_launch = [attn_bytes(w, st.cache.n_q, st.cache.n_res) for st in steppers]
-    sweeps = 20
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(sweeps)]
+    # kernel timing: more fused steps, with a HIP event pair around every
+    # layer's launch on the stream the library launches on; launches of steps
+    # that also flushed (two kernels) are left out of the average
+    i0 = args.warmup + 2 * n_timed + 1
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(layers)] for _ in range(kernel_steps)]
+    flushed = [[0] * layers for _ in range(kernel_steps)]
+    nbytes = [[0.0] * layers for _ in range(kernel_steps)]
     torch.cuda.synchronize()
-    torch.cuda._sleep(100_000_000)
-    for e0, e1 in ev:
-        e0.record()
-        for st in steppers:
-            st.attend()
-        e1.record()
+    # one untimed step first, so that the GPU is busy while the host enqueues
+    # the timed launches (no launch waits for the host after its start event)
+    step(i0 - 1)
+    for j in range(kernel_steps):
+        for layer in range(layers):
+            st = steppers[layer]
+            kn, vn = new_tok[i0 + j][layer]
+            e0, e1 = ev[j][layer]
+            e0.record()
+            flushed[j][layer] = st.step(kn, vn)
+            e1.record()
+            # the step attends over the cache after its append (and flush)
+            nbytes[j][layer] = attn_bytes(w, st.cache.n_q, st.cache.n_res, fused_append=True)
     torch.cuda.synchronize()
-    sweep_ms = [a.elapsed_time(b) for a, b in ev]
-    avg_kern_s = sum(sweep_ms) / len(sweep_ms) / layers / 1e3
-    avg_bytes = sum(bytes_per_launch) / len(bytes_per_launch)
+    kern_us, kern_bytes = [], []
+    for j in range(kernel_steps):
+        for layer in range(layers):
+            if not flushed[j][layer]:
+                kern_us.append(ev[j][layer][0].elapsed_time(ev[j][layer][1]) * 1e3)
+                kern_bytes.append(nbytes[j][layer])
+    avg_kern_s = sum(kern_us) / len(kern_us) / 1e6
+    avg_bytes = sum(kern_bytes) / len(kern_bytes)
     achieved = avg_bytes / avg_kern_s / 1e9
 
     ms_per_step = t_steps / n_timed * 1e3
@@ -261,17 +290,20 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "kv_heads": w.kv_heads,
                    "q_heads": w.q_heads, "head_dim": D, "context": w.seq_len, "bits": w.bits,
                    "group": G, "residual": R, "layers": layers,
-                   "step": "per layer: append + flush-if-full + decode attention"},
+                   "step": "per layer: kivi_decode_step (append + flush-if-full + decode "
+                           "attention; one launch, two on flush steps)"},
+        "ms_per_step_separate_calls": t_steps_sep / n_timed * 1e3,
         "attn_hbm_gbps": achieved,
         "attn_bytes_per_launch": avg_bytes,
         "attn_kernel_us": avg_kern_s * 1e6,
+        "attn_kernel_launches_timed": len(kern_us),
         "attn_tokens_s_kernel_only": w.batch / (avg_kern_s * layers),
         "quantize_gelem_s": quant_gelem_s,
         "quantize_hbm_gbps": pre_gbps,
         "quantize_prefill_ms_per_layer": pre_t / layers * 1e3,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": read_traffic("decode_attn_llama3-8b-gqa-8k")},
+                     "traffic": read_traffic(f"decode_attn_{w.name}")},
         "paper_context": "2.35x-3.47x decode throughput vs FP16 and 2.6x less peak memory "
                          "(Llama-2-7B, one A100 80GB; not comparable, quoted as context)",
     }

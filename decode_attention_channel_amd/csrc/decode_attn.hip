@@ -270,21 +270,32 @@ __device__ void residual_split(ResidSmem<HMAX> &sm, const DecodeArgs &a, int u, 
   for (int t0 = 0; t0 < a.n_res; t0 += kResChunk) {
     const int cn = min(kResChunk, a.n_res - t0);
     __syncthreads();   // q staged / previous chunk consumed
-    // stage V rows: cn rows x 16 chunks of 16 bytes
+    // stage V rows: cn rows x 16 chunks of 16 bytes; the appended token of a
+    // fused step comes from v_new and is stored into its ring slot here
     for (int i = tid; i < cn * (D / 8); i += 256) {
       const int r = i / (D / 8), c16 = i % (D / 8);
       const int slot = (a.res_start + t0 + r) % a.slots;
-      reinterpret_cast<uint4 *>(sm.v[r])[c16] =
-          reinterpret_cast<const uint4 *>(a.v_res + (ring + slot) * D)[c16];
+      uint4 *ring_row = reinterpret_cast<uint4 *>(a.v_res + (ring + slot) * D);
+      if (t0 + r == a.new_idx) {
+        const uint4 x = reinterpret_cast<const uint4 *>(a.v_new + (long long)u * D)[c16];
+        reinterpret_cast<uint4 *>(sm.v[r])[c16] = x;
+        ring_row[c16] = x;
+      } else {
+        reinterpret_cast<uint4 *>(sm.v[r])[c16] = ring_row[c16];
+      }
     }
     // partial scores over 32 channels
     if (tt < cn) {
       const int slot = (a.res_start + t0 + tt) % a.slots;
-      const uint4 *krow = reinterpret_cast<const uint4 *>(a.k_res + (ring + slot) * D + 32 * qt);
+      const bool is_new = t0 + tt == a.new_idx;
+      const uint4 *krow = reinterpret_cast<const uint4 *>(
+          is_new ? a.k_new + (long long)u * D + 32 * qt : a.k_res + (ring + slot) * D + 32 * qt);
+      uint4 *ring_row = reinterpret_cast<uint4 *>(a.k_res + (ring + slot) * D + 32 * qt);
       float kf[32];
 #pragma unroll
       for (int c8 = 0; c8 < 4; ++c8) {
         const uint4 kv = krow[c8];
+        if (is_new) ring_row[c8] = kv;
         const uint32_t w[4] = {kv.x, kv.y, kv.z, kv.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -666,25 +677,49 @@ __device__ __forceinline__ void mfma_rchunk(const DecodeArgs &a, int u, int rc,
   const long long ring = (long long)u * a.slots + slot0;
   const uint16_t *krows = a.k_res + ring * D, *vrows = a.v_res + ring * D;
 
+  // the appended token of a fused step, if it falls in this chunk
+  const int new_row = a.new_idx - t0;   // row within the chunk; wave-uniform
+  const bool has_new = new_row >= 0 && new_row < G;
+
   // stage V rows in LDS: lane -> (row lane/2, 64 channels); rows past `valid`
   // (stale or never written slots) become zeros
   {
     const int row = lane >> 1, c0 = 64 * (lane & 1);
+    const bool is_new = has_new && row == new_row;
     uint4 *dst = reinterpret_cast<uint4 *>(&smf.vres[wave][row][c0]);
-    const uint4 *src = reinterpret_cast<const uint4 *>(vrows + (long long)row * D + c0);
+    const uint4 *src = reinterpret_cast<const uint4 *>(
+        is_new ? a.v_new + (long long)u * D + c0 : vrows + (long long)row * D + c0);
+    uint4 x[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) dst[i] = row < valid ? src[i] : make_uint4(0u, 0u, 0u, 0u);
+    for (int i = 0; i < 8; ++i) x[i] = row < valid ? src[i] : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dst[i] = x[i];
+    if (is_new) {
+      uint4 *ring_row = reinterpret_cast<uint4 *>(a.v_res + (ring + row) * D + c0);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ring_row[i] = x[i];
+    }
   }
   // A operands of q.K^T: K rows of the two tiles, natural channel order
   const int kr0 = 8 * (n >> 2) + (n & 3);
   Op8 ak[2][4];
 #pragma unroll
   for (int tile = 0; tile < 2; ++tile) {
-    const uint4 *kp = reinterpret_cast<const uint4 *>(krows + (long long)(kr0 + 4 * tile) * D + 32 * gq);
+    const int row = kr0 + 4 * tile;
+    const bool is_new = has_new && row == new_row;
+    const uint4 *kp = reinterpret_cast<const uint4 *>(
+        is_new ? a.k_new + (long long)u * D + 32 * gq : krows + (long long)row * D + 32 * gq);
+    uint4 x[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) x[m] = kp[m];
+    if (is_new) {
+      uint4 *ring_row = reinterpret_cast<uint4 *>(a.k_res + (ring + row) * D + 32 * gq);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) ring_row[m] = x[m];
+    }
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      const uint4 x = kp[m];
-      ak[tile][m].u[0] = x.x; ak[tile][m].u[1] = x.y; ak[tile][m].u[2] = x.z; ak[tile][m].u[3] = x.w;
+      ak[tile][m].u[0] = x[m].x; ak[tile][m].u[1] = x[m].y; ak[tile][m].u[2] = x[m].z; ak[tile][m].u[3] = x[m].w;
     }
   }
   __builtin_amdgcn_wave_barrier();

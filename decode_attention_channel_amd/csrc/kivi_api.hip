@@ -87,6 +87,94 @@ int choose_gps(long long units, int n_groups) {
   return (int)gps;
 }
 
+// Quantise the G oldest residual tokens (ring slots res_start..+G-1, which
+// are contiguous because res_start is a multiple of G) into group n_q/G and
+// advance the counters.  The caller has validated everything.
+kivi_status enqueue_flush(const kivi_geom *g, kivi_cache *c, hipStream_t s) {
+  const int G = g->group, slots = g->residual + G;
+  kivi::QuantizeArgs a{};
+  a.src_k = c->k_res; a.src_v = c->v_res;
+  a.src_unit_stride = (long long)slots * g->head_dim;
+  a.src_tok0 = c->res_start;
+  a.n_groups = 1; a.n_units = (int)units_of(g); a.dst_g0 = c->n_q / G;
+  a.max_tokens = g->max_tokens; a.n_groups_cap = g->max_tokens / G;
+  a.k_codes = c->k_codes; a.k_scale = c->k_scale; a.k_zero = c->k_zero;
+  a.v_codes = c->v_codes; a.v_scale = c->v_scale; a.v_zero = c->v_zero;
+  kivi_status st = hip_status(kivi::launch_quantize(g->bits, a, s));
+  if (st != KIVI_OK) return st;
+  c->n_q += G;
+  c->n_res -= G;
+  c->res_start = (c->res_start + G) % slots;
+  return KIVI_OK;
+}
+
+// Copy one token per unit into ring slot (res_start + n_res) mod (R+G).
+kivi_status enqueue_append(const kivi_geom *g, kivi_cache *c, const uint16_t *k_new,
+                           const uint16_t *v_new, hipStream_t s) {
+  const int slots = g->residual + g->group;
+  kivi::CopyRowsArgs a{};
+  a.src_k = k_new; a.src_v = v_new;
+  a.src_unit_stride = g->head_dim;
+  a.src_tok0 = 0;
+  a.dst_k = c->k_res; a.dst_v = c->v_res;
+  a.dst_unit_stride = (long long)slots * g->head_dim;
+  a.dst_row0 = (c->res_start + c->n_res) % slots;
+  a.n_rows = 1; a.n_units = (int)units_of(g);
+  kivi_status st = hip_status(kivi::launch_copy_rows(a, s));
+  if (st != KIVI_OK) return st;
+  c->n_res += 1;
+  return KIVI_OK;
+}
+
+// Validation shared by decode attention and the decode step.
+kivi_status check_attend_args(const kivi_geom *g, const kivi_cache *c, const uint16_t *q,
+                              const float *out, float softmax_scale, const void *ws,
+                              size_t ws_bytes) {
+  if (!q || !out) return KIVI_E_NULL;
+  size_t need = 0;
+  kivi_status st = kivi_decode_workspace_size(g, &need);
+  if (st != KIVI_OK) return st;
+  if (!ws || ws_bytes < need) return KIVI_E_WORKSPACE;
+  if (!isfinite(softmax_scale)) return KIVI_E_GEOMETRY;
+  (void)c;
+  return KIVI_OK;
+}
+
+// Launch decode attention over the cache state in `c`.  With k_new/v_new
+// set, logical residual token c->n_res - 1 is read from them (and stored
+// into its ring slot by the kernel) instead of from the ring.
+kivi_status enqueue_attend(const kivi_geom *g, const kivi_cache *c, const uint16_t *k_new,
+                           const uint16_t *v_new, const uint16_t *q, float *out,
+                           float softmax_scale, void *ws, hipStream_t s) {
+  kivi::DecodeArgs a{};
+  a.k_codes = c->k_codes; a.k_scale = c->k_scale; a.k_zero = c->k_zero;
+  a.v_codes = c->v_codes; a.v_scale = c->v_scale; a.v_zero = c->v_zero;
+  a.k_res = c->k_res; a.v_res = c->v_res;
+  a.k_new = k_new; a.v_new = v_new;
+  a.new_idx = k_new ? c->n_res - 1 : -1;
+  a.q = q; a.out = out;
+  a.counters = (unsigned *)ws;
+  a.part = (float *)((char *)ws + counters_bytes(g));
+  a.qscale = softmax_scale * 1.4426950408889634f;
+  a.kv_heads = g->kv_heads; a.qpk = g->q_per_kv; a.max_tokens = g->max_tokens;
+  a.n_groups_cap = g->max_tokens / g->group;
+  a.slots = g->residual + g->group;
+  a.n_units = (int)units_of(g);
+  a.n_groups = c->n_q / g->group;
+  a.n_res = c->n_res; a.res_start = c->res_start;
+  if (g->q_per_kv == 1) {
+    // MHA: fixed-size splits of the quantised groups plus one residual split
+    a.gps = choose_gps(units_of(g), a.n_groups);
+    a.n_split_q = (a.n_groups + a.gps - 1) / a.gps;
+    a.n_split = a.n_split_q + (c->n_res > 0 ? 1 : 0);
+    if (a.n_split > max_splits(g)) return KIVI_E_WORKSPACE;   // cannot happen: gps >= 4
+  } else {
+    // GQA: the launcher picks the workgroups per unit; pass the capacity
+    a.n_split = max_splits(g);
+  }
+  return hip_status(kivi::launch_decode(g->bits, a, s));
+}
+
 }  // namespace
 
 extern "C" {
@@ -183,19 +271,8 @@ kivi_status kivi_append_token(const kivi_geom *g, kivi_cache *c, const uint16_t 
   if ((st = check_cache(c)) != KIVI_OK) return st;
   if (!k_new || !v_new) return KIVI_E_NULL;
   if ((st = check_state(g, c)) != KIVI_OK) return st;
-  const int slots = g->residual + g->group;
-  if (c->n_res == slots) return KIVI_E_RESIDUAL_FULL;
-  kivi::CopyRowsArgs a{};
-  a.src_k = k_new; a.src_v = v_new;
-  a.src_unit_stride = g->head_dim;
-  a.src_tok0 = 0;
-  a.dst_k = c->k_res; a.dst_v = c->v_res;
-  a.dst_unit_stride = (long long)slots * g->head_dim;
-  a.dst_row0 = (c->res_start + c->n_res) % slots;
-  a.n_rows = 1; a.n_units = (int)units_of(g);
-  if ((st = hip_status(kivi::launch_copy_rows(a, (hipStream_t)stream))) != KIVI_OK) return st;
-  c->n_res += 1;
-  return KIVI_OK;
+  if (c->n_res == g->residual + g->group) return KIVI_E_RESIDUAL_FULL;
+  return enqueue_append(g, c, k_new, v_new, (hipStream_t)stream);
 }
 
 kivi_status kivi_flush_residual(const kivi_geom *g, kivi_cache *c, int32_t *flushed,
@@ -208,19 +285,7 @@ kivi_status kivi_flush_residual(const kivi_geom *g, kivi_cache *c, int32_t *flus
   if (flushed) *flushed = 0;
   if (c->n_res != slots) return KIVI_OK;
   if (c->n_q + G > g->max_tokens) return KIVI_E_CAPACITY;
-  kivi::QuantizeArgs a{};
-  a.src_k = c->k_res; a.src_v = c->v_res;
-  a.src_unit_stride = (long long)slots * g->head_dim;
-  a.src_tok0 = c->res_start;   // a multiple of G: the G oldest tokens are contiguous
-  a.n_groups = 1; a.n_units = (int)units_of(g); a.dst_g0 = c->n_q / G;
-  a.max_tokens = g->max_tokens; a.n_groups_cap = g->max_tokens / G;
-  a.k_codes = c->k_codes; a.k_scale = c->k_scale; a.k_zero = c->k_zero;
-  a.v_codes = c->v_codes; a.v_scale = c->v_scale; a.v_zero = c->v_zero;
-  if ((st = hip_status(kivi::launch_quantize(g->bits, a, (hipStream_t)stream))) != KIVI_OK)
-    return st;
-  c->n_q += G;
-  c->n_res -= G;
-  c->res_start = (c->res_start + G) % slots;
+  if ((st = enqueue_flush(g, c, (hipStream_t)stream)) != KIVI_OK) return st;
   if (flushed) *flushed = 1;
   return KIVI_OK;
 }
@@ -231,39 +296,51 @@ kivi_status kivi_decode_attention(const kivi_geom *g, const kivi_cache *c, const
   kivi_status st = check_geom(g);
   if (st != KIVI_OK) return st;
   if ((st = check_cache(c)) != KIVI_OK) return st;
-  if (!q || !out) return KIVI_E_NULL;
+  if ((st = check_attend_args(g, c, q, out, softmax_scale, ws, ws_bytes)) != KIVI_OK) return st;
   if ((st = check_state(g, c)) != KIVI_OK) return st;
   if (c->n_q + c->n_res == 0) return KIVI_E_STATE;
-  size_t need = 0;
-  kivi_decode_workspace_size(g, &need);
-  if (!ws || ws_bytes < need) return KIVI_E_WORKSPACE;
-  if (!isfinite(softmax_scale)) return KIVI_E_GEOMETRY;
+  return enqueue_attend(g, c, nullptr, nullptr, q, out, softmax_scale, ws, (hipStream_t)stream);
+}
 
-  kivi::DecodeArgs a{};
-  a.k_codes = c->k_codes; a.k_scale = c->k_scale; a.k_zero = c->k_zero;
-  a.v_codes = c->v_codes; a.v_scale = c->v_scale; a.v_zero = c->v_zero;
-  a.k_res = c->k_res; a.v_res = c->v_res;
-  a.q = q; a.out = out;
-  a.counters = (unsigned *)ws;
-  a.part = (float *)((char *)ws + counters_bytes(g));
-  a.qscale = softmax_scale * 1.4426950408889634f;
-  a.kv_heads = g->kv_heads; a.qpk = g->q_per_kv; a.max_tokens = g->max_tokens;
-  a.n_groups_cap = g->max_tokens / g->group;
-  a.slots = g->residual + g->group;
-  a.n_units = (int)units_of(g);
-  a.n_groups = c->n_q / g->group;
-  a.n_res = c->n_res; a.res_start = c->res_start;
-  if (g->q_per_kv == 1) {
-    // MHA: fixed-size splits of the quantised groups plus one residual split
-    a.gps = choose_gps(units_of(g), a.n_groups);
-    a.n_split_q = (a.n_groups + a.gps - 1) / a.gps;
-    a.n_split = a.n_split_q + (c->n_res > 0 ? 1 : 0);
-    if (a.n_split > max_splits(g)) return KIVI_E_WORKSPACE;   // cannot happen: gps >= 4
-  } else {
-    // GQA: the launcher picks the workgroups per unit; pass the capacity
-    a.n_split = max_splits(g);
+kivi_status kivi_decode_step(const kivi_geom *g, kivi_cache *c, const uint16_t *k_new,
+                             const uint16_t *v_new, const uint16_t *q, float *out,
+                             float softmax_scale, void *ws, size_t ws_bytes, int32_t *flushed,
+                             void *stream) {
+  kivi_status st = check_geom(g);
+  if (st != KIVI_OK) return st;
+  if ((st = check_cache(c)) != KIVI_OK) return st;
+  if (!k_new || !v_new) return KIVI_E_NULL;
+  if ((st = check_attend_args(g, c, q, out, softmax_scale, ws, ws_bytes)) != KIVI_OK) return st;
+  if ((st = check_state(g, c)) != KIVI_OK) return st;
+  const int G = g->group, slots = g->residual + G;
+  if (c->n_res == slots) return KIVI_E_RESIDUAL_FULL;
+  const bool flush = c->n_res + 1 == slots;
+  if (flush && c->n_q + G > g->max_tokens) return KIVI_E_CAPACITY;
+  if (flushed) *flushed = 0;
+  hipStream_t s = (hipStream_t)stream;
+  if (flush && g->residual == 0) {
+    // the ring holds exactly one group, which includes the new token: the
+    // three steps run as separate launches
+    if ((st = enqueue_append(g, c, k_new, v_new, s)) != KIVI_OK) return st;
+    if ((st = enqueue_flush(g, c, s)) != KIVI_OK) return st;
+    if (flushed) *flushed = 1;
+    return enqueue_attend(g, c, nullptr, nullptr, q, out, softmax_scale, ws, s);
   }
-  return hip_status(kivi::launch_decode(g->bits, a, (hipStream_t)stream));
+  if (flush) {
+    // With R >= G the G oldest tokens of the full ring exclude the new one
+    // (the newest of R+G), so quantising them before the append leaves the
+    // same state as append-then-flush, and the append can fuse into the
+    // attention launch.
+    if ((st = enqueue_flush(g, c, s)) != KIVI_OK) return st;
+    if (flushed) *flushed = 1;
+  }
+  // attention with the append fused: the new token is logical index n_res
+  kivi_cache next = *c;
+  next.n_res += 1;
+  if ((st = enqueue_attend(g, &next, k_new, v_new, q, out, softmax_scale, ws, s)) != KIVI_OK)
+    return st;
+  c->n_res = next.n_res;
+  return KIVI_OK;
 }
 
 }  // extern "C"

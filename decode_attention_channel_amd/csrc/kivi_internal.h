@@ -47,7 +47,12 @@ hipError_t launch_copy_rows(const CopyRowsArgs &a, hipStream_t s);
 struct DecodeArgs {
   const uint8_t *k_codes; const float *k_scale, *k_zero;
   const uint8_t *v_codes; const float *v_scale, *v_zero;
-  const uint16_t *k_res, *v_res;
+  uint16_t *k_res, *v_res;   // written only for the fused append below
+  // Fused append: logical residual token new_idx (-1: none) is taken from
+  // k_new / v_new ([units][D] bf16) instead of the ring, and the one wave
+  // that reads it also stores it into its ring slot.
+  const uint16_t *k_new, *v_new;
+  int new_idx;
   const uint16_t *q;
   unsigned *counters; // [units] arrival counters, zero between calls
   float *part;        // [units][n_split][QPK][kPartStride]

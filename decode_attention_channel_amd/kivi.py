@@ -24,7 +24,7 @@ STATUS = {
 EXPORTS = (
     "kivi_cache_layout", "kivi_decode_workspace_size", "kivi_quantize_prefill",
     "kivi_append_token", "kivi_flush_residual", "kivi_decode_attention",
-    "kivi_status_string", "kivi_last_hip_error",
+    "kivi_decode_step", "kivi_status_string", "kivi_last_hip_error",
 )
 BUFFERS = ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero", "k_res", "v_res")
 
@@ -52,8 +52,8 @@ class _Cache(ctypes.Structure):
 
 def _load():
     if not os.path.exists(_LIB_PATH):
-        raise ImportError(f"{_LIB_PATH} is not built: run `python -m "
-                          "decode_attention_channel_amd.build` (hipcc, gfx950)")
+        raise ImportError(f"{_LIB_PATH} is not built: run `python "
+                          "decode_attention_channel_amd/build.py` (hipcc, gfx950)")
     lib = ctypes.CDLL(_LIB_PATH)
     G, C, P = ctypes.POINTER(_Geom), ctypes.POINTER(_Cache), ctypes.c_void_p
     sz = ctypes.POINTER(ctypes.c_size_t)
@@ -63,8 +63,11 @@ def _load():
     lib.kivi_append_token.argtypes = [G, C, P, P, P]
     lib.kivi_flush_residual.argtypes = [G, C, ctypes.POINTER(ctypes.c_int32), P]
     lib.kivi_decode_attention.argtypes = [G, C, P, P, ctypes.c_float, P, ctypes.c_size_t, P]
+    lib.kivi_decode_step.argtypes = [G, C, P, P, P, P, ctypes.c_float, P, ctypes.c_size_t,
+                                     ctypes.POINTER(ctypes.c_int32), P]
     for f in ("kivi_cache_layout", "kivi_decode_workspace_size", "kivi_quantize_prefill",
-              "kivi_append_token", "kivi_flush_residual", "kivi_decode_attention"):
+              "kivi_append_token", "kivi_flush_residual", "kivi_decode_attention",
+              "kivi_decode_step"):
         getattr(lib, f).restype = ctypes.c_int
     lib.kivi_status_string.argtypes = [ctypes.c_int]
     lib.kivi_status_string.restype = ctypes.c_char_p
@@ -235,9 +238,34 @@ def decode_attention(g: Geom, c: Cache, q: torch.Tensor, out: torch.Tensor | Non
     return out
 
 
+def decode_step(g: Geom, c: Cache, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor,
+                out: torch.Tensor | None = None, softmax_scale: float | None = None,
+                ws: Workspace | None = None) -> tuple[torch.Tensor, int]:
+    """Append k_new/v_new (bf16 [B][H][D]), flush if the ring is full, attend
+    with q (bf16 [B][H*QPK][D]); returns (out fp32 [B][H*QPK][D], flushed)."""
+    shape = (g.batch, g.q_heads, g.head_dim)
+    tok = (g.batch, g.kv_heads, g.head_dim)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = Workspace(g, q.device)
+    scale = 1.0 / math.sqrt(g.head_dim) if softmax_scale is None else float(softmax_scale)
+    flushed = ctypes.c_int32(0)
+    _check(_lib.kivi_decode_step(ctypes.byref(g.c()), ctypes.byref(c._c),
+                                 _ptr(k_new, torch.bfloat16, tok, "k_new"),
+                                 _ptr(v_new, torch.bfloat16, tok, "v_new"),
+                                 _ptr(q, torch.bfloat16, shape, "q"),
+                                 _ptr(out, torch.float32, shape, "out"), scale,
+                                 ctypes.c_void_p(ws.buf.data_ptr()), ws.nbytes,
+                                 ctypes.byref(flushed), _stream()),
+           "kivi_decode_step")
+    return out, flushed.value
+
+
 class LayerStepper:
     """Pre-marshalled arguments of one layer's decode step (append, flush,
-    attend) for tight loops: the geometry, cache, workspace, q/out buffers,
+    attend as separate calls, or step() for the fused kivi_decode_step) for
+    tight loops: the geometry, cache, workspace, q/out buffers,
     softmax scale and stream (torch's current stream at construction) are
     converted once; append() checks only the new token's tensors."""
 
@@ -257,11 +285,14 @@ class LayerStepper:
         self._flushed = ctypes.c_int32(0)
         self._tok_shape = (g.batch, g.kv_heads, g.head_dim)
 
-    def append(self, k_new: torch.Tensor, v_new: torch.Tensor) -> None:
+    def _check_token(self, k_new: torch.Tensor, v_new: torch.Tensor) -> None:
         if (k_new.shape != self._tok_shape or v_new.shape != self._tok_shape or
                 k_new.dtype != torch.bfloat16 or v_new.dtype != torch.bfloat16 or
                 not k_new.is_contiguous() or not v_new.is_contiguous()):
             raise ValueError("k_new / v_new must be contiguous bf16 [B][H][D]")
+
+    def append(self, k_new: torch.Tensor, v_new: torch.Tensor) -> None:
+        self._check_token(k_new, v_new)
         _check(_lib.kivi_append_token(self._gp, self._cp, ctypes.c_void_p(k_new.data_ptr()),
                                       ctypes.c_void_p(v_new.data_ptr()), self._stream),
                "kivi_append_token")
@@ -275,3 +306,12 @@ class LayerStepper:
         _check(_lib.kivi_decode_attention(self._gp, self._cp, self._q, self._out, self._scale,
                                           self._ws, self._wsn, self._stream),
                "kivi_decode_attention")
+
+    def step(self, k_new: torch.Tensor, v_new: torch.Tensor) -> int:
+        self._check_token(k_new, v_new)
+        _check(_lib.kivi_decode_step(self._gp, self._cp, ctypes.c_void_p(k_new.data_ptr()),
+                                     ctypes.c_void_p(v_new.data_ptr()), self._q, self._out,
+                                     self._scale, self._ws, self._wsn,
+                                     ctypes.byref(self._flushed), self._stream),
+               "kivi_decode_step")
+        return self._flushed.value

@@ -24,9 +24,11 @@
  * ------------------------------------------------------------------------
  *  - Pointers named "device" must point to device memory of the current HIP
  *    device; the caller allocates every buffer and keeps it alive until the
- *    work enqueued on `stream` has finished.  The library never allocates,
- *    never synchronises and keeps no global state apart from a thread-local
- *    copy of the last HIP error.
+ *    work enqueued on `stream` has finished.  The library never allocates
+ *    and never synchronises.  Its only global state is a thread-local copy
+ *    of the last HIP error and, per device, the resident-workgroup count of
+ *    each decode kernel (queried once from the HIP occupancy API and reused;
+ *    safe to share between threads).
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *  - All arguments are validated on the host before anything is enqueued.
  *    On any error nothing is enqueued and the counters in kivi_cache are
@@ -35,8 +37,8 @@
  *  - Supported set (v1): bits in {2,4}; group == 32; head_dim == 128;
  *    residual a multiple of group with 0 <= residual <= 4096;
  *    1 <= q_per_kv <= 16; max_tokens a multiple of group;
- *    batch, kv_heads >= 1.  Anything else: KIVI_E_UNSUPPORTED (or
- *    KIVI_E_GEOMETRY for non-positive sizes).
+ *    batch, kv_heads >= 1 with batch * kv_heads <= 65535.  Anything else:
+ *    KIVI_E_UNSUPPORTED (or KIVI_E_GEOMETRY for non-positive sizes).
  *  - The whole batch moves in lockstep: one (n_q, n_res, res_start) triple
  *    describes every sequence of the batch.
  *  - Numbers: bf16 tensors are passed as uint16_t bit patterns.  Inputs must
@@ -216,6 +218,30 @@ kivi_status kivi_decode_attention(const kivi_geom *geom, const kivi_cache *cache
                                   const uint16_t *q, float *out,
                                   float softmax_scale, void *ws, size_t ws_bytes,
                                   void *stream);
+
+/* One decode step of one layer in (usually) a single launch: append
+ * k_new/v_new, flush iff the ring is then full, and attend with q -- the
+ * same cache bytes, counters and `out` as kivi_append_token,
+ * kivi_flush_residual and kivi_decode_attention called in that order (the
+ * step order of the cache state machine above).
+ * How: when the append would fill the ring (n_res == R+G-1) the G oldest
+ * tokens are quantised first; with R >= G they cannot include the new
+ * token, so the state is the same.  The attention kernel then reads the new
+ * token from k_new/v_new and stores it into its ring slot itself.  With
+ * R == 0 a flush step runs as three launches.
+ * k_new, v_new: device bf16 [B][H][D]; q, out, softmax_scale, ws, ws_bytes
+ * as for kivi_decode_attention; flushed: host pointer (may be NULL), set to
+ * 1 if a group was flushed, else 0.
+ * Errors (checked before anything is enqueued): those of the three calls,
+ * i.e. KIVI_E_NULL, KIVI_E_GEOMETRY, KIVI_E_UNSUPPORTED, KIVI_E_STATE,
+ * KIVI_E_RESIDUAL_FULL (n_res == R+G on entry), KIVI_E_CAPACITY (a flush is
+ * due and n_q + G > max_tokens), KIVI_E_WORKSPACE; KIVI_E_HIP if a launch
+ * fails, with the counters reflecting the launches that were enqueued. */
+kivi_status kivi_decode_step(const kivi_geom *geom, kivi_cache *cache,
+                             const uint16_t *k_new, const uint16_t *v_new,
+                             const uint16_t *q, float *out, float softmax_scale,
+                             void *ws, size_t ws_bytes, int32_t *flushed,
+                             void *stream);
 
 /* Static description of a status code (never NULL). */
 const char *kivi_status_string(kivi_status status);

@@ -20,7 +20,7 @@ def _declared():
 
 def test_exports_every_declared_function():
     names = _declared()
-    assert len(names) == 8
+    assert len(names) == 9
     lib = ctypes.CDLL(kivi.library_path())
     for n in names:
         assert hasattr(lib, n), n
@@ -110,6 +110,38 @@ def test_host_validation_before_any_device_work():
                  fake, ws_need, None) == 2
     assert _call("kivi_decode_attention", P(g), P(c), None, fake, ctypes.c_float(0.1), fake,
                  ws_need, None) == 1
+
+
+def test_decode_step_validation_before_any_device_work():
+    g = _g().c()
+    fake = ctypes.c_void_p(0x2000)
+    P = ctypes.byref
+    ws_need = kivi.workspace_size(_g())
+    flushed = ctypes.c_int32(7)
+
+    def step(c, k=fake, v=fake, q=fake, out=fake, scale=0.1, ws=fake, nbytes=ws_need):
+        return _call("kivi_decode_step", P(g), P(c), k, v, q, out, ctypes.c_float(scale), ws,
+                     nbytes, P(flushed), None)
+
+    c = _cache_struct(n_q=64, n_res=140)
+    assert step(c, k=None) == 1 and step(c, v=None) == 1
+    assert step(c, q=None) == 1 and step(c, out=None) == 1
+    assert step(c, ws=None) == 7 and step(c, nbytes=ws_need - 1) == 7
+    assert step(c, scale=float("inf")) == 2
+    for i in range(8):
+        assert step(_cache_struct(n_q=64, n_res=140, null=i)) == 1
+    # a full ring on entry, as for kivi_append_token
+    c = _cache_struct(n_q=64, n_res=160, res_start=32)
+    assert step(c) == 6
+    # a flush is due (n_res == R+G-1) but the history is at capacity
+    c = _cache_struct(n_q=1024, n_res=159)
+    assert step(c) == 5
+    # inconsistent counters
+    assert step(_cache_struct(n_q=33, n_res=140)) == 9
+    assert step(_cache_struct(n_q=64, n_res=140, res_start=8)) == 9
+    # nothing was enqueued and no counter moved on any error
+    assert (c.n_q, c.n_res, c.res_start) == (1024, 159, 0)
+    assert flushed.value == 7
 
 
 def test_status_strings():
