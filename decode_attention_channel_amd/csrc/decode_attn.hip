@@ -33,6 +33,9 @@
 #include <float.h>
 #include <math.h>
 
+#include <stdio.h>
+#include <stdlib.h>
+
 #include "kivi_internal.h"
 
 namespace kivi {
@@ -804,7 +807,7 @@ __global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeArgs a) {
     MergeSmem<HMAX> mg;
   } sm;
 
-  const int split = blockIdx.x, u = blockIdx.y;
+  const int u = blockIdx.x, split = blockIdx.y;
   // wave index made visibly wave-uniform so that group offsets live in SGPRs
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int n = lane & 15, gq = lane >> 4;          // MFMA column / row, lane group
@@ -815,7 +818,19 @@ __global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeArgs a) {
   // this wave's byte share of the unit, and the items that start inside it
   const int n_rc = (a.n_res + G - 1) / G;
   const long long q0 = (long long)a.n_groups * CQ, total = q0 + (long long)n_rc * CR;
-  const long long wg_lo = total * split / a.n_split, wg_hi = total * (split + 1) / a.n_split;
+  // Workgroups are dispatched in linear order s*n_units + u, one per compute
+  // unit per round, so that index / cus is the workgroup's rank among those
+  // sharing its compute unit.  Older workgroups win the arbitration for the
+  // memory pipeline, so the byte shares are weighted by rank; the weights are
+  // integers and every workgroup of a unit derives the same boundaries.
+  long long cum = 0, wsum = 0, wself = 0;
+  for (int s = 0; s < a.n_split; ++s) {
+    const int w = a.rank_w[min((s * a.n_units + u) / a.cus, 3)];
+    cum += s < split ? w : 0;
+    wself = s == split ? w : wself;
+    wsum += w;
+  }
+  const long long wg_lo = total * cum / wsum, wg_hi = total * (cum + wself) / wsum;
   const long long lo = wg_lo + (wg_hi - wg_lo) * wave / 4, hi = wg_lo + (wg_hi - wg_lo) * (wave + 1) / 4;
   const int g_begin = (int)min((lo + CQ - 1) / CQ, (long long)a.n_groups);
   const int g_end = (int)min((hi + CQ - 1) / CQ, (long long)a.n_groups);
@@ -1123,15 +1138,21 @@ void *gqa_kernel() {
   return reinterpret_cast<void *>(&decode_gqa_kernel<BITS, NHB>);
 }
 
-// Resident workgroups of a GQA kernel variant on the current device
-// (occupancy x compute units), cached per device and variant.
-int resident_slots(int bits, int nhb) {
-  static int cache[16][2][4];   // 0 = not yet queried
+// Occupancy of a GQA kernel variant on the current device: resident
+// workgroups per compute unit and the number of compute units, cached per
+// device and variant.
+struct Residency {
+  int per_cu, cus;
+};
+
+Residency residency(int bits, int nhb) {
+  static int cache[16][2][4][2];   // 0 = not yet queried
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
   const int d = dev & 15, bi = bits == 4 ? 1 : 0;
-  int v = __atomic_load_n(&cache[d][bi][nhb - 1], __ATOMIC_RELAXED);
-  if (v > 0) return v;
+  int *slot = cache[d][bi][nhb - 1];
+  Residency r{__atomic_load_n(&slot[0], __ATOMIC_RELAXED), __atomic_load_n(&slot[1], __ATOMIC_RELAXED)};
+  if (r.per_cu > 0 && r.cus > 0) return r;
   void *fn = nullptr;
   switch ((bi << 2) | (nhb - 1)) {
     case 0: fn = gqa_kernel<2, 1>(); break;
@@ -1143,14 +1164,33 @@ int resident_slots(int bits, int nhb) {
     case 6: fn = gqa_kernel<4, 3>(); break;
     default: fn = gqa_kernel<4, 4>(); break;
   }
-  int per_cu = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 256, 0) != hipSuccess || per_cu < 1)
-    per_cu = 1;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
-    cus = 256;
-  v = per_cu * cus;
-  __atomic_store_n(&cache[d][bi][nhb - 1], v, __ATOMIC_RELAXED);
-  return v;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&r.per_cu, fn, 256, 0) != hipSuccess || r.per_cu < 1)
+    r.per_cu = 1;
+  if (hipDeviceGetAttribute(&r.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || r.cus < 1)
+    r.cus = 256;
+  __atomic_store_n(&slot[0], r.per_cu, __ATOMIC_RELAXED);
+  __atomic_store_n(&slot[1], r.cus, __ATOMIC_RELAXED);
+  return r;
+}
+
+// Byte-share weights of co-resident ranks 0..3 (oldest first).  Measured on
+// MI355X at the 8K GQA workload (2-bit, three workgroups per compute unit)
+// with equal shares, the ranks finish their loops at about 19, 24 and 30 us;
+// the defaults come from a sweep of the launch time there and at the 32K
+// 4-bit workload (two per compute unit).  KIVI_RANK_WEIGHTS="w0,w1,w2,w3"
+// (positive integers) overrides them, for sweeps.
+void rank_weights(int per_cu, int (&w)[4]) {
+  static const int k3[4] = {100, 75, 55, 55};
+  static const int k2[4] = {100, 70, 70, 70};
+  const int *src = per_cu == 3 ? k3 : per_cu == 2 ? k2 : nullptr;
+  for (int i = 0; i < 4; ++i) w[i] = src ? src[i] : 100;
+  const char *env = getenv("KIVI_RANK_WEIGHTS");
+  if (env) {
+    int v[4], n = sscanf(env, "%d,%d,%d,%d", &v[0], &v[1], &v[2], &v[3]);
+    for (int i = 0; i < n && i < 4; ++i)
+      if (v[i] > 0 && v[i] <= 10000) w[i] = v[i];
+    for (int i = n; i < 4 && n > 0; ++i) w[i] = w[n - 1];
+  }
 }
 
 // Workgroups per unit: the count that minimises (rounds of resident
@@ -1188,8 +1228,11 @@ hipError_t launch_decode(int bits, const DecodeArgs &a_in, hipStream_t s) {
   }
   const int nhb = (a_in.qpk + 3) / 4;
   DecodeArgs a = a_in;
-  a.n_split = choose_wpu(bits, a_in, resident_slots(bits, nhb));   // a_in.n_split: capacity
-  const dim3 grid(a.n_split, a.n_units);
+  const Residency res = residency(bits, nhb);
+  a.n_split = choose_wpu(bits, a_in, res.per_cu * res.cus);   // a_in.n_split: capacity
+  a.cus = res.cus;
+  rank_weights(res.per_cu, a.rank_w);
+  const dim3 grid(a.n_units, a.n_split);
 #define KIVI_LAUNCH(BITS)                                                                   \
   do {                                                                                      \
     if (nhb == 1)                                                                           \

@@ -64,7 +64,12 @@ struct DecodeArgs {
   int n_res, res_start;
   int gps;            // groups per quantised split
   int n_split_q;      // quantised splits per unit
-  int n_split;        // n_split_q + (n_res > 0)
+  int n_split;        // n_split_q + (n_res > 0); GQA: workgroups per unit
+  // GQA byte shares: workgroup (unit u, split s) has linear index s*n_units+u
+  // and co-residency rank min(index / cus, 3) on its compute unit; its share
+  // of the unit's bytes is proportional to rank_w[rank]
+  int cus;
+  int rank_w[4];
 };
 hipError_t launch_decode(int bits, const DecodeArgs &a, hipStream_t s);
 
