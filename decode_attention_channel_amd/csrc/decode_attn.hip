@@ -6,12 +6,13 @@
 // residual (catalog record kivi-2bit-llama3-8b-gqa-8k, KV bytes basis);
 // p = softmax(score); out = sum_t p_t v_t, fp32 accumulation.
 //
-// Split-K flash decoding.  Grid (split, unit): splits 0..n_split_q-1 take
-// `gps` consecutive groups of 32 quantised tokens each (4 waves, one group per
-// wave at a time, each wave with its own online-softmax state, merged in LDS
-// at the end); split n_split_q takes the bf16 residual.  Each split writes
+// Split-K flash decoding.  Grid (unit, split): the workgroups of a unit (as
+// many as fill the resident slots of the chip in one round) take byte shares
+// of its work -- quantised groups of 32 tokens, then the bf16 residual in
+// chunks of 32 -- and each of their 4 waves a quarter of that, with its own
+// online-softmax state, merged in LDS at the end.  Each workgroup writes
 // (m, l, o[128]) per query head; the last workgroup of a unit to finish
-// merges that unit's splits into `out` (arrival counter in the workspace).
+// merges that unit's partials into `out` (arrival counter in the workspace).
 //
 // Dequantisation is folded into the products, which is algebraically the
 // same as dequantise-then-dot:
@@ -237,160 +238,6 @@ __device__ void finish_unit(const DecodeArgs &a, int u, int *s_last) {
     __hip_atomic_store(a.counters + u, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// ------------------------------------------------------- residual split ---
-// The bf16 residual of one unit, 64 tokens at a time.  q.k: thread (token tt,
-// quarter qt) takes channels 32qt..32qt+31 of token tt for every head; the
-// four partial sums meet in LDS.  The chunk's V rows are staged in LDS with
-// coalesced loads, then P.V runs with one (head, channel pair) per thread.
-constexpr int kResChunk = 64;
-
-template <int HMAX>
-struct ResidSmem {
-  float q[HMAX][D];
-  float part[4][HMAX][kResChunk];
-  float p[HMAX][kResChunk];
-  uint32_t v[kResChunk][D / 2];
-  float mx[HMAX];
-  int last;
-};
-
-template <int HMAX>
-__device__ void residual_split(ResidSmem<HMAX> &sm, const DecodeArgs &a, int u, int split) {
-  const int tid = threadIdx.x, qpk = a.qpk;
-  const int b = u / a.kv_heads, h = u % a.kv_heads;
-  const uint16_t *qrow = a.q + ((long long)b * a.kv_heads * qpk + (long long)h * qpk) * D;
-  for (int i = tid; i < qpk * D; i += 256) sm.q[i / D][i % D] = bf16_bits_to_f32(qrow[i]) * a.qscale;
-
-  constexpr int ITEMS = (HMAX * (D / 2) + 255) / 256;
-  float m_h[HMAX], oacc[ITEMS][2], lacc[ITEMS];
-#pragma unroll
-  for (int hh = 0; hh < HMAX; ++hh) m_h[hh] = kNegInf;
-#pragma unroll
-  for (int it = 0; it < ITEMS; ++it) { oacc[it][0] = oacc[it][1] = 0.f; lacc[it] = 0.f; }
-
-  const long long ring = (long long)u * a.slots;
-  const int tt = tid & (kResChunk - 1), qt = tid >> 6;
-  for (int t0 = 0; t0 < a.n_res; t0 += kResChunk) {
-    const int cn = min(kResChunk, a.n_res - t0);
-    __syncthreads();   // q staged / previous chunk consumed
-    // stage V rows: cn rows x 16 chunks of 16 bytes; the appended token of a
-    // fused step comes from v_new and is stored into its ring slot here
-    for (int i = tid; i < cn * (D / 8); i += 256) {
-      const int r = i / (D / 8), c16 = i % (D / 8);
-      const int slot = (a.res_start + t0 + r) % a.slots;
-      uint4 *ring_row = reinterpret_cast<uint4 *>(a.v_res + (ring + slot) * D);
-      if (t0 + r == a.new_idx) {
-        const uint4 x = reinterpret_cast<const uint4 *>(a.v_new + (long long)u * D)[c16];
-        reinterpret_cast<uint4 *>(sm.v[r])[c16] = x;
-        ring_row[c16] = x;
-      } else {
-        reinterpret_cast<uint4 *>(sm.v[r])[c16] = ring_row[c16];
-      }
-    }
-    // partial scores over 32 channels
-    if (tt < cn) {
-      const int slot = (a.res_start + t0 + tt) % a.slots;
-      const bool is_new = t0 + tt == a.new_idx;
-      const uint4 *krow = reinterpret_cast<const uint4 *>(
-          is_new ? a.k_new + (long long)u * D + 32 * qt : a.k_res + (ring + slot) * D + 32 * qt);
-      uint4 *ring_row = reinterpret_cast<uint4 *>(a.k_res + (ring + slot) * D + 32 * qt);
-      float kf[32];
-#pragma unroll
-      for (int c8 = 0; c8 < 4; ++c8) {
-        const uint4 kv = krow[c8];
-        if (is_new) ring_row[c8] = kv;
-        const uint32_t w[4] = {kv.x, kv.y, kv.z, kv.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          kf[8 * c8 + 2 * e] = __uint_as_float(w[e] << 16);
-          kf[8 * c8 + 2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
-        }
-      }
-#pragma unroll
-      for (int hh = 0; hh < HMAX; ++hh) {
-        if (hh < qpk) {
-          float s = 0.f;
-#pragma unroll
-          for (int e = 0; e < 32; ++e) s += sm.q[hh][32 * qt + e] * kf[e];
-          sm.part[qt][hh][tt] = s;
-        }
-      }
-    }
-    __syncthreads();
-    for (int i = tid; i < qpk * kResChunk; i += 256) {
-      const int hh = i / kResChunk, t = i % kResChunk;
-      sm.p[hh][t] = sm.part[0][hh][t] + sm.part[1][hh][t] + sm.part[2][hh][t] + sm.part[3][hh][t];
-    }
-    __syncthreads();
-    // chunk max per head: wave w reduces heads w, w+4, ...
-    {
-      const int w = tid >> 6, lane = tid & 63;
-      for (int hh = w; hh < qpk; hh += 4) {
-        float mx = lane < cn ? sm.p[hh][lane] : kNegInf;
-#pragma unroll
-        for (int msk = 32; msk >= 1; msk >>= 1) mx = xor_max(mx, msk);
-        if (lane == 0) sm.mx[hh] = mx;
-      }
-    }
-    __syncthreads();
-    float alpha[HMAX];
-#pragma unroll
-    for (int hh = 0; hh < HMAX; ++hh) {
-      if (hh < qpk) {
-        const float mnew = fmaxf(m_h[hh], sm.mx[hh]);
-        alpha[hh] = m_h[hh] == kNegInf ? 0.f : fast_exp2(m_h[hh] - mnew);
-        m_h[hh] = mnew;
-      } else {
-        alpha[hh] = 0.f;
-      }
-    }
-    for (int i = tid; i < qpk * kResChunk; i += 256) {
-      const int hh = i / kResChunk, t = i % kResChunk;
-      sm.p[hh][t] = t < cn ? fast_exp2(sm.p[hh][t] - m_h[hh]) : 0.f;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int it = 0; it < ITEMS; ++it) {
-      const int item = tid + 256 * it;
-      if (item < qpk * (D / 2)) {
-        const int hh = item / (D / 2), cp = item % (D / 2);
-        float al = 0.f;
-#pragma unroll
-        for (int x = 0; x < HMAX; ++x)
-          if (x == hh) al = alpha[x];
-        float o0 = oacc[it][0] * al, o1 = oacc[it][1] * al, l = lacc[it] * al;
-#pragma unroll 8
-        for (int t = 0; t < cn; ++t) {
-          const uint32_t vv = sm.v[t][cp];
-          const float pr = sm.p[hh][t];
-          o0 += pr * __uint_as_float(vv << 16);
-          o1 += pr * __uint_as_float(vv & 0xFFFF0000u);
-          l += pr;
-        }
-        oacc[it][0] = o0; oacc[it][1] = o1; lacc[it] = l;
-      }
-    }
-  }
-  float *part = a.part + ((long long)u * a.n_split + split) * qpk * kPartStride;
-#pragma unroll
-  for (int it = 0; it < ITEMS; ++it) {
-    const int item = tid + 256 * it;
-    if (item < qpk * (D / 2)) {
-      const int hh = item / (D / 2), cp = item % (D / 2);
-      float mh = kNegInf;
-#pragma unroll
-      for (int x = 0; x < HMAX; ++x)
-        if (x == hh) mh = m_h[x];
-      st_shared_agent(part + hh * kPartStride + 4 + 2 * cp, oacc[it][0]);
-      st_shared_agent(part + hh * kPartStride + 5 + 2 * cp, oacc[it][1]);
-      if (cp == 0) {
-        st_shared_agent(part + hh * kPartStride + 0, mh);
-        st_shared_agent(part + hh * kPartStride + 1, lacc[it]);
-      }
-    }
-  }
-}
-
 // ------------------------------------------------------ MFMA (GQA) path ---
 // ---- cross-lane sums / maxima without LDS round trips.  A wave is 4 rows of
 // 16 lanes; permlane16/32 swaps exchange row pairs, so x + swap(x) is the
@@ -480,24 +327,33 @@ __device__ __forceinline__ UnitView make_view(const DecodeArgs &a, int u, int n,
   return v;
 }
 
+// Loads of group g.  With live == false the same loads are issued with a
+// per-lane offset beyond every buffer's range: they return zeros and touch
+// no memory.  Issuing a fixed number of loads per pipeline step keeps the
+// compiler's count of outstanding loads exact, so each step waits only for
+// the group it computes and not for the prefetches behind it.
+constexpr uint32_t kOutOfRange = 0x80000000u;   // > any unit's buffer size
+
 template <int BITS>
-__device__ __forceinline__ void load_group(GroupRaw<BITS> &r, const UnitView &v, int g) {
+__device__ __forceinline__ void load_group(GroupRaw<BITS> &r, const UnitView &v, int g, bool live) {
   // group offsets are wave-uniform: keep them in SGPRs (scalar buffer offsets)
   const uint32_t sc = __builtin_amdgcn_readfirstlane((uint32_t)g * (G * D * BITS / 8));
   const uint32_t sm = __builtin_amdgcn_readfirstlane((uint32_t)g * (D * 4));
+  const uint32_t ob = live ? 0u : kOutOfRange;
+  const uint32_t o_k0 = v.o_k0 + ob, o_k1 = v.o_k1 + ob, o_v = v.o_v + ob, o_mu = v.o_mu + ob;
   if constexpr (BITS == 2) {
-    const u32x2_t a = __builtin_amdgcn_raw_buffer_load_b64(v.kc, v.o_k0, sc, 0);
-    const u32x2_t b = __builtin_amdgcn_raw_buffer_load_b64(v.kc, v.o_k1, sc, 0);
+    const u32x2_t a = __builtin_amdgcn_raw_buffer_load_b64(v.kc, o_k0, sc, 0);
+    const u32x2_t b = __builtin_amdgcn_raw_buffer_load_b64(v.kc, o_k1, sc, 0);
     r.kw[0][0] = a[0]; r.kw[0][1] = a[1];
     r.kw[1][0] = b[0]; r.kw[1][1] = b[1];
-    const u32x4_t c = __builtin_amdgcn_raw_buffer_load_b128(v.vc, v.o_v, sc, 0);
+    const u32x4_t c = __builtin_amdgcn_raw_buffer_load_b128(v.vc, o_v, sc, 0);
 #pragma unroll
     for (int i = 0; i < 4; ++i) r.vw[i] = c[i];
   } else {
-    const u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(v.kc, v.o_k0, sc, 0);
-    const u32x4_t b = __builtin_amdgcn_raw_buffer_load_b128(v.kc, v.o_k1, sc, 0);
-    const u32x4_t c = __builtin_amdgcn_raw_buffer_load_b128(v.vc, v.o_v, sc, 0);
-    const u32x4_t d = __builtin_amdgcn_raw_buffer_load_b128(v.vc, v.o_v + 16, sc, 0);
+    const u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(v.kc, o_k0, sc, 0);
+    const u32x4_t b = __builtin_amdgcn_raw_buffer_load_b128(v.kc, o_k1, sc, 0);
+    const u32x4_t c = __builtin_amdgcn_raw_buffer_load_b128(v.vc, o_v, sc, 0);
+    const u32x4_t d = __builtin_amdgcn_raw_buffer_load_b128(v.vc, o_v + 16, sc, 0);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       r.kw[0][i] = a[i]; r.kw[1][i] = b[i];
@@ -509,7 +365,7 @@ __device__ __forceinline__ void load_group(GroupRaw<BITS> &r, const UnitView &v,
   const __amdgpu_buffer_rsrc_t mr[4] = {v.ks, v.kz, v.vs, v.vz};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const u32x2_t x = __builtin_amdgcn_raw_buffer_load_b64(mr[i], v.o_mu, sm, 0);
+    const u32x2_t x = __builtin_amdgcn_raw_buffer_load_b64(mr[i], o_mu, sm, 0);
     r.mw[i][0] = x[0];
     r.mw[i][1] = x[1];
   }
@@ -793,15 +649,49 @@ __device__ __forceinline__ void mfma_rchunk(const DecodeArgs &a, int u, int rc,
   __builtin_amdgcn_wave_barrier();
 }
 
-// GQA decode attention.  Grid (wpu, unit): the `wpu` workgroups of a unit
+// Byte range [lo, hi) of the unit's work for wave `wave` of workgroup
+// (u, split): quantised groups cost `cq` units each, then residual chunks of
+// G tokens `cr` each; the workgroup's share is weighted by its co-residency
+// rank, split evenly over the 4 waves.
+//
+// Workgroups are dispatched in linear order s*n_units + u, one per compute
+// unit per round, so that index / cus is the workgroup's rank among those
+// sharing its compute unit.  Older workgroups win the arbitration for the
+// memory pipeline, so the byte shares are weighted by rank; the weights are
+// integers and every workgroup of a unit derives the same boundaries.
+struct WorkRange {
+  int g_begin, g_end, r_begin, r_end;
+};
+
+__device__ __forceinline__ WorkRange wave_work(const DecodeArgs &a, int u, int split, int wave,
+                                               int cq, int cr) {
+  const int n_rc = (a.n_res + G - 1) / G;
+  const long long q0 = (long long)a.n_groups * cq, total = q0 + (long long)n_rc * cr;
+  long long cum = 0, wsum = 0, wself = 0;
+  for (int s = 0; s < a.n_split; ++s) {
+    const int w = a.rank_w[min((s * a.n_units + u) / a.cus, 3)];
+    cum += s < split ? w : 0;
+    wself = s == split ? w : wself;
+    wsum += w;
+  }
+  const long long wg_lo = total * cum / wsum, wg_hi = total * (cum + wself) / wsum;
+  const long long lo = wg_lo + (wg_hi - wg_lo) * wave / 4, hi = wg_lo + (wg_hi - wg_lo) * (wave + 1) / 4;
+  WorkRange r;
+  r.g_begin = (int)min((lo + cq - 1) / cq, (long long)a.n_groups);
+  r.g_end = (int)min((hi + cq - 1) / cq, (long long)a.n_groups);
+  r.r_begin = (int)min(max(lo - q0 + cr - 1, 0ll) / cr, (long long)n_rc);
+  r.r_end = (int)min(max(hi - q0 + cr - 1, 0ll) / cr, (long long)n_rc);
+  return r;
+}
+
+// GQA decode attention.  Grid (unit, wpu): the `wpu` workgroups of a unit
 // split its work -- the quantised groups, then the residual in chunks of 32
-// tokens -- into equal byte shares, and each workgroup splits its share over
-// its 4 waves.  Item costs are in KiB: a group (codes + scale/zero) is
-// bits + 2, a residual chunk (32 bf16 K and V rows) is 16.
+// tokens -- into rank-weighted byte shares (wave_work), and each workgroup
+// splits its share over its 4 waves.  Item costs are in KiB: a group (codes
+// + scale/zero) is bits + 2, a residual chunk (32 bf16 K and V rows) is 16.
 template <int BITS, int NHB>
 __global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeArgs a) {
   constexpr int HMAX = 4 * NHB;
-  constexpr int CQ = BITS + 2, CR = 16;
   __shared__ __align__(16) union {
     MfmaSmem<NHB> mf;
     MergeSmem<HMAX> mg;
@@ -816,48 +706,39 @@ __global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeArgs a) {
   const int b = u / a.kv_heads, h = u % a.kv_heads;
 
   // this wave's byte share of the unit, and the items that start inside it
-  const int n_rc = (a.n_res + G - 1) / G;
-  const long long q0 = (long long)a.n_groups * CQ, total = q0 + (long long)n_rc * CR;
-  // Workgroups are dispatched in linear order s*n_units + u, one per compute
-  // unit per round, so that index / cus is the workgroup's rank among those
-  // sharing its compute unit.  Older workgroups win the arbitration for the
-  // memory pipeline, so the byte shares are weighted by rank; the weights are
-  // integers and every workgroup of a unit derives the same boundaries.
-  long long cum = 0, wsum = 0, wself = 0;
-  for (int s = 0; s < a.n_split; ++s) {
-    const int w = a.rank_w[min((s * a.n_units + u) / a.cus, 3)];
-    cum += s < split ? w : 0;
-    wself = s == split ? w : wself;
-    wsum += w;
+  const WorkRange wr = wave_work(a, u, split, wave, BITS + 2, 16);
+  const int g_begin = wr.g_begin, g_end = wr.g_end, r_begin = wr.r_begin, r_end = wr.r_end;
+
+  // Order of the first loads: the query (needed first), then the first two
+  // groups, so that waiting for the query does not wait for the groups.
+  uint4 qraw[NHB];
+#pragma unroll
+  for (int hb = 0; hb < NHB; ++hb) {
+    const int hh = hb * 4 + ch;
+    qraw[hb] = make_uint4(0u, 0u, 0u, 0u);
+    if (hh < qpk)
+      qraw[hb] = *reinterpret_cast<const uint4 *>(
+          a.q + ((long long)b * a.kv_heads * qpk + (long long)h * qpk + hh) * D + 32 * gq + 8 * cm);
   }
-  const long long wg_lo = total * cum / wsum, wg_hi = total * (cum + wself) / wsum;
-  const long long lo = wg_lo + (wg_hi - wg_lo) * wave / 4, hi = wg_lo + (wg_hi - wg_lo) * (wave + 1) / 4;
-  const int g_begin = (int)min((lo + CQ - 1) / CQ, (long long)a.n_groups);
-  const int g_end = (int)min((hi + CQ - 1) / CQ, (long long)a.n_groups);
-  const int r_begin = (int)min(max(lo - q0 + CR - 1, 0ll) / CR, (long long)n_rc);
-  const int r_end = (int)min(max(hi - q0 + CR - 1, 0ll) / CR, (long long)n_rc);
+  const bool has_groups = g_begin < g_end;
+  const UnitView view = make_view<BITS>(a, u, n, gq, cm);
+  GroupRaw<BITS> r0, r1, r2;
+  load_group<BITS>(r0, view, g_begin, has_groups);
+  load_group<BITS>(r1, view, g_begin + 1, g_begin + 1 < g_end);
 
   // scaled query values in slot order for the cooperative role
   float qv[NHB][8];
 #pragma unroll
   for (int hb = 0; hb < NHB; ++hb) {
-    const int hh = hb * 4 + ch;
-    if (hh < qpk) {
-      const uint4 raw = *reinterpret_cast<const uint4 *>(
-          a.q + ((long long)b * a.kv_heads * qpk + (long long)h * qpk + hh) * D + 32 * gq + 8 * cm);
-      const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-      float x[8];
+    const uint32_t w[4] = {qraw[hb].x, qraw[hb].y, qraw[hb].z, qraw[hb].w};
+    float x[8];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        x[2 * e] = __uint_as_float(w[e] << 16);
-        x[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
-      }
-#pragma unroll
-      for (int s = 0; s < 8; ++s) qv[hb][s] = x[P8[s]] * a.qscale;
-    } else {
-#pragma unroll
-      for (int s = 0; s < 8; ++s) qv[hb][s] = 0.f;
+    for (int e = 0; e < 4; ++e) {
+      x[2 * e] = __uint_as_float(w[e] << 16);
+      x[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
     }
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qv[hb][s] = x[P8[s]] * a.qscale;
   }
 
   WaveState<NHB> st;
@@ -870,20 +751,16 @@ __global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeArgs a) {
 
   // quantised groups: software pipeline over three register sets, the next
   // two groups in flight while the current one is computed
-  if (g_begin < g_end) {
-    const UnitView view = make_view<BITS>(a, u, n, gq, cm);
-    GroupRaw<BITS> r0, r1, r2;
+  if (has_groups) {
     int g = g_begin;
-    load_group<BITS>(r0, view, g);
-    if (g + 1 < g_end) load_group<BITS>(r1, view, g + 1);
     while (true) {
-      if (g + 2 < g_end) load_group<BITS>(r2, view, g + 2);
+      load_group<BITS>(r2, view, g + 2, g + 2 < g_end);
       mfma_group<BITS, NHB>(r0, st, sm.mf, qv, wave, n, gq, ch, cm);
       if (++g >= g_end) break;
-      if (g + 2 < g_end) load_group<BITS>(r0, view, g + 2);
+      load_group<BITS>(r0, view, g + 2, g + 2 < g_end);
       mfma_group<BITS, NHB>(r1, st, sm.mf, qv, wave, n, gq, ch, cm);
       if (++g >= g_end) break;
-      if (g + 2 < g_end) load_group<BITS>(r1, view, g + 2);
+      load_group<BITS>(r1, view, g + 2, g + 2 < g_end);
       mfma_group<BITS, NHB>(r2, st, sm.mf, qv, wave, n, gq, ch, cm);
       if (++g >= g_end) break;
     }
@@ -922,208 +799,350 @@ __global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeArgs a) {
 }
 
 // ------------------------------------------------------- VALU (MHA) path ---
-struct ValuSmem {
-  float p[4][32];
+// One query head per kv head: q.K^T and P.V are matrix-vector products, so
+// they stay on VALU (fp32 FMAs on the exactly unpacked codes).  Work is split
+// like the GQA path (byte shares of quantised groups and residual chunks,
+// weighted by co-residency rank), with the same load pipeline.  Lane roles
+// for a group of 32 tokens:
+//   q.k:  lane = 8 tb + cb  -- tokens 4tb..4tb+3, channels 16cb..16cb+15
+//   P.V:  lane = 16 oc + cq -- tokens 8oc..8oc+7 (octet oc), channels 8cq..8cq+7
+
+template <int BITS>
+struct ValuRaw {
+  uint32_t kw[4][BITS / 2];   // token rows 4tb + r: 16 channels (2*BITS bytes)
+  uint32_t vw[2 * BITS];      // octet oc, channels 8cq..8cq+7: BITS bytes each
+  uint32_t mw[4][2];          // this lane's 8 bytes of each scale/zero array
+};
+
+struct ValuView {
+  __amdgpu_buffer_rsrc_t kc, vc, ks, kz, vs, vz;
+  uint32_t o_k, o_v, o_mu;
 };
 
 template <int BITS>
-__global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
+__device__ __forceinline__ ValuView make_valu_view(const DecodeArgs &a, int u, int tb, int cb,
+                                                   int oc, int cq, int lane) {
   constexpr int KROW = D * BITS / 8;
+  const long long T = a.max_tokens, NG = a.n_groups_cap;
+  ValuView v;
+  const uint32_t code_bytes = (uint32_t)(T * KROW), meta_bytes = (uint32_t)(NG * D * 4);
+  v.kc = make_rsrc(a.k_codes + u * T * KROW, code_bytes);
+  v.vc = make_rsrc(a.v_codes + u * T * KROW, code_bytes);
+  v.ks = make_rsrc(a.k_scale + u * NG * D, meta_bytes);
+  v.kz = make_rsrc(a.k_zero + u * NG * D, meta_bytes);
+  v.vs = make_rsrc(a.v_scale + u * NG * D, meta_bytes);
+  v.vz = make_rsrc(a.v_zero + u * NG * D, meta_bytes);
+  v.o_k = 4 * tb * KROW + 2 * BITS * cb;
+  v.o_v = (oc * D + 8 * cq) * BITS;
+  v.o_mu = 8 * lane;
+  return v;
+}
+
+// Loads of group g (live == false: out-of-range loads, see load_group).
+template <int BITS>
+__device__ __forceinline__ void load_valu_group(ValuRaw<BITS> &r, const ValuView &v, int g, bool live) {
+  constexpr int KROW = D * BITS / 8;
+  const uint32_t sc = __builtin_amdgcn_readfirstlane((uint32_t)g * (G * D * BITS / 8));
+  const uint32_t sm = __builtin_amdgcn_readfirstlane((uint32_t)g * (D * 4));
+  const uint32_t ob = live ? 0u : kOutOfRange;
+  const uint32_t o_k = v.o_k + ob, o_v = v.o_v + ob, o_mu = v.o_mu + ob;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    if constexpr (BITS == 2) {
+      r.kw[t][0] = __builtin_amdgcn_raw_buffer_load_b32(v.kc, o_k + t * KROW, sc, 0);
+    } else {
+      const u32x2_t x = __builtin_amdgcn_raw_buffer_load_b64(v.kc, o_k + t * KROW, sc, 0);
+      r.kw[t][0] = x[0];
+      r.kw[t][1] = x[1];
+    }
+  }
+  {
+    const u32x4_t c = __builtin_amdgcn_raw_buffer_load_b128(v.vc, o_v, sc, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r.vw[i] = c[i];
+    if constexpr (BITS == 4) {
+      const u32x4_t d = __builtin_amdgcn_raw_buffer_load_b128(v.vc, o_v + 16, sc, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) r.vw[4 + i] = d[i];
+    }
+  }
+  const __amdgpu_buffer_rsrc_t mr[4] = {v.ks, v.kz, v.vs, v.vz};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const u32x2_t x = __builtin_amdgcn_raw_buffer_load_b64(mr[i], o_mu, sm, 0);
+    r.mw[i][0] = x[0];
+    r.mw[i][1] = x[1];
+  }
+}
+
+struct ValuSmem {
+  float meta[4][4][D];   // [wave] the current group's k_scale, k_zero, v_scale, v_zero
+  float p[4][G];         // [wave] probabilities handed from the q.k to the P.V role
+};
+
+struct ValuState {
+  float oacc[8];         // channels 8cq..8cq+7, partial over this lane's octets
+  float m_run, l_run, z_run;
+};
+
+struct ValuLane {
+  int wave, lane, tb, cb, oc, cq;
+};
+
+// Online-softmax update for the 4 scores of this lane's q.k role, then the
+// hand-over of p to the P.V role: returns p for tokens 8oc..8oc+7.
+__device__ __forceinline__ void valu_softmax(float (&s4)[4], ValuState &st, ValuSmem &sm,
+                                             const ValuLane &L, float (&p8)[8]) {
+  float mx = fmaxf(fmaxf(s4[0], s4[1]), fmaxf(s4[2], s4[3]));
+  mx = xor_max(xor_max(xor_max(mx, 8), 16), 32);
+  const bool need = mx > st.m_run + kRescaleSlack;
+  if (__any(need)) {
+    const float mnew = need ? mx : st.m_run;
+    const float al = st.m_run == kNegInf ? 0.f : fast_exp2(st.m_run - mnew);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) st.oacc[i] *= al;
+    st.l_run *= al;
+    st.z_run *= al;
+    st.m_run = mnew;
+  }
+  float p4[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    p4[r] = fast_exp2(s4[r] - st.m_run);
+    st.l_run += p4[r];
+  }
+  if (L.cb == 0)
+    *reinterpret_cast<float4 *>(&sm.p[L.wave][4 * L.tb]) = make_float4(p4[0], p4[1], p4[2], p4[3]);
+  __builtin_amdgcn_wave_barrier();
+  const float4 x = *reinterpret_cast<const float4 *>(&sm.p[L.wave][8 * L.oc]);
+  const float4 y = *reinterpret_cast<const float4 *>(&sm.p[L.wave][8 * L.oc + 4]);
+  p8[0] = x.x; p8[1] = x.y; p8[2] = x.z; p8[3] = x.w;
+  p8[4] = y.x; p8[5] = y.y; p8[6] = y.z; p8[7] = y.w;
+  __builtin_amdgcn_wave_barrier();
+}
+
+template <int BITS>
+__device__ __forceinline__ void valu_group(const ValuRaw<BITS> &raw, ValuState &st, ValuSmem &sm,
+                                           const float (&qv)[16], const ValuLane &L) {
+  // scale/zero of this group: stage in LDS, read back what each role needs
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    *reinterpret_cast<uint2 *>(&sm.meta[L.wave][i][2 * L.lane]) = make_uint2(raw.mw[i][0], raw.mw[i][1]);
+  __builtin_amdgcn_wave_barrier();
+  float sk[16], zk[16], sv[8], zv[8];
+  {
+    const int jv = L.cq >> 2;   // channel group of channels 8cq..8cq+7
+    ld16(&sm.meta[L.wave][0][16 * L.cb], sk);
+    ld16(&sm.meta[L.wave][1][16 * L.cb], zk);
+    ld8(&sm.meta[L.wave][2][jv * G + 8 * L.oc], sv);
+    ld8(&sm.meta[L.wave][3][jv * G + 8 * L.oc], zv);
+  }
+  __builtin_amdgcn_wave_barrier();
+
+  float qs[16], beta = 0.f;
+#pragma unroll
+  for (int c = 0; c < 16; ++c) {
+    qs[c] = qv[c] * sk[c];
+    beta += qv[c] * zk[c];
+  }
+  beta = xor_sum(xor_sum(xor_sum(beta, 1), 2), 4);
+
+  float s4[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    float acc = 0.f;
+    if constexpr (BITS == 2) {
+      const uint32_t w = raw.kw[r][0];
+      const uint32_t x = w & 0x33333333u, y = (w >> 2) & 0x33333333u;
+      // byte k of x: channels 4k, 4k+2 ; of y: 4k+1, 4k+3
+      f32x2_t f;
+      f = fp4x2_to_f32x2<0>(x); acc += qs[0] * f[0] + qs[2] * f[1];
+      f = fp4x2_to_f32x2<0>(y); acc += qs[1] * f[0] + qs[3] * f[1];
+      f = fp4x2_to_f32x2<1>(x); acc += qs[4] * f[0] + qs[6] * f[1];
+      f = fp4x2_to_f32x2<1>(y); acc += qs[5] * f[0] + qs[7] * f[1];
+      f = fp4x2_to_f32x2<2>(x); acc += qs[8] * f[0] + qs[10] * f[1];
+      f = fp4x2_to_f32x2<2>(y); acc += qs[9] * f[0] + qs[11] * f[1];
+      f = fp4x2_to_f32x2<3>(x); acc += qs[12] * f[0] + qs[14] * f[1];
+      f = fp4x2_to_f32x2<3>(y); acc += qs[13] * f[0] + qs[15] * f[1];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const uint32_t w = raw.kw[r][i];
+        const uint32_t x = w & 0x0F0F0F0Fu, y = (w >> 4) & 0x0F0F0F0Fu;
+        const float *q8 = qs + 8 * i;
+        f32x2_t f;
+        f = fp8x2_to_f32x2<false>(x); acc += q8[0] * f[0] + q8[2] * f[1];
+        f = fp8x2_to_f32x2<false>(y); acc += q8[1] * f[0] + q8[3] * f[1];
+        f = fp8x2_to_f32x2<true>(x); acc += q8[4] * f[0] + q8[6] * f[1];
+        f = fp8x2_to_f32x2<true>(y); acc += q8[5] * f[0] + q8[7] * f[1];
+      }
+    }
+    s4[r] = xor_sum(xor_sum(xor_sum(acc, 1), 2), 4) + beta;
+  }
+  float p8[8];
+  valu_softmax(s4, st, sm, L, p8);
+  float pp[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    pp[k] = p8[k] * sv[k];
+    st.z_run += p8[k] * zv[k];
+  }
+  if constexpr (BITS == 2) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const uint32_t w = raw.vw[d];
+      const uint32_t x = w & 0x33333333u, y = (w >> 2) & 0x33333333u;
+      // bytes 0,1: channel 2d (tokens (0,2),(4,6) / (1,3),(5,7)); bytes 2,3: channel 2d+1
+      f32x2_t f;
+      float o0 = st.oacc[2 * d], o1 = st.oacc[2 * d + 1];
+      f = fp4x2_to_f32x2<0>(x); o0 += pp[0] * f[0] + pp[2] * f[1];
+      f = fp4x2_to_f32x2<0>(y); o0 += pp[1] * f[0] + pp[3] * f[1];
+      f = fp4x2_to_f32x2<1>(x); o0 += pp[4] * f[0] + pp[6] * f[1];
+      f = fp4x2_to_f32x2<1>(y); o0 += pp[5] * f[0] + pp[7] * f[1];
+      f = fp4x2_to_f32x2<2>(x); o1 += pp[0] * f[0] + pp[2] * f[1];
+      f = fp4x2_to_f32x2<2>(y); o1 += pp[1] * f[0] + pp[3] * f[1];
+      f = fp4x2_to_f32x2<3>(x); o1 += pp[4] * f[0] + pp[6] * f[1];
+      f = fp4x2_to_f32x2<3>(y); o1 += pp[5] * f[0] + pp[7] * f[1];
+      st.oacc[2 * d] = o0; st.oacc[2 * d + 1] = o1;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t w = raw.vw[e];
+      const uint32_t x = w & 0x0F0F0F0Fu, y = (w >> 4) & 0x0F0F0F0Fu;
+      f32x2_t f;
+      float o0 = st.oacc[e];
+      f = fp8x2_to_f32x2<false>(x); o0 += pp[0] * f[0] + pp[2] * f[1];
+      f = fp8x2_to_f32x2<false>(y); o0 += pp[1] * f[0] + pp[3] * f[1];
+      f = fp8x2_to_f32x2<true>(x); o0 += pp[4] * f[0] + pp[6] * f[1];
+      f = fp8x2_to_f32x2<true>(y); o0 += pp[5] * f[0] + pp[7] * f[1];
+      st.oacc[e] = o0;
+    }
+  }
+}
+
+// One residual chunk of 32 bf16 tokens (ring slots contiguous: res_start and
+// the chunk start are multiples of G).  Rows past the valid count are never
+// read; the appended token of a fused step comes from k_new / v_new and the
+// lanes that read it store it into its ring slot.
+__device__ __forceinline__ void valu_rchunk(const DecodeArgs &a, int u, int rc, ValuState &st,
+                                            ValuSmem &sm, const float (&qv)[16], const ValuLane &L) {
+  const int t0 = G * rc, valid = min(G, a.n_res - t0);
+  const int slot0 = (a.res_start + t0) % a.slots;
+  const long long ring = (long long)u * a.slots + slot0;
+  const int new_row = a.new_idx - t0;
+  const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
+
+  float s4[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int row = 4 * L.tb + r;
+    const bool is_new = row == new_row;
+    const uint4 *kp = reinterpret_cast<const uint4 *>(
+        is_new ? a.k_new + (long long)u * D + 16 * L.cb : a.k_res + (ring + row) * D + 16 * L.cb);
+    uint4 x0 = zero, x1 = zero;
+    if (row < valid) { x0 = kp[0]; x1 = kp[1]; }
+    if (is_new) {
+      uint4 *dst = reinterpret_cast<uint4 *>(a.k_res + (ring + row) * D + 16 * L.cb);
+      dst[0] = x0; dst[1] = x1;
+    }
+    const uint32_t w[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    float acc = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      acc += qv[2 * e] * __uint_as_float(w[e] << 16);
+      acc += qv[2 * e + 1] * __uint_as_float(w[e] & 0xFFFF0000u);
+    }
+    acc = xor_sum(xor_sum(xor_sum(acc, 1), 2), 4);
+    s4[r] = row < valid ? acc : kNegInf;
+  }
+  float p8[8];
+  valu_softmax(s4, st, sm, L, p8);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int row = 8 * L.oc + k;
+    const bool is_new = row == new_row;
+    const uint4 *vp = reinterpret_cast<const uint4 *>(
+        is_new ? a.v_new + (long long)u * D + 8 * L.cq : a.v_res + (ring + row) * D + 8 * L.cq);
+    uint4 x = zero;
+    if (row < valid) x = vp[0];
+    if (is_new) *reinterpret_cast<uint4 *>(a.v_res + (ring + row) * D + 8 * L.cq) = x;
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      st.oacc[2 * e] += p8[k] * __uint_as_float(w[e] << 16);
+      st.oacc[2 * e + 1] += p8[k] * __uint_as_float(w[e] & 0xFFFF0000u);
+    }
+  }
+}
+
+template <int BITS>
+__global__ __launch_bounds__(256) void decode_mha_kernel(DecodeArgs a) {
   __shared__ __align__(16) union {
     ValuSmem vs;
     MergeSmem<1> mg;
-    ResidSmem<1> rs;
   } sm;
-  // `mg` and `vs` are live at different times except p[] during the loop;
-  // the merge starts with a barrier after the loop.
+  const int u = blockIdx.x, split = blockIdx.y;
+  ValuLane L;
+  L.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  L.lane = threadIdx.x & 63;
+  L.tb = L.lane >> 3; L.cb = L.lane & 7;
+  L.oc = L.lane >> 4; L.cq = L.lane & 15;
+  const WorkRange wr = wave_work(a, u, split, L.wave, BITS + 2, 16);
 
-  const int split = blockIdx.x, u = blockIdx.y;
-  if (split >= a.n_split_q) {
-    residual_split<1>(sm.rs, a, u, split);
-    finish_unit(a, u, &sm.rs.last);
-    return;
-  }
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int tb = lane >> 3, cb = lane & 7;    // q.k role: tokens 4tb.., channels 16cb..
-  const int oc = lane >> 4, cq = lane & 15;   // P.V role: octet, channels 8cq..
-  const int b = u / a.kv_heads, h = u % a.kv_heads;
-
+  // the query first, then the first two groups (see decode_gqa_kernel)
+  const uint4 *qp = reinterpret_cast<const uint4 *>(a.q + (long long)u * D + 16 * L.cb);
+  const uint4 qraw[2] = {qp[0], qp[1]};
+  const bool has_groups = wr.g_begin < wr.g_end;
+  const ValuView view = make_valu_view<BITS>(a, u, L.tb, L.cb, L.oc, L.cq, L.lane);
+  ValuRaw<BITS> r0, r1, r2;
+  load_valu_group<BITS>(r0, view, wr.g_begin, has_groups);
+  load_valu_group<BITS>(r1, view, wr.g_begin + 1, wr.g_begin + 1 < wr.g_end);
   float qv[16];
-  {
-    const uint4 *qp = reinterpret_cast<const uint4 *>(
-        a.q + ((long long)b * a.kv_heads + h) * D + 16 * cb);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const uint4 raw = qp[i];
-      const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  for (int i = 0; i < 2; ++i) {
+    const uint32_t w[4] = {qraw[i].x, qraw[i].y, qraw[i].z, qraw[i].w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        qv[8 * i + 2 * e] = __uint_as_float(w[e] << 16) * a.qscale;
-        qv[8 * i + 2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u) * a.qscale;
-      }
+    for (int e = 0; e < 4; ++e) {
+      qv[8 * i + 2 * e] = __uint_as_float(w[e] << 16) * a.qscale;
+      qv[8 * i + 2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u) * a.qscale;
     }
   }
-  float oacc[8];
+  ValuState st;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) oacc[i] = 0.f;
-  float m_run = kNegInf, l_run = 0.f, z_run = 0.f;
+  for (int i = 0; i < 8; ++i) st.oacc[i] = 0.f;
+  st.m_run = kNegInf; st.l_run = 0.f; st.z_run = 0.f;
 
-  const int g_begin = split * a.gps;
-  const int g_end = min(g_begin + a.gps, a.n_groups);
-  const int jv = cq >> 2;
-  for (int g = g_begin + wave; g < g_end; g += 4) {
-    const long long ug = (long long)u * a.n_groups_cap + g;
-    const uint8_t *kb = a.k_codes + ((long long)u * a.max_tokens + (long long)g * G + 4 * tb) * KROW +
-                        16 * cb * BITS / 8;
-    uint32_t kw[4][BITS / 2];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      if constexpr (BITS == 2) {
-        kw[r][0] = *reinterpret_cast<const uint32_t *>(kb + r * KROW);
-      } else {
-        const uint2 x = *reinterpret_cast<const uint2 *>(kb + r * KROW);
-        kw[r][0] = x.x;
-        kw[r][1] = x.y;
-      }
-    }
-    const uint8_t *vb = a.v_codes + ((ug * (G / 8) + oc) * D + 8 * cq) * BITS;
-    uint32_t vw[2 * BITS];
-    {
-      const uint4 x = *reinterpret_cast<const uint4 *>(vb);
-      vw[0] = x.x; vw[1] = x.y; vw[2] = x.z; vw[3] = x.w;
-      if constexpr (BITS == 4) {
-        const uint4 y = *reinterpret_cast<const uint4 *>(vb + 16);
-        vw[4] = y.x; vw[5] = y.y; vw[6] = y.z; vw[7] = y.w;
-      }
-    }
-    float sk[16], zk[16], sv[8], zv[8];
-    ld16(a.k_scale + ug * D + 16 * cb, sk);
-    ld16(a.k_zero + ug * D + 16 * cb, zk);
-    ld8(a.v_scale + (ug * (D / G) + jv) * G + 8 * oc, sv);
-    ld8(a.v_zero + (ug * (D / G) + jv) * G + 8 * oc, zv);
-
-    float qs[16], beta = 0.f;
-#pragma unroll
-    for (int c = 0; c < 16; ++c) {
-      qs[c] = qv[c] * sk[c];
-      beta += qv[c] * zk[c];
-    }
-    beta = xor_sum(xor_sum(xor_sum(beta, 1), 2), 4);
-
-    float s4[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float acc = 0.f;
-      if constexpr (BITS == 2) {
-        const uint32_t w = kw[r][0];
-        const uint32_t x = w & 0x33333333u, y = (w >> 2) & 0x33333333u;
-        // byte k of x: channels 4k, 4k+2 ; of y: 4k+1, 4k+3
-        f32x2_t f;
-        f = fp4x2_to_f32x2<0>(x); acc += qs[0] * f[0] + qs[2] * f[1];
-        f = fp4x2_to_f32x2<0>(y); acc += qs[1] * f[0] + qs[3] * f[1];
-        f = fp4x2_to_f32x2<1>(x); acc += qs[4] * f[0] + qs[6] * f[1];
-        f = fp4x2_to_f32x2<1>(y); acc += qs[5] * f[0] + qs[7] * f[1];
-        f = fp4x2_to_f32x2<2>(x); acc += qs[8] * f[0] + qs[10] * f[1];
-        f = fp4x2_to_f32x2<2>(y); acc += qs[9] * f[0] + qs[11] * f[1];
-        f = fp4x2_to_f32x2<3>(x); acc += qs[12] * f[0] + qs[14] * f[1];
-        f = fp4x2_to_f32x2<3>(y); acc += qs[13] * f[0] + qs[15] * f[1];
-      } else {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const uint32_t w = kw[r][i];
-          const uint32_t x = w & 0x0F0F0F0Fu, y = (w >> 4) & 0x0F0F0F0Fu;
-          const float *q8 = qs + 8 * i;
-          f32x2_t f;
-          f = fp8x2_to_f32x2<false>(x); acc += q8[0] * f[0] + q8[2] * f[1];
-          f = fp8x2_to_f32x2<false>(y); acc += q8[1] * f[0] + q8[3] * f[1];
-          f = fp8x2_to_f32x2<true>(x); acc += q8[4] * f[0] + q8[6] * f[1];
-          f = fp8x2_to_f32x2<true>(y); acc += q8[5] * f[0] + q8[7] * f[1];
-        }
-      }
-      acc = xor_sum(xor_sum(xor_sum(acc, 1), 2), 4);
-      s4[r] = acc + beta;
-    }
-    float mx = fmaxf(fmaxf(s4[0], s4[1]), fmaxf(s4[2], s4[3]));
-    mx = xor_max(xor_max(xor_max(mx, 8), 16), 32);
-    const bool need = mx > m_run + kRescaleSlack;
-    if (__any(need)) {
-      const float mnew = need ? mx : m_run;
-      const float al = m_run == kNegInf ? 0.f : fast_exp2(m_run - mnew);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) oacc[i] *= al;
-      l_run *= al;
-      z_run *= al;
-      m_run = mnew;
-    }
-    float p4[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      p4[r] = fast_exp2(s4[r] - m_run);
-      l_run += p4[r];
-    }
-    // hand the 32 probabilities to the P.V layout through LDS (same wave)
-    if (cb == 0) *reinterpret_cast<float4 *>(&sm.vs.p[wave][4 * tb]) = make_float4(p4[0], p4[1], p4[2], p4[3]);
-    __builtin_amdgcn_wave_barrier();
-    float p8[8];
-    {
-      const float4 x = *reinterpret_cast<const float4 *>(&sm.vs.p[wave][8 * oc]);
-      const float4 y = *reinterpret_cast<const float4 *>(&sm.vs.p[wave][8 * oc + 4]);
-      p8[0] = x.x; p8[1] = x.y; p8[2] = x.z; p8[3] = x.w;
-      p8[4] = y.x; p8[5] = y.y; p8[6] = y.z; p8[7] = y.w;
-    }
-    __builtin_amdgcn_wave_barrier();
-    float pp[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      pp[k] = p8[k] * sv[k];
-      z_run += p8[k] * zv[k];
-    }
-    if constexpr (BITS == 2) {
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const uint32_t w = vw[d];
-        const uint32_t x = w & 0x33333333u, y = (w >> 2) & 0x33333333u;
-        // bytes 0,1: channel 2d (tokens (0,2),(4,6) / (1,3),(5,7)); bytes 2,3: channel 2d+1
-        f32x2_t f;
-        float o0 = oacc[2 * d], o1 = oacc[2 * d + 1];
-        f = fp4x2_to_f32x2<0>(x); o0 += pp[0] * f[0] + pp[2] * f[1];
-        f = fp4x2_to_f32x2<0>(y); o0 += pp[1] * f[0] + pp[3] * f[1];
-        f = fp4x2_to_f32x2<1>(x); o0 += pp[4] * f[0] + pp[6] * f[1];
-        f = fp4x2_to_f32x2<1>(y); o0 += pp[5] * f[0] + pp[7] * f[1];
-        f = fp4x2_to_f32x2<2>(x); o1 += pp[0] * f[0] + pp[2] * f[1];
-        f = fp4x2_to_f32x2<2>(y); o1 += pp[1] * f[0] + pp[3] * f[1];
-        f = fp4x2_to_f32x2<3>(x); o1 += pp[4] * f[0] + pp[6] * f[1];
-        f = fp4x2_to_f32x2<3>(y); o1 += pp[5] * f[0] + pp[7] * f[1];
-        oacc[2 * d] = o0; oacc[2 * d + 1] = o1;
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t w = vw[e];
-        const uint32_t x = w & 0x0F0F0F0Fu, y = (w >> 4) & 0x0F0F0F0Fu;
-        f32x2_t f;
-        float o0 = oacc[e];
-        f = fp8x2_to_f32x2<false>(x); o0 += pp[0] * f[0] + pp[2] * f[1];
-        f = fp8x2_to_f32x2<false>(y); o0 += pp[1] * f[0] + pp[3] * f[1];
-        f = fp8x2_to_f32x2<true>(x); o0 += pp[4] * f[0] + pp[6] * f[1];
-        f = fp8x2_to_f32x2<true>(y); o0 += pp[5] * f[0] + pp[7] * f[1];
-        oacc[e] = o0;
-      }
+  // quantised groups: three register sets, two groups in flight
+  if (has_groups) {
+    int g = wr.g_begin;
+    while (true) {
+      load_valu_group<BITS>(r2, view, g + 2, g + 2 < wr.g_end);
+      valu_group<BITS>(r0, st, sm.vs, qv, L);
+      if (++g >= wr.g_end) break;
+      load_valu_group<BITS>(r0, view, g + 2, g + 2 < wr.g_end);
+      valu_group<BITS>(r1, st, sm.vs, qv, L);
+      if (++g >= wr.g_end) break;
+      load_valu_group<BITS>(r1, view, g + 2, g + 2 < wr.g_end);
+      valu_group<BITS>(r2, st, sm.vs, qv, L);
+      if (++g >= wr.g_end) break;
     }
   }
-  const float l = xor_sum(xor_sum(xor_sum(l_run, 8), 16), 32);
-  const float z = xor_sum(xor_sum(z_run, 16), 32);
+  for (int rc = wr.r_begin; rc < wr.r_end; ++rc) valu_rchunk(a, u, rc, st, sm.vs, qv, L);
+
+  const float l = xor_sum(xor_sum(xor_sum(st.l_run, 8), 16), 32);
+  const float z = xor_sum(xor_sum(st.z_run, 16), 32);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) oacc[i] = xor_sum(xor_sum(oacc[i], 16), 32) + z;
-  __syncthreads();   // p[] of every wave consumed before the merge buffer reuses it
-  if (oc == 0) {
-    float *dst = &sm.mg.o[wave][0][8 * cq];
-    *reinterpret_cast<float4 *>(dst) = make_float4(oacc[0], oacc[1], oacc[2], oacc[3]);
-    *reinterpret_cast<float4 *>(dst + 4) = make_float4(oacc[4], oacc[5], oacc[6], oacc[7]);
+  for (int i = 0; i < 8; ++i) st.oacc[i] = xor_sum(xor_sum(st.oacc[i], 16), 32) + z;
+  __syncthreads();   // every wave is done with the staging areas the merge buffer aliases
+  if (L.oc == 0) {
+    float *dst = &sm.mg.o[L.wave][0][8 * L.cq];
+    *reinterpret_cast<float4 *>(dst) = make_float4(st.oacc[0], st.oacc[1], st.oacc[2], st.oacc[3]);
+    *reinterpret_cast<float4 *>(dst + 4) = make_float4(st.oacc[4], st.oacc[5], st.oacc[6], st.oacc[7]);
   }
-  if (lane == 0) {
-    sm.mg.m[wave][0] = m_run;
-    sm.mg.l[wave][0] = l;
+  if (L.lane == 0) {
+    sm.mg.m[L.wave][0] = st.m_run;
+    sm.mg.l[L.wave][0] = l;
   }
   merge_and_store<1>(sm.mg, a, u, split);
   finish_unit(a, u, &sm.mg.last);
@@ -1133,38 +1152,35 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
 
 namespace {
 
-template <int BITS, int NHB>
-void *gqa_kernel() {
-  return reinterpret_cast<void *>(&decode_gqa_kernel<BITS, NHB>);
+// Kernel variants: 0 = MHA (VALU), 1..4 = GQA with that many blocks of 4
+// query heads.
+void *kernel_fn(int bits, int variant) {
+  const bool b4 = bits == 4;
+  switch (variant) {
+    case 0: return b4 ? (void *)&decode_mha_kernel<4> : (void *)&decode_mha_kernel<2>;
+    case 1: return b4 ? (void *)&decode_gqa_kernel<4, 1> : (void *)&decode_gqa_kernel<2, 1>;
+    case 2: return b4 ? (void *)&decode_gqa_kernel<4, 2> : (void *)&decode_gqa_kernel<2, 2>;
+    case 3: return b4 ? (void *)&decode_gqa_kernel<4, 3> : (void *)&decode_gqa_kernel<2, 3>;
+    default: return b4 ? (void *)&decode_gqa_kernel<4, 4> : (void *)&decode_gqa_kernel<2, 4>;
+  }
 }
 
-// Occupancy of a GQA kernel variant on the current device: resident
-// workgroups per compute unit and the number of compute units, cached per
-// device and variant.
+// Occupancy of a kernel variant on the current device: resident workgroups
+// per compute unit and the number of compute units, cached per device and
+// variant.
 struct Residency {
   int per_cu, cus;
 };
 
-Residency residency(int bits, int nhb) {
-  static int cache[16][2][4][2];   // 0 = not yet queried
+Residency residency(int bits, int variant) {
+  static int cache[16][2][5][2];   // 0 = not yet queried
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
-  const int d = dev & 15, bi = bits == 4 ? 1 : 0;
-  int *slot = cache[d][bi][nhb - 1];
+  int *slot = cache[dev & 15][bits == 4 ? 1 : 0][variant];
   Residency r{__atomic_load_n(&slot[0], __ATOMIC_RELAXED), __atomic_load_n(&slot[1], __ATOMIC_RELAXED)};
   if (r.per_cu > 0 && r.cus > 0) return r;
-  void *fn = nullptr;
-  switch ((bi << 2) | (nhb - 1)) {
-    case 0: fn = gqa_kernel<2, 1>(); break;
-    case 1: fn = gqa_kernel<2, 2>(); break;
-    case 2: fn = gqa_kernel<2, 3>(); break;
-    case 3: fn = gqa_kernel<2, 4>(); break;
-    case 4: fn = gqa_kernel<4, 1>(); break;
-    case 5: fn = gqa_kernel<4, 2>(); break;
-    case 6: fn = gqa_kernel<4, 3>(); break;
-    default: fn = gqa_kernel<4, 4>(); break;
-  }
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&r.per_cu, fn, 256, 0) != hipSuccess || r.per_cu < 1)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&r.per_cu, kernel_fn(bits, variant), 256, 0) !=
+          hipSuccess || r.per_cu < 1)
     r.per_cu = 1;
   if (hipDeviceGetAttribute(&r.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || r.cus < 1)
     r.cus = 256;
@@ -1204,6 +1220,10 @@ int choose_wpu(int bits, const DecodeArgs &a, int slots) {
   if (cap < 1) cap = 1;
   if (cap > a.n_split) cap = a.n_split;   // workspace capacity in partials per unit
   if (cap > 256) cap = 256;
+  if (const char *env = getenv("KIVI_WPU")) {   // fixed count, for sweeps
+    const long long v = atoll(env);
+    if (v >= 1) return (int)(v < cap ? v : cap);
+  }
   int best = 1;
   double best_t = 1e30;
   for (int w = 1; w <= cap; ++w) {
@@ -1217,38 +1237,21 @@ int choose_wpu(int bits, const DecodeArgs &a, int slots) {
 }  // namespace
 
 hipError_t launch_decode(int bits, const DecodeArgs &a_in, hipStream_t s) {
-  const dim3 block(256);
-  if (a_in.qpk == 1) {
-    const dim3 grid(a_in.n_split, a_in.n_units);
-    if (bits == 2)
-      hipLaunchKernelGGL((decode_valu_kernel<2>), grid, block, 0, s, a_in);
-    else
-      hipLaunchKernelGGL((decode_valu_kernel<4>), grid, block, 0, s, a_in);
-    return hipGetLastError();
-  }
-  const int nhb = (a_in.qpk + 3) / 4;
+  const int variant = a_in.qpk == 1 ? 0 : (a_in.qpk + 3) / 4;
   DecodeArgs a = a_in;
-  const Residency res = residency(bits, nhb);
-  a.n_split = choose_wpu(bits, a_in, res.per_cu * res.cus);   // a_in.n_split: capacity
+  const Residency res = residency(bits, variant);
+  const int slots = res.per_cu * res.cus;
+  a.n_split = choose_wpu(bits, a_in, slots);   // a_in.n_split: capacity
   a.cus = res.cus;
-  rank_weights(res.per_cu, a.rank_w);
-  const dim3 grid(a.n_units, a.n_split);
-#define KIVI_LAUNCH(BITS)                                                                   \
-  do {                                                                                      \
-    if (nhb == 1)                                                                           \
-      hipLaunchKernelGGL((decode_gqa_kernel<BITS, 1>), grid, block, 0, s, a);              \
-    else if (nhb == 2)                                                                      \
-      hipLaunchKernelGGL((decode_gqa_kernel<BITS, 2>), grid, block, 0, s, a);              \
-    else if (nhb == 3)                                                                      \
-      hipLaunchKernelGGL((decode_gqa_kernel<BITS, 3>), grid, block, 0, s, a);              \
-    else                                                                                    \
-      hipLaunchKernelGGL((decode_gqa_kernel<BITS, 4>), grid, block, 0, s, a);              \
-  } while (0)
-  if (bits == 2)
-    KIVI_LAUNCH(2);
-  else
-    KIVI_LAUNCH(4);
-#undef KIVI_LAUNCH
+  // rank weights only mean something when every workgroup is resident at once
+  if ((long long)a.n_split * a.n_units <= slots) {
+    rank_weights(res.per_cu, a.rank_w);
+  } else {
+    for (int i = 0; i < 4; ++i) a.rank_w[i] = 1;
+  }
+  const dim3 grid(a.n_units, a.n_split), block(256);
+  hipLaunchKernelGGL(reinterpret_cast<void (*)(DecodeArgs)>(kernel_fn(bits, variant)), grid, block,
+                     0, s, a);
   return hipGetLastError();
 }
 

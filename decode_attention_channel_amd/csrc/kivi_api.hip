@@ -70,23 +70,6 @@ int max_splits(const kivi_geom *g) {
   return (ng + kivi::kMinGroupsPerSplit - 1) / kivi::kMinGroupsPerSplit + 1;
 }
 
-// Groups per quantised split.  Enough workgroups to cover the chip several
-// times over, each split a multiple of the 4 waves of a workgroup.  The
-// environment variable KIVI_GROUPS_PER_SPLIT overrides it (sweeps).
-int choose_gps(long long units, int n_groups) {
-  const char *env = getenv("KIVI_GROUPS_PER_SPLIT");
-  if (env) {
-    int v = atoi(env);
-    if (v >= kivi::kMinGroupsPerSplit) return v;
-  }
-  const long long target_wg = 2048;  // 256 CUs x 8
-  long long gps = (units * (long long)n_groups + target_wg - 1) / target_wg;
-  gps = (gps + 3) / 4 * 4;
-  if (gps < 8) gps = 8;
-  if (gps > 64) gps = 64;
-  return (int)gps;
-}
-
 // Quantise the G oldest residual tokens (ring slots res_start..+G-1, which
 // are contiguous because res_start is a multiple of G) into group n_q/G and
 // advance the counters.  The caller has validated everything.
@@ -162,16 +145,8 @@ kivi_status enqueue_attend(const kivi_geom *g, const kivi_cache *c, const uint16
   a.n_units = (int)units_of(g);
   a.n_groups = c->n_q / g->group;
   a.n_res = c->n_res; a.res_start = c->res_start;
-  if (g->q_per_kv == 1) {
-    // MHA: fixed-size splits of the quantised groups plus one residual split
-    a.gps = choose_gps(units_of(g), a.n_groups);
-    a.n_split_q = (a.n_groups + a.gps - 1) / a.gps;
-    a.n_split = a.n_split_q + (c->n_res > 0 ? 1 : 0);
-    if (a.n_split > max_splits(g)) return KIVI_E_WORKSPACE;   // cannot happen: gps >= 4
-  } else {
-    // GQA: the launcher picks the workgroups per unit; pass the capacity
-    a.n_split = max_splits(g);
-  }
+  // the launcher picks the workgroups per unit; pass the workspace capacity
+  a.n_split = max_splits(g);
   return hip_status(kivi::launch_decode(g->bits, a, s));
 }
 

@@ -12,7 +12,7 @@ namespace kivi {
 constexpr int kHeadDim = 128;      // supported head_dim
 constexpr int kGroup = 32;         // supported group size G
 constexpr int kPartStride = 132;   // floats per split partial: m, l, pad, pad, o[128]
-constexpr int kMinGroupsPerSplit = 4;
+constexpr int kMinGroupsPerSplit = 4;   // sizes the workspace: NG/4 + 1 partials per unit
 
 // One launch of the group quantiser: `n_groups` groups of G tokens for each
 // of `n_units` units.  Source token i of local group gl of unit u is row
@@ -62,10 +62,8 @@ struct DecodeArgs {
   int n_units;
   int n_groups;       // quantised groups in the cache (n_q / G)
   int n_res, res_start;
-  int gps;            // groups per quantised split
-  int n_split_q;      // quantised splits per unit
-  int n_split;        // n_split_q + (n_res > 0); GQA: workgroups per unit
-  // GQA byte shares: workgroup (unit u, split s) has linear index s*n_units+u
+  int n_split;        // workgroups per unit (the host passes the workspace capacity)
+  // byte shares: workgroup (unit u, split s) has linear index s*n_units+u
   // and co-residency rank min(index / cus, 3) on its compute unit; its share
   // of the unit's bytes is proportional to rank_w[rank]
   int cus;
