@@ -77,6 +77,9 @@ def lib():
         L.kivio_attend_row.restype = None
         L.kivio_attention_unit.argtypes = [G, C, ctypes.c_long, P, ctypes.c_float, P]
         L.kivio_attention_unit.restype = ctypes.c_int
+        L.kivio_attention_dense_unit.argtypes = [G, P, P, ctypes.c_int, ctypes.c_int,
+                                                 ctypes.c_long, P, ctypes.c_float, P]
+        L.kivio_attention_dense_unit.restype = ctypes.c_int
         L.kivio_bytes_per_token.argtypes = [ctypes.c_int] * 7 + [P]
         L.kivio_bytes_per_token.restype = None
         _lib = L
@@ -242,6 +245,26 @@ def attention(c: Cache, q: np.ndarray, scale: float, units=None,
         if lib().kivio_attention_unit(ctypes.byref(gc), ctypes.byref(cc), int(u), _p(q),
                                       scale, _p(out)) != 0:
             raise ValueError("empty cache")
+    return out
+
+
+def attention_dense(g: Geom, k: np.ndarray, v: np.ndarray, seq_len: int, q: np.ndarray,
+                    scale: float, units=None, out: np.ndarray | None = None) -> np.ndarray:
+    """Decode attention over an uncompressed bf16 cache (the baseline).
+    k, v: uint16 [B][H][T][D] (the first seq_len tokens are attended);
+    q: uint16 [B][H*QPK][D]; returns float32 [B][H*QPK][D]."""
+    k = np.ascontiguousarray(k, np.uint16)
+    v = np.ascontiguousarray(v, np.uint16)
+    q = np.ascontiguousarray(q, np.uint16)
+    assert k.shape == v.shape and k.shape[:2] == (g.batch, g.kv_heads) and k.shape[3] == g.head_dim
+    assert q.shape == (g.batch, g.kv_heads * g.q_per_kv, g.head_dim)
+    if out is None:
+        out = np.zeros(q.shape, np.float32)
+    gc = g._c()
+    for u in (range(g.units) if units is None else units):
+        if lib().kivio_attention_dense_unit(ctypes.byref(gc), _p(k), _p(v), int(seq_len),
+                                            k.shape[2], int(u), _p(q), scale, _p(out)) != 0:
+            raise ValueError("seq_len out of range")
     return out
 
 

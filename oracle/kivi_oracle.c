@@ -22,7 +22,9 @@
  *  - a bf16 residual of the most recent tokens, flushed G at a time into a
  *    new group (catalog record, KV bytes basis);
  *  - decode attention over the dequantised history plus the residual, in
- *    double precision (exact softmax attention; a plain definition);
+ *    double precision (exact softmax attention; a plain definition), and
+ *    the same attention over an uncompressed bf16 cache, the baseline the
+ *    pages compare against;
  *  - the KV-bytes-per-token arithmetic of the catalog record (KV bytes basis
  *    and notes) and of the news article (memory-math paragraph).
  *
@@ -327,6 +329,38 @@ int kivio_attention(const kivio_geom *g, const kivio_cache *c, const uint16_t *q
                     float scale, float *out) {
   for (size_t u = 0; u < unit_count(g); ++u)
     if (kivio_attention_unit(g, c, (long)u, q, scale, out) != 0) return -1;
+  return 0;
+}
+
+/* Decode attention over an uncompressed bf16 cache, the baseline the pages
+ * measure KIVI against (card: "compared with FP16"; catalog record,
+ * Methodology: throughput gain over the FP16 cache).  k, v: bf16
+ * [B][H][stride][D]; the first seq_len tokens of each unit are attended.
+ * q: bf16 [B][H*QPK][D]; out: float [B][H*QPK][D], only the QPK rows of unit
+ * u = b*H + h are written.  Plain softmax attention in doubles.  Returns 0,
+ * -1 when seq_len is out of [1, stride]. */
+int kivio_attention_dense_unit(const kivio_geom *g, const uint16_t *k, const uint16_t *v,
+                               int seq_len, int stride, long unit, const uint16_t *q,
+                               float scale, float *out) {
+  const int D = g->head_dim, QPK = g->q_per_kv;
+  if (seq_len < 1 || seq_len > stride) return -1;
+  double *kk = (double *)malloc((size_t)seq_len * D * sizeof(double));
+  double *vv = (double *)malloc((size_t)seq_len * D * sizeof(double));
+  double qd[256], od[256];
+  const size_t base = (size_t)unit * stride * D;
+  for (size_t i = 0; i < (size_t)seq_len * D; ++i) {
+    kk[i] = bf16_to_float(k[base + i]);
+    vv[i] = bf16_to_float(v[base + i]);
+  }
+  const long b = unit / g->kv_heads, h = unit % g->kv_heads;
+  for (int j = 0; j < QPK; ++j) {
+    const size_t row = ((size_t)b * g->kv_heads * QPK + (size_t)h * QPK + (size_t)j) * D;
+    for (int ch = 0; ch < D; ++ch) qd[ch] = bf16_to_float(q[row + ch]);
+    kivio_attend_row(qd, kk, vv, seq_len, D, (double)scale, od);
+    for (int ch = 0; ch < D; ++ch) out[row + ch] = (float)od[ch];
+  }
+  free(kk);
+  free(vv);
   return 0;
 }
 
