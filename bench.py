@@ -133,6 +133,139 @@ def cpu_baseline(w, seed, units_wanted=256):
     }
 
 
+def _fill_random_cache(cache, n_q, n_res, gen):
+    """Seeded synthetic cache contents for timing: uniform codes, positive
+    scales, normal zeros and residual."""
+    cache.k_codes.random_(0, 256, generator=gen)
+    cache.v_codes.random_(0, 256, generator=gen)
+    for t in (cache.k_scale, cache.v_scale):
+        t.uniform_(0.01, 0.5, generator=gen)
+    for t in (cache.k_zero, cache.v_zero):
+        t.normal_(generator=gen)
+    for t in (cache.k_res, cache.v_res):
+        t.normal_(generator=gen)
+    cache.set_counters(n_q, n_res, 0)
+
+
+def _time_launches(fns, reps):
+    """Mean duration of each launch from HIP event pairs, the GPU kept busy
+    ahead of the timed launches."""
+    import torch
+    for f in fns:
+        f()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps * len(fns))]
+    for f in fns[:2]:
+        f()
+    for i, (e0, e1) in enumerate(ev):
+        e0.record()
+        fns[i % len(fns)]()
+        e1.record()
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in ev) / len(ev) / 1e3
+
+
+def batch_sweep(args):
+    """Memory-wall sweep (Llama-2-13B-shaped MHA: 40 layers x 40 heads, 4096
+    tokens): decode-attention time per layer vs batch for the 2-bit KIVI cache
+    and for the uncompressed bf16 baseline, each up to the largest batch whose
+    40-layer cache fits in free HBM.  Every batch allocates all 40 layer caches
+    (so the largest one shows that it fits) and times launches rotating over
+    them."""
+    import torch
+
+    import synth
+    from decode_attention_channel_amd import kivi
+
+    w = synth.WORKLOADS[args.workload if args.workload != "llama3-8b-gqa-8k"
+                        else "llama2-13b-mha-wall"]
+    dev = torch.device("cuda", 0)
+    D, G, R, S, L = w.head_dim, w.group, w.residual, w.seq_len, w.layers
+    n_q = G * ((S - R) // G)
+    n_res = S - n_q
+    T = n_q   # the quantised history holds exactly the prefill's groups
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(args.seed)
+
+    def kivi_geom(B):
+        return kivi.Geom(B, w.kv_heads, w.q_per_kv, bits=w.bits, max_tokens=T)
+
+    def dense_geom(B):
+        return kivi.Geom(B, w.kv_heads, w.q_per_kv, bits=w.bits, max_tokens=S)
+
+    per_seq_kivi = sum(kivi.cache_layout(kivi_geom(1))) * L
+    per_seq_bf16 = w.kv_heads * S * D * 2 * 2 * L
+    torch.zeros(1, device=dev).add_(1)   # runtime and context set up before measuring
+    torch.cuda.synchronize()
+    free0, total = torch.cuda.mem_get_info()
+    headroom = 8 << 30   # workspace, q/out, allocator slack
+    bmax_kivi = int((free0 - headroom) // per_seq_kivi)
+    bmax_bf16 = int((free0 - headroom) // per_seq_bf16)
+
+    def batches(bmax):
+        out, b = [], 1
+        while b < bmax:
+            out.append(b)
+            b *= 2
+        return out + [bmax]
+
+    rows = {}
+    for B in batches(bmax_kivi):
+        g = kivi_geom(B)
+        n_layers = L
+        caches = [kivi.Cache(g, dev) for _ in range(n_layers)]
+        for c in caches:
+            _fill_random_cache(c, n_q, n_res, gen)
+        ws = kivi.Workspace(g, dev)
+        q = torch.randn(B, w.q_heads, D, device=dev, generator=gen).to(torch.bfloat16)
+        out = torch.empty(B, w.q_heads, D, device=dev)
+        st = [kivi.LayerStepper(g, c, ws, q, out) for c in caches]
+        t = _time_launches([x.attend for x in st], max(2, 40 // n_layers))
+        byt = attn_bytes(synth.Workload(w.name, B, w.kv_heads, w.q_per_kv, S, w.bits, L, 3, 8.0),
+                         n_q, n_res)
+        rows.setdefault(B, {})["kivi"] = {"us_per_layer": t * 1e6, "tokens_s": B / (t * L),
+                                          "hbm_gbps": byt / t / 1e9, "layers_resident": n_layers}
+        del st, caches, ws, q, out
+        torch.cuda.empty_cache()
+    for B in batches(bmax_bf16):
+        g = dense_geom(B)
+        n_layers = L
+        kv = []
+        for _ in range(n_layers):
+            k = torch.empty(B, w.kv_heads, S, D, dtype=torch.bfloat16, device=dev)
+            v = torch.empty_like(k)
+            k.normal_(generator=gen)
+            v.normal_(generator=gen)
+            kv.append((k, v))
+        ws = kivi.Workspace(g, dev)
+        q = torch.randn(B, w.q_heads, D, device=dev, generator=gen).to(torch.bfloat16)
+        out = torch.empty(B, w.q_heads, D, device=dev)
+        fns = [lambda k=k, v=v: kivi.dense_decode_attention(g, k, v, S, q, out=out, ws=ws)
+               for k, v in kv]
+        t = _time_launches(fns, max(2, 40 // n_layers))
+        byt = B * w.kv_heads * S * D * 4 + B * w.q_heads * D * 6
+        rows.setdefault(B, {})["bf16"] = {"us_per_layer": t * 1e6, "tokens_s": B / (t * L),
+                                          "hbm_gbps": byt / t / 1e9, "layers_resident": n_layers}
+        del fns, kv, ws, q, out
+        torch.cuda.empty_cache()
+    best_kivi = max(r["kivi"]["tokens_s"] for r in rows.values() if "kivi" in r)
+    best_bf16 = max(r["bf16"]["tokens_s"] for r in rows.values() if "bf16" in r)
+    res = {
+        "metric": "decode-attention tokens/s vs batch at the memory wall", "unit": "tokens/s",
+        "workload": w.name, "layers": L, "kv_heads": w.kv_heads, "context": S, "bits": w.bits,
+        "hbm_free_bytes": free0, "hbm_total_bytes": total,
+        "bytes_per_sequence": {"kivi": per_seq_kivi, "bf16": per_seq_bf16},
+        "max_batch": {"kivi": bmax_kivi, "bf16": bmax_bf16,
+                      "ratio": bmax_kivi / max(bmax_bf16, 1)},
+        "best_tokens_s": {"kivi": best_kivi, "bf16": best_bf16, "ratio": best_kivi / best_bf16},
+        "rows": [{"batch": B, **rows[B]} for B in sorted(rows)],
+        "data": "synthetic (seeded random cache contents; timing only)",
+        "paper_context": "up to 4x batch and 2.35x-3.47x throughput vs FP16 (Llama-2-7B, one "
+                         "A100 80GB, whole model; not comparable, quoted as context)",
+    }
+    print(json.dumps(res))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -146,6 +279,9 @@ def main():
                     help="run only N decode steps after warmup, no reporting (profilers)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 5 times (scales HBM byte counters)")
+    ap.add_argument("--batch-sweep", action="store_true",
+                    help="memory-wall sweep: KIVI 2-bit vs bf16 decode attention vs batch "
+                         "(Llama-2-13B-shaped MHA); prints its own JSON line")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported on this build "
@@ -158,6 +294,9 @@ def main():
     from decode_attention_channel_amd import kivi
 
     torch.cuda.set_device(0)
+    if args.batch_sweep:
+        batch_sweep(args)
+        return
     if args.copy_calibration:
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)

@@ -1209,26 +1209,34 @@ void rank_weights(int per_cu, int (&w)[4]) {
   }
 }
 
-// Workgroups per unit: the count that minimises (rounds of resident
-// workgroups) / (workgroups per unit), i.e. the finishing time of equal
-// shares, with at least two groups' worth of bytes per wave and no more
-// partials than the workspace holds.
+// Workgroups per unit.  Cost model in the work units of wave_work (KiB):
+// a workgroup that takes K/w of a unit's cost K also pays a fixed kWgFixed
+// (prologue loads, merge, partial stores, arrival count).  When all U*w
+// workgroups are resident at once the launch takes one workgroup time;
+// beyond that the dispatcher refills freed slots, and the launch takes about
+// (U*w/slots + 1/2) workgroup times (half a workgroup of tail).  The count
+// is capped so that every wave has at least two groups' worth of bytes and
+// the workspace holds the partials.  MI355X sweeps: 6 per unit at the 8K GQA
+// workload (one round), 1-2 at the 13B-shaped MHA memory wall (batch
+// 64-316, many rounds).  KIVI_WPU fixes the count (sweeps).
 int choose_wpu(int bits, const DecodeArgs &a, int slots) {
+  constexpr double kWgFixed = 40.0;
   const long long n_rc = (a.n_res + G - 1) / G;
   const long long total = (long long)a.n_groups * (bits + 2) + n_rc * 16;
   long long cap = total / (4 * 2 * (bits + 2));
   if (cap < 1) cap = 1;
   if (cap > a.n_split) cap = a.n_split;   // workspace capacity in partials per unit
   if (cap > 256) cap = 256;
-  if (const char *env = getenv("KIVI_WPU")) {   // fixed count, for sweeps
+  if (const char *env = getenv("KIVI_WPU")) {
     const long long v = atoll(env);
     if (v >= 1) return (int)(v < cap ? v : cap);
   }
   int best = 1;
-  double best_t = 1e30;
+  double best_t = 1e300;
   for (int w = 1; w <= cap; ++w) {
-    const long long rounds = ((long long)a.n_units * w + slots - 1) / slots;
-    const double t = (double)rounds / w;
+    const double rounds = (double)a.n_units * w / slots;
+    const double t_wg = (double)total / w + kWgFixed;
+    const double t = rounds <= 1.0 ? t_wg : (rounds + 0.5) * t_wg;
     if (t < best_t * 0.999) { best_t = t; best = w; }
   }
   return best;

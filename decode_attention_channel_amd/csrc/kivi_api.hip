@@ -33,6 +33,8 @@ kivi_status check_geom(const kivi_geom *g) {
   if (g->q_per_kv > 16) return KIVI_E_UNSUPPORTED;
   if ((long long)g->batch * g->kv_heads > 65535) return KIVI_E_UNSUPPORTED;   // grid.y
   if (g->max_tokens % g->group != 0) return KIVI_E_UNSUPPORTED;
+  // per-unit buffers are addressed with 32-bit offsets
+  if (g->max_tokens > (1 << 24)) return KIVI_E_UNSUPPORTED;
   // keep every byte offset of every buffer inside 2^62
   const double units = (double)g->batch * g->kv_heads;
   if (units * ((double)g->max_tokens + g->residual + g->group) * g->head_dim * 8.0 > 4.0e18)
@@ -128,7 +130,7 @@ kivi_status check_attend_args(const kivi_geom *g, const kivi_cache *c, const uin
 // into its ring slot by the kernel) instead of from the ring.
 kivi_status enqueue_attend(const kivi_geom *g, const kivi_cache *c, const uint16_t *k_new,
                            const uint16_t *v_new, const uint16_t *q, float *out,
-                           float softmax_scale, void *ws, hipStream_t s) {
+                           float softmax_scale, void *ws, hipStream_t s, int slots = 0) {
   kivi::DecodeArgs a{};
   a.k_codes = c->k_codes; a.k_scale = c->k_scale; a.k_zero = c->k_zero;
   a.v_codes = c->v_codes; a.v_scale = c->v_scale; a.v_zero = c->v_zero;
@@ -141,7 +143,7 @@ kivi_status enqueue_attend(const kivi_geom *g, const kivi_cache *c, const uint16
   a.qscale = softmax_scale * 1.4426950408889634f;
   a.kv_heads = g->kv_heads; a.qpk = g->q_per_kv; a.max_tokens = g->max_tokens;
   a.n_groups_cap = g->max_tokens / g->group;
-  a.slots = g->residual + g->group;
+  a.slots = slots > 0 ? slots : g->residual + g->group;
   a.n_units = (int)units_of(g);
   a.n_groups = c->n_q / g->group;
   a.n_res = c->n_res; a.res_start = c->res_start;
@@ -316,6 +318,28 @@ kivi_status kivi_decode_step(const kivi_geom *g, kivi_cache *c, const uint16_t *
     return st;
   c->n_res = next.n_res;
   return KIVI_OK;
+}
+
+kivi_status kivi_dense_decode_attention(const kivi_geom *g, const uint16_t *k, const uint16_t *v,
+                                        int32_t seq_len, const uint16_t *q, float *out,
+                                        float softmax_scale, void *ws, size_t ws_bytes,
+                                        void *stream) {
+  kivi_status st = check_geom(g);
+  if (st != KIVI_OK) return st;
+  if (!k || !v) return KIVI_E_NULL;
+  if ((st = check_attend_args(g, nullptr, q, out, softmax_scale, ws, ws_bytes)) != KIVI_OK)
+    return st;
+  if (seq_len < 1 || seq_len > g->max_tokens) return KIVI_E_SEQLEN;
+  // the dense cache is read as a residual of seq_len tokens in a "ring" of
+  // max_tokens slots starting at slot 0; there is no quantised history
+  kivi_cache c{};
+  c.k_res = const_cast<uint16_t *>(k);
+  c.v_res = const_cast<uint16_t *>(v);
+  c.n_q = 0;
+  c.n_res = seq_len;
+  c.res_start = 0;
+  return enqueue_attend(g, &c, nullptr, nullptr, q, out, softmax_scale, ws, (hipStream_t)stream,
+                        g->max_tokens);
 }
 
 }  // extern "C"

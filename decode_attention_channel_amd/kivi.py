@@ -24,7 +24,8 @@ STATUS = {
 EXPORTS = (
     "kivi_cache_layout", "kivi_decode_workspace_size", "kivi_quantize_prefill",
     "kivi_append_token", "kivi_flush_residual", "kivi_decode_attention",
-    "kivi_decode_step", "kivi_status_string", "kivi_last_hip_error",
+    "kivi_decode_step", "kivi_dense_decode_attention", "kivi_status_string",
+    "kivi_last_hip_error",
 )
 BUFFERS = ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero", "k_res", "v_res")
 
@@ -65,9 +66,11 @@ def _load():
     lib.kivi_decode_attention.argtypes = [G, C, P, P, ctypes.c_float, P, ctypes.c_size_t, P]
     lib.kivi_decode_step.argtypes = [G, C, P, P, P, P, ctypes.c_float, P, ctypes.c_size_t,
                                      ctypes.POINTER(ctypes.c_int32), P]
+    lib.kivi_dense_decode_attention.argtypes = [G, P, P, ctypes.c_int32, P, P, ctypes.c_float, P,
+                                                ctypes.c_size_t, P]
     for f in ("kivi_cache_layout", "kivi_decode_workspace_size", "kivi_quantize_prefill",
               "kivi_append_token", "kivi_flush_residual", "kivi_decode_attention",
-              "kivi_decode_step"):
+              "kivi_decode_step", "kivi_dense_decode_attention"):
         getattr(lib, f).restype = ctypes.c_int
     lib.kivi_status_string.argtypes = [ctypes.c_int]
     lib.kivi_status_string.restype = ctypes.c_char_p
@@ -260,6 +263,31 @@ def decode_step(g: Geom, c: Cache, k_new: torch.Tensor, v_new: torch.Tensor, q: 
                                  ctypes.byref(flushed), _stream()),
            "kivi_decode_step")
     return out, flushed.value
+
+
+def dense_decode_attention(g: Geom, k: torch.Tensor, v: torch.Tensor, seq_len: int,
+                           q: torch.Tensor, out: torch.Tensor | None = None,
+                           softmax_scale: float | None = None, ws: Workspace | None = None
+                           ) -> torch.Tensor:
+    """Baseline attention over an uncompressed cache: k, v bf16
+    [B][H][g.max_tokens][D], first seq_len tokens; q bf16 [B][H*QPK][D] ->
+    fp32 [B][H*QPK][D]."""
+    shape = (g.batch, g.q_heads, g.head_dim)
+    kv_shape = (g.batch, g.kv_heads, g.max_tokens, g.head_dim)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = Workspace(g, q.device)
+    scale = 1.0 / math.sqrt(g.head_dim) if softmax_scale is None else float(softmax_scale)
+    _check(_lib.kivi_dense_decode_attention(ctypes.byref(g.c()),
+                                            _ptr(k, torch.bfloat16, kv_shape, "k"),
+                                            _ptr(v, torch.bfloat16, kv_shape, "v"), int(seq_len),
+                                            _ptr(q, torch.bfloat16, shape, "q"),
+                                            _ptr(out, torch.float32, shape, "out"), scale,
+                                            ctypes.c_void_p(ws.buf.data_ptr()), ws.nbytes,
+                                            _stream()),
+           "kivi_dense_decode_attention")
+    return out
 
 
 class LayerStepper:

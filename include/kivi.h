@@ -36,7 +36,7 @@
  *    when a launch fails; kivi_last_hip_error() then gives the hipError_t.
  *  - Supported set (v1): bits in {2,4}; group == 32; head_dim == 128;
  *    residual a multiple of group with 0 <= residual <= 4096;
- *    1 <= q_per_kv <= 16; max_tokens a multiple of group;
+ *    1 <= q_per_kv <= 16; max_tokens a multiple of group, at most 2^24;
  *    batch, kv_heads >= 1 with batch * kv_heads <= 65535.  Anything else:
  *    KIVI_E_UNSUPPORTED (or KIVI_E_GEOMETRY for non-positive sizes).
  *  - The whole batch moves in lockstep: one (n_q, n_res, res_start) triple
@@ -242,6 +242,26 @@ kivi_status kivi_decode_step(const kivi_geom *geom, kivi_cache *cache,
                              const uint16_t *q, float *out, float softmax_scale,
                              void *ws, size_t ws_bytes, int32_t *flushed,
                              void *stream);
+
+/* Baseline: decode attention over an uncompressed bf16 KV cache, the
+ * reference point of the pages' speed and memory claims ([card]: compared
+ * with the FP16 cache; [record] Methodology: throughput over the FP16
+ * baseline).  Same attention as kivi_decode_attention (no mask, fp32
+ * accumulation, consecutive query heads per kv head), over the first
+ * seq_len tokens of each (sequence, kv head).
+ * geom: batch, kv_heads, q_per_kv and head_dim as usual; max_tokens is the
+ *      token capacity T of the dense cache; bits, group and residual must be
+ *      a supported combination but do not affect the result.
+ * k, v: device bf16 [B][H][T][D], read only.  1 <= seq_len <= T.
+ * q, out, softmax_scale, ws, ws_bytes: as for kivi_decode_attention (the
+ *      workspace size is kivi_decode_workspace_size of the same geom).
+ * Errors: KIVI_E_NULL, KIVI_E_GEOMETRY, KIVI_E_UNSUPPORTED, KIVI_E_SEQLEN,
+ *         KIVI_E_WORKSPACE, KIVI_E_HIP. */
+kivi_status kivi_dense_decode_attention(const kivi_geom *geom, const uint16_t *k,
+                                        const uint16_t *v, int32_t seq_len,
+                                        const uint16_t *q, float *out,
+                                        float softmax_scale, void *ws, size_t ws_bytes,
+                                        void *stream);
 
 /* Static description of a status code (never NULL). */
 const char *kivi_status_string(kivi_status status);

@@ -20,7 +20,7 @@ def _declared():
 
 def test_exports_every_declared_function():
     names = _declared()
-    assert len(names) == 9
+    assert len(names) == 10
     lib = ctypes.CDLL(kivi.library_path())
     for n in names:
         assert hasattr(lib, n), n
@@ -142,6 +142,27 @@ def test_decode_step_validation_before_any_device_work():
     # nothing was enqueued and no counter moved on any error
     assert (c.n_q, c.n_res, c.res_start) == (1024, 159, 0)
     assert flushed.value == 7
+
+
+def test_dense_attention_validation_before_any_device_work():
+    g = _g().c()
+    fake = ctypes.c_void_p(0x2000)
+    ws_need = kivi.workspace_size(_g())
+
+    def dense(k=fake, v=fake, n=100, q=fake, out=fake, scale=0.1, ws=fake, nbytes=ws_need):
+        return _call("kivi_dense_decode_attention", ctypes.byref(g), k, v, n, q, out,
+                     ctypes.c_float(scale), ws, nbytes, None)
+
+    assert dense(k=None) == 1 and dense(v=None) == 1 and dense(q=None) == 1
+    assert dense(out=None) == 1
+    assert dense(n=0) == 4 and dense(n=1025) == 4
+    assert dense(ws=None) == 7 and dense(nbytes=ws_need - 1) == 7
+    assert dense(scale=float("nan")) == 2
+    assert _call("kivi_dense_decode_attention", None, fake, fake, 10, fake, fake,
+                 ctypes.c_float(0.1), fake, ws_need, None) == 1
+    big = _g(max_tokens=(1 << 24) + 32).c()
+    assert _call("kivi_dense_decode_attention", ctypes.byref(big), fake, fake, 10, fake, fake,
+                 ctypes.c_float(0.1), fake, ws_need, None) == 3
 
 
 def test_status_strings():
