@@ -27,6 +27,7 @@ struct QuantizeArgs {
   int max_tokens, n_groups_cap;  // T, NG
   uint8_t *k_codes; float *k_scale, *k_zero;
   uint8_t *v_codes; float *v_scale, *v_zero;
+  int gpw;   // groups per workgroup (set by the launcher)
 };
 hipError_t launch_quantize(int bits, const QuantizeArgs &a, hipStream_t s);
 

@@ -10,17 +10,15 @@
 //     s = (max - min) / L ;  inv = s >= FLT_MIN ? 1 / s : 0 ;
 //     code = clamp(rint((x - min) * inv), 0, L) ;  scale = s, zero = min.
 //
-// One workgroup of 256 threads quantises one group of one unit; blockIdx.z
-// selects K (0) or V (1).
-//  K: thread (wave w, lane) owns channels 2*lane, 2*lane+1 of rows 8w..8w+7:
-//     min/max in registers, across the 4 waves through LDS.
-//  V: thread (row r, chunk q) owns channels 16q..16q+15 of row r; the 32
-//     channels of a value group sit in two adjacent lanes.
-// Codes are staged as bytes in LDS ([token][channel]) and re-read in the
-// order of the packed layout, so every global store is a coalesced dword.
+// Each workgroup takes `gpw` consecutive groups (one by default) of one unit:
+// two waves quantise the keys (one channel half each), two waves the values
+// (one token half each), independently (see quantize_keys / quantize_values).  Codes
+// are staged as bytes in a per-wave LDS tile and re-read in the order of the
+// packed layout, so the global stores are coalesced.
 #pragma clang fp contract(off)
 
 #include <float.h>
+#include <stdlib.h>
 
 #include "kivi_internal.h"
 
@@ -59,118 +57,198 @@ __device__ __forceinline__ uint32_t pack4x4(uint32_t x) {
   return (y & 0xFFu) | ((y >> 8) & 0xFF00u);
 }
 
-template <int BITS>
-__global__ __launch_bounds__(256) void quantize_kernel(QuantizeArgs a) {
-  constexpr int D = kHeadDim, G = kGroup;
-  __shared__ __align__(16) uint8_t s_code[G][D];
-  __shared__ float s_mn[4][D], s_mx[4][D];
+// min / max of x over lanes l and l ^ 32.  permlane32_swap of x with itself
+// returns, in lanes 0-31, (x[l], x[l + 32]) and, in lanes 32-63,
+// (x[l - 32], x[l]): the pair always holds both values.
+__device__ __forceinline__ float min_x32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fminf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_x32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 
-  const int gl = blockIdx.x, u = blockIdx.y, t = threadIdx.x;
+// One wave quantises the keys of one half of the channels (64) of each of
+// its groups.  Lane (pair p, row half h) owns channels cb+2p, cb+2p+1 of rows
+// 16h..16h+15: the per-channel min/max over 32 tokens is 16 values in
+// registers plus one exchange with lane ^ 32.  Byte codes go through the
+// wave's LDS tile ([row][64 channels]) and come back in packed row order.
+template <int BITS>
+__device__ __forceinline__ void key_group(const QuantizeArgs &a, int u, int gl,
+                                          const uint32_t (&raw)[16], int cb, int lane,
+                                          uint8_t *tile) {
+  constexpr int D = kHeadDim, G = kGroup, KROW = D * BITS / 8;
+  const int p = lane & 31, h = lane >> 5;
+  float x0[16], x1[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    x0[i] = bf16_lo(raw[i]);
+    x1[i] = bf16_hi(raw[i]);
+  }
+  float mn0 = x0[0], mx0 = x0[0], mn1 = x1[0], mx1 = x1[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) {
+    mn0 = fminf(mn0, x0[i]); mx0 = fmaxf(mx0, x0[i]);
+    mn1 = fminf(mn1, x1[i]); mx1 = fmaxf(mx1, x1[i]);
+  }
+  // the other row half of the same channels sits in lane ^ 32
+  mn0 = min_x32(mn0); mx0 = max_x32(mx0);
+  mn1 = min_x32(mn1); mx1 = max_x32(mx1);
+  float sc0, inv0, sc1, inv1;
+  group_params<BITS>(mn0, mx0, sc0, inv0);
+  group_params<BITS>(mn1, mx1, sc1, inv1);
   const int g = a.dst_g0 + gl;
   const long long unit_grp = (long long)u * a.n_groups_cap + g;
-
-  if (blockIdx.z == 0) {
-    // ------------------------------------------------------------- keys
-    const int lane = t & 63, w = t >> 6;
-    const uint32_t *src = reinterpret_cast<const uint32_t *>(
-        a.src_k + (long long)u * a.src_unit_stride + (long long)(a.src_tok0 + gl * G) * D);
-    float x0[8], x1[8];
+  if (h == 0) {
+    reinterpret_cast<float2 *>(a.k_scale + unit_grp * D + cb)[p] = make_float2(sc0, sc1);
+    reinterpret_cast<float2 *>(a.k_zero + unit_grp * D + cb)[p] = make_float2(mn0, mn1);
+  }
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const uint32_t x = src[(8 * w + r) * (D / 2) + lane];
-      x0[r] = bf16_lo(x);
-      x1[r] = bf16_hi(x);
-    }
-    float mn0 = x0[0], mx0 = x0[0], mn1 = x1[0], mx1 = x1[0];
-#pragma unroll
-    for (int r = 1; r < 8; ++r) {
-      mn0 = fminf(mn0, x0[r]); mx0 = fmaxf(mx0, x0[r]);
-      mn1 = fminf(mn1, x1[r]); mx1 = fmaxf(mx1, x1[r]);
-    }
-    s_mn[w][2 * lane] = mn0; s_mn[w][2 * lane + 1] = mn1;
-    s_mx[w][2 * lane] = mx0; s_mx[w][2 * lane + 1] = mx1;
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      mn0 = fminf(mn0, s_mn[i][2 * lane]); mn1 = fminf(mn1, s_mn[i][2 * lane + 1]);
-      mx0 = fmaxf(mx0, s_mx[i][2 * lane]); mx1 = fmaxf(mx1, s_mx[i][2 * lane + 1]);
-    }
-    float sc0, inv0, sc1, inv1;
-    group_params<BITS>(mn0, mx0, sc0, inv0);
-    group_params<BITS>(mn1, mx1, sc1, inv1);
-    if (w == 0) {
-      reinterpret_cast<float2 *>(a.k_scale + unit_grp * D)[lane] = make_float2(sc0, sc1);
-      reinterpret_cast<float2 *>(a.k_zero + unit_grp * D)[lane] = make_float2(mn0, mn1);
-    }
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const uint32_t c = code_of<BITS>(x0[r], mn0, inv0) | (code_of<BITS>(x1[r], mn1, inv1) << 8);
-      reinterpret_cast<uint16_t *>(s_code[8 * w + r])[lane] = (uint16_t)c;
-    }
-    __syncthreads();
-    // pack: thread -> (row, 16 consecutive channels)
-    const int row = t >> 3, ch0 = 16 * (t & 7);
-    const uint4 x = *reinterpret_cast<const uint4 *>(&s_code[row][ch0]);
-    uint8_t *dst = a.k_codes + ((long long)u * a.max_tokens + (long long)g * G + row) * (D * BITS / 8);
-    if (BITS == 2) {
-      const uint32_t word = pack4x2(x.x) | (pack4x2(x.y) << 8) | (pack4x2(x.z) << 16) |
-                            (pack4x2(x.w) << 24);
-      reinterpret_cast<uint32_t *>(dst)[t & 7] = word;
-    } else {
-      const uint2 word = make_uint2(pack4x4(x.x) | (pack4x4(x.y) << 16),
-                                    pack4x4(x.z) | (pack4x4(x.w) << 16));
-      reinterpret_cast<uint2 *>(dst)[t & 7] = word;
-    }
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t c = code_of<BITS>(x0[i], mn0, inv0) | (code_of<BITS>(x1[i], mn1, inv1) << 8);
+    reinterpret_cast<uint16_t *>(tile + (16 * h + i) * 64)[p] = (uint16_t)c;
+  }
+  __builtin_amdgcn_wave_barrier();
+  // pack: lane -> (row lane/2, 32 channels)
+  const int row = lane >> 1, c32 = 32 * (lane & 1);
+  const uint4 b0 = *reinterpret_cast<const uint4 *>(tile + row * 64 + c32);
+  const uint4 b1 = *reinterpret_cast<const uint4 *>(tile + row * 64 + c32 + 16);
+  uint8_t *dst = a.k_codes + ((long long)u * a.max_tokens + (long long)g * G + row) * KROW +
+                 (cb + c32) * BITS / 8;
+  if constexpr (BITS == 2) {
+    const uint32_t w0 = pack4x2(b0.x) | (pack4x2(b0.y) << 8) | (pack4x2(b0.z) << 16) |
+                        (pack4x2(b0.w) << 24);
+    const uint32_t w1 = pack4x2(b1.x) | (pack4x2(b1.y) << 8) | (pack4x2(b1.z) << 16) |
+                        (pack4x2(b1.w) << 24);
+    *reinterpret_cast<uint2 *>(dst) = make_uint2(w0, w1);
   } else {
-    // ----------------------------------------------------------- values
-    const int row = t >> 3, q = t & 7, j = q >> 1;
-    const uint4 *src = reinterpret_cast<const uint4 *>(
-        a.src_v + (long long)u * a.src_unit_stride + (long long)(a.src_tok0 + gl * G + row) * D +
-        16 * q);
-    const uint4 p0 = src[0], p1 = src[1];
-    const uint32_t wv[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-    float x[16];
+    *reinterpret_cast<uint4 *>(dst) =
+        make_uint4(pack4x4(b0.x) | (pack4x4(b0.y) << 16), pack4x4(b0.z) | (pack4x4(b0.w) << 16),
+                   pack4x4(b1.x) | (pack4x4(b1.y) << 16), pack4x4(b1.z) | (pack4x4(b1.w) << 16));
+  }
+  __builtin_amdgcn_wave_barrier();   // tile reads done before the next group's writes
+}
+
+template <int BITS>
+__device__ __forceinline__ void quantize_keys(const QuantizeArgs &a, int u, int gl0, int gl1,
+                                              int half, int lane, uint8_t *tile) {
+  constexpr int D = kHeadDim, G = kGroup;
+  const int p = lane & 31, h = lane >> 5, cb = 64 * half;
+  const uint32_t *src = reinterpret_cast<const uint32_t *>(
+      a.src_k + (long long)u * a.src_unit_stride + (long long)a.src_tok0 * D);
+  const int col = cb / 2 + p;   // 32-bit column of this lane's channel pair
+  auto load = [&](int gl, uint32_t (&x)[16]) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      x[2 * i] = bf16_lo(wv[i]);
-      x[2 * i + 1] = bf16_hi(wv[i]);
-    }
-    float mn = x[0], mx = x[0];
+    for (int i = 0; i < 16; ++i) x[i] = src[((long long)gl * G + 16 * h + i) * (D / 2) + col];
+  };
+  // software pipeline: the loop always loads the next group (the last group
+  // is peeled off), so each step waits only for its own rows
+  uint32_t cur[16], nxt[16];
+  load(gl0, nxt);
+  for (int gl = gl0; gl + 1 < gl1; ++gl) {
 #pragma unroll
-    for (int i = 1; i < 16; ++i) { mn = fminf(mn, x[i]); mx = fmaxf(mx, x[i]); }
-    mn = fminf(mn, __shfl_xor(mn, 1));
-    mx = fmaxf(mx, __shfl_xor(mx, 1));
-    float sc, inv;
-    group_params<BITS>(mn, mx, sc, inv);
-    if ((q & 1) == 0) {
-      const long long mi = (unit_grp * (D / G) + j) * G + row;
-      a.v_scale[mi] = sc;
-      a.v_zero[mi] = mn;
-    }
-    uint32_t cw[4];
+    for (int i = 0; i < 16; ++i) cur[i] = nxt[i];
+    load(gl + 1, nxt);
+    key_group<BITS>(a, u, gl, cur, cb, lane, tile);
+  }
+  key_group<BITS>(a, u, gl1 - 1, nxt, cb, lane, tile);
+}
+
+// One wave quantises the values of 16 tokens (two octets) of each of its
+// groups.  Lane (row r, quarter q) owns channels 32q..32q+31 of token r: one
+// whole value group, min/max in registers.  Byte codes go through the wave's
+// LDS tile ([row][128 channels]) and are regathered as octet x channel cells.
+template <int BITS>
+__device__ __forceinline__ void value_group(const QuantizeArgs &a, int u, int gl,
+                                            const uint4 (&raw)[4], int part, int lane,
+                                            uint8_t *tile) {
+  constexpr int D = kHeadDim, G = kGroup;
+  const int r = lane >> 2, q = lane & 3;
+  float x[32];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      cw[i] = code_of<BITS>(x[4 * i], mn, inv) | (code_of<BITS>(x[4 * i + 1], mn, inv) << 8) |
-              (code_of<BITS>(x[4 * i + 2], mn, inv) << 16) |
-              (code_of<BITS>(x[4 * i + 3], mn, inv) << 24);
-    *reinterpret_cast<uint4 *>(&s_code[row][16 * q]) = make_uint4(cw[0], cw[1], cw[2], cw[3]);
-    __syncthreads();
-    // pack: thread -> (octet o, channels 2cp, 2cp+1): two cells of 8 tokens
-    const int o = t >> 6, cp = t & 63;
-    uint32_t c0 = 0, c1 = 0;
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const uint32_t pair = reinterpret_cast<const uint16_t *>(s_code[8 * o + k])[cp];
-      c0 |= (pair & 0xFFu) << (BITS * k);
-      c1 |= (pair >> 8) << (BITS * k);
-    }
-    const long long cell = ((unit_grp * (G / 8) + o) * D) / 2 + cp;   // in channel pairs
-    if (BITS == 2) {
-      reinterpret_cast<uint32_t *>(a.v_codes)[cell] = c0 | (c1 << 16);
-    } else {
-      reinterpret_cast<uint2 *>(a.v_codes)[cell] = make_uint2(c0, c1);
+    for (int e = 0; e < 4; ++e) {
+      x[8 * i + 2 * e] = bf16_lo(w[e]);
+      x[8 * i + 2 * e + 1] = bf16_hi(w[e]);
     }
   }
+  float mn = x[0], mx = x[0];
+#pragma unroll
+  for (int i = 1; i < 32; ++i) { mn = fminf(mn, x[i]); mx = fmaxf(mx, x[i]); }
+  float sc, inv;
+  group_params<BITS>(mn, mx, sc, inv);
+  const int g = a.dst_g0 + gl;
+  const long long unit_grp = (long long)u * a.n_groups_cap + g;
+  const long long mi = (unit_grp * (D / G) + q) * G + 16 * part + r;
+  a.v_scale[mi] = sc;
+  a.v_zero[mi] = mn;
+  uint32_t cw[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    cw[i] = code_of<BITS>(x[4 * i], mn, inv) | (code_of<BITS>(x[4 * i + 1], mn, inv) << 8) |
+            (code_of<BITS>(x[4 * i + 2], mn, inv) << 16) |
+            (code_of<BITS>(x[4 * i + 3], mn, inv) << 24);
+  uint4 *t = reinterpret_cast<uint4 *>(tile + r * D + 32 * q);
+  t[0] = make_uint4(cw[0], cw[1], cw[2], cw[3]);
+  t[1] = make_uint4(cw[4], cw[5], cw[6], cw[7]);
+  __builtin_amdgcn_wave_barrier();
+  // cells: lane -> (octet o, channels 4c4..4c4+3), 8 tokens each
+  const int o = lane >> 5, c4 = lane & 31;
+  uint32_t cell[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const uint32_t w = *reinterpret_cast<const uint32_t *>(tile + (8 * o + k) * D + 4 * c4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) cell[i] |= ((w >> (8 * i)) & 0xFFu) << (BITS * k);
+  }
+  uint8_t *dst = a.v_codes + ((unit_grp * (G / 8) + 2 * part + o) * D + 4 * c4) * BITS;
+  if constexpr (BITS == 2) {
+    *reinterpret_cast<uint2 *>(dst) = make_uint2(cell[0] | (cell[1] << 16), cell[2] | (cell[3] << 16));
+  } else {
+    *reinterpret_cast<uint4 *>(dst) = make_uint4(cell[0], cell[1], cell[2], cell[3]);
+  }
+  __builtin_amdgcn_wave_barrier();
+}
+
+template <int BITS>
+__device__ __forceinline__ void quantize_values(const QuantizeArgs &a, int u, int gl0, int gl1,
+                                                int part, int lane, uint8_t *tile) {
+  constexpr int D = kHeadDim, G = kGroup;
+  const int r = lane >> 2, q = lane & 3;
+  const uint16_t *src = a.src_v + (long long)u * a.src_unit_stride + (long long)a.src_tok0 * D;
+  auto load = [&](int gl, uint4 (&x)[4]) {
+    const uint4 *row = reinterpret_cast<const uint4 *>(
+        src + ((long long)gl * G + 16 * part + r) * D + 32 * q);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = row[i];
+  };
+  uint4 cur[4], nxt[4];
+  load(gl0, nxt);
+  for (int gl = gl0; gl + 1 < gl1; ++gl) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) cur[i] = nxt[i];
+    load(gl + 1, nxt);
+    value_group<BITS>(a, u, gl, cur, part, lane, tile);
+  }
+  value_group<BITS>(a, u, gl1 - 1, nxt, part, lane, tile);
+}
+
+// Grid (ceil(n_groups / gpw), n_units): waves 0-1 take the keys (channel
+// halves), waves 2-3 the values (token halves) of `gpw` consecutive groups
+// (one by default).  The waves share nothing and never wait for each other.
+template <int BITS>
+__global__ __launch_bounds__(256) void quantize_kernel(QuantizeArgs a) {
+  __shared__ __align__(16) uint8_t s_tile[4][16 * kHeadDim];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int u = blockIdx.y;
+  const int gl0 = blockIdx.x * a.gpw, gl1 = min(gl0 + a.gpw, a.n_groups);
+  if (wave < 2)
+    quantize_keys<BITS>(a, u, gl0, gl1, wave, lane, s_tile[wave]);
+  else
+    quantize_values<BITS>(a, u, gl0, gl1, wave - 2, lane, s_tile[wave]);
 }
 
 __global__ __launch_bounds__(256) void copy_rows_kernel(CopyRowsArgs a) {
@@ -188,9 +266,17 @@ __global__ __launch_bounds__(256) void copy_rows_kernel(CopyRowsArgs a) {
 
 }  // namespace
 
-hipError_t launch_quantize(int bits, const QuantizeArgs &a, hipStream_t s) {
-  if (a.n_groups <= 0 || a.n_units <= 0) return hipSuccess;
-  const dim3 grid(a.n_groups, a.n_units, 2);
+hipError_t launch_quantize(int bits, const QuantizeArgs &a_in, hipStream_t s) {
+  if (a_in.n_groups <= 0 || a_in.n_units <= 0) return hipSuccess;
+  // groups per workgroup: one.  Short independent workgroups keep the most
+  // loads in flight; on MI355X at the 8K GQA prefill (16 x 8 units, 252
+  // groups each) 1 group per workgroup runs at 5.4 TB/s, 2 at 5.2, 4 at 4.8,
+  // 8 at 4.5.  KIVI_QGPW sets another count (sweeps).
+  QuantizeArgs a = a_in;
+  long long gpw = 1;
+  if (const char *env = getenv("KIVI_QGPW")) gpw = atoll(env);
+  a.gpw = (int)(gpw < 1 ? 1 : gpw > 8 ? 8 : gpw);
+  const dim3 grid((a.n_groups + a.gpw - 1) / a.gpw, a.n_units);
   if (bits == 2)
     hipLaunchKernelGGL(quantize_kernel<2>, grid, dim3(256), 0, s, a);
   else
