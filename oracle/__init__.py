@@ -38,7 +38,7 @@ _lib = None
 class _Geom(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in (
         "batch", "kv_heads", "q_per_kv", "head_dim", "bits", "group", "residual",
-        "max_tokens")]
+        "max_tokens", "meta")]
 
 
 class _Cache(ctypes.Structure):
@@ -62,6 +62,8 @@ def lib():
         C = ctypes.POINTER(_Cache)
         L.kivio_quantize_values.argtypes = [P, ctypes.c_int, ctypes.c_int, P, P, P]
         L.kivio_quantize_values.restype = None
+        L.kivio_quantize_values_h.argtypes = [P, ctypes.c_int, ctypes.c_int, P, P, P]
+        L.kivio_quantize_values_h.restype = None
         L.kivio_prefill_split.argtypes = [ctypes.c_int] * 3
         L.kivio_prefill_split.restype = ctypes.c_int
         L.kivio_prefill.argtypes = [G, C, P, P, ctypes.c_int]
@@ -101,6 +103,7 @@ class Geom:
     group: int = 32
     residual: int = 128
     max_tokens: int = 0
+    meta: int = 0   # scale/zero format: 0 = fp32/fp32, 1 = fp16 scale, bf16 zero
 
     @property
     def units(self) -> int:
@@ -119,6 +122,8 @@ class Geom:
             raise ValueError("oracle supports head_dim <= 256 and group <= 64, group % 8 == 0")
         if self.max_tokens % self.group:
             raise ValueError("max_tokens must be a multiple of group")
+        if self.meta not in (0, 1):
+            raise ValueError("meta must be 0 (fp32 scale/zero) or 1 (fp16 scale, bf16 zero)")
         return _Geom(*dataclasses.astuple(self))
 
 
@@ -130,10 +135,11 @@ class Cache:
         NG = g.n_groups
         self.geom = g
         self.k_codes = np.zeros((g.batch, g.kv_heads, T, D * b // 8), np.uint8)
-        self.k_scale = np.zeros((g.batch, g.kv_heads, NG, D), np.float32)
+        mt = np.uint16 if g.meta == 1 else np.float32   # fp16 / bf16 bits, or fp32
+        self.k_scale = np.zeros((g.batch, g.kv_heads, NG, D), mt)
         self.k_zero = np.zeros_like(self.k_scale)
         self.v_codes = np.zeros((g.batch, g.kv_heads, NG, G // 8, D, b), np.uint8)
-        self.v_scale = np.zeros((g.batch, g.kv_heads, NG, D // G, G), np.float32)
+        self.v_scale = np.zeros((g.batch, g.kv_heads, NG, D // G, G), mt)
         self.v_zero = np.zeros_like(self.v_scale)
         self.k_res = np.zeros((g.batch, g.kv_heads, g.slots, D), np.uint16)
         self.v_res = np.zeros_like(self.k_res)
@@ -161,13 +167,16 @@ class Cache:
         return out
 
 
-def quantize_values(x: np.ndarray, bits: int):
-    """Asymmetric min-max quantisation of one group: (codes, scale, zero)."""
+def quantize_values(x: np.ndarray, bits: int, meta: int = 0):
+    """Asymmetric min-max quantisation of one group: (codes, scale, zero);
+    with meta=1, scale and zero are the fp16 / bf16 bit patterns (uint16)."""
     x = np.ascontiguousarray(x, dtype=np.float32)
     codes = np.zeros(x.size, np.uint8)
-    s = np.zeros(1, np.float32)
-    z = np.zeros(1, np.float32)
-    lib().kivio_quantize_values(_p(x), x.size, bits, _p(codes), _p(s), _p(z))
+    mt = np.uint16 if meta == 1 else np.float32
+    s = np.zeros(1, mt)
+    z = np.zeros(1, mt)
+    fn = lib().kivio_quantize_values_h if meta == 1 else lib().kivio_quantize_values
+    fn(_p(x), x.size, bits, _p(codes), _p(s), _p(z))
     return codes, s[0], z[0]
 
 
@@ -269,8 +278,9 @@ def attention_dense(g: Geom, k: np.ndarray, v: np.ndarray, seq_len: int, q: np.n
 
 
 def bytes_per_token(layers, kv_heads, head_dim, bits, group, residual, ctx):
-    """(bf16, catalog convention, exact codes, stored incl. scale/zero) B/token."""
-    out = np.zeros(4, np.float64)
+    """(bf16, catalog convention, exact codes, stored incl. fp32 scale/zero,
+    stored with fp16 scale + bf16 zero) B/token."""
+    out = np.zeros(5, np.float64)
     lib().kivio_bytes_per_token(layers, kv_heads, head_dim, bits, group, residual, ctx,
                                 _p(out))
     return tuple(float(x) for x in out)

@@ -41,16 +41,17 @@
 
 typedef struct {
   int batch, kv_heads, q_per_kv, head_dim, bits, group, residual, max_tokens;
+  int meta;   /* scale/zero format: 0 = fp32 scale, fp32 zero; 1 = fp16 scale, bf16 zero */
 } kivio_geom;
 
 /* Host arrays in the documented layout (see the comments of each field). */
 typedef struct {
   uint8_t *k_codes;   /* [B][H][T][D*b/8]                 */
-  float *k_scale;     /* [B][H][T/G][D]                   */
-  float *k_zero;      /* [B][H][T/G][D]                   */
+  void *k_scale;      /* [B][H][T/G][D]        (fp32, or fp16 bits) */
+  void *k_zero;       /* [B][H][T/G][D]        (fp32, or bf16 bits) */
   uint8_t *v_codes;   /* [B][H][T/G][G/8][D][b]           */
-  float *v_scale;     /* [B][H][T/G][D/G][G]              */
-  float *v_zero;      /* [B][H][T/G][D/G][G]              */
+  void *v_scale;      /* [B][H][T/G][D/G][G]   (fp32, or fp16 bits) */
+  void *v_zero;       /* [B][H][T/G][D/G][G]   (fp32, or bf16 bits) */
   uint16_t *k_res;    /* [B][H][R+G][D] bf16 bits         */
   uint16_t *v_res;    /* [B][H][R+G][D] bf16 bits         */
   int n_q, n_res, res_start;
@@ -88,6 +89,66 @@ void kivio_quantize_values(const float *x, int n, int bits, uint8_t *code,
   }
   *scale = s;
   *zero = mn;
+}
+
+/* One group in the 16-bit scale/zero format (no page fixes a metadata
+ * format; the record's byte basis counts none).  The zero stays the group
+ * minimum, a bf16 input value, so bf16 holds it exactly.  The scale
+ * (max - min) / L is rounded to fp16, to nearest even, and saturates at the
+ * largest finite fp16, 65504; the codes are then computed from that rounded
+ * scale with the same formula as above, so that code * scale + zero is the
+ * value the cache represents.  scale / zero receive the fp16 / bf16 bits. */
+static uint16_t fp16_bits_rne(float x);
+static float fp16_value(uint16_t bits);
+
+void kivio_quantize_values_h(const float *x, int n, int bits, uint8_t *code,
+                             uint16_t *scale, uint16_t *zero) {
+  float mn = x[0], mx = x[0];
+  for (int i = 1; i < n; ++i) {
+    if (x[i] < mn) mn = x[i];
+    if (x[i] > mx) mx = x[i];
+  }
+  const float levels = (float)((1 << bits) - 1);
+  const uint16_t sh = fp16_bits_rne((mx - mn) / levels);
+  const float s = fp16_value(sh);
+  const float inv = (s >= FLT_MIN) ? 1.0f / s : 0.0f;
+  for (int i = 0; i < n; ++i) {
+    float y = rintf((x[i] - mn) * inv);
+    y = fminf(fmaxf(y, 0.0f), levels);
+    code[i] = (uint8_t)y;
+  }
+  uint32_t w;
+  memcpy(&w, &mn, sizeof w);
+  *scale = sh;
+  *zero = (uint16_t)(w >> 16);   /* mn is a widened bf16: the low half is zero */
+}
+
+/* IEEE binary16 of a non-negative float, round to nearest even, saturating
+ * at 65504: q = 2^(e-10) is the spacing of binary16 numbers at x's binade
+ * (e >= -14; below that the subnormal spacing 2^-24), x / q is exact in
+ * double and rounded to an integer with ties to even. */
+static uint16_t fp16_bits_rne(float x) {
+  if (!(x > 0.0f)) return 0;
+  if (x >= 65504.0f) return 0x7BFF;
+  int e;
+  frexp((double)x, &e);   /* x = m * 2^e, 0.5 <= m < 1 */
+  e -= 1;                 /* x in [2^e, 2^(e+1)) */
+  if (e < -14) e = -14;
+  const double q = ldexp(1.0, e - 10);
+  double n = nearbyint((double)x / q);   /* default rounding: to nearest even */
+  if (n >= 2048.0) {      /* rounded up into the next binade */
+    n /= 2.0;
+    e += 1;
+  }
+  if (e > 15) return 0x7BFF;
+  if (n < 1024.0) return (uint16_t)n;    /* subnormal (e == -14): mantissa only */
+  return (uint16_t)(((e + 15) << 10) | ((int)n - 1024));
+}
+
+static float fp16_value(uint16_t bits) {
+  const int e = (bits >> 10) & 0x1F, m = bits & 0x3FF;
+  if (e == 0) return (float)ldexp((double)m, -24);
+  return (float)ldexp((double)(1024 + m), e - 25);
 }
 
 /* --------------------------------------------------- layout indexing --- */
@@ -136,6 +197,30 @@ static size_t ring_at(const kivio_geom *g, size_t u, int slot, int ch) {
   return (u * (size_t)ring_slots(g) + (size_t)slot) * (size_t)g->head_dim + (size_t)ch;
 }
 
+/* Quantise the n values of one group in the geometry's scale/zero format and
+ * store scale and zero at index idx of the K (is_v = 0) or V arrays. */
+static void store_group_meta(const kivio_geom *g, kivio_cache *c, int is_v, size_t idx,
+                             const float *x, int n, int bits, uint8_t *code) {
+  void *sc = is_v ? c->v_scale : c->k_scale, *zr = is_v ? c->v_zero : c->k_zero;
+  if (g->meta == 1) {
+    kivio_quantize_values_h(x, n, bits, code, (uint16_t *)sc + idx, (uint16_t *)zr + idx);
+  } else {
+    kivio_quantize_values(x, n, bits, code, (float *)sc + idx, (float *)zr + idx);
+  }
+}
+
+/* scale and zero at index idx of the K (is_v = 0) or V arrays, as doubles */
+static double meta_scale(const kivio_geom *g, const kivio_cache *c, int is_v, size_t idx) {
+  const void *sc = is_v ? c->v_scale : c->k_scale;
+  if (g->meta == 1) return (double)fp16_value(((const uint16_t *)sc)[idx]);
+  return (double)((const float *)sc)[idx];
+}
+static double meta_zero(const kivio_geom *g, const kivio_cache *c, int is_v, size_t idx) {
+  const void *zr = is_v ? c->v_zero : c->k_zero;
+  if (g->meta == 1) return (double)bf16_to_float(((const uint16_t *)zr)[idx]);
+  return (double)((const float *)zr)[idx];
+}
+
 /* Quantise one group of G tokens into group index gi.  src_k / src_v give
  * token i (0..G-1) of unit u as bf16 rows of D values. */
 static void quantize_group(const kivio_geom *g, kivio_cache *c, size_t u, int gi,
@@ -143,22 +228,17 @@ static void quantize_group(const kivio_geom *g, kivio_cache *c, size_t u, int gi
   const int G = g->group, D = g->head_dim, b = g->bits;
   float x[64];
   uint8_t code[64];
-  float s, z;
   /* keys: one group per channel, along the G tokens */
   for (int ch = 0; ch < D; ++ch) {
     for (int i = 0; i < G; ++i) x[i] = bf16_to_float(src_k[i][ch]);
-    kivio_quantize_values(x, G, b, code, &s, &z);
-    c->k_scale[k_meta(g, u, gi, ch)] = s;
-    c->k_zero[k_meta(g, u, gi, ch)] = z;
+    store_group_meta(g, c, 0, k_meta(g, u, gi, ch), x, G, b, code);
     for (int i = 0; i < G; ++i) put_code(k_row(g, c, u, gi * G + i), (size_t)ch, b, code[i]);
   }
   /* values: one group per token and block of G channels */
   for (int i = 0; i < G; ++i) {
     for (int j = 0; j < D / G; ++j) {
       for (int e = 0; e < G; ++e) x[e] = bf16_to_float(src_v[i][j * G + e]);
-      kivio_quantize_values(x, G, b, code, &s, &z);
-      c->v_scale[v_meta(g, u, gi, j, i)] = s;
-      c->v_zero[v_meta(g, u, gi, j, i)] = z;
+      store_group_meta(g, c, 1, v_meta(g, u, gi, j, i), x, G, b, code);
       for (int e = 0; e < G; ++e) {
         int ch = j * G + e;
         put_code(v_cell(g, c, u, gi, i / 8, ch), (size_t)(i % 8), b, code[e]);
@@ -257,12 +337,12 @@ void kivio_dequant_unit(const kivio_geom *g, const kivio_cache *c, long unit,
     const int gi = t / G, i = t % G;
     for (int ch = 0; ch < D; ++ch) {
       uint8_t kc = get_code(k_row(g, c, u, t), (size_t)ch, b);
-      k_out[(size_t)t * D + ch] = (double)kc * (double)c->k_scale[k_meta(g, u, gi, ch)] +
-                                  (double)c->k_zero[k_meta(g, u, gi, ch)];
+      k_out[(size_t)t * D + ch] = (double)kc * meta_scale(g, c, 0, k_meta(g, u, gi, ch)) +
+                                  meta_zero(g, c, 0, k_meta(g, u, gi, ch));
       uint8_t vc = get_code(v_cell(g, c, u, gi, i / 8, ch), (size_t)(i % 8), b);
       const int j = ch / G;
-      v_out[(size_t)t * D + ch] = (double)vc * (double)c->v_scale[v_meta(g, u, gi, j, i)] +
-                                  (double)c->v_zero[v_meta(g, u, gi, j, i)];
+      v_out[(size_t)t * D + ch] = (double)vc * meta_scale(g, c, 1, v_meta(g, u, gi, j, i)) +
+                                  meta_zero(g, c, 1, v_meta(g, u, gi, j, i));
     }
   }
   for (int i = 0; i < c->n_res; ++i) {
@@ -375,9 +455,11 @@ int kivio_attention_dense_unit(const kivio_geom *g, const uint16_t *k, const uin
  *  out[2] exact stored codes: the grouped term covers ctx-R tokens only;
  *  out[3] bytes this cache layout stores, scale and zero included (two fp32
  *         per group of G in K and in V), with the prefill split
- *         n_q = G*floor((ctx-R)/G) and n_q stored tokens + (ctx-n_q) bf16. */
+ *         n_q = G*floor((ctx-R)/G) and n_q stored tokens + (ctx-n_q) bf16;
+ *  out[4] the same with the 16-bit scale/zero format (fp16 scale, bf16
+ *         zero). */
 void kivio_bytes_per_token(int layers, int kv_heads, int head_dim, int bits, int group,
-                           int residual, int ctx, double out[4]) {
+                           int residual, int ctx, double out[5]) {
   const double lhd = (double)layers * kv_heads * head_dim;
   const double bf16 = lhd * 2.0 * 2.0;
   const double grouped = lhd * 2.0 * bits / 8.0;
@@ -388,4 +470,6 @@ void kivio_bytes_per_token(int layers, int kv_heads, int head_dim, int bits, int
   const int n_q = kivio_prefill_split(ctx, group, residual);
   const double per_q_token = lhd * (2.0 * bits / 8.0 + 2.0 * 2.0 * 4.0 / group);
   out[3] = ((double)n_q * per_q_token + (double)(ctx - n_q) * bf16) / (double)ctx;
+  const double per_q_token16 = lhd * (2.0 * bits / 8.0 + 2.0 * 2.0 * 2.0 / group);
+  out[4] = ((double)n_q * per_q_token16 + (double)(ctx - n_q) * bf16) / (double)ctx;
 }

@@ -24,7 +24,7 @@ def _rows():
 def test_golden_byte_figures():
     seen = set()
     for (L, H, D, b, G, R, ctx), what, want in _rows():
-        bf16, conv, exact, stored = oracle.bytes_per_token(L, H, D, b, G, R, ctx)
+        bf16, conv, exact, stored, stored16 = oracle.bytes_per_token(L, H, D, b, G, R, ctx)
         grouped = conv - R * bf16 / ctx
         got = {
             "grouped_term": grouped,
@@ -65,3 +65,18 @@ def test_stored_bytes_count_every_buffer():
         total = (k_codes + v_codes + k_meta + v_meta + resid) * L * H / S
         assert oracle.bytes_per_token(L, H, D, b, G, R, S)[3] == pytest.approx(total)
     assert oracle.bytes_per_token(L, H, D, 2, G, R, S)[3] == 34304.0
+
+
+def test_stored_bytes_with_16bit_scale_and_zero():
+    """Same count with fp16 scale and bf16 zero: 2 bytes each instead of 4."""
+    L, H, D, G, R, S = 32, 8, 128, 32, 128, 8192
+    for b in (2, 4):
+        n_q = oracle.prefill_split(S, G, R)
+        meta = ((n_q // G) * D + n_q * (D // G)) * 2 * 2
+        codes = 2 * n_q * D * b / 8
+        resid = (S - n_q) * D * 2 * 2
+        total = (codes + meta + resid) * L * H / S
+        assert oracle.bytes_per_token(L, H, D, b, G, R, S)[4] == pytest.approx(total)
+    bf16, _, _, stored, stored16 = oracle.bytes_per_token(L, H, D, 2, G, R, S)
+    assert stored16 == 26240.0
+    assert round(bf16 / stored16, 2) == 5.0 and round(bf16 / stored, 2) == 3.82
