@@ -40,20 +40,22 @@ HBM_PEAK_GBPS = 8000.0
 METRIC = "KIVI decode-attention achieved HBM GB/s + tokens/sec; quantize Gelem/s"
 
 
-def attn_bytes(w, n_q, n_res, fused_append=False):
+def attn_bytes(w, n_q, n_res, fused_append=False, meta_bytes=4):
     """Algorithmic bytes of one decode-attention launch: the packed history
-    (codes + fp32 scale/zero), the bf16 residual (the appended token included,
-    read from its input in a fused step), q (bf16) and out (fp32); a fused
-    step also writes the appended K and V rows into the ring."""
+    (codes + scale/zero of meta_bytes each), the bf16 residual (the appended
+    token included, read from its input in a fused step), q (bf16) and out
+    (fp32); a fused step also writes the appended K and V rows into the ring."""
     D, G, b = w.head_dim, w.group, w.bits
-    per_unit = n_q * (2 * D * b / 8 + 16 * D / G) + n_res * 4 * D + (4 * D if fused_append else 0)
+    per_unit = (n_q * (2 * D * b / 8 + 4 * meta_bytes * D / G) + n_res * 4 * D +
+                (4 * D if fused_append else 0))
     return w.batch * w.kv_heads * per_unit + w.batch * w.q_heads * D * (2 + 4)
 
 
-def prefill_bytes(w, S, n_q):
+def prefill_bytes(w, S, n_q, meta_bytes=4):
     D, G, b = w.head_dim, w.group, w.bits
     r = S - n_q
-    return w.batch * w.kv_heads * (4 * S * D + n_q * (2 * D * b / 8 + 16 * D / G) + 4 * r * D)
+    return w.batch * w.kv_heads * (4 * S * D + n_q * (2 * D * b / 8 + 4 * meta_bytes * D / G) +
+                                   4 * r * D)
 
 
 def read_traffic(kernel_tag: str):
@@ -78,13 +80,13 @@ def read_traffic(kernel_tag: str):
         return None
 
 
-def cpu_baseline(w, seed, units_wanted=256):
+def cpu_baseline(w, seed, units_wanted=256, meta=0):
     import numpy as np
 
     import oracle
     import synth
     threads = max(1, min(16, len(os.sched_getaffinity(0))))
-    og = oracle.Geom(1, 1, w.q_per_kv, bits=w.bits, max_tokens=w.seq_len)
+    og = oracle.Geom(1, 1, w.q_per_kv, bits=w.bits, max_tokens=w.seq_len, meta=meta)
     per_layer = w.batch * w.kv_heads
     jobs = []
     for layer in range(math.ceil(units_wanted / per_layer)):
@@ -280,6 +282,9 @@ def main():
                     help="run only N decode steps after warmup, no reporting (profilers)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 5 times (scales HBM byte counters)")
+    ap.add_argument("--meta", choices=("fp32", "fp16"), default="fp32",
+                    help="scale/zero format: fp32 scale + zero (default), or fp16 scale + "
+                         "bf16 zero")
     ap.add_argument("--batch-sweep", action="store_true",
                     help="memory-wall sweep: KIVI 2-bit vs bf16 decode attention vs batch "
                          "(Llama-2-13B-shaped MHA); prints its own JSON line")
@@ -314,7 +319,9 @@ def main():
     kernel_steps = 10   # extra fused steps with HIP events around every launch
     total_steps = args.warmup + (args.profile_steps or 2 * args.steps + kernel_steps + 1)
     max_tokens = G * math.ceil((w.seq_len - R + total_steps + G) / G)
-    geom = kivi.Geom(w.batch, w.kv_heads, w.q_per_kv, bits=w.bits, max_tokens=max_tokens)
+    meta = kivi.META_FP16_BF16 if args.meta == "fp16" else kivi.META_FP32
+    geom = kivi.Geom(w.batch, w.kv_heads, w.q_per_kv, bits=w.bits, max_tokens=max_tokens,
+                     meta_format=meta)
 
     caches = [kivi.Cache(geom, dev) for _ in range(layers)]
     ws = kivi.Workspace(geom, dev)
@@ -341,7 +348,8 @@ def main():
     torch.cuda.empty_cache()
     pre_t = sum(pre_ms) / 1e3
     quant_gelem_s = 2 * w.batch * w.kv_heads * n_q0 * D * layers / pre_t / 1e9
-    pre_gbps = prefill_bytes(w, w.seq_len, n_q0) * layers / pre_t / 1e9
+    mbytes = 2 if meta == kivi.META_FP16_BF16 else 4
+    pre_gbps = prefill_bytes(w, w.seq_len, n_q0, mbytes) * layers / pre_t / 1e9
 
     # ---- decode inputs (resident before timing)
     qs = [synth.query(w, args.seed, layer, device=dev) for layer in range(layers)]
@@ -411,7 +419,8 @@ def main():
             flushed[j][layer] = st.step(kn, vn)
             e1.record()
             # the step attends over the cache after its append (and flush)
-            nbytes[j][layer] = attn_bytes(w, st.cache.n_q, st.cache.n_res, fused_append=True)
+            nbytes[j][layer] = attn_bytes(w, st.cache.n_q, st.cache.n_res, fused_append=True,
+                                          meta_bytes=mbytes)
     torch.cuda.synchronize()
     kern_us, kern_bytes = [], []
     for j in range(kernel_steps):
@@ -433,6 +442,7 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "kv_heads": w.kv_heads,
                    "q_heads": w.q_heads, "head_dim": D, "context": w.seq_len, "bits": w.bits,
                    "group": G, "residual": R, "layers": layers,
+                   "scale_zero": "fp16 scale + bf16 zero" if args.meta == "fp16" else "fp32",
                    "step": "per layer: kivi_decode_step (append + flush-if-full + decode "
                            "attention; one launch, two on flush steps)"},
         "ms_per_step_separate_calls": t_steps_sep / n_timed * 1e3,
@@ -446,12 +456,13 @@ def main():
         "quantize_prefill_ms_per_layer": pre_t / layers * 1e3,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": read_traffic(f"decode_attn_{w.name}")},
+                     "traffic": (read_traffic(f"decode_attn_{w.name}") if args.meta == "fp32"
+                                 else None)},
         "paper_context": "2.35x-3.47x decode throughput vs FP16 and 2.6x less peak memory "
                          "(Llama-2-7B, one A100 80GB; not comparable, quoted as context)",
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, args.seed)
+        res["cpu_baseline"] = cpu_baseline(w, args.seed, meta=meta)
     print(json.dumps(res))
 
 

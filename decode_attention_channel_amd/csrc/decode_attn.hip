@@ -306,24 +306,35 @@ struct UnitView {
   uint32_t o_k0, o_k1, o_v, o_mu;
 };
 
-template <int BITS>
+// Bytes of one scale or zero value: fp32, or fp16 / bf16 (META == 1).
+template <int META>
+constexpr int kMetaBytes = META == 1 ? 2 : 4;
+
+// Per-unit buffer of one scale/zero array.
+template <int META>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t meta_rsrc(const void *base, int u, long long NG) {
+  const long long per_unit = NG * D * kMetaBytes<META>;
+  return make_rsrc(static_cast<const char *>(base) + u * per_unit, (uint32_t)per_unit);
+}
+
+template <int BITS, int META>
 __device__ __forceinline__ UnitView make_view(const DecodeArgs &a, int u, int n, int gq, int cm) {
   constexpr int KROW = D * BITS / 8;
   constexpr int CB = 32 * BITS / 8;
   const long long T = a.max_tokens, NG = a.n_groups_cap;
   UnitView v;
-  const uint32_t code_bytes = (uint32_t)(T * KROW), meta_bytes = (uint32_t)(NG * D * 4);
+  const uint32_t code_bytes = (uint32_t)(T * KROW);
   v.kc = make_rsrc(a.k_codes + u * T * KROW, code_bytes);
   v.vc = make_rsrc(a.v_codes + u * T * KROW, code_bytes);
-  v.ks = make_rsrc(a.k_scale + u * NG * D, meta_bytes);
-  v.kz = make_rsrc(a.k_zero + u * NG * D, meta_bytes);
-  v.vs = make_rsrc(a.v_scale + u * NG * D, meta_bytes);
-  v.vz = make_rsrc(a.v_zero + u * NG * D, meta_bytes);
+  v.ks = meta_rsrc<META>(a.k_scale, u, NG);
+  v.kz = meta_rsrc<META>(a.k_zero, u, NG);
+  v.vs = meta_rsrc<META>(a.v_scale, u, NG);
+  v.vz = meta_rsrc<META>(a.v_zero, u, NG);
   const int kr0 = 8 * (n >> 2) + (n & 3);   // A-operand row n of tile 0 -> token; tile 1: +4
   v.o_k0 = kr0 * KROW + gq * CB;
   v.o_k1 = (kr0 + 4) * KROW + gq * CB;
   v.o_v = (gq * D + 8 * n) * BITS;
-  v.o_mu = (16 * gq + n) * 8;   // = 8 * lane
+  v.o_mu = (16 * gq + n) * 2 * kMetaBytes<META>;   // two values per lane
   return v;
 }
 
@@ -334,11 +345,11 @@ __device__ __forceinline__ UnitView make_view(const DecodeArgs &a, int u, int n,
 // the group it computes and not for the prefetches behind it.
 constexpr uint32_t kOutOfRange = 0x80000000u;   // > any unit's buffer size
 
-template <int BITS>
+template <int BITS, int META>
 __device__ __forceinline__ void load_group(GroupRaw<BITS> &r, const UnitView &v, int g, bool live) {
   // group offsets are wave-uniform: keep them in SGPRs (scalar buffer offsets)
   const uint32_t sc = __builtin_amdgcn_readfirstlane((uint32_t)g * (G * D * BITS / 8));
-  const uint32_t sm = __builtin_amdgcn_readfirstlane((uint32_t)g * (D * 4));
+  const uint32_t sm = __builtin_amdgcn_readfirstlane((uint32_t)g * (D * kMetaBytes<META>));
   const uint32_t ob = live ? 0u : kOutOfRange;
   const uint32_t o_k0 = v.o_k0 + ob, o_k1 = v.o_k1 + ob, o_v = v.o_v + ob, o_mu = v.o_mu + ob;
   if constexpr (BITS == 2) {
@@ -360,14 +371,46 @@ __device__ __forceinline__ void load_group(GroupRaw<BITS> &r, const UnitView &v,
       r.vw[i] = c[i]; r.vw[4 + i] = d[i];
     }
   }
-  // scale/zero: each lane loads 8 unique bytes of each 512-byte array; the
-  // values every role needs are re-read from LDS (mfma_group)
+  // scale/zero: each lane loads the two values at 2*lane of each array (128
+  // values per group); the values every role needs are re-read from LDS
+  // (stage_meta)
   const __amdgpu_buffer_rsrc_t mr[4] = {v.ks, v.kz, v.vs, v.vz};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const u32x2_t x = __builtin_amdgcn_raw_buffer_load_b64(mr[i], o_mu, sm, 0);
-    r.mw[i][0] = x[0];
-    r.mw[i][1] = x[1];
+    if constexpr (META == 1) {
+      r.mw[i][0] = __builtin_amdgcn_raw_buffer_load_b32(mr[i], o_mu, sm, 0);
+      r.mw[i][1] = 0;
+    } else {
+      const u32x2_t x = __builtin_amdgcn_raw_buffer_load_b64(mr[i], o_mu, sm, 0);
+      r.mw[i][0] = x[0];
+      r.mw[i][1] = x[1];
+    }
+  }
+}
+
+// Write this lane's two values of each scale/zero array to the wave's LDS
+// slot as floats (arrays: k_scale, k_zero, v_scale, v_zero).  META == 1:
+// fp16 scales and bf16 zeros are widened exactly.
+template <int META>
+__device__ __forceinline__ void stage_meta(const uint32_t (&mw)[4][2], float (*meta)[D], int lane) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint2 w;
+    if constexpr (META == 1) {
+      const uint32_t x = mw[i][0];
+      float lo, hi;
+      if (i == 0 || i == 2) {   // fp16 scale
+        lo = (float)__builtin_bit_cast(_Float16, (uint16_t)(x & 0xFFFFu));
+        hi = (float)__builtin_bit_cast(_Float16, (uint16_t)(x >> 16));
+      } else {                  // bf16 zero
+        lo = __uint_as_float(x << 16);
+        hi = __uint_as_float(x & 0xFFFF0000u);
+      }
+      w = make_uint2(__float_as_uint(lo), __float_as_uint(hi));
+    } else {
+      w = make_uint2(mw[i][0], mw[i][1]);
+    }
+    *reinterpret_cast<uint2 *>(&meta[i][2 * lane]) = w;
   }
 }
 
@@ -396,17 +439,12 @@ struct WaveState {
   float m_run[NHB], l_run[NHB], z_run[NHB];
 };
 
-template <int BITS, int NHB>
+template <int BITS, int NHB, int META>
 __device__ __forceinline__ void mfma_group(const GroupRaw<BITS> &raw, WaveState<NHB> &st,
                                            MfmaSmem<NHB> &smf, const float (&qv)[NHB][8],
                                            int wave, int n, int gq, int ch, int cm) {
   // scale/zero of this group: stage in LDS, read back what each role needs
-  {
-    const int lane = 16 * gq + n;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<uint2 *>(&smf.meta[wave][i][2 * lane]) = make_uint2(raw.mw[i][0], raw.mw[i][1]);
-  }
+  stage_meta<META>(raw.mw, smf.meta[wave], 16 * gq + n);
   __builtin_amdgcn_wave_barrier();
   struct {
     const uint32_t (&kw)[2][BITS];
@@ -689,7 +727,7 @@ __device__ __forceinline__ WorkRange wave_work(const DecodeArgs &a, int u, int s
 // tokens -- into rank-weighted byte shares (wave_work), and each workgroup
 // splits its share over its 4 waves.  Item costs are in KiB: a group (codes
 // + scale/zero) is bits + 2, a residual chunk (32 bf16 K and V rows) is 16.
-template <int BITS, int NHB>
+template <int BITS, int NHB, int META>
 __global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeArgs a) {
   constexpr int HMAX = 4 * NHB;
   __shared__ __align__(16) union {
@@ -706,7 +744,7 @@ __global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeArgs a) {
   const int b = u / a.kv_heads, h = u % a.kv_heads;
 
   // this wave's byte share of the unit, and the items that start inside it
-  const WorkRange wr = wave_work(a, u, split, wave, BITS + 2, 16);
+  const WorkRange wr = wave_work(a, u, split, wave, BITS + kMetaBytes<META> / 2, 16);
   const int g_begin = wr.g_begin, g_end = wr.g_end, r_begin = wr.r_begin, r_end = wr.r_end;
 
   // Order of the first loads: the query (needed first), then the first two
@@ -721,10 +759,10 @@ __global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeArgs a) {
           a.q + ((long long)b * a.kv_heads * qpk + (long long)h * qpk + hh) * D + 32 * gq + 8 * cm);
   }
   const bool has_groups = g_begin < g_end;
-  const UnitView view = make_view<BITS>(a, u, n, gq, cm);
+  const UnitView view = make_view<BITS, META>(a, u, n, gq, cm);
   GroupRaw<BITS> r0, r1, r2;
-  load_group<BITS>(r0, view, g_begin, has_groups);
-  load_group<BITS>(r1, view, g_begin + 1, g_begin + 1 < g_end);
+  load_group<BITS, META>(r0, view, g_begin, has_groups);
+  load_group<BITS, META>(r1, view, g_begin + 1, g_begin + 1 < g_end);
 
   // scaled query values in slot order for the cooperative role
   float qv[NHB][8];
@@ -754,14 +792,14 @@ __global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeArgs a) {
   if (has_groups) {
     int g = g_begin;
     while (true) {
-      load_group<BITS>(r2, view, g + 2, g + 2 < g_end);
-      mfma_group<BITS, NHB>(r0, st, sm.mf, qv, wave, n, gq, ch, cm);
+      load_group<BITS, META>(r2, view, g + 2, g + 2 < g_end);
+      mfma_group<BITS, NHB, META>(r0, st, sm.mf, qv, wave, n, gq, ch, cm);
       if (++g >= g_end) break;
-      load_group<BITS>(r0, view, g + 2, g + 2 < g_end);
-      mfma_group<BITS, NHB>(r1, st, sm.mf, qv, wave, n, gq, ch, cm);
+      load_group<BITS, META>(r0, view, g + 2, g + 2 < g_end);
+      mfma_group<BITS, NHB, META>(r1, st, sm.mf, qv, wave, n, gq, ch, cm);
       if (++g >= g_end) break;
-      load_group<BITS>(r1, view, g + 2, g + 2 < g_end);
-      mfma_group<BITS, NHB>(r2, st, sm.mf, qv, wave, n, gq, ch, cm);
+      load_group<BITS, META>(r1, view, g + 2, g + 2 < g_end);
+      mfma_group<BITS, NHB, META>(r2, st, sm.mf, qv, wave, n, gq, ch, cm);
       if (++g >= g_end) break;
     }
   }
@@ -819,31 +857,31 @@ struct ValuView {
   uint32_t o_k, o_v, o_mu;
 };
 
-template <int BITS>
+template <int BITS, int META>
 __device__ __forceinline__ ValuView make_valu_view(const DecodeArgs &a, int u, int tb, int cb,
                                                    int oc, int cq, int lane) {
   constexpr int KROW = D * BITS / 8;
   const long long T = a.max_tokens, NG = a.n_groups_cap;
   ValuView v;
-  const uint32_t code_bytes = (uint32_t)(T * KROW), meta_bytes = (uint32_t)(NG * D * 4);
+  const uint32_t code_bytes = (uint32_t)(T * KROW);
   v.kc = make_rsrc(a.k_codes + u * T * KROW, code_bytes);
   v.vc = make_rsrc(a.v_codes + u * T * KROW, code_bytes);
-  v.ks = make_rsrc(a.k_scale + u * NG * D, meta_bytes);
-  v.kz = make_rsrc(a.k_zero + u * NG * D, meta_bytes);
-  v.vs = make_rsrc(a.v_scale + u * NG * D, meta_bytes);
-  v.vz = make_rsrc(a.v_zero + u * NG * D, meta_bytes);
+  v.ks = meta_rsrc<META>(a.k_scale, u, NG);
+  v.kz = meta_rsrc<META>(a.k_zero, u, NG);
+  v.vs = meta_rsrc<META>(a.v_scale, u, NG);
+  v.vz = meta_rsrc<META>(a.v_zero, u, NG);
   v.o_k = 4 * tb * KROW + 2 * BITS * cb;
   v.o_v = (oc * D + 8 * cq) * BITS;
-  v.o_mu = 8 * lane;
+  v.o_mu = 2 * kMetaBytes<META> * lane;
   return v;
 }
 
 // Loads of group g (live == false: out-of-range loads, see load_group).
-template <int BITS>
+template <int BITS, int META>
 __device__ __forceinline__ void load_valu_group(ValuRaw<BITS> &r, const ValuView &v, int g, bool live) {
   constexpr int KROW = D * BITS / 8;
   const uint32_t sc = __builtin_amdgcn_readfirstlane((uint32_t)g * (G * D * BITS / 8));
-  const uint32_t sm = __builtin_amdgcn_readfirstlane((uint32_t)g * (D * 4));
+  const uint32_t sm = __builtin_amdgcn_readfirstlane((uint32_t)g * (D * kMetaBytes<META>));
   const uint32_t ob = live ? 0u : kOutOfRange;
   const uint32_t o_k = v.o_k + ob, o_v = v.o_v + ob, o_mu = v.o_mu + ob;
 #pragma unroll
@@ -869,9 +907,14 @@ __device__ __forceinline__ void load_valu_group(ValuRaw<BITS> &r, const ValuView
   const __amdgpu_buffer_rsrc_t mr[4] = {v.ks, v.kz, v.vs, v.vz};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const u32x2_t x = __builtin_amdgcn_raw_buffer_load_b64(mr[i], o_mu, sm, 0);
-    r.mw[i][0] = x[0];
-    r.mw[i][1] = x[1];
+    if constexpr (META == 1) {
+      r.mw[i][0] = __builtin_amdgcn_raw_buffer_load_b32(mr[i], o_mu, sm, 0);
+      r.mw[i][1] = 0;
+    } else {
+      const u32x2_t x = __builtin_amdgcn_raw_buffer_load_b64(mr[i], o_mu, sm, 0);
+      r.mw[i][0] = x[0];
+      r.mw[i][1] = x[1];
+    }
   }
 }
 
@@ -921,13 +964,11 @@ __device__ __forceinline__ void valu_softmax(float (&s4)[4], ValuState &st, Valu
   __builtin_amdgcn_wave_barrier();
 }
 
-template <int BITS>
+template <int BITS, int META>
 __device__ __forceinline__ void valu_group(const ValuRaw<BITS> &raw, ValuState &st, ValuSmem &sm,
                                            const float (&qv)[16], const ValuLane &L) {
   // scale/zero of this group: stage in LDS, read back what each role needs
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    *reinterpret_cast<uint2 *>(&sm.meta[L.wave][i][2 * L.lane]) = make_uint2(raw.mw[i][0], raw.mw[i][1]);
+  stage_meta<META>(raw.mw, sm.meta[L.wave], L.lane);
   __builtin_amdgcn_wave_barrier();
   float sk[16], zk[16], sv[8], zv[8];
   {
@@ -1076,7 +1117,7 @@ __device__ __forceinline__ void valu_rchunk(const DecodeArgs &a, int u, int rc, 
   }
 }
 
-template <int BITS>
+template <int BITS, int META>
 __global__ __launch_bounds__(256) void decode_mha_kernel(DecodeArgs a) {
   __shared__ __align__(16) union {
     ValuSmem vs;
@@ -1088,16 +1129,16 @@ __global__ __launch_bounds__(256) void decode_mha_kernel(DecodeArgs a) {
   L.lane = threadIdx.x & 63;
   L.tb = L.lane >> 3; L.cb = L.lane & 7;
   L.oc = L.lane >> 4; L.cq = L.lane & 15;
-  const WorkRange wr = wave_work(a, u, split, L.wave, BITS + 2, 16);
+  const WorkRange wr = wave_work(a, u, split, L.wave, BITS + kMetaBytes<META> / 2, 16);
 
   // the query first, then the first two groups (see decode_gqa_kernel)
   const uint4 *qp = reinterpret_cast<const uint4 *>(a.q + (long long)u * D + 16 * L.cb);
   const uint4 qraw[2] = {qp[0], qp[1]};
   const bool has_groups = wr.g_begin < wr.g_end;
-  const ValuView view = make_valu_view<BITS>(a, u, L.tb, L.cb, L.oc, L.cq, L.lane);
+  const ValuView view = make_valu_view<BITS, META>(a, u, L.tb, L.cb, L.oc, L.cq, L.lane);
   ValuRaw<BITS> r0, r1, r2;
-  load_valu_group<BITS>(r0, view, wr.g_begin, has_groups);
-  load_valu_group<BITS>(r1, view, wr.g_begin + 1, wr.g_begin + 1 < wr.g_end);
+  load_valu_group<BITS, META>(r0, view, wr.g_begin, has_groups);
+  load_valu_group<BITS, META>(r1, view, wr.g_begin + 1, wr.g_begin + 1 < wr.g_end);
   float qv[16];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -1117,14 +1158,14 @@ __global__ __launch_bounds__(256) void decode_mha_kernel(DecodeArgs a) {
   if (has_groups) {
     int g = wr.g_begin;
     while (true) {
-      load_valu_group<BITS>(r2, view, g + 2, g + 2 < wr.g_end);
-      valu_group<BITS>(r0, st, sm.vs, qv, L);
+      load_valu_group<BITS, META>(r2, view, g + 2, g + 2 < wr.g_end);
+      valu_group<BITS, META>(r0, st, sm.vs, qv, L);
       if (++g >= wr.g_end) break;
-      load_valu_group<BITS>(r0, view, g + 2, g + 2 < wr.g_end);
-      valu_group<BITS>(r1, st, sm.vs, qv, L);
+      load_valu_group<BITS, META>(r0, view, g + 2, g + 2 < wr.g_end);
+      valu_group<BITS, META>(r1, st, sm.vs, qv, L);
       if (++g >= wr.g_end) break;
-      load_valu_group<BITS>(r1, view, g + 2, g + 2 < wr.g_end);
-      valu_group<BITS>(r2, st, sm.vs, qv, L);
+      load_valu_group<BITS, META>(r1, view, g + 2, g + 2 < wr.g_end);
+      valu_group<BITS, META>(r2, st, sm.vs, qv, L);
       if (++g >= wr.g_end) break;
     }
   }
@@ -1153,16 +1194,21 @@ __global__ __launch_bounds__(256) void decode_mha_kernel(DecodeArgs a) {
 namespace {
 
 // Kernel variants: 0 = MHA (VALU), 1..4 = GQA with that many blocks of 4
-// query heads.
-void *kernel_fn(int bits, int variant) {
-  const bool b4 = bits == 4;
+// query heads; for each bit width and scale/zero format.
+template <int BITS, int META>
+void *kernel_fn_t(int variant) {
   switch (variant) {
-    case 0: return b4 ? (void *)&decode_mha_kernel<4> : (void *)&decode_mha_kernel<2>;
-    case 1: return b4 ? (void *)&decode_gqa_kernel<4, 1> : (void *)&decode_gqa_kernel<2, 1>;
-    case 2: return b4 ? (void *)&decode_gqa_kernel<4, 2> : (void *)&decode_gqa_kernel<2, 2>;
-    case 3: return b4 ? (void *)&decode_gqa_kernel<4, 3> : (void *)&decode_gqa_kernel<2, 3>;
-    default: return b4 ? (void *)&decode_gqa_kernel<4, 4> : (void *)&decode_gqa_kernel<2, 4>;
+    case 0: return (void *)&decode_mha_kernel<BITS, META>;
+    case 1: return (void *)&decode_gqa_kernel<BITS, 1, META>;
+    case 2: return (void *)&decode_gqa_kernel<BITS, 2, META>;
+    case 3: return (void *)&decode_gqa_kernel<BITS, 3, META>;
+    default: return (void *)&decode_gqa_kernel<BITS, 4, META>;
   }
+}
+
+void *kernel_fn(int bits, int meta, int variant) {
+  if (bits == 2) return meta == 1 ? kernel_fn_t<2, 1>(variant) : kernel_fn_t<2, 0>(variant);
+  return meta == 1 ? kernel_fn_t<4, 1>(variant) : kernel_fn_t<4, 0>(variant);
 }
 
 // Occupancy of a kernel variant on the current device: resident workgroups
@@ -1172,15 +1218,16 @@ struct Residency {
   int per_cu, cus;
 };
 
-Residency residency(int bits, int variant) {
-  static int cache[16][2][5][2];   // 0 = not yet queried
+Residency residency(int bits, int meta, int variant) {
+  static int cache[16][2][2][5][2];   // 0 = not yet queried
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
-  int *slot = cache[dev & 15][bits == 4 ? 1 : 0][variant];
+  int *slot = cache[dev & 15][bits == 4 ? 1 : 0][meta == 1 ? 1 : 0][variant];
   Residency r{__atomic_load_n(&slot[0], __ATOMIC_RELAXED), __atomic_load_n(&slot[1], __ATOMIC_RELAXED)};
   if (r.per_cu > 0 && r.cus > 0) return r;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&r.per_cu, kernel_fn(bits, variant), 256, 0) !=
-          hipSuccess || r.per_cu < 1)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&r.per_cu, kernel_fn(bits, meta, variant), 256,
+                                                   0) != hipSuccess ||
+      r.per_cu < 1)
     r.per_cu = 1;
   if (hipDeviceGetAttribute(&r.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || r.cus < 1)
     r.cus = 256;
@@ -1219,11 +1266,11 @@ void rank_weights(int per_cu, int (&w)[4]) {
 // the workspace holds the partials.  MI355X sweeps: 6 per unit at the 8K GQA
 // workload (one round), 1-2 at the 13B-shaped MHA memory wall (batch
 // 64-316, many rounds).  KIVI_WPU fixes the count (sweeps).
-int choose_wpu(int bits, const DecodeArgs &a, int slots) {
+int choose_wpu(int group_cost, const DecodeArgs &a, int slots) {
   constexpr double kWgFixed = 40.0;
   const long long n_rc = (a.n_res + G - 1) / G;
-  const long long total = (long long)a.n_groups * (bits + 2) + n_rc * 16;
-  long long cap = total / (4 * 2 * (bits + 2));
+  const long long total = (long long)a.n_groups * group_cost + n_rc * 16;
+  long long cap = total / (4 * 2 * group_cost);
   if (cap < 1) cap = 1;
   if (cap > a.n_split) cap = a.n_split;   // workspace capacity in partials per unit
   if (cap > 256) cap = 256;
@@ -1244,12 +1291,14 @@ int choose_wpu(int bits, const DecodeArgs &a, int slots) {
 
 }  // namespace
 
-hipError_t launch_decode(int bits, const DecodeArgs &a_in, hipStream_t s) {
+hipError_t launch_decode(int bits, int meta, const DecodeArgs &a_in, hipStream_t s) {
   const int variant = a_in.qpk == 1 ? 0 : (a_in.qpk + 3) / 4;
   DecodeArgs a = a_in;
-  const Residency res = residency(bits, variant);
+  const Residency res = residency(bits, meta, variant);
   const int slots = res.per_cu * res.cus;
-  a.n_split = choose_wpu(bits, a_in, slots);   // a_in.n_split: capacity
+  // KiB per group: codes (bits) + scale/zero (2 fp32 or 1 16-bit)
+  const int group_cost = bits + (meta == 1 ? 1 : 2);
+  a.n_split = choose_wpu(group_cost, a_in, slots);   // a_in.n_split: capacity
   a.cus = res.cus;
   // rank weights only mean something when every workgroup is resident at once
   if ((long long)a.n_split * a.n_units <= slots) {
@@ -1258,8 +1307,8 @@ hipError_t launch_decode(int bits, const DecodeArgs &a_in, hipStream_t s) {
     for (int i = 0; i < 4; ++i) a.rank_w[i] = 1;
   }
   const dim3 grid(a.n_units, a.n_split), block(256);
-  hipLaunchKernelGGL(reinterpret_cast<void (*)(DecodeArgs)>(kernel_fn(bits, variant)), grid, block,
-                     0, s, a);
+  hipLaunchKernelGGL(reinterpret_cast<void (*)(DecodeArgs)>(kernel_fn(bits, meta, variant)), grid,
+                     block, 0, s, a);
   return hipGetLastError();
 }
 

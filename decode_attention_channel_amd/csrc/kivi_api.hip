@@ -28,6 +28,8 @@ kivi_status check_geom(const kivi_geom *g) {
       g->bits <= 0 || g->group <= 0 || g->residual < 0 || g->max_tokens < 0)
     return KIVI_E_GEOMETRY;
   if (g->bits != 2 && g->bits != 4) return KIVI_E_UNSUPPORTED;
+  if (g->meta_format != KIVI_META_FP32 && g->meta_format != KIVI_META_FP16_BF16)
+    return KIVI_E_UNSUPPORTED;
   if (g->group != kivi::kGroup || g->head_dim != kivi::kHeadDim) return KIVI_E_UNSUPPORTED;
   if (g->residual % g->group != 0 || g->residual > 4096) return KIVI_E_UNSUPPORTED;
   if (g->q_per_kv > 16) return KIVI_E_UNSUPPORTED;
@@ -85,7 +87,7 @@ kivi_status enqueue_flush(const kivi_geom *g, kivi_cache *c, hipStream_t s) {
   a.max_tokens = g->max_tokens; a.n_groups_cap = g->max_tokens / G;
   a.k_codes = c->k_codes; a.k_scale = c->k_scale; a.k_zero = c->k_zero;
   a.v_codes = c->v_codes; a.v_scale = c->v_scale; a.v_zero = c->v_zero;
-  kivi_status st = hip_status(kivi::launch_quantize(g->bits, a, s));
+  kivi_status st = hip_status(kivi::launch_quantize(g->bits, g->meta_format, a, s));
   if (st != KIVI_OK) return st;
   c->n_q += G;
   c->n_res -= G;
@@ -149,7 +151,7 @@ kivi_status enqueue_attend(const kivi_geom *g, const kivi_cache *c, const uint16
   a.n_res = c->n_res; a.res_start = c->res_start;
   // the launcher picks the workgroups per unit; pass the workspace capacity
   a.n_split = max_splits(g);
-  return hip_status(kivi::launch_decode(g->bits, a, s));
+  return hip_status(kivi::launch_decode(g->bits, g->meta_format, a, s));
 }
 
 }  // namespace
@@ -181,12 +183,13 @@ kivi_status kivi_cache_layout(const kivi_geom *g, size_t bytes[8]) {
   const size_t U = (size_t)units_of(g), T = (size_t)g->max_tokens, D = (size_t)g->head_dim;
   const size_t G = (size_t)g->group, NG = T / G, b = (size_t)g->bits;
   const size_t slots = (size_t)(g->residual + g->group);
+  const size_t mb = g->meta_format == KIVI_META_FP16_BF16 ? 2 : 4;   // bytes per scale/zero
   bytes[KIVI_BUF_K_CODES] = U * T * D * b / 8;
-  bytes[KIVI_BUF_K_SCALE] = U * NG * D * 4;
-  bytes[KIVI_BUF_K_ZERO] = U * NG * D * 4;
+  bytes[KIVI_BUF_K_SCALE] = U * NG * D * mb;
+  bytes[KIVI_BUF_K_ZERO] = U * NG * D * mb;
   bytes[KIVI_BUF_V_CODES] = U * NG * (G / 8) * D * b;
-  bytes[KIVI_BUF_V_SCALE] = U * NG * (D / G) * G * 4;
-  bytes[KIVI_BUF_V_ZERO] = U * NG * (D / G) * G * 4;
+  bytes[KIVI_BUF_V_SCALE] = U * NG * (D / G) * G * mb;
+  bytes[KIVI_BUF_V_ZERO] = U * NG * (D / G) * G * mb;
   bytes[KIVI_BUF_K_RES] = U * slots * D * 2;
   bytes[KIVI_BUF_V_RES] = U * slots * D * 2;
   return KIVI_OK;
@@ -223,7 +226,7 @@ kivi_status kivi_quantize_prefill(const kivi_geom *g, kivi_cache *c, const uint1
     a.max_tokens = g->max_tokens; a.n_groups_cap = g->max_tokens / G;
     a.k_codes = c->k_codes; a.k_scale = c->k_scale; a.k_zero = c->k_zero;
     a.v_codes = c->v_codes; a.v_scale = c->v_scale; a.v_zero = c->v_zero;
-    if ((st = hip_status(kivi::launch_quantize(g->bits, a, s))) != KIVI_OK) return st;
+    if ((st = hip_status(kivi::launch_quantize(g->bits, g->meta_format, a, s))) != KIVI_OK) return st;
   }
   if (r > 0) {
     kivi::CopyRowsArgs a{};

@@ -25,11 +25,11 @@ struct QuantizeArgs {
   int n_groups, n_units;
   int dst_g0;
   int max_tokens, n_groups_cap;  // T, NG
-  uint8_t *k_codes; float *k_scale, *k_zero;
-  uint8_t *v_codes; float *v_scale, *v_zero;
+  uint8_t *k_codes; void *k_scale, *k_zero;   // fp32, or fp16 / bf16 bits (meta)
+  uint8_t *v_codes; void *v_scale, *v_zero;
   int gpw;   // groups per workgroup (set by the launcher)
 };
-hipError_t launch_quantize(int bits, const QuantizeArgs &a, hipStream_t s);
+hipError_t launch_quantize(int bits, int meta, const QuantizeArgs &a, hipStream_t s);
 
 // Copy `n_rows` bf16 rows of D channels per unit (K and V) from
 // src + u*src_unit_stride + (src_tok0 + i)*D to dst + u*dst_unit_stride +
@@ -46,8 +46,8 @@ struct CopyRowsArgs {
 hipError_t launch_copy_rows(const CopyRowsArgs &a, hipStream_t s);
 
 struct DecodeArgs {
-  const uint8_t *k_codes; const float *k_scale, *k_zero;
-  const uint8_t *v_codes; const float *v_scale, *v_zero;
+  const uint8_t *k_codes; const void *k_scale, *k_zero;   // fp32, or fp16 / bf16 bits
+  const uint8_t *v_codes; const void *v_scale, *v_zero;
   uint16_t *k_res, *v_res;   // written only for the fused append below
   // Fused append: logical residual token new_idx (-1: none) is taken from
   // k_new / v_new ([units][D] bf16) instead of the ring, and the one wave
@@ -70,6 +70,6 @@ struct DecodeArgs {
   int cus;
   int rank_w[4];
 };
-hipError_t launch_decode(int bits, const DecodeArgs &a, hipStream_t s);
+hipError_t launch_decode(int bits, int meta, const DecodeArgs &a, hipStream_t s);
 
 }  // namespace kivi

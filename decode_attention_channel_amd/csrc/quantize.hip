@@ -9,6 +9,8 @@
 // single IEEE fp32 operation, rounded to nearest even, nothing fused:
 //     s = (max - min) / L ;  inv = s >= FLT_MIN ? 1 / s : 0 ;
 //     code = clamp(rint((x - min) * inv), 0, L) ;  scale = s, zero = min.
+// With the 16-bit scale/zero format the scale is first rounded to fp16 and
+// the codes use the rounded value; the zero is stored as bf16 (exact).
 //
 // Each workgroup takes `gpw` consecutive groups (one by default) of one unit:
 // two waves quantise the keys (one channel half each), two waves the values
@@ -33,11 +35,25 @@ struct Q {
 __device__ __forceinline__ float bf16_lo(uint32_t x) { return __uint_as_float(x << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t x) { return __uint_as_float(x & 0xFFFF0000u); }
 
-template <int BITS>
-__device__ __forceinline__ void group_params(float mn, float mx, float &s, float &inv) {
+// Scale and reciprocal of one group.  META == 1 (fp16 scale): the scale is
+// rounded to fp16 (nearest even; clamping to 65504 first makes overflow
+// saturate) and the codes are computed from the rounded value; s_bits gets
+// the fp16 bits.
+template <int BITS, int META>
+__device__ __forceinline__ void group_params(float mn, float mx, float &s, float &inv,
+                                             uint32_t &s_bits) {
   s = __fdiv_rn(__fsub_rn(mx, mn), Q<BITS>::kLevels);
+  s_bits = 0;
+  if constexpr (META == 1) {
+    const _Float16 h = (_Float16)fminf(s, 65504.0f);
+    s_bits = __builtin_bit_cast(uint16_t, h);
+    s = (float)h;
+  }
   inv = (s >= FLT_MIN) ? __fdiv_rn(1.0f, s) : 0.0f;
 }
+
+// bf16 bits of a group minimum (a widened bf16 value: exact)
+__device__ __forceinline__ uint32_t zero_bits(float mn) { return __float_as_uint(mn) >> 16; }
 
 template <int BITS>
 __device__ __forceinline__ uint32_t code_of(float x, float mn, float inv) {
@@ -74,7 +90,7 @@ __device__ __forceinline__ float max_x32(float x) {
 // 16h..16h+15: the per-channel min/max over 32 tokens is 16 values in
 // registers plus one exchange with lane ^ 32.  Byte codes go through the
 // wave's LDS tile ([row][64 channels]) and come back in packed row order.
-template <int BITS>
+template <int BITS, int META>
 __device__ __forceinline__ void key_group(const QuantizeArgs &a, int u, int gl,
                                           const uint32_t (&raw)[16], int cb, int lane,
                                           uint8_t *tile) {
@@ -96,13 +112,21 @@ __device__ __forceinline__ void key_group(const QuantizeArgs &a, int u, int gl,
   mn0 = min_x32(mn0); mx0 = max_x32(mx0);
   mn1 = min_x32(mn1); mx1 = max_x32(mx1);
   float sc0, inv0, sc1, inv1;
-  group_params<BITS>(mn0, mx0, sc0, inv0);
-  group_params<BITS>(mn1, mx1, sc1, inv1);
+  uint32_t sb0, sb1;
+  group_params<BITS, META>(mn0, mx0, sc0, inv0, sb0);
+  group_params<BITS, META>(mn1, mx1, sc1, inv1, sb1);
   const int g = a.dst_g0 + gl;
   const long long unit_grp = (long long)u * a.n_groups_cap + g;
   if (h == 0) {
-    reinterpret_cast<float2 *>(a.k_scale + unit_grp * D + cb)[p] = make_float2(sc0, sc1);
-    reinterpret_cast<float2 *>(a.k_zero + unit_grp * D + cb)[p] = make_float2(mn0, mn1);
+    const long long m = unit_grp * D + cb;   // element index of channel cb
+    if constexpr (META == 1) {
+      reinterpret_cast<uint32_t *>(static_cast<uint16_t *>(a.k_scale) + m)[p] = sb0 | (sb1 << 16);
+      reinterpret_cast<uint32_t *>(static_cast<uint16_t *>(a.k_zero) + m)[p] =
+          zero_bits(mn0) | (zero_bits(mn1) << 16);
+    } else {
+      reinterpret_cast<float2 *>(static_cast<float *>(a.k_scale) + m)[p] = make_float2(sc0, sc1);
+      reinterpret_cast<float2 *>(static_cast<float *>(a.k_zero) + m)[p] = make_float2(mn0, mn1);
+    }
   }
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
@@ -130,7 +154,7 @@ __device__ __forceinline__ void key_group(const QuantizeArgs &a, int u, int gl,
   __builtin_amdgcn_wave_barrier();   // tile reads done before the next group's writes
 }
 
-template <int BITS>
+template <int BITS, int META>
 __device__ __forceinline__ void quantize_keys(const QuantizeArgs &a, int u, int gl0, int gl1,
                                               int half, int lane, uint8_t *tile) {
   constexpr int D = kHeadDim, G = kGroup;
@@ -150,16 +174,16 @@ __device__ __forceinline__ void quantize_keys(const QuantizeArgs &a, int u, int 
 #pragma unroll
     for (int i = 0; i < 16; ++i) cur[i] = nxt[i];
     load(gl + 1, nxt);
-    key_group<BITS>(a, u, gl, cur, cb, lane, tile);
+    key_group<BITS, META>(a, u, gl, cur, cb, lane, tile);
   }
-  key_group<BITS>(a, u, gl1 - 1, nxt, cb, lane, tile);
+  key_group<BITS, META>(a, u, gl1 - 1, nxt, cb, lane, tile);
 }
 
 // One wave quantises the values of 16 tokens (two octets) of each of its
 // groups.  Lane (row r, quarter q) owns channels 32q..32q+31 of token r: one
 // whole value group, min/max in registers.  Byte codes go through the wave's
 // LDS tile ([row][128 channels]) and are regathered as octet x channel cells.
-template <int BITS>
+template <int BITS, int META>
 __device__ __forceinline__ void value_group(const QuantizeArgs &a, int u, int gl,
                                             const uint4 (&raw)[4], int part, int lane,
                                             uint8_t *tile) {
@@ -179,12 +203,18 @@ __device__ __forceinline__ void value_group(const QuantizeArgs &a, int u, int gl
 #pragma unroll
   for (int i = 1; i < 32; ++i) { mn = fminf(mn, x[i]); mx = fmaxf(mx, x[i]); }
   float sc, inv;
-  group_params<BITS>(mn, mx, sc, inv);
+  uint32_t sb;
+  group_params<BITS, META>(mn, mx, sc, inv, sb);
   const int g = a.dst_g0 + gl;
   const long long unit_grp = (long long)u * a.n_groups_cap + g;
   const long long mi = (unit_grp * (D / G) + q) * G + 16 * part + r;
-  a.v_scale[mi] = sc;
-  a.v_zero[mi] = mn;
+  if constexpr (META == 1) {
+    static_cast<uint16_t *>(a.v_scale)[mi] = (uint16_t)sb;
+    static_cast<uint16_t *>(a.v_zero)[mi] = (uint16_t)zero_bits(mn);
+  } else {
+    static_cast<float *>(a.v_scale)[mi] = sc;
+    static_cast<float *>(a.v_zero)[mi] = mn;
+  }
   uint32_t cw[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
@@ -213,7 +243,7 @@ __device__ __forceinline__ void value_group(const QuantizeArgs &a, int u, int gl
   __builtin_amdgcn_wave_barrier();
 }
 
-template <int BITS>
+template <int BITS, int META>
 __device__ __forceinline__ void quantize_values(const QuantizeArgs &a, int u, int gl0, int gl1,
                                                 int part, int lane, uint8_t *tile) {
   constexpr int D = kHeadDim, G = kGroup;
@@ -231,24 +261,24 @@ __device__ __forceinline__ void quantize_values(const QuantizeArgs &a, int u, in
 #pragma unroll
     for (int i = 0; i < 4; ++i) cur[i] = nxt[i];
     load(gl + 1, nxt);
-    value_group<BITS>(a, u, gl, cur, part, lane, tile);
+    value_group<BITS, META>(a, u, gl, cur, part, lane, tile);
   }
-  value_group<BITS>(a, u, gl1 - 1, nxt, part, lane, tile);
+  value_group<BITS, META>(a, u, gl1 - 1, nxt, part, lane, tile);
 }
 
 // Grid (ceil(n_groups / gpw), n_units): waves 0-1 take the keys (channel
 // halves), waves 2-3 the values (token halves) of `gpw` consecutive groups
 // (one by default).  The waves share nothing and never wait for each other.
-template <int BITS>
+template <int BITS, int META>
 __global__ __launch_bounds__(256) void quantize_kernel(QuantizeArgs a) {
   __shared__ __align__(16) uint8_t s_tile[4][16 * kHeadDim];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int u = blockIdx.y;
   const int gl0 = blockIdx.x * a.gpw, gl1 = min(gl0 + a.gpw, a.n_groups);
   if (wave < 2)
-    quantize_keys<BITS>(a, u, gl0, gl1, wave, lane, s_tile[wave]);
+    quantize_keys<BITS, META>(a, u, gl0, gl1, wave, lane, s_tile[wave]);
   else
-    quantize_values<BITS>(a, u, gl0, gl1, wave - 2, lane, s_tile[wave]);
+    quantize_values<BITS, META>(a, u, gl0, gl1, wave - 2, lane, s_tile[wave]);
 }
 
 __global__ __launch_bounds__(256) void copy_rows_kernel(CopyRowsArgs a) {
@@ -266,7 +296,7 @@ __global__ __launch_bounds__(256) void copy_rows_kernel(CopyRowsArgs a) {
 
 }  // namespace
 
-hipError_t launch_quantize(int bits, const QuantizeArgs &a_in, hipStream_t s) {
+hipError_t launch_quantize(int bits, int meta, const QuantizeArgs &a_in, hipStream_t s) {
   if (a_in.n_groups <= 0 || a_in.n_units <= 0) return hipSuccess;
   // groups per workgroup: one.  Short independent workgroups keep the most
   // loads in flight; on MI355X at the 8K GQA prefill (16 x 8 units, 252
@@ -276,11 +306,15 @@ hipError_t launch_quantize(int bits, const QuantizeArgs &a_in, hipStream_t s) {
   long long gpw = 1;
   if (const char *env = getenv("KIVI_QGPW")) gpw = atoll(env);
   a.gpw = (int)(gpw < 1 ? 1 : gpw > 8 ? 8 : gpw);
-  const dim3 grid((a.n_groups + a.gpw - 1) / a.gpw, a.n_units);
-  if (bits == 2)
-    hipLaunchKernelGGL(quantize_kernel<2>, grid, dim3(256), 0, s, a);
+  const dim3 grid((a.n_groups + a.gpw - 1) / a.gpw, a.n_units), block(256);
+  if (bits == 2 && meta == 0)
+    hipLaunchKernelGGL((quantize_kernel<2, 0>), grid, block, 0, s, a);
+  else if (bits == 2)
+    hipLaunchKernelGGL((quantize_kernel<2, 1>), grid, block, 0, s, a);
+  else if (meta == 0)
+    hipLaunchKernelGGL((quantize_kernel<4, 0>), grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL(quantize_kernel<4>, grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((quantize_kernel<4, 1>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 

@@ -28,6 +28,7 @@ EXPORTS = (
     "kivi_last_hip_error",
 )
 BUFFERS = ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero", "k_res", "v_res")
+META_FP32, META_FP16_BF16 = 0, 1   # scale/zero formats (kivi_geom.meta_format)
 
 
 class KiviError(RuntimeError):
@@ -43,7 +44,7 @@ class KiviError(RuntimeError):
 class _Geom(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "kv_heads", "q_per_kv", "head_dim", "bits", "group", "residual",
-        "max_tokens")]
+        "max_tokens", "meta_format")]
 
 
 class _Cache(ctypes.Structure):
@@ -99,6 +100,7 @@ class Geom:
     group: int = 32
     residual: int = 128
     max_tokens: int = 0
+    meta_format: int = META_FP32
 
     def c(self) -> _Geom:
         return _Geom(*dataclasses.astuple(self))
@@ -151,13 +153,16 @@ class Cache:
         sizes = cache_layout(g)
         B, H, T, D, b, G = g.batch, g.kv_heads, g.max_tokens, g.head_dim, g.bits, g.group
         NG, S = T // G, g.residual + g.group
+        m16 = g.meta_format == META_FP16_BF16
+        st = torch.float16 if m16 else torch.float32   # scale
+        zt = torch.bfloat16 if m16 else torch.float32  # zero
         shapes = {
             "k_codes": ((B, H, T, D * b // 8), torch.uint8),
-            "k_scale": ((B, H, NG, D), torch.float32),
-            "k_zero": ((B, H, NG, D), torch.float32),
+            "k_scale": ((B, H, NG, D), st),
+            "k_zero": ((B, H, NG, D), zt),
             "v_codes": ((B, H, NG, G // 8, D, b), torch.uint8),
-            "v_scale": ((B, H, NG, D // G, G), torch.float32),
-            "v_zero": ((B, H, NG, D // G, G), torch.float32),
+            "v_scale": ((B, H, NG, D // G, G), st),
+            "v_zero": ((B, H, NG, D // G, G), zt),
             "k_res": ((B, H, S, D), torch.bfloat16),
             "v_res": ((B, H, S, D), torch.bfloat16),
         }

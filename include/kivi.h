@@ -35,6 +35,7 @@
  *    left unchanged.  No exception crosses the ABI.  KIVI_E_HIP is returned
  *    when a launch fails; kivi_last_hip_error() then gives the hipError_t.
  *  - Supported set (v1): bits in {2,4}; group == 32; head_dim == 128;
+ *    meta_format in {KIVI_META_FP32, KIVI_META_FP16_BF16};
  *    residual a multiple of group with 0 <= residual <= 4096;
  *    1 <= q_per_kv <= 16; max_tokens a multiple of group, at most 2^24;
  *    batch, kv_heads >= 1 with batch * kv_heads <= 65535.  Anything else:
@@ -68,17 +69,33 @@
  *  group is G consecutive channels of one token (per-token values).
  *
  * ------------------------------------------------------------------------
+ * 16-bit scale/zero (geom.meta_format = KIVI_META_FP16_BF16; READING: no page
+ * fixes a metadata format, and the record's byte basis counts none)
+ * ------------------------------------------------------------------------
+ *  The zero, the group minimum, is a bf16 input value and is stored exactly
+ *  as bf16.  The scale s = (mx - mn) / L is rounded to fp16 (nearest even;
+ *  values above 65504 saturate to 65504) and the codes are computed from
+ *  that rounded scale with the formula above.  Scale and zero then take 4
+ *  bytes per group instead of 8: at 2-bit, 96 instead of 128 bytes per
+ *  quantised token and kv head.  The error bound is half a step of the
+ *  rounded scale while it is a normal fp16 number (group range >= L * 2^-14);
+ *  below that the scale's own rounding adds up to L times its error.
+ *
+ * ------------------------------------------------------------------------
  * Byte layout of the cache buffers (part of the contract: packed codes and
  * scale/zero are compared byte for byte with an independent CPU oracle)
  * ------------------------------------------------------------------------
  *  k_codes  uint8 [B][H][T][D*b/8]   token row t holds channel c at byte
  *           c*b/8, bits [(c*b)%8, (c*b)%8 + b)  (LSB first).
- *  k_scale, k_zero  fp32 [B][H][NG][D]      (group g, channel c)
+ *  k_scale, k_zero  [B][H][NG][D]          (group g, channel c)
  *  v_codes  uint8 [B][H][NG][G/8][D][b]     group g, octet o (tokens
  *           8o..8o+7 of the group), channel c: b bytes holding the 8 codes
  *           of that channel, token 8o+k at bits [k*b, k*b + b) (LSB first).
- *  v_scale, v_zero  fp32 [B][H][NG][D/G][G] (group g, channel group j,
+ *  v_scale, v_zero  [B][H][NG][D/G][G]     (group g, channel group j,
  *           token i of the group)
+ *           Element type by geom.meta_format: KIVI_META_FP32 -- fp32 scale and
+ *           fp32 zero; KIVI_META_FP16_BF16 -- fp16 scale bits and bf16 zero
+ *           bits (uint16_t), see "16-bit scale/zero" below.
  *  k_res, v_res  bf16 [B][H][R+G][D]        residual ring of R+G slots.
  *           Logical residual token i (0 = oldest) lives in slot
  *           (res_start + i) mod (R+G).  res_start is always a multiple of G.
@@ -120,9 +137,15 @@ typedef enum {
   KIVI_E_STATE = 9           /* cache counters invalid (e.g. empty cache)    */
 } kivi_status;
 
+/* Element types of the scale/zero buffers (kivi_geom.meta_format). */
+enum {
+  KIVI_META_FP32 = 0,        /* fp32 scale, fp32 zero                        */
+  KIVI_META_FP16_BF16 = 1    /* fp16 scale, bf16 zero (uint16_t bit patterns) */
+};
+
 /* Problem statement: batch, kv heads, query heads per kv head (GQA),
- * head_dim, bits, group size G, residual length R, and the capacity of the
- * quantised history in tokens. */
+ * head_dim, bits, group size G, residual length R, the capacity of the
+ * quantised history in tokens, and the scale/zero format (KIVI_META_*). */
 typedef struct {
   int32_t batch;
   int32_t kv_heads;
@@ -132,17 +155,18 @@ typedef struct {
   int32_t group;
   int32_t residual;
   int32_t max_tokens;
+  int32_t meta_format;
 } kivi_geom;
 
 /* The cache: eight caller-owned device buffers laid out as described above,
  * plus three host-side counters that the calls below update. */
 typedef struct {
   uint8_t  *k_codes;
-  float    *k_scale;
-  float    *k_zero;
+  void     *k_scale;    /* fp32, or fp16 bits (meta_format)                */
+  void     *k_zero;     /* fp32, or bf16 bits                              */
   uint8_t  *v_codes;
-  float    *v_scale;
-  float    *v_zero;
+  void     *v_scale;
+  void     *v_zero;
   uint16_t *k_res;
   uint16_t *v_res;
   int32_t   n_q;        /* tokens in the quantised history (multiple of G) */

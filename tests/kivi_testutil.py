@@ -15,8 +15,9 @@ ATTN_TOL = 1e-3
 
 
 def to_np(t: torch.Tensor) -> np.ndarray:
+    """Host copy; 16-bit floats (bf16, fp16) come back as their uint16 bits."""
     t = t.detach().cpu().contiguous()
-    if t.dtype == torch.bfloat16:
+    if t.dtype in (torch.bfloat16, torch.float16):
         return t.view(torch.int16).numpy().view(np.uint16)
     return t.numpy()
 
@@ -51,8 +52,8 @@ def assert_same_cache(got: oracle.Cache, ref: oracle.Cache, units=None, ref_unit
         np.testing.assert_array_equal(got.k_codes[b, h, :nq], ref.k_codes[rb, rh, :nq], msg)
         np.testing.assert_array_equal(got.v_codes[b, h, :ng], ref.v_codes[rb, rh, :ng], msg)
         for name in ("k_scale", "k_zero", "v_scale", "v_zero"):
-            a = getattr(got, name)[b, h, :ng].view(np.uint32)
-            r = getattr(ref, name)[rb, rh, :ng].view(np.uint32)
+            a = np.ascontiguousarray(getattr(got, name)[b, h, :ng]).view(np.uint8)
+            r = np.ascontiguousarray(getattr(ref, name)[rb, rh, :ng]).view(np.uint8)
             np.testing.assert_array_equal(a, r, f"{msg} {name}")
         go = [(got.res_start + i) % slots for i in range(got.n_res)]
         ro = [(ref.res_start + i) % slots for i in range(ref.n_res)]

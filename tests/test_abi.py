@@ -165,6 +165,18 @@ def test_dense_attention_validation_before_any_device_work():
                  ctypes.c_float(0.1), fake, ws_need, None) == 3
 
 
+def test_16bit_meta_layout_and_rejected_formats():
+    g = _g(meta_format=kivi.META_FP16_BF16)
+    U, T, D, NG, S = 6, 1024, 128, 32, 160
+    assert kivi.cache_layout(g) == [U * T * D * 2 // 8, U * NG * D * 2, U * NG * D * 2,
+                                    U * NG * 4 * D * 2, U * NG * 4 * 32 * 2, U * NG * 4 * 32 * 2,
+                                    U * S * D * 2, U * S * D * 2]
+    for bad in (2, -1):
+        with pytest.raises(kivi.KiviError) as e:
+            kivi.cache_layout(_g(meta_format=bad))
+        assert e.value.status == 3
+
+
 def test_status_strings():
     lib = kivi.raw_library()
     for s in range(10):

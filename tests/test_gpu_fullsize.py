@@ -3,7 +3,8 @@ that bench.py times), checked on sampled (sequence, kv head) units that the
 oracle recomputes one by one:
 
 * Llama-3-8B GQA, batch 16, 8 kv / 32 q heads, 8192 tokens, 2-bit: prefill
-  bytes and decode attention on sampled units;
+  bytes and decode attention on sampled units, with fp32 and with 16-bit
+  (fp16 scale, bf16 zero) scale/zero;
 * Llama-2-7B-shaped MHA layer, batch 8, 32 heads, 4096 tokens, 2-bit:
   prefill, then 128 decode steps (append, flush, attend) with 4 flushes;
 * long-context 4-bit GQA, batch 4, 8 kv / 32 q heads, 32768 tokens: prefill,
@@ -27,8 +28,8 @@ kivi = pytest.importorskip("decode_attention_channel_amd.kivi")
 pytestmark = pytest.mark.gpu
 
 
-def _unit_geoms(w, T):
-    return oracle.Geom(1, 1, w.q_per_kv, bits=w.bits, max_tokens=T)
+def _unit_geoms(w, T, meta=0):
+    return oracle.Geom(1, 1, w.q_per_kv, bits=w.bits, max_tokens=T, meta=meta)
 
 
 def _check_unit_cache(gc, oc1, b, h):
@@ -38,8 +39,8 @@ def _check_unit_cache(gc, oc1, b, h):
     np.testing.assert_array_equal(to_np(gc.k_codes[b, h, :nq]), oc1.k_codes[0, 0, :nq])
     np.testing.assert_array_equal(to_np(gc.v_codes[b, h, :ng]), oc1.v_codes[0, 0, :ng])
     for name in ("k_scale", "k_zero", "v_scale", "v_zero"):
-        np.testing.assert_array_equal(to_np(getattr(gc, name)[b, h, :ng]).view(np.uint32),
-                                      getattr(oc1, name)[0, 0, :ng].view(np.uint32), name)
+        np.testing.assert_array_equal(to_np(getattr(gc, name)[b, h, :ng]).view(np.uint8),
+                                      getattr(oc1, name)[0, 0, :ng].view(np.uint8), name)
     slots = 160
     go = [(gc.res_start + i) % slots for i in range(gc.n_res)]
     ro = [(oc1.res_start + i) % slots for i in range(oc1.n_res)]
@@ -63,15 +64,16 @@ def _sample_units(w, k, seed):
     return sorted(units)
 
 
-@pytest.mark.parametrize("name", ["llama3-8b-gqa-8k", "llama2-13b-mha-wall"])
-def test_prefill_and_decode_full_size(name):
+@pytest.mark.parametrize("name,meta", [("llama3-8b-gqa-8k", 0), ("llama2-13b-mha-wall", 0),
+                                       ("llama3-8b-gqa-8k", 1)])
+def test_prefill_and_decode_full_size(name, meta):
     w = synth.WORKLOADS[name]
     batch = 8 if name == "llama2-13b-mha-wall" else w.batch
-    print(f"workload {name} batch {batch}", flush=True)
+    print(f"workload {name} batch {batch} meta {meta}", flush=True)
     k, v = synth.prefill_kv(w, 11, batch=batch)
     q = synth.query(w, 11, batch=batch)
     T = 32 * math.ceil((w.seq_len - 128 + 32) / 32)
-    g = kivi.Geom(batch, w.kv_heads, w.q_per_kv, bits=w.bits, max_tokens=T)
+    g = kivi.Geom(batch, w.kv_heads, w.q_per_kv, bits=w.bits, max_tokens=T, meta_format=meta)
     gc = kivi.Cache(g)
     kivi.quantize_prefill(g, gc, k.cuda(), v.cuda())
     out = torch.full((batch, w.q_heads, 128), float("nan"), device="cuda")
@@ -80,7 +82,7 @@ def test_prefill_and_decode_full_size(name):
     out_np = to_np(out)
     assert np.isfinite(out_np).all()
     kb, vb, qb = synth.bits_u16(k), synth.bits_u16(v), synth.bits_u16(q)
-    og = _unit_geoms(w, T)
+    og = _unit_geoms(w, T, meta)
     scale = 1.0 / math.sqrt(128)
     for b, h in _sample_units(synth.Workload(name, batch, w.kv_heads, w.q_per_kv, w.seq_len,
                                              w.bits, 1, 3, 8.0), 4, 1):
