@@ -6,4 +6,4 @@ The product is libkivi.so (C ABI in include/kivi.h, HIP kernels in csrc/);
 from . import kivi  # noqa: F401  (raises if libkivi.so is missing)
 from .kivi import (Cache, Geom, KiviError, Workspace, append_token, cache_layout,  # noqa: F401
                    decode_attention, decode_step, dense_decode_attention, flush_residual,
-                   quantize_prefill, workspace_size)
+                   quantize_prefill, ragged_decode_step, ragged_prefill, workspace_size)

@@ -2,6 +2,7 @@
 from __future__ import annotations
 
 import os
+import re
 import subprocess
 import sys
 
@@ -19,7 +20,24 @@ FLAGS = [
     # MFMA accumulators in VGPRs: the kernels stay well inside 256 registers,
     # and AGPR<->VGPR copies around the softmax rescale disappear
     "-mllvm", "-amdgpu-mfma-vgpr-form=1",
+    # per-kernel register / scratch report, checked below
+    "-Rpass-analysis=kernel-resource-usage",
 ]
+
+
+def kernel_resources(remarks: str) -> dict:
+    """{kernel: {"VGPRs": n, "ScratchSize": bytes per lane, ...}} from the
+    compiler's kernel-resource-usage remarks."""
+    out, cur = {}, None
+    for line in remarks.splitlines():
+        m = re.search(r"remark: Function Name: (\S+)", line)
+        if m:
+            cur = out.setdefault(m.group(1), {})
+            continue
+        m = re.search(r"remark:\s+([A-Za-z ]+?)(?: \[[^\]]*\])?: (\d+) \[", line)
+        if m and cur is not None:
+            cur[m.group(1)] = int(m.group(2))
+    return out
 
 
 def build(verbose: bool = False) -> str:
@@ -32,6 +50,15 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
         raise RuntimeError("hipcc failed building libkivi.so")
+    # a kernel that lands in scratch memory (spills, or an argument copy with
+    # an indexed member) runs several times slower: refuse to ship it
+    res = kernel_resources(r.stderr)
+    if not res:
+        raise RuntimeError("no kernel resource report from hipcc")
+    bad = {k: v for k, v in res.items() if v.get("ScratchSize", 0) or v.get("VGPRs Spill", 0)}
+    if bad:
+        os.remove(tmp)
+        raise RuntimeError(f"kernels using scratch memory: {bad}")
     os.replace(tmp, LIB)
     return LIB
 

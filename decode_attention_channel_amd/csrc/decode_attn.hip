@@ -190,7 +190,7 @@ __device__ void merge_and_store(MergeSmem<HMAX> &sm, const DecodeArgs &a, int u,
 // partials of each of its query heads,
 //   M = max m_s,  out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s,
 // writes `out`, and re-arms the counter to zero for the next call.
-__device__ void finish_unit(const DecodeArgs &a, int u, int *s_last) {
+__device__ void finish_unit(const DecodeArgs &a, int u, int *s_last, int4 next_state) {
   // the barrier waits for this workgroup's partial stores (vmcnt) before the
   // arrival is counted
   __syncthreads();
@@ -232,10 +232,47 @@ __device__ void finish_unit(const DecodeArgs &a, int u, int *s_last) {
       }
       M = Mn;
     }
-    a.out[((long long)u * qpk + hh) * D + c] = o / l;
+    // a unit with no token (a flagged sequence of a mixed-length batch) gets 0
+    a.out[((long long)u * qpk + hh) * D + c] = l > 0.f ? o / l : 0.f;
   }
-  if (threadIdx.x == 0)
+  if (threadIdx.x == 0) {
     __hip_atomic_store(a.counters + u, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (a.state_out && u % a.kv_heads == 0)
+      reinterpret_cast<int4 *>(a.state_out)[u / a.kv_heads] = next_state;
+  }
+}
+
+// Mixed-length batches: this unit's counters from its sequence's state
+// (DecodeArgs::state_in), with the step's flush and the fused append applied
+// the same way as kivi_decode_step; the counters of `a` are replaced.  Returns
+// the sequence's state after the step.  A sequence with a flag keeps its
+// cache; one that needs a flush without room for another group gets
+// kSeqFull and no append.  A state row out of range (state_ok) becomes an
+// empty sequence with kSeqBadLength.
+__device__ __forceinline__ int4 apply_unit_state(DecodeArgs &a, int u) {
+  const int4 s = reinterpret_cast<const int4 *>(a.state_in)[u / a.kv_heads];
+  int n_q = s.x, n_res = s.y, res_start = s.z, flags = s.w;
+  if (!state_ok(n_q, n_res, res_start, flags, G, a.slots, a.max_tokens)) {
+    n_q = n_res = res_start = 0;
+    flags = kSeqBadLength;
+  }
+  bool append = flags == 0;
+  if (append && n_res + 1 >= a.slots) {
+    if (n_res + 1 == a.slots && n_q + G <= a.max_tokens) {
+      n_q += G;   // flushed by the launch before this one
+      n_res -= G;
+      res_start = (res_start + G) % a.slots;
+    } else {
+      flags |= kSeqFull;
+      append = false;
+    }
+  }
+  if (flags & kSeqBadLength) n_res = 0;   // nothing valid to attend to
+  a.n_groups = (flags & kSeqBadLength) ? 0 : n_q / G;
+  a.res_start = res_start;
+  a.new_idx = append ? n_res : -1;
+  a.n_res = append ? n_res + 1 : n_res;
+  return make_int4(n_q, a.n_res, res_start, flags);
 }
 
 // ------------------------------------------------------ MFMA (GQA) path ---
@@ -707,7 +744,11 @@ __device__ __forceinline__ WorkRange wave_work(const DecodeArgs &a, int u, int s
   const long long q0 = (long long)a.n_groups * cq, total = q0 + (long long)n_rc * cr;
   long long cum = 0, wsum = 0, wself = 0;
   for (int s = 0; s < a.n_split; ++s) {
-    const int w = a.rank_w[min((s * a.n_units + u) / a.cus, 3)];
+    // a select chain, not an indexed load: the kernel's copy of the
+    // arguments stays in registers (mixed-length batches rewrite its
+    // counters, and an indexed member would move the whole copy to scratch)
+    const int rank = (s * a.n_units + u) / a.cus;
+    const int w = rank == 0 ? a.rank_w[0] : rank == 1 ? a.rank_w[1] : rank == 2 ? a.rank_w[2] : a.rank_w[3];
     cum += s < split ? w : 0;
     wself = s == split ? w : wself;
     wsum += w;
@@ -736,6 +777,7 @@ __global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeArgs a) {
   } sm;
 
   const int u = blockIdx.x, split = blockIdx.y;
+  const int4 next_state = a.state_in ? apply_unit_state(a, u) : make_int4(0, 0, 0, 0);
   // wave index made visibly wave-uniform so that group offsets live in SGPRs
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int n = lane & 15, gq = lane >> 4;          // MFMA column / row, lane group
@@ -833,7 +875,7 @@ __global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeArgs a) {
     }
   }
   merge_and_store<HMAX>(sm.mg, a, u, split);
-  finish_unit(a, u, &sm.mg.last);
+  finish_unit(a, u, &sm.mg.last, next_state);
 }
 
 // ------------------------------------------------------- VALU (MHA) path ---
@@ -1124,6 +1166,7 @@ __global__ __launch_bounds__(256) void decode_mha_kernel(DecodeArgs a) {
     MergeSmem<1> mg;
   } sm;
   const int u = blockIdx.x, split = blockIdx.y;
+  const int4 next_state = a.state_in ? apply_unit_state(a, u) : make_int4(0, 0, 0, 0);
   ValuLane L;
   L.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   L.lane = threadIdx.x & 63;
@@ -1186,7 +1229,7 @@ __global__ __launch_bounds__(256) void decode_mha_kernel(DecodeArgs a) {
     sm.mg.l[L.wave][0] = l;
   }
   merge_and_store<1>(sm.mg, a, u, split);
-  finish_unit(a, u, &sm.mg.last);
+  finish_unit(a, u, &sm.mg.last, next_state);
 }
 
 }  // namespace

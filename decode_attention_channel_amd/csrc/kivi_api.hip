@@ -132,7 +132,8 @@ kivi_status check_attend_args(const kivi_geom *g, const kivi_cache *c, const uin
 // into its ring slot by the kernel) instead of from the ring.
 kivi_status enqueue_attend(const kivi_geom *g, const kivi_cache *c, const uint16_t *k_new,
                            const uint16_t *v_new, const uint16_t *q, float *out,
-                           float softmax_scale, void *ws, hipStream_t s, int slots = 0) {
+                           float softmax_scale, void *ws, hipStream_t s, int slots = 0,
+                           const int32_t *state_in = nullptr, int32_t *state_out = nullptr) {
   kivi::DecodeArgs a{};
   a.k_codes = c->k_codes; a.k_scale = c->k_scale; a.k_zero = c->k_zero;
   a.v_codes = c->v_codes; a.v_scale = c->v_scale; a.v_zero = c->v_zero;
@@ -149,6 +150,7 @@ kivi_status enqueue_attend(const kivi_geom *g, const kivi_cache *c, const uint16
   a.n_units = (int)units_of(g);
   a.n_groups = c->n_q / g->group;
   a.n_res = c->n_res; a.res_start = c->res_start;
+  a.state_in = state_in; a.state_out = state_out;
   // the launcher picks the workgroups per unit; pass the workspace capacity
   a.n_split = max_splits(g);
   return hip_status(kivi::launch_decode(g->bits, g->meta_format, a, s));
@@ -343,6 +345,81 @@ kivi_status kivi_dense_decode_attention(const kivi_geom *g, const uint16_t *k, c
   c.res_start = 0;
   return enqueue_attend(g, &c, nullptr, nullptr, q, out, softmax_scale, ws, (hipStream_t)stream,
                         g->max_tokens);
+}
+
+kivi_status kivi_ragged_prefill(const kivi_geom *g, const kivi_cache *c, const uint16_t *k,
+                                const uint16_t *v, int32_t stride, const int32_t *seq_lens,
+                                int32_t *state, void *stream) {
+  kivi_status st = check_geom(g);
+  if (st != KIVI_OK) return st;
+  if ((st = check_cache(c)) != KIVI_OK) return st;
+  if (!k || !v || !seq_lens || !state) return KIVI_E_NULL;
+  if (stride < 1 || stride > (1 << 24)) return KIVI_E_SEQLEN;
+  hipStream_t s = (hipStream_t)stream;
+  const int G = g->group, R = g->residual, slots = R + G;
+  // the longest possible quantised part sizes the quantiser's grid
+  int nq_max = 0, r_max = 0;
+  if (!kivi::seq_split(stride, stride, G, R, 1 << 30, nq_max, r_max)) return KIVI_E_SEQLEN;
+  if (nq_max > g->max_tokens) nq_max = g->max_tokens / G * G;
+  if (nq_max > 0) {
+    kivi::QuantizeArgs a{};
+    a.src_k = k; a.src_v = v;
+    a.src_unit_stride = (long long)stride * g->head_dim;
+    a.src_tok0 = 0;
+    a.n_groups = nq_max / G; a.n_units = (int)units_of(g); a.dst_g0 = 0;
+    a.max_tokens = g->max_tokens; a.n_groups_cap = g->max_tokens / G;
+    a.k_codes = c->k_codes; a.k_scale = c->k_scale; a.k_zero = c->k_zero;
+    a.v_codes = c->v_codes; a.v_scale = c->v_scale; a.v_zero = c->v_zero;
+    a.seq_lens = seq_lens;
+    a.kv_heads = g->kv_heads; a.residual = R; a.slots = slots; a.stride = stride;
+    if ((st = hip_status(kivi::launch_quantize(g->bits, g->meta_format, a, s))) != KIVI_OK)
+      return st;
+  }
+  kivi::RaggedResidualArgs r{};
+  r.src_k = k; r.src_v = v;
+  r.dst_k = c->k_res; r.dst_v = c->v_res;
+  r.seq_lens = seq_lens; r.state = state;
+  r.n_units = (int)units_of(g); r.kv_heads = g->kv_heads; r.stride = stride;
+  r.group = G; r.residual = R; r.slots = slots; r.max_tokens = g->max_tokens;
+  return hip_status(kivi::launch_ragged_residual(r, s));
+}
+
+kivi_status kivi_ragged_decode_step(const kivi_geom *g, const kivi_cache *c,
+                                    const int32_t *state_in, int32_t *state_out,
+                                    const uint16_t *k_new, const uint16_t *v_new,
+                                    const uint16_t *q, float *out, float softmax_scale, void *ws,
+                                    size_t ws_bytes, void *stream) {
+  kivi_status st = check_geom(g);
+  if (st != KIVI_OK) return st;
+  if ((st = check_cache(c)) != KIVI_OK) return st;
+  if (!state_in || !state_out || !k_new || !v_new) return KIVI_E_NULL;
+  if (state_in == state_out) return KIVI_E_STATE;
+  if ((st = check_attend_args(g, c, q, out, softmax_scale, ws, ws_bytes)) != KIVI_OK) return st;
+  // the flush runs before the fused append, which needs R >= G (see
+  // kivi_decode_step)
+  if (g->residual < g->group) return KIVI_E_UNSUPPORTED;
+  hipStream_t s = (hipStream_t)stream;
+  const int G = g->group, slots = g->residual + G;
+  // 1. flush: each sequence whose ring fills with this step's append
+  kivi::QuantizeArgs f{};
+  f.src_k = c->k_res; f.src_v = c->v_res;
+  f.src_unit_stride = (long long)slots * g->head_dim;
+  f.n_groups = 1; f.n_units = (int)units_of(g);
+  f.max_tokens = g->max_tokens; f.n_groups_cap = g->max_tokens / G;
+  f.k_codes = c->k_codes; f.k_scale = c->k_scale; f.k_zero = c->k_zero;
+  f.v_codes = c->v_codes; f.v_scale = c->v_scale; f.v_zero = c->v_zero;
+  f.state = state_in;
+  f.kv_heads = g->kv_heads; f.residual = g->residual; f.slots = slots;
+  if ((st = hip_status(kivi::launch_quantize(g->bits, g->meta_format, f, s))) != KIVI_OK)
+    return st;
+  // 2. attention with the fused append; every sequence's counters come from
+  // state_in, the launch shape from the capacity
+  kivi_cache bound = *c;
+  bound.n_q = g->max_tokens / G * G;
+  bound.n_res = slots;
+  bound.res_start = 0;
+  return enqueue_attend(g, &bound, k_new, v_new, q, out, softmax_scale, ws, s, 0, state_in,
+                        state_out);
 }
 
 }  // extern "C"

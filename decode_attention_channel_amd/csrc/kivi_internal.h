@@ -14,6 +14,33 @@ constexpr int kGroup = 32;         // supported group size G
 constexpr int kPartStride = 132;   // floats per split partial: m, l, pad, pad, o[128]
 constexpr int kMinGroupsPerSplit = 4;   // sizes the workspace: NG/4 + 1 partials per unit
 
+// Per-sequence state of a mixed-length batch (device memory): int32
+// {n_q, n_res, res_start, flags} per sequence.  Flag bits (kivi.h):
+constexpr int kSeqBadLength = 1;   // KIVI_SEQ_BAD_LENGTH
+constexpr int kSeqFull = 2;        // KIVI_SEQ_FULL
+
+// A state row that the mixed-length calls can have written: whole groups of
+// history within capacity, a ring that is not yet full, a ring start on a
+// group boundary, known flags.  Anything else is taken as a bad sequence, so
+// that no launch indexes the cache with it.
+__host__ __device__ inline bool state_ok(int n_q, int n_res, int res_start, int flags, int G,
+                                         int slots, int T) {
+  return n_q >= 0 && n_q <= T && n_q % G == 0 && n_res >= 0 && n_res < slots &&
+         res_start >= 0 && res_start < slots && res_start % G == 0 && (flags & ~3) == 0;
+}
+
+// Prefill split of a sequence of S tokens (see kivi.h): false when S is out
+// of [1, stride] or the quantised part does not fit T tokens.
+__host__ __device__ inline bool seq_split(int S, int stride, int G, int R, int T, int &n_q,
+                                          int &r) {
+  n_q = 0;
+  r = 0;
+  if (S < 1 || S > stride) return false;
+  n_q = S > R ? G * ((S - R) / G) : 0;
+  r = S - n_q;
+  return n_q <= T;
+}
+
 // One launch of the group quantiser: `n_groups` groups of G tokens for each
 // of `n_units` units.  Source token i of local group gl of unit u is row
 // (src_tok0 + gl*G + i) of a [rows][D] bf16 block starting at
@@ -28,6 +55,12 @@ struct QuantizeArgs {
   uint8_t *k_codes; void *k_scale, *k_zero;   // fp32, or fp16 / bf16 bits (meta)
   uint8_t *v_codes; void *v_scale, *v_zero;
   int gpw;   // groups per workgroup (set by the launcher)
+  // Mixed-length batches (null otherwise).  seq_lens (prefill): sequence b
+  // quantises its own n_q tokens, n_groups being the largest count.  state
+  // (flush): sequence b flushes iff its ring will be full after this step's
+  // append, from its own ring start into its own next group.
+  const int32_t *seq_lens, *state;
+  int kv_heads, residual, slots, stride;
 };
 hipError_t launch_quantize(int bits, int meta, const QuantizeArgs &a, hipStream_t s);
 
@@ -44,6 +77,17 @@ struct CopyRowsArgs {
   int n_rows, n_units;
 };
 hipError_t launch_copy_rows(const CopyRowsArgs &a, hipStream_t s);
+
+// Mixed-length prefill: copy each sequence's residual tokens into ring slots
+// 0.. and write its state.
+struct RaggedResidualArgs {
+  const uint16_t *src_k, *src_v;   // [B][H][stride][D]
+  uint16_t *dst_k, *dst_v;         // [B][H][slots][D]
+  const int32_t *seq_lens;         // [B]
+  int32_t *state;                  // [B][4]
+  int n_units, kv_heads, stride, group, residual, slots, max_tokens;
+};
+hipError_t launch_ragged_residual(const RaggedResidualArgs &a, hipStream_t s);
 
 struct DecodeArgs {
   const uint8_t *k_codes; const void *k_scale, *k_zero;   // fp32, or fp16 / bf16 bits
@@ -64,6 +108,13 @@ struct DecodeArgs {
   int n_groups;       // quantised groups in the cache (n_q / G)
   int n_res, res_start;
   int n_split;        // workgroups per unit (the host passes the workspace capacity)
+  // Mixed-length batches: with state_in set the counters above are upper
+  // bounds (for the launch shape) and each sequence reads its own {n_q, n_res,
+  // res_start, flags} from state_in, applies this step's flush (done by the
+  // launch before) and the fused append, and the combining workgroup of kv
+  // head 0 writes the result to state_out.
+  const int32_t *state_in;
+  int32_t *state_out;
   // byte shares: workgroup (unit u, split s) has linear index s*n_units+u
   // and co-residency rank min(index / cus, 3) on its compute unit; its share
   // of the unit's bytes is proportional to rank_w[rank]

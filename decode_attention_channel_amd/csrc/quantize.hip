@@ -274,7 +274,25 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantizeArgs a) {
   __shared__ __align__(16) uint8_t s_tile[4][16 * kHeadDim];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int u = blockIdx.y;
-  const int gl0 = blockIdx.x * a.gpw, gl1 = min(gl0 + a.gpw, a.n_groups);
+  const int gl0 = blockIdx.x * a.gpw;
+  int gl1 = min(gl0 + a.gpw, a.n_groups);
+  if (a.seq_lens) {
+    // mixed-length prefill: this sequence's own quantised groups
+    int n_q, r;
+    if (!seq_split(a.seq_lens[u / a.kv_heads], a.stride, kGroup, a.residual, a.max_tokens, n_q, r))
+      return;
+    gl1 = min(gl1, n_q / kGroup);
+    if (gl0 >= gl1) return;
+  } else if (a.state) {
+    // mixed-length flush: only sequences whose ring fills with this step's
+    // append, and that have room for one more group
+    const int4 st = reinterpret_cast<const int4 *>(a.state)[u / a.kv_heads];
+    if (!state_ok(st.x, st.y, st.z, st.w, kGroup, a.slots, a.max_tokens) || st.w != 0 ||
+        st.y + 1 != a.slots || st.x + kGroup > a.max_tokens)
+      return;
+    a.dst_g0 = st.x / kGroup;
+    a.src_tok0 = st.z;   // a multiple of G: the G oldest ring tokens are contiguous
+  }
   if (wave < 2)
     quantize_keys<BITS, META>(a, u, gl0, gl1, wave, lane, s_tile[wave]);
   else
@@ -294,7 +312,35 @@ __global__ __launch_bounds__(256) void copy_rows_kernel(CopyRowsArgs a) {
                              (long long)(a.dst_row0 + i) * kHeadDim + 8 * c) = v;
 }
 
+__global__ __launch_bounds__(256) void ragged_residual_kernel(RaggedResidualArgs a) {
+  constexpr int CH = kHeadDim / 8;   // 16-byte chunks per row
+  const int u = blockIdx.y, b = u / a.kv_heads;
+  int n_q, r;
+  const bool ok = seq_split(a.seq_lens[b], a.stride, a.group, a.residual, a.max_tokens, n_q, r);
+  if (blockIdx.x == 0 && blockIdx.z == 0 && threadIdx.x == 0 && u % a.kv_heads == 0) {
+    const int flags = ok ? 0 : kSeqBadLength;
+    reinterpret_cast<int4 *>(a.state)[b] = ok ? make_int4(n_q, r, 0, 0) : make_int4(0, 0, 0, flags);
+  }
+  if (!ok) return;
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= r * CH) return;
+  const int i = idx / CH, c = idx % CH;
+  const uint16_t *src = blockIdx.z == 0 ? a.src_k : a.src_v;
+  uint16_t *dst = blockIdx.z == 0 ? a.dst_k : a.dst_v;
+  const uint4 v = *reinterpret_cast<const uint4 *>(
+      src + ((long long)u * a.stride + n_q + i) * kHeadDim + 8 * c);
+  *reinterpret_cast<uint4 *>(dst + ((long long)u * a.slots + i) * kHeadDim + 8 * c) = v;
+}
+
 }  // namespace
+
+hipError_t launch_ragged_residual(const RaggedResidualArgs &a, hipStream_t s) {
+  if (a.n_units <= 0) return hipSuccess;
+  const int chunks = a.slots * (kHeadDim / 8);
+  const dim3 grid((chunks + 255) / 256, a.n_units, 2);
+  hipLaunchKernelGGL(ragged_residual_kernel, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_quantize(int bits, int meta, const QuantizeArgs &a_in, hipStream_t s) {
   if (a_in.n_groups <= 0 || a_in.n_units <= 0) return hipSuccess;

@@ -24,11 +24,12 @@ STATUS = {
 EXPORTS = (
     "kivi_cache_layout", "kivi_decode_workspace_size", "kivi_quantize_prefill",
     "kivi_append_token", "kivi_flush_residual", "kivi_decode_attention",
-    "kivi_decode_step", "kivi_dense_decode_attention", "kivi_status_string",
-    "kivi_last_hip_error",
+    "kivi_decode_step", "kivi_dense_decode_attention", "kivi_ragged_prefill",
+    "kivi_ragged_decode_step", "kivi_status_string", "kivi_last_hip_error",
 )
 BUFFERS = ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero", "k_res", "v_res")
 META_FP32, META_FP16_BF16 = 0, 1   # scale/zero formats (kivi_geom.meta_format)
+SEQ_BAD_LENGTH, SEQ_FULL = 1, 2     # per-sequence state flags (mixed-length batches)
 
 
 class KiviError(RuntimeError):
@@ -69,9 +70,13 @@ def _load():
                                      ctypes.POINTER(ctypes.c_int32), P]
     lib.kivi_dense_decode_attention.argtypes = [G, P, P, ctypes.c_int32, P, P, ctypes.c_float, P,
                                                 ctypes.c_size_t, P]
+    lib.kivi_ragged_prefill.argtypes = [G, C, P, P, ctypes.c_int32, P, P, P]
+    lib.kivi_ragged_decode_step.argtypes = [G, C, P, P, P, P, P, P, ctypes.c_float, P,
+                                            ctypes.c_size_t, P]
     for f in ("kivi_cache_layout", "kivi_decode_workspace_size", "kivi_quantize_prefill",
               "kivi_append_token", "kivi_flush_residual", "kivi_decode_attention",
-              "kivi_decode_step", "kivi_dense_decode_attention"):
+              "kivi_decode_step", "kivi_dense_decode_attention", "kivi_ragged_prefill",
+              "kivi_ragged_decode_step"):
         getattr(lib, f).restype = ctypes.c_int
     lib.kivi_status_string.argtypes = [ctypes.c_int]
     lib.kivi_status_string.restype = ctypes.c_char_p
@@ -292,6 +297,47 @@ def dense_decode_attention(g: Geom, k: torch.Tensor, v: torch.Tensor, seq_len: i
                                             ctypes.c_void_p(ws.buf.data_ptr()), ws.nbytes,
                                             _stream()),
            "kivi_dense_decode_attention")
+    return out
+
+
+def ragged_prefill(g: Geom, c: Cache, k: torch.Tensor, v: torch.Tensor,
+                   seq_lens: torch.Tensor, state: torch.Tensor | None = None) -> torch.Tensor:
+    """Mixed-length prefill.  k, v: bf16 [B][H][stride][D]; seq_lens: int32
+    [B] on the device.  Returns the per-sequence state, int32 [B][4]
+    {n_q, n_res, res_start, flags} (written into `state` if given)."""
+    stride = k.shape[2] if k.dim() == 4 else -1
+    shape = (g.batch, g.kv_heads, stride, g.head_dim)
+    if state is None:
+        state = torch.empty(g.batch, 4, dtype=torch.int32, device=k.device)
+    _check(_lib.kivi_ragged_prefill(ctypes.byref(g.c()), ctypes.byref(c._c),
+                                    _ptr(k, torch.bfloat16, shape, "k"),
+                                    _ptr(v, torch.bfloat16, shape, "v"), stride,
+                                    _ptr(seq_lens, torch.int32, (g.batch,), "seq_lens"),
+                                    _ptr(state, torch.int32, (g.batch, 4), "state"), _stream()),
+           "kivi_ragged_prefill")
+    return state
+
+
+def ragged_decode_step(g: Geom, c: Cache, state_in: torch.Tensor, state_out: torch.Tensor,
+                       k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor,
+                       out: torch.Tensor | None = None, softmax_scale: float | None = None,
+                       ws: Workspace | None = None) -> torch.Tensor:
+    """One step of a mixed-length batch: reads state_in, writes state_out
+    (int32 [B][4] each), returns out fp32 [B][H*QPK][D]."""
+    shape = (g.batch, g.q_heads, g.head_dim)
+    tok = (g.batch, g.kv_heads, g.head_dim)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = Workspace(g, q.device)
+    scale = 1.0 / math.sqrt(g.head_dim) if softmax_scale is None else float(softmax_scale)
+    _check(_lib.kivi_ragged_decode_step(
+        ctypes.byref(g.c()), ctypes.byref(c._c),
+        _ptr(state_in, torch.int32, (g.batch, 4), "state_in"),
+        _ptr(state_out, torch.int32, (g.batch, 4), "state_out"),
+        _ptr(k_new, torch.bfloat16, tok, "k_new"), _ptr(v_new, torch.bfloat16, tok, "v_new"),
+        _ptr(q, torch.bfloat16, shape, "q"), _ptr(out, torch.float32, shape, "out"), scale,
+        ctypes.c_void_p(ws.buf.data_ptr()), ws.nbytes, _stream()), "kivi_ragged_decode_step")
     return out
 
 

@@ -287,6 +287,57 @@ kivi_status kivi_dense_decode_attention(const kivi_geom *geom, const uint16_t *k
                                         float softmax_scale, void *ws, size_t ws_bytes,
                                         void *stream);
 
+/* ------------------------------------------------------------------------
+ * Mixed-length batches (per-sequence lengths).  The lockstep calls above
+ * keep one (n_q, n_res, res_start) for the whole batch.  These two calls keep
+ * it per sequence instead, in device memory, so that sequences of different
+ * lengths share one cache and one launch per step, and so that a step's
+ * launches take the same arguments every step (they can be captured in a
+ * HIP graph; the state buffers alternate between two captured steps).
+ *
+ * State: int32 [B][4] per sequence: {n_q, n_res, res_start, flags}, with
+ * the meaning of the kivi_cache counters.  flags: 0, or KIVI_SEQ_BAD_LENGTH
+ * (the prefill length was out of range; the sequence is empty and its
+ * output rows are 0) or KIVI_SEQ_FULL (a flush was due with no room for
+ * another group; the sequence keeps its cache and takes no more tokens).
+ * A state row that these calls cannot have written (history not whole
+ * groups or beyond max_tokens, ring count or start out of range, unknown flag
+ * bits) is taken as an empty KIVI_SEQ_BAD_LENGTH sequence.
+ * The counters of kivi_cache are ignored by these calls.
+ * ------------------------------------------------------------------------ */
+enum { KIVI_SEQ_BAD_LENGTH = 1, KIVI_SEQ_FULL = 2 };
+
+/* Prefill of a mixed-length batch: sequence b has seq_lens[b] tokens (device
+ * int32 [B]), the first ones of each row block of k, v (device bf16
+ * [B][H][stride][D]).  Each sequence is split and quantised exactly as
+ * kivi_quantize_prefill splits a batch of that length; state (device int32
+ * [B][4]) receives every sequence's counters.  A length outside
+ * [1, stride], or one whose quantised part exceeds max_tokens, gives that
+ * sequence KIVI_SEQ_BAD_LENGTH.
+ * Errors: KIVI_E_NULL, KIVI_E_GEOMETRY, KIVI_E_UNSUPPORTED, KIVI_E_SEQLEN
+ *         (stride < 1), KIVI_E_HIP. */
+kivi_status kivi_ragged_prefill(const kivi_geom *geom, const kivi_cache *cache,
+                                const uint16_t *k, const uint16_t *v, int32_t stride,
+                                const int32_t *seq_lens, int32_t *state, void *stream);
+
+/* One decode step of a mixed-length batch: for every sequence, append
+ * k_new/v_new, flush iff its ring is then full, and attend with q -- per
+ * sequence the same cache bytes and output as kivi_decode_step on a batch
+ * of that sequence alone.  Two launches with fixed arguments: a flush launch
+ * in which only the sequences due to flush work, then decode attention with
+ * the append fused.  The state is read from state_in and the state after
+ * the step written to state_out (distinct device int32 [B][4] buffers; the
+ * next step reads state_out).  Requires residual >= group.
+ * k_new, v_new: device bf16 [B][H][D]; q, out, softmax_scale, ws, ws_bytes
+ * as for kivi_decode_attention (the workspace size of the same geom).
+ * Errors: KIVI_E_NULL, KIVI_E_GEOMETRY, KIVI_E_UNSUPPORTED, KIVI_E_STATE
+ *         (state_in == state_out), KIVI_E_WORKSPACE, KIVI_E_HIP. */
+kivi_status kivi_ragged_decode_step(const kivi_geom *geom, const kivi_cache *cache,
+                                    const int32_t *state_in, int32_t *state_out,
+                                    const uint16_t *k_new, const uint16_t *v_new,
+                                    const uint16_t *q, float *out, float softmax_scale,
+                                    void *ws, size_t ws_bytes, void *stream);
+
 /* Static description of a status code (never NULL). */
 const char *kivi_status_string(kivi_status status);
 

@@ -20,7 +20,7 @@ def _declared():
 
 def test_exports_every_declared_function():
     names = _declared()
-    assert len(names) == 10
+    assert len(names) == 12
     lib = ctypes.CDLL(kivi.library_path())
     for n in names:
         assert hasattr(lib, n), n
@@ -175,6 +175,30 @@ def test_16bit_meta_layout_and_rejected_formats():
         with pytest.raises(kivi.KiviError) as e:
             kivi.cache_layout(_g(meta_format=bad))
         assert e.value.status == 3
+
+
+def test_ragged_calls_validation_before_any_device_work():
+    g = _g().c()
+    fake = ctypes.c_void_p(0x2000)
+    fake2 = ctypes.c_void_p(0x3000)
+    P = ctypes.byref
+    ws_need = kivi.workspace_size(_g())
+    c = _cache_struct()
+    assert _call("kivi_ragged_prefill", P(g), P(c), None, fake, 100, fake, fake, None) == 1
+    assert _call("kivi_ragged_prefill", P(g), P(c), fake, fake, 100, None, fake, None) == 1
+    assert _call("kivi_ragged_prefill", P(g), P(c), fake, fake, 100, fake, None, None) == 1
+    assert _call("kivi_ragged_prefill", P(g), P(c), fake, fake, 0, fake, fake, None) == 4
+    assert _call("kivi_ragged_prefill", P(g), P(_cache_struct(null=3)), fake, fake, 100, fake,
+                 fake, None) == 1
+
+    def step(geom=g, si=fake, so=fake2, nbytes=ws_need):
+        return _call("kivi_ragged_decode_step", P(geom), P(c), si, so, fake, fake, fake, fake,
+                     ctypes.c_float(0.1), fake, nbytes, None)
+
+    assert step(si=None) == 1 and step(so=None) == 1
+    assert step(so=fake) == 9           # state_in and state_out must differ
+    assert step(nbytes=ws_need - 1) == 7
+    assert step(geom=_g(residual=0).c()) == 3   # the fused append needs R >= G
 
 
 def test_status_strings():
