@@ -18,6 +18,11 @@ Workload (Llama-3-8B GQA geometry of the catalog record kivi-2bit-llama3-8b-gqa-
 * roofline of the dominant kernel (decode attention with the fused append,
   one launch per layer): algorithmic bytes per launch / its duration from HIP
   event pairs around each launch of 10 further decode steps, against 8 TB/s;
+* mixed-length leg (reported beside, not in, value): the same caches
+  stepped through kivi_ragged_decode_step with per-sequence counters in
+  device memory, all sequences at the lockstep length and then with lengths
+  drawn uniformly from [S/2, S]; eager launches and HIP graph replays of
+  all layers (two launches per layer) are timed;
 * cpu_baseline: the CPU oracle (plain C) on a bounded sample of the same
   workload (two layers' worth of (sequence, kv head) units), threads over units.
 
@@ -263,10 +268,128 @@ def batch_sweep(args):
         "best_tokens_s": {"kivi": best_kivi, "bf16": best_bf16, "ratio": best_kivi / best_bf16},
         "rows": [{"batch": B, **rows[B]} for B in sorted(rows)],
         "data": "synthetic (seeded random cache contents; timing only)",
+        "mixed_length_steps": ragged,
         "paper_context": "up to 4x batch and 2.35x-3.47x throughput vs FP16 (Llama-2-7B, one "
                          "A100 80GB, whole model; not comparable, quoted as context)",
     }
     print(json.dumps(res))
+
+
+def _advance(counters, steps, slots, group):
+    """Per-sequence (n_q, n_res) after `steps` mixed-length steps (a flush
+    when the ring would fill, then the append)."""
+    out = [list(x) for x in counters]
+    for _ in range(steps):
+        for x in out:
+            if x[1] + 1 == slots:
+                x[0] += group
+                x[1] -= group
+            x[1] += 1
+    return out
+
+
+def _ragged_bytes(w, counters, steps, slots, meta_bytes):
+    """Algorithmic attention bytes of `steps` mixed-length steps from the
+    given per-sequence (n_q, n_res) counters (each step attends over the
+    cache after its flush and append, and writes the appended rows)."""
+    D, G, b = w.head_dim, w.group, w.bits
+    total = 0.0
+    for i in range(steps):
+        for n_q, n_res in _advance(counters, i + 1, slots, G):
+            total += w.kv_heads * (n_q * (2 * D * b / 8 + 4 * meta_bytes * D / G) +
+                                   n_res * 4 * D + 4 * D)
+        total += w.batch * w.q_heads * D * (2 + 4)
+    return total
+
+
+RAGGED_EXTRA_STEPS = 4   # untimed steps per case: two eager, two graph replays
+
+
+def ragged_leg(w, geom, caches, ws, qs, outs, tok, steps, seed, meta_bytes):
+    """Mixed-length decode steps (kivi_ragged_decode_step, per-sequence
+    counters in device memory) on the same caches: all sequences at the
+    lockstep length, then lengths drawn uniformly from [S/2, S] per sequence
+    (the cache bytes beyond a sequence's length are not read).  Each case is
+    timed as eager launches and as HIP graph replays (one graph per state
+    parity, all layers, two launches per layer).  `steps` is even."""
+    import numpy as np
+    import torch
+
+    from decode_attention_channel_amd import kivi
+
+    assert steps % 2 == 0
+    dev = caches[0].k_codes.device
+    G, R = w.group, w.residual
+    slots = R + G
+    layers = len(caches)
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(w.seq_len // 2, w.seq_len + 1, size=w.batch)
+    mixed = []
+    for L in lens:
+        n_q = G * ((int(L) - R) // G)
+        mixed.append((n_q, int(L) - n_q))
+    c0 = caches[0]
+    cases = {"uniform": [(c0.n_q, c0.n_res)] * w.batch, "mixed": mixed}
+    res = {"lengths_mixed": "uniform integers in [%d, %d] per sequence, numpy default_rng(%d); "
+                            "min %d, mean %.0f, max %d" % (w.seq_len // 2, w.seq_len, seed,
+                                                          lens.min(), lens.mean(), lens.max())}
+    for name, counters in cases.items():
+        # the uniform case continues the lockstep caches' rings; the mixed
+        # case starts its rings at slot 0 (the ring contents are valid bf16)
+        rs = c0.res_start if name == "uniform" else 0
+        st_rows = torch.tensor([(n_q, n_res, rs, 0) for n_q, n_res in counters],
+                               dtype=torch.int32)
+        states, steppers = [], []
+        for layer in range(layers):
+            a = st_rows.to(dev)
+            b = torch.empty_like(a)
+            states.append((a, b))
+            kn, vn = tok[layer]
+            steppers.append(kivi.RaggedStepper(geom, caches[layer], ws, a, b, kn, vn, qs[layer],
+                                               outs[layer]))
+
+        def eager(parity):
+            for sp in steppers:
+                sp.step(parity)
+
+        eager(0)
+        eager(1)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            eager(i & 1)
+        torch.cuda.synchronize()
+        t_eager = (time.perf_counter() - t0) / steps
+        # one graph per parity; capturing enqueues nothing, so the replays
+        # continue from the state the eager steps left (parity 0 next)
+        graphs = []
+        for parity in (0, 1):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                eager(parity)
+            graphs.append(g)
+        graphs[0].replay()
+        graphs[1].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            graphs[i & 1].replay()
+        torch.cuda.synchronize()
+        t_graph = (time.perf_counter() - t0) / steps
+        # the device counters must be where the host model says
+        done = _advance(counters, 2 * steps + RAGGED_EXTRA_STEPS, slots, G)
+        for layer in (0, layers - 1):
+            got = [list(r[:2]) for r in states[layer][0].cpu().tolist()]
+            if got != done:
+                raise RuntimeError(f"mixed-length state of layer {layer} off the host model")
+        start = _advance(counters, steps + RAGGED_EXTRA_STEPS, slots, G)
+        gbytes = _ragged_bytes(w, start, steps, slots, meta_bytes) * layers / steps
+        res[name] = {"ms_per_step_eager": t_eager * 1e3, "ms_per_step_graph": t_graph * 1e3,
+                     "tokens_s_eager": w.batch / t_eager, "tokens_s_graph": w.batch / t_graph,
+                     "attn_bytes_per_step": gbytes,
+                     "step_hbm_gbps_graph": gbytes / t_graph / 1e9}
+        del graphs
+    return res
 
 
 def main():
@@ -285,6 +408,8 @@ def main():
     ap.add_argument("--meta", choices=("fp32", "fp16"), default="fp32",
                     help="scale/zero format: fp32 scale + zero (default), or fp16 scale + "
                          "bf16 zero")
+    ap.add_argument("--no-ragged", action="store_true",
+                    help="skip the mixed-length (per-sequence state) step timing")
     ap.add_argument("--batch-sweep", action="store_true",
                     help="memory-wall sweep: KIVI 2-bit vs bf16 decode attention vs batch "
                          "(Llama-2-13B-shaped MHA); prints its own JSON line")
@@ -317,8 +442,11 @@ def main():
     dev = torch.device("cuda", 0)
     D, G, R = w.head_dim, w.group, w.residual
     kernel_steps = 10   # extra fused steps with HIP events around every launch
+    ragged_steps = args.steps + (args.steps & 1)
     total_steps = args.warmup + (args.profile_steps or 2 * args.steps + kernel_steps + 1)
-    max_tokens = G * math.ceil((w.seq_len - R + total_steps + G) / G)
+    # the mixed-length leg continues the caches for 2 * (2 * steps + 4) more tokens
+    cap_steps = total_steps + 2 * (2 * ragged_steps + RAGGED_EXTRA_STEPS)
+    max_tokens = G * math.ceil((w.seq_len - R + cap_steps + G) / G)
     meta = kivi.META_FP16_BF16 if args.meta == "fp16" else kivi.META_FP32
     geom = kivi.Geom(w.batch, w.kv_heads, w.q_per_kv, bits=w.bits, max_tokens=max_tokens,
                      meta_format=meta)
@@ -432,6 +560,11 @@ def main():
     avg_bytes = sum(kern_bytes) / len(kern_bytes)
     achieved = avg_bytes / avg_kern_s / 1e9
 
+    ragged = None
+    if not args.no_ragged:
+        tok = new_tok[i0]
+        ragged = ragged_leg(w, geom, caches, ws, qs, outs, tok, ragged_steps, args.seed, mbytes)
+
     ms_per_step = t_steps / n_timed * 1e3
     tokens_s = w.batch / (t_steps / n_timed)
     res = {
@@ -458,6 +591,7 @@ def main():
                      "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": (read_traffic(f"decode_attn_{w.name}") if args.meta == "fp32"
                                  else None)},
+        "mixed_length_steps": ragged,
         "paper_context": "2.35x-3.47x decode throughput vs FP16 and 2.6x less peak memory "
                          "(Llama-2-7B, one A100 80GB; not comparable, quoted as context)",
     }

@@ -382,6 +382,12 @@ __device__ __forceinline__ UnitView make_view(const DecodeArgs &a, int u, int n,
 // the group it computes and not for the prefetches behind it.
 constexpr uint32_t kOutOfRange = 0x80000000u;   // > any unit's buffer size
 
+// Groups in flight per wave beyond the one being computed (MFMA path).
+#ifndef KIVI_PREFETCH
+#define KIVI_PREFETCH 2
+#endif
+constexpr int kPrefetch = KIVI_PREFETCH;
+
 template <int BITS, int META>
 __device__ __forceinline__ void load_group(GroupRaw<BITS> &r, const UnitView &v, int g, bool live) {
   // group offsets are wave-uniform: keep them in SGPRs (scalar buffer offsets)
@@ -802,9 +808,15 @@ __global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeArgs a) {
   }
   const bool has_groups = g_begin < g_end;
   const UnitView view = make_view<BITS, META>(a, u, n, gq, cm);
-  GroupRaw<BITS> r0, r1, r2;
-  load_group<BITS, META>(r0, view, g_begin, has_groups);
-  load_group<BITS, META>(r1, view, g_begin + 1, g_begin + 1 < g_end);
+  // register sets of the load pipeline: kPrefetch groups in flight
+  GroupRaw<BITS> r[kPrefetch + 1];
+#pragma unroll
+  for (int i = 0; i < kPrefetch; ++i) {
+    load_group<BITS, META>(r[i], view, g_begin + i, g_begin + i < g_end);
+    // keep the groups' loads in group order, as in the loop, so that the
+    // wait counts at the loop head are the steady-state ones
+    __builtin_amdgcn_sched_barrier(0);
+  }
 
   // scaled query values in slot order for the cooperative role
   float qv[NHB][8];
@@ -829,20 +841,19 @@ __global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeArgs a) {
     st.m_run[hb] = kNegInf; st.l_run[hb] = 0.f; st.z_run[hb] = 0.f;
   }
 
-  // quantised groups: software pipeline over three register sets, the next
-  // two groups in flight while the current one is computed
-  if (has_groups) {
-    int g = g_begin;
-    while (true) {
-      load_group<BITS, META>(r2, view, g + 2, g + 2 < g_end);
-      mfma_group<BITS, NHB, META>(r0, st, sm.mf, qv, wave, n, gq, ch, cm);
-      if (++g >= g_end) break;
-      load_group<BITS, META>(r0, view, g + 2, g + 2 < g_end);
-      mfma_group<BITS, NHB, META>(r1, st, sm.mf, qv, wave, n, gq, ch, cm);
-      if (++g >= g_end) break;
-      load_group<BITS, META>(r1, view, g + 2, g + 2 < g_end);
-      mfma_group<BITS, NHB, META>(r2, st, sm.mf, qv, wave, n, gq, ch, cm);
-      if (++g >= g_end) break;
+  // quantised groups: software pipeline over kPrefetch + 1 register sets
+  // (unrolled, so the sets rotate without copies), the next kPrefetch groups
+  // in flight while the current one is computed
+  // Every pass issues the loads of kPrefetch + 1 groups, so that the
+  // outstanding loads at the loop head are the same from either edge; the
+  // last pass skips the groups past the end (a wave-uniform branch).
+  for (int g0 = g_begin; g0 < g_end; g0 += kPrefetch + 1) {
+#pragma unroll
+    for (int k = 0; k <= kPrefetch; ++k) {
+      const int g = g0 + k;
+      load_group<BITS, META>(r[(k + kPrefetch) % (kPrefetch + 1)], view, g + kPrefetch,
+                             g + kPrefetch < g_end);
+      if (g < g_end) mfma_group<BITS, NHB, META>(r[k], st, sm.mf, qv, wave, n, gq, ch, cm);
     }
   }
   // residual chunks

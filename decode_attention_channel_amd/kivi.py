@@ -394,3 +394,39 @@ class LayerStepper:
                                      ctypes.byref(self._flushed), self._stream),
                "kivi_decode_step")
         return self._flushed.value
+
+
+class RaggedStepper:
+    """Pre-marshalled kivi_ragged_decode_step of one layer for tight loops
+    and graph capture: the new token, q and out buffers are fixed (the
+    caller refills them), and the two state buffers alternate, step(0)
+    reading state_a and writing state_b, step(1) the other way round.  The
+    stream is torch's current stream at each call, so that a capture sees
+    its capture stream."""
+
+    def __init__(self, g: Geom, c: Cache, ws: Workspace, state_a: torch.Tensor,
+                 state_b: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                 q: torch.Tensor, out: torch.Tensor, softmax_scale: float | None = None):
+        shape_q = (g.batch, g.q_heads, g.head_dim)
+        tok = (g.batch, g.kv_heads, g.head_dim)
+        self.geom, self.cache = g, c
+        self._g = g.c()
+        self._gp, self._cp = ctypes.byref(self._g), ctypes.byref(c._c)
+        st = [_ptr(x, torch.int32, (g.batch, 4), "state") for x in (state_a, state_b)]
+        if st[0].value == st[1].value:
+            raise ValueError("state_a and state_b must be distinct buffers")
+        self._st = st
+        self._k = _ptr(k_new, torch.bfloat16, tok, "k_new")
+        self._v = _ptr(v_new, torch.bfloat16, tok, "v_new")
+        self._q = _ptr(q, torch.bfloat16, shape_q, "q")
+        self._out = _ptr(out, torch.float32, shape_q, "out")
+        self._keep = (ws, state_a, state_b, k_new, v_new, q, out)
+        self._ws, self._wsn = ctypes.c_void_p(ws.buf.data_ptr()), ws.nbytes
+        scale = 1.0 / math.sqrt(g.head_dim) if softmax_scale is None else float(softmax_scale)
+        self._scale = ctypes.c_float(scale)
+
+    def step(self, parity: int) -> None:
+        a, b = self._st[parity & 1], self._st[(parity & 1) ^ 1]
+        _check(_lib.kivi_ragged_decode_step(self._gp, self._cp, a, b, self._k, self._v, self._q,
+                                            self._out, self._scale, self._ws, self._wsn,
+                                            _stream()), "kivi_ragged_decode_step")
