@@ -18,11 +18,12 @@ Workload (Llama-3-8B GQA geometry of the catalog record kivi-2bit-llama3-8b-gqa-
 * roofline of the dominant kernel (decode attention with the fused append,
   one launch per layer): algorithmic bytes per launch / its duration from HIP
   event pairs around each launch of 10 further decode steps, against 8 TB/s;
-* mixed-length leg (reported beside, not in, value): the same caches
-  stepped through kivi_ragged_decode_step with per-sequence counters in
-  device memory, all sequences at the lockstep length and then with lengths
-  drawn uniformly from [S/2, S]; eager launches and HIP graph replays of
-  all layers (two launches per layer) are timed;
+* mixed-length leg (reported beside, not in, value): per-sequence counters
+  in device memory -- paged copies of the caches (pages of 4 groups from a
+  shuffled pool) through kivi_paged_decode_step at the lockstep length, then
+  the caches themselves through kivi_ragged_decode_step at the lockstep
+  length and with lengths drawn uniformly from [S/2, S]; eager launches and
+  HIP graph replays of all layers (two launches per layer) are timed;
 * cpu_baseline: the CPU oracle (plain C) on a bounded sample of the same
   workload (two layers' worth of (sequence, kv head) units), threads over units.
 
@@ -305,13 +306,46 @@ def _ragged_bytes(w, counters, steps, slots, meta_bytes):
 RAGGED_EXTRA_STEPS = 4   # untimed steps per case: two eager, two graph replays
 
 
+PAGE_GROUPS = 4   # groups per page of the paged case (128 tokens)
+
+
+def _paged_copy(geom, cache, page_groups, rng):
+    """A kivi.PagedCache holding the same quantised history and rings as a
+    lockstep cache, its pages drawn from a shuffled pool."""
+    import numpy as np
+    import torch
+
+    from decode_attention_channel_amd import kivi
+
+    B, H, G, T = geom.batch, geom.kv_heads, geom.group, geom.max_tokens
+    NG = T // G
+    per_seq = -(-NG // page_groups)
+    pc = kivi.PagedCache(geom, page_groups, B * per_seq)
+    table = rng.permutation(B * per_seq).astype(np.int32).reshape(B, per_seq)
+    pc.block_table.copy_(torch.from_numpy(table))
+    tb = pc.block_table.long()
+    g = torch.arange(NG, device=tb.device)
+    h = torch.arange(H, device=tb.device)
+    slot = ((tb[:, g // page_groups][:, None, :] * H + h[None, :, None]) * page_groups +
+            (g % page_groups)[None, None, :]).reshape(-1)
+    for name in ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero"):
+        src = getattr(cache, name)
+        dst = getattr(pc, name)
+        dst[slot] = src.reshape(B * H * NG, *dst.shape[1:])
+    pc.k_res.copy_(cache.k_res)
+    pc.v_res.copy_(cache.v_res)
+    return pc
+
+
 def ragged_leg(w, geom, caches, ws, qs, outs, tok, steps, seed, meta_bytes):
-    """Mixed-length decode steps (kivi_ragged_decode_step, per-sequence
-    counters in device memory) on the same caches: all sequences at the
-    lockstep length, then lengths drawn uniformly from [S/2, S] per sequence
-    (the cache bytes beyond a sequence's length are not read).  Each case is
-    timed as eager launches and as HIP graph replays (one graph per state
-    parity, all layers, two launches per layer).  `steps` is even."""
+    """Mixed-length decode steps (per-sequence counters in device memory):
+    first on paged copies of the caches (kivi_paged_decode_step, pages of
+    PAGE_GROUPS groups from a shuffled pool) at the lockstep length, then
+    (kivi_ragged_decode_step) on the caches themselves at the lockstep
+    length and with lengths drawn uniformly from [S/2, S] per sequence (the
+    cache bytes beyond a sequence's length are not read).  Each case is timed
+    as eager launches and as HIP graph replays (one graph per state parity,
+    all layers, two launches per layer).  `steps` is even."""
     import numpy as np
     import torch
 
@@ -329,14 +363,20 @@ def ragged_leg(w, geom, caches, ws, qs, outs, tok, steps, seed, meta_bytes):
         n_q = G * ((int(L) - R) // G)
         mixed.append((n_q, int(L) - n_q))
     c0 = caches[0]
-    cases = {"uniform": [(c0.n_q, c0.n_res)] * w.batch, "mixed": mixed}
+    uniform = [(c0.n_q, c0.n_res)] * w.batch
+    cases = {"paged_uniform": uniform, "uniform": uniform, "mixed": mixed}
     res = {"lengths_mixed": "uniform integers in [%d, %d] per sequence, numpy default_rng(%d); "
                             "min %d, mean %.0f, max %d" % (w.seq_len // 2, w.seq_len, seed,
                                                           lens.min(), lens.mean(), lens.max())}
     for name, counters in cases.items():
-        # the uniform case continues the lockstep caches' rings; the mixed
+        # the uniform cases continue the lockstep caches' rings; the mixed
         # case starts its rings at slot 0 (the ring contents are valid bf16)
-        rs = c0.res_start if name == "uniform" else 0
+        rs = 0 if name == "mixed" else c0.res_start
+        store = caches
+        if name == "paged_uniform":
+            prng = np.random.default_rng(seed + 1)
+            store = [_paged_copy(geom, c, PAGE_GROUPS, prng) for c in caches]
+            torch.cuda.synchronize()
         st_rows = torch.tensor([(n_q, n_res, rs, 0) for n_q, n_res in counters],
                                dtype=torch.int32)
         states, steppers = [], []
@@ -345,7 +385,7 @@ def ragged_leg(w, geom, caches, ws, qs, outs, tok, steps, seed, meta_bytes):
             b = torch.empty_like(a)
             states.append((a, b))
             kn, vn = tok[layer]
-            steppers.append(kivi.RaggedStepper(geom, caches[layer], ws, a, b, kn, vn, qs[layer],
+            steppers.append(kivi.RaggedStepper(geom, store[layer], ws, a, b, kn, vn, qs[layer],
                                                outs[layer]))
 
         def eager(parity):
@@ -388,7 +428,9 @@ def ragged_leg(w, geom, caches, ws, qs, outs, tok, steps, seed, meta_bytes):
                      "tokens_s_eager": w.batch / t_eager, "tokens_s_graph": w.batch / t_graph,
                      "attn_bytes_per_step": gbytes,
                      "step_hbm_gbps_graph": gbytes / t_graph / 1e9}
-        del graphs
+        if name == "paged_uniform":
+            res[name]["page_groups"] = PAGE_GROUPS
+        del graphs, steppers, states, store
     return res
 
 

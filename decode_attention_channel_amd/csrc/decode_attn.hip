@@ -258,8 +258,11 @@ __device__ __forceinline__ int4 apply_unit_state(DecodeArgs &a, int u) {
   }
   bool append = flags == 0;
   if (append && n_res + 1 >= a.slots) {
-    if (n_res + 1 == a.slots && n_q + G <= a.max_tokens) {
-      n_q += G;   // flushed by the launch before this one
+    // the flush launch quantised the G oldest ring tokens into group n_q / G
+    // iff there is room for it (and, paged, a page)
+    if (n_res + 1 == a.slots && n_q + G <= a.max_tokens &&
+        (!a.pages.table || group_slot(a.pages, a.kv_heads, 0, u, n_q / G) >= 0)) {
+      n_q += G;
       n_res -= G;
       res_start = (res_start + G) % a.slots;
     } else {
@@ -354,19 +357,78 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t meta_rsrc(const void *base, in
   return make_rsrc(static_cast<const char *>(base) + u * per_unit, (uint32_t)per_unit);
 }
 
-template <int BITS, int META>
+// The six group-major buffers of a unit's history: the unit's own block of
+// each array, or (PAGED) the whole pools, which the host keeps below 2 GiB
+// each so that kOutOfRange offsets stay out of range.
+struct HistBufs {
+  __amdgpu_buffer_rsrc_t kc, vc, ks, kz, vs, vz;
+};
+
+template <int BITS, int META, bool PAGED>
+__device__ __forceinline__ HistBufs hist_bufs(const DecodeArgs &a, int u) {
+  constexpr int KROW = D * BITS / 8;
+  HistBufs v;
+  if constexpr (PAGED) {
+    const long long groups = (long long)a.pages.num_pages * a.kv_heads << a.pages.shift;
+    const uint32_t cb = (uint32_t)(groups * G * KROW), mb = (uint32_t)(groups * D * kMetaBytes<META>);
+    v.kc = make_rsrc(a.k_codes, cb);
+    v.vc = make_rsrc(a.v_codes, cb);
+    v.ks = make_rsrc(a.k_scale, mb);
+    v.kz = make_rsrc(a.k_zero, mb);
+    v.vs = make_rsrc(a.v_scale, mb);
+    v.vz = make_rsrc(a.v_zero, mb);
+  } else {
+    const long long T = a.max_tokens, NG = a.n_groups_cap;
+    const uint32_t code_bytes = (uint32_t)(T * KROW);
+    v.kc = make_rsrc(a.k_codes + u * T * KROW, code_bytes);
+    v.vc = make_rsrc(a.v_codes + u * T * KROW, code_bytes);
+    v.ks = meta_rsrc<META>(a.k_scale, u, NG);
+    v.kz = meta_rsrc<META>(a.k_zero, u, NG);
+    v.vs = meta_rsrc<META>(a.v_scale, u, NG);
+    v.vz = meta_rsrc<META>(a.v_zero, u, NG);
+  }
+  return v;
+}
+
+// Page table entry read through the scalar cache (the table is read-only
+// for the whole launch), so that it does not count among the vector loads
+// of the group pipeline.
+__device__ __forceinline__ int page_entry(const int32_t *table, long long i) {
+  typedef __attribute__((address_space(4))) const int32_t *ConstPtr;
+  return ((ConstPtr)table)[i];
+}
+
+// Scalar byte offsets of group g in the history buffers: codes (sc) and one
+// scale/zero array (sm).  PAGED: the group's slot in the pools; a group
+// without a page is loaded as not live (zeros, no memory access).
+template <int BITS, int META, bool PAGED>
+__device__ __forceinline__ void group_offsets(const DecodeArgs &a, int u, int g, bool &live,
+                                              uint32_t &sc, uint32_t &sm) {
+  long long slot = g;
+  if constexpr (PAGED) {
+    slot = -1;
+    const int pi = g >> a.pages.shift;
+    if (live && pi < a.pages.max_pages) {
+      const int b = u / a.kv_heads, h = u - b * a.kv_heads;
+      const int e = page_entry(a.pages.table, (long long)b * a.pages.max_pages + pi);
+      if (e >= 0 && e < a.pages.num_pages)
+        slot = (((long long)e * a.kv_heads + h) << a.pages.shift) + (g & ((1 << a.pages.shift) - 1));
+    }
+    live = slot >= 0;
+    if (!live) slot = 0;
+  }
+  // wave-uniform: keep them in SGPRs (scalar buffer offsets)
+  sc = __builtin_amdgcn_readfirstlane((uint32_t)slot * (G * D * BITS / 8));
+  sm = __builtin_amdgcn_readfirstlane((uint32_t)slot * (D * kMetaBytes<META>));
+}
+
+template <int BITS, int META, bool PAGED>
 __device__ __forceinline__ UnitView make_view(const DecodeArgs &a, int u, int n, int gq, int cm) {
   constexpr int KROW = D * BITS / 8;
   constexpr int CB = 32 * BITS / 8;
-  const long long T = a.max_tokens, NG = a.n_groups_cap;
   UnitView v;
-  const uint32_t code_bytes = (uint32_t)(T * KROW);
-  v.kc = make_rsrc(a.k_codes + u * T * KROW, code_bytes);
-  v.vc = make_rsrc(a.v_codes + u * T * KROW, code_bytes);
-  v.ks = meta_rsrc<META>(a.k_scale, u, NG);
-  v.kz = meta_rsrc<META>(a.k_zero, u, NG);
-  v.vs = meta_rsrc<META>(a.v_scale, u, NG);
-  v.vz = meta_rsrc<META>(a.v_zero, u, NG);
+  const HistBufs hb = hist_bufs<BITS, META, PAGED>(a, u);
+  v.kc = hb.kc; v.vc = hb.vc; v.ks = hb.ks; v.kz = hb.kz; v.vs = hb.vs; v.vz = hb.vz;
   const int kr0 = 8 * (n >> 2) + (n & 3);   // A-operand row n of tile 0 -> token; tile 1: +4
   v.o_k0 = kr0 * KROW + gq * CB;
   v.o_k1 = (kr0 + 4) * KROW + gq * CB;
@@ -388,11 +450,11 @@ constexpr uint32_t kOutOfRange = 0x80000000u;   // > any unit's buffer size
 #endif
 constexpr int kPrefetch = KIVI_PREFETCH;
 
-template <int BITS, int META>
-__device__ __forceinline__ void load_group(GroupRaw<BITS> &r, const UnitView &v, int g, bool live) {
-  // group offsets are wave-uniform: keep them in SGPRs (scalar buffer offsets)
-  const uint32_t sc = __builtin_amdgcn_readfirstlane((uint32_t)g * (G * D * BITS / 8));
-  const uint32_t sm = __builtin_amdgcn_readfirstlane((uint32_t)g * (D * kMetaBytes<META>));
+template <int BITS, int META, bool PAGED>
+__device__ __forceinline__ void load_group(GroupRaw<BITS> &r, const UnitView &v,
+                                           const DecodeArgs &a, int u, int g, bool live) {
+  uint32_t sc, sm;
+  group_offsets<BITS, META, PAGED>(a, u, g, live, sc, sm);
   const uint32_t ob = live ? 0u : kOutOfRange;
   const uint32_t o_k0 = v.o_k0 + ob, o_k1 = v.o_k1 + ob, o_v = v.o_v + ob, o_mu = v.o_mu + ob;
   if constexpr (BITS == 2) {
@@ -774,7 +836,7 @@ __device__ __forceinline__ WorkRange wave_work(const DecodeArgs &a, int u, int s
 // tokens -- into rank-weighted byte shares (wave_work), and each workgroup
 // splits its share over its 4 waves.  Item costs are in KiB: a group (codes
 // + scale/zero) is bits + 2, a residual chunk (32 bf16 K and V rows) is 16.
-template <int BITS, int NHB, int META>
+template <int BITS, int NHB, int META, bool PAGED>
 __global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeArgs a) {
   constexpr int HMAX = 4 * NHB;
   __shared__ __align__(16) union {
@@ -807,12 +869,12 @@ __global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeArgs a) {
           a.q + ((long long)b * a.kv_heads * qpk + (long long)h * qpk + hh) * D + 32 * gq + 8 * cm);
   }
   const bool has_groups = g_begin < g_end;
-  const UnitView view = make_view<BITS, META>(a, u, n, gq, cm);
+  const UnitView view = make_view<BITS, META, PAGED>(a, u, n, gq, cm);
   // register sets of the load pipeline: kPrefetch groups in flight
   GroupRaw<BITS> r[kPrefetch + 1];
 #pragma unroll
   for (int i = 0; i < kPrefetch; ++i) {
-    load_group<BITS, META>(r[i], view, g_begin + i, g_begin + i < g_end);
+    load_group<BITS, META, PAGED>(r[i], view, a, u, g_begin + i, g_begin + i < g_end);
     // keep the groups' loads in group order, as in the loop, so that the
     // wait counts at the loop head are the steady-state ones
     __builtin_amdgcn_sched_barrier(0);
@@ -851,8 +913,8 @@ __global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeArgs a) {
 #pragma unroll
     for (int k = 0; k <= kPrefetch; ++k) {
       const int g = g0 + k;
-      load_group<BITS, META>(r[(k + kPrefetch) % (kPrefetch + 1)], view, g + kPrefetch,
-                             g + kPrefetch < g_end);
+      load_group<BITS, META, PAGED>(r[(k + kPrefetch) % (kPrefetch + 1)], view, a, u,
+                                    g + kPrefetch, g + kPrefetch < g_end);
       if (g < g_end) mfma_group<BITS, NHB, META>(r[k], st, sm.mf, qv, wave, n, gq, ch, cm);
     }
   }
@@ -910,19 +972,13 @@ struct ValuView {
   uint32_t o_k, o_v, o_mu;
 };
 
-template <int BITS, int META>
+template <int BITS, int META, bool PAGED>
 __device__ __forceinline__ ValuView make_valu_view(const DecodeArgs &a, int u, int tb, int cb,
                                                    int oc, int cq, int lane) {
   constexpr int KROW = D * BITS / 8;
-  const long long T = a.max_tokens, NG = a.n_groups_cap;
   ValuView v;
-  const uint32_t code_bytes = (uint32_t)(T * KROW);
-  v.kc = make_rsrc(a.k_codes + u * T * KROW, code_bytes);
-  v.vc = make_rsrc(a.v_codes + u * T * KROW, code_bytes);
-  v.ks = meta_rsrc<META>(a.k_scale, u, NG);
-  v.kz = meta_rsrc<META>(a.k_zero, u, NG);
-  v.vs = meta_rsrc<META>(a.v_scale, u, NG);
-  v.vz = meta_rsrc<META>(a.v_zero, u, NG);
+  const HistBufs hb = hist_bufs<BITS, META, PAGED>(a, u);
+  v.kc = hb.kc; v.vc = hb.vc; v.ks = hb.ks; v.kz = hb.kz; v.vs = hb.vs; v.vz = hb.vz;
   v.o_k = 4 * tb * KROW + 2 * BITS * cb;
   v.o_v = (oc * D + 8 * cq) * BITS;
   v.o_mu = 2 * kMetaBytes<META> * lane;
@@ -930,11 +986,12 @@ __device__ __forceinline__ ValuView make_valu_view(const DecodeArgs &a, int u, i
 }
 
 // Loads of group g (live == false: out-of-range loads, see load_group).
-template <int BITS, int META>
-__device__ __forceinline__ void load_valu_group(ValuRaw<BITS> &r, const ValuView &v, int g, bool live) {
+template <int BITS, int META, bool PAGED>
+__device__ __forceinline__ void load_valu_group(ValuRaw<BITS> &r, const ValuView &v,
+                                                const DecodeArgs &a, int u, int g, bool live) {
   constexpr int KROW = D * BITS / 8;
-  const uint32_t sc = __builtin_amdgcn_readfirstlane((uint32_t)g * (G * D * BITS / 8));
-  const uint32_t sm = __builtin_amdgcn_readfirstlane((uint32_t)g * (D * kMetaBytes<META>));
+  uint32_t sc, sm;
+  group_offsets<BITS, META, PAGED>(a, u, g, live, sc, sm);
   const uint32_t ob = live ? 0u : kOutOfRange;
   const uint32_t o_k = v.o_k + ob, o_v = v.o_v + ob, o_mu = v.o_mu + ob;
 #pragma unroll
@@ -1170,7 +1227,7 @@ __device__ __forceinline__ void valu_rchunk(const DecodeArgs &a, int u, int rc, 
   }
 }
 
-template <int BITS, int META>
+template <int BITS, int META, bool PAGED>
 __global__ __launch_bounds__(256) void decode_mha_kernel(DecodeArgs a) {
   __shared__ __align__(16) union {
     ValuSmem vs;
@@ -1189,10 +1246,13 @@ __global__ __launch_bounds__(256) void decode_mha_kernel(DecodeArgs a) {
   const uint4 *qp = reinterpret_cast<const uint4 *>(a.q + (long long)u * D + 16 * L.cb);
   const uint4 qraw[2] = {qp[0], qp[1]};
   const bool has_groups = wr.g_begin < wr.g_end;
-  const ValuView view = make_valu_view<BITS, META>(a, u, L.tb, L.cb, L.oc, L.cq, L.lane);
-  ValuRaw<BITS> r0, r1, r2;
-  load_valu_group<BITS, META>(r0, view, wr.g_begin, has_groups);
-  load_valu_group<BITS, META>(r1, view, wr.g_begin + 1, wr.g_begin + 1 < wr.g_end);
+  const ValuView view = make_valu_view<BITS, META, PAGED>(a, u, L.tb, L.cb, L.oc, L.cq, L.lane);
+  ValuRaw<BITS> r[kPrefetch + 1];
+#pragma unroll
+  for (int i = 0; i < kPrefetch; ++i) {
+    load_valu_group<BITS, META, PAGED>(r[i], view, a, u, wr.g_begin + i, wr.g_begin + i < wr.g_end);
+    __builtin_amdgcn_sched_barrier(0);   // group order, as in the loop
+  }
   float qv[16];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -1208,19 +1268,15 @@ __global__ __launch_bounds__(256) void decode_mha_kernel(DecodeArgs a) {
   for (int i = 0; i < 8; ++i) st.oacc[i] = 0.f;
   st.m_run = kNegInf; st.l_run = 0.f; st.z_run = 0.f;
 
-  // quantised groups: three register sets, two groups in flight
-  if (has_groups) {
-    int g = wr.g_begin;
-    while (true) {
-      load_valu_group<BITS, META>(r2, view, g + 2, g + 2 < wr.g_end);
-      valu_group<BITS, META>(r0, st, sm.vs, qv, L);
-      if (++g >= wr.g_end) break;
-      load_valu_group<BITS, META>(r0, view, g + 2, g + 2 < wr.g_end);
-      valu_group<BITS, META>(r1, st, sm.vs, qv, L);
-      if (++g >= wr.g_end) break;
-      load_valu_group<BITS, META>(r1, view, g + 2, g + 2 < wr.g_end);
-      valu_group<BITS, META>(r2, st, sm.vs, qv, L);
-      if (++g >= wr.g_end) break;
+  // quantised groups: the load pipeline of the MFMA path (fixed loads per
+  // pass, kPrefetch groups in flight)
+  for (int g0 = wr.g_begin; g0 < wr.g_end; g0 += kPrefetch + 1) {
+#pragma unroll
+    for (int k = 0; k <= kPrefetch; ++k) {
+      const int g = g0 + k;
+      load_valu_group<BITS, META, PAGED>(r[(k + kPrefetch) % (kPrefetch + 1)], view, a, u,
+                                         g + kPrefetch, g + kPrefetch < wr.g_end);
+      if (g < wr.g_end) valu_group<BITS, META>(r[k], st, sm.vs, qv, L);
     }
   }
   for (int rc = wr.r_begin; rc < wr.r_end; ++rc) valu_rchunk(a, u, rc, st, sm.vs, qv, L);
@@ -1249,20 +1305,25 @@ namespace {
 
 // Kernel variants: 0 = MHA (VALU), 1..4 = GQA with that many blocks of 4
 // query heads; for each bit width and scale/zero format.
-template <int BITS, int META>
+template <int BITS, int META, bool PAGED>
 void *kernel_fn_t(int variant) {
   switch (variant) {
-    case 0: return (void *)&decode_mha_kernel<BITS, META>;
-    case 1: return (void *)&decode_gqa_kernel<BITS, 1, META>;
-    case 2: return (void *)&decode_gqa_kernel<BITS, 2, META>;
-    case 3: return (void *)&decode_gqa_kernel<BITS, 3, META>;
-    default: return (void *)&decode_gqa_kernel<BITS, 4, META>;
+    case 0: return (void *)&decode_mha_kernel<BITS, META, PAGED>;
+    case 1: return (void *)&decode_gqa_kernel<BITS, 1, META, PAGED>;
+    case 2: return (void *)&decode_gqa_kernel<BITS, 2, META, PAGED>;
+    case 3: return (void *)&decode_gqa_kernel<BITS, 3, META, PAGED>;
+    default: return (void *)&decode_gqa_kernel<BITS, 4, META, PAGED>;
   }
 }
 
-void *kernel_fn(int bits, int meta, int variant) {
-  if (bits == 2) return meta == 1 ? kernel_fn_t<2, 1>(variant) : kernel_fn_t<2, 0>(variant);
-  return meta == 1 ? kernel_fn_t<4, 1>(variant) : kernel_fn_t<4, 0>(variant);
+template <bool PAGED>
+void *kernel_fn_p(int bits, int meta, int variant) {
+  if (bits == 2)
+    return meta == 1 ? kernel_fn_t<2, 1, PAGED>(variant) : kernel_fn_t<2, 0, PAGED>(variant);
+  return meta == 1 ? kernel_fn_t<4, 1, PAGED>(variant) : kernel_fn_t<4, 0, PAGED>(variant);
+}
+void *kernel_fn(int bits, int meta, int variant, bool paged) {
+  return paged ? kernel_fn_p<true>(bits, meta, variant) : kernel_fn_p<false>(bits, meta, variant);
 }
 
 // Occupancy of a kernel variant on the current device: resident workgroups
@@ -1272,14 +1333,14 @@ struct Residency {
   int per_cu, cus;
 };
 
-Residency residency(int bits, int meta, int variant) {
-  static int cache[16][2][2][5][2];   // 0 = not yet queried
+Residency residency(int bits, int meta, int variant, bool paged) {
+  static int cache[16][2][2][2][5][2];   // 0 = not yet queried
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
-  int *slot = cache[dev & 15][bits == 4 ? 1 : 0][meta == 1 ? 1 : 0][variant];
+  int *slot = cache[dev & 15][bits == 4 ? 1 : 0][meta == 1 ? 1 : 0][paged ? 1 : 0][variant];
   Residency r{__atomic_load_n(&slot[0], __ATOMIC_RELAXED), __atomic_load_n(&slot[1], __ATOMIC_RELAXED)};
   if (r.per_cu > 0 && r.cus > 0) return r;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&r.per_cu, kernel_fn(bits, meta, variant), 256,
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&r.per_cu, kernel_fn(bits, meta, variant, paged), 256,
                                                    0) != hipSuccess ||
       r.per_cu < 1)
     r.per_cu = 1;
@@ -1348,7 +1409,8 @@ int choose_wpu(int group_cost, const DecodeArgs &a, int slots) {
 hipError_t launch_decode(int bits, int meta, const DecodeArgs &a_in, hipStream_t s) {
   const int variant = a_in.qpk == 1 ? 0 : (a_in.qpk + 3) / 4;
   DecodeArgs a = a_in;
-  const Residency res = residency(bits, meta, variant);
+  const bool paged = a_in.pages.table != nullptr;
+  const Residency res = residency(bits, meta, variant, paged);
   const int slots = res.per_cu * res.cus;
   // KiB per group: codes (bits) + scale/zero (2 fp32 or 1 16-bit)
   const int group_cost = bits + (meta == 1 ? 1 : 2);
@@ -1361,7 +1423,7 @@ hipError_t launch_decode(int bits, int meta, const DecodeArgs &a_in, hipStream_t
     for (int i = 0; i < 4; ++i) a.rank_w[i] = 1;
   }
   const dim3 grid(a.n_units, a.n_split), block(256);
-  hipLaunchKernelGGL(reinterpret_cast<void (*)(DecodeArgs)>(kernel_fn(bits, meta, variant)), grid,
+  hipLaunchKernelGGL(reinterpret_cast<void (*)(DecodeArgs)>(kernel_fn(bits, meta, variant, paged)), grid,
                      block, 0, s, a);
   return hipGetLastError();
 }

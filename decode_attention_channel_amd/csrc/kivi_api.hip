@@ -133,8 +133,10 @@ kivi_status check_attend_args(const kivi_geom *g, const kivi_cache *c, const uin
 kivi_status enqueue_attend(const kivi_geom *g, const kivi_cache *c, const uint16_t *k_new,
                            const uint16_t *v_new, const uint16_t *q, float *out,
                            float softmax_scale, void *ws, hipStream_t s, int slots = 0,
-                           const int32_t *state_in = nullptr, int32_t *state_out = nullptr) {
+                           const int32_t *state_in = nullptr, int32_t *state_out = nullptr,
+                           const kivi::PageMap &pages = kivi::PageMap{}) {
   kivi::DecodeArgs a{};
+  a.pages = pages;
   a.k_codes = c->k_codes; a.k_scale = c->k_scale; a.k_zero = c->k_zero;
   a.v_codes = c->v_codes; a.v_scale = c->v_scale; a.v_zero = c->v_zero;
   a.k_res = c->k_res; a.v_res = c->v_res;
@@ -347,15 +349,19 @@ kivi_status kivi_dense_decode_attention(const kivi_geom *g, const uint16_t *k, c
                         g->max_tokens);
 }
 
-kivi_status kivi_ragged_prefill(const kivi_geom *g, const kivi_cache *c, const uint16_t *k,
-                                const uint16_t *v, int32_t stride, const int32_t *seq_lens,
-                                int32_t *state, void *stream) {
-  kivi_status st = check_geom(g);
-  if (st != KIVI_OK) return st;
-  if ((st = check_cache(c)) != KIVI_OK) return st;
+}  // extern "C"
+
+namespace {
+
+// Mixed-length prefill and decode step over a contiguous (pages.table ==
+// nullptr) or paged history; the caller has validated the geometry, the
+// cache pointers and the page map.
+kivi_status ragged_prefill_impl(const kivi_geom *g, const kivi_cache *c, const kivi::PageMap &pm,
+                                const uint16_t *k, const uint16_t *v, int32_t stride,
+                                const int32_t *seq_lens, int32_t *state, hipStream_t s) {
+  kivi_status st = KIVI_OK;
   if (!k || !v || !seq_lens || !state) return KIVI_E_NULL;
   if (stride < 1 || stride > (1 << 24)) return KIVI_E_SEQLEN;
-  hipStream_t s = (hipStream_t)stream;
   const int G = g->group, R = g->residual, slots = R + G;
   // the longest possible quantised part sizes the quantiser's grid
   int nq_max = 0, r_max = 0;
@@ -372,6 +378,7 @@ kivi_status kivi_ragged_prefill(const kivi_geom *g, const kivi_cache *c, const u
     a.v_codes = c->v_codes; a.v_scale = c->v_scale; a.v_zero = c->v_zero;
     a.seq_lens = seq_lens;
     a.kv_heads = g->kv_heads; a.residual = R; a.slots = slots; a.stride = stride;
+    a.pages = pm;
     if ((st = hip_status(kivi::launch_quantize(g->bits, g->meta_format, a, s))) != KIVI_OK)
       return st;
   }
@@ -381,24 +388,21 @@ kivi_status kivi_ragged_prefill(const kivi_geom *g, const kivi_cache *c, const u
   r.seq_lens = seq_lens; r.state = state;
   r.n_units = (int)units_of(g); r.kv_heads = g->kv_heads; r.stride = stride;
   r.group = G; r.residual = R; r.slots = slots; r.max_tokens = g->max_tokens;
+  r.pages = pm;
   return hip_status(kivi::launch_ragged_residual(r, s));
 }
 
-kivi_status kivi_ragged_decode_step(const kivi_geom *g, const kivi_cache *c,
-                                    const int32_t *state_in, int32_t *state_out,
-                                    const uint16_t *k_new, const uint16_t *v_new,
-                                    const uint16_t *q, float *out, float softmax_scale, void *ws,
-                                    size_t ws_bytes, void *stream) {
-  kivi_status st = check_geom(g);
-  if (st != KIVI_OK) return st;
-  if ((st = check_cache(c)) != KIVI_OK) return st;
+kivi_status ragged_step_impl(const kivi_geom *g, const kivi_cache *c, const kivi::PageMap &pm,
+                             const int32_t *state_in, int32_t *state_out, const uint16_t *k_new,
+                             const uint16_t *v_new, const uint16_t *q, float *out,
+                             float softmax_scale, void *ws, size_t ws_bytes, hipStream_t s) {
+  kivi_status st = KIVI_OK;
   if (!state_in || !state_out || !k_new || !v_new) return KIVI_E_NULL;
   if (state_in == state_out) return KIVI_E_STATE;
   if ((st = check_attend_args(g, c, q, out, softmax_scale, ws, ws_bytes)) != KIVI_OK) return st;
   // the flush runs before the fused append, which needs R >= G (see
   // kivi_decode_step)
   if (g->residual < g->group) return KIVI_E_UNSUPPORTED;
-  hipStream_t s = (hipStream_t)stream;
   const int G = g->group, slots = g->residual + G;
   // 1. flush: each sequence whose ring fills with this step's append
   kivi::QuantizeArgs f{};
@@ -410,6 +414,7 @@ kivi_status kivi_ragged_decode_step(const kivi_geom *g, const kivi_cache *c,
   f.v_codes = c->v_codes; f.v_scale = c->v_scale; f.v_zero = c->v_zero;
   f.state = state_in;
   f.kv_heads = g->kv_heads; f.residual = g->residual; f.slots = slots;
+  f.pages = pm;
   if ((st = hip_status(kivi::launch_quantize(g->bits, g->meta_format, f, s))) != KIVI_OK)
     return st;
   // 2. attention with the fused append; every sequence's counters come from
@@ -419,7 +424,114 @@ kivi_status kivi_ragged_decode_step(const kivi_geom *g, const kivi_cache *c,
   bound.n_res = slots;
   bound.res_start = 0;
   return enqueue_attend(g, &bound, k_new, v_new, q, out, softmax_scale, ws, s, 0, state_in,
-                        state_out);
+                        state_out, pm);
+}
+
+// Page map of a paged cache; KIVI_E_NULL / KIVI_E_UNSUPPORTED when the pool
+// description is unusable (see kivi_paged_layout).
+kivi_status paged_map(const kivi_geom *g, const kivi_paged_cache *pc, kivi::PageMap &pm,
+                      kivi_cache &c) {
+  if (!pc) return KIVI_E_NULL;
+  if (!pc->k_codes || !pc->k_scale || !pc->k_zero || !pc->v_codes || !pc->v_scale ||
+      !pc->v_zero || !pc->k_res || !pc->v_res || !pc->block_table)
+    return KIVI_E_NULL;
+  size_t bytes[8];
+  int32_t max_pages = 0;
+  kivi_status st = kivi_paged_layout(g, pc->page_groups, pc->num_pages, bytes, &max_pages);
+  if (st != KIVI_OK) return st;
+  int shift = 0;
+  while ((1 << shift) < pc->page_groups) ++shift;
+  pm.table = pc->block_table;
+  pm.shift = shift;
+  pm.max_pages = max_pages;
+  pm.num_pages = pc->num_pages;
+  c = kivi_cache{};
+  c.k_codes = pc->k_codes; c.k_scale = pc->k_scale; c.k_zero = pc->k_zero;
+  c.v_codes = pc->v_codes; c.v_scale = pc->v_scale; c.v_zero = pc->v_zero;
+  c.k_res = pc->k_res; c.v_res = pc->v_res;
+  return KIVI_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kivi_status kivi_ragged_prefill(const kivi_geom *g, const kivi_cache *c, const uint16_t *k,
+                                const uint16_t *v, int32_t stride, const int32_t *seq_lens,
+                                int32_t *state, void *stream) {
+  kivi_status st = check_geom(g);
+  if (st != KIVI_OK) return st;
+  if ((st = check_cache(c)) != KIVI_OK) return st;
+  return ragged_prefill_impl(g, c, kivi::PageMap{}, k, v, stride, seq_lens, state,
+                             (hipStream_t)stream);
+}
+
+kivi_status kivi_ragged_decode_step(const kivi_geom *g, const kivi_cache *c,
+                                    const int32_t *state_in, int32_t *state_out,
+                                    const uint16_t *k_new, const uint16_t *v_new,
+                                    const uint16_t *q, float *out, float softmax_scale, void *ws,
+                                    size_t ws_bytes, void *stream) {
+  kivi_status st = check_geom(g);
+  if (st != KIVI_OK) return st;
+  if ((st = check_cache(c)) != KIVI_OK) return st;
+  return ragged_step_impl(g, c, kivi::PageMap{}, state_in, state_out, k_new, v_new, q, out,
+                          softmax_scale, ws, ws_bytes, (hipStream_t)stream);
+}
+
+kivi_status kivi_paged_layout(const kivi_geom *g, int32_t page_groups, int32_t num_pages,
+                              size_t bytes[8], int32_t *max_pages) {
+  kivi_status st = check_geom(g);
+  if (st != KIVI_OK) return st;
+  if (!bytes) return KIVI_E_NULL;
+  if (page_groups < 1 || page_groups > (1 << 20) || (page_groups & (page_groups - 1)) != 0 ||
+      num_pages < 1)
+    return KIVI_E_UNSUPPORTED;
+  const size_t D = (size_t)g->head_dim, G = (size_t)g->group, b = (size_t)g->bits;
+  const size_t slots = (size_t)(g->residual + g->group);
+  const size_t mb = g->meta_format == KIVI_META_FP16_BF16 ? 2 : 4;
+  const double groups = (double)num_pages * g->kv_heads * page_groups;
+  // every pool is addressed with 32-bit offsets that must stay below 2^31
+  if (groups * G * D * b / 8 >= 2147483648.0 || groups * D * mb >= 2147483648.0)
+    return KIVI_E_UNSUPPORTED;
+  const size_t n = (size_t)groups;
+  bytes[KIVI_BUF_K_CODES] = n * G * D * b / 8;
+  bytes[KIVI_BUF_K_SCALE] = n * D * mb;
+  bytes[KIVI_BUF_K_ZERO] = n * D * mb;
+  bytes[KIVI_BUF_V_CODES] = n * G * D * b / 8;
+  bytes[KIVI_BUF_V_SCALE] = n * D * mb;
+  bytes[KIVI_BUF_V_ZERO] = n * D * mb;
+  bytes[KIVI_BUF_K_RES] = (size_t)units_of(g) * slots * D * 2;
+  bytes[KIVI_BUF_V_RES] = (size_t)units_of(g) * slots * D * 2;
+  if (max_pages) {
+    const int ng = g->max_tokens / g->group;
+    *max_pages = (ng + page_groups - 1) / page_groups;
+  }
+  return KIVI_OK;
+}
+
+kivi_status kivi_paged_prefill(const kivi_geom *g, const kivi_paged_cache *pc, const uint16_t *k,
+                               const uint16_t *v, int32_t stride, const int32_t *seq_lens,
+                               int32_t *state, void *stream) {
+  kivi_status st = check_geom(g);
+  if (st != KIVI_OK) return st;
+  kivi::PageMap pm{};
+  kivi_cache c{};
+  if ((st = paged_map(g, pc, pm, c)) != KIVI_OK) return st;
+  return ragged_prefill_impl(g, &c, pm, k, v, stride, seq_lens, state, (hipStream_t)stream);
+}
+
+kivi_status kivi_paged_decode_step(const kivi_geom *g, const kivi_paged_cache *pc,
+                                   const int32_t *state_in, int32_t *state_out,
+                                   const uint16_t *k_new, const uint16_t *v_new, const uint16_t *q,
+                                   float *out, float softmax_scale, void *ws, size_t ws_bytes,
+                                   void *stream) {
+  kivi_status st = check_geom(g);
+  if (st != KIVI_OK) return st;
+  kivi::PageMap pm{};
+  kivi_cache c{};
+  if ((st = paged_map(g, pc, pm, c)) != KIVI_OK) return st;
+  return ragged_step_impl(g, &c, pm, state_in, state_out, k_new, v_new, q, out, softmax_scale,
+                          ws, ws_bytes, (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -41,6 +41,30 @@ __host__ __device__ inline bool seq_split(int S, int stride, int G, int R, int T
   return n_q <= T;
 }
 
+// Paged quantised history.  With table == nullptr every unit owns one
+// contiguous block of n_groups_cap groups in each group-major array (group
+// slot u * NG + g).  Otherwise the arrays are pools of pages; a page holds
+// 2^shift consecutive groups of every kv head of one sequence, and group g of
+// unit (b, h) has slot (table[b][g >> shift] * H + h) * 2^shift + g % 2^shift.
+// Page entries outside [0, num_pages) map nothing.
+struct PageMap {
+  const int32_t *table;   // [B][max_pages]
+  int shift, max_pages, num_pages;
+};
+
+// Group slot of group g of unit u (the multiplier of a group's bytes in the
+// group-major arrays), or -1 when a paged unit has no page for it.
+__host__ __device__ inline long long group_slot(const PageMap &p, int kv_heads, int n_groups_cap,
+                                                int u, int g) {
+  if (!p.table) return (long long)u * n_groups_cap + g;
+  const int pi = g >> p.shift;
+  if (g < 0 || pi >= p.max_pages) return -1;
+  const int b = u / kv_heads, h = u % kv_heads;
+  const int e = p.table[(long long)b * p.max_pages + pi];
+  if (e < 0 || e >= p.num_pages) return -1;
+  return (((long long)e * kv_heads + h) << p.shift) + (g & ((1 << p.shift) - 1));
+}
+
 // One launch of the group quantiser: `n_groups` groups of G tokens for each
 // of `n_units` units.  Source token i of local group gl of unit u is row
 // (src_tok0 + gl*G + i) of a [rows][D] bf16 block starting at
@@ -61,6 +85,7 @@ struct QuantizeArgs {
   // append, from its own ring start into its own next group.
   const int32_t *seq_lens, *state;
   int kv_heads, residual, slots, stride;
+  PageMap pages;   // destination group slots (group_slot)
 };
 hipError_t launch_quantize(int bits, int meta, const QuantizeArgs &a, hipStream_t s);
 
@@ -86,6 +111,7 @@ struct RaggedResidualArgs {
   const int32_t *seq_lens;         // [B]
   int32_t *state;                  // [B][4]
   int n_units, kv_heads, stride, group, residual, slots, max_tokens;
+  PageMap pages;                   // a sequence whose history lacks a page is bad
 };
 hipError_t launch_ragged_residual(const RaggedResidualArgs &a, hipStream_t s);
 
@@ -115,6 +141,9 @@ struct DecodeArgs {
   // head 0 writes the result to state_out.
   const int32_t *state_in;
   int32_t *state_out;
+  // paged history (table == nullptr: contiguous per unit); with pages, a
+  // flush also needs a page for the new group
+  PageMap pages;
   // byte shares: workgroup (unit u, split s) has linear index s*n_units+u
   // and co-residency rank min(index / cus, 3) on its compute unit; its share
   // of the unit's bytes is proportional to rank_w[rank]

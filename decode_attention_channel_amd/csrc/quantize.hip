@@ -96,6 +96,8 @@ __device__ __forceinline__ void key_group(const QuantizeArgs &a, int u, int gl,
                                           uint8_t *tile) {
   constexpr int D = kHeadDim, G = kGroup, KROW = D * BITS / 8;
   const int p = lane & 31, h = lane >> 5;
+  const long long slot = group_slot(a.pages, a.kv_heads, a.n_groups_cap, u, a.dst_g0 + gl);
+  if (slot < 0) return;   // paged: no page for this group
   float x0[16], x1[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
@@ -115,10 +117,8 @@ __device__ __forceinline__ void key_group(const QuantizeArgs &a, int u, int gl,
   uint32_t sb0, sb1;
   group_params<BITS, META>(mn0, mx0, sc0, inv0, sb0);
   group_params<BITS, META>(mn1, mx1, sc1, inv1, sb1);
-  const int g = a.dst_g0 + gl;
-  const long long unit_grp = (long long)u * a.n_groups_cap + g;
   if (h == 0) {
-    const long long m = unit_grp * D + cb;   // element index of channel cb
+    const long long m = slot * D + cb;   // element index of channel cb
     if constexpr (META == 1) {
       reinterpret_cast<uint32_t *>(static_cast<uint16_t *>(a.k_scale) + m)[p] = sb0 | (sb1 << 16);
       reinterpret_cast<uint32_t *>(static_cast<uint16_t *>(a.k_zero) + m)[p] =
@@ -138,8 +138,7 @@ __device__ __forceinline__ void key_group(const QuantizeArgs &a, int u, int gl,
   const int row = lane >> 1, c32 = 32 * (lane & 1);
   const uint4 b0 = *reinterpret_cast<const uint4 *>(tile + row * 64 + c32);
   const uint4 b1 = *reinterpret_cast<const uint4 *>(tile + row * 64 + c32 + 16);
-  uint8_t *dst = a.k_codes + ((long long)u * a.max_tokens + (long long)g * G + row) * KROW +
-                 (cb + c32) * BITS / 8;
+  uint8_t *dst = a.k_codes + (slot * G + row) * KROW + (cb + c32) * BITS / 8;
   if constexpr (BITS == 2) {
     const uint32_t w0 = pack4x2(b0.x) | (pack4x2(b0.y) << 8) | (pack4x2(b0.z) << 16) |
                         (pack4x2(b0.w) << 24);
@@ -189,6 +188,8 @@ __device__ __forceinline__ void value_group(const QuantizeArgs &a, int u, int gl
                                             uint8_t *tile) {
   constexpr int D = kHeadDim, G = kGroup;
   const int r = lane >> 2, q = lane & 3;
+  const long long slot = group_slot(a.pages, a.kv_heads, a.n_groups_cap, u, a.dst_g0 + gl);
+  if (slot < 0) return;   // paged: no page for this group
   float x[32];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -205,9 +206,7 @@ __device__ __forceinline__ void value_group(const QuantizeArgs &a, int u, int gl
   float sc, inv;
   uint32_t sb;
   group_params<BITS, META>(mn, mx, sc, inv, sb);
-  const int g = a.dst_g0 + gl;
-  const long long unit_grp = (long long)u * a.n_groups_cap + g;
-  const long long mi = (unit_grp * (D / G) + q) * G + 16 * part + r;
+  const long long mi = (slot * (D / G) + q) * G + 16 * part + r;
   if constexpr (META == 1) {
     static_cast<uint16_t *>(a.v_scale)[mi] = (uint16_t)sb;
     static_cast<uint16_t *>(a.v_zero)[mi] = (uint16_t)zero_bits(mn);
@@ -234,7 +233,7 @@ __device__ __forceinline__ void value_group(const QuantizeArgs &a, int u, int gl
 #pragma unroll
     for (int i = 0; i < 4; ++i) cell[i] |= ((w >> (8 * i)) & 0xFFu) << (BITS * k);
   }
-  uint8_t *dst = a.v_codes + ((unit_grp * (G / 8) + 2 * part + o) * D + 4 * c4) * BITS;
+  uint8_t *dst = a.v_codes + ((slot * (G / 8) + 2 * part + o) * D + 4 * c4) * BITS;
   if constexpr (BITS == 2) {
     *reinterpret_cast<uint2 *>(dst) = make_uint2(cell[0] | (cell[1] << 16), cell[2] | (cell[3] << 16));
   } else {
@@ -316,10 +315,20 @@ __global__ __launch_bounds__(256) void ragged_residual_kernel(RaggedResidualArgs
   constexpr int CH = kHeadDim / 8;   // 16-byte chunks per row
   const int u = blockIdx.y, b = u / a.kv_heads;
   int n_q, r;
-  const bool ok = seq_split(a.seq_lens[b], a.stride, a.group, a.residual, a.max_tokens, n_q, r);
-  if (blockIdx.x == 0 && blockIdx.z == 0 && threadIdx.x == 0 && u % a.kv_heads == 0) {
-    const int flags = ok ? 0 : kSeqBadLength;
-    reinterpret_cast<int4 *>(a.state)[b] = ok ? make_int4(n_q, r, 0, 0) : make_int4(0, 0, 0, flags);
+  bool ok = seq_split(a.seq_lens[b], a.stride, a.group, a.residual, a.max_tokens, n_q, r);
+  if (blockIdx.x == 0 && blockIdx.z == 0 && u % a.kv_heads == 0) {
+    // the state block: with pages, every history group needs its page
+    // (the quantiser skips groups without one)
+    bool missing = false;
+    if (ok && a.pages.table) {
+      const int n_pages = ((n_q / a.group) + (1 << a.pages.shift) - 1) >> a.pages.shift;
+      for (int i = threadIdx.x; i < n_pages; i += blockDim.x)
+        missing |= group_slot(a.pages, a.kv_heads, 0, u, i << a.pages.shift) < 0;
+    }
+    ok = ok && !__syncthreads_or(missing);
+    if (threadIdx.x == 0)
+      reinterpret_cast<int4 *>(a.state)[b] = ok ? make_int4(n_q, r, 0, 0)
+                                               : make_int4(0, 0, 0, kSeqBadLength);
   }
   if (!ok) return;
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;

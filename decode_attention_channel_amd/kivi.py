@@ -25,7 +25,8 @@ EXPORTS = (
     "kivi_cache_layout", "kivi_decode_workspace_size", "kivi_quantize_prefill",
     "kivi_append_token", "kivi_flush_residual", "kivi_decode_attention",
     "kivi_decode_step", "kivi_dense_decode_attention", "kivi_ragged_prefill",
-    "kivi_ragged_decode_step", "kivi_status_string", "kivi_last_hip_error",
+    "kivi_ragged_decode_step", "kivi_paged_layout", "kivi_paged_prefill",
+    "kivi_paged_decode_step", "kivi_status_string", "kivi_last_hip_error",
 )
 BUFFERS = ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero", "k_res", "v_res")
 META_FP32, META_FP16_BF16 = 0, 1   # scale/zero formats (kivi_geom.meta_format)
@@ -53,6 +54,12 @@ class _Cache(ctypes.Structure):
         ("n_q", ctypes.c_int32), ("n_res", ctypes.c_int32), ("res_start", ctypes.c_int32)]
 
 
+class _PagedCache(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in BUFFERS] + [
+        ("block_table", ctypes.c_void_p), ("page_groups", ctypes.c_int32),
+        ("num_pages", ctypes.c_int32)]
+
+
 def _load():
     if not os.path.exists(_LIB_PATH):
         raise ImportError(f"{_LIB_PATH} is not built: run `python "
@@ -73,10 +80,13 @@ def _load():
     lib.kivi_ragged_prefill.argtypes = [G, C, P, P, ctypes.c_int32, P, P, P]
     lib.kivi_ragged_decode_step.argtypes = [G, C, P, P, P, P, P, P, ctypes.c_float, P,
                                             ctypes.c_size_t, P]
-    for f in ("kivi_cache_layout", "kivi_decode_workspace_size", "kivi_quantize_prefill",
-              "kivi_append_token", "kivi_flush_residual", "kivi_decode_attention",
-              "kivi_decode_step", "kivi_dense_decode_attention", "kivi_ragged_prefill",
-              "kivi_ragged_decode_step"):
+    PC = ctypes.POINTER(_PagedCache)
+    lib.kivi_paged_layout.argtypes = [G, ctypes.c_int32, ctypes.c_int32, sz,
+                                      ctypes.POINTER(ctypes.c_int32)]
+    lib.kivi_paged_prefill.argtypes = [G, PC, P, P, ctypes.c_int32, P, P, P]
+    lib.kivi_paged_decode_step.argtypes = [G, PC, P, P, P, P, P, P, ctypes.c_float, P,
+                                           ctypes.c_size_t, P]
+    for f in EXPORTS[:-2]:
         getattr(lib, f).restype = ctypes.c_int
     lib.kivi_status_string.argtypes = [ctypes.c_int]
     lib.kivi_status_string.restype = ctypes.c_char_p
@@ -196,6 +206,94 @@ class Cache:
 
     def nbytes(self) -> int:
         return sum(getattr(self, n).numel() * getattr(self, n).element_size() for n in BUFFERS)
+
+
+def paged_layout(g: Geom, page_groups: int, num_pages: int) -> tuple[list[int], int]:
+    out = (ctypes.c_size_t * 8)()
+    mp = ctypes.c_int32(0)
+    _check(_lib.kivi_paged_layout(ctypes.byref(g.c()), page_groups, num_pages, out,
+                                  ctypes.byref(mp)), "kivi_paged_layout")
+    return list(out), mp.value
+
+
+class PagedCache:
+    """Pools of a paged history (shaped [slots][...] by the documented
+    layout), the residual rings and the block table (int32 [B][max_pages],
+    all entries -1 = unassigned until the caller assigns pages)."""
+
+    def __init__(self, g: Geom, page_groups: int, num_pages: int, device=None):
+        device = torch.device("cuda", torch.cuda.current_device()) if device is None else device
+        sizes, self.max_pages = paged_layout(g, page_groups, num_pages)
+        B, H, D, b, G = g.batch, g.kv_heads, g.head_dim, g.bits, g.group
+        n, S = num_pages * H * page_groups, g.residual + g.group
+        m16 = g.meta_format == META_FP16_BF16
+        st = torch.float16 if m16 else torch.float32
+        zt = torch.bfloat16 if m16 else torch.float32
+        shapes = {
+            "k_codes": ((n, G, D * b // 8), torch.uint8),
+            "k_scale": ((n, D), st),
+            "k_zero": ((n, D), zt),
+            "v_codes": ((n, G // 8, D, b), torch.uint8),
+            "v_scale": ((n, D // G, G), st),
+            "v_zero": ((n, D // G, G), zt),
+            "k_res": ((B, H, S, D), torch.bfloat16),
+            "v_res": ((B, H, S, D), torch.bfloat16),
+        }
+        self.geom, self.page_groups, self.num_pages = g, page_groups, num_pages
+        for (name, (shape, dt)), nbytes in zip(shapes.items(), sizes):
+            t = torch.empty(shape, dtype=dt, device=device)
+            assert t.numel() * t.element_size() == nbytes, name
+            setattr(self, name, t)
+        self.block_table = torch.full((B, self.max_pages), -1, dtype=torch.int32, device=device)
+        self._c = _PagedCache(*[ctypes.c_void_p(getattr(self, n).data_ptr()) for n in BUFFERS],
+                              ctypes.c_void_p(self.block_table.data_ptr()), page_groups,
+                              num_pages)
+
+    def slot(self, b: int, h: int, g: int, table=None) -> int:
+        """Pool slot of group g of (sequence b, kv head h); -1 without a page."""
+        table = self.block_table.cpu() if table is None else table
+        e = int(table[b, g // self.page_groups])
+        if e < 0 or e >= self.num_pages:
+            return -1
+        return (e * self.geom.kv_heads + h) * self.page_groups + g % self.page_groups
+
+
+def paged_prefill(g: Geom, c: PagedCache, k: torch.Tensor, v: torch.Tensor,
+                  seq_lens: torch.Tensor, state: torch.Tensor | None = None) -> torch.Tensor:
+    """Mixed-length prefill into a paged cache (see ragged_prefill)."""
+    stride = k.shape[2] if k.dim() == 4 else -1
+    shape = (g.batch, g.kv_heads, stride, g.head_dim)
+    if state is None:
+        state = torch.empty(g.batch, 4, dtype=torch.int32, device=k.device)
+    _check(_lib.kivi_paged_prefill(ctypes.byref(g.c()), ctypes.byref(c._c),
+                                   _ptr(k, torch.bfloat16, shape, "k"),
+                                   _ptr(v, torch.bfloat16, shape, "v"), stride,
+                                   _ptr(seq_lens, torch.int32, (g.batch,), "seq_lens"),
+                                   _ptr(state, torch.int32, (g.batch, 4), "state"), _stream()),
+           "kivi_paged_prefill")
+    return state
+
+
+def paged_decode_step(g: Geom, c: PagedCache, state_in: torch.Tensor, state_out: torch.Tensor,
+                      k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor,
+                      out: torch.Tensor | None = None, softmax_scale: float | None = None,
+                      ws: Workspace | None = None) -> torch.Tensor:
+    """One mixed-length step over a paged cache (see ragged_decode_step)."""
+    shape = (g.batch, g.q_heads, g.head_dim)
+    tok = (g.batch, g.kv_heads, g.head_dim)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = Workspace(g, q.device)
+    scale = 1.0 / math.sqrt(g.head_dim) if softmax_scale is None else float(softmax_scale)
+    _check(_lib.kivi_paged_decode_step(
+        ctypes.byref(g.c()), ctypes.byref(c._c),
+        _ptr(state_in, torch.int32, (g.batch, 4), "state_in"),
+        _ptr(state_out, torch.int32, (g.batch, 4), "state_out"),
+        _ptr(k_new, torch.bfloat16, tok, "k_new"), _ptr(v_new, torch.bfloat16, tok, "v_new"),
+        _ptr(q, torch.bfloat16, shape, "q"), _ptr(out, torch.float32, shape, "out"), scale,
+        ctypes.c_void_p(ws.buf.data_ptr()), ws.nbytes, _stream()), "kivi_paged_decode_step")
+    return out
 
 
 def quantize_prefill(g: Geom, c: Cache, k: torch.Tensor, v: torch.Tensor) -> None:
@@ -397,7 +495,8 @@ class LayerStepper:
 
 
 class RaggedStepper:
-    """Pre-marshalled kivi_ragged_decode_step of one layer for tight loops
+    """Pre-marshalled kivi_ragged_decode_step (kivi_paged_decode_step for a
+    PagedCache) of one layer for tight loops
     and graph capture: the new token, q and out buffers are fixed (the
     caller refills them), and the two state buffers alternate, step(0)
     reading state_a and writing state_b, step(1) the other way round.  The
@@ -412,6 +511,8 @@ class RaggedStepper:
         self.geom, self.cache = g, c
         self._g = g.c()
         self._gp, self._cp = ctypes.byref(self._g), ctypes.byref(c._c)
+        self._fn = (_lib.kivi_paged_decode_step if isinstance(c, PagedCache)
+                    else _lib.kivi_ragged_decode_step)
         st = [_ptr(x, torch.int32, (g.batch, 4), "state") for x in (state_a, state_b)]
         if st[0].value == st[1].value:
             raise ValueError("state_a and state_b must be distinct buffers")
@@ -427,6 +528,5 @@ class RaggedStepper:
 
     def step(self, parity: int) -> None:
         a, b = self._st[parity & 1], self._st[(parity & 1) ^ 1]
-        _check(_lib.kivi_ragged_decode_step(self._gp, self._cp, a, b, self._k, self._v, self._q,
-                                            self._out, self._scale, self._ws, self._wsn,
-                                            _stream()), "kivi_ragged_decode_step")
+        _check(self._fn(self._gp, self._cp, a, b, self._k, self._v, self._q, self._out,
+                        self._scale, self._ws, self._wsn, _stream()), self._fn.__name__)

@@ -338,6 +338,72 @@ kivi_status kivi_ragged_decode_step(const kivi_geom *geom, const kivi_cache *cac
                                     const uint16_t *q, float *out, float softmax_scale,
                                     void *ws, size_t ws_bytes, void *stream);
 
+/* ------------------------------------------------------------------------
+ * Paged history (for serving: a pool of fixed-size pages shared by the
+ * sequences of a batch, assigned by the caller through a block table).  The
+ * quantised history is split into pages of page_groups consecutive groups
+ * (page_groups * 32 tokens); one page holds those groups for every kv head
+ * of one sequence.  Sequence b's group g lives in page block_table[b][g /
+ * page_groups]; inside the pools, (page p, kv head h, group i of the page)
+ * is group slot s = (p * H + h) * page_groups + i, and every pool keeps the
+ * per-group layout of kivi_cache with the unit block replaced by slots:
+ *   k_codes  [slots][G][D*b/8]      k_scale, k_zero  [slots][D]
+ *   v_codes  [slots][G/8][D][b]     v_scale, v_zero  [slots][D/G][G]
+ * (scale/zero in the geom's meta_format).  The residual rings are not paged:
+ * k_res, v_res are [B][H][R+G][D] as in kivi_cache.  Lengths are per
+ * sequence, in the same device state as the mixed-length calls above.
+ *
+ * block_table: device int32 [B][max_pages] (kivi_paged_layout gives
+ * max_pages = ceil(max_tokens / G / page_groups)); entries outside
+ * [0, num_pages) are unassigned.  The library only reads it; the caller
+ * assigns pages (a page must not serve two sequences) and may add pages
+ * between calls.  A prefill whose history needs an unassigned page gives the
+ * sequence KIVI_SEQ_BAD_LENGTH; a flush into an unassigned page is treated
+ * like a full cache (KIVI_SEQ_FULL: the sequence keeps its cache and takes
+ * no more tokens), so assigning the next page before it is needed keeps a
+ * sequence going.  A history group whose entry is changed to an unassigned
+ * one after it was written reads as zeros.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  uint8_t  *k_codes;            /* pools (kivi_paged_layout sizes)          */
+  void     *k_scale;
+  void     *k_zero;
+  uint8_t  *v_codes;
+  void     *v_scale;
+  void     *v_zero;
+  uint16_t *k_res;              /* [B][H][R+G][D] rings, as in kivi_cache  */
+  uint16_t *v_res;
+  const int32_t *block_table;   /* device [B][max_pages]                    */
+  int32_t   page_groups;        /* groups per page: a power of two <= 2^20  */
+  int32_t   num_pages;          /* pages in each pool                        */
+} kivi_paged_cache;
+
+/* Byte sizes of the buffers of a paged cache (indexed by kivi_buffer: the
+ * six pools, then the two rings) and the block table's row length.  Every
+ * pool must stay below 2 GiB (its offsets are 32-bit).
+ * Errors: KIVI_E_NULL (bytes), KIVI_E_GEOMETRY, KIVI_E_UNSUPPORTED (geom
+ *         outside the supported set, page_groups not a power of two in
+ *         [1, 2^20], num_pages < 1, or a pool of 2 GiB or more). */
+kivi_status kivi_paged_layout(const kivi_geom *geom, int32_t page_groups, int32_t num_pages,
+                              size_t bytes[8], int32_t *max_pages);
+
+/* kivi_ragged_prefill into a paged cache: the same split, codes and
+ * scale/zero bytes per sequence, stored in the sequence's pages.
+ * Errors: those of kivi_ragged_prefill and kivi_paged_layout; KIVI_E_NULL
+ *         for a NULL pool, ring or block table. */
+kivi_status kivi_paged_prefill(const kivi_geom *geom, const kivi_paged_cache *cache,
+                               const uint16_t *k, const uint16_t *v, int32_t stride,
+                               const int32_t *seq_lens, int32_t *state, void *stream);
+
+/* kivi_ragged_decode_step over a paged cache (flushes write the new group
+ * into its page).  The same two launches with fixed arguments.
+ * Errors: those of kivi_ragged_decode_step and kivi_paged_layout. */
+kivi_status kivi_paged_decode_step(const kivi_geom *geom, const kivi_paged_cache *cache,
+                                   const int32_t *state_in, int32_t *state_out,
+                                   const uint16_t *k_new, const uint16_t *v_new,
+                                   const uint16_t *q, float *out, float softmax_scale,
+                                   void *ws, size_t ws_bytes, void *stream);
+
 /* Static description of a status code (never NULL). */
 const char *kivi_status_string(kivi_status status);
 

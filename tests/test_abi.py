@@ -20,7 +20,7 @@ def _declared():
 
 def test_exports_every_declared_function():
     names = _declared()
-    assert len(names) == 12
+    assert len(names) == 15
     lib = ctypes.CDLL(kivi.library_path())
     for n in names:
         assert hasattr(lib, n), n
@@ -199,6 +199,61 @@ def test_ragged_calls_validation_before_any_device_work():
     assert step(so=fake) == 9           # state_in and state_out must differ
     assert step(nbytes=ws_need - 1) == 7
     assert step(geom=_g(residual=0).c()) == 3   # the fused append needs R >= G
+
+
+def _paged_struct(P=4, pages=20, null=None):
+    ptrs = [ctypes.c_void_p(0x1000 * (i + 1)) for i in range(9)]
+    if null is not None:
+        ptrs[null] = ctypes.c_void_p(0)
+    return kivi._PagedCache(*ptrs, P, pages)
+
+
+@pytest.mark.parametrize("bits,meta", [(2, 0), (4, 1)])
+def test_paged_layout_sizes(bits, meta):
+    g = _g(bits=bits, meta_format=meta)
+    sizes, max_pages = kivi.paged_layout(g, 4, 10)
+    n = 10 * 3 * 4                         # pages * kv heads * groups per page
+    mb = 2 if meta else 4
+    assert max_pages == 8                  # 32 groups of capacity / 4
+    assert sizes == [n * 32 * 128 * bits // 8, n * 128 * mb, n * 128 * mb,
+                     n * 32 * 128 * bits // 8, n * 128 * mb, n * 128 * mb,
+                     6 * 160 * 128 * 2, 6 * 160 * 128 * 2]
+    assert kivi.paged_layout(g, 16, 1)[1] == 2
+    assert kivi.paged_layout(g, 64, 1)[1] == 1
+
+
+def test_paged_calls_validation_before_any_device_work():
+    g = _g().c()
+    fake = ctypes.c_void_p(0x2000)
+    fake2 = ctypes.c_void_p(0x3000)
+    P = ctypes.byref
+    out = (ctypes.c_size_t * 8)()
+    mp = ctypes.c_int32(0)
+    for pg, pages, status in [(3, 10, 3), (0, 10, 3), (1 << 21, 1, 3), (4, 0, 3), (4, 1, 0),
+                              (1 << 20, 1, 3)]:   # the last: pools of 2 GiB and more
+        assert _call("kivi_paged_layout", P(g), pg, pages, out, P(mp)) == status, (pg, pages)
+    assert _call("kivi_paged_layout", P(g), 4, 10, None, P(mp)) == 1
+    assert _call("kivi_paged_layout", P(g), 4, 10, out, None) == 0
+    ws_need = kivi.workspace_size(_g())
+    for null in range(9):
+        assert _call("kivi_paged_prefill", P(g), P(_paged_struct(null=null)), fake, fake, 100,
+                     fake, fake, None) == 1, null
+    assert _call("kivi_paged_prefill", P(g), P(_paged_struct(P=6)), fake, fake, 100, fake, fake,
+                 None) == 3
+    assert _call("kivi_paged_prefill", P(g), P(_paged_struct()), fake, fake, 0, fake, fake,
+                 None) == 4
+    assert _call("kivi_paged_prefill", P(g), None, fake, fake, 100, fake, fake, None) == 1
+
+    def step(geom=g, pc=_paged_struct(), si=fake, so=fake2, nbytes=ws_need):
+        return _call("kivi_paged_decode_step", P(geom), P(pc), si, so, fake, fake, fake, fake,
+                     ctypes.c_float(0.1), fake, nbytes, None)
+
+    assert step(si=None) == 1 and step(so=None) == 1
+    assert step(so=fake) == 9
+    assert step(nbytes=ws_need - 1) == 7
+    assert step(pc=_paged_struct(pages=0)) == 3
+    assert step(pc=_paged_struct(null=8)) == 1   # block table
+    assert step(geom=_g(residual=0).c()) == 3
 
 
 def test_status_strings():
