@@ -151,16 +151,16 @@ __device__ __forceinline__ void ld16(const float *p, float (&x)[16]) {
 // ---------------------------------------------------------------- merge ---
 // Each wave contributes (m, l, o[128]) per head; the workgroup writes one
 // partial per head: M = max m_w, l = sum 2^(m_w - M) l_w, o likewise.
-template <int HMAX>
+template <int HMAX, int NW>
 struct MergeSmem {
-  float m[4][HMAX];
-  float l[4][HMAX];
-  float o[4][HMAX][D];
+  float m[NW][HMAX];
+  float l[NW][HMAX];
+  float o[NW][HMAX][D];
   int last;
 };
 
-template <int HMAX>
-__device__ void merge_and_store(MergeSmem<HMAX> &sm, const DecodeArgs &a, int u, int split) {
+template <int HMAX, int NW>
+__device__ void merge_and_store(MergeSmem<HMAX, NW> &sm, const DecodeArgs &a, int u, int split) {
   __syncthreads();
   const int qpk = a.qpk;
   float *part = a.part + ((long long)u * a.n_split + split) * qpk * kPartStride;
@@ -168,10 +168,10 @@ __device__ void merge_and_store(MergeSmem<HMAX> &sm, const DecodeArgs &a, int u,
     const int hh = idx / D, c = idx % D;
     float M = kNegInf;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, sm.m[w][hh]);
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm.m[w][hh]);
     float l = 0.f, o = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < NW; ++w) {
       const float f = sm.m[w][hh] == kNegInf ? 0.f : fast_exp2(sm.m[w][hh] - M);
       l += f * sm.l[w][hh];
       o += f * sm.o[w][hh][c];
@@ -444,6 +444,12 @@ __device__ __forceinline__ UnitView make_view(const DecodeArgs &a, int u, int n,
 // the group it computes and not for the prefetches behind it.
 constexpr uint32_t kOutOfRange = 0x80000000u;   // > any unit's buffer size
 
+// Unpack the codes of a group next to the MFMAs that read them (1) or all
+// at the start of the group (0).
+#ifndef KIVI_LAZY_UNPACK
+#define KIVI_LAZY_UNPACK 1
+#endif
+
 // Groups in flight per wave beyond the one being computed (MFMA path).
 #ifndef KIVI_PREFETCH
 #define KIVI_PREFETCH 2
@@ -519,12 +525,19 @@ __device__ __forceinline__ void stage_meta(const uint32_t (&mw)[4][2], float (*m
   }
 }
 
+// Per-wave LDS staging.  A wave works on quantised groups (bq, meta) and,
+// after them, on residual chunks (vres), so the two share storage.
 template <int NHB>
+union WaveSmem {
+  struct {
+    uint4 bq[NHB][128];    // q' operand chunks (8 bf16) per head block, indexed by bq_index
+    float meta[4][D];      // the current group's k_scale, k_zero, v_scale, v_zero
+  } g;
+  uint16_t vres[G][D];     // one residual chunk of V rows (bf16)
+};
+template <int NHB, int NW>
 struct MfmaSmem {
-  // q' operand chunks (8 bf16) per wave and head block, indexed by bq_index
-  uint4 bq[4][NHB][128];
-  float meta[4][4][D];             // [wave] the current group's k_scale, k_zero, v_scale, v_zero
-  uint16_t vres[4][G][D];          // [wave] one residual chunk of V rows (bf16)
+  WaveSmem<NHB> w[NW];
 };
 
 // LDS chunk of the q' operand for (hi/lo xx, head h, MFMA step m, lane group
@@ -544,12 +557,12 @@ struct WaveState {
   float m_run[NHB], l_run[NHB], z_run[NHB];
 };
 
-template <int BITS, int NHB, int META>
+template <int BITS, int NHB, int META, int NW>
 __device__ __forceinline__ void mfma_group(const GroupRaw<BITS> &raw, WaveState<NHB> &st,
-                                           MfmaSmem<NHB> &smf, const float (&qv)[NHB][8],
+                                           MfmaSmem<NHB, NW> &smf, const float (&qv)[NHB][8],
                                            int wave, int n, int gq, int ch, int cm) {
   // scale/zero of this group: stage in LDS, read back what each role needs
-  stage_meta<META>(raw.mw, smf.meta[wave], 16 * gq + n);
+  stage_meta<META>(raw.mw, smf.w[wave].g.meta, 16 * gq + n);
   __builtin_amdgcn_wave_barrier();
   struct {
     const uint32_t (&kw)[2][BITS];
@@ -557,34 +570,43 @@ __device__ __forceinline__ void mfma_group(const GroupRaw<BITS> &raw, WaveState<
     float sk[8], zk[8], sv[8], zv[8];
   } cur{raw.kw, raw.vw, {}, {}, {}, {}};
   {
-    const float *km = &smf.meta[wave][0][32 * gq + 8 * cm];
-    const float *kz = &smf.meta[wave][1][32 * gq + 8 * cm];
-    const float *vm = &smf.meta[wave][2][(n >> 2) * G + 8 * gq];
-    const float *vz = &smf.meta[wave][3][(n >> 2) * G + 8 * gq];
+    const float *km = &smf.w[wave].g.meta[0][32 * gq + 8 * cm];
+    const float *kz = &smf.w[wave].g.meta[1][32 * gq + 8 * cm];
+    const float *vm = &smf.w[wave].g.meta[2][(n >> 2) * G + 8 * gq];
+    const float *vz = &smf.w[wave].g.meta[3][(n >> 2) * G + 8 * gq];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       cur.sk[i] = km[i]; cur.zk[i] = kz[i]; cur.sv[i] = vm[i]; cur.zv[i] = vz[i];
     }
   }
-  // ---- A operands (exact codes)
+  // ---- A operands (exact codes).  With one head block they are unpacked
+  // next to the MFMAs that read them (fewer live registers, and the
+  // converts issue while the matrix core works); otherwise once, up front.
+  constexpr bool kLazy = NHB == 1 && KIVI_LAZY_UNPACK;
   Op8 ak[2][4];
-#pragma unroll
-  for (int tile = 0; tile < 2; ++tile) {
-    if constexpr (BITS == 2) {
-      unpack2(cur.kw[tile][0], ak[tile][0], ak[tile][1]);
-      unpack2(cur.kw[tile][1], ak[tile][2], ak[tile][3]);
-    } else {
-#pragma unroll
-      for (int m = 0; m < 4; ++m) unpack4(cur.kw[tile][m], ak[tile][m]);
-    }
-  }
   Op8 av[8];
-  if constexpr (BITS == 2) {
+  auto unpack_k = [&](int tile, int m) {   // fills ak[tile][m] (and its pair)
+    if constexpr (BITS == 2) {
+      if ((m & 1) == 0) unpack2(cur.kw[tile][m / 2], ak[tile][m], ak[tile][m + 1]);
+    } else {
+      unpack4(cur.kw[tile][m], ak[tile][m]);
+    }
+  };
+  auto unpack_v = [&](int mt) {            // fills av[mt] (and its pair)
+    if constexpr (BITS == 2) {
+      if ((mt & 1) == 0) unpack2(cur.vw[mt / 2], av[mt], av[mt + 1]);
+    } else {
+      unpack4(cur.vw[mt], av[mt]);
+    }
+  };
+  if constexpr (!kLazy) {
 #pragma unroll
-    for (int d = 0; d < 4; ++d) unpack2(cur.vw[d], av[2 * d], av[2 * d + 1]);
-  } else {
+    for (int m = 0; m < 4; ++m) {
+      unpack_k(0, m);
+      unpack_k(1, m);
+    }
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) unpack4(cur.vw[mt], av[mt]);
+    for (int mt = 0; mt < 8; ++mt) unpack_v(mt);
   }
 
 #pragma unroll
@@ -600,8 +622,8 @@ __device__ __forceinline__ void mfma_group(const GroupRaw<BITS> &raw, WaveState<
         beta += qv[hb][s] * cur.zk[P8[s]];
         beta += qv[hb][s + 1] * cur.zk[P8[s + 1]];
       }
-      smf.bq[wave][hb][bq_index(0, ch, cm, gq)] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-      smf.bq[wave][hb][bq_index(1, ch, cm, gq)] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+      smf.w[wave].g.bq[hb][bq_index(0, ch, cm, gq)] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+      smf.w[wave].g.bq[hb][bq_index(1, ch, cm, gq)] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
     }
     // every lane with (lane & 3) == head gets beta[head]
     beta = sum_x32(sum_x16(sum_row_stride4(beta)));
@@ -615,8 +637,12 @@ __device__ __forceinline__ void mfma_group(const GroupRaw<BITS> &raw, WaveState<
     }
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
+      if constexpr (kLazy) {
+        unpack_k(0, m);
+        unpack_k(1, m);
+      }
       Op8 bq;
-      const uint4 x = smf.bq[wave][hb][bq_index((n >> 2) & 1, n & 3, m, gq)];
+      const uint4 x = smf.w[wave].g.bq[hb][bq_index((n >> 2) & 1, n & 3, m, gq)];
       bq.u[0] = x.x; bq.u[1] = x.y; bq.u[2] = x.z; bq.u[3] = x.w;
 #pragma unroll
       for (int tile = 0; tile < 2; ++tile)
@@ -658,6 +684,7 @@ __device__ __forceinline__ void mfma_group(const GroupRaw<BITS> &raw, WaveState<
                  bl.u[s / 2]);
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) {
+      if constexpr (kLazy) unpack_v(mt);
       st.acc[hb][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mt].v, bh.v, st.acc[hb][mt], 0, 0, 0);
       st.acc[hb][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mt].v, bl.v, st.acc[hb][mt], 0, 0, 0);
     }
@@ -669,9 +696,9 @@ __device__ __forceinline__ void mfma_group(const GroupRaw<BITS> &raw, WaveState<
 // operand and the raw query as B (hi columns; lo columns zero; the softmax
 // scale applied to the scores); P.V with the chunk's V rows transposed
 // through LDS as the A operand and p (hi/lo) as B for every channel block.
-template <int NHB>
+template <int NHB, int NW>
 __device__ __forceinline__ void mfma_rchunk(const DecodeArgs &a, int u, int rc,
-                                            WaveState<NHB> &st, MfmaSmem<NHB> &smf, int wave,
+                                            WaveState<NHB> &st, MfmaSmem<NHB, NW> &smf, int wave,
                                             int lane, int n, int gq) {
   const int qpk = a.qpk;
   const int t0 = G * rc, valid = min(G, a.n_res - t0);
@@ -688,7 +715,7 @@ __device__ __forceinline__ void mfma_rchunk(const DecodeArgs &a, int u, int rc,
   {
     const int row = lane >> 1, c0 = 64 * (lane & 1);
     const bool is_new = has_new && row == new_row;
-    uint4 *dst = reinterpret_cast<uint4 *>(&smf.vres[wave][row][c0]);
+    uint4 *dst = reinterpret_cast<uint4 *>(&smf.w[wave].vres[row][c0]);
     const uint4 *src = reinterpret_cast<const uint4 *>(
         is_new ? a.v_new + (long long)u * D + c0 : vrows + (long long)row * D + c0);
     uint4 x[8];
@@ -731,8 +758,8 @@ __device__ __forceinline__ void mfma_rchunk(const DecodeArgs &a, int u, int rc,
   for (int mt = 0; mt < 8; ++mt) {
 #pragma unroll
     for (int s2 = 0; s2 < 4; ++s2) {
-      const uint32_t lo = smf.vres[wave][8 * gq + 2 * s2][8 * n + mt];
-      const uint32_t hi = smf.vres[wave][8 * gq + 2 * s2 + 1][8 * n + mt];
+      const uint32_t lo = smf.w[wave].vres[8 * gq + 2 * s2][8 * n + mt];
+      const uint32_t hi = smf.w[wave].vres[8 * gq + 2 * s2 + 1][8 * n + mt];
       av[mt].u[s2] = lo | (hi << 16);
     }
   }
@@ -807,7 +834,7 @@ struct WorkRange {
 };
 
 __device__ __forceinline__ WorkRange wave_work(const DecodeArgs &a, int u, int split, int wave,
-                                               int cq, int cr) {
+                                               int nw, int cq, int cr) {
   const int n_rc = (a.n_res + G - 1) / G;
   const long long q0 = (long long)a.n_groups * cq, total = q0 + (long long)n_rc * cr;
   long long cum = 0, wsum = 0, wself = 0;
@@ -822,7 +849,7 @@ __device__ __forceinline__ WorkRange wave_work(const DecodeArgs &a, int u, int s
     wsum += w;
   }
   const long long wg_lo = total * cum / wsum, wg_hi = total * (cum + wself) / wsum;
-  const long long lo = wg_lo + (wg_hi - wg_lo) * wave / 4, hi = wg_lo + (wg_hi - wg_lo) * (wave + 1) / 4;
+  const long long lo = wg_lo + (wg_hi - wg_lo) * wave / nw, hi = wg_lo + (wg_hi - wg_lo) * (wave + 1) / nw;
   WorkRange r;
   r.g_begin = (int)min((lo + cq - 1) / cq, (long long)a.n_groups);
   r.g_end = (int)min((hi + cq - 1) / cq, (long long)a.n_groups);
@@ -833,16 +860,26 @@ __device__ __forceinline__ WorkRange wave_work(const DecodeArgs &a, int u, int s
 
 // GQA decode attention.  Grid (unit, wpu): the `wpu` workgroups of a unit
 // split its work -- the quantised groups, then the residual in chunks of 32
-// tokens -- into rank-weighted byte shares (wave_work), and each workgroup
-// splits its share over its 4 waves.  Item costs are in KiB: a group (codes
-// + scale/zero) is bits + 2, a residual chunk (32 bf16 K and V rows) is 16.
-template <int BITS, int NHB, int META, bool PAGED>
-__global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeArgs a) {
+// tokens -- into rank-weighted byte shares (wave_work).  Item costs are in
+// KiB: a group (codes + scale/zero) is bits + 2, a residual chunk (32 bf16
+// K and V rows) is 16.  NW == 4: each workgroup splits its share over its
+// waves statically.  NW > 4 (one workgroup per compute unit): the waves take
+// the share's groups one at a time from an LDS counter, so waves that the
+// hardware issues less often take fewer groups and all finish together; the
+// grouping of the online-softmax sums then depends on timing, so results may
+// differ between launches in the last bits.
+template <int BITS, int NHB, int META, bool PAGED, int NW>
+__global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeArgs a) {
   constexpr int HMAX = 4 * NHB;
   __shared__ __align__(16) union {
-    MfmaSmem<NHB> mf;
-    MergeSmem<HMAX> mg;
+    MfmaSmem<NHB, NW> mf;
+    MergeSmem<HMAX, NW> mg;
   } sm;
+  // NW > 4: the workgroup's groups are handed out to its waves one at a
+  // time from this counter (the first kPrefetch + 1 of each wave fixed)
+  constexpr bool kDyn = NW > 4;
+  constexpr int C = kPrefetch + 1;
+  __shared__ int s_next;
 
   const int u = blockIdx.x, split = blockIdx.y;
   const int4 next_state = a.state_in ? apply_unit_state(a, u) : make_int4(0, 0, 0, 0);
@@ -854,8 +891,14 @@ __global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeArgs a) {
   const int b = u / a.kv_heads, h = u % a.kv_heads;
 
   // this wave's byte share of the unit, and the items that start inside it
-  const WorkRange wr = wave_work(a, u, split, wave, BITS + kMetaBytes<META> / 2, 16);
-  const int g_begin = wr.g_begin, g_end = wr.g_end, r_begin = wr.r_begin, r_end = wr.r_end;
+  // (kDyn: the workgroup's share; the waves take its groups dynamically and
+  // one residual chunk each)
+  const WorkRange wr = kDyn ? wave_work(a, u, split, 0, 1, BITS + kMetaBytes<META> / 2, 16)
+                            : wave_work(a, u, split, wave, NW, BITS + kMetaBytes<META> / 2, 16);
+  const int g_end = wr.g_end;
+  const int g_begin = kDyn ? wr.g_begin + wave * C : wr.g_begin;
+  const int r_begin = kDyn ? wr.r_begin + wave : wr.r_begin;
+  const int r_end = kDyn ? min(r_begin + 1, wr.r_end) : wr.r_end;
 
   // Order of the first loads: the query (needed first), then the first two
   // groups, so that waiting for the query does not wait for the groups.
@@ -903,6 +946,31 @@ __global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeArgs a) {
     st.m_run[hb] = kNegInf; st.l_run[hb] = 0.f; st.z_run[hb] = 0.f;
   }
 
+  if constexpr (kDyn) {
+    if (threadIdx.x == 0) s_next = wr.g_begin + NW * C;
+    __syncthreads();
+    // gk[k]: the group in register set k; the wave's groups are its fixed
+    // ones, then one claimed per step, claimed a step before it is loaded
+    int gk[C];
+#pragma unroll
+    for (int k = 0; k < C; ++k) gk[k] = g_begin + k;
+    int to_load = g_begin + kPrefetch;   // loaded at the next step
+    int claim = 0;
+    if (lane == 0) claim = __hip_atomic_fetch_add(&s_next, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    while (gk[0] < g_end) {
+#pragma unroll
+      for (int k = 0; k <= kPrefetch; ++k) {
+        const int slot = (k + kPrefetch) % (kPrefetch + 1);
+        gk[slot] = to_load;
+        load_group<BITS, META, PAGED>(r[slot], view, a, u, to_load, to_load < g_end);
+        to_load = __builtin_amdgcn_readfirstlane(claim);
+        if (lane == 0)
+          claim = __hip_atomic_fetch_add(&s_next, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if (gk[k] < g_end)
+          mfma_group<BITS, NHB, META, NW>(r[k], st, sm.mf, qv, wave, n, gq, ch, cm);
+      }
+    }
+  } else {
   // quantised groups: software pipeline over kPrefetch + 1 register sets
   // (unrolled, so the sets rotate without copies), the next kPrefetch groups
   // in flight while the current one is computed
@@ -915,11 +983,12 @@ __global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeArgs a) {
       const int g = g0 + k;
       load_group<BITS, META, PAGED>(r[(k + kPrefetch) % (kPrefetch + 1)], view, a, u,
                                     g + kPrefetch, g + kPrefetch < g_end);
-      if (g < g_end) mfma_group<BITS, NHB, META>(r[k], st, sm.mf, qv, wave, n, gq, ch, cm);
+      if (g < g_end) mfma_group<BITS, NHB, META, NW>(r[k], st, sm.mf, qv, wave, n, gq, ch, cm);
     }
   }
+  }
   // residual chunks
-  for (int rc = r_begin; rc < r_end; ++rc) mfma_rchunk<NHB>(a, u, rc, st, sm.mf, wave, lane, n, gq);
+  for (int rc = r_begin; rc < r_end; ++rc) mfma_rchunk<NHB, NW>(a, u, rc, st, sm.mf, wave, lane, n, gq);
 
   // ---- per-wave totals, then the workgroup merge (the merge buffer aliases
   // the staging areas of the other waves: wait until every wave is done)
@@ -947,7 +1016,7 @@ __global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeArgs a) {
       sm.mg.l[wave][hb * 4 + n] = l;
     }
   }
-  merge_and_store<HMAX>(sm.mg, a, u, split);
+  merge_and_store<HMAX, NW>(sm.mg, a, u, split);
   finish_unit(a, u, &sm.mg.last, next_state);
 }
 
@@ -1231,7 +1300,7 @@ template <int BITS, int META, bool PAGED>
 __global__ __launch_bounds__(256) void decode_mha_kernel(DecodeArgs a) {
   __shared__ __align__(16) union {
     ValuSmem vs;
-    MergeSmem<1> mg;
+    MergeSmem<1, 4> mg;
   } sm;
   const int u = blockIdx.x, split = blockIdx.y;
   const int4 next_state = a.state_in ? apply_unit_state(a, u) : make_int4(0, 0, 0, 0);
@@ -1240,7 +1309,7 @@ __global__ __launch_bounds__(256) void decode_mha_kernel(DecodeArgs a) {
   L.lane = threadIdx.x & 63;
   L.tb = L.lane >> 3; L.cb = L.lane & 7;
   L.oc = L.lane >> 4; L.cq = L.lane & 15;
-  const WorkRange wr = wave_work(a, u, split, L.wave, BITS + kMetaBytes<META> / 2, 16);
+  const WorkRange wr = wave_work(a, u, split, L.wave, 4, BITS + kMetaBytes<META> / 2, 16);
 
   // the query first, then the first two groups (see decode_gqa_kernel)
   const uint4 *qp = reinterpret_cast<const uint4 *>(a.q + (long long)u * D + 16 * L.cb);
@@ -1295,7 +1364,7 @@ __global__ __launch_bounds__(256) void decode_mha_kernel(DecodeArgs a) {
     sm.mg.m[L.wave][0] = st.m_run;
     sm.mg.l[L.wave][0] = l;
   }
-  merge_and_store<1>(sm.mg, a, u, split);
+  merge_and_store<1, 4>(sm.mg, a, u, split);
   finish_unit(a, u, &sm.mg.last, next_state);
 }
 
@@ -1305,14 +1374,29 @@ namespace {
 
 // Kernel variants: 0 = MHA (VALU), 1..4 = GQA with that many blocks of 4
 // query heads; for each bit width and scale/zero format.
+// Waves per workgroup of each kernel variant (the MHA kernel and the GQA
+// kernels of 5+ query heads per kv head use 4).
+// Kernel variants: 0 MHA; 1-4 GQA with 4, 8, 12 or 16 query heads per block
+// of kv head (4 waves per workgroup, static shares); 5 GQA up to 4 heads,
+// one large workgroup per compute unit whose waves take groups dynamically
+// (12 waves at 2-bit, 8 at 4-bit: three or two per SIMD by registers).
+constexpr int kDynVariant = 5;
+template <int BITS>
+constexpr int kDynWaves = BITS == 2 ? 12 : 8;
+int variant_waves(int bits, int variant) {
+  if (variant != kDynVariant) return 4;
+  return bits == 2 ? kDynWaves<2> : kDynWaves<4>;
+}
+
 template <int BITS, int META, bool PAGED>
 void *kernel_fn_t(int variant) {
   switch (variant) {
     case 0: return (void *)&decode_mha_kernel<BITS, META, PAGED>;
-    case 1: return (void *)&decode_gqa_kernel<BITS, 1, META, PAGED>;
-    case 2: return (void *)&decode_gqa_kernel<BITS, 2, META, PAGED>;
-    case 3: return (void *)&decode_gqa_kernel<BITS, 3, META, PAGED>;
-    default: return (void *)&decode_gqa_kernel<BITS, 4, META, PAGED>;
+    case 1: return (void *)&decode_gqa_kernel<BITS, 1, META, PAGED, 4>;
+    case kDynVariant: return (void *)&decode_gqa_kernel<BITS, 1, META, PAGED, kDynWaves<BITS>>;
+    case 2: return (void *)&decode_gqa_kernel<BITS, 2, META, PAGED, 4>;
+    case 3: return (void *)&decode_gqa_kernel<BITS, 3, META, PAGED, 4>;
+    default: return (void *)&decode_gqa_kernel<BITS, 4, META, PAGED, 4>;
   }
 }
 
@@ -1334,13 +1418,14 @@ struct Residency {
 };
 
 Residency residency(int bits, int meta, int variant, bool paged) {
-  static int cache[16][2][2][2][5][2];   // 0 = not yet queried
+  static int cache[16][2][2][2][6][2];   // 0 = not yet queried
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
   int *slot = cache[dev & 15][bits == 4 ? 1 : 0][meta == 1 ? 1 : 0][paged ? 1 : 0][variant];
   Residency r{__atomic_load_n(&slot[0], __ATOMIC_RELAXED), __atomic_load_n(&slot[1], __ATOMIC_RELAXED)};
   if (r.per_cu > 0 && r.cus > 0) return r;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&r.per_cu, kernel_fn(bits, meta, variant, paged), 256,
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&r.per_cu, kernel_fn(bits, meta, variant, paged),
+                                                   64 * variant_waves(bits, variant),
                                                    0) != hipSuccess ||
       r.per_cu < 1)
     r.per_cu = 1;
@@ -1407,9 +1492,20 @@ int choose_wpu(int group_cost, const DecodeArgs &a, int slots) {
 }  // namespace
 
 hipError_t launch_decode(int bits, int meta, const DecodeArgs &a_in, hipStream_t s) {
-  const int variant = a_in.qpk == 1 ? 0 : (a_in.qpk + 3) / 4;
+  int variant = a_in.qpk == 1 ? 0 : (a_in.qpk + 3) / 4;
   DecodeArgs a = a_in;
   const bool paged = a_in.pages.table != nullptr;
+  // Up to 4 query heads per kv head and at most one unit per compute unit:
+  // the launch is a single round, whose end the slowest wave sets, so the
+  // dynamic variant (one workgroup per compute unit, waves balanced by an
+  // LDS counter) is used.  Longer launches refill their slots as workgroups
+  // finish and keep the static variant.  KIVI_DYN=0/1 forces the choice.
+  if (variant == 1) {
+    const Residency rd = residency(bits, meta, kDynVariant, paged);
+    bool dyn = (long long)a_in.n_units <= (long long)rd.per_cu * rd.cus;
+    if (const char *env = getenv("KIVI_DYN")) dyn = atoi(env) != 0;
+    if (dyn) variant = kDynVariant;
+  }
   const Residency res = residency(bits, meta, variant, paged);
   const int slots = res.per_cu * res.cus;
   // KiB per group: codes (bits) + scale/zero (2 fp32 or 1 16-bit)
@@ -1422,7 +1518,7 @@ hipError_t launch_decode(int bits, int meta, const DecodeArgs &a_in, hipStream_t
   } else {
     for (int i = 0; i < 4; ++i) a.rank_w[i] = 1;
   }
-  const dim3 grid(a.n_units, a.n_split), block(256);
+  const dim3 grid(a.n_units, a.n_split), block(64 * variant_waves(bits, variant));
   hipLaunchKernelGGL(reinterpret_cast<void (*)(DecodeArgs)>(kernel_fn(bits, meta, variant, paged)), grid,
                      block, 0, s, a);
   return hipGetLastError();
