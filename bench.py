@@ -16,8 +16,9 @@ Workload (Llama-3-8B GQA geometry of the catalog record kivi-2bit-llama3-8b-gqa-
   calls (append, flush, attend) for comparison.  The 32 layer caches (4.5 GB)
   rotate, so the 256 MB MALL cannot serve them;
 * roofline of the dominant kernel (decode attention with the fused append,
-  one launch per layer): algorithmic bytes per launch / its duration from HIP
-  event pairs around each launch of 10 further decode steps, against 8 TB/s;
+  one launch per layer): algorithmic bytes per launch / its duration, from
+  one HIP event pair around a block of 10 further flush-free decode steps
+  (320 back-to-back launches), against 8 TB/s;
 * mixed-length leg (reported beside, not in, value): per-sequence counters
   in device memory -- paged copies of the caches (pages of 4 groups from a
   shuffled pool) through kivi_paged_decode_step at the lockstep length, then
@@ -483,9 +484,10 @@ def main():
     layers = args.layers or w.layers
     dev = torch.device("cuda", 0)
     D, G, R = w.head_dim, w.group, w.residual
-    kernel_steps = 10   # extra fused steps with HIP events around every launch
+    kernel_steps = 10   # flush-free fused steps timed as one block
     ragged_steps = args.steps + (args.steps & 1)
-    total_steps = args.warmup + (args.profile_steps or 2 * args.steps + kernel_steps + 1)
+    # timed steps, then up to R+G steps to a flush-free block, a lead-in and the block
+    total_steps = args.warmup + (args.profile_steps or 2 * args.steps + R + G + kernel_steps + 1)
     # the mixed-length leg continues the caches for 2 * (2 * steps + 4) more tokens
     cap_steps = total_steps + 2 * (2 * ragged_steps + RAGGED_EXTRA_STEPS)
     max_tokens = G * math.ceil((w.seq_len - R + cap_steps + G) / G)
@@ -568,43 +570,40 @@ def main():
     torch.cuda.synchronize()
     t_steps_sep = time.perf_counter() - t0
 
-    # kernel timing: more fused steps, with a HIP event pair around every
-    # layer's launch on the stream the library launches on; launches of steps
-    # that also flushed (two kernels) are left out of the average
-    i0 = args.warmup + 2 * n_timed + 1
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(layers)] for _ in range(kernel_steps)]
-    flushed = [[0] * layers for _ in range(kernel_steps)]
-    nbytes = [[0.0] * layers for _ in range(kernel_steps)]
-    torch.cuda.synchronize()
-    # one untimed step first, so that the GPU is busy while the host enqueues
-    # the timed launches (no launch waits for the host after its start event)
-    step(i0 - 1)
+    # kernel timing: a block of further fused steps in which no layer flushes
+    # (all layers flush on the same steps: their counters move in lockstep),
+    # between one HIP event pair on the stream the library launches on.  The
+    # launches run back to back as in the timed steps; the block's time over
+    # its launch count is the per-launch time.  A step flushes iff n_res + 1
+    # == R + G before it, so the block starts after the next flush if one
+    # would fall inside it.
+    slots = R + G
+    c0 = caches[0]
+    i = args.warmup + 2 * n_timed
+    while c0.n_res + kernel_steps + 1 >= slots:
+        step(i)
+        i += 1
+    n_q0 = c0.n_q
+    # after the lead-in step, timed step j attends over n_res + 2 + j tokens
+    kern_bytes = [attn_bytes(w, n_q0, c0.n_res + 2 + j, fused_append=True, meta_bytes=mbytes)
+                  for j in range(kernel_steps)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    step(i)           # lead-in: keeps the GPU busy while the block is enqueued
+    e0.record()
     for j in range(kernel_steps):
-        for layer in range(layers):
-            st = steppers[layer]
-            kn, vn = new_tok[i0 + j][layer]
-            e0, e1 = ev[j][layer]
-            e0.record()
-            flushed[j][layer] = st.step(kn, vn)
-            e1.record()
-            # the step attends over the cache after its append (and flush)
-            nbytes[j][layer] = attn_bytes(w, st.cache.n_q, st.cache.n_res, fused_append=True,
-                                          meta_bytes=mbytes)
+        step(i + 1 + j)
+    e1.record()
     torch.cuda.synchronize()
-    kern_us, kern_bytes = [], []
-    for j in range(kernel_steps):
-        for layer in range(layers):
-            if not flushed[j][layer]:
-                kern_us.append(ev[j][layer][0].elapsed_time(ev[j][layer][1]) * 1e3)
-                kern_bytes.append(nbytes[j][layer])
+    if any(c.n_q != n_q0 for c in caches):
+        raise RuntimeError("a layer flushed inside the kernel-timing block")
+    kern_us = [e0.elapsed_time(e1) * 1e3 / (kernel_steps * layers)]
     avg_kern_s = sum(kern_us) / len(kern_us) / 1e6
     avg_bytes = sum(kern_bytes) / len(kern_bytes)
     achieved = avg_bytes / avg_kern_s / 1e9
 
     ragged = None
     if not args.no_ragged:
-        tok = new_tok[i0]
+        tok = new_tok[0]
         ragged = ragged_leg(w, geom, caches, ws, qs, outs, tok, ragged_steps, args.seed, mbytes)
 
     ms_per_step = t_steps / n_timed * 1e3
@@ -624,7 +623,7 @@ def main():
         "attn_hbm_gbps": achieved,
         "attn_bytes_per_launch": avg_bytes,
         "attn_kernel_us": avg_kern_s * 1e6,
-        "attn_kernel_launches_timed": len(kern_us),
+        "attn_kernel_launches_timed": kernel_steps * layers,
         "attn_tokens_s_kernel_only": w.batch / (avg_kern_s * layers),
         "quantize_gelem_s": quant_gelem_s,
         "quantize_hbm_gbps": pre_gbps,
