@@ -117,8 +117,10 @@ __device__ __forceinline__ void split_bf16(float x0, float x1, uint32_t &hi, uin
 }
 
 __device__ __forceinline__ float dpp_ror4(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x124,
-                                                             0xF, 0xF, false));
+  // row_ror:4 reads every lane of the row, so bound_ctrl is moot; setting it
+  // lets the compiler fold the move into the add that consumes it
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x124,
+                                                                0xF, 0xF, true));
 }
 __device__ __forceinline__ float xor_max(float x, int m) { return fmaxf(x, __shfl_xor(x, m)); }
 __device__ __forceinline__ float xor_sum(float x, int m) { return x + __shfl_xor(x, m); }
@@ -300,8 +302,8 @@ __device__ __forceinline__ float max_x32(float x) {
 }
 // sum over the 4 lanes n, n+-4, n+-8, n+-12 of each 16-lane row (DPP rotations)
 __device__ __forceinline__ float sum_row_stride4(float x) {
-  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x124, 0xF, 0xF, false));
-  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x128, 0xF, 0xF, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x124, 0xF, 0xF, true));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xF, 0xF, true));
   return x;
 }
 
@@ -1381,8 +1383,11 @@ namespace {
 // one large workgroup per compute unit whose waves take groups dynamically
 // (12 waves at 2-bit, 8 at 4-bit: three or two per SIMD by registers).
 constexpr int kDynVariant = 5;
+#ifndef KIVI_DYN_WAVES2
+#define KIVI_DYN_WAVES2 12
+#endif
 template <int BITS>
-constexpr int kDynWaves = BITS == 2 ? 12 : 8;
+constexpr int kDynWaves = BITS == 2 ? KIVI_DYN_WAVES2 : 8;
 int variant_waves(int bits, int variant) {
   if (variant != kDynVariant) return 4;
   return bits == 2 ? kDynWaves<2> : kDynWaves<4>;
