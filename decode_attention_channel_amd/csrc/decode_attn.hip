@@ -446,12 +446,6 @@ __device__ __forceinline__ UnitView make_view(const DecodeArgs &a, int u, int n,
 // the group it computes and not for the prefetches behind it.
 constexpr uint32_t kOutOfRange = 0x80000000u;   // > any unit's buffer size
 
-// Unpack the codes of a group next to the MFMAs that read them (1) or all
-// at the start of the group (0).
-#ifndef KIVI_LAZY_UNPACK
-#define KIVI_LAZY_UNPACK 1
-#endif
-
 // Groups in flight per wave beyond the one being computed (MFMA path).
 #ifndef KIVI_PREFETCH
 #define KIVI_PREFETCH 2
@@ -584,7 +578,7 @@ __device__ __forceinline__ void mfma_group(const GroupRaw<BITS> &raw, WaveState<
   // ---- A operands (exact codes).  With one head block they are unpacked
   // next to the MFMAs that read them (fewer live registers, and the
   // converts issue while the matrix core works); otherwise once, up front.
-  constexpr bool kLazy = NHB == 1 && KIVI_LAZY_UNPACK;
+  constexpr bool kLazy = NHB == 1;
   Op8 ak[2][4];
   Op8 av[8];
   auto unpack_k = [&](int tile, int m) {   // fills ak[tile][m] (and its pair)
@@ -1383,11 +1377,8 @@ namespace {
 // one large workgroup per compute unit whose waves take groups dynamically
 // (12 waves at 2-bit, 8 at 4-bit: three or two per SIMD by registers).
 constexpr int kDynVariant = 5;
-#ifndef KIVI_DYN_WAVES2
-#define KIVI_DYN_WAVES2 12
-#endif
 template <int BITS>
-constexpr int kDynWaves = BITS == 2 ? KIVI_DYN_WAVES2 : 8;
+constexpr int kDynWaves = BITS == 2 ? 12 : 8;
 int variant_waves(int bits, int variant) {
   if (variant != kDynVariant) return 4;
   return bits == 2 ? kDynWaves<2> : kDynWaves<4>;
