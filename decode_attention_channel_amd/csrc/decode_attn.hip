@@ -109,11 +109,13 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   bf16x2_t v = {(__bf16)a, (__bf16)b};
   return __builtin_bit_cast(uint32_t, v);
 }
-// x ~= hi + lo with hi = bf16(x), lo = bf16(x - hi): two packed words for a pair
+// x ~= hi + lo with hi = x truncated to bf16 (its upper 16 bits) and
+// lo = bf16(x - hi), x - hi being exact in fp32: two packed words for a pair,
+// |x - hi - lo| <= 2^-16 |x|
 __device__ __forceinline__ void split_bf16(float x0, float x1, uint32_t &hi, uint32_t &lo) {
-  hi = pack_bf16x2(x0, x1);
-  const float h0 = __uint_as_float(hi << 16), h1 = __uint_as_float(hi & 0xFFFF0000u);
-  lo = pack_bf16x2(x0 - h0, x1 - h1);
+  const uint32_t b0 = __float_as_uint(x0), b1 = __float_as_uint(x1);
+  hi = __builtin_amdgcn_perm(b1, b0, 0x07060302u);   // upper halves of x0 (low word), x1
+  lo = pack_bf16x2(x0 - __uint_as_float(b0 & 0xFFFF0000u), x1 - __uint_as_float(b1 & 0xFFFF0000u));
 }
 
 __device__ __forceinline__ float dpp_ror4(float x) {
@@ -292,13 +294,16 @@ __device__ __forceinline__ float sum_x32(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
+// IEEE maximum (NaN-propagating): one v_maximum3_f32, where fmaxf on
+// values from a lane exchange would first quiet both operands
+__device__ __forceinline__ float max2(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 __device__ __forceinline__ float max_x16(float x) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return max2(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float max_x32(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return max2(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 // sum over the 4 lanes n, n+-4, n+-8, n+-12 of each 16-lane row (DPP rotations)
 __device__ __forceinline__ float sum_row_stride4(float x) {
@@ -445,12 +450,16 @@ __device__ __forceinline__ UnitView make_view(const DecodeArgs &a, int u, int n,
 // compiler's count of outstanding loads exact, so each step waits only for
 // the group it computes and not for the prefetches behind it.
 constexpr uint32_t kOutOfRange = 0x80000000u;   // > any unit's buffer size
+// cache policy of the history loads: non-temporal (each byte is read once per
+// step), which keeps them from displacing other lines in the caches
+constexpr int kStream = 2;
 
 // Groups in flight per wave beyond the one being computed (MFMA path).
 #ifndef KIVI_PREFETCH
 #define KIVI_PREFETCH 2
 #endif
 constexpr int kPrefetch = KIVI_PREFETCH;
+
 
 template <int BITS, int META, bool PAGED>
 __device__ __forceinline__ void load_group(GroupRaw<BITS> &r, const UnitView &v,
@@ -460,18 +469,18 @@ __device__ __forceinline__ void load_group(GroupRaw<BITS> &r, const UnitView &v,
   const uint32_t ob = live ? 0u : kOutOfRange;
   const uint32_t o_k0 = v.o_k0 + ob, o_k1 = v.o_k1 + ob, o_v = v.o_v + ob, o_mu = v.o_mu + ob;
   if constexpr (BITS == 2) {
-    const u32x2_t a = __builtin_amdgcn_raw_buffer_load_b64(v.kc, o_k0, sc, 0);
-    const u32x2_t b = __builtin_amdgcn_raw_buffer_load_b64(v.kc, o_k1, sc, 0);
+    const u32x2_t a = __builtin_amdgcn_raw_buffer_load_b64(v.kc, o_k0, sc, kStream);
+    const u32x2_t b = __builtin_amdgcn_raw_buffer_load_b64(v.kc, o_k1, sc, kStream);
     r.kw[0][0] = a[0]; r.kw[0][1] = a[1];
     r.kw[1][0] = b[0]; r.kw[1][1] = b[1];
-    const u32x4_t c = __builtin_amdgcn_raw_buffer_load_b128(v.vc, o_v, sc, 0);
+    const u32x4_t c = __builtin_amdgcn_raw_buffer_load_b128(v.vc, o_v, sc, kStream);
 #pragma unroll
     for (int i = 0; i < 4; ++i) r.vw[i] = c[i];
   } else {
-    const u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(v.kc, o_k0, sc, 0);
-    const u32x4_t b = __builtin_amdgcn_raw_buffer_load_b128(v.kc, o_k1, sc, 0);
-    const u32x4_t c = __builtin_amdgcn_raw_buffer_load_b128(v.vc, o_v, sc, 0);
-    const u32x4_t d = __builtin_amdgcn_raw_buffer_load_b128(v.vc, o_v + 16, sc, 0);
+    const u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(v.kc, o_k0, sc, kStream);
+    const u32x4_t b = __builtin_amdgcn_raw_buffer_load_b128(v.kc, o_k1, sc, kStream);
+    const u32x4_t c = __builtin_amdgcn_raw_buffer_load_b128(v.vc, o_v, sc, kStream);
+    const u32x4_t d = __builtin_amdgcn_raw_buffer_load_b128(v.vc, o_v + 16, sc, kStream);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       r.kw[0][i] = a[i]; r.kw[1][i] = b[i];
@@ -485,10 +494,10 @@ __device__ __forceinline__ void load_group(GroupRaw<BITS> &r, const UnitView &v,
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     if constexpr (META == 1) {
-      r.mw[i][0] = __builtin_amdgcn_raw_buffer_load_b32(mr[i], o_mu, sm, 0);
+      r.mw[i][0] = __builtin_amdgcn_raw_buffer_load_b32(mr[i], o_mu, sm, kStream);
       r.mw[i][1] = 0;
     } else {
-      const u32x2_t x = __builtin_amdgcn_raw_buffer_load_b64(mr[i], o_mu, sm, 0);
+      const u32x2_t x = __builtin_amdgcn_raw_buffer_load_b64(mr[i], o_mu, sm, kStream);
       r.mw[i][0] = x[0];
       r.mw[i][1] = x[1];
     }
@@ -521,14 +530,16 @@ __device__ __forceinline__ void stage_meta(const uint32_t (&mw)[4][2], float (*m
   }
 }
 
-// Per-wave LDS staging.  A wave works on quantised groups (bq, meta) and,
-// after them, on residual chunks (vres), so the two share storage.
+// Per-wave LDS staging.  A wave works on quantised groups and, after them,
+// on residual chunks (vres), so the two share storage.  The groups use two
+// buffer sets: while a group is computed from one set, the next group's
+// scale/zero and q' operand are staged in the other.
 template <int NHB>
 union WaveSmem {
   struct {
     uint4 bq[NHB][128];    // q' operand chunks (8 bf16) per head block, indexed by bq_index
-    float meta[4][D];      // the current group's k_scale, k_zero, v_scale, v_zero
-  } g;
+    float meta[4][D];      // the group's k_scale, k_zero, v_scale, v_zero
+  } g[2];
   uint16_t vres[G][D];     // one residual chunk of V rows (bf16)
 };
 template <int NHB, int NW>
@@ -551,30 +562,60 @@ template <int NHB>
 struct WaveState {
   f32x4_t acc[NHB][8];
   float m_run[NHB], l_run[NHB], z_run[NHB];
+  // finite reference the quantised groups' scores are taken relative to
+  // (their MFMA accumulators start at beta - m_ref): m_run once it is
+  // finite, 0 before
+  float m_ref[NHB];
 };
 
-template <int BITS, int NHB, int META, int NW>
-__device__ __forceinline__ void mfma_group(const GroupRaw<BITS> &raw, WaveState<NHB> &st,
-                                           MfmaSmem<NHB, NW> &smf, const float (&qv)[NHB][8],
-                                           int wave, int n, int gq, int ch, int cm) {
-  // scale/zero of this group: stage in LDS, read back what each role needs
-  stage_meta<META>(raw.mw, smf.w[wave].g.meta, 16 * gq + n);
+// First half of a group: stage its scale/zero in buffer set `buf`, build the
+// q' = q * s^K operand (hi/lo) of every head block there, and return
+// beta = q . z^K per head block (lane with (lane & 3) == head holds it).
+// A group past the end has all-zero loads: its q' and beta are zeros and the
+// buffer set is not read.
+template <int NHB, int META, int NW>
+__device__ __forceinline__ void prep_group(const uint32_t (&mw)[4][2], MfmaSmem<NHB, NW> &smf,
+                                           int buf, const float (&qv)[NHB][8], float (&beta)[NHB],
+                                           int wave, int lane, int gq, int ch, int cm) {
+  auto &gs = smf.w[wave].g[buf];
+  stage_meta<META>(mw, gs.meta, lane);
   __builtin_amdgcn_wave_barrier();
-  struct {
-    const uint32_t (&kw)[2][BITS];
-    const uint32_t (&vw)[2 * BITS];
-    float sk[8], zk[8], sv[8], zv[8];
-  } cur{raw.kw, raw.vw, {}, {}, {}, {}};
+  float sk[8], zk[8];
   {
-    const float *km = &smf.w[wave].g.meta[0][32 * gq + 8 * cm];
-    const float *kz = &smf.w[wave].g.meta[1][32 * gq + 8 * cm];
-    const float *vm = &smf.w[wave].g.meta[2][(n >> 2) * G + 8 * gq];
-    const float *vz = &smf.w[wave].g.meta[3][(n >> 2) * G + 8 * gq];
+    const float *km = &gs.meta[0][32 * gq + 8 * cm];
+    const float *kz = &gs.meta[1][32 * gq + 8 * cm];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      cur.sk[i] = km[i]; cur.zk[i] = kz[i]; cur.sv[i] = vm[i]; cur.zv[i] = vz[i];
+      sk[i] = km[i]; zk[i] = kz[i];
     }
   }
+#pragma unroll
+  for (int hb = 0; hb < NHB; ++hb) {
+    float bt = 0.f;
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int s = 0; s < 8; s += 2) {
+      split_bf16(qv[hb][s] * sk[P8[s]], qv[hb][s + 1] * sk[P8[s + 1]], hi[s / 2], lo[s / 2]);
+      bt += qv[hb][s] * zk[P8[s]];
+      bt += qv[hb][s + 1] * zk[P8[s + 1]];
+    }
+    gs.bq[hb][bq_index(0, ch, cm, gq)] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+    gs.bq[hb][bq_index(1, ch, cm, gq)] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    // every lane with (lane & 3) == head gets beta[head]
+    beta[hb] = sum_x32(sum_x16(sum_row_stride4(bt)));
+  }
+}
+
+// Second half of a group, from buffer set `buf` (filled by prep_group): the
+// scores on the MFMA, the online softmax and P.V.  `mid` runs once, after the
+// first head block's score MFMAs are issued: the next group's prep_group goes
+// there, so that its VALU and LDS work overlaps the matrix core.
+template <int BITS, int NHB, int NW, class Mid>
+__device__ __forceinline__ void attend_group(const GroupRaw<BITS> &raw, WaveState<NHB> &st,
+                                             MfmaSmem<NHB, NW> &smf, int buf,
+                                             const float (&beta)[NHB], int wave, int n, int gq,
+                                             Mid &&mid) {
+  auto &gs = smf.w[wave].g[buf];
   // ---- A operands (exact codes).  With one head block they are unpacked
   // next to the MFMAs that read them (fewer live registers, and the
   // converts issue while the matrix core works); otherwise once, up front.
@@ -583,16 +624,16 @@ __device__ __forceinline__ void mfma_group(const GroupRaw<BITS> &raw, WaveState<
   Op8 av[8];
   auto unpack_k = [&](int tile, int m) {   // fills ak[tile][m] (and its pair)
     if constexpr (BITS == 2) {
-      if ((m & 1) == 0) unpack2(cur.kw[tile][m / 2], ak[tile][m], ak[tile][m + 1]);
+      if ((m & 1) == 0) unpack2(raw.kw[tile][m / 2], ak[tile][m], ak[tile][m + 1]);
     } else {
-      unpack4(cur.kw[tile][m], ak[tile][m]);
+      unpack4(raw.kw[tile][m], ak[tile][m]);
     }
   };
   auto unpack_v = [&](int mt) {            // fills av[mt] (and its pair)
     if constexpr (BITS == 2) {
-      if ((mt & 1) == 0) unpack2(cur.vw[mt / 2], av[mt], av[mt + 1]);
+      if ((mt & 1) == 0) unpack2(raw.vw[mt / 2], av[mt], av[mt + 1]);
     } else {
-      unpack4(cur.vw[mt], av[mt]);
+      unpack4(raw.vw[mt], av[mt]);
     }
   };
   if constexpr (!kLazy) {
@@ -607,28 +648,12 @@ __device__ __forceinline__ void mfma_group(const GroupRaw<BITS> &raw, WaveState<
 
 #pragma unroll
   for (int hb = 0; hb < NHB; ++hb) {
-    // ---- cooperative q' = q * s^K (hi/lo) and beta = q . z^K
-    float beta = 0.f;
-    {
-      uint32_t hi[4], lo[4];
-#pragma unroll
-      for (int s = 0; s < 8; s += 2) {
-        split_bf16(qv[hb][s] * cur.sk[P8[s]], qv[hb][s + 1] * cur.sk[P8[s + 1]], hi[s / 2],
-                   lo[s / 2]);
-        beta += qv[hb][s] * cur.zk[P8[s]];
-        beta += qv[hb][s + 1] * cur.zk[P8[s + 1]];
-      }
-      smf.w[wave].g.bq[hb][bq_index(0, ch, cm, gq)] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-      smf.w[wave].g.bq[hb][bq_index(1, ch, cm, gq)] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-    }
-    // every lane with (lane & 3) == head gets beta[head]
-    beta = sum_x32(sum_x16(sum_row_stride4(beta)));
-    __builtin_amdgcn_wave_barrier();
-
     // ---- scores: columns n = 4x + head, x in {hi, lo, hi, lo}
-    f32x4_t sc[2] = {f32x4_t{beta, beta, beta, beta}, f32x4_t{beta, beta, beta, beta}};
-    if (n & 4) {   // lo columns: beta enters once, through the hi column
-      sc[0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // scores relative to m_ref: beta - m_ref enters through the hi columns
+    f32x4_t sc[2];
+    {
+      const float bt = (n & 4) ? 0.f : beta[hb] - st.m_ref[hb];
+      sc[0] = f32x4_t{bt, bt, bt, bt};
       sc[1] = sc[0];
     }
 #pragma unroll
@@ -638,11 +663,22 @@ __device__ __forceinline__ void mfma_group(const GroupRaw<BITS> &raw, WaveState<
         unpack_k(1, m);
       }
       Op8 bq;
-      const uint4 x = smf.w[wave].g.bq[hb][bq_index((n >> 2) & 1, n & 3, m, gq)];
+      const uint4 x = gs.bq[hb][bq_index((n >> 2) & 1, n & 3, m, gq)];
       bq.u[0] = x.x; bq.u[1] = x.y; bq.u[2] = x.z; bq.u[3] = x.w;
 #pragma unroll
       for (int tile = 0; tile < 2; ++tile)
         sc[tile] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak[tile][m].v, bq.v, sc[tile], 0, 0, 0);
+    }
+    if (hb == 0) mid();
+    // this lane's V scale/zero: channel block n >> 2, tokens 8gq .. 8gq + 7
+    float sv[8], zv[8];
+    {
+      const float *vm = &gs.meta[2][(n >> 2) * G + 8 * gq];
+      const float *vz = &gs.meta[3][(n >> 2) * G + 8 * gq];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        sv[i] = vm[i]; zv[i] = vz[i];
+      }
     }
     // token 8gq + 4*tile + r  <->  p index 4*tile + r
     float s8[8];
@@ -651,33 +687,37 @@ __device__ __forceinline__ void mfma_group(const GroupRaw<BITS> &raw, WaveState<
 #pragma unroll
       for (int r = 0; r < 4; ++r) s8[4 * tile + r] = sc[tile][r] + dpp_ror4(sc[tile][r]);
 
-    // ---- online softmax (log2 domain), lazily rescaled
+    // ---- online softmax (log2 domain), lazily rescaled; s8 is relative to
+    // m_ref, which equals m_run except before the first rescale
     float mx = fmaxf(fmaxf(fmaxf(s8[0], s8[1]), fmaxf(s8[2], s8[3])),
                      fmaxf(fmaxf(s8[4], s8[5]), fmaxf(s8[6], s8[7])));
     mx = max_x32(max_x16(mx));
-    const bool need = mx > st.m_run[hb] + kRescaleSlack;
+    const bool need = mx > st.m_run[hb] - st.m_ref[hb] + kRescaleSlack;
     if (__any(need)) {
-      const float mnew = need ? mx : st.m_run[hb];
+      const float mnew = need ? mx + st.m_ref[hb] : st.m_run[hb];
       const float al = st.m_run[hb] == kNegInf ? 0.f : fast_exp2(st.m_run[hb] - mnew);
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) st.acc[hb][mt] *= al;
       st.l_run[hb] *= al;
       st.z_run[hb] *= al;
+      const float d = mnew - st.m_ref[hb];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) s8[k] -= d;
       st.m_run[hb] = mnew;
+      st.m_ref[hb] = mnew;
     }
     float p[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      p[k] = fast_exp2(s8[k] - st.m_run[hb]);
+      p[k] = fast_exp2(s8[k]);
       st.l_run[hb] += p[k];
-      st.z_run[hb] += p[k] * cur.zv[k];
+      st.z_run[hb] += p[k] * zv[k];
     }
     // ---- P.V: columns n = 4j + head; B slot s <-> token 8gq + P8[s]
     Op8 bh, bl;
 #pragma unroll
     for (int s = 0; s < 8; s += 2)
-      split_bf16(p[P8[s]] * cur.sv[P8[s]], p[P8[s + 1]] * cur.sv[P8[s + 1]], bh.u[s / 2],
-                 bl.u[s / 2]);
+      split_bf16(p[P8[s]] * sv[P8[s]], p[P8[s + 1]] * sv[P8[s + 1]], bh.u[s / 2], bl.u[s / 2]);
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) {
       if constexpr (kLazy) unpack_v(mt);
@@ -796,6 +836,7 @@ __device__ __forceinline__ void mfma_rchunk(const DecodeArgs &a, int u, int rc,
       st.l_run[hb] *= al;
       st.z_run[hb] *= al;
       st.m_run[hb] = mnew;
+      st.m_ref[hb] = mnew;
     }
     float p[8];
 #pragma unroll
@@ -907,6 +948,13 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeArgs a) {
       qraw[hb] = *reinterpret_cast<const uint4 *>(
           a.q + ((long long)b * a.kv_heads * qpk + (long long)h * qpk + hh) * D + 32 * gq + 8 * cm);
   }
+  WaveState<NHB> st;
+#pragma unroll
+  for (int hb = 0; hb < NHB; ++hb) {
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) st.acc[hb][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    st.m_run[hb] = kNegInf; st.l_run[hb] = 0.f; st.z_run[hb] = 0.f; st.m_ref[hb] = 0.f;
+  }
   const bool has_groups = g_begin < g_end;
   const UnitView view = make_view<BITS, META, PAGED>(a, u, n, gq, cm);
   // register sets of the load pipeline: kPrefetch groups in flight
@@ -934,14 +982,11 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeArgs a) {
     for (int s = 0; s < 8; ++s) qv[hb][s] = x[P8[s]] * a.qscale;
   }
 
-  WaveState<NHB> st;
-#pragma unroll
-  for (int hb = 0; hb < NHB; ++hb) {
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt) st.acc[hb][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    st.m_run[hb] = kNegInf; st.l_run[hb] = 0.f; st.z_run[hb] = 0.f;
-  }
 
+  // q' and beta of the group in flight between prep_group and attend_group,
+  // and the buffer set it occupies
+  float beta[NHB];
+  int buf = 0;
   if constexpr (kDyn) {
     if (threadIdx.x == 0) s_next = wr.g_begin + NW * C;
     __syncthreads();
@@ -953,6 +998,9 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeArgs a) {
     int to_load = g_begin + kPrefetch;   // loaded at the next step
     int claim = 0;
     if (lane == 0) claim = __hip_atomic_fetch_add(&s_next, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    // the first group's prep; each step then preps the wave's next group
+    // (in register set k + 1) while it attends to the current one
+    prep_group<NHB, META, NW>(r[0].mw, sm.mf, 0, qv, beta, wave, lane, gq, ch, cm);
     while (gk[0] < g_end) {
 #pragma unroll
       for (int k = 0; k <= kPrefetch; ++k) {
@@ -962,8 +1010,16 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeArgs a) {
         to_load = __builtin_amdgcn_readfirstlane(claim);
         if (lane == 0)
           claim = __hip_atomic_fetch_add(&s_next, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        if (gk[k] < g_end)
-          mfma_group<BITS, NHB, META, NW>(r[k], st, sm.mf, qv, wave, n, gq, ch, cm);
+        if (gk[k] < g_end) {
+          float bn[NHB];
+          attend_group<BITS, NHB, NW>(r[k], st, sm.mf, buf, beta, wave, n, gq, [&] {
+            prep_group<NHB, META, NW>(r[(k + 1) % (kPrefetch + 1)].mw, sm.mf, buf ^ 1, qv, bn,
+                                      wave, lane, gq, ch, cm);
+          });
+#pragma unroll
+          for (int hb = 0; hb < NHB; ++hb) beta[hb] = bn[hb];
+          buf ^= 1;
+        }
       }
     }
   } else {
@@ -973,13 +1029,23 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeArgs a) {
   // Every pass issues the loads of kPrefetch + 1 groups, so that the
   // outstanding loads at the loop head are the same from either edge; the
   // last pass skips the groups past the end (a wave-uniform branch).
+  prep_group<NHB, META, NW>(r[0].mw, sm.mf, 0, qv, beta, wave, lane, gq, ch, cm);
   for (int g0 = g_begin; g0 < g_end; g0 += kPrefetch + 1) {
 #pragma unroll
     for (int k = 0; k <= kPrefetch; ++k) {
       const int g = g0 + k;
       load_group<BITS, META, PAGED>(r[(k + kPrefetch) % (kPrefetch + 1)], view, a, u,
                                     g + kPrefetch, g + kPrefetch < g_end);
-      if (g < g_end) mfma_group<BITS, NHB, META, NW>(r[k], st, sm.mf, qv, wave, n, gq, ch, cm);
+      if (g < g_end) {
+        float bn[NHB];
+        attend_group<BITS, NHB, NW>(r[k], st, sm.mf, buf, beta, wave, n, gq, [&] {
+          prep_group<NHB, META, NW>(r[(k + 1) % (kPrefetch + 1)].mw, sm.mf, buf ^ 1, qv, bn,
+                                    wave, lane, gq, ch, cm);
+        });
+#pragma unroll
+        for (int hb = 0; hb < NHB; ++hb) beta[hb] = bn[hb];
+        buf ^= 1;
+      }
     }
   }
   }
@@ -1062,19 +1128,19 @@ __device__ __forceinline__ void load_valu_group(ValuRaw<BITS> &r, const ValuView
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     if constexpr (BITS == 2) {
-      r.kw[t][0] = __builtin_amdgcn_raw_buffer_load_b32(v.kc, o_k + t * KROW, sc, 0);
+      r.kw[t][0] = __builtin_amdgcn_raw_buffer_load_b32(v.kc, o_k + t * KROW, sc, kStream);
     } else {
-      const u32x2_t x = __builtin_amdgcn_raw_buffer_load_b64(v.kc, o_k + t * KROW, sc, 0);
+      const u32x2_t x = __builtin_amdgcn_raw_buffer_load_b64(v.kc, o_k + t * KROW, sc, kStream);
       r.kw[t][0] = x[0];
       r.kw[t][1] = x[1];
     }
   }
   {
-    const u32x4_t c = __builtin_amdgcn_raw_buffer_load_b128(v.vc, o_v, sc, 0);
+    const u32x4_t c = __builtin_amdgcn_raw_buffer_load_b128(v.vc, o_v, sc, kStream);
 #pragma unroll
     for (int i = 0; i < 4; ++i) r.vw[i] = c[i];
     if constexpr (BITS == 4) {
-      const u32x4_t d = __builtin_amdgcn_raw_buffer_load_b128(v.vc, o_v + 16, sc, 0);
+      const u32x4_t d = __builtin_amdgcn_raw_buffer_load_b128(v.vc, o_v + 16, sc, kStream);
 #pragma unroll
       for (int i = 0; i < 4; ++i) r.vw[4 + i] = d[i];
     }
@@ -1083,10 +1149,10 @@ __device__ __forceinline__ void load_valu_group(ValuRaw<BITS> &r, const ValuView
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     if constexpr (META == 1) {
-      r.mw[i][0] = __builtin_amdgcn_raw_buffer_load_b32(mr[i], o_mu, sm, 0);
+      r.mw[i][0] = __builtin_amdgcn_raw_buffer_load_b32(mr[i], o_mu, sm, kStream);
       r.mw[i][1] = 0;
     } else {
-      const u32x2_t x = __builtin_amdgcn_raw_buffer_load_b64(mr[i], o_mu, sm, 0);
+      const u32x2_t x = __builtin_amdgcn_raw_buffer_load_b64(mr[i], o_mu, sm, kStream);
       r.mw[i][0] = x[0];
       r.mw[i][1] = x[1];
     }
