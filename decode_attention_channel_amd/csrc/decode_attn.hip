@@ -346,13 +346,6 @@ struct GroupRaw {
   uint32_t mw[4][2];      // this lane's 8 bytes of each of k_scale, k_zero, v_scale, v_zero
 };
 
-// Per-unit buffer views and the lane-constant byte offsets of one lane; the
-// group enters only through scalar offsets (g * bytes per group).
-struct UnitView {
-  __amdgpu_buffer_rsrc_t kc, vc, ks, kz, vs, vz;
-  uint32_t o_k0, o_k1, o_v, o_mu;
-};
-
 // Bytes of one scale or zero value: fp32, or fp16 / bf16 (META == 1).
 template <int META>
 constexpr int kMetaBytes = META == 1 ? 2 : 4;
@@ -429,18 +422,25 @@ __device__ __forceinline__ void group_offsets(const DecodeArgs &a, int u, int g,
   sm = __builtin_amdgcn_readfirstlane((uint32_t)slot * (D * kMetaBytes<META>));
 }
 
+// Group records (q_per_kv >= 2, layout in kivi_internal.h): one buffer
+// resource over the unit's records (or the paged pool); lane l reads bytes
+// [16 l, 16 l + 16) of every plane, the group entering as a scalar offset.
+struct RecView {
+  __amdgpu_buffer_rsrc_t rec;
+  uint32_t o_lane;
+};
+
 template <int BITS, int META, bool PAGED>
-__device__ __forceinline__ UnitView make_view(const DecodeArgs &a, int u, int n, int gq, int cm) {
-  constexpr int KROW = D * BITS / 8;
-  constexpr int CB = 32 * BITS / 8;
-  UnitView v;
-  const HistBufs hb = hist_bufs<BITS, META, PAGED>(a, u);
-  v.kc = hb.kc; v.vc = hb.vc; v.ks = hb.ks; v.kz = hb.kz; v.vs = hb.vs; v.vz = hb.vz;
-  const int kr0 = 8 * (n >> 2) + (n & 3);   // A-operand row n of tile 0 -> token; tile 1: +4
-  v.o_k0 = kr0 * KROW + gq * CB;
-  v.o_k1 = (kr0 + 4) * KROW + gq * CB;
-  v.o_v = (gq * D + 8 * n) * BITS;
-  v.o_mu = (16 * gq + n) * 2 * kMetaBytes<META>;   // two values per lane
+__device__ __forceinline__ RecView make_rec_view(const DecodeArgs &a, int u, int lane) {
+  constexpr long long REC = rec_bytes(BITS, META);
+  RecView v;
+  if constexpr (PAGED) {
+    const long long groups = (long long)a.pages.num_pages * a.kv_heads << a.pages.shift;
+    v.rec = make_rsrc(a.k_codes, (uint32_t)(groups * REC));
+  } else {
+    v.rec = make_rsrc(a.k_codes + u * a.n_groups_cap * REC, (uint32_t)(a.n_groups_cap * REC));
+  }
+  v.o_lane = 16 * lane;
   return v;
 }
 
@@ -462,44 +462,52 @@ constexpr int kPrefetch = KIVI_PREFETCH;
 
 
 template <int BITS, int META, bool PAGED>
-__device__ __forceinline__ void load_group(GroupRaw<BITS> &r, const UnitView &v,
+__device__ __forceinline__ void load_group(GroupRaw<BITS> &r, const RecView &v,
                                            const DecodeArgs &a, int u, int g, bool live) {
-  uint32_t sc, sm;
-  group_offsets<BITS, META, PAGED>(a, u, g, live, sc, sm);
-  const uint32_t ob = live ? 0u : kOutOfRange;
-  const uint32_t o_k0 = v.o_k0 + ob, o_k1 = v.o_k1 + ob, o_v = v.o_v + ob, o_mu = v.o_mu + ob;
-  if constexpr (BITS == 2) {
-    const u32x2_t a = __builtin_amdgcn_raw_buffer_load_b64(v.kc, o_k0, sc, kStream);
-    const u32x2_t b = __builtin_amdgcn_raw_buffer_load_b64(v.kc, o_k1, sc, kStream);
-    r.kw[0][0] = a[0]; r.kw[0][1] = a[1];
-    r.kw[1][0] = b[0]; r.kw[1][1] = b[1];
-    const u32x4_t c = __builtin_amdgcn_raw_buffer_load_b128(v.vc, o_v, sc, kStream);
+  constexpr int NP = rec_planes(BITS, META);
+  long long slot = g;   // contiguous: the view starts at the unit's records
+  if constexpr (PAGED) {
+    slot = -1;
+    const int pi = g >> a.pages.shift;
+    if (live && pi < a.pages.max_pages) {
+      const int b = u / a.kv_heads, h = u - b * a.kv_heads;
+      const int e = page_entry(a.pages.table, (long long)b * a.pages.max_pages + pi);
+      if (e >= 0 && e < a.pages.num_pages)
+        slot = (((long long)e * a.kv_heads + h) << a.pages.shift) + (g & ((1 << a.pages.shift) - 1));
+    }
+    live = slot >= 0;
+    if (!live) slot = 0;
+  }
+  // wave-uniform: a scalar buffer offset
+  const uint32_t sc = __builtin_amdgcn_readfirstlane((uint32_t)slot * (uint32_t)rec_bytes(BITS, META));
+  const uint32_t o = v.o_lane + (live ? 0u : kOutOfRange);
+  u32x4_t q[NP];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) r.vw[i] = c[i];
+  for (int p = 0; p < NP; ++p)
+    q[p] = __builtin_amdgcn_raw_buffer_load_b128(v.rec, o + p * kPlaneBytes, sc, kStream);
+  if constexpr (BITS == 2) {
+    r.kw[0][0] = q[0][0]; r.kw[0][1] = q[0][1];
+    r.kw[1][0] = q[0][2]; r.kw[1][1] = q[0][3];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r.vw[i] = q[1][i];
   } else {
-    const u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(v.kc, o_k0, sc, kStream);
-    const u32x4_t b = __builtin_amdgcn_raw_buffer_load_b128(v.kc, o_k1, sc, kStream);
-    const u32x4_t c = __builtin_amdgcn_raw_buffer_load_b128(v.vc, o_v, sc, kStream);
-    const u32x4_t d = __builtin_amdgcn_raw_buffer_load_b128(v.vc, o_v + 16, sc, kStream);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      r.kw[0][i] = a[i]; r.kw[1][i] = b[i];
-      r.vw[i] = c[i]; r.vw[4 + i] = d[i];
+      r.kw[0][i] = q[0][i]; r.kw[1][i] = q[1][i];
+      r.vw[i] = q[2][i]; r.vw[4 + i] = q[3][i];
     }
   }
-  // scale/zero: each lane loads the two values at 2*lane of each array (128
-  // values per group); the values every role needs are re-read from LDS
-  // (stage_meta)
-  const __amdgpu_buffer_rsrc_t mr[4] = {v.ks, v.kz, v.vs, v.vz};
+  if constexpr (META == 1) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if constexpr (META == 1) {
-      r.mw[i][0] = __builtin_amdgcn_raw_buffer_load_b32(mr[i], o_mu, sm, kStream);
+    for (int i = 0; i < 4; ++i) {
+      r.mw[i][0] = q[BITS][i];
       r.mw[i][1] = 0;
-    } else {
-      const u32x2_t x = __builtin_amdgcn_raw_buffer_load_b64(mr[i], o_mu, sm, kStream);
-      r.mw[i][0] = x[0];
-      r.mw[i][1] = x[1];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      r.mw[i][0] = q[BITS + (i >> 1)][2 * (i & 1)];
+      r.mw[i][1] = q[BITS + (i >> 1)][2 * (i & 1) + 1];
     }
   }
 }
@@ -746,45 +754,73 @@ __device__ __forceinline__ void mfma_rchunk(const DecodeArgs &a, int u, int rc,
   const int new_row = a.new_idx - t0;   // row within the chunk; wave-uniform
   const bool has_new = new_row >= 0 && new_row < G;
 
-  // stage V rows in LDS: lane -> (row lane/2, 64 channels); rows past `valid`
-  // (stale or never written slots) become zeros
-  {
-    const int row = lane >> 1, c0 = 64 * (lane & 1);
-    const bool is_new = has_new && row == new_row;
-    uint4 *dst = reinterpret_cast<uint4 *>(&smf.w[wave].vres[row][c0]);
-    const uint4 *src = reinterpret_cast<const uint4 *>(
-        is_new ? a.v_new + (long long)u * D + c0 : vrows + (long long)row * D + c0);
-    uint4 x[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] = row < valid ? src[i] : make_uint4(0u, 0u, 0u, 0u);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) dst[i] = x[i];
-    if (is_new) {
-      uint4 *ring_row = reinterpret_cast<uint4 *>(a.v_res + (ring + row) * D + c0);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) ring_row[i] = x[i];
-    }
-  }
-  // A operands of q.K^T: K rows of the two tiles, natural channel order
+  // All loads first, in one batch (one memory latency for the chunk): V rows
+  // for the LDS transpose, lane -> (row lane/2, 64 channels); K rows of the
+  // two tiles as A operands of q.K^T (natural channel order).  Ring rows past
+  // `valid` (stale or never written slots, inside the ring) are loaded and
+  // then replaced by zeros (V) or masked out of the softmax (K).
+  const int vrow = lane >> 1, vc0 = 64 * (lane & 1);
+  const bool v_new = has_new && vrow == new_row;
+  const uint4 *vsrc = reinterpret_cast<const uint4 *>(
+      v_new ? a.v_new + (long long)u * D + vc0 : vrows + (long long)vrow * D + vc0);
   const int kr0 = 8 * (n >> 2) + (n & 3);
-  Op8 ak[2][4];
+  bool k_new[2];
+  const uint4 *ksrc[2];
 #pragma unroll
   for (int tile = 0; tile < 2; ++tile) {
     const int row = kr0 + 4 * tile;
-    const bool is_new = has_new && row == new_row;
-    const uint4 *kp = reinterpret_cast<const uint4 *>(
-        is_new ? a.k_new + (long long)u * D + 32 * gq : krows + (long long)row * D + 32 * gq);
-    uint4 x[4];
+    k_new[tile] = has_new && row == new_row;
+    ksrc[tile] = reinterpret_cast<const uint4 *>(
+        k_new[tile] ? a.k_new + (long long)u * D + 32 * gq : krows + (long long)row * D + 32 * gq);
+  }
+  const int b = u / a.kv_heads, h = u % a.kv_heads;
+  // query rows as B operands of q.K^T (hi columns; the lo columns get zeros):
+  // every lane loads a valid row; with one workgroup per compute unit (NW >
+  // 4, registers to spare) those of head block 0 come with the chunk
+  constexpr bool kQFirst = NW > 4;
+  auto q_rows = [&](int hb) {
+    const int hh = hb * 4 + (n & 3);
+    return reinterpret_cast<const uint4 *>(
+        a.q + ((long long)b * a.kv_heads * qpk + (long long)h * qpk + (hh < qpk ? hh : 0)) * D +
+        32 * gq);
+  };
+  uint4 xq[4];
+  if constexpr (kQFirst) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m) x[m] = kp[m];
-    if (is_new) {
-      uint4 *ring_row = reinterpret_cast<uint4 *>(a.k_res + (ring + row) * D + 32 * gq);
+    for (int m = 0; m < 4; ++m) xq[m] = q_rows(0)[m];
+  }
+  uint4 xv[8], xk[2][4];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) ring_row[m] = x[m];
+  for (int i = 0; i < 8; ++i) xv[i] = vsrc[i];
+#pragma unroll
+  for (int tile = 0; tile < 2; ++tile)
+#pragma unroll
+    for (int m = 0; m < 4; ++m) xk[tile][m] = ksrc[tile][m];
+  // stage V rows in LDS
+  {
+    const bool live = vrow < valid;
+    uint4 *dst = reinterpret_cast<uint4 *>(&smf.w[wave].vres[vrow][vc0]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dst[i] = live ? xv[i] : make_uint4(0u, 0u, 0u, 0u);
+  }
+  // the fused append: the new token's rows go into their ring slot
+  if (v_new) {
+    uint4 *ring_row = reinterpret_cast<uint4 *>(a.v_res + (ring + vrow) * D + vc0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ring_row[i] = xv[i];
+  }
+  Op8 ak[2][4];
+#pragma unroll
+  for (int tile = 0; tile < 2; ++tile) {
+    if (k_new[tile]) {
+      uint4 *ring_row = reinterpret_cast<uint4 *>(a.k_res + (ring + kr0 + 4 * tile) * D + 32 * gq);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) ring_row[m] = xk[tile][m];
     }
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      ak[tile][m].u[0] = x[m].x; ak[tile][m].u[1] = x[m].y; ak[tile][m].u[2] = x[m].z; ak[tile][m].u[3] = x[m].w;
+      ak[tile][m].u[0] = xk[tile][m].x; ak[tile][m].u[1] = xk[tile][m].y;
+      ak[tile][m].u[2] = xk[tile][m].z; ak[tile][m].u[3] = xk[tile][m].w;
     }
   }
   __builtin_amdgcn_wave_barrier();
@@ -799,18 +835,19 @@ __device__ __forceinline__ void mfma_rchunk(const DecodeArgs &a, int u, int rc,
       av[mt].u[s2] = lo | (hi << 16);
     }
   }
-  const int b = u / a.kv_heads, h = u % a.kv_heads;
 #pragma unroll
   for (int hb = 0; hb < NHB; ++hb) {
     const int hh = hb * 4 + (n & 3);
     const bool hi_col = (n & 4) == 0 && hh < qpk;
-    const uint4 *qp = reinterpret_cast<const uint4 *>(
-        a.q + ((long long)b * a.kv_heads * qpk + (long long)h * qpk + (hi_col ? hh : 0)) * D + 32 * gq);
+    if (hb > 0 || !kQFirst) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) xq[m] = q_rows(hb)[m];
+    }
     f32x4_t sc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       Op8 bq;
-      const uint4 x = hi_col ? qp[m] : make_uint4(0u, 0u, 0u, 0u);
+      const uint4 x = hi_col ? xq[m] : make_uint4(0u, 0u, 0u, 0u);
       bq.u[0] = x.x; bq.u[1] = x.y; bq.u[2] = x.z; bq.u[3] = x.w;
 #pragma unroll
       for (int tile = 0; tile < 2; ++tile)
@@ -956,7 +993,7 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeArgs a) {
     st.m_run[hb] = kNegInf; st.l_run[hb] = 0.f; st.z_run[hb] = 0.f; st.m_ref[hb] = 0.f;
   }
   const bool has_groups = g_begin < g_end;
-  const UnitView view = make_view<BITS, META, PAGED>(a, u, n, gq, cm);
+  const RecView view = make_rec_view<BITS, META, PAGED>(a, u, lane);
   // register sets of the load pipeline: kPrefetch groups in flight
   GroupRaw<BITS> r[kPrefetch + 1];
 #pragma unroll

@@ -44,10 +44,14 @@ kivi_status check_geom(const kivi_geom *g) {
   return KIVI_OK;
 }
 
-kivi_status check_cache(const kivi_cache *c) {
+// q_per_kv >= 2: the quantised history is kept as group records (kivi.h) in
+// the K_CODES buffer; the other five history buffers are unused
+bool records(const kivi_geom *g) { return g->q_per_kv >= 2; }
+
+kivi_status check_cache(const kivi_geom *g, const kivi_cache *c) {
   if (!c) return KIVI_E_NULL;
-  if (!c->k_codes || !c->k_scale || !c->k_zero || !c->v_codes || !c->v_scale ||
-      !c->v_zero || !c->k_res || !c->v_res)
+  if (!c->k_codes || !c->k_res || !c->v_res) return KIVI_E_NULL;
+  if (!records(g) && (!c->k_scale || !c->k_zero || !c->v_codes || !c->v_scale || !c->v_zero))
     return KIVI_E_NULL;
   return KIVI_OK;
 }
@@ -87,6 +91,7 @@ kivi_status enqueue_flush(const kivi_geom *g, kivi_cache *c, hipStream_t s) {
   a.max_tokens = g->max_tokens; a.n_groups_cap = g->max_tokens / G;
   a.k_codes = c->k_codes; a.k_scale = c->k_scale; a.k_zero = c->k_zero;
   a.v_codes = c->v_codes; a.v_scale = c->v_scale; a.v_zero = c->v_zero;
+  a.records = records(g);
   kivi_status st = hip_status(kivi::launch_quantize(g->bits, g->meta_format, a, s));
   if (st != KIVI_OK) return st;
   c->n_q += G;
@@ -188,12 +193,17 @@ kivi_status kivi_cache_layout(const kivi_geom *g, size_t bytes[8]) {
   const size_t G = (size_t)g->group, NG = T / G, b = (size_t)g->bits;
   const size_t slots = (size_t)(g->residual + g->group);
   const size_t mb = g->meta_format == KIVI_META_FP16_BF16 ? 2 : 4;   // bytes per scale/zero
-  bytes[KIVI_BUF_K_CODES] = U * T * D * b / 8;
-  bytes[KIVI_BUF_K_SCALE] = U * NG * D * mb;
-  bytes[KIVI_BUF_K_ZERO] = U * NG * D * mb;
-  bytes[KIVI_BUF_V_CODES] = U * NG * (G / 8) * D * b;
-  bytes[KIVI_BUF_V_SCALE] = U * NG * (D / G) * G * mb;
-  bytes[KIVI_BUF_V_ZERO] = U * NG * (D / G) * G * mb;
+  if (records(g)) {
+    bytes[KIVI_BUF_K_CODES] = U * NG * (size_t)kivi::rec_bytes(g->bits, g->meta_format);
+    for (int i = KIVI_BUF_K_SCALE; i <= KIVI_BUF_V_ZERO; ++i) bytes[i] = 0;
+  } else {
+    bytes[KIVI_BUF_K_CODES] = U * T * D * b / 8;
+    bytes[KIVI_BUF_K_SCALE] = U * NG * D * mb;
+    bytes[KIVI_BUF_K_ZERO] = U * NG * D * mb;
+    bytes[KIVI_BUF_V_CODES] = U * NG * (G / 8) * D * b;
+    bytes[KIVI_BUF_V_SCALE] = U * NG * (D / G) * G * mb;
+    bytes[KIVI_BUF_V_ZERO] = U * NG * (D / G) * G * mb;
+  }
   bytes[KIVI_BUF_K_RES] = U * slots * D * 2;
   bytes[KIVI_BUF_V_RES] = U * slots * D * 2;
   return KIVI_OK;
@@ -212,7 +222,7 @@ kivi_status kivi_quantize_prefill(const kivi_geom *g, kivi_cache *c, const uint1
                                   const uint16_t *v, int32_t seq_len, void *stream) {
   kivi_status st = check_geom(g);
   if (st != KIVI_OK) return st;
-  if ((st = check_cache(c)) != KIVI_OK) return st;
+  if ((st = check_cache(g, c)) != KIVI_OK) return st;
   if (!k || !v) return KIVI_E_NULL;
   if (seq_len < 1) return KIVI_E_SEQLEN;
   const int G = g->group, R = g->residual, slots = R + G;
@@ -230,6 +240,7 @@ kivi_status kivi_quantize_prefill(const kivi_geom *g, kivi_cache *c, const uint1
     a.max_tokens = g->max_tokens; a.n_groups_cap = g->max_tokens / G;
     a.k_codes = c->k_codes; a.k_scale = c->k_scale; a.k_zero = c->k_zero;
     a.v_codes = c->v_codes; a.v_scale = c->v_scale; a.v_zero = c->v_zero;
+    a.records = records(g);
     if ((st = hip_status(kivi::launch_quantize(g->bits, g->meta_format, a, s))) != KIVI_OK) return st;
   }
   if (r > 0) {
@@ -252,7 +263,7 @@ kivi_status kivi_append_token(const kivi_geom *g, kivi_cache *c, const uint16_t 
                               const uint16_t *v_new, void *stream) {
   kivi_status st = check_geom(g);
   if (st != KIVI_OK) return st;
-  if ((st = check_cache(c)) != KIVI_OK) return st;
+  if ((st = check_cache(g, c)) != KIVI_OK) return st;
   if (!k_new || !v_new) return KIVI_E_NULL;
   if ((st = check_state(g, c)) != KIVI_OK) return st;
   if (c->n_res == g->residual + g->group) return KIVI_E_RESIDUAL_FULL;
@@ -263,7 +274,7 @@ kivi_status kivi_flush_residual(const kivi_geom *g, kivi_cache *c, int32_t *flus
                                 void *stream) {
   kivi_status st = check_geom(g);
   if (st != KIVI_OK) return st;
-  if ((st = check_cache(c)) != KIVI_OK) return st;
+  if ((st = check_cache(g, c)) != KIVI_OK) return st;
   if ((st = check_state(g, c)) != KIVI_OK) return st;
   const int G = g->group, slots = g->residual + G;
   if (flushed) *flushed = 0;
@@ -279,7 +290,7 @@ kivi_status kivi_decode_attention(const kivi_geom *g, const kivi_cache *c, const
                                   void *stream) {
   kivi_status st = check_geom(g);
   if (st != KIVI_OK) return st;
-  if ((st = check_cache(c)) != KIVI_OK) return st;
+  if ((st = check_cache(g, c)) != KIVI_OK) return st;
   if ((st = check_attend_args(g, c, q, out, softmax_scale, ws, ws_bytes)) != KIVI_OK) return st;
   if ((st = check_state(g, c)) != KIVI_OK) return st;
   if (c->n_q + c->n_res == 0) return KIVI_E_STATE;
@@ -292,7 +303,7 @@ kivi_status kivi_decode_step(const kivi_geom *g, kivi_cache *c, const uint16_t *
                              void *stream) {
   kivi_status st = check_geom(g);
   if (st != KIVI_OK) return st;
-  if ((st = check_cache(c)) != KIVI_OK) return st;
+  if ((st = check_cache(g, c)) != KIVI_OK) return st;
   if (!k_new || !v_new) return KIVI_E_NULL;
   if ((st = check_attend_args(g, c, q, out, softmax_scale, ws, ws_bytes)) != KIVI_OK) return st;
   if ((st = check_state(g, c)) != KIVI_OK) return st;
@@ -376,6 +387,7 @@ kivi_status ragged_prefill_impl(const kivi_geom *g, const kivi_cache *c, const k
     a.max_tokens = g->max_tokens; a.n_groups_cap = g->max_tokens / G;
     a.k_codes = c->k_codes; a.k_scale = c->k_scale; a.k_zero = c->k_zero;
     a.v_codes = c->v_codes; a.v_scale = c->v_scale; a.v_zero = c->v_zero;
+    a.records = records(g);
     a.seq_lens = seq_lens;
     a.kv_heads = g->kv_heads; a.residual = R; a.slots = slots; a.stride = stride;
     a.pages = pm;
@@ -412,6 +424,7 @@ kivi_status ragged_step_impl(const kivi_geom *g, const kivi_cache *c, const kivi
   f.max_tokens = g->max_tokens; f.n_groups_cap = g->max_tokens / G;
   f.k_codes = c->k_codes; f.k_scale = c->k_scale; f.k_zero = c->k_zero;
   f.v_codes = c->v_codes; f.v_scale = c->v_scale; f.v_zero = c->v_zero;
+  f.records = records(g);
   f.state = state_in;
   f.kv_heads = g->kv_heads; f.residual = g->residual; f.slots = slots;
   f.pages = pm;
@@ -432,8 +445,9 @@ kivi_status ragged_step_impl(const kivi_geom *g, const kivi_cache *c, const kivi
 kivi_status paged_map(const kivi_geom *g, const kivi_paged_cache *pc, kivi::PageMap &pm,
                       kivi_cache &c) {
   if (!pc) return KIVI_E_NULL;
-  if (!pc->k_codes || !pc->k_scale || !pc->k_zero || !pc->v_codes || !pc->v_scale ||
-      !pc->v_zero || !pc->k_res || !pc->v_res || !pc->block_table)
+  if (!pc->k_codes || !pc->k_res || !pc->v_res || !pc->block_table) return KIVI_E_NULL;
+  if (!records(g) &&
+      (!pc->k_scale || !pc->k_zero || !pc->v_codes || !pc->v_scale || !pc->v_zero))
     return KIVI_E_NULL;
   size_t bytes[8];
   int32_t max_pages = 0;
@@ -461,7 +475,7 @@ kivi_status kivi_ragged_prefill(const kivi_geom *g, const kivi_cache *c, const u
                                 int32_t *state, void *stream) {
   kivi_status st = check_geom(g);
   if (st != KIVI_OK) return st;
-  if ((st = check_cache(c)) != KIVI_OK) return st;
+  if ((st = check_cache(g, c)) != KIVI_OK) return st;
   return ragged_prefill_impl(g, c, kivi::PageMap{}, k, v, stride, seq_lens, state,
                              (hipStream_t)stream);
 }
@@ -473,7 +487,7 @@ kivi_status kivi_ragged_decode_step(const kivi_geom *g, const kivi_cache *c,
                                     size_t ws_bytes, void *stream) {
   kivi_status st = check_geom(g);
   if (st != KIVI_OK) return st;
-  if ((st = check_cache(c)) != KIVI_OK) return st;
+  if ((st = check_cache(g, c)) != KIVI_OK) return st;
   return ragged_step_impl(g, c, kivi::PageMap{}, state_in, state_out, k_new, v_new, q, out,
                           softmax_scale, ws, ws_bytes, (hipStream_t)stream);
 }
@@ -491,15 +505,22 @@ kivi_status kivi_paged_layout(const kivi_geom *g, int32_t page_groups, int32_t n
   const size_t mb = g->meta_format == KIVI_META_FP16_BF16 ? 2 : 4;
   const double groups = (double)num_pages * g->kv_heads * page_groups;
   // every pool is addressed with 32-bit offsets that must stay below 2^31
-  if (groups * G * D * b / 8 >= 2147483648.0 || groups * D * mb >= 2147483648.0)
+  const size_t rec = (size_t)kivi::rec_bytes(g->bits, g->meta_format);
+  if (records(g) ? groups * rec >= 2147483648.0
+                 : (groups * G * D * b / 8 >= 2147483648.0 || groups * D * mb >= 2147483648.0))
     return KIVI_E_UNSUPPORTED;
   const size_t n = (size_t)groups;
-  bytes[KIVI_BUF_K_CODES] = n * G * D * b / 8;
-  bytes[KIVI_BUF_K_SCALE] = n * D * mb;
-  bytes[KIVI_BUF_K_ZERO] = n * D * mb;
-  bytes[KIVI_BUF_V_CODES] = n * G * D * b / 8;
-  bytes[KIVI_BUF_V_SCALE] = n * D * mb;
-  bytes[KIVI_BUF_V_ZERO] = n * D * mb;
+  if (records(g)) {
+    bytes[KIVI_BUF_K_CODES] = n * rec;
+    for (int i = KIVI_BUF_K_SCALE; i <= KIVI_BUF_V_ZERO; ++i) bytes[i] = 0;
+  } else {
+    bytes[KIVI_BUF_K_CODES] = n * G * D * b / 8;
+    bytes[KIVI_BUF_K_SCALE] = n * D * mb;
+    bytes[KIVI_BUF_K_ZERO] = n * D * mb;
+    bytes[KIVI_BUF_V_CODES] = n * G * D * b / 8;
+    bytes[KIVI_BUF_V_SCALE] = n * D * mb;
+    bytes[KIVI_BUF_V_ZERO] = n * D * mb;
+  }
   bytes[KIVI_BUF_K_RES] = (size_t)units_of(g) * slots * D * 2;
   bytes[KIVI_BUF_V_RES] = (size_t)units_of(g) * slots * D * 2;
   if (max_pages) {

@@ -65,6 +65,29 @@ __host__ __device__ inline long long group_slot(const PageMap &p, int kv_heads, 
   return (((long long)e * kv_heads + h) << p.shift) + (g & ((1 << p.shift) - 1));
 }
 
+// Group records (q_per_kv >= 2, kivi.h): the quantised history of one group
+// is one contiguous record of rec_planes() planes of 1 KiB; plane p holds 16
+// bytes for each lane l (0..63) of the decode wave at p * 1024 + 16 * l:
+//   planes [0, b/2)      K codes: lane 16 j + 4 (t >> 3) + (t & 3) holds the
+//                        32-channel block j of token rows t with (t >> 2) & 1
+//                        = 0 and = 1 (2-bit: 8 bytes each in one plane;
+//                        4-bit: one plane each)
+//   planes [b/2, b)      V codes: lane 16 o + (c >> 3) holds channels
+//                        8 (c >> 3) .. + 7 of octet o (b bytes per channel)
+//   planes [b, b + 2)    fp32 scale/zero: values 2l, 2l + 1 of k_scale,
+//                        k_zero (plane b) and v_scale, v_zero (plane b + 1)
+//   plane b              16-bit scale/zero: value pairs 2l, 2l + 1 of
+//                        k_scale, k_zero, v_scale, v_zero
+// Each piece holds the bytes of the per-array layout (kivi.h), so a record
+// is a fixed permutation of those bytes.
+constexpr int kPlaneBytes = 1024;
+__host__ __device__ constexpr int rec_planes(int bits, int meta) {
+  return bits + (meta == 1 ? 1 : 2);
+}
+__host__ __device__ constexpr int rec_bytes(int bits, int meta) {
+  return rec_planes(bits, meta) * kPlaneBytes;
+}
+
 // One launch of the group quantiser: `n_groups` groups of G tokens for each
 // of `n_units` units.  Source token i of local group gl of unit u is row
 // (src_tok0 + gl*G + i) of a [rows][D] bf16 block starting at
@@ -78,6 +101,7 @@ struct QuantizeArgs {
   int max_tokens, n_groups_cap;  // T, NG
   uint8_t *k_codes; void *k_scale, *k_zero;   // fp32, or fp16 / bf16 bits (meta)
   uint8_t *v_codes; void *v_scale, *v_zero;
+  int records;   // 1: group records in k_codes (q_per_kv >= 2), 0: per-array layout
   int gpw;   // groups per workgroup (set by the launcher)
   // Mixed-length batches (null otherwise).  seq_lens (prefill): sequence b
   // quantises its own n_q tokens, n_groups being the largest count.  state
@@ -116,6 +140,7 @@ struct RaggedResidualArgs {
 hipError_t launch_ragged_residual(const RaggedResidualArgs &a, hipStream_t s);
 
 struct DecodeArgs {
+  // per-array layout (q_per_kv == 1); q_per_kv >= 2: group records in k_codes
   const uint8_t *k_codes; const void *k_scale, *k_zero;   // fp32, or fp16 / bf16 bits
   const uint8_t *v_codes; const void *v_scale, *v_zero;
   uint16_t *k_res, *v_res;   // written only for the fused append below

@@ -85,6 +85,27 @@ __device__ __forceinline__ float max_x32(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// Byte offsets inside a group record (kivi_internal.h).  K piece: token row
+// t, 32-channel block j; V cell: octet o, channels 4 c4 .. 4 c4 + 3; scale /
+// zero value v (0..127) of array i (0 k_scale, 1 k_zero, 2 v_scale, 3 v_zero).
+template <int BITS>
+__device__ __forceinline__ int rec_k_piece(int t, int j) {
+  const int lane = 16 * j + 4 * (t >> 3) + (t & 3), tile = (t >> 2) & 1;
+  return BITS == 2 ? lane * 16 + tile * 8 : tile * kPlaneBytes + lane * 16;
+}
+template <int BITS>
+__device__ __forceinline__ int rec_v_cell(int o, int c4) {
+  const int lane = 16 * o + (c4 >> 1);
+  return BITS == 2 ? kPlaneBytes + lane * 16 + (c4 & 1) * 8
+                   : (2 + (c4 & 1)) * kPlaneBytes + lane * 16;
+}
+template <int BITS, int META>
+__device__ __forceinline__ int rec_meta(int i, int v) {
+  const int lane = v >> 1, e = v & 1;
+  return META == 1 ? BITS * kPlaneBytes + lane * 16 + i * 4 + e * 2
+                   : (BITS + (i >> 1)) * kPlaneBytes + lane * 16 + (i & 1) * 8 + e * 4;
+}
+
 // One wave quantises the keys of one half of the channels (64) of each of
 // its groups.  Lane (pair p, row half h) owns channels cb+2p, cb+2p+1 of rows
 // 16h..16h+15: the per-channel min/max over 32 tokens is 16 values in
@@ -117,7 +138,18 @@ __device__ __forceinline__ void key_group(const QuantizeArgs &a, int u, int gl,
   uint32_t sb0, sb1;
   group_params<BITS, META>(mn0, mx0, sc0, inv0, sb0);
   group_params<BITS, META>(mn1, mx1, sc1, inv1, sb1);
-  if (h == 0) {
+  if (h == 0 && a.records) {
+    uint8_t *rec = a.k_codes + slot * rec_bytes(BITS, META);
+    const int c = cb + 2 * p;   // channels c, c + 1: one lane's value pair
+    if constexpr (META == 1) {
+      *reinterpret_cast<uint32_t *>(rec + rec_meta<BITS, META>(0, c)) = sb0 | (sb1 << 16);
+      *reinterpret_cast<uint32_t *>(rec + rec_meta<BITS, META>(1, c)) =
+          zero_bits(mn0) | (zero_bits(mn1) << 16);
+    } else {
+      *reinterpret_cast<float2 *>(rec + rec_meta<BITS, META>(0, c)) = make_float2(sc0, sc1);
+      *reinterpret_cast<float2 *>(rec + rec_meta<BITS, META>(1, c)) = make_float2(mn0, mn1);
+    }
+  } else if (h == 0) {
     const long long m = slot * D + cb;   // element index of channel cb
     if constexpr (META == 1) {
       reinterpret_cast<uint32_t *>(static_cast<uint16_t *>(a.k_scale) + m)[p] = sb0 | (sb1 << 16);
@@ -138,7 +170,9 @@ __device__ __forceinline__ void key_group(const QuantizeArgs &a, int u, int gl,
   const int row = lane >> 1, c32 = 32 * (lane & 1);
   const uint4 b0 = *reinterpret_cast<const uint4 *>(tile + row * 64 + c32);
   const uint4 b1 = *reinterpret_cast<const uint4 *>(tile + row * 64 + c32 + 16);
-  uint8_t *dst = a.k_codes + (slot * G + row) * KROW + (cb + c32) * BITS / 8;
+  uint8_t *dst = a.records
+                     ? a.k_codes + slot * rec_bytes(BITS, META) + rec_k_piece<BITS>(row, (cb + c32) / 32)
+                     : a.k_codes + (slot * G + row) * KROW + (cb + c32) * BITS / 8;
   if constexpr (BITS == 2) {
     const uint32_t w0 = pack4x2(b0.x) | (pack4x2(b0.y) << 8) | (pack4x2(b0.z) << 16) |
                         (pack4x2(b0.w) << 24);
@@ -206,13 +240,25 @@ __device__ __forceinline__ void value_group(const QuantizeArgs &a, int u, int gl
   float sc, inv;
   uint32_t sb;
   group_params<BITS, META>(mn, mx, sc, inv, sb);
-  const long long mi = (slot * (D / G) + q) * G + 16 * part + r;
-  if constexpr (META == 1) {
-    static_cast<uint16_t *>(a.v_scale)[mi] = (uint16_t)sb;
-    static_cast<uint16_t *>(a.v_zero)[mi] = (uint16_t)zero_bits(mn);
+  if (a.records) {
+    uint8_t *rec = a.k_codes + slot * rec_bytes(BITS, META);
+    const int v = q * G + 16 * part + r;   // value index within the group
+    if constexpr (META == 1) {
+      *reinterpret_cast<uint16_t *>(rec + rec_meta<BITS, META>(2, v)) = (uint16_t)sb;
+      *reinterpret_cast<uint16_t *>(rec + rec_meta<BITS, META>(3, v)) = (uint16_t)zero_bits(mn);
+    } else {
+      *reinterpret_cast<float *>(rec + rec_meta<BITS, META>(2, v)) = sc;
+      *reinterpret_cast<float *>(rec + rec_meta<BITS, META>(3, v)) = mn;
+    }
   } else {
-    static_cast<float *>(a.v_scale)[mi] = sc;
-    static_cast<float *>(a.v_zero)[mi] = mn;
+    const long long mi = (slot * (D / G) + q) * G + 16 * part + r;
+    if constexpr (META == 1) {
+      static_cast<uint16_t *>(a.v_scale)[mi] = (uint16_t)sb;
+      static_cast<uint16_t *>(a.v_zero)[mi] = (uint16_t)zero_bits(mn);
+    } else {
+      static_cast<float *>(a.v_scale)[mi] = sc;
+      static_cast<float *>(a.v_zero)[mi] = mn;
+    }
   }
   uint32_t cw[8];
 #pragma unroll
@@ -233,7 +279,9 @@ __device__ __forceinline__ void value_group(const QuantizeArgs &a, int u, int gl
 #pragma unroll
     for (int i = 0; i < 4; ++i) cell[i] |= ((w >> (8 * i)) & 0xFFu) << (BITS * k);
   }
-  uint8_t *dst = a.v_codes + ((slot * (G / 8) + 2 * part + o) * D + 4 * c4) * BITS;
+  uint8_t *dst = a.records
+                     ? a.k_codes + slot * rec_bytes(BITS, META) + rec_v_cell<BITS>(2 * part + o, c4)
+                     : a.v_codes + ((slot * (G / 8) + 2 * part + o) * D + 4 * c4) * BITS;
   if constexpr (BITS == 2) {
     *reinterpret_cast<uint2 *>(dst) = make_uint2(cell[0] | (cell[1] << 16), cell[2] | (cell[3] << 16));
   } else {

@@ -12,6 +12,7 @@ import dataclasses
 import math
 import os
 
+import numpy as np
 import torch
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkivi.so")
@@ -159,6 +160,81 @@ def _ptr(t: torch.Tensor, dtype, shape=None, name="tensor") -> ctypes.c_void_p:
     return ctypes.c_void_p(t.data_ptr())
 
 
+def grouped(g: Geom) -> bool:
+    """True when the cache keeps its quantised history as group records
+    (q_per_kv >= 2; kivi.h)."""
+    return g.q_per_kv >= 2
+
+
+def record_bytes(g: Geom) -> int:
+    return 1024 * (g.bits + (1 if g.meta_format == META_FP16_BF16 else 2))
+
+
+def _group_shapes(g: Geom) -> dict:
+    """(shape, dtype) of one group's part of each of the six history buffers
+    (group records: all in k_codes, the other five empty)."""
+    D, b, G = g.head_dim, g.bits, g.group
+    m16 = g.meta_format == META_FP16_BF16
+    st = torch.float16 if m16 else torch.float32   # scale
+    zt = torch.bfloat16 if m16 else torch.float32  # zero
+    if grouped(g):
+        return {"k_codes": ((record_bytes(g),), torch.uint8), "k_scale": (None, st),
+                "k_zero": (None, zt), "v_codes": (None, torch.uint8), "v_scale": (None, st),
+                "v_zero": (None, zt)}
+    return {"k_codes": ((G, D * b // 8), torch.uint8), "k_scale": ((D,), st), "k_zero": ((D,), zt),
+            "v_codes": ((G // 8, D, b), torch.uint8), "v_scale": ((D // G, G), st),
+            "v_zero": ((D // G, G), zt)}
+
+
+def _history_shapes(g: Geom, lead: tuple) -> dict:
+    """Tensor shapes of the six history buffers for `lead` group slots
+    (empty buffers: shape (0,))."""
+    return {n: ((0,) if sh is None else lead + sh, dt) for n, (sh, dt) in _group_shapes(g).items()}
+
+
+def _np_bits(t: torch.Tensor) -> np.ndarray:
+    """numpy copy; 16-bit floats as their uint16 bit patterns"""
+    if t.dtype in (torch.float16, torch.bfloat16):
+        t = t.view(torch.int16)
+        return t.cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def records_to_arrays(rec: np.ndarray, bits: int, meta: int) -> dict:
+    """Group records [N][bytes] -> per-array layout of N groups (kivi.h):
+    k_codes [N][G][D*b/8], k_scale/k_zero [N][D], v_codes [N][G/8][D][b],
+    v_scale/v_zero [N][D/G][G]; scale/zero as fp32 or as 16-bit patterns."""
+    N = rec.shape[0]
+    r = rec.reshape(N, -1, 64, 16)
+    t = np.arange(32)[:, None]
+    j = np.arange(4)[None, :]
+    lane = 16 * j + 4 * (t >> 3) + (t & 3)              # [32][4]
+    tile = np.broadcast_to((t >> 2) & 1, lane.shape)
+    if bits == 2:
+        kc = r[:, 0][:, lane[..., None], 8 * tile[..., None] + np.arange(8)]   # [N][32][4][8]
+    else:
+        kc = r[:, tile, lane, :]                                                # [N][32][4][16]
+    kc = kc.reshape(N, 32, 4 * 8 * bits // 2)
+    o = np.arange(4)[:, None]
+    c4 = np.arange(32)[None, :]
+    vl = 16 * o + (c4 >> 1)                                                     # [4][32]
+    if bits == 2:
+        vc = r[:, 1][:, vl[..., None], 8 * np.broadcast_to(c4 & 1, vl.shape)[..., None] + np.arange(8)]
+    else:
+        vc = r[:, 2 + np.broadcast_to(c4 & 1, vl.shape), vl, :]
+    vc = vc.reshape(N, 4, 128, bits)
+    if meta == 1:
+        m = np.ascontiguousarray(r[:, bits]).view(np.uint16).reshape(N, 64, 8)
+        ks, kz, vs, vz = (m[:, :, 2 * i:2 * i + 2].reshape(N, 128) for i in range(4))
+    else:
+        m0 = np.ascontiguousarray(r[:, bits]).view(np.float32).reshape(N, 64, 4)
+        m1 = np.ascontiguousarray(r[:, bits + 1]).view(np.float32).reshape(N, 64, 4)
+        ks, kz = m0[:, :, 0:2].reshape(N, 128), m0[:, :, 2:4].reshape(N, 128)
+        vs, vz = m1[:, :, 0:2].reshape(N, 128), m1[:, :, 2:4].reshape(N, 128)
+    return {"k_codes": kc, "k_scale": ks, "k_zero": kz, "v_codes": vc,
+            "v_scale": vs.reshape(N, 4, 32), "v_zero": vz.reshape(N, 4, 32)}
+
+
 class Cache:
     """The eight cache buffers (torch tensors, shaped by the documented layout)
     and the host-side counters."""
@@ -168,19 +244,11 @@ class Cache:
         sizes = cache_layout(g)
         B, H, T, D, b, G = g.batch, g.kv_heads, g.max_tokens, g.head_dim, g.bits, g.group
         NG, S = T // G, g.residual + g.group
-        m16 = g.meta_format == META_FP16_BF16
-        st = torch.float16 if m16 else torch.float32   # scale
-        zt = torch.bfloat16 if m16 else torch.float32  # zero
-        shapes = {
-            "k_codes": ((B, H, T, D * b // 8), torch.uint8),
-            "k_scale": ((B, H, NG, D), st),
-            "k_zero": ((B, H, NG, D), zt),
-            "v_codes": ((B, H, NG, G // 8, D, b), torch.uint8),
-            "v_scale": ((B, H, NG, D // G, G), st),
-            "v_zero": ((B, H, NG, D // G, G), zt),
-            "k_res": ((B, H, S, D), torch.bfloat16),
-            "v_res": ((B, H, S, D), torch.bfloat16),
-        }
+        shapes = _history_shapes(g, (B, H, NG))
+        if not grouped(g):   # K codes of a unit as token rows [T][D*b/8]
+            shapes["k_codes"] = ((B, H, T, D * b // 8), torch.uint8)
+        shapes["k_res"] = ((B, H, S, D), torch.bfloat16)
+        shapes["v_res"] = ((B, H, S, D), torch.bfloat16)
         self.geom = g
         for (name, (shape, dt)), nbytes in zip(shapes.items(), sizes):
             t = torch.empty(shape, dtype=dt, device=device)
@@ -207,6 +275,20 @@ class Cache:
     def nbytes(self) -> int:
         return sum(getattr(self, n).numel() * getattr(self, n).element_size() for n in BUFFERS)
 
+    def history(self) -> dict:
+        """Host copy of the quantised history in the per-array layout
+        (k_codes [B][H][T][D*b/8], k_scale ..., as numpy arrays), whichever
+        layout the cache keeps (group records when q_per_kv >= 2)."""
+        g = self.geom
+        B, H, NG = g.batch, g.kv_heads, g.max_tokens // g.group
+        if not grouped(g):
+            return {n: _np_bits(getattr(self, n)) for n in BUFFERS[:6]}
+        arr = records_to_arrays(self.k_codes.cpu().numpy().reshape(B * H * NG, -1), g.bits,
+                                g.meta_format)
+        out = {n: a.reshape((B, H, NG) + a.shape[1:]) for n, a in arr.items()}
+        out["k_codes"] = out["k_codes"].reshape(B, H, NG * g.group, -1)
+        return out
+
 
 def paged_layout(g: Geom, page_groups: int, num_pages: int) -> tuple[list[int], int]:
     out = (ctypes.c_size_t * 8)()
@@ -226,19 +308,9 @@ class PagedCache:
         sizes, self.max_pages = paged_layout(g, page_groups, num_pages)
         B, H, D, b, G = g.batch, g.kv_heads, g.head_dim, g.bits, g.group
         n, S = num_pages * H * page_groups, g.residual + g.group
-        m16 = g.meta_format == META_FP16_BF16
-        st = torch.float16 if m16 else torch.float32
-        zt = torch.bfloat16 if m16 else torch.float32
-        shapes = {
-            "k_codes": ((n, G, D * b // 8), torch.uint8),
-            "k_scale": ((n, D), st),
-            "k_zero": ((n, D), zt),
-            "v_codes": ((n, G // 8, D, b), torch.uint8),
-            "v_scale": ((n, D // G, G), st),
-            "v_zero": ((n, D // G, G), zt),
-            "k_res": ((B, H, S, D), torch.bfloat16),
-            "v_res": ((B, H, S, D), torch.bfloat16),
-        }
+        shapes = _history_shapes(g, (n,))
+        shapes["k_res"] = ((B, H, S, D), torch.bfloat16)
+        shapes["v_res"] = ((B, H, S, D), torch.bfloat16)
         self.geom, self.page_groups, self.num_pages = g, page_groups, num_pages
         for (name, (shape, dt)), nbytes in zip(shapes.items(), sizes):
             t = torch.empty(shape, dtype=dt, device=device)
@@ -248,6 +320,15 @@ class PagedCache:
         self._c = _PagedCache(*[ctypes.c_void_p(getattr(self, n).data_ptr()) for n in BUFFERS],
                               ctypes.c_void_p(self.block_table.data_ptr()), page_groups,
                               num_pages)
+
+    def pool_history(self) -> dict:
+        """Host copy of the pools in the per-array per-slot layout (k_codes
+        [slots][G][D*b/8], k_scale [slots][D], ...), whichever layout the
+        pools keep."""
+        g = self.geom
+        if not grouped(g):
+            return {n: _np_bits(getattr(self, n)) for n in BUFFERS[:6]}
+        return records_to_arrays(self.k_codes.cpu().numpy(), g.bits, g.meta_format)
 
     def slot(self, b: int, h: int, g: int, table=None) -> int:
         """Pool slot of group g of (sequence b, kv head h); -1 without a page."""

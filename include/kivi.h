@@ -96,6 +96,31 @@
  *           Element type by geom.meta_format: KIVI_META_FP32 -- fp32 scale and
  *           fp32 zero; KIVI_META_FP16_BF16 -- fp16 scale bits and bf16 zero
  *           bits (uint16_t), see "16-bit scale/zero" below.
+ *  Group records (q_per_kv >= 2): the quantised history is one buffer,
+ *           k_codes (kivi_cache_layout gives the five other history buffers
+ *           size 0; they may be NULL), of one record per group:
+ *           uint8 [B][H][NG][P * 1024], P = b + 2 (fp32 scale/zero) or b + 1
+ *           (16-bit).  A record is a fixed permutation of the group's bytes
+ *           in the layout above, in the order one 64-lane wave of the decode
+ *           kernel reads them: plane p (1024 bytes) holds 16 bytes for each
+ *           lane l at p*1024 + 16*l.
+ *             K codes, planes [0, b/2): lane 16*j + 4*(t>>3) + (t&3) holds
+ *               bytes [j*4*b, (j+1)*4*b) of k_codes token rows t (first) and
+ *               t+4 (second) of the group, t with (t>>2)&1 == 0 (b = 2: 8
+ *               bytes each, one plane; b = 4: one plane each).
+ *             V codes, planes [b/2, b): lane 16*o + c/8 holds the 8*b bytes
+ *               of octet o, channels c..c+7 (c a multiple of 8); b = 4: the
+ *               first 16 bytes in plane 2, the other 16 in plane 3.
+ *             fp32 scale/zero, planes b and b+1: lane l holds values 2l, 2l+1
+ *               of k_scale then of k_zero (plane b) and of v_scale then of
+ *               v_zero (plane b+1), value index = channel (K) or
+ *               j*G + token (V).
+ *             16-bit scale/zero, plane b: lane l holds the pairs 2l, 2l+1 of
+ *               k_scale, k_zero, v_scale, v_zero (4 bytes each).
+ *           The record keeps every group's bytes contiguous (one 1 KiB load
+ *           per plane per wave, from one place in memory) instead of spread
+ *           over six arrays.  Paged pools (kivi_paged_layout) hold records the
+ *           same way, one per pool slot.
  *  k_res, v_res  bf16 [B][H][R+G][D]        residual ring of R+G slots.
  *           Logical residual token i (0 = oldest) lives in slot
  *           (res_start + i) mod (R+G).  res_start is always a multiple of G.
@@ -182,7 +207,9 @@ enum {
 };
 
 /* Byte sizes of the eight cache buffers for `geom`, in the order of the
- * KIVI_BUF_* enum.  Host-only, touches no device.
+ * KIVI_BUF_* enum (q_per_kv >= 2: the group records in K_CODES and 0 for
+ * K_SCALE .. V_ZERO, whose pointers the calls then ignore and accept NULL).
+ * Host-only, touches no device.
  * Errors: KIVI_E_NULL, KIVI_E_GEOMETRY, KIVI_E_UNSUPPORTED. */
 kivi_status kivi_cache_layout(const kivi_geom *geom, size_t bytes_out[8]);
 
@@ -349,7 +376,9 @@ kivi_status kivi_ragged_decode_step(const kivi_geom *geom, const kivi_cache *cac
  * per-group layout of kivi_cache with the unit block replaced by slots:
  *   k_codes  [slots][G][D*b/8]      k_scale, k_zero  [slots][D]
  *   v_codes  [slots][G/8][D][b]     v_scale, v_zero  [slots][D/G][G]
- * (scale/zero in the geom's meta_format).  The residual rings are not paged:
+ * (scale/zero in the geom's meta_format); with q_per_kv >= 2 there is one
+ * pool, k_codes [slots][record bytes] of group records, and the five other
+ * pool pointers are ignored (may be NULL).  The residual rings are not paged:
  * k_res, v_res are [B][H][R+G][D] as in kivi_cache.  Lengths are per
  * sequence, in the same device state as the mixed-length calls above.
  *
@@ -379,8 +408,9 @@ typedef struct {
 } kivi_paged_cache;
 
 /* Byte sizes of the buffers of a paged cache (indexed by kivi_buffer: the
- * six pools, then the two rings) and the block table's row length.  Every
- * pool must stay below 2 GiB (its offsets are 32-bit).
+ * six pools, then the two rings; q_per_kv >= 2: the record pool, five zeros,
+ * the rings) and the block table's row length.  Every pool must stay below
+ * 2 GiB (its offsets are 32-bit).
  * Errors: KIVI_E_NULL (bytes), KIVI_E_GEOMETRY, KIVI_E_UNSUPPORTED (geom
  *         outside the supported set, page_groups not a power of two in
  *         [1, 2^20], num_pages < 1, or a pool of 2 GiB or more). */
@@ -390,7 +420,7 @@ kivi_status kivi_paged_layout(const kivi_geom *geom, int32_t page_groups, int32_
 /* kivi_ragged_prefill into a paged cache: the same split, codes and
  * scale/zero bytes per sequence, stored in the sequence's pages.
  * Errors: those of kivi_ragged_prefill and kivi_paged_layout; KIVI_E_NULL
- *         for a NULL pool, ring or block table. */
+ *         for a NULL pool (that the layout uses), ring or block table. */
 kivi_status kivi_paged_prefill(const kivi_geom *geom, const kivi_paged_cache *cache,
                                const uint16_t *k, const uint16_t *v, int32_t stride,
                                const int32_t *seq_lens, int32_t *state, void *stream);

@@ -28,9 +28,15 @@ def bits_to_dev(x: np.ndarray, device="cuda") -> torch.Tensor:
 
 
 def host_cache(gc, og: oracle.Geom) -> oracle.Cache:
-    """Copy a device cache into an oracle.Cache (same documented layout)."""
+    """Copy a device cache into an oracle.Cache (per-array layout; a cache
+    with group records is brought to it by the binding's documented byte
+    permutation)."""
     hc = oracle.Cache(og)
-    for name in ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero", "k_res", "v_res"):
+    hist = gc.history()
+    for name in ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero"):
+        arr = getattr(hc, name)
+        arr[...] = np.ascontiguousarray(hist[name]).view(arr.dtype).reshape(arr.shape)
+    for name in ("k_res", "v_res"):
         arr = getattr(hc, name)
         arr[...] = to_np(getattr(gc, name)).reshape(arr.shape)
     hc.n_q, hc.n_res, hc.res_start = gc.n_q, gc.n_res, gc.res_start

@@ -36,10 +36,11 @@ def _check_unit_cache(gc, oc1, b, h):
     """Device cache unit (b, h) against a one-unit oracle cache."""
     nq, ng = oc1.n_q, oc1.n_q // 32
     assert (gc.n_q, gc.n_res) == (oc1.n_q, oc1.n_res)
-    np.testing.assert_array_equal(to_np(gc.k_codes[b, h, :nq]), oc1.k_codes[0, 0, :nq])
-    np.testing.assert_array_equal(to_np(gc.v_codes[b, h, :ng]), oc1.v_codes[0, 0, :ng])
+    hist = gc.history()
+    np.testing.assert_array_equal(hist["k_codes"][b, h, :nq], oc1.k_codes[0, 0, :nq])
+    np.testing.assert_array_equal(hist["v_codes"][b, h, :ng], oc1.v_codes[0, 0, :ng])
     for name in ("k_scale", "k_zero", "v_scale", "v_zero"):
-        np.testing.assert_array_equal(to_np(getattr(gc, name)[b, h, :ng]).view(np.uint8),
+        np.testing.assert_array_equal(np.ascontiguousarray(hist[name][b, h, :ng]).view(np.uint8),
                                       getattr(oc1, name)[0, 0, :ng].view(np.uint8), name)
     slots = 160
     go = [(gc.res_start + i) % slots for i in range(gc.n_res)]

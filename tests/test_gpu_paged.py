@@ -51,19 +51,18 @@ def _gather(pc, b, table, og1, n_q, n_res, res_start):
     """oracle.Cache (batch 1) of sequence b read out of the device pools."""
     hc = oracle.Cache(og1)
     G, H = og1.group, og1.kv_heads
-    pools = {n: to_np(getattr(pc, n)) for n in kivi.BUFFERS}
+    pools = pc.pool_history()   # per-array layout, whichever layout the pools keep
+    res = {n: to_np(getattr(pc, n)) for n in ("k_res", "v_res")}
     for h in range(H):
         for g in range(n_q // G):
             s = pc.slot(b, h, g, table)
             assert s >= 0
             hc.k_codes[0, h, g * G:(g + 1) * G] = pools["k_codes"][s]
-            hc.k_scale[0, h, g] = pools["k_scale"][s]
-            hc.k_zero[0, h, g] = pools["k_zero"][s]
-            hc.v_codes[0, h, g] = pools["v_codes"][s]
-            hc.v_scale[0, h, g] = pools["v_scale"][s]
-            hc.v_zero[0, h, g] = pools["v_zero"][s]
-        hc.k_res[0, h] = pools["k_res"][b, h]
-        hc.v_res[0, h] = pools["v_res"][b, h]
+            for n in ("k_scale", "k_zero", "v_codes", "v_scale", "v_zero"):
+                getattr(hc, n)[0, h, g] = np.ascontiguousarray(pools[n][s]).view(
+                    getattr(hc, n).dtype).reshape(getattr(hc, n)[0, h, g].shape)
+        hc.k_res[0, h] = res["k_res"][b, h]
+        hc.v_res[0, h] = res["v_res"][b, h]
     hc.n_q, hc.n_res, hc.res_start = n_q, n_res, res_start
     return hc
 
