@@ -168,7 +168,7 @@ __device__ void merge_and_store(MergeSmem<HMAX, NW> &sm, const DecodeArgs &a, in
   __syncthreads();
   const int qpk = a.qpk;
   float *part = a.part + ((long long)u * a.n_split + split) * qpk * kPartStride;
-  for (int idx = threadIdx.x; idx < qpk * D; idx += blockDim.x) {
+  for (int idx = threadIdx.x; idx < qpk * D; idx += 64 * NW) {
     const int hh = idx / D, c = idx % D;
     float M = kNegInf;
 #pragma unroll
@@ -194,6 +194,9 @@ __device__ void merge_and_store(MergeSmem<HMAX, NW> &sm, const DecodeArgs &a, in
 // partials of each of its query heads,
 //   M = max m_s,  out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s,
 // writes `out`, and re-arms the counter to zero for the next call.
+// NT: threads of the workgroup (a constant: blockDim would be a late scalar
+// load from the dispatch packet)
+template <int NT>
 __device__ void finish_unit(const DecodeArgs &a, int u, int *s_last, int4 next_state) {
   // the barrier waits for this workgroup's partial stores (vmcnt) before the
   // arrival is counted
@@ -208,7 +211,7 @@ __device__ void finish_unit(const DecodeArgs &a, int u, int *s_last, int4 next_s
   const int qpk = a.qpk;
   const long long stride = (long long)qpk * kPartStride;
   constexpr int kBatch = 8;   // splits whose partials are loaded together
-  for (int idx = threadIdx.x; idx < qpk * D; idx += blockDim.x) {
+  for (int idx = threadIdx.x; idx < qpk * D; idx += NT) {
     const int hh = idx / D, c = idx % D;
     const float *base = a.part + ((long long)u * a.n_split * qpk + hh) * kPartStride;
     float M = kNegInf, l = 0.f, o = 0.f;
@@ -1116,7 +1119,7 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeArgs a) {
     }
   }
   merge_and_store<HMAX, NW>(sm.mg, a, u, split);
-  finish_unit(a, u, &sm.mg.last, next_state);
+  finish_unit<64 * NW>(a, u, &sm.mg.last, next_state);
 }
 
 // ------------------------------------------------------- VALU (MHA) path ---
@@ -1464,7 +1467,7 @@ __global__ __launch_bounds__(256) void decode_mha_kernel(DecodeArgs a) {
     sm.mg.l[L.wave][0] = l;
   }
   merge_and_store<1, 4>(sm.mg, a, u, split);
-  finish_unit(a, u, &sm.mg.last, next_state);
+  finish_unit<256>(a, u, &sm.mg.last, next_state);
 }
 
 }  // namespace
