@@ -1050,6 +1050,18 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeArgs a) {
         to_load = __builtin_amdgcn_readfirstlane(claim);
         if (lane == 0)
           claim = __hip_atomic_fetch_add(&s_next, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        // issue priority = live groups still in this wave's register sets:
+        // equal (3) while groups remain to be claimed; at the end the waves
+        // with more left are served first, so that the waves of a SIMD finish
+        // together instead of the oldest first (the default tie-break)
+        {
+          int left = 0;
+#pragma unroll
+          for (int i = 0; i < C; ++i) left += gk[i] < g_end ? 1 : 0;
+          if (left >= 3) __builtin_amdgcn_s_setprio(3);
+          else if (left == 2) __builtin_amdgcn_s_setprio(2);
+          else __builtin_amdgcn_s_setprio(1);
+        }
         if (gk[k] < g_end) {
           float bn[NHB];
           attend_group<BITS, NHB, NW>(r[k], st, sm.mf, buf, beta, wave, n, gq, [&] {
