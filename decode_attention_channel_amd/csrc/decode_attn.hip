@@ -457,11 +457,11 @@ constexpr uint32_t kOutOfRange = 0x80000000u;   // > any unit's buffer size
 // step), which keeps them from displacing other lines in the caches
 constexpr int kStream = 2;
 
-// Groups in flight per wave beyond the one being computed (MFMA path).
-#ifndef KIVI_PREFETCH
-#define KIVI_PREFETCH 2
-#endif
-constexpr int kPrefetch = KIVI_PREFETCH;
+// Groups in flight per wave beyond the one being computed.  With 8-12 waves
+// per compute unit one is enough to keep HBM busy, and fewer groups
+// committed per wave end the launch with less imbalance between waves (it
+// measured faster than two or three on both paths).
+constexpr int kPrefetch = 1;
 
 
 template <int BITS, int META, bool PAGED>
@@ -977,7 +977,7 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeArgs a) {
   const int r_begin = kDyn ? wr.r_begin + wave : wr.r_begin;
   const int r_end = kDyn ? min(r_begin + 1, wr.r_end) : wr.r_end;
 
-  // Order of the first loads: the query (needed first), then the first two
+  // Order of the first loads: the query (needed first), then the first
   // groups, so that waiting for the query does not wait for the groups.
   uint4 qraw[NHB];
 #pragma unroll
@@ -1050,16 +1050,17 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeArgs a) {
         to_load = __builtin_amdgcn_readfirstlane(claim);
         if (lane == 0)
           claim = __hip_atomic_fetch_add(&s_next, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        // issue priority = live groups still in this wave's register sets:
-        // equal (3) while groups remain to be claimed; at the end the waves
-        // with more left are served first, so that the waves of a SIMD finish
-        // together instead of the oldest first (the default tie-break)
+        // issue priority from the live groups still in this wave's register
+        // sets: the same for all waves while groups remain to be claimed; at
+        // the end the waves with more left are served first, so that the
+        // waves of a SIMD finish together instead of the oldest first (the
+        // default tie-break)
         {
           int left = 0;
 #pragma unroll
           for (int i = 0; i < C; ++i) left += gk[i] < g_end ? 1 : 0;
-          if (left >= 3) __builtin_amdgcn_s_setprio(3);
-          else if (left == 2) __builtin_amdgcn_s_setprio(2);
+          if (left == C) __builtin_amdgcn_s_setprio(3);
+          else if (left == C - 1) __builtin_amdgcn_s_setprio(2);
           else __builtin_amdgcn_s_setprio(1);
         }
         if (gk[k] < g_end) {
