@@ -292,7 +292,6 @@ def batch_sweep(args):
         "best_tokens_s": {"kivi": best_kivi, "bf16": best_bf16, "ratio": best_kivi / best_bf16},
         "rows": [{"batch": B, **rows[B]} for B in sorted(rows)],
         "data": "synthetic (seeded random cache contents; timing only)",
-        "mixed_length_steps": ragged,
         "paper_context": "up to 4x batch and 2.35x-3.47x throughput vs FP16 (Llama-2-7B, one "
                          "A100 80GB, whole model; not comparable, quoted as context)",
     }
