@@ -145,35 +145,26 @@ def cpu_baseline(w, seed, units_wanted=256, meta=0):
 
 def _fill_random_cache(cache, n_q, n_res, gen):
     """Seeded synthetic cache contents for timing: uniform codes, positive
-    scales, normal zeros and residual (group records: the same values in
-    their record planes)."""
+    scales, normal zeros and residual, placed in the record planes."""
     import torch
 
     from decode_attention_channel_amd import kivi
 
     g = cache.geom
-    if kivi.grouped(g):
-        rec = cache.k_codes.view(-1, kivi.record_bytes(g) // 1024, 1024)
-        rec[:, :g.bits].random_(0, 256, generator=gen)
-        meta = rec[:, g.bits:].contiguous()
-        if g.meta_format == kivi.META_FP16_BF16:   # per lane: ks, kz, vs, vz pairs
-            m = meta.view(torch.int16).view(-1, 64, 4, 2)
-            sc = torch.empty(m[:, :, 0::2].shape, device=m.device).uniform_(0.01, 0.5, generator=gen)
-            zr = torch.empty(m[:, :, 1::2].shape, device=m.device).normal_(generator=gen)
-            m[:, :, 0::2] = sc.to(torch.float16).view(torch.int16)
-            m[:, :, 1::2] = zr.to(torch.bfloat16).view(torch.int16)
-        else:                                      # per lane: scale pair, zero pair
-            m = meta.view(torch.float32).view(-1, 64, 2, 2)
-            m[:, :, 0].uniform_(0.01, 0.5, generator=gen)
-            m[:, :, 1].normal_(generator=gen)
-        rec[:, g.bits:] = meta
-    else:
-        cache.k_codes.random_(0, 256, generator=gen)
-        cache.v_codes.random_(0, 256, generator=gen)
-        for t in (cache.k_scale, cache.v_scale):
-            t.uniform_(0.01, 0.5, generator=gen)
-        for t in (cache.k_zero, cache.v_zero):
-            t.normal_(generator=gen)
+    rec = cache.k_codes.view(-1, kivi.record_bytes(g) // 1024, 1024)
+    rec[:, :g.bits].random_(0, 256, generator=gen)
+    meta = rec[:, g.bits:].contiguous()
+    if g.meta_format == kivi.META_FP16_BF16:   # per lane: ks, kz, vs, vz pairs
+        m = meta.view(torch.int16).view(-1, 64, 4, 2)
+        sc = torch.empty(m[:, :, 0::2].shape, device=m.device).uniform_(0.01, 0.5, generator=gen)
+        zr = torch.empty(m[:, :, 1::2].shape, device=m.device).normal_(generator=gen)
+        m[:, :, 0::2] = sc.to(torch.float16).view(torch.int16)
+        m[:, :, 1::2] = zr.to(torch.bfloat16).view(torch.int16)
+    else:                                      # per lane: scale pair, zero pair
+        m = meta.view(torch.float32).view(-1, 64, 2, 2)
+        m[:, :, 0].uniform_(0.01, 0.5, generator=gen)
+        m[:, :, 1].normal_(generator=gen)
+    rec[:, g.bits:] = meta
     for t in (cache.k_res, cache.v_res):
         t.normal_(generator=gen)
     cache.set_counters(n_q, n_res, 0)
@@ -350,12 +341,7 @@ def _paged_copy(geom, cache, page_groups, rng):
     h = torch.arange(H, device=tb.device)
     slot = ((tb[:, g // page_groups][:, None, :] * H + h[None, :, None]) * page_groups +
             (g % page_groups)[None, None, :]).reshape(-1)
-    for name in ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero"):
-        src = getattr(cache, name)
-        dst = getattr(pc, name)
-        if src.numel() == 0:   # group records: the history is all in k_codes
-            continue
-        dst[slot] = src.reshape(B * H * NG, *dst.shape[1:])
+    pc.k_codes[slot] = cache.k_codes.reshape(B * H * NG, -1)   # the group records
     pc.k_res.copy_(cache.k_res)
     pc.v_res.copy_(cache.v_res)
     return pc

@@ -353,46 +353,6 @@ struct GroupRaw {
 template <int META>
 constexpr int kMetaBytes = META == 1 ? 2 : 4;
 
-// Per-unit buffer of one scale/zero array.
-template <int META>
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t meta_rsrc(const void *base, int u, long long NG) {
-  const long long per_unit = NG * D * kMetaBytes<META>;
-  return make_rsrc(static_cast<const char *>(base) + u * per_unit, (uint32_t)per_unit);
-}
-
-// The six group-major buffers of a unit's history: the unit's own block of
-// each array, or (PAGED) the whole pools, which the host keeps below 2 GiB
-// each so that kOutOfRange offsets stay out of range.
-struct HistBufs {
-  __amdgpu_buffer_rsrc_t kc, vc, ks, kz, vs, vz;
-};
-
-template <int BITS, int META, bool PAGED>
-__device__ __forceinline__ HistBufs hist_bufs(const DecodeArgs &a, int u) {
-  constexpr int KROW = D * BITS / 8;
-  HistBufs v;
-  if constexpr (PAGED) {
-    const long long groups = (long long)a.pages.num_pages * a.kv_heads << a.pages.shift;
-    const uint32_t cb = (uint32_t)(groups * G * KROW), mb = (uint32_t)(groups * D * kMetaBytes<META>);
-    v.kc = make_rsrc(a.k_codes, cb);
-    v.vc = make_rsrc(a.v_codes, cb);
-    v.ks = make_rsrc(a.k_scale, mb);
-    v.kz = make_rsrc(a.k_zero, mb);
-    v.vs = make_rsrc(a.v_scale, mb);
-    v.vz = make_rsrc(a.v_zero, mb);
-  } else {
-    const long long T = a.max_tokens, NG = a.n_groups_cap;
-    const uint32_t code_bytes = (uint32_t)(T * KROW);
-    v.kc = make_rsrc(a.k_codes + u * T * KROW, code_bytes);
-    v.vc = make_rsrc(a.v_codes + u * T * KROW, code_bytes);
-    v.ks = meta_rsrc<META>(a.k_scale, u, NG);
-    v.kz = meta_rsrc<META>(a.k_zero, u, NG);
-    v.vs = meta_rsrc<META>(a.v_scale, u, NG);
-    v.vz = meta_rsrc<META>(a.v_zero, u, NG);
-  }
-  return v;
-}
-
 // Page table entry read through the scalar cache (the table is read-only
 // for the whole launch), so that it does not count among the vector loads
 // of the group pipeline.
@@ -401,32 +361,9 @@ __device__ __forceinline__ int page_entry(const int32_t *table, long long i) {
   return ((ConstPtr)table)[i];
 }
 
-// Scalar byte offsets of group g in the history buffers: codes (sc) and one
-// scale/zero array (sm).  PAGED: the group's slot in the pools; a group
-// without a page is loaded as not live (zeros, no memory access).
-template <int BITS, int META, bool PAGED>
-__device__ __forceinline__ void group_offsets(const DecodeArgs &a, int u, int g, bool &live,
-                                              uint32_t &sc, uint32_t &sm) {
-  long long slot = g;
-  if constexpr (PAGED) {
-    slot = -1;
-    const int pi = g >> a.pages.shift;
-    if (live && pi < a.pages.max_pages) {
-      const int b = u / a.kv_heads, h = u - b * a.kv_heads;
-      const int e = page_entry(a.pages.table, (long long)b * a.pages.max_pages + pi);
-      if (e >= 0 && e < a.pages.num_pages)
-        slot = (((long long)e * a.kv_heads + h) << a.pages.shift) + (g & ((1 << a.pages.shift) - 1));
-    }
-    live = slot >= 0;
-    if (!live) slot = 0;
-  }
-  // wave-uniform: keep them in SGPRs (scalar buffer offsets)
-  sc = __builtin_amdgcn_readfirstlane((uint32_t)slot * (G * D * BITS / 8));
-  sm = __builtin_amdgcn_readfirstlane((uint32_t)slot * (D * kMetaBytes<META>));
-}
-
-// Group records (q_per_kv >= 2, layout in kivi_internal.h): one buffer
-// resource over the unit's records (or the paged pool); lane l reads bytes
+// Group records (layout in kivi_internal.h): one buffer resource over the
+// unit's records, or (PAGED) over the whole pool, which the host keeps below
+// 2 GiB so that kOutOfRange offsets stay out of range.  Lane l reads bytes
 // [16 l, 16 l + 16) of every plane, the group entering as a scalar offset.
 struct RecView {
   __amdgpu_buffer_rsrc_t rec;
@@ -464,10 +401,11 @@ constexpr int kStream = 2;
 constexpr int kPrefetch = 1;
 
 
+// The planes of group g as this lane's 16-byte pieces.  PAGED: the group's
+// slot in the pool; a group without a page is loaded as not live.
 template <int BITS, int META, bool PAGED>
-__device__ __forceinline__ void load_group(GroupRaw<BITS> &r, const RecView &v,
-                                           const DecodeArgs &a, int u, int g, bool live) {
-  constexpr int NP = rec_planes(BITS, META);
+__device__ __forceinline__ void load_record(u32x4_t (&q)[rec_planes(BITS, META)], const RecView &v,
+                                            const DecodeArgs &a, int u, int g, bool live) {
   long long slot = g;   // contiguous: the view starts at the unit's records
   if constexpr (PAGED) {
     slot = -1;
@@ -484,10 +422,36 @@ __device__ __forceinline__ void load_group(GroupRaw<BITS> &r, const RecView &v,
   // wave-uniform: a scalar buffer offset
   const uint32_t sc = __builtin_amdgcn_readfirstlane((uint32_t)slot * (uint32_t)rec_bytes(BITS, META));
   const uint32_t o = v.o_lane + (live ? 0u : kOutOfRange);
-  u32x4_t q[NP];
 #pragma unroll
-  for (int p = 0; p < NP; ++p)
+  for (int p = 0; p < rec_planes(BITS, META); ++p)
     q[p] = __builtin_amdgcn_raw_buffer_load_b128(v.rec, o + p * kPlaneBytes, sc, kStream);
+}
+
+// Scale/zero pairs of this lane (values 2l, 2l + 1 of each array) from the
+// meta plane(s) of a record.
+template <int BITS, int META>
+__device__ __forceinline__ void record_meta(uint32_t (&mw)[4][2],
+                                            const u32x4_t (&q)[rec_planes(BITS, META)]) {
+  if constexpr (META == 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      mw[i][0] = q[BITS][i];
+      mw[i][1] = 0;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      mw[i][0] = q[BITS + (i >> 1)][2 * (i & 1)];
+      mw[i][1] = q[BITS + (i >> 1)][2 * (i & 1) + 1];
+    }
+  }
+}
+
+template <int BITS, int META, bool PAGED>
+__device__ __forceinline__ void load_group(GroupRaw<BITS> &r, const RecView &v,
+                                           const DecodeArgs &a, int u, int g, bool live) {
+  u32x4_t q[rec_planes(BITS, META)];
+  load_record<BITS, META, PAGED>(q, v, a, u, g, live);
   if constexpr (BITS == 2) {
     r.kw[0][0] = q[0][0]; r.kw[0][1] = q[0][1];
     r.kw[1][0] = q[0][2]; r.kw[1][1] = q[0][3];
@@ -500,19 +464,7 @@ __device__ __forceinline__ void load_group(GroupRaw<BITS> &r, const RecView &v,
       r.vw[i] = q[2][i]; r.vw[4 + i] = q[3][i];
     }
   }
-  if constexpr (META == 1) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      r.mw[i][0] = q[BITS][i];
-      r.mw[i][1] = 0;
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      r.mw[i][0] = q[BITS + (i >> 1)][2 * (i & 1)];
-      r.mw[i][1] = q[BITS + (i >> 1)][2 * (i & 1) + 1];
-    }
-  }
+  record_meta<BITS, META>(r.mw, q);
 }
 
 // Write this lane's two values of each scale/zero array to the wave's LDS
@@ -1151,65 +1103,29 @@ struct ValuRaw {
   uint32_t mw[4][2];          // this lane's 8 bytes of each scale/zero array
 };
 
-struct ValuView {
-  __amdgpu_buffer_rsrc_t kc, vc, ks, kz, vs, vz;
-  uint32_t o_k, o_v, o_mu;
-};
-
+// Loads of group g (live == false: out-of-range loads, see load_group).  The
+// record's K planes hold the q.k roles above (lane 8 tb + cb), its V planes
+// the P.V roles (lane 16 oc + cq), as the MFMA path's V planes do.
 template <int BITS, int META, bool PAGED>
-__device__ __forceinline__ ValuView make_valu_view(const DecodeArgs &a, int u, int tb, int cb,
-                                                   int oc, int cq, int lane) {
-  constexpr int KROW = D * BITS / 8;
-  ValuView v;
-  const HistBufs hb = hist_bufs<BITS, META, PAGED>(a, u);
-  v.kc = hb.kc; v.vc = hb.vc; v.ks = hb.ks; v.kz = hb.kz; v.vs = hb.vs; v.vz = hb.vz;
-  v.o_k = 4 * tb * KROW + 2 * BITS * cb;
-  v.o_v = (oc * D + 8 * cq) * BITS;
-  v.o_mu = 2 * kMetaBytes<META> * lane;
-  return v;
-}
-
-// Loads of group g (live == false: out-of-range loads, see load_group).
-template <int BITS, int META, bool PAGED>
-__device__ __forceinline__ void load_valu_group(ValuRaw<BITS> &r, const ValuView &v,
+__device__ __forceinline__ void load_valu_group(ValuRaw<BITS> &r, const RecView &v,
                                                 const DecodeArgs &a, int u, int g, bool live) {
-  constexpr int KROW = D * BITS / 8;
-  uint32_t sc, sm;
-  group_offsets<BITS, META, PAGED>(a, u, g, live, sc, sm);
-  const uint32_t ob = live ? 0u : kOutOfRange;
-  const uint32_t o_k = v.o_k + ob, o_v = v.o_v + ob, o_mu = v.o_mu + ob;
+  u32x4_t q[rec_planes(BITS, META)];
+  load_record<BITS, META, PAGED>(q, v, a, u, g, live);
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     if constexpr (BITS == 2) {
-      r.kw[t][0] = __builtin_amdgcn_raw_buffer_load_b32(v.kc, o_k + t * KROW, sc, kStream);
+      r.kw[t][0] = q[0][t];
     } else {
-      const u32x2_t x = __builtin_amdgcn_raw_buffer_load_b64(v.kc, o_k + t * KROW, sc, kStream);
-      r.kw[t][0] = x[0];
-      r.kw[t][1] = x[1];
+      r.kw[t][0] = q[t >> 1][2 * (t & 1)];
+      r.kw[t][1] = q[t >> 1][2 * (t & 1) + 1];
     }
   }
-  {
-    const u32x4_t c = __builtin_amdgcn_raw_buffer_load_b128(v.vc, o_v, sc, kStream);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) r.vw[i] = c[i];
-    if constexpr (BITS == 4) {
-      const u32x4_t d = __builtin_amdgcn_raw_buffer_load_b128(v.vc, o_v + 16, sc, kStream);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) r.vw[4 + i] = d[i];
-    }
-  }
-  const __amdgpu_buffer_rsrc_t mr[4] = {v.ks, v.kz, v.vs, v.vz};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    if constexpr (META == 1) {
-      r.mw[i][0] = __builtin_amdgcn_raw_buffer_load_b32(mr[i], o_mu, sm, kStream);
-      r.mw[i][1] = 0;
-    } else {
-      const u32x2_t x = __builtin_amdgcn_raw_buffer_load_b64(mr[i], o_mu, sm, kStream);
-      r.mw[i][0] = x[0];
-      r.mw[i][1] = x[1];
-    }
+    r.vw[i] = q[BITS / 2][i];
+    if constexpr (BITS == 4) r.vw[4 + i] = q[3][i];
   }
+  record_meta<BITS, META>(r.mw, q);
 }
 
 struct ValuSmem {
@@ -1430,7 +1346,7 @@ __global__ __launch_bounds__(256) void decode_mha_kernel(DecodeArgs a) {
   const uint4 *qp = reinterpret_cast<const uint4 *>(a.q + (long long)u * D + 16 * L.cb);
   const uint4 qraw[2] = {qp[0], qp[1]};
   const bool has_groups = wr.g_begin < wr.g_end;
-  const ValuView view = make_valu_view<BITS, META, PAGED>(a, u, L.tb, L.cb, L.oc, L.cq, L.lane);
+  const RecView view = make_rec_view<BITS, META, PAGED>(a, u, L.lane);
   ValuRaw<BITS> r[kPrefetch + 1];
 #pragma unroll
   for (int i = 0; i < kPrefetch; ++i) {

@@ -44,15 +44,14 @@ kivi_status check_geom(const kivi_geom *g) {
   return KIVI_OK;
 }
 
-// q_per_kv >= 2: the quantised history is kept as group records (kivi.h) in
-// the K_CODES buffer; the other five history buffers are unused
-bool records(const kivi_geom *g) { return g->q_per_kv >= 2; }
+// The quantised history is kept as group records (kivi.h) in the K_CODES
+// buffer; the other five history buffers are unused.  K codes take the lane
+// roles of the kernel that reads them: VALU for q_per_kv = 1, MFMA otherwise.
+int valu_k(const kivi_geom *g) { return g->q_per_kv == 1 ? 1 : 0; }
 
 kivi_status check_cache(const kivi_geom *g, const kivi_cache *c) {
   if (!c) return KIVI_E_NULL;
   if (!c->k_codes || !c->k_res || !c->v_res) return KIVI_E_NULL;
-  if (!records(g) && (!c->k_scale || !c->k_zero || !c->v_codes || !c->v_scale || !c->v_zero))
-    return KIVI_E_NULL;
   return KIVI_OK;
 }
 
@@ -89,9 +88,8 @@ kivi_status enqueue_flush(const kivi_geom *g, kivi_cache *c, hipStream_t s) {
   a.src_tok0 = c->res_start;
   a.n_groups = 1; a.n_units = (int)units_of(g); a.dst_g0 = c->n_q / G;
   a.max_tokens = g->max_tokens; a.n_groups_cap = g->max_tokens / G;
-  a.k_codes = c->k_codes; a.k_scale = c->k_scale; a.k_zero = c->k_zero;
-  a.v_codes = c->v_codes; a.v_scale = c->v_scale; a.v_zero = c->v_zero;
-  a.records = records(g);
+  a.k_codes = c->k_codes;
+  a.valu_k = valu_k(g);
   kivi_status st = hip_status(kivi::launch_quantize(g->bits, g->meta_format, a, s));
   if (st != KIVI_OK) return st;
   c->n_q += G;
@@ -142,8 +140,7 @@ kivi_status enqueue_attend(const kivi_geom *g, const kivi_cache *c, const uint16
                            const kivi::PageMap &pages = kivi::PageMap{}) {
   kivi::DecodeArgs a{};
   a.pages = pages;
-  a.k_codes = c->k_codes; a.k_scale = c->k_scale; a.k_zero = c->k_zero;
-  a.v_codes = c->v_codes; a.v_scale = c->v_scale; a.v_zero = c->v_zero;
+  a.k_codes = c->k_codes;
   a.k_res = c->k_res; a.v_res = c->v_res;
   a.k_new = k_new; a.v_new = v_new;
   a.new_idx = k_new ? c->n_res - 1 : -1;
@@ -189,21 +186,11 @@ kivi_status kivi_cache_layout(const kivi_geom *g, size_t bytes[8]) {
   kivi_status st = check_geom(g);
   if (st != KIVI_OK) return st;
   if (!bytes) return KIVI_E_NULL;
-  const size_t U = (size_t)units_of(g), T = (size_t)g->max_tokens, D = (size_t)g->head_dim;
-  const size_t G = (size_t)g->group, NG = T / G, b = (size_t)g->bits;
+  const size_t U = (size_t)units_of(g), D = (size_t)g->head_dim;
+  const size_t NG = (size_t)(g->max_tokens / g->group);
   const size_t slots = (size_t)(g->residual + g->group);
-  const size_t mb = g->meta_format == KIVI_META_FP16_BF16 ? 2 : 4;   // bytes per scale/zero
-  if (records(g)) {
-    bytes[KIVI_BUF_K_CODES] = U * NG * (size_t)kivi::rec_bytes(g->bits, g->meta_format);
-    for (int i = KIVI_BUF_K_SCALE; i <= KIVI_BUF_V_ZERO; ++i) bytes[i] = 0;
-  } else {
-    bytes[KIVI_BUF_K_CODES] = U * T * D * b / 8;
-    bytes[KIVI_BUF_K_SCALE] = U * NG * D * mb;
-    bytes[KIVI_BUF_K_ZERO] = U * NG * D * mb;
-    bytes[KIVI_BUF_V_CODES] = U * NG * (G / 8) * D * b;
-    bytes[KIVI_BUF_V_SCALE] = U * NG * (D / G) * G * mb;
-    bytes[KIVI_BUF_V_ZERO] = U * NG * (D / G) * G * mb;
-  }
+  bytes[KIVI_BUF_K_CODES] = U * NG * (size_t)kivi::rec_bytes(g->bits, g->meta_format);
+  for (int i = KIVI_BUF_K_SCALE; i <= KIVI_BUF_V_ZERO; ++i) bytes[i] = 0;
   bytes[KIVI_BUF_K_RES] = U * slots * D * 2;
   bytes[KIVI_BUF_V_RES] = U * slots * D * 2;
   return KIVI_OK;
@@ -238,9 +225,8 @@ kivi_status kivi_quantize_prefill(const kivi_geom *g, kivi_cache *c, const uint1
     a.src_tok0 = 0;
     a.n_groups = n_q / G; a.n_units = U; a.dst_g0 = 0;
     a.max_tokens = g->max_tokens; a.n_groups_cap = g->max_tokens / G;
-    a.k_codes = c->k_codes; a.k_scale = c->k_scale; a.k_zero = c->k_zero;
-    a.v_codes = c->v_codes; a.v_scale = c->v_scale; a.v_zero = c->v_zero;
-    a.records = records(g);
+    a.k_codes = c->k_codes;
+    a.valu_k = valu_k(g);
     if ((st = hip_status(kivi::launch_quantize(g->bits, g->meta_format, a, s))) != KIVI_OK) return st;
   }
   if (r > 0) {
@@ -385,9 +371,8 @@ kivi_status ragged_prefill_impl(const kivi_geom *g, const kivi_cache *c, const k
     a.src_tok0 = 0;
     a.n_groups = nq_max / G; a.n_units = (int)units_of(g); a.dst_g0 = 0;
     a.max_tokens = g->max_tokens; a.n_groups_cap = g->max_tokens / G;
-    a.k_codes = c->k_codes; a.k_scale = c->k_scale; a.k_zero = c->k_zero;
-    a.v_codes = c->v_codes; a.v_scale = c->v_scale; a.v_zero = c->v_zero;
-    a.records = records(g);
+    a.k_codes = c->k_codes;
+    a.valu_k = valu_k(g);
     a.seq_lens = seq_lens;
     a.kv_heads = g->kv_heads; a.residual = R; a.slots = slots; a.stride = stride;
     a.pages = pm;
@@ -422,9 +407,8 @@ kivi_status ragged_step_impl(const kivi_geom *g, const kivi_cache *c, const kivi
   f.src_unit_stride = (long long)slots * g->head_dim;
   f.n_groups = 1; f.n_units = (int)units_of(g);
   f.max_tokens = g->max_tokens; f.n_groups_cap = g->max_tokens / G;
-  f.k_codes = c->k_codes; f.k_scale = c->k_scale; f.k_zero = c->k_zero;
-  f.v_codes = c->v_codes; f.v_scale = c->v_scale; f.v_zero = c->v_zero;
-  f.records = records(g);
+  f.k_codes = c->k_codes;
+  f.valu_k = valu_k(g);
   f.state = state_in;
   f.kv_heads = g->kv_heads; f.residual = g->residual; f.slots = slots;
   f.pages = pm;
@@ -446,9 +430,6 @@ kivi_status paged_map(const kivi_geom *g, const kivi_paged_cache *pc, kivi::Page
                       kivi_cache &c) {
   if (!pc) return KIVI_E_NULL;
   if (!pc->k_codes || !pc->k_res || !pc->v_res || !pc->block_table) return KIVI_E_NULL;
-  if (!records(g) &&
-      (!pc->k_scale || !pc->k_zero || !pc->v_codes || !pc->v_scale || !pc->v_zero))
-    return KIVI_E_NULL;
   size_t bytes[8];
   int32_t max_pages = 0;
   kivi_status st = kivi_paged_layout(g, pc->page_groups, pc->num_pages, bytes, &max_pages);
@@ -500,27 +481,15 @@ kivi_status kivi_paged_layout(const kivi_geom *g, int32_t page_groups, int32_t n
   if (page_groups < 1 || page_groups > (1 << 20) || (page_groups & (page_groups - 1)) != 0 ||
       num_pages < 1)
     return KIVI_E_UNSUPPORTED;
-  const size_t D = (size_t)g->head_dim, G = (size_t)g->group, b = (size_t)g->bits;
+  const size_t D = (size_t)g->head_dim;
   const size_t slots = (size_t)(g->residual + g->group);
-  const size_t mb = g->meta_format == KIVI_META_FP16_BF16 ? 2 : 4;
   const double groups = (double)num_pages * g->kv_heads * page_groups;
-  // every pool is addressed with 32-bit offsets that must stay below 2^31
+  // the pool is addressed with 32-bit offsets that must stay below 2^31
   const size_t rec = (size_t)kivi::rec_bytes(g->bits, g->meta_format);
-  if (records(g) ? groups * rec >= 2147483648.0
-                 : (groups * G * D * b / 8 >= 2147483648.0 || groups * D * mb >= 2147483648.0))
-    return KIVI_E_UNSUPPORTED;
+  if (groups * rec >= 2147483648.0) return KIVI_E_UNSUPPORTED;
   const size_t n = (size_t)groups;
-  if (records(g)) {
-    bytes[KIVI_BUF_K_CODES] = n * rec;
-    for (int i = KIVI_BUF_K_SCALE; i <= KIVI_BUF_V_ZERO; ++i) bytes[i] = 0;
-  } else {
-    bytes[KIVI_BUF_K_CODES] = n * G * D * b / 8;
-    bytes[KIVI_BUF_K_SCALE] = n * D * mb;
-    bytes[KIVI_BUF_K_ZERO] = n * D * mb;
-    bytes[KIVI_BUF_V_CODES] = n * G * D * b / 8;
-    bytes[KIVI_BUF_V_SCALE] = n * D * mb;
-    bytes[KIVI_BUF_V_ZERO] = n * D * mb;
-  }
+  bytes[KIVI_BUF_K_CODES] = n * rec;
+  for (int i = KIVI_BUF_K_SCALE; i <= KIVI_BUF_V_ZERO; ++i) bytes[i] = 0;
   bytes[KIVI_BUF_K_RES] = (size_t)units_of(g) * slots * D * 2;
   bytes[KIVI_BUF_V_RES] = (size_t)units_of(g) * slots * D * 2;
   if (max_pages) {

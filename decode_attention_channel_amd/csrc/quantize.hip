@@ -85,13 +85,19 @@ __device__ __forceinline__ float max_x32(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-// Byte offsets inside a group record (kivi_internal.h).  K piece: token row
-// t, 32-channel block j; V cell: octet o, channels 4 c4 .. 4 c4 + 3; scale /
+// Byte offsets inside a group record (kivi_internal.h).  K piece of the
+// MFMA roles: token row t, 32-channel block j; of the VALU roles: token row
+// t, 16-channel block c.  V cell: octet o, channels 4 c4 .. 4 c4 + 3; scale /
 // zero value v (0..127) of array i (0 k_scale, 1 k_zero, 2 v_scale, 3 v_zero).
 template <int BITS>
 __device__ __forceinline__ int rec_k_piece(int t, int j) {
   const int lane = 16 * j + 4 * (t >> 3) + (t & 3), tile = (t >> 2) & 1;
   return BITS == 2 ? lane * 16 + tile * 8 : tile * kPlaneBytes + lane * 16;
+}
+template <int BITS>
+__device__ __forceinline__ int rec_k_piece_valu(int t, int c) {
+  const int lane = 8 * (t >> 2) + c, r = t & 3;
+  return BITS == 2 ? lane * 16 + r * 4 : (r >> 1) * kPlaneBytes + lane * 16 + (r & 1) * 8;
 }
 template <int BITS>
 __device__ __forceinline__ int rec_v_cell(int o, int c4) {
@@ -138,7 +144,7 @@ __device__ __forceinline__ void key_group(const QuantizeArgs &a, int u, int gl,
   uint32_t sb0, sb1;
   group_params<BITS, META>(mn0, mx0, sc0, inv0, sb0);
   group_params<BITS, META>(mn1, mx1, sc1, inv1, sb1);
-  if (h == 0 && a.records) {
+  if (h == 0) {
     uint8_t *rec = a.k_codes + slot * rec_bytes(BITS, META);
     const int c = cb + 2 * p;   // channels c, c + 1: one lane's value pair
     if constexpr (META == 1) {
@@ -148,16 +154,6 @@ __device__ __forceinline__ void key_group(const QuantizeArgs &a, int u, int gl,
     } else {
       *reinterpret_cast<float2 *>(rec + rec_meta<BITS, META>(0, c)) = make_float2(sc0, sc1);
       *reinterpret_cast<float2 *>(rec + rec_meta<BITS, META>(1, c)) = make_float2(mn0, mn1);
-    }
-  } else if (h == 0) {
-    const long long m = slot * D + cb;   // element index of channel cb
-    if constexpr (META == 1) {
-      reinterpret_cast<uint32_t *>(static_cast<uint16_t *>(a.k_scale) + m)[p] = sb0 | (sb1 << 16);
-      reinterpret_cast<uint32_t *>(static_cast<uint16_t *>(a.k_zero) + m)[p] =
-          zero_bits(mn0) | (zero_bits(mn1) << 16);
-    } else {
-      reinterpret_cast<float2 *>(static_cast<float *>(a.k_scale) + m)[p] = make_float2(sc0, sc1);
-      reinterpret_cast<float2 *>(static_cast<float *>(a.k_zero) + m)[p] = make_float2(mn0, mn1);
     }
   }
 #pragma unroll
@@ -170,19 +166,32 @@ __device__ __forceinline__ void key_group(const QuantizeArgs &a, int u, int gl,
   const int row = lane >> 1, c32 = 32 * (lane & 1);
   const uint4 b0 = *reinterpret_cast<const uint4 *>(tile + row * 64 + c32);
   const uint4 b1 = *reinterpret_cast<const uint4 *>(tile + row * 64 + c32 + 16);
-  uint8_t *dst = a.records
-                     ? a.k_codes + slot * rec_bytes(BITS, META) + rec_k_piece<BITS>(row, (cb + c32) / 32)
-                     : a.k_codes + (slot * G + row) * KROW + (cb + c32) * BITS / 8;
+  // the packed row piece: 32 channels of token `row` (channels 16h..16h+15
+  // in word(s) h of the piece)
+  uint8_t *rec = a.k_codes + slot * rec_bytes(BITS, META);
+  const int j = (cb + c32) / 32;
   if constexpr (BITS == 2) {
     const uint32_t w0 = pack4x2(b0.x) | (pack4x2(b0.y) << 8) | (pack4x2(b0.z) << 16) |
                         (pack4x2(b0.w) << 24);
     const uint32_t w1 = pack4x2(b1.x) | (pack4x2(b1.y) << 8) | (pack4x2(b1.z) << 16) |
                         (pack4x2(b1.w) << 24);
-    *reinterpret_cast<uint2 *>(dst) = make_uint2(w0, w1);
+    if (a.valu_k) {
+      *reinterpret_cast<uint32_t *>(rec + rec_k_piece_valu<BITS>(row, 2 * j)) = w0;
+      *reinterpret_cast<uint32_t *>(rec + rec_k_piece_valu<BITS>(row, 2 * j + 1)) = w1;
+    } else {
+      *reinterpret_cast<uint2 *>(rec + rec_k_piece<BITS>(row, j)) = make_uint2(w0, w1);
+    }
   } else {
-    *reinterpret_cast<uint4 *>(dst) =
-        make_uint4(pack4x4(b0.x) | (pack4x4(b0.y) << 16), pack4x4(b0.z) | (pack4x4(b0.w) << 16),
-                   pack4x4(b1.x) | (pack4x4(b1.y) << 16), pack4x4(b1.z) | (pack4x4(b1.w) << 16));
+    const uint2 h0 = make_uint2(pack4x4(b0.x) | (pack4x4(b0.y) << 16),
+                                pack4x4(b0.z) | (pack4x4(b0.w) << 16));
+    const uint2 h1 = make_uint2(pack4x4(b1.x) | (pack4x4(b1.y) << 16),
+                                pack4x4(b1.z) | (pack4x4(b1.w) << 16));
+    if (a.valu_k) {
+      *reinterpret_cast<uint2 *>(rec + rec_k_piece_valu<BITS>(row, 2 * j)) = h0;
+      *reinterpret_cast<uint2 *>(rec + rec_k_piece_valu<BITS>(row, 2 * j + 1)) = h1;
+    } else {
+      *reinterpret_cast<uint4 *>(rec + rec_k_piece<BITS>(row, j)) = make_uint4(h0.x, h0.y, h1.x, h1.y);
+    }
   }
   __builtin_amdgcn_wave_barrier();   // tile reads done before the next group's writes
 }
@@ -240,7 +249,7 @@ __device__ __forceinline__ void value_group(const QuantizeArgs &a, int u, int gl
   float sc, inv;
   uint32_t sb;
   group_params<BITS, META>(mn, mx, sc, inv, sb);
-  if (a.records) {
+  {
     uint8_t *rec = a.k_codes + slot * rec_bytes(BITS, META);
     const int v = q * G + 16 * part + r;   // value index within the group
     if constexpr (META == 1) {
@@ -249,15 +258,6 @@ __device__ __forceinline__ void value_group(const QuantizeArgs &a, int u, int gl
     } else {
       *reinterpret_cast<float *>(rec + rec_meta<BITS, META>(2, v)) = sc;
       *reinterpret_cast<float *>(rec + rec_meta<BITS, META>(3, v)) = mn;
-    }
-  } else {
-    const long long mi = (slot * (D / G) + q) * G + 16 * part + r;
-    if constexpr (META == 1) {
-      static_cast<uint16_t *>(a.v_scale)[mi] = (uint16_t)sb;
-      static_cast<uint16_t *>(a.v_zero)[mi] = (uint16_t)zero_bits(mn);
-    } else {
-      static_cast<float *>(a.v_scale)[mi] = sc;
-      static_cast<float *>(a.v_zero)[mi] = mn;
     }
   }
   uint32_t cw[8];
@@ -279,9 +279,7 @@ __device__ __forceinline__ void value_group(const QuantizeArgs &a, int u, int gl
 #pragma unroll
     for (int i = 0; i < 4; ++i) cell[i] |= ((w >> (8 * i)) & 0xFFu) << (BITS * k);
   }
-  uint8_t *dst = a.records
-                     ? a.k_codes + slot * rec_bytes(BITS, META) + rec_v_cell<BITS>(2 * part + o, c4)
-                     : a.v_codes + ((slot * (G / 8) + 2 * part + o) * D + 4 * c4) * BITS;
+  uint8_t *dst = a.k_codes + slot * rec_bytes(BITS, META) + rec_v_cell<BITS>(2 * part + o, c4);
   if constexpr (BITS == 2) {
     *reinterpret_cast<uint2 *>(dst) = make_uint2(cell[0] | (cell[1] << 16), cell[2] | (cell[3] << 16));
   } else {

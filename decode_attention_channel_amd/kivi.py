@@ -160,30 +160,20 @@ def _ptr(t: torch.Tensor, dtype, shape=None, name="tensor") -> ctypes.c_void_p:
     return ctypes.c_void_p(t.data_ptr())
 
 
-def grouped(g: Geom) -> bool:
-    """True when the cache keeps its quantised history as group records
-    (q_per_kv >= 2; kivi.h)."""
-    return g.q_per_kv >= 2
-
-
 def record_bytes(g: Geom) -> int:
     return 1024 * (g.bits + (1 if g.meta_format == META_FP16_BF16 else 2))
 
 
 def _group_shapes(g: Geom) -> dict:
     """(shape, dtype) of one group's part of each of the six history buffers
-    (group records: all in k_codes, the other five empty)."""
-    D, b, G = g.head_dim, g.bits, g.group
+    (group records: all in k_codes, the other five empty; they keep the
+    scale and zero dtypes)."""
     m16 = g.meta_format == META_FP16_BF16
     st = torch.float16 if m16 else torch.float32   # scale
     zt = torch.bfloat16 if m16 else torch.float32  # zero
-    if grouped(g):
-        return {"k_codes": ((record_bytes(g),), torch.uint8), "k_scale": (None, st),
-                "k_zero": (None, zt), "v_codes": (None, torch.uint8), "v_scale": (None, st),
-                "v_zero": (None, zt)}
-    return {"k_codes": ((G, D * b // 8), torch.uint8), "k_scale": ((D,), st), "k_zero": ((D,), zt),
-            "v_codes": ((G // 8, D, b), torch.uint8), "v_scale": ((D // G, G), st),
-            "v_zero": ((D // G, G), zt)}
+    return {"k_codes": ((record_bytes(g),), torch.uint8), "k_scale": (None, st),
+            "k_zero": (None, zt), "v_codes": (None, torch.uint8), "v_scale": (None, st),
+            "v_zero": (None, zt)}
 
 
 def _history_shapes(g: Geom, lead: tuple) -> dict:
@@ -192,29 +182,30 @@ def _history_shapes(g: Geom, lead: tuple) -> dict:
     return {n: ((0,) if sh is None else lead + sh, dt) for n, (sh, dt) in _group_shapes(g).items()}
 
 
-def _np_bits(t: torch.Tensor) -> np.ndarray:
-    """numpy copy; 16-bit floats as their uint16 bit patterns"""
-    if t.dtype in (torch.float16, torch.bfloat16):
-        t = t.view(torch.int16)
-        return t.cpu().numpy().view(np.uint16)
-    return t.cpu().numpy()
-
-
-def records_to_arrays(rec: np.ndarray, bits: int, meta: int) -> dict:
+def records_to_arrays(rec: np.ndarray, bits: int, meta: int, valu_k: bool) -> dict:
     """Group records [N][bytes] -> per-array layout of N groups (kivi.h):
     k_codes [N][G][D*b/8], k_scale/k_zero [N][D], v_codes [N][G/8][D][b],
-    v_scale/v_zero [N][D/G][G]; scale/zero as fp32 or as 16-bit patterns."""
+    v_scale/v_zero [N][D/G][G]; scale/zero as fp32 or as 16-bit patterns.
+    valu_k: K codes in the lane roles of q_per_kv = 1, else of q_per_kv >= 2."""
     N = rec.shape[0]
     r = rec.reshape(N, -1, 64, 16)
     t = np.arange(32)[:, None]
-    j = np.arange(4)[None, :]
-    lane = 16 * j + 4 * (t >> 3) + (t & 3)              # [32][4]
-    tile = np.broadcast_to((t >> 2) & 1, lane.shape)
-    if bits == 2:
-        kc = r[:, 0][:, lane[..., None], 8 * tile[..., None] + np.arange(8)]   # [N][32][4][8]
-    else:
-        kc = r[:, tile, lane, :]                                                # [N][32][4][16]
-    kc = kc.reshape(N, 32, 4 * 8 * bits // 2)
+    if valu_k:   # lane 8 (t >> 2) + c: 16-channel block c of row t, 2b bytes
+        c = np.arange(8)[None, :]
+        lane = 8 * (t >> 2) + c                             # [32][8]
+        per = 16 // (2 * bits)                              # pieces per lane and plane
+        rr = np.broadcast_to(t & 3, lane.shape)
+        kc = r[:, (rr // per)[..., None], lane[..., None],
+               (2 * bits * (rr % per))[..., None] + np.arange(2 * bits)]       # [N][32][8][2b]
+    else:        # lane 16 j + 4 (t >> 3) + (t & 3): 32-channel block j of row t
+        j = np.arange(4)[None, :]
+        lane = 16 * j + 4 * (t >> 3) + (t & 3)              # [32][4]
+        tile = np.broadcast_to((t >> 2) & 1, lane.shape)
+        if bits == 2:
+            kc = r[:, 0][:, lane[..., None], 8 * tile[..., None] + np.arange(8)]   # [N][32][4][8]
+        else:
+            kc = r[:, tile, lane, :]                                                # [N][32][4][16]
+    kc = kc.reshape(N, 32, 16 * bits)
     o = np.arange(4)[:, None]
     c4 = np.arange(32)[None, :]
     vl = 16 * o + (c4 >> 1)                                                     # [4][32]
@@ -242,11 +233,9 @@ class Cache:
     def __init__(self, g: Geom, device=None):
         device = torch.device("cuda", torch.cuda.current_device()) if device is None else device
         sizes = cache_layout(g)
-        B, H, T, D, b, G = g.batch, g.kv_heads, g.max_tokens, g.head_dim, g.bits, g.group
-        NG, S = T // G, g.residual + g.group
+        B, H, D = g.batch, g.kv_heads, g.head_dim
+        NG, S = g.max_tokens // g.group, g.residual + g.group
         shapes = _history_shapes(g, (B, H, NG))
-        if not grouped(g):   # K codes of a unit as token rows [T][D*b/8]
-            shapes["k_codes"] = ((B, H, T, D * b // 8), torch.uint8)
         shapes["k_res"] = ((B, H, S, D), torch.bfloat16)
         shapes["v_res"] = ((B, H, S, D), torch.bfloat16)
         self.geom = g
@@ -277,14 +266,12 @@ class Cache:
 
     def history(self) -> dict:
         """Host copy of the quantised history in the per-array layout
-        (k_codes [B][H][T][D*b/8], k_scale ..., as numpy arrays), whichever
-        layout the cache keeps (group records when q_per_kv >= 2)."""
+        (k_codes [B][H][T][D*b/8], k_scale ..., as numpy arrays) from the
+        group records the cache keeps."""
         g = self.geom
         B, H, NG = g.batch, g.kv_heads, g.max_tokens // g.group
-        if not grouped(g):
-            return {n: _np_bits(getattr(self, n)) for n in BUFFERS[:6]}
         arr = records_to_arrays(self.k_codes.cpu().numpy().reshape(B * H * NG, -1), g.bits,
-                                g.meta_format)
+                                g.meta_format, g.q_per_kv == 1)
         out = {n: a.reshape((B, H, NG) + a.shape[1:]) for n, a in arr.items()}
         out["k_codes"] = out["k_codes"].reshape(B, H, NG * g.group, -1)
         return out
@@ -306,7 +293,7 @@ class PagedCache:
     def __init__(self, g: Geom, page_groups: int, num_pages: int, device=None):
         device = torch.device("cuda", torch.cuda.current_device()) if device is None else device
         sizes, self.max_pages = paged_layout(g, page_groups, num_pages)
-        B, H, D, b, G = g.batch, g.kv_heads, g.head_dim, g.bits, g.group
+        B, H, D = g.batch, g.kv_heads, g.head_dim
         n, S = num_pages * H * page_groups, g.residual + g.group
         shapes = _history_shapes(g, (n,))
         shapes["k_res"] = ((B, H, S, D), torch.bfloat16)
@@ -322,13 +309,11 @@ class PagedCache:
                               num_pages)
 
     def pool_history(self) -> dict:
-        """Host copy of the pools in the per-array per-slot layout (k_codes
-        [slots][G][D*b/8], k_scale [slots][D], ...), whichever layout the
-        pools keep."""
+        """Host copy of the pool in the per-array per-slot layout (k_codes
+        [slots][G][D*b/8], k_scale [slots][D], ...) from its group records."""
         g = self.geom
-        if not grouped(g):
-            return {n: _np_bits(getattr(self, n)) for n in BUFFERS[:6]}
-        return records_to_arrays(self.k_codes.cpu().numpy(), g.bits, g.meta_format)
+        return records_to_arrays(self.k_codes.cpu().numpy(), g.bits, g.meta_format,
+                                 g.q_per_kv == 1)
 
     def slot(self, b: int, h: int, g: int, table=None) -> int:
         """Pool slot of group g of (sequence b, kv head h); -1 without a page."""

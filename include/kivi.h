@@ -85,29 +85,36 @@
  * Byte layout of the cache buffers (part of the contract: packed codes and
  * scale/zero are compared byte for byte with an independent CPU oracle)
  * ------------------------------------------------------------------------
- *  k_codes  uint8 [B][H][T][D*b/8]   token row t holds channel c at byte
- *           c*b/8, bits [(c*b)%8, (c*b)%8 + b)  (LSB first).
- *  k_scale, k_zero  [B][H][NG][D]          (group g, channel c)
- *  v_codes  uint8 [B][H][NG][G/8][D][b]     group g, octet o (tokens
- *           8o..8o+7 of the group), channel c: b bytes holding the 8 codes
- *           of that channel, token 8o+k at bits [k*b, k*b + b) (LSB first).
- *  v_scale, v_zero  [B][H][NG][D/G][G]     (group g, channel group j,
- *           token i of the group)
+ *  The quantised history of a group is defined in the per-array form
+ *  below; the cache stores each group as one record (further below), a
+ *  fixed permutation of those bytes.
+ *  k_codes  uint8 [G][D*b/8]   token row t of the group holds channel c at
+ *           byte c*b/8, bits [(c*b)%8, (c*b)%8 + b)  (LSB first).
+ *  k_scale, k_zero  [D]              (channel c)
+ *  v_codes  uint8 [G/8][D][b]        octet o (tokens 8o..8o+7 of the group),
+ *           channel c: b bytes holding the 8 codes of that channel, token
+ *           8o+k at bits [k*b, k*b + b) (LSB first).
+ *  v_scale, v_zero  [D/G][G]         (channel group j, token i of the group)
  *           Element type by geom.meta_format: KIVI_META_FP32 -- fp32 scale and
  *           fp32 zero; KIVI_META_FP16_BF16 -- fp16 scale bits and bf16 zero
  *           bits (uint16_t), see "16-bit scale/zero" below.
- *  Group records (q_per_kv >= 2): the quantised history is one buffer,
- *           k_codes (kivi_cache_layout gives the five other history buffers
- *           size 0; they may be NULL), of one record per group:
- *           uint8 [B][H][NG][P * 1024], P = b + 2 (fp32 scale/zero) or b + 1
- *           (16-bit).  A record is a fixed permutation of the group's bytes
- *           in the layout above, in the order one 64-lane wave of the decode
- *           kernel reads them: plane p (1024 bytes) holds 16 bytes for each
- *           lane l at p*1024 + 16*l.
- *             K codes, planes [0, b/2): lane 16*j + 4*(t>>3) + (t&3) holds
- *               bytes [j*4*b, (j+1)*4*b) of k_codes token rows t (first) and
- *               t+4 (second) of the group, t with (t>>2)&1 == 0 (b = 2: 8
- *               bytes each, one plane; b = 4: one plane each).
+ *  Group records: the quantised history is one buffer, k_codes
+ *           (kivi_cache_layout gives the five other history buffers size 0;
+ *           their pointers are ignored and may be NULL), of one record per
+ *           group: uint8 [B][H][NG][P * 1024], P = b + 2 (fp32 scale/zero)
+ *           or b + 1 (16-bit).  Bytes are laid out in the order one 64-lane
+ *           wave of the decode kernel reads them: plane p (1024 bytes) holds
+ *           16 bytes for each lane l at p*1024 + 16*l.
+ *             K codes, planes [0, b/2), in the lane roles of the kernel that
+ *               reads them:
+ *               q_per_kv >= 2: lane 16*j + 4*(t>>3) + (t&3) holds bytes
+ *               [j*4*b, (j+1)*4*b) of k_codes token rows t (first) and t+4
+ *               (second), t with (t>>2)&1 == 0 (b = 2: 8 bytes each, one
+ *               plane; b = 4: one plane each).
+ *               q_per_kv = 1: lane 8*k + c holds bytes [c*2*b, (c+1)*2*b)
+ *               of token rows 4k .. 4k+3 in that order (b = 2: 4 bytes each,
+ *               one plane; b = 4: 8 bytes each, rows 4k, 4k+1 in plane 0
+ *               and 4k+2, 4k+3 in plane 1).
  *             V codes, planes [b/2, b): lane 16*o + c/8 holds the 8*b bytes
  *               of octet o, channels c..c+7 (c a multiple of 8); b = 4: the
  *               first 16 bytes in plane 2, the other 16 in plane 3.
@@ -186,12 +193,12 @@ typedef struct {
 /* The cache: eight caller-owned device buffers laid out as described above,
  * plus three host-side counters that the calls below update. */
 typedef struct {
-  uint8_t  *k_codes;
-  void     *k_scale;    /* fp32, or fp16 bits (meta_format)                */
-  void     *k_zero;     /* fp32, or bf16 bits                              */
-  uint8_t  *v_codes;
-  void     *v_scale;
-  void     *v_zero;
+  uint8_t  *k_codes;    /* the group records                           */
+  void     *k_scale;    /* unused (size 0): may be NULL                    */
+  void     *k_zero;     /* unused                                          */
+  uint8_t  *v_codes;    /* unused                                          */
+  void     *v_scale;    /* unused                                          */
+  void     *v_zero;     /* unused                                          */
   uint16_t *k_res;
   uint16_t *v_res;
   int32_t   n_q;        /* tokens in the quantised history (multiple of G) */
@@ -207,8 +214,8 @@ enum {
 };
 
 /* Byte sizes of the eight cache buffers for `geom`, in the order of the
- * KIVI_BUF_* enum (q_per_kv >= 2: the group records in K_CODES and 0 for
- * K_SCALE .. V_ZERO, whose pointers the calls then ignore and accept NULL).
+ * KIVI_BUF_* enum: the group records in K_CODES and 0 for K_SCALE ..
+ * V_ZERO, whose pointers the calls ignore and accept NULL.
  * Host-only, touches no device.
  * Errors: KIVI_E_NULL, KIVI_E_GEOMETRY, KIVI_E_UNSUPPORTED. */
 kivi_status kivi_cache_layout(const kivi_geom *geom, size_t bytes_out[8]);
@@ -372,13 +379,9 @@ kivi_status kivi_ragged_decode_step(const kivi_geom *geom, const kivi_cache *cac
  * (page_groups * 32 tokens); one page holds those groups for every kv head
  * of one sequence.  Sequence b's group g lives in page block_table[b][g /
  * page_groups]; inside the pools, (page p, kv head h, group i of the page)
- * is group slot s = (p * H + h) * page_groups + i, and every pool keeps the
- * per-group layout of kivi_cache with the unit block replaced by slots:
- *   k_codes  [slots][G][D*b/8]      k_scale, k_zero  [slots][D]
- *   v_codes  [slots][G/8][D][b]     v_scale, v_zero  [slots][D/G][G]
- * (scale/zero in the geom's meta_format); with q_per_kv >= 2 there is one
- * pool, k_codes [slots][record bytes] of group records, and the five other
- * pool pointers are ignored (may be NULL).  The residual rings are not paged:
+ * is group slot s = (p * H + h) * page_groups + i.  The history is one
+ * pool, k_codes [slots][record bytes] of group records (as in kivi_cache);
+ * the five other pool pointers are ignored (may be NULL).  The residual rings are not paged:
  * k_res, v_res are [B][H][R+G][D] as in kivi_cache.  Lengths are per
  * sequence, in the same device state as the mixed-length calls above.
  *
@@ -394,12 +397,12 @@ kivi_status kivi_ragged_decode_step(const kivi_geom *geom, const kivi_cache *cac
  * one after it was written reads as zeros.
  * ------------------------------------------------------------------------ */
 typedef struct {
-  uint8_t  *k_codes;            /* pools (kivi_paged_layout sizes)          */
-  void     *k_scale;
-  void     *k_zero;
-  uint8_t  *v_codes;
-  void     *v_scale;
-  void     *v_zero;
+  uint8_t  *k_codes;            /* record pool (kivi_paged_layout size)     */
+  void     *k_scale;            /* unused (size 0): may be NULL             */
+  void     *k_zero;             /* unused                                   */
+  uint8_t  *v_codes;            /* unused                                   */
+  void     *v_scale;            /* unused                                   */
+  void     *v_zero;             /* unused                                   */
   uint16_t *k_res;              /* [B][H][R+G][D] rings, as in kivi_cache  */
   uint16_t *v_res;
   const int32_t *block_table;   /* device [B][max_pages]                    */
@@ -408,9 +411,8 @@ typedef struct {
 } kivi_paged_cache;
 
 /* Byte sizes of the buffers of a paged cache (indexed by kivi_buffer: the
- * six pools, then the two rings; q_per_kv >= 2: the record pool, five zeros,
- * the rings) and the block table's row length.  Every pool must stay below
- * 2 GiB (its offsets are 32-bit).
+ * record pool, five zeros, the two rings) and the block table's row length.
+ * The record pool must stay below 2 GiB (its offsets are 32-bit).
  * Errors: KIVI_E_NULL (bytes), KIVI_E_GEOMETRY, KIVI_E_UNSUPPORTED (geom
  *         outside the supported set, page_groups not a power of two in
  *         [1, 2^20], num_pages < 1, or a pool of 2 GiB or more). */

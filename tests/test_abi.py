@@ -37,19 +37,15 @@ def _g(**kw):
 @pytest.mark.parametrize("bits", [2, 4])
 def test_layout_sizes(bits):
     U, T, D, NG, S = 6, 1024, 128, 32, 160
-    # one query head per kv head: per-array layout
-    g = _g(bits=bits, q_per_kv=1)
-    assert kivi.cache_layout(g) == [U * T * D * bits // 8, U * NG * D * 4, U * NG * D * 4,
-                                    U * NG * 4 * D * bits, U * NG * 4 * 32 * 4,
-                                    U * NG * 4 * 32 * 4, U * S * D * 2, U * S * D * 2]
-    assert kivi.workspace_size(g) == 256 + U * (NG // 4 + 1) * 1 * 132 * 4
-    # GQA: one record per group in the K_CODES buffer, of the same bytes
-    # (codes, fp32 scale/zero) in 1 KiB planes
-    g = _g(bits=bits)
+    # one record per group in the K_CODES buffer, of the bytes of the
+    # per-array layout (codes, fp32 scale/zero) in 1 KiB planes, for every
+    # number of query heads per kv head
     rec = 1024 * (bits + 2)
     assert rec == 32 * D * bits // 8 * 2 + 4 * D * 4
-    assert kivi.cache_layout(g) == [U * NG * rec, 0, 0, 0, 0, 0, U * S * D * 2, U * S * D * 2]
-    assert kivi.workspace_size(g) == 256 + U * (NG // 4 + 1) * 4 * 132 * 4
+    for qpk in (1, 4):
+        g = _g(bits=bits, q_per_kv=qpk)
+        assert kivi.cache_layout(g) == [U * NG * rec, 0, 0, 0, 0, 0, U * S * D * 2, U * S * D * 2]
+        assert kivi.workspace_size(g) == 256 + U * (NG // 4 + 1) * qpk * 132 * 4
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -81,14 +77,11 @@ def test_host_validation_before_any_device_work():
     # NULL geometry / cache / buffers / inputs
     assert _call("kivi_quantize_prefill", None, P(_cache_struct()), fake, fake, 10, None) == 1
     assert _call("kivi_quantize_prefill", P(g), None, fake, fake, 10, None) == 1
-    # GQA caches need K_CODES (the records) and the rings; one query head per
-    # kv head needs all eight buffers
-    for i in (0, 6, 7):
-        assert _call("kivi_quantize_prefill", P(g), P(_cache_struct(null=i)), fake, fake, 10,
-                     None) == 1
-    for i in range(8):
-        assert _call("kivi_quantize_prefill", P(_g(q_per_kv=1).c()), P(_cache_struct(null=i)),
-                     fake, fake, 10, None) == 1
+    # a cache needs K_CODES (the records) and the rings
+    for geom in (g, _g(q_per_kv=1).c()):
+        for i in (0, 6, 7):
+            assert _call("kivi_quantize_prefill", P(geom), P(_cache_struct(null=i)), fake, fake,
+                         10, None) == 1
     assert _call("kivi_quantize_prefill", P(g), P(_cache_struct()), None, fake, 10, None) == 1
     # sequence length and capacity
     assert _call("kivi_quantize_prefill", P(g), P(_cache_struct()), fake, fake, 0, None) == 4
@@ -141,10 +134,9 @@ def test_decode_step_validation_before_any_device_work():
     assert step(c, q=None) == 1 and step(c, out=None) == 1
     assert step(c, ws=None) == 7 and step(c, nbytes=ws_need - 1) == 7
     assert step(c, scale=float("inf")) == 2
-    for i in (0, 6, 7):   # GQA: records and rings
-        assert step(_cache_struct(n_q=64, n_res=140, null=i)) == 1
     g1 = _g(q_per_kv=1)
-    for i in range(8):
+    for i in (0, 6, 7):   # records and rings
+        assert step(_cache_struct(n_q=64, n_res=140, null=i)) == 1
         assert step(_cache_struct(n_q=64, n_res=140, null=i), geom=g1.c(),
                     nbytes=kivi.workspace_size(g1)) == 1
     # a full ring on entry, as for kivi_append_token
@@ -183,13 +175,13 @@ def test_dense_attention_validation_before_any_device_work():
 
 
 def test_16bit_meta_layout_and_rejected_formats():
-    g = _g(meta_format=kivi.META_FP16_BF16, q_per_kv=1)
     U, T, D, NG, S = 6, 1024, 128, 32, 160
-    assert kivi.cache_layout(g) == [U * T * D * 2 // 8, U * NG * D * 2, U * NG * D * 2,
-                                    U * NG * 4 * D * 2, U * NG * 4 * 32 * 2, U * NG * 4 * 32 * 2,
-                                    U * S * D * 2, U * S * D * 2]
-    g = _g(meta_format=kivi.META_FP16_BF16)
-    assert kivi.cache_layout(g) == [U * NG * 3072, 0, 0, 0, 0, 0, U * S * D * 2, U * S * D * 2]
+    # 2-bit records with 16-bit scale/zero: two code planes, one meta plane
+    assert 3072 == 32 * D * 2 // 8 * 2 + 4 * D * 2
+    for qpk in (1, 4):
+        g = _g(meta_format=kivi.META_FP16_BF16, q_per_kv=qpk)
+        assert kivi.cache_layout(g) == [U * NG * 3072, 0, 0, 0, 0, 0, U * S * D * 2,
+                                        U * S * D * 2]
     for bad in (2, -1):
         with pytest.raises(kivi.KiviError) as e:
             kivi.cache_layout(_g(meta_format=bad))
@@ -209,7 +201,7 @@ def test_ragged_calls_validation_before_any_device_work():
     assert _call("kivi_ragged_prefill", P(g), P(c), fake, fake, 0, fake, fake, None) == 4
     assert _call("kivi_ragged_prefill", P(g), P(_cache_struct(null=0)), fake, fake, 100, fake,
                  fake, None) == 1
-    assert _call("kivi_ragged_prefill", P(_g(q_per_kv=1).c()), P(_cache_struct(null=3)), fake,
+    assert _call("kivi_ragged_prefill", P(_g(q_per_kv=1).c()), P(_cache_struct(null=7)), fake,
                  fake, 100, fake, fake, None) == 1
 
     def step(geom=g, si=fake, so=fake2, nbytes=ws_need):
@@ -232,18 +224,12 @@ def _paged_struct(P=4, pages=20, null=None):
 @pytest.mark.parametrize("bits,meta", [(2, 0), (4, 1)])
 def test_paged_layout_sizes(bits, meta):
     n = 10 * 3 * 4                         # pages * kv heads * groups per page
-    mb = 2 if meta else 4
-    g = _g(bits=bits, meta_format=meta, q_per_kv=1)
-    sizes, max_pages = kivi.paged_layout(g, 4, 10)
-    assert max_pages == 8                  # 32 groups of capacity / 4
-    assert sizes == [n * 32 * 128 * bits // 8, n * 128 * mb, n * 128 * mb,
-                     n * 32 * 128 * bits // 8, n * 128 * mb, n * 128 * mb,
-                     6 * 160 * 128 * 2, 6 * 160 * 128 * 2]
-    g = _g(bits=bits, meta_format=meta)    # GQA: a pool of group records
-    sizes, max_pages = kivi.paged_layout(g, 4, 10)
-    assert max_pages == 8
-    assert sizes == [n * 1024 * (bits + (1 if meta else 2)), 0, 0, 0, 0, 0,
-                     6 * 160 * 128 * 2, 6 * 160 * 128 * 2]
+    for qpk in (1, 4):                     # a pool of group records
+        g = _g(bits=bits, meta_format=meta, q_per_kv=qpk)
+        sizes, max_pages = kivi.paged_layout(g, 4, 10)
+        assert max_pages == 8              # 32 groups of capacity / 4
+        assert sizes == [n * 1024 * (bits + (1 if meta else 2)), 0, 0, 0, 0, 0,
+                         6 * 160 * 128 * 2, 6 * 160 * 128 * 2]
     assert kivi.paged_layout(g, 16, 1)[1] == 2
     assert kivi.paged_layout(g, 64, 1)[1] == 1
 
@@ -261,12 +247,10 @@ def test_paged_calls_validation_before_any_device_work():
     assert _call("kivi_paged_layout", P(g), 4, 10, None, P(mp)) == 1
     assert _call("kivi_paged_layout", P(g), 4, 10, out, None) == 0
     ws_need = kivi.workspace_size(_g())
-    for null in (0, 6, 7, 8):   # GQA: record pool, rings, block table
-        assert _call("kivi_paged_prefill", P(g), P(_paged_struct(null=null)), fake, fake, 100,
-                     fake, fake, None) == 1, null
-    for null in range(9):
-        assert _call("kivi_paged_prefill", P(_g(q_per_kv=1).c()), P(_paged_struct(null=null)),
-                     fake, fake, 100, fake, fake, None) == 1, null
+    for geom in (g, _g(q_per_kv=1).c()):
+        for null in (0, 6, 7, 8):   # record pool, rings, block table
+            assert _call("kivi_paged_prefill", P(geom), P(_paged_struct(null=null)), fake, fake,
+                         100, fake, fake, None) == 1, null
     assert _call("kivi_paged_prefill", P(g), P(_paged_struct(P=6)), fake, fake, 100, fake, fake,
                  None) == 3
     assert _call("kivi_paged_prefill", P(g), P(_paged_struct()), fake, fake, 0, fake, fake,

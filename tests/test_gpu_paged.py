@@ -51,7 +51,7 @@ def _gather(pc, b, table, og1, n_q, n_res, res_start):
     """oracle.Cache (batch 1) of sequence b read out of the device pools."""
     hc = oracle.Cache(og1)
     G, H = og1.group, og1.kv_heads
-    pools = pc.pool_history()   # per-array layout, whichever layout the pools keep
+    pools = pc.pool_history()   # per-array layout, from the group records
     res = {n: to_np(getattr(pc, n)) for n in ("k_res", "v_res")}
     for h in range(H):
         for g in range(n_q // G):
