@@ -24,13 +24,13 @@
 // exactly code * 2^-9; the convert's power-of-two scale (2, 512) restores the
 // integer exactly.
 //
-// GQA (q_per_kv >= 2): q.K^T and P.V run on v_mfma_f32_16x16x32_bf16 with the
-// codes as the A operand (16 tokens x 32 channels for q.K^T, 16 channels x 32
-// tokens for P.V) and the scaled queries / probabilities as the B operand.
-// The B operand is split into bf16 hi + lo parts (relative error ~2^-16), the
-// parts occupying different MFMA columns (q.K^T) or two MFMAs (P.V), so the
-// result carries close to fp32 precision.  MHA (q_per_kv == 1) stays on VALU
-// with fp32 FMAs: one query row is not a dense contraction.
+// q.K^T and P.V run on v_mfma_f32_16x16x32_bf16 with the codes as the A
+// operand (16 tokens x 32 channels for q.K^T, 16 channels x 32 tokens for
+// P.V) and the scaled queries / probabilities of up to 4 query heads of the
+// kv head as the B operand (MHA, one query head per kv head, leaves three
+// head columns idle).  The B operand is split into bf16 hi + lo parts
+// (relative error ~2^-16), the parts occupying different MFMA columns (q.K^T)
+// or two MFMAs (P.V), so the result carries close to fp32 precision.
 #include <float.h>
 #include <math.h>
 
@@ -45,7 +45,6 @@ namespace {
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
-typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2_t;
 
 union Op8 {
   bf16x8_t v;
@@ -73,14 +72,6 @@ __device__ __forceinline__ uint32_t fp4x2_to_bf16x2(uint32_t w) {
 template <bool HI>
 __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 512.0f, HI));
-}
-template <int SEL>
-__device__ __forceinline__ f32x2_t fp4x2_to_f32x2(uint32_t w) {
-  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 2.0f, SEL);
-}
-template <bool HI>
-__device__ __forceinline__ f32x2_t fp8x2_to_f32x2(uint32_t w) {
-  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 512.0f, HI);
 }
 
 // 16 two-bit codes of one word -> two 8-slot bf16 operands (codes 0..7 and
@@ -285,7 +276,7 @@ __device__ __forceinline__ int4 apply_unit_state(DecodeArgs &a, int u) {
   return make_int4(n_q, a.n_res, res_start, flags);
 }
 
-// ------------------------------------------------------ MFMA (GQA) path ---
+// ------------------------------------------------------------ MFMA path ---
 // ---- cross-lane sums / maxima without LDS round trips.  A wave is 4 rows of
 // 16 lanes; permlane16/32 swaps exchange row pairs, so x + swap(x) is the
 // sum over lanes l and l^16 (l^32) in every lane.
@@ -887,7 +878,7 @@ __device__ __forceinline__ WorkRange wave_work(const DecodeArgs &a, int u, int s
   return r;
 }
 
-// GQA decode attention.  Grid (unit, wpu): the `wpu` workgroups of a unit
+// Decode attention, any number of query heads per kv head.  Grid (unit, wpu): the `wpu` workgroups of a unit
 // split its work -- the quantised groups, then the residual in chunks of 32
 // tokens -- into rank-weighted byte shares (wave_work).  Item costs are in
 // KiB: a group (codes + scale/zero) is bits + 2, a residual chunk (32 bf16
@@ -1087,330 +1078,18 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeArgs a) {
   finish_unit<64 * NW>(a, u, &sm.mg.last, next_state);
 }
 
-// ------------------------------------------------------- VALU (MHA) path ---
-// One query head per kv head: q.K^T and P.V are matrix-vector products, so
-// they stay on VALU (fp32 FMAs on the exactly unpacked codes).  Work is split
-// like the GQA path (byte shares of quantised groups and residual chunks,
-// weighted by co-residency rank), with the same load pipeline.  Lane roles
-// for a group of 32 tokens:
-//   q.k:  lane = 8 tb + cb  -- tokens 4tb..4tb+3, channels 16cb..16cb+15
-//   P.V:  lane = 16 oc + cq -- tokens 8oc..8oc+7 (octet oc), channels 8cq..8cq+7
-
-template <int BITS>
-struct ValuRaw {
-  uint32_t kw[4][BITS / 2];   // token rows 4tb + r: 16 channels (2*BITS bytes)
-  uint32_t vw[2 * BITS];      // octet oc, channels 8cq..8cq+7: BITS bytes each
-  uint32_t mw[4][2];          // this lane's 8 bytes of each scale/zero array
-};
-
-// Loads of group g (live == false: out-of-range loads, see load_group).  The
-// record's K planes hold the q.k roles above (lane 8 tb + cb), its V planes
-// the P.V roles (lane 16 oc + cq), as the MFMA path's V planes do.
-template <int BITS, int META, bool PAGED>
-__device__ __forceinline__ void load_valu_group(ValuRaw<BITS> &r, const RecView &v,
-                                                const DecodeArgs &a, int u, int g, bool live) {
-  u32x4_t q[rec_planes(BITS, META)];
-  load_record<BITS, META, PAGED>(q, v, a, u, g, live);
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    if constexpr (BITS == 2) {
-      r.kw[t][0] = q[0][t];
-    } else {
-      r.kw[t][0] = q[t >> 1][2 * (t & 1)];
-      r.kw[t][1] = q[t >> 1][2 * (t & 1) + 1];
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    r.vw[i] = q[BITS / 2][i];
-    if constexpr (BITS == 4) r.vw[4 + i] = q[3][i];
-  }
-  record_meta<BITS, META>(r.mw, q);
-}
-
-struct ValuSmem {
-  float meta[4][4][D];   // [wave] the current group's k_scale, k_zero, v_scale, v_zero
-  float p[4][G];         // [wave] probabilities handed from the q.k to the P.V role
-};
-
-struct ValuState {
-  float oacc[8];         // channels 8cq..8cq+7, partial over this lane's octets
-  float m_run, l_run, z_run;
-};
-
-struct ValuLane {
-  int wave, lane, tb, cb, oc, cq;
-};
-
-// Online-softmax update for the 4 scores of this lane's q.k role, then the
-// hand-over of p to the P.V role: returns p for tokens 8oc..8oc+7.
-__device__ __forceinline__ void valu_softmax(float (&s4)[4], ValuState &st, ValuSmem &sm,
-                                             const ValuLane &L, float (&p8)[8]) {
-  float mx = fmaxf(fmaxf(s4[0], s4[1]), fmaxf(s4[2], s4[3]));
-  mx = xor_max(xor_max(xor_max(mx, 8), 16), 32);
-  const bool need = mx > st.m_run + kRescaleSlack;
-  if (__any(need)) {
-    const float mnew = need ? mx : st.m_run;
-    const float al = st.m_run == kNegInf ? 0.f : fast_exp2(st.m_run - mnew);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) st.oacc[i] *= al;
-    st.l_run *= al;
-    st.z_run *= al;
-    st.m_run = mnew;
-  }
-  float p4[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    p4[r] = fast_exp2(s4[r] - st.m_run);
-    st.l_run += p4[r];
-  }
-  if (L.cb == 0)
-    *reinterpret_cast<float4 *>(&sm.p[L.wave][4 * L.tb]) = make_float4(p4[0], p4[1], p4[2], p4[3]);
-  __builtin_amdgcn_wave_barrier();
-  const float4 x = *reinterpret_cast<const float4 *>(&sm.p[L.wave][8 * L.oc]);
-  const float4 y = *reinterpret_cast<const float4 *>(&sm.p[L.wave][8 * L.oc + 4]);
-  p8[0] = x.x; p8[1] = x.y; p8[2] = x.z; p8[3] = x.w;
-  p8[4] = y.x; p8[5] = y.y; p8[6] = y.z; p8[7] = y.w;
-  __builtin_amdgcn_wave_barrier();
-}
-
-template <int BITS, int META>
-__device__ __forceinline__ void valu_group(const ValuRaw<BITS> &raw, ValuState &st, ValuSmem &sm,
-                                           const float (&qv)[16], const ValuLane &L) {
-  // scale/zero of this group: stage in LDS, read back what each role needs
-  stage_meta<META>(raw.mw, sm.meta[L.wave], L.lane);
-  __builtin_amdgcn_wave_barrier();
-  float sk[16], zk[16], sv[8], zv[8];
-  {
-    const int jv = L.cq >> 2;   // channel group of channels 8cq..8cq+7
-    ld16(&sm.meta[L.wave][0][16 * L.cb], sk);
-    ld16(&sm.meta[L.wave][1][16 * L.cb], zk);
-    ld8(&sm.meta[L.wave][2][jv * G + 8 * L.oc], sv);
-    ld8(&sm.meta[L.wave][3][jv * G + 8 * L.oc], zv);
-  }
-  __builtin_amdgcn_wave_barrier();
-
-  float qs[16], beta = 0.f;
-#pragma unroll
-  for (int c = 0; c < 16; ++c) {
-    qs[c] = qv[c] * sk[c];
-    beta += qv[c] * zk[c];
-  }
-  beta = xor_sum(xor_sum(xor_sum(beta, 1), 2), 4);
-
-  float s4[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    float acc = 0.f;
-    if constexpr (BITS == 2) {
-      const uint32_t w = raw.kw[r][0];
-      const uint32_t x = w & 0x33333333u, y = (w >> 2) & 0x33333333u;
-      // byte k of x: channels 4k, 4k+2 ; of y: 4k+1, 4k+3
-      f32x2_t f;
-      f = fp4x2_to_f32x2<0>(x); acc += qs[0] * f[0] + qs[2] * f[1];
-      f = fp4x2_to_f32x2<0>(y); acc += qs[1] * f[0] + qs[3] * f[1];
-      f = fp4x2_to_f32x2<1>(x); acc += qs[4] * f[0] + qs[6] * f[1];
-      f = fp4x2_to_f32x2<1>(y); acc += qs[5] * f[0] + qs[7] * f[1];
-      f = fp4x2_to_f32x2<2>(x); acc += qs[8] * f[0] + qs[10] * f[1];
-      f = fp4x2_to_f32x2<2>(y); acc += qs[9] * f[0] + qs[11] * f[1];
-      f = fp4x2_to_f32x2<3>(x); acc += qs[12] * f[0] + qs[14] * f[1];
-      f = fp4x2_to_f32x2<3>(y); acc += qs[13] * f[0] + qs[15] * f[1];
-    } else {
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const uint32_t w = raw.kw[r][i];
-        const uint32_t x = w & 0x0F0F0F0Fu, y = (w >> 4) & 0x0F0F0F0Fu;
-        const float *q8 = qs + 8 * i;
-        f32x2_t f;
-        f = fp8x2_to_f32x2<false>(x); acc += q8[0] * f[0] + q8[2] * f[1];
-        f = fp8x2_to_f32x2<false>(y); acc += q8[1] * f[0] + q8[3] * f[1];
-        f = fp8x2_to_f32x2<true>(x); acc += q8[4] * f[0] + q8[6] * f[1];
-        f = fp8x2_to_f32x2<true>(y); acc += q8[5] * f[0] + q8[7] * f[1];
-      }
-    }
-    s4[r] = xor_sum(xor_sum(xor_sum(acc, 1), 2), 4) + beta;
-  }
-  float p8[8];
-  valu_softmax(s4, st, sm, L, p8);
-  float pp[8];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    pp[k] = p8[k] * sv[k];
-    st.z_run += p8[k] * zv[k];
-  }
-  if constexpr (BITS == 2) {
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      const uint32_t w = raw.vw[d];
-      const uint32_t x = w & 0x33333333u, y = (w >> 2) & 0x33333333u;
-      // bytes 0,1: channel 2d (tokens (0,2),(4,6) / (1,3),(5,7)); bytes 2,3: channel 2d+1
-      f32x2_t f;
-      float o0 = st.oacc[2 * d], o1 = st.oacc[2 * d + 1];
-      f = fp4x2_to_f32x2<0>(x); o0 += pp[0] * f[0] + pp[2] * f[1];
-      f = fp4x2_to_f32x2<0>(y); o0 += pp[1] * f[0] + pp[3] * f[1];
-      f = fp4x2_to_f32x2<1>(x); o0 += pp[4] * f[0] + pp[6] * f[1];
-      f = fp4x2_to_f32x2<1>(y); o0 += pp[5] * f[0] + pp[7] * f[1];
-      f = fp4x2_to_f32x2<2>(x); o1 += pp[0] * f[0] + pp[2] * f[1];
-      f = fp4x2_to_f32x2<2>(y); o1 += pp[1] * f[0] + pp[3] * f[1];
-      f = fp4x2_to_f32x2<3>(x); o1 += pp[4] * f[0] + pp[6] * f[1];
-      f = fp4x2_to_f32x2<3>(y); o1 += pp[5] * f[0] + pp[7] * f[1];
-      st.oacc[2 * d] = o0; st.oacc[2 * d + 1] = o1;
-    }
-  } else {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t w = raw.vw[e];
-      const uint32_t x = w & 0x0F0F0F0Fu, y = (w >> 4) & 0x0F0F0F0Fu;
-      f32x2_t f;
-      float o0 = st.oacc[e];
-      f = fp8x2_to_f32x2<false>(x); o0 += pp[0] * f[0] + pp[2] * f[1];
-      f = fp8x2_to_f32x2<false>(y); o0 += pp[1] * f[0] + pp[3] * f[1];
-      f = fp8x2_to_f32x2<true>(x); o0 += pp[4] * f[0] + pp[6] * f[1];
-      f = fp8x2_to_f32x2<true>(y); o0 += pp[5] * f[0] + pp[7] * f[1];
-      st.oacc[e] = o0;
-    }
-  }
-}
-
-// One residual chunk of 32 bf16 tokens (ring slots contiguous: res_start and
-// the chunk start are multiples of G).  Rows past the valid count are never
-// read; the appended token of a fused step comes from k_new / v_new and the
-// lanes that read it store it into its ring slot.
-__device__ __forceinline__ void valu_rchunk(const DecodeArgs &a, int u, int rc, ValuState &st,
-                                            ValuSmem &sm, const float (&qv)[16], const ValuLane &L) {
-  const int t0 = G * rc, valid = min(G, a.n_res - t0);
-  const int slot0 = (a.res_start + t0) % a.slots;
-  const long long ring = (long long)u * a.slots + slot0;
-  const int new_row = a.new_idx - t0;
-  const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
-
-  float s4[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int row = 4 * L.tb + r;
-    const bool is_new = row == new_row;
-    const uint4 *kp = reinterpret_cast<const uint4 *>(
-        is_new ? a.k_new + (long long)u * D + 16 * L.cb : a.k_res + (ring + row) * D + 16 * L.cb);
-    uint4 x0 = zero, x1 = zero;
-    if (row < valid) { x0 = kp[0]; x1 = kp[1]; }
-    if (is_new) {
-      uint4 *dst = reinterpret_cast<uint4 *>(a.k_res + (ring + row) * D + 16 * L.cb);
-      dst[0] = x0; dst[1] = x1;
-    }
-    const uint32_t w[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-    float acc = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      acc += qv[2 * e] * __uint_as_float(w[e] << 16);
-      acc += qv[2 * e + 1] * __uint_as_float(w[e] & 0xFFFF0000u);
-    }
-    acc = xor_sum(xor_sum(xor_sum(acc, 1), 2), 4);
-    s4[r] = row < valid ? acc : kNegInf;
-  }
-  float p8[8];
-  valu_softmax(s4, st, sm, L, p8);
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const int row = 8 * L.oc + k;
-    const bool is_new = row == new_row;
-    const uint4 *vp = reinterpret_cast<const uint4 *>(
-        is_new ? a.v_new + (long long)u * D + 8 * L.cq : a.v_res + (ring + row) * D + 8 * L.cq);
-    uint4 x = zero;
-    if (row < valid) x = vp[0];
-    if (is_new) *reinterpret_cast<uint4 *>(a.v_res + (ring + row) * D + 8 * L.cq) = x;
-    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      st.oacc[2 * e] += p8[k] * __uint_as_float(w[e] << 16);
-      st.oacc[2 * e + 1] += p8[k] * __uint_as_float(w[e] & 0xFFFF0000u);
-    }
-  }
-}
-
-template <int BITS, int META, bool PAGED>
-__global__ __launch_bounds__(256) void decode_mha_kernel(DecodeArgs a) {
-  __shared__ __align__(16) union {
-    ValuSmem vs;
-    MergeSmem<1, 4> mg;
-  } sm;
-  const int u = blockIdx.x, split = blockIdx.y;
-  const int4 next_state = a.state_in ? apply_unit_state(a, u) : make_int4(0, 0, 0, 0);
-  ValuLane L;
-  L.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  L.lane = threadIdx.x & 63;
-  L.tb = L.lane >> 3; L.cb = L.lane & 7;
-  L.oc = L.lane >> 4; L.cq = L.lane & 15;
-  const WorkRange wr = wave_work(a, u, split, L.wave, 4, BITS + kMetaBytes<META> / 2, 16);
-
-  // the query first, then the first two groups (see decode_gqa_kernel)
-  const uint4 *qp = reinterpret_cast<const uint4 *>(a.q + (long long)u * D + 16 * L.cb);
-  const uint4 qraw[2] = {qp[0], qp[1]};
-  const bool has_groups = wr.g_begin < wr.g_end;
-  const RecView view = make_rec_view<BITS, META, PAGED>(a, u, L.lane);
-  ValuRaw<BITS> r[kPrefetch + 1];
-#pragma unroll
-  for (int i = 0; i < kPrefetch; ++i) {
-    load_valu_group<BITS, META, PAGED>(r[i], view, a, u, wr.g_begin + i, wr.g_begin + i < wr.g_end);
-    __builtin_amdgcn_sched_barrier(0);   // group order, as in the loop
-  }
-  float qv[16];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const uint32_t w[4] = {qraw[i].x, qraw[i].y, qraw[i].z, qraw[i].w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      qv[8 * i + 2 * e] = __uint_as_float(w[e] << 16) * a.qscale;
-      qv[8 * i + 2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u) * a.qscale;
-    }
-  }
-  ValuState st;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) st.oacc[i] = 0.f;
-  st.m_run = kNegInf; st.l_run = 0.f; st.z_run = 0.f;
-
-  // quantised groups: the load pipeline of the MFMA path (fixed loads per
-  // pass, kPrefetch groups in flight)
-  for (int g0 = wr.g_begin; g0 < wr.g_end; g0 += kPrefetch + 1) {
-#pragma unroll
-    for (int k = 0; k <= kPrefetch; ++k) {
-      const int g = g0 + k;
-      load_valu_group<BITS, META, PAGED>(r[(k + kPrefetch) % (kPrefetch + 1)], view, a, u,
-                                         g + kPrefetch, g + kPrefetch < wr.g_end);
-      if (g < wr.g_end) valu_group<BITS, META>(r[k], st, sm.vs, qv, L);
-    }
-  }
-  for (int rc = wr.r_begin; rc < wr.r_end; ++rc) valu_rchunk(a, u, rc, st, sm.vs, qv, L);
-
-  const float l = xor_sum(xor_sum(xor_sum(st.l_run, 8), 16), 32);
-  const float z = xor_sum(xor_sum(st.z_run, 16), 32);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) st.oacc[i] = xor_sum(xor_sum(st.oacc[i], 16), 32) + z;
-  __syncthreads();   // every wave is done with the staging areas the merge buffer aliases
-  if (L.oc == 0) {
-    float *dst = &sm.mg.o[L.wave][0][8 * L.cq];
-    *reinterpret_cast<float4 *>(dst) = make_float4(st.oacc[0], st.oacc[1], st.oacc[2], st.oacc[3]);
-    *reinterpret_cast<float4 *>(dst + 4) = make_float4(st.oacc[4], st.oacc[5], st.oacc[6], st.oacc[7]);
-  }
-  if (L.lane == 0) {
-    sm.mg.m[L.wave][0] = st.m_run;
-    sm.mg.l[L.wave][0] = l;
-  }
-  merge_and_store<1, 4>(sm.mg, a, u, split);
-  finish_unit<256>(a, u, &sm.mg.last, next_state);
-}
-
 }  // namespace
 
 namespace {
 
-// Kernel variants: 0 = MHA (VALU), 1..4 = GQA with that many blocks of 4
-// query heads; for each bit width and scale/zero format.
-// Waves per workgroup of each kernel variant (the MHA kernel and the GQA
-// kernels of 5+ query heads per kv head use 4).
-// Kernel variants: 0 MHA; 1-4 GQA with 4, 8, 12 or 16 query heads per block
-// of kv head (4 waves per workgroup, static shares); 5 GQA up to 4 heads,
-// one large workgroup per compute unit whose waves take groups dynamically
-// (12 waves at 2-bit, 8 at 4-bit: three or two per SIMD by registers).
+// Kernel variants, for each bit width and scale/zero format: 1-4 with 4, 8,
+// 12 or 16 query-head columns per kv head (4 waves per workgroup, static
+// shares); 5 up to 4 heads, one large workgroup per compute unit whose waves
+// take groups dynamically (12 waves at 2-bit, 8 at 4-bit: three or two per
+// SIMD by registers).  One query head per kv head (MHA) runs in the 4-column
+// kernels with the other three columns idle: the matrix core has the time to
+// spare, and its unpack-once path needs fewer vector instructions per group
+// than fp32 FMAs would.
 constexpr int kDynVariant = 5;
 template <int BITS>
 constexpr int kDynWaves = BITS == 2 ? 12 : 8;
@@ -1422,7 +1101,6 @@ int variant_waves(int bits, int variant) {
 template <int BITS, int META, bool PAGED>
 void *kernel_fn_t(int variant) {
   switch (variant) {
-    case 0: return (void *)&decode_mha_kernel<BITS, META, PAGED>;
     case 1: return (void *)&decode_gqa_kernel<BITS, 1, META, PAGED, 4>;
     case kDynVariant: return (void *)&decode_gqa_kernel<BITS, 1, META, PAGED, kDynWaves<BITS>>;
     case 2: return (void *)&decode_gqa_kernel<BITS, 2, META, PAGED, 4>;
@@ -1523,7 +1201,7 @@ int choose_wpu(int group_cost, const DecodeArgs &a, int slots) {
 }  // namespace
 
 hipError_t launch_decode(int bits, int meta, const DecodeArgs &a_in, hipStream_t s) {
-  int variant = a_in.qpk == 1 ? 0 : (a_in.qpk + 3) / 4;
+  int variant = (a_in.qpk + 3) / 4;   // 1..4
   DecodeArgs a = a_in;
   const bool paged = a_in.pages.table != nullptr;
   // Up to 4 query heads per kv head and at most one unit per compute unit:

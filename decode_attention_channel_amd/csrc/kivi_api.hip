@@ -45,9 +45,7 @@ kivi_status check_geom(const kivi_geom *g) {
 }
 
 // The quantised history is kept as group records (kivi.h) in the K_CODES
-// buffer; the other five history buffers are unused.  K codes take the lane
-// roles of the kernel that reads them: VALU for q_per_kv = 1, MFMA otherwise.
-int valu_k(const kivi_geom *g) { return g->q_per_kv == 1 ? 1 : 0; }
+// buffer; the other five history buffers are unused.
 
 kivi_status check_cache(const kivi_geom *g, const kivi_cache *c) {
   if (!c) return KIVI_E_NULL;
@@ -89,7 +87,6 @@ kivi_status enqueue_flush(const kivi_geom *g, kivi_cache *c, hipStream_t s) {
   a.n_groups = 1; a.n_units = (int)units_of(g); a.dst_g0 = c->n_q / G;
   a.max_tokens = g->max_tokens; a.n_groups_cap = g->max_tokens / G;
   a.k_codes = c->k_codes;
-  a.valu_k = valu_k(g);
   kivi_status st = hip_status(kivi::launch_quantize(g->bits, g->meta_format, a, s));
   if (st != KIVI_OK) return st;
   c->n_q += G;
@@ -226,8 +223,7 @@ kivi_status kivi_quantize_prefill(const kivi_geom *g, kivi_cache *c, const uint1
     a.n_groups = n_q / G; a.n_units = U; a.dst_g0 = 0;
     a.max_tokens = g->max_tokens; a.n_groups_cap = g->max_tokens / G;
     a.k_codes = c->k_codes;
-    a.valu_k = valu_k(g);
-    if ((st = hip_status(kivi::launch_quantize(g->bits, g->meta_format, a, s))) != KIVI_OK) return st;
+      if ((st = hip_status(kivi::launch_quantize(g->bits, g->meta_format, a, s))) != KIVI_OK) return st;
   }
   if (r > 0) {
     kivi::CopyRowsArgs a{};
@@ -372,8 +368,7 @@ kivi_status ragged_prefill_impl(const kivi_geom *g, const kivi_cache *c, const k
     a.n_groups = nq_max / G; a.n_units = (int)units_of(g); a.dst_g0 = 0;
     a.max_tokens = g->max_tokens; a.n_groups_cap = g->max_tokens / G;
     a.k_codes = c->k_codes;
-    a.valu_k = valu_k(g);
-    a.seq_lens = seq_lens;
+      a.seq_lens = seq_lens;
     a.kv_heads = g->kv_heads; a.residual = R; a.slots = slots; a.stride = stride;
     a.pages = pm;
     if ((st = hip_status(kivi::launch_quantize(g->bits, g->meta_format, a, s))) != KIVI_OK)
@@ -408,7 +403,6 @@ kivi_status ragged_step_impl(const kivi_geom *g, const kivi_cache *c, const kivi
   f.n_groups = 1; f.n_units = (int)units_of(g);
   f.max_tokens = g->max_tokens; f.n_groups_cap = g->max_tokens / G;
   f.k_codes = c->k_codes;
-  f.valu_k = valu_k(g);
   f.state = state_in;
   f.kv_heads = g->kv_heads; f.residual = g->residual; f.slots = slots;
   f.pages = pm;

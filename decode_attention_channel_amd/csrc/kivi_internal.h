@@ -68,15 +68,10 @@ __host__ __device__ inline long long group_slot(const PageMap &p, int kv_heads, 
 // Group records (kivi.h): the quantised history of one group is one
 // contiguous record of rec_planes() planes of 1 KiB; plane p holds 16 bytes
 // for each lane l (0..63) of the decode wave at p * 1024 + 16 * l:
-//   planes [0, b/2)      K codes, in the lane roles of the kernel that reads
-//                        them.  q_per_kv >= 2 (MFMA): lane 16 j + 4 (t >> 3)
-//                        + (t & 3) holds the 32-channel block j of token rows
-//                        t and t + 4, (t >> 2) & 1 = 0 (2-bit: 8 bytes each
-//                        in one plane; 4-bit: one plane each).  q_per_kv = 1
-//                        (VALU): lane 8 k + c holds the 16-channel block c of
-//                        token rows 4 k .. 4 k + 3 (2-bit: 4 bytes each;
-//                        4-bit: 8 bytes each, rows 4k, 4k+1 in plane 0 and
-//                        4k+2, 4k+3 in plane 1)
+//   planes [0, b/2)      K codes: lane 16 j + 4 (t >> 3) + (t & 3) holds
+//                        the 32-channel block j of token rows t and t + 4,
+//                        (t >> 2) & 1 = 0 (2-bit: 8 bytes each in one plane;
+//                        4-bit: one plane each)
 //   planes [b/2, b)      V codes: lane 16 o + (c >> 3) holds channels
 //                        8 (c >> 3) .. + 7 of octet o (b bytes per channel)
 //   planes [b, b + 2)    fp32 scale/zero: values 2l, 2l + 1 of k_scale,
@@ -105,7 +100,6 @@ struct QuantizeArgs {
   int dst_g0;
   int max_tokens, n_groups_cap;  // T, NG
   uint8_t *k_codes;   // group records
-  int valu_k;   // K lane roles of the group records: 1 VALU (q_per_kv = 1), 0 MFMA
   int gpw;   // groups per workgroup (set by the launcher)
   // Mixed-length batches (null otherwise).  seq_lens (prefill): sequence b
   // quantises its own n_q tokens, n_groups being the largest count.  state

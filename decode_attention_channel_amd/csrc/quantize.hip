@@ -85,19 +85,13 @@ __device__ __forceinline__ float max_x32(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-// Byte offsets inside a group record (kivi_internal.h).  K piece of the
-// MFMA roles: token row t, 32-channel block j; of the VALU roles: token row
-// t, 16-channel block c.  V cell: octet o, channels 4 c4 .. 4 c4 + 3; scale /
+// Byte offsets inside a group record (kivi_internal.h).  K piece: token row
+// t, 32-channel block j; V cell: octet o, channels 4 c4 .. 4 c4 + 3; scale /
 // zero value v (0..127) of array i (0 k_scale, 1 k_zero, 2 v_scale, 3 v_zero).
 template <int BITS>
 __device__ __forceinline__ int rec_k_piece(int t, int j) {
   const int lane = 16 * j + 4 * (t >> 3) + (t & 3), tile = (t >> 2) & 1;
   return BITS == 2 ? lane * 16 + tile * 8 : tile * kPlaneBytes + lane * 16;
-}
-template <int BITS>
-__device__ __forceinline__ int rec_k_piece_valu(int t, int c) {
-  const int lane = 8 * (t >> 2) + c, r = t & 3;
-  return BITS == 2 ? lane * 16 + r * 4 : (r >> 1) * kPlaneBytes + lane * 16 + (r & 1) * 8;
 }
 template <int BITS>
 __device__ __forceinline__ int rec_v_cell(int o, int c4) {
@@ -121,7 +115,6 @@ template <int BITS, int META>
 __device__ __forceinline__ void key_group(const QuantizeArgs &a, int u, int gl,
                                           const uint32_t (&raw)[16], int cb, int lane,
                                           uint8_t *tile) {
-  constexpr int D = kHeadDim, G = kGroup, KROW = D * BITS / 8;
   const int p = lane & 31, h = lane >> 5;
   const long long slot = group_slot(a.pages, a.kv_heads, a.n_groups_cap, u, a.dst_g0 + gl);
   if (slot < 0) return;   // paged: no page for this group
@@ -166,32 +159,18 @@ __device__ __forceinline__ void key_group(const QuantizeArgs &a, int u, int gl,
   const int row = lane >> 1, c32 = 32 * (lane & 1);
   const uint4 b0 = *reinterpret_cast<const uint4 *>(tile + row * 64 + c32);
   const uint4 b1 = *reinterpret_cast<const uint4 *>(tile + row * 64 + c32 + 16);
-  // the packed row piece: 32 channels of token `row` (channels 16h..16h+15
-  // in word(s) h of the piece)
-  uint8_t *rec = a.k_codes + slot * rec_bytes(BITS, META);
-  const int j = (cb + c32) / 32;
+  // the packed row piece: 32 channels of token `row`
+  uint8_t *dst = a.k_codes + slot * rec_bytes(BITS, META) + rec_k_piece<BITS>(row, (cb + c32) / 32);
   if constexpr (BITS == 2) {
     const uint32_t w0 = pack4x2(b0.x) | (pack4x2(b0.y) << 8) | (pack4x2(b0.z) << 16) |
                         (pack4x2(b0.w) << 24);
     const uint32_t w1 = pack4x2(b1.x) | (pack4x2(b1.y) << 8) | (pack4x2(b1.z) << 16) |
                         (pack4x2(b1.w) << 24);
-    if (a.valu_k) {
-      *reinterpret_cast<uint32_t *>(rec + rec_k_piece_valu<BITS>(row, 2 * j)) = w0;
-      *reinterpret_cast<uint32_t *>(rec + rec_k_piece_valu<BITS>(row, 2 * j + 1)) = w1;
-    } else {
-      *reinterpret_cast<uint2 *>(rec + rec_k_piece<BITS>(row, j)) = make_uint2(w0, w1);
-    }
+    *reinterpret_cast<uint2 *>(dst) = make_uint2(w0, w1);
   } else {
-    const uint2 h0 = make_uint2(pack4x4(b0.x) | (pack4x4(b0.y) << 16),
-                                pack4x4(b0.z) | (pack4x4(b0.w) << 16));
-    const uint2 h1 = make_uint2(pack4x4(b1.x) | (pack4x4(b1.y) << 16),
-                                pack4x4(b1.z) | (pack4x4(b1.w) << 16));
-    if (a.valu_k) {
-      *reinterpret_cast<uint2 *>(rec + rec_k_piece_valu<BITS>(row, 2 * j)) = h0;
-      *reinterpret_cast<uint2 *>(rec + rec_k_piece_valu<BITS>(row, 2 * j + 1)) = h1;
-    } else {
-      *reinterpret_cast<uint4 *>(rec + rec_k_piece<BITS>(row, j)) = make_uint4(h0.x, h0.y, h1.x, h1.y);
-    }
+    *reinterpret_cast<uint4 *>(dst) =
+        make_uint4(pack4x4(b0.x) | (pack4x4(b0.y) << 16), pack4x4(b0.z) | (pack4x4(b0.w) << 16),
+                   pack4x4(b1.x) | (pack4x4(b1.y) << 16), pack4x4(b1.z) | (pack4x4(b1.w) << 16));
   }
   __builtin_amdgcn_wave_barrier();   // tile reads done before the next group's writes
 }

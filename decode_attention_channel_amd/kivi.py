@@ -182,29 +182,20 @@ def _history_shapes(g: Geom, lead: tuple) -> dict:
     return {n: ((0,) if sh is None else lead + sh, dt) for n, (sh, dt) in _group_shapes(g).items()}
 
 
-def records_to_arrays(rec: np.ndarray, bits: int, meta: int, valu_k: bool) -> dict:
+def records_to_arrays(rec: np.ndarray, bits: int, meta: int) -> dict:
     """Group records [N][bytes] -> per-array layout of N groups (kivi.h):
     k_codes [N][G][D*b/8], k_scale/k_zero [N][D], v_codes [N][G/8][D][b],
-    v_scale/v_zero [N][D/G][G]; scale/zero as fp32 or as 16-bit patterns.
-    valu_k: K codes in the lane roles of q_per_kv = 1, else of q_per_kv >= 2."""
+    v_scale/v_zero [N][D/G][G]; scale/zero as fp32 or as 16-bit patterns."""
     N = rec.shape[0]
     r = rec.reshape(N, -1, 64, 16)
     t = np.arange(32)[:, None]
-    if valu_k:   # lane 8 (t >> 2) + c: 16-channel block c of row t, 2b bytes
-        c = np.arange(8)[None, :]
-        lane = 8 * (t >> 2) + c                             # [32][8]
-        per = 16 // (2 * bits)                              # pieces per lane and plane
-        rr = np.broadcast_to(t & 3, lane.shape)
-        kc = r[:, (rr // per)[..., None], lane[..., None],
-               (2 * bits * (rr % per))[..., None] + np.arange(2 * bits)]       # [N][32][8][2b]
-    else:        # lane 16 j + 4 (t >> 3) + (t & 3): 32-channel block j of row t
-        j = np.arange(4)[None, :]
-        lane = 16 * j + 4 * (t >> 3) + (t & 3)              # [32][4]
-        tile = np.broadcast_to((t >> 2) & 1, lane.shape)
-        if bits == 2:
-            kc = r[:, 0][:, lane[..., None], 8 * tile[..., None] + np.arange(8)]   # [N][32][4][8]
-        else:
-            kc = r[:, tile, lane, :]                                                # [N][32][4][16]
+    j = np.arange(4)[None, :]
+    lane = 16 * j + 4 * (t >> 3) + (t & 3)              # [32][4]: 32-channel block j of row t
+    tile = np.broadcast_to((t >> 2) & 1, lane.shape)
+    if bits == 2:
+        kc = r[:, 0][:, lane[..., None], 8 * tile[..., None] + np.arange(8)]   # [N][32][4][8]
+    else:
+        kc = r[:, tile, lane, :]                                                # [N][32][4][16]
     kc = kc.reshape(N, 32, 16 * bits)
     o = np.arange(4)[:, None]
     c4 = np.arange(32)[None, :]
@@ -271,7 +262,7 @@ class Cache:
         g = self.geom
         B, H, NG = g.batch, g.kv_heads, g.max_tokens // g.group
         arr = records_to_arrays(self.k_codes.cpu().numpy().reshape(B * H * NG, -1), g.bits,
-                                g.meta_format, g.q_per_kv == 1)
+                                g.meta_format)
         out = {n: a.reshape((B, H, NG) + a.shape[1:]) for n, a in arr.items()}
         out["k_codes"] = out["k_codes"].reshape(B, H, NG * g.group, -1)
         return out
@@ -312,8 +303,7 @@ class PagedCache:
         """Host copy of the pool in the per-array per-slot layout (k_codes
         [slots][G][D*b/8], k_scale [slots][D], ...) from its group records."""
         g = self.geom
-        return records_to_arrays(self.k_codes.cpu().numpy(), g.bits, g.meta_format,
-                                 g.q_per_kv == 1)
+        return records_to_arrays(self.k_codes.cpu().numpy(), g.bits, g.meta_format)
 
     def slot(self, b: int, h: int, g: int, table=None) -> int:
         """Pool slot of group g of (sequence b, kv head h); -1 without a page."""

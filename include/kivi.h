@@ -105,16 +105,10 @@
  *           or b + 1 (16-bit).  Bytes are laid out in the order one 64-lane
  *           wave of the decode kernel reads them: plane p (1024 bytes) holds
  *           16 bytes for each lane l at p*1024 + 16*l.
- *             K codes, planes [0, b/2), in the lane roles of the kernel that
- *               reads them:
- *               q_per_kv >= 2: lane 16*j + 4*(t>>3) + (t&3) holds bytes
- *               [j*4*b, (j+1)*4*b) of k_codes token rows t (first) and t+4
- *               (second), t with (t>>2)&1 == 0 (b = 2: 8 bytes each, one
- *               plane; b = 4: one plane each).
- *               q_per_kv = 1: lane 8*k + c holds bytes [c*2*b, (c+1)*2*b)
- *               of token rows 4k .. 4k+3 in that order (b = 2: 4 bytes each,
- *               one plane; b = 4: 8 bytes each, rows 4k, 4k+1 in plane 0
- *               and 4k+2, 4k+3 in plane 1).
+ *             K codes, planes [0, b/2): lane 16*j + 4*(t>>3) + (t&3) holds
+ *               bytes [j*4*b, (j+1)*4*b) of k_codes token rows t (first) and
+ *               t+4 (second) of the group, t with (t>>2)&1 == 0 (b = 2: 8
+ *               bytes each, one plane; b = 4: one plane each).
  *             V codes, planes [b/2, b): lane 16*o + c/8 holds the 8*b bytes
  *               of octet o, channels c..c+7 (c a multiple of 8); b = 4: the
  *               first 16 bytes in plane 2, the other 16 in plane 3.

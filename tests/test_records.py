@@ -1,20 +1,21 @@
 """Host logic of the group records: the binding's inverse permutation
 (records_to_arrays), which the GPU parity tests use to compare a device
 cache with the oracle's per-array layout, must be a bijection between the
-record's bytes and the per-array bytes of one group, for both K lane roles,
-both bit widths and both scale/zero formats; and the record must hold the
-same number of bytes as the per-array layout (no padding)."""
+record's bytes and the per-array bytes of one group, for both bit widths and
+both scale/zero formats, and must put each K piece where the decode lanes
+read it; the record holds the same number of bytes as the per-array layout
+(no padding)."""
 import numpy as np
 import pytest
 
 from decode_attention_channel_amd import kivi
 
 
-def _ids(bits, meta, valu_k):
+def _ids(bits, meta):
     rec_bytes = 1024 * (bits + (1 if meta else 2))
     pos = np.arange(rec_bytes)
-    lo = kivi.records_to_arrays((pos & 0xFF).astype(np.uint8)[None], bits, meta, valu_k)
-    hi = kivi.records_to_arrays((pos >> 8).astype(np.uint8)[None], bits, meta, valu_k)
+    lo = kivi.records_to_arrays((pos & 0xFF).astype(np.uint8)[None], bits, meta)
+    hi = kivi.records_to_arrays((pos >> 8).astype(np.uint8)[None], bits, meta)
     out = {}
     for name in lo:
         a = np.ascontiguousarray(lo[name]).view(np.uint8).reshape(-1).astype(np.int64)
@@ -23,10 +24,9 @@ def _ids(bits, meta, valu_k):
     return rec_bytes, out
 
 
-@pytest.mark.parametrize("valu_k", [False, True])
 @pytest.mark.parametrize("bits,meta", [(2, 0), (4, 0), (2, 1), (4, 1)])
-def test_record_inverse_is_a_bijection(bits, meta, valu_k):
-    rec_bytes, ids = _ids(bits, meta, valu_k)
+def test_record_inverse_is_a_bijection(bits, meta):
+    rec_bytes, ids = _ids(bits, meta)
     D, G, mb = 128, 32, 2 if meta else 4
     sizes = {"k_codes": G * D * bits // 8, "k_scale": D * mb, "k_zero": D * mb,
              "v_codes": G * D * bits // 8, "v_scale": D * mb, "v_zero": D * mb}
@@ -38,32 +38,22 @@ def test_record_inverse_is_a_bijection(bits, meta, valu_k):
 
 
 @pytest.mark.parametrize("bits", [2, 4])
-def test_key_roles_differ_only_in_the_key_planes(bits):
-    # both K lane roles share the V and scale/zero planes; their K codes are
-    # two permutations of the same code planes
-    _, mfma = _ids(bits, 0, False)
-    _, valu = _ids(bits, 0, True)
-    for name in ("k_scale", "k_zero", "v_codes", "v_scale", "v_zero"):
-        assert np.array_equal(mfma[name], valu[name]), name
-    assert not np.array_equal(mfma["k_codes"], valu["k_codes"])
-    assert np.array_equal(np.sort(mfma["k_codes"]), np.sort(valu["k_codes"]))
-    assert mfma["k_codes"].max() < 1024 * bits // 2
-
-
-def test_valu_key_pieces_follow_the_lane_roles():
-    # q_per_kv = 1 readers: lane 8 k + c reads, at its 16 bytes of each K
-    # plane, channels 16 c .. 16 c + 15 of token rows 4 k .. 4 k + 3
-    _, ids = _ids(2, 0, True)
-    k = ids["k_codes"].reshape(32, 32)         # [row][byte], 4 channels per byte
+def test_key_pieces_follow_the_lane_roles(bits):
+    # lane 16 j + 4 (t >> 3) + (t & 3), for t with (t >> 2) & 1 == 0, reads
+    # the 32-channel block j of token rows t and t + 4 (the two MFMA tiles):
+    # 2-bit, 8 bytes each in plane 0; 4-bit, 16 bytes each in planes 0, 1
+    _, ids = _ids(bits, 0)
+    piece = 4 * bits
+    k = ids["k_codes"].reshape(32, 4, piece)   # [row][block j][bytes]
     for t in range(32):
-        for c in range(8):
-            lane = 8 * (t // 4) + c
-            got = k[t, 4 * c:4 * c + 4]
-            assert np.all(got // 16 == lane) and np.all(got < 1024), (t, c)
-    _, ids = _ids(4, 0, True)
-    k = ids["k_codes"].reshape(32, 64)         # 2 channels per byte
-    for t in range(32):
-        for c in range(8):
-            got = k[t, 8 * c:8 * c + 8]
-            assert np.all((got % 1024) // 16 == 8 * (t // 4) + c), (t, c)
-            assert np.all(got // 1024 == (t % 4) // 2), (t, c)
+        if (t >> 2) & 1:
+            continue
+        for j in range(4):
+            lane = 16 * j + 4 * (t >> 3) + (t & 3)
+            for tile, row in enumerate((t, t + 4)):
+                got = k[row, j]
+                if bits == 2:
+                    want = lane * 16 + 8 * tile + np.arange(8)
+                else:
+                    want = tile * 1024 + lane * 16 + np.arange(16)
+                assert np.array_equal(got, want), (t, j, tile)
