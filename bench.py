@@ -87,7 +87,7 @@ def read_traffic(kernel_tag: str):
         return None
 
 
-def cpu_baseline(w, seed, units_wanted=256, meta=0):
+def cpu_baseline(w, seed, units_wanted=1024, meta=0):
     import numpy as np
 
     import oracle
