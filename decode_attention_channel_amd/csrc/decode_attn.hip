@@ -912,13 +912,14 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeArgs a) {
 
   // this wave's byte share of the unit, and the items that start inside it
   // (kDyn: the workgroup's share; the waves take its groups dynamically and
-  // one residual chunk each)
+  // its residual chunks round-robin, wave w the chunks w, w + NW, ...)
   const WorkRange wr = kDyn ? wave_work(a, u, split, 0, 1, BITS + kMetaBytes<META> / 2, 16)
                             : wave_work(a, u, split, wave, NW, BITS + kMetaBytes<META> / 2, 16);
   const int g_end = wr.g_end;
   const int g_begin = kDyn ? wr.g_begin + wave * C : wr.g_begin;
   const int r_begin = kDyn ? wr.r_begin + wave : wr.r_begin;
-  const int r_end = kDyn ? min(r_begin + 1, wr.r_end) : wr.r_end;
+  const int r_end = wr.r_end;
+  constexpr int r_step = kDyn ? NW : 1;
 
   // Order of the first loads: the query (needed first), then the first
   // groups, so that waiting for the query does not wait for the groups.
@@ -1046,7 +1047,8 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeArgs a) {
   }
   }
   // residual chunks
-  for (int rc = r_begin; rc < r_end; ++rc) mfma_rchunk<NHB, NW>(a, u, rc, st, sm.mf, wave, lane, n, gq);
+  for (int rc = r_begin; rc < r_end; rc += r_step)
+    mfma_rchunk<NHB, NW>(a, u, rc, st, sm.mf, wave, lane, n, gq);
 
   // ---- per-wave totals, then the workgroup merge (the merge buffer aliases
   // the staging areas of the other waves: wait until every wave is done)

@@ -1,9 +1,10 @@
 """GPU parity of the uncompressed bf16 baseline (kivi_dense_decode_attention)
-against the oracle's dense attention: GQA (MFMA kernel) and MHA (VALU
-kernel), ragged lengths that end inside a 32-token chunk, one token, a
-length below the capacity (the tail must not be read: it is filled with
-Inf/NaN), and a sampled check at the Llama-2-13B-shaped memory-wall
-geometry (40 heads, 4096 tokens)."""
+against the oracle's dense attention: GQA and MHA, ragged lengths that end
+inside a 32-token chunk, one token, a length below the capacity (the tail
+must not be read: it is filled with Inf/NaN), and sampled checks at the
+Llama-2-13B-shaped memory-wall geometry (40 heads, 4096 tokens): batch 8
+(more units than compute units: static shares) and batch 2 (one workgroup
+per compute unit, each with more 32-token chunks than waves)."""
 import math
 
 import numpy as np
@@ -57,10 +58,12 @@ def test_dense_attention_matches_oracle(B, H, QPK, T, S):
     assert err <= ATTN_TOL, f"row-relative error {err:.3e}"
 
 
-def test_dense_attention_memory_wall_geometry_sampled():
-    """40 heads x 4096 tokens at batch 8; a few (sequence, head) units
-    recomputed by the oracle."""
-    B, H, T = 8, 40, 4096
+@pytest.mark.parametrize("B", [8, 2])
+def test_dense_attention_memory_wall_geometry_sampled(B):
+    """40 heads x 4096 tokens; a few (sequence, head) units recomputed by the
+    oracle."""
+    print(f"dense wall B={B}", flush=True)
+    H, T = 40, 4096
     w = synth.WORKLOADS["llama2-13b-mha-wall"]
     k, v = synth.prefill_kv(w, 77, batch=B)
     q = synth.query(w, 77, batch=B)
