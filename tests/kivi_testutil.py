@@ -28,8 +28,8 @@ def bits_to_dev(x: np.ndarray, device="cuda") -> torch.Tensor:
 
 
 def host_cache(gc, og: oracle.Geom) -> oracle.Cache:
-    """Copy a device cache into an oracle.Cache (per-array layout; a cache
-    with group records is brought to it by the binding's documented byte
+    """Copy a device cache into an oracle.Cache (per-array layout; the
+    cache's group records are brought to it by the binding's documented byte
     permutation)."""
     hc = oracle.Cache(og)
     hist = gc.history()

@@ -11,7 +11,7 @@ the CPU oracle:
 * outputs agree with the oracle within the attention tolerance, and the
   final cache equals the oracle's byte for byte.
 
-Cases cover GQA (MFMA kernel) and MHA (VALU kernel), both bit widths, a ring
+Cases cover GQA and MHA (one query head per kv head), both bit widths, a ring
 of R = 32, R = 0 (where a flush step runs as three launches), prefill lengths
 that start with an empty history, and several flushes per run.
 """

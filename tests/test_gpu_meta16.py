@@ -1,7 +1,7 @@
 """GPU parity of the 16-bit scale/zero format (fp16 scale, bf16 zero) against
 the oracle: byte-exact quantised history (codes, fp16 scale bits, bf16 zero
-bits) and decode attention within the tolerance, for GQA (MFMA kernel) and
-MHA (VALU kernel), both bit widths, ragged lengths, streaming with flushes
+bits) and decode attention within the tolerance, for GQA and MHA (one query
+head per kv head), both bit widths, ragged lengths, streaming with flushes
 through the separate calls and through kivi_decode_step, groups whose
 scales are fp16 subnormals, and a saturated scale."""
 import math
