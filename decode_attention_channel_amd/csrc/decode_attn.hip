@@ -1087,24 +1087,28 @@ namespace {
 // Kernel variants, for each bit width and scale/zero format: 1-4 with 4, 8,
 // 12 or 16 query-head columns per kv head (4 waves per workgroup, static
 // shares); 5 up to 4 heads, one large workgroup per compute unit whose waves
-// take groups dynamically (12 waves at 2-bit, 8 at 4-bit: three or two per
-// SIMD by registers).  One query head per kv head (MHA) runs in the 4-column
+// take groups dynamically (three waves per SIMD, 12 per workgroup, except
+// 4-bit with fp32 scale/zero: 8).  The register allocator fits every
+// variant into the 168 VGPRs of three waves per SIMD; at 4-bit with fp32
+// scale/zero two waves per SIMD measured 0.6-0.9 us faster on the 8K and
+// 32K GQA workloads, with 16-bit scale/zero three were 1.5 us faster.
+// One query head per kv head (MHA) runs in the 4-column
 // kernels with the other three columns idle: the matrix core has the time to
 // spare, and its unpack-once path needs fewer vector instructions per group
 // than fp32 FMAs would.
 constexpr int kDynVariant = 5;
-template <int BITS>
-constexpr int kDynWaves = BITS == 2 ? 12 : 8;
-int variant_waves(int bits, int variant) {
+template <int BITS, int META>
+constexpr int kDynWaves = BITS == 2 || META == 1 ? 12 : 8;
+int variant_waves(int bits, int meta, int variant) {
   if (variant != kDynVariant) return 4;
-  return bits == 2 ? kDynWaves<2> : kDynWaves<4>;
+  return bits == 2 || meta == 1 ? 12 : 8;
 }
 
 template <int BITS, int META, bool PAGED>
 void *kernel_fn_t(int variant) {
   switch (variant) {
     case 1: return (void *)&decode_gqa_kernel<BITS, 1, META, PAGED, 4>;
-    case kDynVariant: return (void *)&decode_gqa_kernel<BITS, 1, META, PAGED, kDynWaves<BITS>>;
+    case kDynVariant: return (void *)&decode_gqa_kernel<BITS, 1, META, PAGED, kDynWaves<BITS, META>>;
     case 2: return (void *)&decode_gqa_kernel<BITS, 2, META, PAGED, 4>;
     case 3: return (void *)&decode_gqa_kernel<BITS, 3, META, PAGED, 4>;
     default: return (void *)&decode_gqa_kernel<BITS, 4, META, PAGED, 4>;
@@ -1136,7 +1140,7 @@ Residency residency(int bits, int meta, int variant, bool paged) {
   Residency r{__atomic_load_n(&slot[0], __ATOMIC_RELAXED), __atomic_load_n(&slot[1], __ATOMIC_RELAXED)};
   if (r.per_cu > 0 && r.cus > 0) return r;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&r.per_cu, kernel_fn(bits, meta, variant, paged),
-                                                   64 * variant_waves(bits, variant),
+                                                   64 * variant_waves(bits, meta, variant),
                                                    0) != hipSuccess ||
       r.per_cu < 1)
     r.per_cu = 1;
@@ -1229,7 +1233,7 @@ hipError_t launch_decode(int bits, int meta, const DecodeArgs &a_in, hipStream_t
   } else {
     for (int i = 0; i < 4; ++i) a.rank_w[i] = 1;
   }
-  const dim3 grid(a.n_units, a.n_split), block(64 * variant_waves(bits, variant));
+  const dim3 grid(a.n_units, a.n_split), block(64 * variant_waves(bits, meta, variant));
   hipLaunchKernelGGL(reinterpret_cast<void (*)(DecodeArgs)>(kernel_fn(bits, meta, variant, paged)), grid,
                      block, 0, s, a);
   return hipGetLastError();
