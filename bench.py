@@ -467,8 +467,9 @@ def main():
                          "(Llama-2-13B-shaped MHA); prints its own JSON line")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported on this build "
-              "(multi-GPU sharding is a design note only)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the library "
+              "runs on one GPU, and sharding across GPUs is described, not built",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
