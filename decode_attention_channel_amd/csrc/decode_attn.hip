@@ -701,14 +701,14 @@ __device__ __forceinline__ void mfma_rchunk(const DecodeArgs &a, int u, int rc,
   const bool has_new = new_row >= 0 && new_row < G;
 
   // All loads first, in one batch (one memory latency for the chunk): V rows
-  // for the LDS transpose, lane -> (row lane/2, 64 channels); K rows of the
-  // two tiles as A operands of q.K^T (natural channel order).  Ring rows past
-  // `valid` (stale or never written slots, inside the ring) are loaded and
-  // then replaced by zeros (V) or masked out of the softmax (K).
-  const int vrow = lane >> 1, vc0 = 64 * (lane & 1);
-  const bool v_new = has_new && vrow == new_row;
-  const uint4 *vsrc = reinterpret_cast<const uint4 *>(
-      v_new ? a.v_new + (long long)u * D + vc0 : vrows + (long long)vrow * D + vc0);
+  // for the LDS transpose, one contiguous KiB of the chunk per load (load i,
+  // lane l: row 4i + l/16, channels 8 (l % 16) .. + 7); K rows of the two
+  // tiles as A operands of q.K^T, MFMA step m taking channels 32m + 8gq ..
+  // + 7 so that the four lanes of a row read 64 contiguous bytes per load
+  // (the query rows use the same order).  Ring rows past `valid` (stale or
+  // never written slots, inside the ring) are loaded and then replaced by
+  // zeros (V) or masked out of the softmax (K).
+  const int vr0 = lane >> 4, vcol = 8 * (lane & 15);
   const int kr0 = 8 * (n >> 2) + (n & 3);
   bool k_new[2];
   const uint4 *ksrc[2];
@@ -717,7 +717,7 @@ __device__ __forceinline__ void mfma_rchunk(const DecodeArgs &a, int u, int rc,
     const int row = kr0 + 4 * tile;
     k_new[tile] = has_new && row == new_row;
     ksrc[tile] = reinterpret_cast<const uint4 *>(
-        k_new[tile] ? a.k_new + (long long)u * D + 32 * gq : krows + (long long)row * D + 32 * gq);
+        k_new[tile] ? a.k_new + (long long)u * D + 8 * gq : krows + (long long)row * D + 8 * gq);
   }
   const int b = u / a.kv_heads, h = u % a.kv_heads;
   // query rows as B operands of q.K^T (hi columns; the lo columns get zeros):
@@ -728,40 +728,45 @@ __device__ __forceinline__ void mfma_rchunk(const DecodeArgs &a, int u, int rc,
     const int hh = hb * 4 + (n & 3);
     return reinterpret_cast<const uint4 *>(
         a.q + ((long long)b * a.kv_heads * qpk + (long long)h * qpk + (hh < qpk ? hh : 0)) * D +
-        32 * gq);
+        8 * gq);
   };
   uint4 xq[4];
   if constexpr (kQFirst) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m) xq[m] = q_rows(0)[m];
+    for (int m = 0; m < 4; ++m) xq[m] = q_rows(0)[4 * m];
   }
   uint4 xv[8], xk[2][4];
+  const uint4 *vbase = reinterpret_cast<const uint4 *>(vrows + (long long)vr0 * D + vcol);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) xv[i] = vsrc[i];
+  for (int i = 0; i < 8; ++i) xv[i] = vbase[i * (4 * D / 8)];   // row 4i + vr0
 #pragma unroll
   for (int tile = 0; tile < 2; ++tile)
 #pragma unroll
-    for (int m = 0; m < 4; ++m) xk[tile][m] = ksrc[tile][m];
-  // stage V rows in LDS
-  {
-    const bool live = vrow < valid;
-    uint4 *dst = reinterpret_cast<uint4 *>(&smf.w[wave].vres[vrow][vc0]);
+    for (int m = 0; m < 4; ++m) xk[tile][m] = ksrc[tile][4 * m];
+  // the fused append (wave-uniform): the new token's V row comes from v_new
+  // (load new_row / 4, lanes with vr0 == new_row % 4) and goes into its ring
+  // slot
+  if (has_new && vr0 == (new_row & 3)) {
+    const uint4 x = *reinterpret_cast<const uint4 *>(a.v_new + (long long)u * D + vcol);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) dst[i] = live ? xv[i] : make_uint4(0u, 0u, 0u, 0u);
+    for (int i = 0; i < 8; ++i)
+      if (i == (new_row >> 2)) xv[i] = x;
+    *reinterpret_cast<uint4 *>(a.v_res + (ring + new_row) * D + vcol) = x;
   }
-  // the fused append: the new token's rows go into their ring slot
-  if (v_new) {
-    uint4 *ring_row = reinterpret_cast<uint4 *>(a.v_res + (ring + vrow) * D + vc0);
+  // stage V rows in LDS
 #pragma unroll
-    for (int i = 0; i < 8; ++i) ring_row[i] = xv[i];
+  for (int i = 0; i < 8; ++i) {
+    const int row = 4 * i + vr0;
+    *reinterpret_cast<uint4 *>(&smf.w[wave].vres[row][vcol]) =
+        row < valid ? xv[i] : make_uint4(0u, 0u, 0u, 0u);
   }
   Op8 ak[2][4];
 #pragma unroll
   for (int tile = 0; tile < 2; ++tile) {
     if (k_new[tile]) {
-      uint4 *ring_row = reinterpret_cast<uint4 *>(a.k_res + (ring + kr0 + 4 * tile) * D + 32 * gq);
+      uint4 *ring_row = reinterpret_cast<uint4 *>(a.k_res + (ring + kr0 + 4 * tile) * D + 8 * gq);
 #pragma unroll
-      for (int m = 0; m < 4; ++m) ring_row[m] = xk[tile][m];
+      for (int m = 0; m < 4; ++m) ring_row[4 * m] = xk[tile][m];
     }
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
@@ -787,7 +792,7 @@ __device__ __forceinline__ void mfma_rchunk(const DecodeArgs &a, int u, int rc,
     const bool hi_col = (n & 4) == 0 && hh < qpk;
     if (hb > 0 || !kQFirst) {
 #pragma unroll
-      for (int m = 0; m < 4; ++m) xq[m] = q_rows(hb)[m];
+      for (int m = 0; m < 4; ++m) xq[m] = q_rows(hb)[4 * m];
     }
     f32x4_t sc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
