@@ -61,9 +61,6 @@ constexpr float kRescaleSlack = 8.0f;   // running max may lag the true max by 8
 // converts below deliver codes.
 constexpr int P8[8] = {0, 2, 1, 3, 4, 6, 5, 7};
 
-__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
-  return __uint_as_float(bits16 << 16);
-}
 
 template <int SEL>
 __device__ __forceinline__ uint32_t fp4x2_to_bf16x2(uint32_t w) {
@@ -115,11 +112,8 @@ __device__ __forceinline__ float dpp_ror4(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x124,
                                                                 0xF, 0xF, true));
 }
-__device__ __forceinline__ float xor_max(float x, int m) { return fmaxf(x, __shfl_xor(x, m)); }
-__device__ __forceinline__ float xor_sum(float x, int m) { return x + __shfl_xor(x, m); }
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__device__ __forceinline__ float4 ld4(const float *p) { return *reinterpret_cast<const float4 *>(p); }
 
 // Split partials cross workgroups (and XCDs, whose L2 caches are not coherent
 // with each other), so they are written and read with agent-scope atomic
@@ -129,18 +123,6 @@ __device__ __forceinline__ void st_shared_agent(float *p, float v) {
 }
 __device__ __forceinline__ float ld_shared_agent(const float *p) {
   return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void ld8(const float *p, float (&x)[8]) {
-  const float4 a = ld4(p), b = ld4(p + 4);
-  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-}
-__device__ __forceinline__ void ld16(const float *p, float (&x)[16]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float4 v = ld4(p + 4 * i);
-    x[4 * i] = v.x; x[4 * i + 1] = v.y; x[4 * i + 2] = v.z; x[4 * i + 3] = v.w;
-  }
 }
 
 // ---------------------------------------------------------------- merge ---
@@ -319,15 +301,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
   const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
   return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>((hi << 32) | lo), (short)0,
                                            (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
-}
-__device__ __forceinline__ void buf8f(__amdgpu_buffer_rsrc_t r, uint32_t vo, uint32_t so, float (&x)[8]) {
-  const u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(r, vo, so, 0);
-  const u32x4_t b = __builtin_amdgcn_raw_buffer_load_b128(r, vo + 16, so, 0);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    x[i] = __uint_as_float(a[i]);
-    x[4 + i] = __uint_as_float(b[i]);
-  }
 }
 
 // Raw bytes of one group as one lane of the MFMA path needs them: K codes of
