@@ -267,17 +267,39 @@ __device__ __forceinline__ void value_group(const QuantizeArgs &a, int u, int gl
   __builtin_amdgcn_wave_barrier();
 }
 
+// Row stride of the value staging tile, in 16-byte units: 17 (one unit of
+// padding) keeps both its row-wise writes and the (row r, channel group q)
+// reads free of bank conflicts.
+constexpr int kStageStride = kHeadDim / 8 + 1;
+
+// In place: x holds load i's piece (row 4i + lr, channels 8 lc .. + 7) on
+// entry and the lane's value group (row r, channels 32q + 8i .. + 7) on exit.
+__device__ __forceinline__ void regather_values(uint4 (&x)[4], uint4 *stage, int lr, int lc, int r,
+                                                int q) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) stage[(4 * i + lr) * kStageStride + lc] = x[i];
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) x[i] = stage[r * kStageStride + 4 * q + i];
+  __builtin_amdgcn_wave_barrier();   // reads done before the next group's writes
+}
+
+// The 16 token rows of a half group are contiguous in the source, so each
+// load covers one contiguous KiB of them (load i, lane l: row 4i + l/16,
+// channels 8 (l % 16) .. + 7); the wave's staging tile in LDS hands each lane
+// its value group (row r, channels 32q .. 32q + 31).
 template <int BITS, int META>
 __device__ __forceinline__ void quantize_values(const QuantizeArgs &a, int u, int gl0, int gl1,
-                                                int part, int lane, uint8_t *tile) {
+                                                int part, int lane, uint8_t *tile, uint4 *stage) {
   constexpr int D = kHeadDim, G = kGroup;
   const int r = lane >> 2, q = lane & 3;
+  const int lr = lane >> 4, lc = lane & 15;
   const uint16_t *src = a.src_v + (long long)u * a.src_unit_stride + (long long)a.src_tok0 * D;
   auto load = [&](int gl, uint4 (&x)[4]) {
-    const uint4 *row = reinterpret_cast<const uint4 *>(
-        src + ((long long)gl * G + 16 * part + r) * D + 32 * q);
+    const uint4 *base =
+        reinterpret_cast<const uint4 *>(src + ((long long)gl * G + 16 * part + lr) * D) + lc;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) x[i] = row[i];
+    for (int i = 0; i < 4; ++i) x[i] = base[i * (4 * D / 8)];   // row 4i + lr
   };
   uint4 cur[4], nxt[4];
   load(gl0, nxt);
@@ -285,8 +307,10 @@ __device__ __forceinline__ void quantize_values(const QuantizeArgs &a, int u, in
 #pragma unroll
     for (int i = 0; i < 4; ++i) cur[i] = nxt[i];
     load(gl + 1, nxt);
+    regather_values(cur, stage, lr, lc, r, q);
     value_group<BITS, META>(a, u, gl, cur, part, lane, tile);
   }
+  regather_values(nxt, stage, lr, lc, r, q);
   value_group<BITS, META>(a, u, gl1 - 1, nxt, part, lane, tile);
 }
 
@@ -296,6 +320,7 @@ __device__ __forceinline__ void quantize_values(const QuantizeArgs &a, int u, in
 template <int BITS, int META>
 __global__ __launch_bounds__(256) void quantize_kernel(QuantizeArgs a) {
   __shared__ __align__(16) uint8_t s_tile[4][16 * kHeadDim];
+  __shared__ uint4 s_stage[2][16 * kStageStride];   // value waves' bf16 staging
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int u = blockIdx.y;
   const int gl0 = blockIdx.x * a.gpw;
@@ -320,7 +345,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantizeArgs a) {
   if (wave < 2)
     quantize_keys<BITS, META>(a, u, gl0, gl1, wave, lane, s_tile[wave]);
   else
-    quantize_values<BITS, META>(a, u, gl0, gl1, wave - 2, lane, s_tile[wave]);
+    quantize_values<BITS, META>(a, u, gl0, gl1, wave - 2, lane, s_tile[wave], s_stage[wave - 2]);
 }
 
 __global__ __launch_bounds__(256) void copy_rows_kernel(CopyRowsArgs a) {
