@@ -33,7 +33,7 @@ def env():
             os.environ[k] = v
 
 
-@pytest.mark.parametrize("bits,meta", [(2, 0), (4, 0), (2, 1)])
+@pytest.mark.parametrize("bits,meta", [(2, 0), (4, 0), (2, 1), (4, 1)])
 def test_static_and_dynamic_launches_match_the_oracle(env, bits, meta):
     B, H, QPK, S = 2, 2, 4, 8192
     print(f"variants bits={bits} meta={meta}", flush=True)
