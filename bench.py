@@ -151,7 +151,7 @@ def _fill_random_cache(cache, n_q, n_res, gen):
     from decode_attention_channel_amd import kivi
 
     g = cache.geom
-    rec = cache.k_codes.view(-1, kivi.record_bytes(g) // 1024, 1024)
+    rec = cache.records.view(-1, kivi.record_bytes(g) // 1024, 1024)
     rec[:, :g.bits].random_(0, 256, generator=gen)
     meta = rec[:, g.bits:].contiguous()
     if g.meta_format == kivi.META_FP16_BF16:   # per lane: ks, kz, vs, vz pairs
@@ -341,7 +341,7 @@ def _paged_copy(geom, cache, page_groups, rng):
     h = torch.arange(H, device=tb.device)
     slot = ((tb[:, g // page_groups][:, None, :] * H + h[None, :, None]) * page_groups +
             (g % page_groups)[None, None, :]).reshape(-1)
-    pc.k_codes[slot] = cache.k_codes.reshape(B * H * NG, -1)   # the group records
+    pc.records[slot] = cache.records.reshape(B * H * NG, -1)   # the group records
     pc.k_res.copy_(cache.k_res)
     pc.v_res.copy_(cache.v_res)
     return pc
@@ -362,7 +362,7 @@ def ragged_leg(w, geom, caches, ws, qs, outs, tok, steps, seed, meta_bytes):
     from decode_attention_channel_amd import kivi
 
     assert steps % 2 == 0
-    dev = caches[0].k_codes.device
+    dev = caches[0].records.device
     G, R = w.group, w.residual
     slots = R + G
     layers = len(caches)

@@ -8,4 +8,4 @@ from .kivi import (Cache, Geom, KiviError, PagedCache, RaggedStepper, Workspace,
                    append_token, cache_layout, decode_attention, decode_step,
                    dense_decode_attention, flush_residual, paged_decode_step, paged_layout,
                    paged_prefill, quantize_prefill, ragged_decode_step, ragged_prefill,
-                   workspace_size)
+                   workspace_bytes)

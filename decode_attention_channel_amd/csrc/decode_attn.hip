@@ -115,6 +115,10 @@ __device__ __forceinline__ float dpp_ror4(float x) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 
+// s_waitcnt operand that waits for vmcnt == 0 only: vmcnt bits [3:0] and
+// [15:14] zero, expcnt [6:4] and lgkmcnt [11:8] at their maxima (no wait).
+constexpr int kWaitVmcnt0 = 0x0F70;
+
 // Split partials cross workgroups (and XCDs, whose L2 caches are not coherent
 // with each other), so they are written and read with agent-scope atomic
 // accesses, which are coherent without flushing or invalidating the L2.
@@ -171,8 +175,13 @@ __device__ void merge_and_store(MergeSmem<HMAX, NW> &sm, const DecodeArgs &a, in
 // load from the dispatch packet)
 template <int NT>
 __device__ void finish_unit(const DecodeArgs &a, int u, int *s_last, int4 next_state) {
-  // the barrier waits for this workgroup's partial stores (vmcnt) before the
-  // arrival is counted
+  // Every wave first waits until its own partial stores have completed
+  // (vmcnt counts stores on this architecture; a completed agent-scope store
+  // is visible to every compute unit).  The barrier alone would only wait for
+  // LDS traffic, so without this wait the arrival could be counted while
+  // another wave's stores are still in flight, and the last workgroup could
+  // merge a stale partial left by an earlier launch on the same workspace.
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
   if (threadIdx.x == 0) {
     const unsigned prev =
@@ -326,8 +335,9 @@ __device__ __forceinline__ int page_entry(const int32_t *table, long long i) {
 }
 
 // Group records (layout in kivi_internal.h): one buffer resource over the
-// unit's records, or (PAGED) over the whole pool, which the host keeps below
-// 2 GiB so that kOutOfRange offsets stay out of range.  Lane l reads bytes
+// unit's records, or (PAGED) over the whole pool.  The host keeps a unit's
+// records within kMaxUnitRecordBytes (2^30) and a pool below 2^31 bytes, so
+// that kOutOfRange offsets stay out of range (see load_record).  Lane l reads bytes
 // [16 l, 16 l + 16) of every plane, the group entering as a scalar offset.
 struct RecView {
   __amdgpu_buffer_rsrc_t rec;
@@ -340,9 +350,9 @@ __device__ __forceinline__ RecView make_rec_view(const DecodeArgs &a, int u, int
   RecView v;
   if constexpr (PAGED) {
     const long long groups = (long long)a.pages.num_pages * a.kv_heads << a.pages.shift;
-    v.rec = make_rsrc(a.k_codes, (uint32_t)(groups * REC));
+    v.rec = make_rsrc(a.records, (uint32_t)(groups * REC));
   } else {
-    v.rec = make_rsrc(a.k_codes + u * a.n_groups_cap * REC, (uint32_t)(a.n_groups_cap * REC));
+    v.rec = make_rsrc(a.records + u * a.n_groups_cap * REC, (uint32_t)(a.n_groups_cap * REC));
   }
   v.o_lane = 16 * lane;
   return v;
@@ -353,7 +363,13 @@ __device__ __forceinline__ RecView make_rec_view(const DecodeArgs &a, int u, int
 // no memory.  Issuing a fixed number of loads per pipeline step keeps the
 // compiler's count of outstanding loads exact, so each step waits only for
 // the group it computes and not for the prefetches behind it.
-constexpr uint32_t kOutOfRange = 0x80000000u;   // > any unit's buffer size
+// 2^31: at least twice a unit's record range (kMaxUnitRecordBytes) and above
+// any pool (< 2^31).  The scalar offset of a not-live contiguous group is at
+// most a few records past the unit's range, so offset + kOutOfRange stays
+// below 2^32 and above every range, whether or not the hardware adds the
+// scalar offset before its range check.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+static_assert(kOutOfRange >= 2u * (uint32_t)kMaxUnitRecordBytes, "sentinel inside a unit's range");
 // cache policy of the history loads: non-temporal (each byte is read once per
 // step), which keeps them from displacing other lines in the caches
 constexpr int kStream = 2;
@@ -1134,19 +1150,30 @@ Residency residency(int bits, int meta, int variant, bool paged) {
 // with equal shares, the ranks finish their loops at about 19, 24 and 30 us;
 // the defaults come from a sweep of the launch time there and at the 32K
 // 4-bit workload (two per compute unit).  KIVI_RANK_WEIGHTS="w0,w1,w2,w3"
-// (positive integers) overrides them, for sweeps.
+// (positive integers) overrides them, for sweeps; like every tuning variable
+// of the library it is read once per process, at the first launch.
+struct RankOverride {
+  int n = 0;
+  int w[4] = {0, 0, 0, 0};
+};
+RankOverride read_rank_override() {
+  RankOverride r;
+  if (const char *env = getenv("KIVI_RANK_WEIGHTS")) {
+    int v[4];
+    const int n = sscanf(env, "%d,%d,%d,%d", &v[0], &v[1], &v[2], &v[3]);
+    for (int i = 0; i < n && i < 4; ++i)
+      if (v[i] > 0 && v[i] <= 10000) r.w[r.n++] = v[i];
+      else break;
+  }
+  return r;
+}
 void rank_weights(int per_cu, int (&w)[4]) {
   static const int k3[4] = {100, 75, 55, 55};
   static const int k2[4] = {100, 70, 70, 70};
+  static const RankOverride ov = read_rank_override();   // once per process
   const int *src = per_cu == 3 ? k3 : per_cu == 2 ? k2 : nullptr;
   for (int i = 0; i < 4; ++i) w[i] = src ? src[i] : 100;
-  const char *env = getenv("KIVI_RANK_WEIGHTS");
-  if (env) {
-    int v[4], n = sscanf(env, "%d,%d,%d,%d", &v[0], &v[1], &v[2], &v[3]);
-    for (int i = 0; i < n && i < 4; ++i)
-      if (v[i] > 0 && v[i] <= 10000) w[i] = v[i];
-    for (int i = n; i < 4 && n > 0; ++i) w[i] = w[n - 1];
-  }
+  for (int i = 0; i < 4 && ov.n > 0; ++i) w[i] = ov.w[i < ov.n ? i : ov.n - 1];
 }
 
 // Workgroups per unit.  Cost model in the work units of wave_work (KiB):
@@ -1158,19 +1185,21 @@ void rank_weights(int per_cu, int (&w)[4]) {
 // is capped so that every wave has at least two groups' worth of bytes and
 // the workspace holds the partials.  MI355X sweeps: 6 per unit at the 8K GQA
 // workload (one round), 1-2 at the 13B-shaped MHA memory wall (batch
-// 64-316, many rounds).  KIVI_WPU fixes the count (sweeps).
+// 64-316, many rounds).  KIVI_WPU fixes the count (sweeps; read once per
+// process).
 int choose_wpu(int group_cost, const DecodeArgs &a, int slots) {
   constexpr double kWgFixed = 40.0;
   const long long n_rc = (a.n_res + G - 1) / G;
   const long long total = (long long)a.n_groups * group_cost + n_rc * 16;
-  long long cap = total / (4 * 2 * group_cost);
-  if (cap < 1) cap = 1;
-  if (cap > a.n_split) cap = a.n_split;   // workspace capacity in partials per unit
-  if (cap > 256) cap = 256;
-  if (const char *env = getenv("KIVI_WPU")) {
-    const long long v = atoll(env);
-    if (v >= 1) return (int)(v < cap ? v : cap);
-  }
+  // the bound the workspace is sized by (kivi_decode_workspace_bytes), and
+  // the workspace's capacity in partials per unit
+  long long cap = max_splits_for(a.n_groups, a.n_res, group_cost);
+  if (cap > a.n_split) cap = a.n_split;
+  static const long long env_wpu = [] {
+    const char *env = getenv("KIVI_WPU");
+    return env ? atoll(env) : 0ll;
+  }();
+  if (env_wpu >= 1) return (int)(env_wpu < cap ? env_wpu : cap);
   int best = 1;
   double best_t = 1e300;
   for (int w = 1; w <= cap; ++w) {
@@ -1184,20 +1213,20 @@ int choose_wpu(int group_cost, const DecodeArgs &a, int slots) {
 
 }  // namespace
 
-hipError_t launch_decode(int bits, int meta, const DecodeArgs &a_in, hipStream_t s) {
+hipError_t launch_decode(int bits, int meta, const DecodeArgs &a_in, bool deterministic,
+                         hipStream_t s) {
   int variant = (a_in.qpk + 3) / 4;   // 1..4
   DecodeArgs a = a_in;
   const bool paged = a_in.pages.table != nullptr;
   // Up to 4 query heads per kv head and at most one unit per compute unit:
   // the launch is a single round, whose end the slowest wave sets, so the
   // dynamic variant (one workgroup per compute unit, waves balanced by an
-  // LDS counter) is used.  Longer launches refill their slots as workgroups
-  // finish and keep the static variant.  KIVI_DYN=0/1 forces the choice.
-  if (variant == 1) {
+  // LDS counter) is used, unless the caller asked for bitwise-repeatable
+  // results (its summation order depends on timing).  Longer launches refill
+  // their slots as workgroups finish and keep the static variant.
+  if (variant == 1 && !deterministic) {
     const Residency rd = residency(bits, meta, kDynVariant, paged);
-    bool dyn = (long long)a_in.n_units <= (long long)rd.per_cu * rd.cus;
-    if (const char *env = getenv("KIVI_DYN")) dyn = atoi(env) != 0;
-    if (dyn) variant = kDynVariant;
+    if ((long long)a_in.n_units <= (long long)rd.per_cu * rd.cus) variant = kDynVariant;
   }
   const Residency res = residency(bits, meta, variant, paged);
   const int slots = res.per_cu * res.cus;

@@ -34,9 +34,13 @@ kivi_status check_geom(const kivi_geom *g) {
   if (g->residual % g->group != 0 || g->residual > 4096) return KIVI_E_UNSUPPORTED;
   if (g->q_per_kv > 16) return KIVI_E_UNSUPPORTED;
   if ((long long)g->batch * g->kv_heads > 65535) return KIVI_E_UNSUPPORTED;   // grid.y
+  if ((g->flags & ~KIVI_FLAG_DETERMINISTIC) != 0) return KIVI_E_UNSUPPORTED;
   if (g->max_tokens % g->group != 0) return KIVI_E_UNSUPPORTED;
-  // per-unit buffers are addressed with 32-bit offsets
-  if (g->max_tokens > (1 << 24)) return KIVI_E_UNSUPPORTED;
+  // a unit's records are addressed with 32-bit offsets, and the decode
+  // kernel's not-live offset (2^31) must lie beyond all of them
+  if ((long long)(g->max_tokens / g->group) * kivi::rec_bytes(g->bits, g->meta_format) >
+      kivi::kMaxUnitRecordBytes)
+    return KIVI_E_UNSUPPORTED;
   // keep every byte offset of every buffer inside 2^62
   const double units = (double)g->batch * g->kv_heads;
   if (units * ((double)g->max_tokens + g->residual + g->group) * g->head_dim * 8.0 > 4.0e18)
@@ -44,12 +48,9 @@ kivi_status check_geom(const kivi_geom *g) {
   return KIVI_OK;
 }
 
-// The quantised history is kept as group records (kivi.h) in the K_CODES
-// buffer; the other five history buffers are unused.
-
 kivi_status check_cache(const kivi_geom *g, const kivi_cache *c) {
   if (!c) return KIVI_E_NULL;
-  if (!c->k_codes || !c->k_res || !c->v_res) return KIVI_E_NULL;
+  if (!c->records || !c->k_res || !c->v_res) return KIVI_E_NULL;
   return KIVI_OK;
 }
 
@@ -65,14 +66,31 @@ kivi_status check_state(const kivi_geom *g, const kivi_cache *c) {
 long long units_of(const kivi_geom *g) { return (long long)g->batch * g->kv_heads; }
 
 // decode workspace: one arrival counter per unit (padded to 256 B), then the
-// split partials
+// split partials, QPK of kPartStride floats per (unit, split)
 size_t counters_bytes(const kivi_geom *g) {
   return ((size_t)units_of(g) * sizeof(unsigned) + 255) / 256 * 256;
 }
 
-int max_splits(const kivi_geom *g) {
-  const int ng = g->max_tokens / g->group;
-  return (ng + kivi::kMinGroupsPerSplit - 1) / kivi::kMinGroupsPerSplit + 1;
+size_t partial_bytes(const kivi_geom *g) {
+  return (size_t)units_of(g) * (size_t)g->q_per_kv * kivi::kPartStride * sizeof(float);
+}
+
+// KiB per quantised group in the launcher's cost model: codes (bits) plus
+// scale/zero (two fp32 arrays, or one 16-bit pair)
+int group_cost(const kivi_geom *g) { return g->bits + (g->meta_format == KIVI_META_FP16_BF16 ? 1 : 2); }
+
+// Workspace for a launch over n_q quantised and n_res residual tokens (the
+// caller has validated the geometry).
+size_t workspace_need(const kivi_geom *g, long long n_q, long long n_res) {
+  return counters_bytes(g) +
+         partial_bytes(g) * (size_t)kivi::max_splits_for(n_q / g->group, n_res, group_cost(g));
+}
+
+// Split partials per unit that a workspace of ws_bytes holds (the launcher's
+// capacity), at most kMaxSplits.
+int splits_capacity(const kivi_geom *g, size_t ws_bytes) {
+  const size_t n = (ws_bytes - counters_bytes(g)) / partial_bytes(g);
+  return n > (size_t)kivi::kMaxSplits ? kivi::kMaxSplits : (int)n;
 }
 
 // Quantise the G oldest residual tokens (ring slots res_start..+G-1, which
@@ -86,7 +104,7 @@ kivi_status enqueue_flush(const kivi_geom *g, kivi_cache *c, hipStream_t s) {
   a.src_tok0 = c->res_start;
   a.n_groups = 1; a.n_units = (int)units_of(g); a.dst_g0 = c->n_q / G;
   a.max_tokens = g->max_tokens; a.n_groups_cap = g->max_tokens / G;
-  a.k_codes = c->k_codes;
+  a.records = c->records;
   kivi_status st = hip_status(kivi::launch_quantize(g->bits, g->meta_format, a, s));
   if (st != KIVI_OK) return st;
   c->n_q += G;
@@ -113,17 +131,14 @@ kivi_status enqueue_append(const kivi_geom *g, kivi_cache *c, const uint16_t *k_
   return KIVI_OK;
 }
 
-// Validation shared by decode attention and the decode step.
-kivi_status check_attend_args(const kivi_geom *g, const kivi_cache *c, const uint16_t *q,
-                              const float *out, float softmax_scale, const void *ws,
-                              size_t ws_bytes) {
+// Validation shared by the decode-attention calls: the launch will attend
+// over (at most) n_q quantised and n_res residual tokens.
+kivi_status check_attend_args(const kivi_geom *g, long long n_q, long long n_res,
+                              const uint16_t *q, const float *out, float softmax_scale,
+                              const void *ws, size_t ws_bytes) {
   if (!q || !out) return KIVI_E_NULL;
-  size_t need = 0;
-  kivi_status st = kivi_decode_workspace_size(g, &need);
-  if (st != KIVI_OK) return st;
-  if (!ws || ws_bytes < need) return KIVI_E_WORKSPACE;
+  if (!ws || ws_bytes < workspace_need(g, n_q, n_res)) return KIVI_E_WORKSPACE;
   if (!isfinite(softmax_scale)) return KIVI_E_GEOMETRY;
-  (void)c;
   return KIVI_OK;
 }
 
@@ -132,12 +147,13 @@ kivi_status check_attend_args(const kivi_geom *g, const kivi_cache *c, const uin
 // into its ring slot by the kernel) instead of from the ring.
 kivi_status enqueue_attend(const kivi_geom *g, const kivi_cache *c, const uint16_t *k_new,
                            const uint16_t *v_new, const uint16_t *q, float *out,
-                           float softmax_scale, void *ws, hipStream_t s, int slots = 0,
+                           float softmax_scale, void *ws, size_t ws_bytes, hipStream_t s,
+                           int slots = 0,
                            const int32_t *state_in = nullptr, int32_t *state_out = nullptr,
                            const kivi::PageMap &pages = kivi::PageMap{}) {
   kivi::DecodeArgs a{};
   a.pages = pages;
-  a.k_codes = c->k_codes;
+  a.records = c->records;
   a.k_res = c->k_res; a.v_res = c->v_res;
   a.k_new = k_new; a.v_new = v_new;
   a.new_idx = k_new ? c->n_res - 1 : -1;
@@ -153,8 +169,9 @@ kivi_status enqueue_attend(const kivi_geom *g, const kivi_cache *c, const uint16
   a.n_res = c->n_res; a.res_start = c->res_start;
   a.state_in = state_in; a.state_out = state_out;
   // the launcher picks the workgroups per unit; pass the workspace capacity
-  a.n_split = max_splits(g);
-  return hip_status(kivi::launch_decode(g->bits, g->meta_format, a, s));
+  a.n_split = splits_capacity(g, ws_bytes);
+  return hip_status(kivi::launch_decode(g->bits, g->meta_format, a,
+                                        (g->flags & KIVI_FLAG_DETERMINISTIC) != 0, s));
 }
 
 }  // namespace
@@ -179,27 +196,23 @@ const char *kivi_status_string(kivi_status s) {
 
 int32_t kivi_last_hip_error(void) { return g_last_hip_error; }
 
-kivi_status kivi_cache_layout(const kivi_geom *g, size_t bytes[8]) {
+kivi_status kivi_cache_layout(const kivi_geom *g, size_t bytes[KIVI_NUM_BUFS]) {
   kivi_status st = check_geom(g);
   if (st != KIVI_OK) return st;
   if (!bytes) return KIVI_E_NULL;
   const size_t U = (size_t)units_of(g), D = (size_t)g->head_dim;
   const size_t NG = (size_t)(g->max_tokens / g->group);
   const size_t slots = (size_t)(g->residual + g->group);
-  bytes[KIVI_BUF_K_CODES] = U * NG * (size_t)kivi::rec_bytes(g->bits, g->meta_format);
-  for (int i = KIVI_BUF_K_SCALE; i <= KIVI_BUF_V_ZERO; ++i) bytes[i] = 0;
+  bytes[KIVI_BUF_RECORDS] = U * NG * (size_t)kivi::rec_bytes(g->bits, g->meta_format);
   bytes[KIVI_BUF_K_RES] = U * slots * D * 2;
   bytes[KIVI_BUF_V_RES] = U * slots * D * 2;
   return KIVI_OK;
 }
 
-kivi_status kivi_decode_workspace_size(const kivi_geom *g, size_t *bytes) {
-  kivi_status st = check_geom(g);
-  if (st != KIVI_OK) return st;
-  if (!bytes) return KIVI_E_NULL;
-  *bytes = counters_bytes(g) + (size_t)units_of(g) * (size_t)max_splits(g) *
-                                   (size_t)g->q_per_kv * (size_t)kivi::kPartStride * sizeof(float);
-  return KIVI_OK;
+size_t kivi_decode_workspace_bytes(const kivi_geom *g, int32_t n_q, int32_t n_res) {
+  if (check_geom(g) != KIVI_OK) return 0;
+  if (n_q < 0 || n_q > g->max_tokens || n_q % g->group != 0 || n_res < 0) return 0;
+  return workspace_need(g, n_q, n_res);
 }
 
 kivi_status kivi_quantize_prefill(const kivi_geom *g, kivi_cache *c, const uint16_t *k,
@@ -222,7 +235,7 @@ kivi_status kivi_quantize_prefill(const kivi_geom *g, kivi_cache *c, const uint1
     a.src_tok0 = 0;
     a.n_groups = n_q / G; a.n_units = U; a.dst_g0 = 0;
     a.max_tokens = g->max_tokens; a.n_groups_cap = g->max_tokens / G;
-    a.k_codes = c->k_codes;
+    a.records = c->records;
       if ((st = hip_status(kivi::launch_quantize(g->bits, g->meta_format, a, s))) != KIVI_OK) return st;
   }
   if (r > 0) {
@@ -273,10 +286,12 @@ kivi_status kivi_decode_attention(const kivi_geom *g, const kivi_cache *c, const
   kivi_status st = check_geom(g);
   if (st != KIVI_OK) return st;
   if ((st = check_cache(g, c)) != KIVI_OK) return st;
-  if ((st = check_attend_args(g, c, q, out, softmax_scale, ws, ws_bytes)) != KIVI_OK) return st;
   if ((st = check_state(g, c)) != KIVI_OK) return st;
+  if ((st = check_attend_args(g, c->n_q, c->n_res, q, out, softmax_scale, ws, ws_bytes)) != KIVI_OK)
+    return st;
   if (c->n_q + c->n_res == 0) return KIVI_E_STATE;
-  return enqueue_attend(g, c, nullptr, nullptr, q, out, softmax_scale, ws, (hipStream_t)stream);
+  return enqueue_attend(g, c, nullptr, nullptr, q, out, softmax_scale, ws, ws_bytes,
+                        (hipStream_t)stream);
 }
 
 kivi_status kivi_decode_step(const kivi_geom *g, kivi_cache *c, const uint16_t *k_new,
@@ -287,12 +302,16 @@ kivi_status kivi_decode_step(const kivi_geom *g, kivi_cache *c, const uint16_t *
   if (st != KIVI_OK) return st;
   if ((st = check_cache(g, c)) != KIVI_OK) return st;
   if (!k_new || !v_new) return KIVI_E_NULL;
-  if ((st = check_attend_args(g, c, q, out, softmax_scale, ws, ws_bytes)) != KIVI_OK) return st;
   if ((st = check_state(g, c)) != KIVI_OK) return st;
   const int G = g->group, slots = g->residual + G;
   if (c->n_res == slots) return KIVI_E_RESIDUAL_FULL;
   const bool flush = c->n_res + 1 == slots;
   if (flush && c->n_q + G > g->max_tokens) return KIVI_E_CAPACITY;
+  // the attention runs over the counters after the step
+  const long long nq_after = c->n_q + (flush ? G : 0), nres_after = c->n_res + 1 - (flush ? G : 0);
+  if ((st = check_attend_args(g, nq_after, nres_after, q, out, softmax_scale, ws, ws_bytes)) !=
+      KIVI_OK)
+    return st;
   if (flushed) *flushed = 0;
   hipStream_t s = (hipStream_t)stream;
   if (flush && g->residual == 0) {
@@ -301,7 +320,7 @@ kivi_status kivi_decode_step(const kivi_geom *g, kivi_cache *c, const uint16_t *
     if ((st = enqueue_append(g, c, k_new, v_new, s)) != KIVI_OK) return st;
     if ((st = enqueue_flush(g, c, s)) != KIVI_OK) return st;
     if (flushed) *flushed = 1;
-    return enqueue_attend(g, c, nullptr, nullptr, q, out, softmax_scale, ws, s);
+    return enqueue_attend(g, c, nullptr, nullptr, q, out, softmax_scale, ws, ws_bytes, s);
   }
   if (flush) {
     // With R >= G the G oldest tokens of the full ring exclude the new one
@@ -314,7 +333,8 @@ kivi_status kivi_decode_step(const kivi_geom *g, kivi_cache *c, const uint16_t *
   // attention with the append fused: the new token is logical index n_res
   kivi_cache next = *c;
   next.n_res += 1;
-  if ((st = enqueue_attend(g, &next, k_new, v_new, q, out, softmax_scale, ws, s)) != KIVI_OK)
+  if ((st = enqueue_attend(g, &next, k_new, v_new, q, out, softmax_scale, ws, ws_bytes, s)) !=
+      KIVI_OK)
     return st;
   c->n_res = next.n_res;
   return KIVI_OK;
@@ -327,9 +347,9 @@ kivi_status kivi_dense_decode_attention(const kivi_geom *g, const uint16_t *k, c
   kivi_status st = check_geom(g);
   if (st != KIVI_OK) return st;
   if (!k || !v) return KIVI_E_NULL;
-  if ((st = check_attend_args(g, nullptr, q, out, softmax_scale, ws, ws_bytes)) != KIVI_OK)
-    return st;
   if (seq_len < 1 || seq_len > g->max_tokens) return KIVI_E_SEQLEN;
+  if ((st = check_attend_args(g, 0, seq_len, q, out, softmax_scale, ws, ws_bytes)) != KIVI_OK)
+    return st;
   // the dense cache is read as a residual of seq_len tokens in a "ring" of
   // max_tokens slots starting at slot 0; there is no quantised history
   kivi_cache c{};
@@ -338,8 +358,8 @@ kivi_status kivi_dense_decode_attention(const kivi_geom *g, const uint16_t *k, c
   c.n_q = 0;
   c.n_res = seq_len;
   c.res_start = 0;
-  return enqueue_attend(g, &c, nullptr, nullptr, q, out, softmax_scale, ws, (hipStream_t)stream,
-                        g->max_tokens);
+  return enqueue_attend(g, &c, nullptr, nullptr, q, out, softmax_scale, ws, ws_bytes,
+                        (hipStream_t)stream, g->max_tokens);
 }
 
 }  // extern "C"
@@ -367,7 +387,7 @@ kivi_status ragged_prefill_impl(const kivi_geom *g, const kivi_cache *c, const k
     a.src_tok0 = 0;
     a.n_groups = nq_max / G; a.n_units = (int)units_of(g); a.dst_g0 = 0;
     a.max_tokens = g->max_tokens; a.n_groups_cap = g->max_tokens / G;
-    a.k_codes = c->k_codes;
+    a.records = c->records;
       a.seq_lens = seq_lens;
     a.kv_heads = g->kv_heads; a.residual = R; a.slots = slots; a.stride = stride;
     a.pages = pm;
@@ -391,7 +411,9 @@ kivi_status ragged_step_impl(const kivi_geom *g, const kivi_cache *c, const kivi
   kivi_status st = KIVI_OK;
   if (!state_in || !state_out || !k_new || !v_new) return KIVI_E_NULL;
   if (state_in == state_out) return KIVI_E_STATE;
-  if ((st = check_attend_args(g, c, q, out, softmax_scale, ws, ws_bytes)) != KIVI_OK) return st;
+  if ((st = check_attend_args(g, g->max_tokens, g->residual + g->group, q, out, softmax_scale, ws,
+                              ws_bytes)) != KIVI_OK)
+    return st;
   // the flush runs before the fused append, which needs R >= G (see
   // kivi_decode_step)
   if (g->residual < g->group) return KIVI_E_UNSUPPORTED;
@@ -402,7 +424,7 @@ kivi_status ragged_step_impl(const kivi_geom *g, const kivi_cache *c, const kivi
   f.src_unit_stride = (long long)slots * g->head_dim;
   f.n_groups = 1; f.n_units = (int)units_of(g);
   f.max_tokens = g->max_tokens; f.n_groups_cap = g->max_tokens / G;
-  f.k_codes = c->k_codes;
+  f.records = c->records;
   f.state = state_in;
   f.kv_heads = g->kv_heads; f.residual = g->residual; f.slots = slots;
   f.pages = pm;
@@ -414,8 +436,8 @@ kivi_status ragged_step_impl(const kivi_geom *g, const kivi_cache *c, const kivi
   bound.n_q = g->max_tokens / G * G;
   bound.n_res = slots;
   bound.res_start = 0;
-  return enqueue_attend(g, &bound, k_new, v_new, q, out, softmax_scale, ws, s, 0, state_in,
-                        state_out, pm);
+  return enqueue_attend(g, &bound, k_new, v_new, q, out, softmax_scale, ws, ws_bytes, s, 0,
+                        state_in, state_out, pm);
 }
 
 // Page map of a paged cache; KIVI_E_NULL / KIVI_E_UNSUPPORTED when the pool
@@ -423,8 +445,8 @@ kivi_status ragged_step_impl(const kivi_geom *g, const kivi_cache *c, const kivi
 kivi_status paged_map(const kivi_geom *g, const kivi_paged_cache *pc, kivi::PageMap &pm,
                       kivi_cache &c) {
   if (!pc) return KIVI_E_NULL;
-  if (!pc->k_codes || !pc->k_res || !pc->v_res || !pc->block_table) return KIVI_E_NULL;
-  size_t bytes[8];
+  if (!pc->records || !pc->k_res || !pc->v_res || !pc->block_table) return KIVI_E_NULL;
+  size_t bytes[KIVI_NUM_BUFS];
   int32_t max_pages = 0;
   kivi_status st = kivi_paged_layout(g, pc->page_groups, pc->num_pages, bytes, &max_pages);
   if (st != KIVI_OK) return st;
@@ -435,8 +457,7 @@ kivi_status paged_map(const kivi_geom *g, const kivi_paged_cache *pc, kivi::Page
   pm.max_pages = max_pages;
   pm.num_pages = pc->num_pages;
   c = kivi_cache{};
-  c.k_codes = pc->k_codes; c.k_scale = pc->k_scale; c.k_zero = pc->k_zero;
-  c.v_codes = pc->v_codes; c.v_scale = pc->v_scale; c.v_zero = pc->v_zero;
+  c.records = pc->records;
   c.k_res = pc->k_res; c.v_res = pc->v_res;
   return KIVI_OK;
 }
@@ -468,7 +489,7 @@ kivi_status kivi_ragged_decode_step(const kivi_geom *g, const kivi_cache *c,
 }
 
 kivi_status kivi_paged_layout(const kivi_geom *g, int32_t page_groups, int32_t num_pages,
-                              size_t bytes[8], int32_t *max_pages) {
+                              size_t bytes[KIVI_NUM_BUFS], int32_t *max_pages) {
   kivi_status st = check_geom(g);
   if (st != KIVI_OK) return st;
   if (!bytes) return KIVI_E_NULL;
@@ -482,8 +503,7 @@ kivi_status kivi_paged_layout(const kivi_geom *g, int32_t page_groups, int32_t n
   const size_t rec = (size_t)kivi::rec_bytes(g->bits, g->meta_format);
   if (groups * rec >= 2147483648.0) return KIVI_E_UNSUPPORTED;
   const size_t n = (size_t)groups;
-  bytes[KIVI_BUF_K_CODES] = n * rec;
-  for (int i = KIVI_BUF_K_SCALE; i <= KIVI_BUF_V_ZERO; ++i) bytes[i] = 0;
+  bytes[KIVI_BUF_RECORDS] = n * rec;
   bytes[KIVI_BUF_K_RES] = (size_t)units_of(g) * slots * D * 2;
   bytes[KIVI_BUF_V_RES] = (size_t)units_of(g) * slots * D * 2;
   if (max_pages) {

@@ -12,7 +12,26 @@ namespace kivi {
 constexpr int kHeadDim = 128;      // supported head_dim
 constexpr int kGroup = 32;         // supported group size G
 constexpr int kPartStride = 132;   // floats per split partial: m, l, pad, pad, o[128]
-constexpr int kMinGroupsPerSplit = 4;   // sizes the workspace: NG/4 + 1 partials per unit
+constexpr int kMaxSplits = 256;    // workgroups per unit of one decode launch, at most
+
+// Largest byte range of one unit's group records (its NG records).  The
+// decode kernel's out-of-range load offset (2^31) relies on it; the host
+// refuses geometries beyond it.
+constexpr long long kMaxUnitRecordBytes = 1ll << 30;
+
+// Upper bound on the workgroups (split partials) per unit of a decode launch
+// over n_groups quantised groups and n_res residual tokens, in the cost units
+// of the launcher (KiB: a group costs group_cost, a residual chunk of 32
+// tokens 16): every wave keeps at least two groups' worth of work.  The
+// workspace is sized by this bound and the launcher never exceeds it.
+__host__ __device__ inline int max_splits_for(long long n_groups, long long n_res,
+                                              int group_cost) {
+  const long long total = n_groups * group_cost + (n_res + 31) / 32 * 16;
+  long long cap = total / (4 * 2 * group_cost);
+  if (cap < 1) cap = 1;
+  if (cap > kMaxSplits) cap = kMaxSplits;
+  return (int)cap;
+}
 
 // Per-sequence state of a mixed-length batch (device memory): int32
 // {n_q, n_res, res_start, flags} per sequence.  Flag bits (kivi.h):
@@ -99,7 +118,7 @@ struct QuantizeArgs {
   int n_groups, n_units;
   int dst_g0;
   int max_tokens, n_groups_cap;  // T, NG
-  uint8_t *k_codes;   // group records
+  uint8_t *records;   // group records
   int gpw;   // groups per workgroup (set by the launcher)
   // Mixed-length batches (null otherwise).  seq_lens (prefill): sequence b
   // quantises its own n_q tokens, n_groups being the largest count.  state
@@ -138,7 +157,7 @@ struct RaggedResidualArgs {
 hipError_t launch_ragged_residual(const RaggedResidualArgs &a, hipStream_t s);
 
 struct DecodeArgs {
-  const uint8_t *k_codes;    // group records
+  const uint8_t *records;    // group records
   uint16_t *k_res, *v_res;   // written only for the fused append below
   // Fused append: logical residual token new_idx (-1: none) is taken from
   // k_new / v_new ([units][D] bf16) instead of the ring, and the one wave
@@ -154,7 +173,8 @@ struct DecodeArgs {
   int n_units;
   int n_groups;       // quantised groups in the cache (n_q / G)
   int n_res, res_start;
-  int n_split;        // workgroups per unit (the host passes the workspace capacity)
+  int n_split;        // workgroups per unit (the host passes the workspace capacity,
+                      // at most kMaxSplits)
   // Mixed-length batches: with state_in set the counters above are upper
   // bounds (for the launch shape) and each sequence reads its own {n_q, n_res,
   // res_start, flags} from state_in, applies this step's flush (done by the
@@ -171,6 +191,9 @@ struct DecodeArgs {
   int cus;
   int rank_w[4];
 };
-hipError_t launch_decode(int bits, int meta, const DecodeArgs &a, hipStream_t s);
+// deterministic: keep to the static launch variant, whose results are
+// bitwise repeatable for the same inputs on the same device.
+hipError_t launch_decode(int bits, int meta, const DecodeArgs &a, bool deterministic,
+                         hipStream_t s);
 
 }  // namespace kivi

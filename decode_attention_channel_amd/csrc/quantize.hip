@@ -138,7 +138,7 @@ __device__ __forceinline__ void key_group(const QuantizeArgs &a, int u, int gl,
   group_params<BITS, META>(mn0, mx0, sc0, inv0, sb0);
   group_params<BITS, META>(mn1, mx1, sc1, inv1, sb1);
   if (h == 0) {
-    uint8_t *rec = a.k_codes + slot * rec_bytes(BITS, META);
+    uint8_t *rec = a.records + slot * rec_bytes(BITS, META);
     const int c = cb + 2 * p;   // channels c, c + 1: one lane's value pair
     if constexpr (META == 1) {
       *reinterpret_cast<uint32_t *>(rec + rec_meta<BITS, META>(0, c)) = sb0 | (sb1 << 16);
@@ -160,7 +160,7 @@ __device__ __forceinline__ void key_group(const QuantizeArgs &a, int u, int gl,
   const uint4 b0 = *reinterpret_cast<const uint4 *>(tile + row * 64 + c32);
   const uint4 b1 = *reinterpret_cast<const uint4 *>(tile + row * 64 + c32 + 16);
   // the packed row piece: 32 channels of token `row`
-  uint8_t *dst = a.k_codes + slot * rec_bytes(BITS, META) + rec_k_piece<BITS>(row, (cb + c32) / 32);
+  uint8_t *dst = a.records + slot * rec_bytes(BITS, META) + rec_k_piece<BITS>(row, (cb + c32) / 32);
   if constexpr (BITS == 2) {
     const uint32_t w0 = pack4x2(b0.x) | (pack4x2(b0.y) << 8) | (pack4x2(b0.z) << 16) |
                         (pack4x2(b0.w) << 24);
@@ -229,7 +229,7 @@ __device__ __forceinline__ void value_group(const QuantizeArgs &a, int u, int gl
   uint32_t sb;
   group_params<BITS, META>(mn, mx, sc, inv, sb);
   {
-    uint8_t *rec = a.k_codes + slot * rec_bytes(BITS, META);
+    uint8_t *rec = a.records + slot * rec_bytes(BITS, META);
     const int v = q * G + 16 * part + r;   // value index within the group
     if constexpr (META == 1) {
       *reinterpret_cast<uint16_t *>(rec + rec_meta<BITS, META>(2, v)) = (uint16_t)sb;
@@ -258,7 +258,7 @@ __device__ __forceinline__ void value_group(const QuantizeArgs &a, int u, int gl
 #pragma unroll
     for (int i = 0; i < 4; ++i) cell[i] |= ((w >> (8 * i)) & 0xFFu) << (BITS * k);
   }
-  uint8_t *dst = a.k_codes + slot * rec_bytes(BITS, META) + rec_v_cell<BITS>(2 * part + o, c4);
+  uint8_t *dst = a.records + slot * rec_bytes(BITS, META) + rec_v_cell<BITS>(2 * part + o, c4);
   if constexpr (BITS == 2) {
     *reinterpret_cast<uint2 *>(dst) = make_uint2(cell[0] | (cell[1] << 16), cell[2] | (cell[3] << 16));
   } else {
@@ -406,10 +406,12 @@ hipError_t launch_quantize(int bits, int meta, const QuantizeArgs &a_in, hipStre
   // groups per workgroup: one.  Short independent workgroups keep the most
   // loads in flight; on MI355X at the 8K GQA prefill (16 x 8 units, 252
   // groups each) 1 group per workgroup runs at 5.4 TB/s, 2 at 5.2, 4 at 4.8,
-  // 8 at 4.5.  KIVI_QGPW sets another count (sweeps).
+  // 8 at 4.5.  KIVI_QGPW sets another count (sweeps; read once per process).
   QuantizeArgs a = a_in;
-  long long gpw = 1;
-  if (const char *env = getenv("KIVI_QGPW")) gpw = atoll(env);
+  static const long long gpw = [] {
+    const char *env = getenv("KIVI_QGPW");
+    return env ? atoll(env) : 1ll;
+  }();
   a.gpw = (int)(gpw < 1 ? 1 : gpw > 8 ? 8 : gpw);
   const dim3 grid((a.n_groups + a.gpw - 1) / a.gpw, a.n_units), block(256);
   if (bits == 2 && meta == 0)

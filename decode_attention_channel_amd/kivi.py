@@ -23,14 +23,15 @@ STATUS = {
     7: "KIVI_E_WORKSPACE", 8: "KIVI_E_HIP", 9: "KIVI_E_STATE",
 }
 EXPORTS = (
-    "kivi_cache_layout", "kivi_decode_workspace_size", "kivi_quantize_prefill",
+    "kivi_cache_layout", "kivi_decode_workspace_bytes", "kivi_quantize_prefill",
     "kivi_append_token", "kivi_flush_residual", "kivi_decode_attention",
     "kivi_decode_step", "kivi_dense_decode_attention", "kivi_ragged_prefill",
     "kivi_ragged_decode_step", "kivi_paged_layout", "kivi_paged_prefill",
     "kivi_paged_decode_step", "kivi_status_string", "kivi_last_hip_error",
 )
-BUFFERS = ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero", "k_res", "v_res")
+BUFFERS = ("records", "k_res", "v_res")   # order of the KIVI_BUF_* sizes
 META_FP32, META_FP16_BF16 = 0, 1   # scale/zero formats (kivi_geom.meta_format)
+FLAG_DETERMINISTIC = 1              # kivi_geom.flags: bitwise-repeatable decode launches
 SEQ_BAD_LENGTH, SEQ_FULL = 1, 2     # per-sequence state flags (mixed-length batches)
 
 
@@ -47,7 +48,7 @@ class KiviError(RuntimeError):
 class _Geom(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "kv_heads", "q_per_kv", "head_dim", "bits", "group", "residual",
-        "max_tokens", "meta_format")]
+        "max_tokens", "meta_format", "flags")]
 
 
 class _Cache(ctypes.Structure):
@@ -69,7 +70,7 @@ def _load():
     G, C, P = ctypes.POINTER(_Geom), ctypes.POINTER(_Cache), ctypes.c_void_p
     sz = ctypes.POINTER(ctypes.c_size_t)
     lib.kivi_cache_layout.argtypes = [G, sz]
-    lib.kivi_decode_workspace_size.argtypes = [G, sz]
+    lib.kivi_decode_workspace_bytes.argtypes = [G, ctypes.c_int32, ctypes.c_int32]
     lib.kivi_quantize_prefill.argtypes = [G, C, P, P, ctypes.c_int32, P]
     lib.kivi_append_token.argtypes = [G, C, P, P, P]
     lib.kivi_flush_residual.argtypes = [G, C, ctypes.POINTER(ctypes.c_int32), P]
@@ -89,6 +90,7 @@ def _load():
                                            ctypes.c_size_t, P]
     for f in EXPORTS[:-2]:
         getattr(lib, f).restype = ctypes.c_int
+    lib.kivi_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.kivi_status_string.argtypes = [ctypes.c_int]
     lib.kivi_status_string.restype = ctypes.c_char_p
     lib.kivi_last_hip_error.restype = ctypes.c_int32
@@ -117,6 +119,7 @@ class Geom:
     residual: int = 128
     max_tokens: int = 0
     meta_format: int = META_FP32
+    flags: int = 0
 
     def c(self) -> _Geom:
         return _Geom(*dataclasses.astuple(self))
@@ -125,6 +128,10 @@ class Geom:
     def q_heads(self) -> int:
         return self.kv_heads * self.q_per_kv
 
+    @property
+    def slots(self) -> int:
+        return self.residual + self.group
+
 
 def _check(status: int, where: str):
     if status != 0:
@@ -132,16 +139,22 @@ def _check(status: int, where: str):
 
 
 def cache_layout(g: Geom) -> list[int]:
-    out = (ctypes.c_size_t * 8)()
+    """Byte sizes of the cache buffers, in the order of BUFFERS."""
+    out = (ctypes.c_size_t * len(BUFFERS))()
     _check(_lib.kivi_cache_layout(ctypes.byref(g.c()), out), "kivi_cache_layout")
     return list(out)
 
 
-def workspace_size(g: Geom) -> int:
-    out = ctypes.c_size_t(0)
-    _check(_lib.kivi_decode_workspace_size(ctypes.byref(g.c()), ctypes.byref(out)),
-           "kivi_decode_workspace_size")
-    return out.value
+def workspace_bytes(g: Geom, n_q: int | None = None, n_res: int | None = None) -> int:
+    """kivi_decode_workspace_bytes; by default for the fullest cache state
+    (n_q = max_tokens, n_res = R+G), which serves every state."""
+    n_q = g.max_tokens if n_q is None else n_q
+    n_res = g.slots if n_res is None else n_res
+    n = _lib.kivi_decode_workspace_bytes(ctypes.byref(g.c()), n_q, n_res)
+    if n == 0:
+        raise ValueError(f"kivi_decode_workspace_bytes: invalid geometry or counts "
+                         f"({g}, n_q={n_q}, n_res={n_res})")
+    return n
 
 
 def _stream() -> ctypes.c_void_p:
@@ -162,24 +175,6 @@ def _ptr(t: torch.Tensor, dtype, shape=None, name="tensor") -> ctypes.c_void_p:
 
 def record_bytes(g: Geom) -> int:
     return 1024 * (g.bits + (1 if g.meta_format == META_FP16_BF16 else 2))
-
-
-def _group_shapes(g: Geom) -> dict:
-    """(shape, dtype) of one group's part of each of the six history buffers
-    (group records: all in k_codes, the other five empty; they keep the
-    scale and zero dtypes)."""
-    m16 = g.meta_format == META_FP16_BF16
-    st = torch.float16 if m16 else torch.float32   # scale
-    zt = torch.bfloat16 if m16 else torch.float32  # zero
-    return {"k_codes": ((record_bytes(g),), torch.uint8), "k_scale": (None, st),
-            "k_zero": (None, zt), "v_codes": (None, torch.uint8), "v_scale": (None, st),
-            "v_zero": (None, zt)}
-
-
-def _history_shapes(g: Geom, lead: tuple) -> dict:
-    """Tensor shapes of the six history buffers for `lead` group slots
-    (empty buffers: shape (0,))."""
-    return {n: ((0,) if sh is None else lead + sh, dt) for n, (sh, dt) in _group_shapes(g).items()}
 
 
 def records_to_arrays(rec: np.ndarray, bits: int, meta: int) -> dict:
@@ -218,7 +213,8 @@ def records_to_arrays(rec: np.ndarray, bits: int, meta: int) -> dict:
 
 
 class Cache:
-    """The eight cache buffers (torch tensors, shaped by the documented layout)
+    """The cache buffers (torch tensors, shaped by the documented layout:
+    records uint8 [B][H][NG][record bytes], k_res / v_res bf16 [B][H][R+G][D])
     and the host-side counters."""
 
     def __init__(self, g: Geom, device=None):
@@ -226,9 +222,9 @@ class Cache:
         sizes = cache_layout(g)
         B, H, D = g.batch, g.kv_heads, g.head_dim
         NG, S = g.max_tokens // g.group, g.residual + g.group
-        shapes = _history_shapes(g, (B, H, NG))
-        shapes["k_res"] = ((B, H, S, D), torch.bfloat16)
-        shapes["v_res"] = ((B, H, S, D), torch.bfloat16)
+        shapes = {"records": ((B, H, NG, record_bytes(g)), torch.uint8),
+                  "k_res": ((B, H, S, D), torch.bfloat16),
+                  "v_res": ((B, H, S, D), torch.bfloat16)}
         self.geom = g
         for (name, (shape, dt)), nbytes in zip(shapes.items(), sizes):
             t = torch.empty(shape, dtype=dt, device=device)
@@ -261,7 +257,7 @@ class Cache:
         group records the cache keeps."""
         g = self.geom
         B, H, NG = g.batch, g.kv_heads, g.max_tokens // g.group
-        arr = records_to_arrays(self.k_codes.cpu().numpy().reshape(B * H * NG, -1), g.bits,
+        arr = records_to_arrays(self.records.cpu().numpy().reshape(B * H * NG, -1), g.bits,
                                 g.meta_format)
         out = {n: a.reshape((B, H, NG) + a.shape[1:]) for n, a in arr.items()}
         out["k_codes"] = out["k_codes"].reshape(B, H, NG * g.group, -1)
@@ -269,7 +265,7 @@ class Cache:
 
 
 def paged_layout(g: Geom, page_groups: int, num_pages: int) -> tuple[list[int], int]:
-    out = (ctypes.c_size_t * 8)()
+    out = (ctypes.c_size_t * len(BUFFERS))()
     mp = ctypes.c_int32(0)
     _check(_lib.kivi_paged_layout(ctypes.byref(g.c()), page_groups, num_pages, out,
                                   ctypes.byref(mp)), "kivi_paged_layout")
@@ -286,9 +282,9 @@ class PagedCache:
         sizes, self.max_pages = paged_layout(g, page_groups, num_pages)
         B, H, D = g.batch, g.kv_heads, g.head_dim
         n, S = num_pages * H * page_groups, g.residual + g.group
-        shapes = _history_shapes(g, (n,))
-        shapes["k_res"] = ((B, H, S, D), torch.bfloat16)
-        shapes["v_res"] = ((B, H, S, D), torch.bfloat16)
+        shapes = {"records": ((n, record_bytes(g)), torch.uint8),
+                  "k_res": ((B, H, S, D), torch.bfloat16),
+                  "v_res": ((B, H, S, D), torch.bfloat16)}
         self.geom, self.page_groups, self.num_pages = g, page_groups, num_pages
         for (name, (shape, dt)), nbytes in zip(shapes.items(), sizes):
             t = torch.empty(shape, dtype=dt, device=device)
@@ -303,7 +299,7 @@ class PagedCache:
         """Host copy of the pool in the per-array per-slot layout (k_codes
         [slots][G][D*b/8], k_scale [slots][D], ...) from its group records."""
         g = self.geom
-        return records_to_arrays(self.k_codes.cpu().numpy(), g.bits, g.meta_format)
+        return records_to_arrays(self.records.cpu().numpy(), g.bits, g.meta_format)
 
     def slot(self, b: int, h: int, g: int, table=None) -> int:
         """Pool slot of group g of (sequence b, kv head h); -1 without a page."""
@@ -378,12 +374,14 @@ def flush_residual(g: Geom, c: Cache) -> int:
 
 
 class Workspace:
-    """Device workspace for decode attention, sized for a geometry and
-    zero-filled once (the calls leave its arrival counters at zero)."""
+    """Device workspace for decode attention, zero-filled once (the calls
+    leave its arrival counters at zero).  Sized by kivi_decode_workspace_bytes
+    for a cache of n_q quantised and n_res residual tokens; by default for the
+    fullest state of the geometry, which serves every call on it."""
 
-    def __init__(self, g: Geom, device=None):
+    def __init__(self, g: Geom, device=None, n_q: int | None = None, n_res: int | None = None):
         device = torch.device("cuda", torch.cuda.current_device()) if device is None else device
-        self.nbytes = workspace_size(g)
+        self.nbytes = workspace_bytes(g, n_q, n_res)
         self.buf = torch.zeros(max(self.nbytes, 16), dtype=torch.uint8, device=device)
 
 

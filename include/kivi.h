@@ -35,11 +35,26 @@
  *    left unchanged.  No exception crosses the ABI.  KIVI_E_HIP is returned
  *    when a launch fails; kivi_last_hip_error() then gives the hipError_t.
  *  - Supported set (v1): bits in {2,4}; group == 32; head_dim == 128;
- *    meta_format in {KIVI_META_FP32, KIVI_META_FP16_BF16};
- *    residual a multiple of group with 0 <= residual <= 4096;
- *    1 <= q_per_kv <= 16; max_tokens a multiple of group, at most 2^24;
- *    batch, kv_heads >= 1 with batch * kv_heads <= 65535.  Anything else:
- *    KIVI_E_UNSUPPORTED (or KIVI_E_GEOMETRY for non-positive sizes).
+ *    meta_format in {KIVI_META_FP32, KIVI_META_FP16_BF16}; flags a
+ *    combination of KIVI_FLAG_*; residual a multiple of group with
+ *    0 <= residual <= 4096; 1 <= q_per_kv <= 16; max_tokens a multiple of
+ *    group whose records take at most 2^30 bytes per (sequence, kv head),
+ *    i.e. (max_tokens / 32) * record bytes <= 2^30 (max_tokens <= 8,388,608
+ *    at 2-bit with fp32 scale/zero, 5,592,384 at 4-bit); batch, kv_heads >= 1
+ *    with batch * kv_heads <= 65535.  Anything else: KIVI_E_UNSUPPORTED (or
+ *    KIVI_E_GEOMETRY for non-positive sizes).
+ *  - Repeatability.  With KIVI_FLAG_DETERMINISTIC in geom.flags every
+ *    decode-attention launch (kivi_decode_attention, kivi_decode_step, the
+ *    dense, mixed-length and paged calls) splits its work the same way each
+ *    time and sums in a fixed order: the same inputs on the same device give
+ *    bitwise the same output.  Without it, a launch of at most 4 query heads
+ *    per kv head and at most one (sequence, kv head) per compute unit (the
+ *    Llama-3-8B-shaped batch of 16 at 8K tokens is one) lets the waves of a
+ *    workgroup take token groups as they become free; the grouping of the
+ *    fp32 online-softmax sums then depends on timing, and two calls on the
+ *    same inputs can differ in the last bits (measured: below 1e-5 of the
+ *    row's largest output; the bound of the accuracy target, 1e-3, holds
+ *    for both).  Quantised codes and scale/zero bytes never depend on it.
  *  - The whole batch moves in lockstep: one (n_q, n_res, res_start) triple
  *    describes every sequence of the batch.
  *  - Numbers: bf16 tensors are passed as uint16_t bit patterns.  Inputs must
@@ -98,9 +113,8 @@
  *           Element type by geom.meta_format: KIVI_META_FP32 -- fp32 scale and
  *           fp32 zero; KIVI_META_FP16_BF16 -- fp16 scale bits and bf16 zero
  *           bits (uint16_t), see "16-bit scale/zero" below.
- *  Group records: the quantised history is one buffer, k_codes
- *           (kivi_cache_layout gives the five other history buffers size 0;
- *           their pointers are ignored and may be NULL), of one record per
+ *  Group records: the six arrays above are not stored as six buffers.  The
+ *           quantised history is one buffer, `records`, of one record per
  *           group: uint8 [B][H][NG][P * 1024], P = b + 2 (fp32 scale/zero)
  *           or b + 1 (16-bit).  Bytes are laid out in the order one 64-lane
  *           wave of the decode kernel reads them: plane p (1024 bytes) holds
@@ -129,8 +143,9 @@
  *  codes (channels for q.K^T, tokens for P.V), orthogonal to the group.
  *
  * ------------------------------------------------------------------------
- * Cache state machine (READING of "the most recent R tokens stay in bf16
- * until flushed into a new group", [record] KV bytes basis)
+ * Cache state machine (READING of [record] KV bytes basis: a bf16 residual of
+ * the latest R tokens sits beside the grouped history, which alone is
+ * quantised; the pages do not say when tokens leave the residual)
  * ------------------------------------------------------------------------
  *  prefill(S):  n_q = G*floor((S-R)/G) if S > R else 0;  n_res = S - n_q
  *               (so R <= n_res < R+G once S >= R);  res_start = 0.
@@ -169,9 +184,16 @@ enum {
   KIVI_META_FP16_BF16 = 1    /* fp16 scale, bf16 zero (uint16_t bit patterns) */
 };
 
+/* Launch options (kivi_geom.flags). */
+enum {
+  KIVI_FLAG_DETERMINISTIC = 1   /* bitwise-repeatable decode attention (see
+                                 * "Repeatability" above)                    */
+};
+
 /* Problem statement: batch, kv heads, query heads per kv head (GQA),
  * head_dim, bits, group size G, residual length R, the capacity of the
- * quantised history in tokens, and the scale/zero format (KIVI_META_*). */
+ * quantised history in tokens, the scale/zero format (KIVI_META_*), and
+ * launch options (KIVI_FLAG_*, 0 for none). */
 typedef struct {
   int32_t batch;
   int32_t kv_heads;
@@ -182,42 +204,44 @@ typedef struct {
   int32_t residual;
   int32_t max_tokens;
   int32_t meta_format;
+  int32_t flags;
 } kivi_geom;
 
-/* The cache: eight caller-owned device buffers laid out as described above,
- * plus three host-side counters that the calls below update. */
+/* The cache: three caller-owned device buffers laid out as described above
+ * (the group records and the two residual rings), plus three host-side
+ * counters that the calls below update. */
 typedef struct {
-  uint8_t  *k_codes;    /* the group records                           */
-  void     *k_scale;    /* unused (size 0): may be NULL                    */
-  void     *k_zero;     /* unused                                          */
-  uint8_t  *v_codes;    /* unused                                          */
-  void     *v_scale;    /* unused                                          */
-  void     *v_zero;     /* unused                                          */
-  uint16_t *k_res;
-  uint16_t *v_res;
+  uint8_t  *records;    /* group records [B][H][NG][record bytes]          */
+  uint16_t *k_res;      /* bf16 ring [B][H][R+G][D]                        */
+  uint16_t *v_res;      /* bf16 ring [B][H][R+G][D]                        */
   int32_t   n_q;        /* tokens in the quantised history (multiple of G) */
   int32_t   n_res;      /* tokens in the residual ring                     */
   int32_t   res_start;  /* ring slot of the oldest residual token          */
 } kivi_cache;
 
-/* Order of the eight sizes written by kivi_cache_layout. */
-enum {
-  KIVI_BUF_K_CODES = 0, KIVI_BUF_K_SCALE, KIVI_BUF_K_ZERO,
-  KIVI_BUF_V_CODES, KIVI_BUF_V_SCALE, KIVI_BUF_V_ZERO,
-  KIVI_BUF_K_RES, KIVI_BUF_V_RES, KIVI_NUM_BUFS
-};
+/* Order of the sizes written by kivi_cache_layout and kivi_paged_layout. */
+enum { KIVI_BUF_RECORDS = 0, KIVI_BUF_K_RES, KIVI_BUF_V_RES, KIVI_NUM_BUFS };
 
-/* Byte sizes of the eight cache buffers for `geom`, in the order of the
- * KIVI_BUF_* enum: the group records in K_CODES and 0 for K_SCALE ..
- * V_ZERO, whose pointers the calls ignore and accept NULL.
- * Host-only, touches no device.
+/* Byte sizes of the KIVI_NUM_BUFS cache buffers for `geom`, in the order of
+ * the KIVI_BUF_* enum.  Host-only, touches no device.
  * Errors: KIVI_E_NULL, KIVI_E_GEOMETRY, KIVI_E_UNSUPPORTED. */
-kivi_status kivi_cache_layout(const kivi_geom *geom, size_t bytes_out[8]);
+kivi_status kivi_cache_layout(const kivi_geom *geom, size_t bytes_out[KIVI_NUM_BUFS]);
 
-/* Bytes of decode workspace that kivi_decode_attention needs for `geom`
- * (enough for any cache state of that geometry).  Host-only.
- * Errors: KIVI_E_NULL, KIVI_E_GEOMETRY, KIVI_E_UNSUPPORTED. */
-kivi_status kivi_decode_workspace_size(const kivi_geom *geom, size_t *bytes_out);
+/* Bytes of decode workspace that a decode-attention launch needs for `geom`
+ * over a cache of n_q quantised and n_res residual tokens.  The need grows
+ * with both counts, so a workspace of that size also serves every smaller
+ * state: n_q = max_tokens, n_res = R+G gives one for every state of the
+ * cache (the mixed-length and paged calls need that one; the dense baseline
+ * needs n_q = 0, n_res = seq_len).  Host-only.  The size is
+ *   256 * ceil(4 * B * H / 256) + B * H * QPK * 528 * S,
+ *   S = min(max(floor((n_q / G * c + ceil(n_res / 32) * 16) / (8 * c)), 1), 256),
+ * c = bits + 2 (fp32 scale/zero) or bits + 1 (16-bit): one arrival counter
+ * per (sequence, kv head), then up to S split partials of 132 floats per
+ * query head (S bounds the workgroups a launch gives one (sequence, kv
+ * head)).
+ * Returns 0 when geom is NULL or outside the supported set, or when n_q is
+ * not a multiple of G in [0, max_tokens] or n_res < 0. */
+size_t kivi_decode_workspace_bytes(const kivi_geom *geom, int32_t n_q, int32_t n_res);
 
 /* Prefill: quantise the first n_q tokens of k and v into the grouped
  * history ([card] method: per-channel K, per-token V; [record] Methodology:
@@ -232,7 +256,8 @@ kivi_status kivi_quantize_prefill(const kivi_geom *geom, kivi_cache *cache,
                                   const uint16_t *k, const uint16_t *v,
                                   int32_t seq_len, void *stream);
 
-/* Append one decoded token per sequence and kv head to the residual ring:
+/* Append one decoded token per sequence and kv head to the residual ring
+ * ([record] KV bytes basis: the newest tokens are kept unquantised in bf16):
  * slot (res_start + n_res) mod (R+G); then n_res += 1.
  * k_new, v_new: device bf16 [B][H][D].
  * Errors: KIVI_E_NULL, KIVI_E_GEOMETRY, KIVI_E_UNSUPPORTED,
@@ -242,8 +267,12 @@ kivi_status kivi_append_token(const kivi_geom *geom, kivi_cache *cache,
                               const uint16_t *k_new, const uint16_t *v_new,
                               void *stream);
 
-/* Flush: iff n_res == R+G, quantise the G oldest residual tokens into group
- * n_q/G with the same quantiser as prefill, then n_q += G, n_res -= G,
+/* Flush ([record] KV bytes basis: only the grouped history is quantised, in
+ * groups of G = 32 tokens, while the latest R stay in bf16; READING: a group
+ * leaves the residual as soon as R tokens remain without it): iff
+ * n_res == R+G, quantise the G oldest residual tokens into group n_q/G with
+ * the same quantiser as prefill ([card] method: per-channel K, per-token
+ * V), then n_q += G, n_res -= G,
  * res_start = (res_start + G) mod (R+G), and *flushed = 1; otherwise do
  * nothing and set *flushed = 0.  `flushed` is a host pointer (may be NULL).
  * Errors: KIVI_E_NULL, KIVI_E_GEOMETRY, KIVI_E_UNSUPPORTED,
@@ -258,8 +287,9 @@ kivi_status kivi_flush_residual(const kivi_geom *geom, kivi_cache *cache,
  * tokens (dequantised history and bf16 residual; no mask, no position
  * handling), p = softmax(score), out = sum_t p_t v_t, accumulated in fp32.
  * q:   device bf16 [B][Hq][D];  out: device fp32 [B][Hq][D] (written fully).
- * ws:  device workspace of at least kivi_decode_workspace_size bytes, filled
- *      with zero bytes before its first use.  It holds one arrival counter per
+ * ws:  device workspace of at least kivi_decode_workspace_bytes(geom, n_q,
+ *      n_res) bytes for the cache's counters, filled with zero bytes before
+ *      its first use.  It holds one arrival counter per
  *      (sequence, kv head) and the split-K partials; every call returns the
  *      counters to zero, so a workspace is reusable by later calls ordered on
  *      the same stream.  Calls that overlap in time on one workspace race.
@@ -282,8 +312,11 @@ kivi_status kivi_decode_attention(const kivi_geom *geom, const kivi_cache *cache
  * token from k_new/v_new and stores it into its ring slot itself.  With
  * R == 0 a flush step runs as three launches.
  * k_new, v_new: device bf16 [B][H][D]; q, out, softmax_scale, ws, ws_bytes
- * as for kivi_decode_attention; flushed: host pointer (may be NULL), set to
- * 1 if a group was flushed, else 0.
+ * as for kivi_decode_attention, the workspace sized for the counters after
+ * the step (kivi_decode_workspace_bytes(geom, n_q, n_res + 1) serves every
+ * step, a flush only moving tokens from the residual to the history);
+ * flushed: host pointer (may be NULL), set to 1 if a group was flushed, else
+ * 0.
  * Errors (checked before anything is enqueued): those of the three calls,
  * i.e. KIVI_E_NULL, KIVI_E_GEOMETRY, KIVI_E_UNSUPPORTED, KIVI_E_STATE,
  * KIVI_E_RESIDUAL_FULL (n_res == R+G on entry), KIVI_E_CAPACITY (a flush is
@@ -305,8 +338,8 @@ kivi_status kivi_decode_step(const kivi_geom *geom, kivi_cache *cache,
  *      token capacity T of the dense cache; bits, group and residual must be
  *      a supported combination but do not affect the result.
  * k, v: device bf16 [B][H][T][D], read only.  1 <= seq_len <= T.
- * q, out, softmax_scale, ws, ws_bytes: as for kivi_decode_attention (the
- *      workspace size is kivi_decode_workspace_size of the same geom).
+ * q, out, softmax_scale, ws, ws_bytes: as for kivi_decode_attention, the
+ *      workspace at least kivi_decode_workspace_bytes(geom, 0, seq_len).
  * Errors: KIVI_E_NULL, KIVI_E_GEOMETRY, KIVI_E_UNSUPPORTED, KIVI_E_SEQLEN,
  *         KIVI_E_WORKSPACE, KIVI_E_HIP. */
 kivi_status kivi_dense_decode_attention(const kivi_geom *geom, const uint16_t *k,
@@ -357,7 +390,8 @@ kivi_status kivi_ragged_prefill(const kivi_geom *geom, const kivi_cache *cache,
  * the step written to state_out (distinct device int32 [B][4] buffers; the
  * next step reads state_out).  Requires residual >= group.
  * k_new, v_new: device bf16 [B][H][D]; q, out, softmax_scale, ws, ws_bytes
- * as for kivi_decode_attention (the workspace size of the same geom).
+ * as for kivi_decode_attention, the workspace at least
+ * kivi_decode_workspace_bytes(geom, max_tokens, R+G).
  * Errors: KIVI_E_NULL, KIVI_E_GEOMETRY, KIVI_E_UNSUPPORTED, KIVI_E_STATE
  *         (state_in == state_out), KIVI_E_WORKSPACE, KIVI_E_HIP. */
 kivi_status kivi_ragged_decode_step(const kivi_geom *geom, const kivi_cache *cache,
@@ -374,8 +408,8 @@ kivi_status kivi_ragged_decode_step(const kivi_geom *geom, const kivi_cache *cac
  * of one sequence.  Sequence b's group g lives in page block_table[b][g /
  * page_groups]; inside the pools, (page p, kv head h, group i of the page)
  * is group slot s = (p * H + h) * page_groups + i.  The history is one
- * pool, k_codes [slots][record bytes] of group records (as in kivi_cache);
- * the five other pool pointers are ignored (may be NULL).  The residual rings are not paged:
+ * pool, records [slots][record bytes] of group records (as in kivi_cache).
+ * The residual rings are not paged:
  * k_res, v_res are [B][H][R+G][D] as in kivi_cache.  Lengths are per
  * sequence, in the same device state as the mixed-length calls above.
  *
@@ -391,12 +425,7 @@ kivi_status kivi_ragged_decode_step(const kivi_geom *geom, const kivi_cache *cac
  * one after it was written reads as zeros.
  * ------------------------------------------------------------------------ */
 typedef struct {
-  uint8_t  *k_codes;            /* record pool (kivi_paged_layout size)     */
-  void     *k_scale;            /* unused (size 0): may be NULL             */
-  void     *k_zero;             /* unused                                   */
-  uint8_t  *v_codes;            /* unused                                   */
-  void     *v_scale;            /* unused                                   */
-  void     *v_zero;             /* unused                                   */
+  uint8_t  *records;            /* record pool (kivi_paged_layout size)     */
   uint16_t *k_res;              /* [B][H][R+G][D] rings, as in kivi_cache  */
   uint16_t *v_res;
   const int32_t *block_table;   /* device [B][max_pages]                    */
@@ -404,14 +433,14 @@ typedef struct {
   int32_t   num_pages;          /* pages in each pool                        */
 } kivi_paged_cache;
 
-/* Byte sizes of the buffers of a paged cache (indexed by kivi_buffer: the
- * record pool, five zeros, the two rings) and the block table's row length.
+/* Byte sizes of the buffers of a paged cache (in the order of the KIVI_BUF_*
+ * enum: the record pool, the two rings) and the block table's row length.
  * The record pool must stay below 2 GiB (its offsets are 32-bit).
  * Errors: KIVI_E_NULL (bytes), KIVI_E_GEOMETRY, KIVI_E_UNSUPPORTED (geom
  *         outside the supported set, page_groups not a power of two in
  *         [1, 2^20], num_pages < 1, or a pool of 2 GiB or more). */
 kivi_status kivi_paged_layout(const kivi_geom *geom, int32_t page_groups, int32_t num_pages,
-                              size_t bytes[8], int32_t *max_pages);
+                              size_t bytes[KIVI_NUM_BUFS], int32_t *max_pages);
 
 /* kivi_ragged_prefill into a paged cache: the same split, codes and
  * scale/zero bytes per sequence, stored in the sequence's pages.

@@ -18,6 +18,14 @@ def _declared():
     return sorted(set(re.findall(r"\b(kivi_[a-z_]+)\s*\(", src)))
 
 
+# the boundary planned before any kernel was written: buffer sizes, workspace
+# bytes for a cache state, prefill, append, flush, decode attention, and the
+# two error helpers
+PLANNED = ("kivi_cache_layout", "kivi_decode_workspace_bytes", "kivi_quantize_prefill",
+           "kivi_append_token", "kivi_flush_residual", "kivi_decode_attention",
+           "kivi_status_string", "kivi_last_hip_error")
+
+
 def test_exports_every_declared_function():
     names = _declared()
     assert len(names) == 15
@@ -25,6 +33,7 @@ def test_exports_every_declared_function():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(kivi.EXPORTS)
+    assert set(PLANNED) <= set(names)
 
 
 def _g(**kw):
@@ -34,24 +43,55 @@ def _g(**kw):
     return kivi.Geom(**base)
 
 
+def _ws(U, qpk, n_q, n_res, c):
+    """The workspace size kivi.h documents: counters, then split partials."""
+    s = min(max((n_q // 32 * c + -(-n_res // 32) * 16) // (8 * c), 1), 256)
+    return 256 * -(-4 * U // 256) + U * qpk * 528 * s
+
+
 @pytest.mark.parametrize("bits", [2, 4])
 def test_layout_sizes(bits):
     U, T, D, NG, S = 6, 1024, 128, 32, 160
-    # one record per group in the K_CODES buffer, of the bytes of the
+    # one record per group in the records buffer, of the bytes of the
     # per-array layout (codes, fp32 scale/zero) in 1 KiB planes, for every
     # number of query heads per kv head
     rec = 1024 * (bits + 2)
     assert rec == 32 * D * bits // 8 * 2 + 4 * D * 4
     for qpk in (1, 4):
         g = _g(bits=bits, q_per_kv=qpk)
-        assert kivi.cache_layout(g) == [U * NG * rec, 0, 0, 0, 0, 0, U * S * D * 2, U * S * D * 2]
-        assert kivi.workspace_size(g) == 256 + U * (NG // 4 + 1) * qpk * 132 * 4
+        assert kivi.cache_layout(g) == [U * NG * rec, U * S * D * 2, U * S * D * 2]
+        assert kivi.workspace_bytes(g) == _ws(U, qpk, T, S, bits + 2)
+        assert kivi.workspace_bytes(g, 0, 1) == _ws(U, qpk, 0, 1, bits + 2)
+        assert kivi.workspace_bytes(g, 512, 140) == _ws(U, qpk, 512, 140, bits + 2)
+
+
+def test_workspace_bytes_grows_with_the_state():
+    lib = kivi.raw_library()
+    g = _g(max_tokens=1 << 20)
+    P = ctypes.byref
+    prev = 0
+    for n_q in range(0, 1 << 20, 4096):
+        n = lib.kivi_decode_workspace_bytes(P(g.c()), n_q, 150)
+        assert n >= prev and n >= lib.kivi_decode_workspace_bytes(P(g.c()), n_q, 100)
+        prev = n
+    # capped at 256 partials per (sequence, kv head)
+    assert prev == _ws(6, 4, 1 << 20, 150, 4) == 256 + 6 * 4 * 528 * 256
+    # invalid counts or geometry: 0
+    for n_q, n_res in [(-32, 0), (33, 0), ((1 << 20) + 32, 0), (0, -1)]:
+        assert lib.kivi_decode_workspace_bytes(P(g.c()), n_q, n_res) == 0
+    assert lib.kivi_decode_workspace_bytes(None, 0, 0) == 0
+    assert lib.kivi_decode_workspace_bytes(P(_g(bits=3).c()), 0, 0) == 0
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(batch=0), 2), (dict(kv_heads=-1), 2), (dict(bits=3), 3), (dict(bits=8), 3),
     (dict(head_dim=64), 3), (dict(group=64), 3), (dict(residual=100), 3),
     (dict(q_per_kv=17), 3), (dict(max_tokens=1000), 3), (dict(residual=-32), 2),
+    (dict(flags=2), 3), (dict(flags=-1), 3),
+    # a (sequence, kv head) may hold at most 2^30 bytes of group records
+    (dict(max_tokens=((1 << 18) + 1) * 32), 3),                    # 2-bit, 4 KiB records
+    (dict(bits=4, max_tokens=((1 << 30) // 6144 + 1) * 32), 3),   # 4-bit, 6 KiB records
+    (dict(bits=2, meta_format=1, max_tokens=((1 << 30) // 3072 + 1) * 32), 3),
 ])
 def test_geometry_rejected(kw, status):
     with pytest.raises(kivi.KiviError) as e:
@@ -59,8 +99,16 @@ def test_geometry_rejected(kw, status):
     assert e.value.status == status
 
 
+def test_largest_record_range_accepted():
+    for bits, meta, rec in [(2, 0, 4096), (4, 0, 6144), (2, 1, 3072), (4, 1, 5120)]:
+        ng = (1 << 30) // rec
+        g = _g(bits=bits, meta_format=meta, max_tokens=ng * 32, batch=1, kv_heads=1)
+        assert kivi.cache_layout(g)[0] == ng * rec <= 1 << 30
+    assert kivi.cache_layout(_g(flags=kivi.FLAG_DETERMINISTIC))[0] > 0
+
+
 def _cache_struct(n_q=0, n_res=0, res_start=0, null=None):
-    ptrs = [ctypes.c_void_p(0x1000 * (i + 1)) for i in range(8)]
+    ptrs = [ctypes.c_void_p(0x1000 * (i + 1)) for i in range(3)]
     if null is not None:
         ptrs[null] = ctypes.c_void_p(0)
     return kivi._Cache(*ptrs, n_q, n_res, res_start)
@@ -77,9 +125,9 @@ def test_host_validation_before_any_device_work():
     # NULL geometry / cache / buffers / inputs
     assert _call("kivi_quantize_prefill", None, P(_cache_struct()), fake, fake, 10, None) == 1
     assert _call("kivi_quantize_prefill", P(g), None, fake, fake, 10, None) == 1
-    # a cache needs K_CODES (the records) and the rings
+    # a cache needs the records and the rings
     for geom in (g, _g(q_per_kv=1).c()):
-        for i in (0, 6, 7):
+        for i in (0, 1, 2):
             assert _call("kivi_quantize_prefill", P(geom), P(_cache_struct(null=i)), fake, fake,
                          10, None) == 1
     assert _call("kivi_quantize_prefill", P(g), P(_cache_struct()), None, fake, 10, None) == 1
@@ -104,8 +152,9 @@ def test_host_validation_before_any_device_work():
                 dict(res_start=160), dict(n_q=1056)]:
         c = _cache_struct(**bad)
         assert _call("kivi_append_token", P(g), P(c), fake, fake, None) == 9, bad
-    # decode: empty cache, workspace, scale
-    ws_need = kivi.workspace_size(_g())
+    # decode: empty cache, workspace (sized for the cache's counters), scale
+    ws_need = kivi.workspace_bytes(_g(), 64, 130)
+    assert ws_need < kivi.workspace_bytes(_g())
     args = (fake, fake, ctypes.c_float(0.1))
     assert _call("kivi_decode_attention", P(g), P(_cache_struct()), *args, fake, ws_need,
                  None) == 9
@@ -122,7 +171,8 @@ def test_decode_step_validation_before_any_device_work():
     g = _g().c()
     fake = ctypes.c_void_p(0x2000)
     P = ctypes.byref
-    ws_need = kivi.workspace_size(_g())
+    # the attention of a step runs over the counters after it: 64 + 141
+    ws_need = kivi.workspace_bytes(_g(), 64, 141)
     flushed = ctypes.c_int32(7)
 
     def step(c, k=fake, v=fake, q=fake, out=fake, scale=0.1, ws=fake, nbytes=ws_need, geom=g):
@@ -135,10 +185,10 @@ def test_decode_step_validation_before_any_device_work():
     assert step(c, ws=None) == 7 and step(c, nbytes=ws_need - 1) == 7
     assert step(c, scale=float("inf")) == 2
     g1 = _g(q_per_kv=1)
-    for i in (0, 6, 7):   # records and rings
+    for i in (0, 1, 2):   # records and rings
         assert step(_cache_struct(n_q=64, n_res=140, null=i)) == 1
         assert step(_cache_struct(n_q=64, n_res=140, null=i), geom=g1.c(),
-                    nbytes=kivi.workspace_size(g1)) == 1
+                    nbytes=kivi.workspace_bytes(g1)) == 1
     # a full ring on entry, as for kivi_append_token
     c = _cache_struct(n_q=64, n_res=160, res_start=32)
     assert step(c) == 6
@@ -156,7 +206,7 @@ def test_decode_step_validation_before_any_device_work():
 def test_dense_attention_validation_before_any_device_work():
     g = _g().c()
     fake = ctypes.c_void_p(0x2000)
-    ws_need = kivi.workspace_size(_g())
+    ws_need = kivi.workspace_bytes(_g(), 0, 100)
 
     def dense(k=fake, v=fake, n=100, q=fake, out=fake, scale=0.1, ws=fake, nbytes=ws_need):
         return _call("kivi_dense_decode_attention", ctypes.byref(g), k, v, n, q, out,
@@ -180,8 +230,8 @@ def test_16bit_meta_layout_and_rejected_formats():
     assert 3072 == 32 * D * 2 // 8 * 2 + 4 * D * 2
     for qpk in (1, 4):
         g = _g(meta_format=kivi.META_FP16_BF16, q_per_kv=qpk)
-        assert kivi.cache_layout(g) == [U * NG * 3072, 0, 0, 0, 0, 0, U * S * D * 2,
-                                        U * S * D * 2]
+        assert kivi.cache_layout(g) == [U * NG * 3072, U * S * D * 2, U * S * D * 2]
+        assert kivi.workspace_bytes(g) == _ws(U, qpk, T, S, 3)
     for bad in (2, -1):
         with pytest.raises(kivi.KiviError) as e:
             kivi.cache_layout(_g(meta_format=bad))
@@ -193,7 +243,7 @@ def test_ragged_calls_validation_before_any_device_work():
     fake = ctypes.c_void_p(0x2000)
     fake2 = ctypes.c_void_p(0x3000)
     P = ctypes.byref
-    ws_need = kivi.workspace_size(_g())
+    ws_need = kivi.workspace_bytes(_g())   # the fullest state: lengths live on the device
     c = _cache_struct()
     assert _call("kivi_ragged_prefill", P(g), P(c), None, fake, 100, fake, fake, None) == 1
     assert _call("kivi_ragged_prefill", P(g), P(c), fake, fake, 100, None, fake, None) == 1
@@ -201,7 +251,7 @@ def test_ragged_calls_validation_before_any_device_work():
     assert _call("kivi_ragged_prefill", P(g), P(c), fake, fake, 0, fake, fake, None) == 4
     assert _call("kivi_ragged_prefill", P(g), P(_cache_struct(null=0)), fake, fake, 100, fake,
                  fake, None) == 1
-    assert _call("kivi_ragged_prefill", P(_g(q_per_kv=1).c()), P(_cache_struct(null=7)), fake,
+    assert _call("kivi_ragged_prefill", P(_g(q_per_kv=1).c()), P(_cache_struct(null=2)), fake,
                  fake, 100, fake, fake, None) == 1
 
     def step(geom=g, si=fake, so=fake2, nbytes=ws_need):
@@ -215,7 +265,7 @@ def test_ragged_calls_validation_before_any_device_work():
 
 
 def _paged_struct(P=4, pages=20, null=None):
-    ptrs = [ctypes.c_void_p(0x1000 * (i + 1)) for i in range(9)]
+    ptrs = [ctypes.c_void_p(0x1000 * (i + 1)) for i in range(4)]
     if null is not None:
         ptrs[null] = ctypes.c_void_p(0)
     return kivi._PagedCache(*ptrs, P, pages)
@@ -228,8 +278,8 @@ def test_paged_layout_sizes(bits, meta):
         g = _g(bits=bits, meta_format=meta, q_per_kv=qpk)
         sizes, max_pages = kivi.paged_layout(g, 4, 10)
         assert max_pages == 8              # 32 groups of capacity / 4
-        assert sizes == [n * 1024 * (bits + (1 if meta else 2)), 0, 0, 0, 0, 0,
-                         6 * 160 * 128 * 2, 6 * 160 * 128 * 2]
+        assert sizes == [n * 1024 * (bits + (1 if meta else 2)), 6 * 160 * 128 * 2,
+                         6 * 160 * 128 * 2]
     assert kivi.paged_layout(g, 16, 1)[1] == 2
     assert kivi.paged_layout(g, 64, 1)[1] == 1
 
@@ -239,16 +289,16 @@ def test_paged_calls_validation_before_any_device_work():
     fake = ctypes.c_void_p(0x2000)
     fake2 = ctypes.c_void_p(0x3000)
     P = ctypes.byref
-    out = (ctypes.c_size_t * 8)()
+    out = (ctypes.c_size_t * 3)()
     mp = ctypes.c_int32(0)
     for pg, pages, status in [(3, 10, 3), (0, 10, 3), (1 << 21, 1, 3), (4, 0, 3), (4, 1, 0),
                               (1 << 20, 1, 3)]:   # the last: pools of 2 GiB and more
         assert _call("kivi_paged_layout", P(g), pg, pages, out, P(mp)) == status, (pg, pages)
     assert _call("kivi_paged_layout", P(g), 4, 10, None, P(mp)) == 1
     assert _call("kivi_paged_layout", P(g), 4, 10, out, None) == 0
-    ws_need = kivi.workspace_size(_g())
+    ws_need = kivi.workspace_bytes(_g())
     for geom in (g, _g(q_per_kv=1).c()):
-        for null in (0, 6, 7, 8):   # record pool, rings, block table
+        for null in (0, 1, 2, 3):   # record pool, rings, block table
             assert _call("kivi_paged_prefill", P(geom), P(_paged_struct(null=null)), fake, fake,
                          100, fake, fake, None) == 1, null
     assert _call("kivi_paged_prefill", P(g), P(_paged_struct(P=6)), fake, fake, 100, fake, fake,
@@ -265,7 +315,7 @@ def test_paged_calls_validation_before_any_device_work():
     assert step(so=fake) == 9
     assert step(nbytes=ws_need - 1) == 7
     assert step(pc=_paged_struct(pages=0)) == 3
-    assert step(pc=_paged_struct(null=8)) == 1   # block table
+    assert step(pc=_paged_struct(null=3)) == 1   # block table
     assert step(geom=_g(residual=0).c()) == 3
 
 
