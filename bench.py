@@ -25,8 +25,15 @@ Workload (Llama-3-8B GQA geometry of the catalog record kivi-2bit-llama3-8b-gqa-
   the caches themselves through kivi_ragged_decode_step at the lockstep
   length and with lengths drawn uniformly from [S/2, S]; eager launches and
   HIP graph replays of all layers (two launches per layer) are timed;
+* flush-amortised rate: a further window of 32 fused steps, in which every
+  layer flushes exactly once (value's window of `steps` steps holds
+  floor or ceil of steps/32 flushes);
+* copy bandwidth: a plain 1 GiB device-to-device copy (torch copy_), timed
+  with HIP events; the decode kernel's rate is also reported as a fraction of
+  it;
 * cpu_baseline: the CPU oracle (plain C) on a bounded sample of the same
-  workload (two layers' worth of (sequence, kv head) units), threads over units.
+  workload (eight layers' worth of (sequence, kv head) units), threads over
+  units, plus a single-thread rate on a smaller sample.
 
 Prints one JSON line.
 """
@@ -87,11 +94,42 @@ def read_traffic(kernel_tag: str):
         return None
 
 
-def cpu_baseline(w, seed, units_wanted=1024, meta=0):
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def copy_bandwidth(nbytes=1 << 30, reps=10):
+    """GB/s of a plain device-to-device copy (bytes read + bytes written per
+    second), HIP events around `reps` back-to-back copies."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / 1e3 / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * nbytes / t / 1e9
+
+
+def cpu_baseline(w, seed, units_wanted=1024, meta=0, units_1thread=64):
     import numpy as np
 
     import oracle
     import synth
+    # the box's CPU share for one GPU is 16 threads, whatever the host has
     threads = max(1, min(16, len(os.sched_getaffinity(0))))
     og = oracle.Geom(1, 1, w.q_per_kv, bits=w.bits, max_tokens=w.seq_len, meta=meta)
     per_layer = w.batch * w.kv_heads
@@ -128,18 +166,29 @@ def cpu_baseline(w, seed, units_wanted=1024, meta=0):
         t0 = time.perf_counter()
         outs = list(ex.map(attend_one, range(len(units))))
         t_attn = time.perf_counter() - t0
+    # one thread, on the first units_1thread units
+    n1 = min(units_1thread, len(units))
+    t0 = time.perf_counter()
+    for i in range(n1):
+        attend_one(i)
+    t_attn1 = time.perf_counter() - t0
     assert all(np.isfinite(o).all() for o in outs)
     n = len(units)
     n_q = caches[0].n_q
     units_per_step = w.layers * w.batch * w.kv_heads
     step_s = t_attn / n * units_per_step
+    step_s1 = t_attn1 / n1 * units_per_step
     return {
         "value": w.batch / step_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
         "sample": (f"{n} (sequence, kv head) units at {w.seq_len} tokens ({n / per_layer:.0f} "
                    f"layers' worth): oracle prefill + one decode-attention step per unit; "
                    f"decode time scaled to {units_per_step} units per 32-layer step"),
+        "value_1thread": w.batch / step_s1,
+        "sample_1thread": f"decode attention of {n1} of those units on one thread",
+        "nproc": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)),
+        "cpu_model": _cpu_model(),
         "quantize_gelem_s": 2 * n * n_q * w.head_dim / t_prefill / 1e9,
-        "attn_wall_s": t_attn, "prefill_wall_s": t_prefill,
+        "attn_wall_s": t_attn, "prefill_wall_s": t_prefill, "attn_wall_s_1thread": t_attn1,
     }
 
 
@@ -260,7 +309,7 @@ def batch_sweep(args):
             k.normal_(generator=gen)
             v.normal_(generator=gen)
             kv.append((k, v))
-        ws = kivi.Workspace(g, dev)
+        ws = kivi.Workspace(g, dev, n_q=0, n_res=S)
         q = torch.randn(B, w.q_heads, D, device=dev, generator=gen).to(torch.bfloat16)
         out = torch.empty(B, w.q_heads, D, device=dev)
         fns = [lambda k=k, v=v: kivi.dense_decode_attention(g, k, v, S, q, out=out, ws=ws)
@@ -495,9 +544,12 @@ def main():
     dev = torch.device("cuda", 0)
     D, G, R = w.head_dim, w.group, w.residual
     kernel_steps = 10   # flush-free fused steps timed as one block
+    amort_steps = G     # a window in which every layer flushes exactly once
     ragged_steps = args.steps + (args.steps & 1)
-    # timed steps, then up to R+G steps to a flush-free block, a lead-in and the block
-    total_steps = args.warmup + (args.profile_steps or 2 * args.steps + R + G + kernel_steps + 1)
+    # timed steps (fused, then separate calls), the flush-amortised window, then
+    # up to R+G steps to a flush-free block, a lead-in and the block
+    total_steps = args.warmup + (args.profile_steps or
+                                 2 * args.steps + amort_steps + R + G + kernel_steps + 1)
     # the mixed-length leg continues the caches for 2 * (2 * steps + 4) more tokens
     cap_steps = total_steps + 2 * (2 * ragged_steps + RAGGED_EXTRA_STEPS)
     max_tokens = G * math.ceil((w.seq_len - R + cap_steps + G) / G)
@@ -579,6 +631,17 @@ def main():
         step_separate(i)
     torch.cuda.synchronize()
     t_steps_sep = time.perf_counter() - t0
+    # flush-amortised: G consecutive fused steps hold exactly one flush per layer
+    i0 = args.warmup + 2 * n_timed
+    nq_before = caches[0].n_q
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(i0, i0 + amort_steps):
+        step(i)
+    torch.cuda.synchronize()
+    t_amort = time.perf_counter() - t0
+    if caches[0].n_q != nq_before + G:
+        raise RuntimeError("the flush-amortised window does not hold one flush per layer")
 
     # kernel timing: a block of further fused steps in which no layer flushes
     # (all layers flush on the same steps: their counters move in lockstep),
@@ -589,7 +652,7 @@ def main():
     # would fall inside it.
     slots = R + G
     c0 = caches[0]
-    i = args.warmup + 2 * n_timed
+    i = args.warmup + 2 * n_timed + amort_steps
     while c0.n_res + kernel_steps + 1 >= slots:
         step(i)
         i += 1
@@ -611,6 +674,8 @@ def main():
     avg_bytes = sum(kern_bytes) / len(kern_bytes)
     achieved = avg_bytes / avg_kern_s / 1e9
 
+    copy_gbps = copy_bandwidth()
+
     ragged = None
     if not args.no_ragged:
         tok = new_tok[0]
@@ -630,6 +695,10 @@ def main():
                    "step": "per layer: kivi_decode_step (append + flush-if-full + decode "
                            "attention; one launch, two on flush steps)"},
         "ms_per_step_separate_calls": t_steps_sep / n_timed * 1e3,
+        "tokens_s_flush_amortised": w.batch * amort_steps / t_amort,
+        "ms_per_step_flush_amortised": t_amort / amort_steps * 1e3,
+        "copy_gbps": copy_gbps,
+        "attn_frac_of_copy": achieved / copy_gbps,
         "attn_hbm_gbps": achieved,
         "attn_bytes_per_launch": avg_bytes,
         "attn_kernel_us": avg_kern_s * 1e6,

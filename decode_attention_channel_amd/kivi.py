@@ -433,13 +433,14 @@ def dense_decode_attention(g: Geom, k: torch.Tensor, v: torch.Tensor, seq_len: i
                            ) -> torch.Tensor:
     """Baseline attention over an uncompressed cache: k, v bf16
     [B][H][g.max_tokens][D], first seq_len tokens; q bf16 [B][H*QPK][D] ->
-    fp32 [B][H*QPK][D]."""
+    fp32 [B][H*QPK][D].  A workspace passed in must hold
+    workspace_bytes(g, 0, seq_len)."""
     shape = (g.batch, g.q_heads, g.head_dim)
     kv_shape = (g.batch, g.kv_heads, g.max_tokens, g.head_dim)
     if out is None:
         out = torch.empty(shape, dtype=torch.float32, device=q.device)
     if ws is None:
-        ws = Workspace(g, q.device)
+        ws = Workspace(g, q.device, n_q=0, n_res=int(seq_len))
     scale = 1.0 / math.sqrt(g.head_dim) if softmax_scale is None else float(softmax_scale)
     _check(_lib.kivi_dense_decode_attention(ctypes.byref(g.c()),
                                             _ptr(k, torch.bfloat16, kv_shape, "k"),

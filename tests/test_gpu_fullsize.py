@@ -11,7 +11,11 @@ oracle recomputes one by one:
   then 1024 streamed tokens with a flush every 32, attention checked along
   the way;
 * Llama-2-13B-shaped MHA, 40 heads, 4096 tokens, at batch 8 (the memory-wall
-  sweep of that workload is a benchmark, not a test).
+  sweep of that workload is a benchmark, not a test);
+* the timed call itself, kivi_decode_step, at the 8K GQA and 32K 4-bit
+  sizes across flushes, against the oracle and against separate calls;
+* one workspace reused by back-to-back launches (every unit checked);
+* bitwise repeatability of the deterministic launch at the 8K GQA size.
 """
 import math
 
@@ -135,3 +139,138 @@ def test_streaming_decode_full_size(name, steps, check_every):
     torch.cuda.synchronize()
     for (b, h), oc1 in ocs.items():
         _check_unit_cache(gc, oc1, b, h)
+
+
+@pytest.mark.parametrize("name,steps", [("llama3-8b-gqa-8k", 40), ("llama3-8b-gqa-32k-4bit", 64)])
+def test_fused_decode_step_full_size(name, steps):
+    """The timed call (kivi_decode_step through LayerStepper.step: append fused
+    into the attention launch, flush launched first when the ring fills) at
+    the full workload size, across flushes: sampled units against the
+    oracle at every flush step and at the end (cache bytes exact, attention
+    within the bound), and every output against the same steps made of the
+    three separate calls on a second cache, both sharing one workspace."""
+    w = synth.WORKLOADS[name]
+    print(f"fused step {name} steps {steps}", flush=True)
+    k, v = synth.prefill_kv(w, 31)
+    T = 32 * math.ceil((w.seq_len - 128 + steps + 32) / 32)
+    g = kivi.Geom(w.batch, w.kv_heads, w.q_per_kv, bits=w.bits, max_tokens=T)
+    fused, sep = kivi.Cache(g), kivi.Cache(g)
+    kd, vd = k.cuda(), v.cuda()
+    kivi.quantize_prefill(g, fused, kd, vd)
+    kivi.quantize_prefill(g, sep, kd, vd)
+    del kd, vd
+    units = _sample_units(w, 4, 3)
+    og = _unit_geoms(w, T)
+    kb, vb = synth.bits_u16(k), synth.bits_u16(v)
+    ocs = {(b, h): oracle.prefill(og, kb[b:b + 1, h:h + 1].copy(), vb[b:b + 1, h:h + 1].copy())
+           for b, h in units}
+    del k, v, kb, vb
+    ws = kivi.Workspace(g)
+    q_dev = torch.empty(w.batch, w.q_heads, 128, dtype=torch.bfloat16, device="cuda")
+    out_f = torch.empty(w.batch, w.q_heads, 128, device="cuda")
+    out_s = torch.empty_like(out_f)
+    stepper = kivi.LayerStepper(g, fused, ws, q_dev, out_f)
+    separate = kivi.LayerStepper(g, sep, ws, q_dev, out_s)
+    scale = 1.0 / math.sqrt(128)
+    flush_steps = []
+    for step in range(steps):
+        kn, vn = synth.new_token(w, 31, 0, step)
+        q = synth.query(w, 31, 0, step)
+        q_dev.copy_(q)
+        kn_d, vn_d = kn.cuda(), vn.cuda()
+        out_f.fill_(float("nan"))
+        out_s.fill_(float("nan"))
+        f = stepper.step(kn_d, vn_d)
+        separate.append(kn_d, vn_d)
+        assert separate.flush() == f
+        separate.attend()
+        knb, vnb = synth.bits_u16(kn), synth.bits_u16(vn)
+        for (b, h), oc1 in ocs.items():
+            oracle.append(oc1, knb[b:b + 1, h:h + 1].copy(), vnb[b:b + 1, h:h + 1].copy())
+            assert oracle.flush(oc1) == f
+        torch.cuda.synchronize()
+        of, os_ = to_np(out_f), to_np(out_s)
+        assert np.isfinite(of).all() and np.isfinite(os_).all()
+        assert row_rel_err(of, os_) <= 1e-4, f"step {step}: fused vs separate calls"
+        assert (fused.n_q, fused.n_res, fused.res_start) == (sep.n_q, sep.n_res, sep.res_start)
+        if f or step == steps - 1:
+            flush_steps += [step] if f else []
+            qb = synth.bits_u16(q)
+            errs = [_check_unit_attention(of, oc1, qb, b, h, w.q_per_kv, scale)
+                    for (b, h), oc1 in ocs.items()]
+            for (b, h), oc1 in ocs.items():
+                _check_unit_cache(fused, oc1, b, h)
+                _check_unit_cache(sep, oc1, b, h)
+            print(f"step {step}: flushed {f} n_q {fused.n_q} n_res {fused.n_res} "
+                  f"max err {max(errs):.2e}", flush=True)
+    assert len(flush_steps) == steps // 32
+    # the two caches hold the same bytes everywhere the cache is in use
+    torch.cuda.synchronize()
+    ng = fused.n_q // 32
+    assert torch.equal(fused.records[:, :, :ng], sep.records[:, :, :ng])
+
+
+def test_workspace_reuse_back_to_back():
+    """One workspace, many back-to-back decode launches over different caches
+    and queries with no synchronisation in between: every unit of every
+    launch against the oracle.  A launch whose combine read a partial still
+    in flight, or left by the previous launch, would fail here."""
+    B, H, QPK, S, layers = 4, 8, 4, 4096, 6
+    w = synth.Workload("reuse", B, H, QPK, S, 2, layers, 3, 8.0)
+    T = 32 * ((S - 128) // 32)
+    g = kivi.Geom(B, H, QPK, max_tokens=T)
+    ws = kivi.Workspace(g)
+    caches, qs, refs = [], [], []
+    for layer in range(layers):
+        k, v = synth.prefill_kv(w, 41, layer)
+        c = kivi.Cache(g)
+        kivi.quantize_prefill(g, c, k.cuda(), v.cuda())
+        q = synth.query(w, 41, layer)
+        oc = oracle.prefill(oracle.Geom(B, H, QPK, max_tokens=T), synth.bits_u16(k),
+                            synth.bits_u16(v))
+        refs.append(oracle.attention(oc, synth.bits_u16(q), 1 / math.sqrt(128)))
+        caches.append(c)
+        qs.append(q.cuda())
+    outs = [torch.full((B, H * QPK, 128), float("nan"), device="cuda") for _ in range(layers)]
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for layer in range(layers):
+            kivi.decode_attention(g, caches[layer], qs[layer], out=outs[layer], ws=ws)
+        torch.cuda.synchronize()
+        for layer in range(layers):
+            o = to_np(outs[layer])
+            assert np.isfinite(o).all()
+            err = row_rel_err(o, refs[layer])
+            assert err <= ATTN_TOL, f"rep {rep} layer {layer}: {err:.3e}"
+            outs[layer].fill_(float("nan"))
+
+
+def test_deterministic_launch_repeats_bitwise_full_size():
+    """With KIVI_FLAG_DETERMINISTIC the 8K GQA launch is bitwise repeatable;
+    the default launch (dynamic claims) stays within 1e-4 of it."""
+    w = synth.WORKLOADS["llama3-8b-gqa-8k"]
+    k, v = synth.prefill_kv(w, 51)
+    q = synth.query(w, 51).cuda()
+    T = 32 * ((w.seq_len - 128) // 32)
+    outs = {}
+    for flags in (kivi.FLAG_DETERMINISTIC, 0):
+        g = kivi.Geom(w.batch, w.kv_heads, w.q_per_kv, bits=w.bits, max_tokens=T, flags=flags)
+        c = kivi.Cache(g)
+        kivi.quantize_prefill(g, c, k.cuda(), v.cuda())
+        ws = kivi.Workspace(g)
+        runs = []
+        for _ in range(4):
+            out = torch.full((w.batch, w.q_heads, 128), float("nan"), device="cuda")
+            kivi.decode_attention(g, c, q, out=out, ws=ws)
+            runs.append(out)
+        torch.cuda.synchronize()
+        runs = [to_np(o) for o in runs]
+        if flags:
+            for o in runs[1:]:
+                np.testing.assert_array_equal(o, runs[0])
+        else:
+            for o in runs[1:]:
+                assert row_rel_err(o, runs[0]) <= 1e-4
+        outs[flags] = runs[0]
+        del c, ws
+    assert row_rel_err(outs[0], outs[kivi.FLAG_DETERMINISTIC]) <= 1e-4
