@@ -10,6 +10,8 @@
 #include <math.h>
 #include <stdlib.h>
 
+#include <mutex>
+
 #include "kivi_internal.h"
 
 namespace {
@@ -174,6 +176,107 @@ kivi_status enqueue_attend(const kivi_geom *g, const kivi_cache *c, const uint16
                                         (g->flags & KIVI_FLAG_DETERMINISTIC) != 0, s));
 }
 
+// Arrival counters and split partials of kivi_decode_step_noalloc, for
+// callers that cannot allocate (graph capture, tight serving loops,
+// harnesses that forbid allocation).  Each device that runs the call holds
+// its own copy of this array until the process ends.  In host code the
+// array's name is only a host-side handle: its device address comes from
+// hipGetSymbolAddress (static_scratch), per device.
+constexpr size_t kScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+// the arrival counters that must start at zero: one per (sequence, kv head),
+// at most 65535 of them
+constexpr int kScratchCounterWords = 65536;
+static_assert(kScratchCounterWords * 4 <= (int)kScratchBytes, "scratch too small");
+
+__global__ void zero_words_kernel(uint32_t *p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch[kMaxDevices];   // device address of `scratch` per device, once known
+
+// Device address of `scratch` on the current device.  The first call on a
+// device takes the address (hipGetSymbolAddress, with that device current)
+// and zeroes the arrival counters with a small kernel on stream s (a kernel
+// rather than a memset, so that a captured call records a kernel node); the
+// decode launches return the counters to zero, so later calls reuse them.
+kivi_status static_scratch(hipStream_t s, void **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return KIVI_E_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e);
+    hipLaunchKernelGGL(zero_words_kernel, dim3(kScratchCounterWords / 256), dim3(256), 0, s,
+                       static_cast<uint32_t *>(p), kScratchCounterWords);
+    if ((e = hipGetLastError()) != hipSuccess) return hip_status(e);
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return KIVI_OK;
+}
+
+// kivi_decode_step; with static_ws the workspace is the `scratch` array of
+// the current device instead of (ws, ws_bytes).
+kivi_status decode_step_impl(const kivi_geom *g, kivi_cache *c, const uint16_t *k_new,
+                             const uint16_t *v_new, const uint16_t *q, float *out,
+                             float softmax_scale, void *ws, size_t ws_bytes, int32_t *flushed,
+                             hipStream_t s, bool static_ws) {
+  kivi_status st = check_geom(g);
+  if (st != KIVI_OK) return st;
+  if ((st = check_cache(g, c)) != KIVI_OK) return st;
+  if (!k_new || !v_new) return KIVI_E_NULL;
+  if ((st = check_state(g, c)) != KIVI_OK) return st;
+  const int G = g->group, slots = g->residual + G;
+  if (c->n_res == slots) return KIVI_E_RESIDUAL_FULL;
+  const bool flush = c->n_res + 1 == slots;
+  if (flush && c->n_q + G > g->max_tokens) return KIVI_E_CAPACITY;
+  // the attention runs over the counters after the step
+  const long long nq_after = c->n_q + (flush ? G : 0), nres_after = c->n_res + 1 - (flush ? G : 0);
+  if (static_ws) {
+    if (!q || !out) return KIVI_E_NULL;
+    if (!isfinite(softmax_scale)) return KIVI_E_GEOMETRY;
+    if (workspace_need(g, nq_after, nres_after) > kScratchBytes) return KIVI_E_WORKSPACE;
+    if ((st = static_scratch(s, &ws)) != KIVI_OK) return st;
+    ws_bytes = kScratchBytes;
+  }
+  if ((st = check_attend_args(g, nq_after, nres_after, q, out, softmax_scale, ws, ws_bytes)) !=
+      KIVI_OK)
+    return st;
+  if (flushed) *flushed = 0;
+
+  if (flush && g->residual == 0) {
+    // the ring holds exactly one group, which includes the new token: the
+    // three steps run as separate launches
+    if ((st = enqueue_append(g, c, k_new, v_new, s)) != KIVI_OK) return st;
+    if ((st = enqueue_flush(g, c, s)) != KIVI_OK) return st;
+    if (flushed) *flushed = 1;
+    return enqueue_attend(g, c, nullptr, nullptr, q, out, softmax_scale, ws, ws_bytes, s);
+  }
+  if (flush) {
+    // With R >= G the G oldest tokens of the full ring exclude the new one
+    // (the newest of R+G), so quantising them before the append leaves the
+    // same state as append-then-flush, and the append can fuse into the
+    // attention launch.
+    if ((st = enqueue_flush(g, c, s)) != KIVI_OK) return st;
+    if (flushed) *flushed = 1;
+  }
+  // attention with the append fused: the new token is logical index n_res
+  kivi_cache next = *c;
+  next.n_res += 1;
+  if ((st = enqueue_attend(g, &next, k_new, v_new, q, out, softmax_scale, ws, ws_bytes, s)) !=
+      KIVI_OK)
+    return st;
+  c->n_res = next.n_res;
+  return KIVI_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -298,46 +401,15 @@ kivi_status kivi_decode_step(const kivi_geom *g, kivi_cache *c, const uint16_t *
                              const uint16_t *v_new, const uint16_t *q, float *out,
                              float softmax_scale, void *ws, size_t ws_bytes, int32_t *flushed,
                              void *stream) {
-  kivi_status st = check_geom(g);
-  if (st != KIVI_OK) return st;
-  if ((st = check_cache(g, c)) != KIVI_OK) return st;
-  if (!k_new || !v_new) return KIVI_E_NULL;
-  if ((st = check_state(g, c)) != KIVI_OK) return st;
-  const int G = g->group, slots = g->residual + G;
-  if (c->n_res == slots) return KIVI_E_RESIDUAL_FULL;
-  const bool flush = c->n_res + 1 == slots;
-  if (flush && c->n_q + G > g->max_tokens) return KIVI_E_CAPACITY;
-  // the attention runs over the counters after the step
-  const long long nq_after = c->n_q + (flush ? G : 0), nres_after = c->n_res + 1 - (flush ? G : 0);
-  if ((st = check_attend_args(g, nq_after, nres_after, q, out, softmax_scale, ws, ws_bytes)) !=
-      KIVI_OK)
-    return st;
-  if (flushed) *flushed = 0;
-  hipStream_t s = (hipStream_t)stream;
-  if (flush && g->residual == 0) {
-    // the ring holds exactly one group, which includes the new token: the
-    // three steps run as separate launches
-    if ((st = enqueue_append(g, c, k_new, v_new, s)) != KIVI_OK) return st;
-    if ((st = enqueue_flush(g, c, s)) != KIVI_OK) return st;
-    if (flushed) *flushed = 1;
-    return enqueue_attend(g, c, nullptr, nullptr, q, out, softmax_scale, ws, ws_bytes, s);
-  }
-  if (flush) {
-    // With R >= G the G oldest tokens of the full ring exclude the new one
-    // (the newest of R+G), so quantising them before the append leaves the
-    // same state as append-then-flush, and the append can fuse into the
-    // attention launch.
-    if ((st = enqueue_flush(g, c, s)) != KIVI_OK) return st;
-    if (flushed) *flushed = 1;
-  }
-  // attention with the append fused: the new token is logical index n_res
-  kivi_cache next = *c;
-  next.n_res += 1;
-  if ((st = enqueue_attend(g, &next, k_new, v_new, q, out, softmax_scale, ws, ws_bytes, s)) !=
-      KIVI_OK)
-    return st;
-  c->n_res = next.n_res;
-  return KIVI_OK;
+  return decode_step_impl(g, c, k_new, v_new, q, out, softmax_scale, ws, ws_bytes, flushed,
+                          (hipStream_t)stream, false);
+}
+
+kivi_status kivi_decode_step_noalloc(const kivi_geom *g, kivi_cache *c, const uint16_t *k_new,
+                                     const uint16_t *v_new, const uint16_t *q, float *out,
+                                     float softmax_scale, int32_t *flushed, void *stream) {
+  return decode_step_impl(g, c, k_new, v_new, q, out, softmax_scale, nullptr, 0, flushed,
+                          (hipStream_t)stream, true);
 }
 
 kivi_status kivi_dense_decode_attention(const kivi_geom *g, const uint16_t *k, const uint16_t *v,

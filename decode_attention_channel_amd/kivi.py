@@ -27,7 +27,8 @@ EXPORTS = (
     "kivi_append_token", "kivi_flush_residual", "kivi_decode_attention",
     "kivi_decode_step", "kivi_dense_decode_attention", "kivi_ragged_prefill",
     "kivi_ragged_decode_step", "kivi_paged_layout", "kivi_paged_prefill",
-    "kivi_paged_decode_step", "kivi_status_string", "kivi_last_hip_error",
+    "kivi_paged_decode_step", "kivi_decode_step_noalloc", "kivi_status_string",
+    "kivi_last_hip_error",
 )
 BUFFERS = ("records", "k_res", "v_res")   # order of the KIVI_BUF_* sizes
 META_FP32, META_FP16_BF16 = 0, 1   # scale/zero formats (kivi_geom.meta_format)
@@ -77,6 +78,8 @@ def _load():
     lib.kivi_decode_attention.argtypes = [G, C, P, P, ctypes.c_float, P, ctypes.c_size_t, P]
     lib.kivi_decode_step.argtypes = [G, C, P, P, P, P, ctypes.c_float, P, ctypes.c_size_t,
                                      ctypes.POINTER(ctypes.c_int32), P]
+    lib.kivi_decode_step_noalloc.argtypes = [G, C, P, P, P, P, ctypes.c_float,
+                                             ctypes.POINTER(ctypes.c_int32), P]
     lib.kivi_dense_decode_attention.argtypes = [G, P, P, ctypes.c_int32, P, P, ctypes.c_float, P,
                                                 ctypes.c_size_t, P]
     lib.kivi_ragged_prefill.argtypes = [G, C, P, P, ctypes.c_int32, P, P, P]
@@ -425,6 +428,26 @@ def decode_step(g: Geom, c: Cache, k_new: torch.Tensor, v_new: torch.Tensor, q: 
                                  ctypes.byref(flushed), _stream()),
            "kivi_decode_step")
     return out, flushed.value
+
+
+def decode_step_noalloc(g: Geom, c: Cache, k_new: torch.Tensor, v_new: torch.Tensor,
+                        q: torch.Tensor, out: torch.Tensor, softmax_scale: float | None = None
+                        ) -> int:
+    """kivi_decode_step_noalloc: decode_step with the library's static device
+    workspace (no workspace argument; `out` must be given, so that nothing is
+    allocated).  Returns 1 if a group was flushed, else 0."""
+    shape = (g.batch, g.q_heads, g.head_dim)
+    tok = (g.batch, g.kv_heads, g.head_dim)
+    scale = 1.0 / math.sqrt(g.head_dim) if softmax_scale is None else float(softmax_scale)
+    flushed = ctypes.c_int32(0)
+    _check(_lib.kivi_decode_step_noalloc(ctypes.byref(g.c()), ctypes.byref(c._c),
+                                         _ptr(k_new, torch.bfloat16, tok, "k_new"),
+                                         _ptr(v_new, torch.bfloat16, tok, "v_new"),
+                                         _ptr(q, torch.bfloat16, shape, "q"),
+                                         _ptr(out, torch.float32, shape, "out"), scale,
+                                         ctypes.byref(flushed), _stream()),
+           "kivi_decode_step_noalloc")
+    return flushed.value
 
 
 def dense_decode_attention(g: Geom, k: torch.Tensor, v: torch.Tensor, seq_len: int,

@@ -328,6 +328,27 @@ kivi_status kivi_decode_step(const kivi_geom *geom, kivi_cache *cache,
                              void *ws, size_t ws_bytes, int32_t *flushed,
                              void *stream);
 
+/* kivi_decode_step for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The same launches, cache bytes, counters and output as
+ * kivi_decode_step, with the decode workspace taken from a static device
+ * array of the library (16 MiB per device that runs the call, held until
+ * the process ends) instead of (ws, ws_bytes); the call allocates nothing.
+ * The first call on a device takes the array's address and zeroes its
+ * arrival counters with a kernel on `stream`; every call leaves them at zero.
+ * All calls on one device share the array, so calls that overlap in time on
+ * one device (other streams, other threads) race; order them on one stream.
+ * Errors: those of kivi_decode_step, and KIVI_E_WORKSPACE when the step
+ * needs more than the array holds, i.e. kivi_decode_workspace_bytes(geom,
+ * n_q, n_res + 1) > 16 MiB (at 4 query heads per kv head and 8K tokens:
+ * about 72 KB per (sequence, kv head), so at most 233 of them; the
+ * Llama-3-8B-shaped batch of 16 x 8 kv heads needs 9.2 MB);
+ * KIVI_E_UNSUPPORTED for a device index of 64 or more. */
+kivi_status kivi_decode_step_noalloc(const kivi_geom *geom, kivi_cache *cache,
+                                     const uint16_t *k_new, const uint16_t *v_new,
+                                     const uint16_t *q, float *out, float softmax_scale,
+                                     int32_t *flushed, void *stream);
+
 /* Baseline: decode attention over an uncompressed bf16 KV cache, the
  * reference point of the pages' speed and memory claims ([card]: compared
  * with the FP16 cache; [record] Methodology: throughput over the FP16

@@ -28,7 +28,7 @@ PLANNED = ("kivi_cache_layout", "kivi_decode_workspace_bytes", "kivi_quantize_pr
 
 def test_exports_every_declared_function():
     names = _declared()
-    assert len(names) == 15
+    assert len(names) == 16
     lib = ctypes.CDLL(kivi.library_path())
     for n in names:
         assert hasattr(lib, n), n
@@ -201,6 +201,34 @@ def test_decode_step_validation_before_any_device_work():
     # nothing was enqueued and no counter moved on any error
     assert (c.n_q, c.n_res, c.res_start) == (1024, 159, 0)
     assert flushed.value == 7
+
+
+def test_noalloc_step_validation_before_any_device_work():
+    """kivi_decode_step_noalloc checks everything, including that the step's
+    workspace fits the library's 16 MiB array, before it touches a device."""
+    g = _g().c()
+    fake = ctypes.c_void_p(0x2000)
+    P = ctypes.byref
+    flushed = ctypes.c_int32(7)
+
+    def step(c, k=fake, v=fake, q=fake, out=fake, scale=0.1, geom=g):
+        return _call("kivi_decode_step_noalloc", P(geom), P(c), k, v, q, out,
+                     ctypes.c_float(scale), P(flushed), None)
+
+    c = _cache_struct(n_q=64, n_res=140)
+    assert step(c, k=None) == 1 and step(c, v=None) == 1
+    assert step(c, q=None) == 1 and step(c, out=None) == 1
+    assert step(c, scale=float("nan")) == 2
+    assert step(_cache_struct(n_q=64, n_res=140, null=0)) == 1
+    assert step(_cache_struct(n_q=64, n_res=160)) == 6
+    assert step(_cache_struct(n_q=33, n_res=140)) == 9
+    # 512 (sequence, kv head) pairs x 4 query heads at 24K tokens: ~106 MB of
+    # partials, beyond the array
+    big = _g(batch=64, kv_heads=8, max_tokens=32768)
+    assert kivi.workspace_bytes(big, 24576, 141) > 16 << 20
+    c = _cache_struct(n_q=24576, n_res=140)
+    assert step(c, geom=big.c()) == 7
+    assert (c.n_q, c.n_res, c.res_start) == (24576, 140, 0) and flushed.value == 7
 
 
 def test_dense_attention_validation_before_any_device_work():
