@@ -24,13 +24,17 @@
 // exactly code * 2^-9; the convert's power-of-two scale (2, 512) restores the
 // integer exactly.
 //
-// q.K^T and P.V run on v_mfma_f32_16x16x32_bf16 with the codes as the A
-// operand (16 tokens x 32 channels for q.K^T, 16 channels x 32 tokens for
-// P.V) and the scaled queries / probabilities of up to 4 query heads of the
-// kv head as the B operand (MHA, one query head per kv head, leaves three
-// head columns idle).  The B operand is split into bf16 hi + lo parts
-// (relative error ~2^-16), the parts occupying different MFMA columns (q.K^T)
-// or two MFMAs (P.V), so the result carries close to fp32 precision.
+// q.K^T and P.V run on v_mfma_f32_16x16x32_bf16.  The scores are computed
+// transposed: the scaled queries of up to 4 query heads of the kv head are
+// the A operand (rows head x {hi, lo, hi, lo}) and the codes the B operand
+// (32 channels x 16 tokens), so each lane ends with the scores of two tokens
+// of one head and the softmax is evaluated once per (token, head).  For P.V
+// the codes are the A operand (16 channels x 32 tokens) and the scaled
+// probabilities the B operand (columns channel block x head), reached through
+// a per-wave LDS exchange.  MHA (one query head per kv head) leaves three
+// heads idle.  The scaled queries and probabilities are split into bf16 hi +
+// lo parts (relative error ~2^-16), occupying different MFMA rows (q.K^T) or
+// two MFMAs (P.V), so the result carries close to fp32 precision.
 #include <float.h>
 #include <math.h>
 
@@ -106,12 +110,6 @@ __device__ __forceinline__ void split_bf16(float x0, float x1, uint32_t &hi, uin
   lo = pack_bf16x2(x0 - __uint_as_float(b0 & 0xFFFF0000u), x1 - __uint_as_float(b1 & 0xFFFF0000u));
 }
 
-__device__ __forceinline__ float dpp_ror4(float x) {
-  // row_ror:4 reads every lane of the row, so bound_ctrl is moot; setting it
-  // lets the compiler fold the move into the add that consumes it
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x124,
-                                                                0xF, 0xF, true));
-}
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 
@@ -282,14 +280,6 @@ __device__ __forceinline__ float sum_x32(float x) {
 // IEEE maximum (NaN-propagating): one v_maximum3_f32, where fmaxf on
 // values from a lane exchange would first quiet both operands
 __device__ __forceinline__ float max2(float a, float b) { return __builtin_elementwise_maximum(a, b); }
-__device__ __forceinline__ float max_x16(float x) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return max2(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float max_x32(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return max2(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
 // sum over the 4 lanes n, n+-4, n+-8, n+-12 of each 16-lane row (DPP rotations)
 __device__ __forceinline__ float sum_row_stride4(float x) {
   x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x124, 0xF, 0xF, true));
@@ -482,12 +472,16 @@ union WaveSmem {
   struct {
     uint4 bq[NHB][128];    // q' operand chunks (8 bf16) per head block, indexed by bq_index
     float meta[4][D];      // the group's k_scale, k_zero, v_scale, v_zero
+    float beta[NHB][4];    // q . z^K per head of each block
   } g[2];
   uint16_t vres[G][D];     // one residual chunk of V rows (bf16)
 };
 template <int NHB, int NW>
 struct MfmaSmem {
   WaveSmem<NHB> w[NW];
+  // probabilities of the current group or residual chunk, [head][token],
+  // handed from the score lanes to the P.V lanes
+  float pex[NW][NHB][4][G];
 };
 
 // LDS chunk of the q' operand for (hi/lo xx, head h, MFMA step m, lane group
@@ -498,28 +492,61 @@ __device__ __forceinline__ int bq_index(int xx, int h, int m, int gq) {
   return (m * 4 + h) * 8 + ((xx + h + 2 * gq) & 7);
 }
 
-// Online-softmax state of one wave (per head block): P.V accumulators in the
-// MFMA output layout, running max (log2 units), and per-lane partial sums of
-// p and of p * zero^V.
+// Online-softmax state of one wave (per head block), in two lane roles.
+// Score lanes (column = token slot lane & 15, row group = head lane >> 4):
+// running max (log2 units), the partial sum of p over the lane's tokens, and
+// the finite reference the quantised groups' scores are taken relative to
+// (their MFMA accumulators start at beta - m_ref): m_run once it is finite,
+// 0 before.  P.V lanes (column n = 4j + head, n = lane & 15): accumulators in
+// the MFMA output layout and the partial sum of p * zero^V.
 template <int NHB>
 struct WaveState {
   f32x4_t acc[NHB][8];
-  float m_run[NHB], l_run[NHB], z_run[NHB];
-  // finite reference the quantised groups' scores are taken relative to
-  // (their MFMA accumulators start at beta - m_ref): m_run once it is
-  // finite, 0 before
-  float m_ref[NHB];
+  float z_run[NHB];
+  float m_run[NHB], l_run[NHB], m_ref[NHB];
 };
 
+// Maximum / sum over the 16 lanes of a row (DPP rotations; every lane gets
+// the result).  A row rotation reads every lane of the row, so bound_ctrl is
+// moot; setting it lets the compiler fold the move into the operation that
+// consumes it.
+template <int CTRL>
+__device__ __forceinline__ float dpp_rot(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
+                                                                0xF, 0xF, true));
+}
+__device__ __forceinline__ float row_max16(float x) {
+  x = max2(x, dpp_rot<0x128>(x));   // row_ror:8
+  x = max2(x, dpp_rot<0x124>(x));   // row_ror:4
+  x = max2(x, dpp_rot<0x122>(x));   // row_ror:2
+  return max2(x, dpp_rot<0x121>(x));   // row_ror:1
+}
+__device__ __forceinline__ float row_sum16(float x) {
+  x += dpp_rot<0x128>(x);
+  x += dpp_rot<0x124>(x);
+  x += dpp_rot<0x122>(x);
+  return x + dpp_rot<0x121>(x);
+}
+// x is uniform within each row (a value per head, head = row); returns, in
+// every lane, the value of head lane & 3 (the head of its P.V column)
+__device__ __forceinline__ float head_value_for_pv(float x, int lane) {
+  const int xi = __builtin_bit_cast(int, x);
+  const float a0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 0));
+  const float a1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 16));
+  const float a2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 32));
+  const float a3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 48));
+  const int h = lane & 3;
+  return h == 0 ? a0 : h == 1 ? a1 : h == 2 ? a2 : a3;
+}
+
 // First half of a group: stage its scale/zero in buffer set `buf`, build the
-// q' = q * s^K operand (hi/lo) of every head block there, and return
-// beta = q . z^K per head block (lane with (lane & 3) == head holds it).
-// A group past the end has all-zero loads: its q' and beta are zeros and the
-// buffer set is not read.
+// q' = q * s^K operand (hi/lo) of every head block there, and beta = q . z^K
+// per head (into the set's beta).  A group past the end has all-zero loads:
+// its q' and beta are zeros and the buffer set is not read.
 template <int NHB, int META, int NW>
 __device__ __forceinline__ void prep_group(const uint32_t (&mw)[4][2], MfmaSmem<NHB, NW> &smf,
-                                           int buf, const float (&qv)[NHB][8], float (&beta)[NHB],
-                                           int wave, int lane, int gq, int ch, int cm) {
+                                           int buf, const float (&qv)[NHB][8], int wave, int lane,
+                                           int gq, int ch, int cm) {
   auto &gs = smf.w[wave].g[buf];
   stage_meta<META>(mw, gs.meta, lane);
   __builtin_amdgcn_wave_barrier();
@@ -544,8 +571,8 @@ __device__ __forceinline__ void prep_group(const uint32_t (&mw)[4][2], MfmaSmem<
     }
     gs.bq[hb][bq_index(0, ch, cm, gq)] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
     gs.bq[hb][bq_index(1, ch, cm, gq)] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-    // every lane with (lane & 3) == head gets beta[head]
-    beta[hb] = sum_x32(sum_x16(sum_row_stride4(bt)));
+    // every lane with (lane & 3) == head holds the sum for that head
+    gs.beta[hb][lane & 3] = sum_x32(sum_x16(sum_row_stride4(bt)));
   }
 }
 
@@ -553,12 +580,19 @@ __device__ __forceinline__ void prep_group(const uint32_t (&mw)[4][2], MfmaSmem<
 // scores on the MFMA, the online softmax and P.V.  `mid` runs once, after the
 // first head block's score MFMAs are issued: the next group's prep_group goes
 // there, so that its VALU and LDS work overlaps the matrix core.
+//
+// The scores are computed transposed: q' is the A operand (row 4 head + x,
+// x = hi, lo, hi, lo) and the codes the B operand (column = token slot), so a
+// score lane (column n, row group gq) holds the scores of its two tokens for
+// head gq alone, and the softmax runs once per (token, head).  The
+// probabilities reach the P.V lanes (column n = 4j + head, tokens 8gq ..
+// 8gq + 7) through the wave's LDS exchange area.
 template <int BITS, int NHB, int NW, class Mid>
 __device__ __forceinline__ void attend_group(const GroupRaw<BITS> &raw, WaveState<NHB> &st,
-                                             MfmaSmem<NHB, NW> &smf, int buf,
-                                             const float (&beta)[NHB], int wave, int n, int gq,
+                                             MfmaSmem<NHB, NW> &smf, int buf, int wave, int lane,
                                              Mid &&mid) {
   auto &gs = smf.w[wave].g[buf];
+  const int n = lane & 15, gq = lane >> 4;
   // ---- A operands (exact codes).  With one head block they are unpacked
   // next to the MFMAs that read them (fewer live registers, and the
   // converts issue while the matrix core works); otherwise once, up front.
@@ -591,12 +625,12 @@ __device__ __forceinline__ void attend_group(const GroupRaw<BITS> &raw, WaveStat
 
 #pragma unroll
   for (int hb = 0; hb < NHB; ++hb) {
-    // ---- scores: columns n = 4x + head, x in {hi, lo, hi, lo}
-    // scores relative to m_ref: beta - m_ref enters through the hi columns
+    // ---- scores, transposed: this lane's rows 4gq + r are head gq, x = r;
+    // relative to m_ref, beta - m_ref entering through the hi row (r = 0)
     f32x4_t sc[2];
     {
-      const float bt = (n & 4) ? 0.f : beta[hb] - st.m_ref[hb];
-      sc[0] = f32x4_t{bt, bt, bt, bt};
+      const float bt = gs.beta[hb][gq] - st.m_ref[hb];
+      sc[0] = f32x4_t{bt, 0.f, 0.f, 0.f};
       sc[1] = sc[0];
     }
 #pragma unroll
@@ -605,12 +639,13 @@ __device__ __forceinline__ void attend_group(const GroupRaw<BITS> &raw, WaveStat
         unpack_k(0, m);
         unpack_k(1, m);
       }
-      Op8 bq;
-      const uint4 x = gs.bq[hb][bq_index((n >> 2) & 1, n & 3, m, gq)];
-      bq.u[0] = x.x; bq.u[1] = x.y; bq.u[2] = x.z; bq.u[3] = x.w;
+      // A row n = 4 head + x: q' of head n >> 2, hi / lo by x & 1
+      Op8 aq;
+      const uint4 x = gs.bq[hb][bq_index(n & 1, n >> 2, m, gq)];
+      aq.u[0] = x.x; aq.u[1] = x.y; aq.u[2] = x.z; aq.u[3] = x.w;
 #pragma unroll
       for (int tile = 0; tile < 2; ++tile)
-        sc[tile] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak[tile][m].v, bq.v, sc[tile], 0, 0, 0);
+        sc[tile] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq.v, ak[tile][m].v, sc[tile], 0, 0, 0);
     }
     if (hb == 0) mid();
     // this lane's V scale/zero: channel block n >> 2, tokens 8gq .. 8gq + 7
@@ -623,39 +658,53 @@ __device__ __forceinline__ void attend_group(const GroupRaw<BITS> &raw, WaveStat
         sv[i] = vm[i]; zv[i] = vz[i];
       }
     }
-    // token 8gq + 4*tile + r  <->  p index 4*tile + r
-    float s8[8];
+    // the lane's two scores: tile t holds token 8 (n >> 2) + (n & 3) + 4t
+    float s2[2];
 #pragma unroll
-    for (int tile = 0; tile < 2; ++tile)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) s8[4 * tile + r] = sc[tile][r] + dpp_ror4(sc[tile][r]);
+    for (int tile = 0; tile < 2; ++tile) s2[tile] = sc[tile][0] + sc[tile][1];
 
-    // ---- online softmax (log2 domain), lazily rescaled; s8 is relative to
-    // m_ref, which equals m_run except before the first rescale
-    float mx = fmaxf(fmaxf(fmaxf(s8[0], s8[1]), fmaxf(s8[2], s8[3])),
-                     fmaxf(fmaxf(s8[4], s8[5]), fmaxf(s8[6], s8[7])));
-    mx = max_x32(max_x16(mx));
-    const bool need = mx > st.m_run[hb] - st.m_ref[hb] + kRescaleSlack;
-    if (__any(need)) {
+    // ---- online softmax (log2 domain), lazily rescaled; s2 is relative to
+    // m_ref, which equals m_run except before the first rescale.  A rescale
+    // is due for a head iff its maximum over the wave's 32 tokens passes the
+    // bound, i.e. iff some lane's own maximum does: the lane-local test
+    // decides, and the maximum across the row is taken only when it is due.
+    float mx = fmaxf(s2[0], s2[1]);
+    const float bound = st.m_run[hb] - st.m_ref[hb] + kRescaleSlack;
+    if (__any(mx > bound)) {
+      mx = row_max16(mx);
+      const bool need = mx > bound;
       const float mnew = need ? mx + st.m_ref[hb] : st.m_run[hb];
       const float al = st.m_run[hb] == kNegInf ? 0.f : fast_exp2(st.m_run[hb] - mnew);
-#pragma unroll
-      for (int mt = 0; mt < 8; ++mt) st.acc[hb][mt] *= al;
       st.l_run[hb] *= al;
-      st.z_run[hb] *= al;
       const float d = mnew - st.m_ref[hb];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) s8[k] -= d;
+      s2[0] -= d;
+      s2[1] -= d;
       st.m_run[hb] = mnew;
       st.m_ref[hb] = mnew;
-    }
-    float p[8];
+      // the P.V lanes of each head rescale by that head's factor
+      const float alp = head_value_for_pv(al, lane);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      p[k] = fast_exp2(s8[k]);
-      st.l_run[hb] += p[k];
-      st.z_run[hb] += p[k] * zv[k];
+      for (int mt = 0; mt < 8; ++mt) st.acc[hb][mt] *= alp;
+      st.z_run[hb] *= alp;
     }
+    {
+      const float p0 = fast_exp2(s2[0]), p1 = fast_exp2(s2[1]);
+      st.l_run[hb] += p0 + p1;
+      float *pe = &smf.pex[wave][hb][gq][8 * (n >> 2) + (n & 3)];
+      pe[0] = p0;
+      pe[4] = p1;
+    }
+    __builtin_amdgcn_wave_barrier();
+    // P.V lanes: p of head n & 3 for tokens 8gq .. 8gq + 7
+    float p[8];
+    {
+      const float4 *pr = reinterpret_cast<const float4 *>(&smf.pex[wave][hb][n & 3][8 * gq]);
+      const float4 a = pr[0], b = pr[1];
+      p[0] = a.x; p[1] = a.y; p[2] = a.z; p[3] = a.w;
+      p[4] = b.x; p[5] = b.y; p[6] = b.z; p[7] = b.w;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) st.z_run[hb] += p[k] * zv[k];
     // ---- P.V: columns n = 4j + head; B slot s <-> token 8gq + P8[s]
     Op8 bh, bl;
 #pragma unroll
@@ -671,10 +720,12 @@ __device__ __forceinline__ void attend_group(const GroupRaw<BITS> &raw, WaveStat
 }
 
 // One residual chunk (32 ring slots, `valid` of them live) through the same
-// MFMA pipeline as a quantised group: q.K^T with the bf16 K rows as the A
-// operand and the raw query as B (hi columns; lo columns zero; the softmax
-// scale applied to the scores); P.V with the chunk's V rows transposed
-// through LDS as the A operand and p (hi/lo) as B for every channel block.
+// MFMA pipeline as a quantised group: the transposed scores with the raw
+// query as the A operand (the hi row of each head; the other rows zero; the
+// softmax scale applied to the scores) and the bf16 K rows as B; P.V with the
+// chunk's V rows transposed through LDS as the A operand and p (hi/lo) as B
+// for every channel block, p handed over through the exchange area as for a
+// group.
 template <int NHB, int NW>
 __device__ __forceinline__ void mfma_rchunk(const DecodeArgs &a, int u, int rc,
                                             WaveState<NHB> &st, MfmaSmem<NHB, NW> &smf, int wave,
@@ -709,12 +760,13 @@ __device__ __forceinline__ void mfma_rchunk(const DecodeArgs &a, int u, int rc,
         k_new[tile] ? a.k_new + (long long)u * D + 8 * gq : krows + (long long)row * D + 8 * gq);
   }
   const int b = u / a.kv_heads, h = u % a.kv_heads;
-  // query rows as B operands of q.K^T (hi columns; the lo columns get zeros):
-  // every lane loads a valid row; with one workgroup per compute unit (NW >
-  // 4, registers to spare) those of head block 0 come with the chunk
+  // query rows as A operands of the transposed q.K^T (row n = 4 head + x; the
+  // hi rows x = 0 take the query, the others zeros): every lane loads a
+  // valid row; with one workgroup per compute unit (NW > 4, registers to
+  // spare) those of head block 0 come with the chunk
   constexpr bool kQFirst = NW > 4;
   auto q_rows = [&](int hb) {
-    const int hh = hb * 4 + (n & 3);
+    const int hh = hb * 4 + (n >> 2);
     return reinterpret_cast<const uint4 *>(
         a.q + ((long long)b * a.kv_heads * qpk + (long long)h * qpk + (hh < qpk ? hh : 0)) * D +
         8 * gq);
@@ -777,8 +829,8 @@ __device__ __forceinline__ void mfma_rchunk(const DecodeArgs &a, int u, int rc,
   }
 #pragma unroll
   for (int hb = 0; hb < NHB; ++hb) {
-    const int hh = hb * 4 + (n & 3);
-    const bool hi_col = (n & 4) == 0 && hh < qpk;
+    const int hh = hb * 4 + (n >> 2);
+    const bool hi_row = (n & 3) == 0 && hh < qpk;
     if (hb > 0 || !kQFirst) {
 #pragma unroll
       for (int m = 0; m < 4; ++m) xq[m] = q_rows(hb)[4 * m];
@@ -786,40 +838,48 @@ __device__ __forceinline__ void mfma_rchunk(const DecodeArgs &a, int u, int rc,
     f32x4_t sc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      Op8 bq;
-      const uint4 x = hi_col ? xq[m] : make_uint4(0u, 0u, 0u, 0u);
-      bq.u[0] = x.x; bq.u[1] = x.y; bq.u[2] = x.z; bq.u[3] = x.w;
+      Op8 aq;
+      const uint4 x = hi_row ? xq[m] : make_uint4(0u, 0u, 0u, 0u);
+      aq.u[0] = x.x; aq.u[1] = x.y; aq.u[2] = x.z; aq.u[3] = x.w;
 #pragma unroll
       for (int tile = 0; tile < 2; ++tile)
-        sc[tile] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak[tile][m].v, bq.v, sc[tile], 0, 0, 0);
+        sc[tile] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq.v, ak[tile][m].v, sc[tile], 0, 0, 0);
     }
-    float s8[8];
+    // this lane: head gq, tokens 8 (n >> 2) + (n & 3) + 4 tile of the chunk
+    const int tl = 8 * (n >> 2) + (n & 3);
+    float s2[2];
 #pragma unroll
     for (int tile = 0; tile < 2; ++tile)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float x = (sc[tile][r] + dpp_ror4(sc[tile][r])) * a.qscale;
-        s8[4 * tile + r] = 8 * gq + 4 * tile + r < valid ? x : kNegInf;
-      }
-    float mx = fmaxf(fmaxf(fmaxf(s8[0], s8[1]), fmaxf(s8[2], s8[3])),
-                     fmaxf(fmaxf(s8[4], s8[5]), fmaxf(s8[6], s8[7])));
-    mx = max_x32(max_x16(mx));
-    const bool need = mx > st.m_run[hb] + kRescaleSlack;
-    if (__any(need)) {
+      s2[tile] = tl + 4 * tile < valid ? sc[tile][0] * a.qscale : kNegInf;
+    float mx = fmaxf(s2[0], s2[1]);
+    const float bound = st.m_run[hb] + kRescaleSlack;
+    if (__any(mx > bound)) {
+      mx = row_max16(mx);
+      const bool need = mx > bound;
       const float mnew = need ? mx : st.m_run[hb];
       const float al = st.m_run[hb] == kNegInf ? 0.f : fast_exp2(st.m_run[hb] - mnew);
-#pragma unroll
-      for (int mt = 0; mt < 8; ++mt) st.acc[hb][mt] *= al;
       st.l_run[hb] *= al;
-      st.z_run[hb] *= al;
       st.m_run[hb] = mnew;
       st.m_ref[hb] = mnew;
-    }
-    float p[8];
+      const float alp = head_value_for_pv(al, lane);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      p[k] = fast_exp2(s8[k] - st.m_run[hb]);
-      st.l_run[hb] += p[k];
+      for (int mt = 0; mt < 8; ++mt) st.acc[hb][mt] *= alp;
+      st.z_run[hb] *= alp;
+    }
+    {
+      const float p0 = fast_exp2(s2[0] - st.m_run[hb]), p1 = fast_exp2(s2[1] - st.m_run[hb]);
+      st.l_run[hb] += p0 + p1;
+      float *pe = &smf.pex[wave][hb][gq][tl];
+      pe[0] = p0;
+      pe[4] = p1;
+    }
+    __builtin_amdgcn_wave_barrier();
+    float p[8];
+    {
+      const float4 *pr = reinterpret_cast<const float4 *>(&smf.pex[wave][hb][n & 3][8 * gq]);
+      const float4 a0 = pr[0], a1 = pr[1];
+      p[0] = a0.x; p[1] = a0.y; p[2] = a0.z; p[3] = a0.w;
+      p[4] = a1.x; p[5] = a1.y; p[6] = a1.z; p[7] = a1.w;
     }
     Op8 bh, bl;
 #pragma unroll
@@ -961,9 +1021,8 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeArgs a) {
   }
 
 
-  // q' and beta of the group in flight between prep_group and attend_group,
-  // and the buffer set it occupies
-  float beta[NHB];
+  // the buffer set that holds the q' operand and beta of the group between
+  // prep_group and attend_group
   int buf = 0;
   if constexpr (kDyn) {
     if (threadIdx.x == 0) s_next = wr.g_begin + NW * C;
@@ -978,7 +1037,7 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeArgs a) {
     if (lane == 0) claim = __hip_atomic_fetch_add(&s_next, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     // the first group's prep; each step then preps the wave's next group
     // (in register set k + 1) while it attends to the current one
-    prep_group<NHB, META, NW>(r[0].mw, sm.mf, 0, qv, beta, wave, lane, gq, ch, cm);
+    prep_group<NHB, META, NW>(r[0].mw, sm.mf, 0, qv, wave, lane, gq, ch, cm);
     while (gk[0] < g_end) {
 #pragma unroll
       for (int k = 0; k <= kPrefetch; ++k) {
@@ -1002,13 +1061,10 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeArgs a) {
           else __builtin_amdgcn_s_setprio(1);
         }
         if (gk[k] < g_end) {
-          float bn[NHB];
-          attend_group<BITS, NHB, NW>(r[k], st, sm.mf, buf, beta, wave, n, gq, [&] {
-            prep_group<NHB, META, NW>(r[(k + 1) % (kPrefetch + 1)].mw, sm.mf, buf ^ 1, qv, bn,
+          attend_group<BITS, NHB, NW>(r[k], st, sm.mf, buf, wave, lane, [&] {
+            prep_group<NHB, META, NW>(r[(k + 1) % (kPrefetch + 1)].mw, sm.mf, buf ^ 1, qv,
                                       wave, lane, gq, ch, cm);
           });
-#pragma unroll
-          for (int hb = 0; hb < NHB; ++hb) beta[hb] = bn[hb];
           buf ^= 1;
         }
       }
@@ -1020,7 +1076,7 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeArgs a) {
   // Every pass issues the loads of kPrefetch + 1 groups, so that the
   // outstanding loads at the loop head are the same from either edge; the
   // last pass skips the groups past the end (a wave-uniform branch).
-  prep_group<NHB, META, NW>(r[0].mw, sm.mf, 0, qv, beta, wave, lane, gq, ch, cm);
+  prep_group<NHB, META, NW>(r[0].mw, sm.mf, 0, qv, wave, lane, gq, ch, cm);
   for (int g0 = g_begin; g0 < g_end; g0 += kPrefetch + 1) {
 #pragma unroll
     for (int k = 0; k <= kPrefetch; ++k) {
@@ -1028,13 +1084,10 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeArgs a) {
       load_group<BITS, META, PAGED>(r[(k + kPrefetch) % (kPrefetch + 1)], view, a, u,
                                     g + kPrefetch, g + kPrefetch < g_end);
       if (g < g_end) {
-        float bn[NHB];
-        attend_group<BITS, NHB, NW>(r[k], st, sm.mf, buf, beta, wave, n, gq, [&] {
-          prep_group<NHB, META, NW>(r[(k + 1) % (kPrefetch + 1)].mw, sm.mf, buf ^ 1, qv, bn,
+        attend_group<BITS, NHB, NW>(r[k], st, sm.mf, buf, wave, lane, [&] {
+          prep_group<NHB, META, NW>(r[(k + 1) % (kPrefetch + 1)].mw, sm.mf, buf ^ 1, qv,
                                     wave, lane, gq, ch, cm);
         });
-#pragma unroll
-        for (int hb = 0; hb < NHB; ++hb) beta[hb] = bn[hb];
         buf ^= 1;
       }
     }
@@ -1050,8 +1103,8 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeArgs a) {
   const int jv = n >> 2, hv = n & 3;
 #pragma unroll
   for (int hb = 0; hb < NHB; ++hb) {
-    const float l = sum_x32(sum_x16(st.l_run[hb]));
-    const float z = sum_x32(sum_x16(st.z_run[hb]));
+    const float l = row_sum16(st.l_run[hb]);                // score lanes: head gq
+    const float z = sum_x32(sum_x16(st.z_run[hb]));         // P.V lanes: column n
     // lane (n, gq) holds rows 4gq + r of M-tile mt = channel 32gq + 8r + mt,
     // for column n = 4j + head; the column is useful when j == gq.
     if (jv == gq) {
@@ -1065,9 +1118,9 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeArgs a) {
         *reinterpret_cast<float4 *>(dst + 4) = make_float4(o8[4], o8[5], o8[6], o8[7]);
       }
     }
-    if (gq == 0 && n < 4) {
-      sm.mg.m[wave][hb * 4 + n] = st.m_run[hb];
-      sm.mg.l[wave][hb * 4 + n] = l;
+    if (n == 0) {
+      sm.mg.m[wave][hb * 4 + gq] = st.m_run[hb];
+      sm.mg.l[wave][hb * 4 + gq] = l;
     }
   }
   merge_and_store<HMAX, NW>(sm.mg, a, u, split);
