@@ -12,6 +12,12 @@ import torch
 import oracle
 
 ATTN_TOL = 1e-3
+# Two default launches on the same inputs: the waves of a workgroup may merge
+# their softmax states in the order they finish, a reordering of at most a few
+# dozen fp32 multiply-adds per output (each rounding at 2^-24 relative), so
+# repeats agree far inside this; launches with the deterministic flag repeat
+# bit for bit.
+REPEAT_TOL = 1e-5
 
 
 def to_np(t: torch.Tensor) -> np.ndarray:

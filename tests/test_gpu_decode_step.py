@@ -5,9 +5,11 @@ ring fills and attends.  The check runs the same token stream through the
 three separate calls (append, flush, attend) on a second cache and through
 the CPU oracle:
 
-* the fused and separate paths agree bit for bit: every output, the flush
-  flags, the counters and the cache bytes (the new token's ring slot is
-  written by the attention kernel in the fused path);
+* the fused and separate paths agree bit for bit in the flush flags, the
+  counters and the cache bytes (the new token's ring slot is written by the
+  attention kernel in the fused path), and in every output when launched with
+  the deterministic flag (in the default launch, whose waves may merge in the
+  order they finish, to within 1e-5 row-relative);
 * outputs agree with the oracle within the attention tolerance, and the
   final cache equals the oracle's byte for byte.
 
@@ -23,34 +25,39 @@ import torch
 
 import oracle
 import synth
-from kivi_testutil import ATTN_TOL, assert_same_cache, bits_to_dev, host_cache, row_rel_err, to_np
+from kivi_testutil import ATTN_TOL, REPEAT_TOL, assert_same_cache, bits_to_dev, host_cache, row_rel_err, to_np
 
 kivi = pytest.importorskip("decode_attention_channel_amd.kivi")
 
 pytestmark = pytest.mark.gpu
 
+DET = kivi.FLAG_DETERMINISTIC
 CASES = [
-    # B, H, QPK, bits, R, S0, N
-    (2, 2, 4, 2, 128, 150, 45),
-    (2, 2, 4, 4, 128, 300, 40),
-    (2, 2, 1, 2, 128, 150, 45),
-    (1, 3, 1, 4, 128, 1000, 40),
-    (1, 2, 3, 2, 32, 70, 80),
-    (1, 2, 8, 4, 0, 100, 70),
-    (1, 1, 1, 2, 0, 40, 40),
-    (2, 1, 16, 2, 128, 1, 165),
+    # B, H, QPK, bits, R, S0, N, flags
+    (2, 2, 4, 2, 128, 150, 45, 0),
+    (2, 2, 4, 2, 128, 150, 45, DET),
+    (2, 2, 4, 4, 128, 300, 40, 0),
+    (2, 2, 1, 2, 128, 150, 45, 0),
+    (1, 3, 1, 4, 128, 1000, 40, 0),
+    (1, 3, 1, 4, 128, 1000, 40, DET),
+    (1, 2, 3, 2, 32, 70, 80, 0),
+    (1, 2, 8, 4, 0, 100, 70, 0),
+    (1, 2, 8, 4, 0, 100, 70, DET),
+    (1, 1, 1, 2, 0, 40, 40, 0),
+    (2, 1, 16, 2, 128, 1, 165, 0),
 ]
 
 
-@pytest.mark.parametrize("B,H,QPK,bits,R,S0,N", CASES)
-def test_decode_step_matches_separate_calls_and_oracle(B, H, QPK, bits, R, S0, N):
-    print(f"decode_step B={B} H={H} QPK={QPK} bits={bits} R={R} S0={S0} N={N}", flush=True)
+@pytest.mark.parametrize("B,H,QPK,bits,R,S0,N,flags", CASES)
+def test_decode_step_matches_separate_calls_and_oracle(B, H, QPK, bits, R, S0, N, flags):
+    print(f"decode_step B={B} H={H} QPK={QPK} bits={bits} R={R} S0={S0} N={N} flags={flags}",
+          flush=True)
     w = synth.Workload("case", B, H, QPK, S0 + N, bits, 1, 3, 8.0)
     seed = 1000 + 7 * QPK + bits + R
     k, v = synth.prefill_kv(w, seed)
     kb, vb = synth.bits_u16(k), synth.bits_u16(v)
     T = 32 * ((S0 + N) // 32 + 1)
-    kg = kivi.Geom(B, H, QPK, bits=bits, residual=R, max_tokens=T)
+    kg = kivi.Geom(B, H, QPK, bits=bits, residual=R, max_tokens=T, flags=flags)
     og = oracle.Geom(B, H, QPK, bits=bits, residual=R, max_tokens=T)
     sep, fus = kivi.Cache(kg), kivi.Cache(kg)
     k0, v0 = bits_to_dev(kb[:, :, :S0].copy()), bits_to_dev(vb[:, :, :S0].copy())
@@ -84,7 +91,10 @@ def test_decode_step_matches_separate_calls_and_oracle(B, H, QPK, bits, R, S0, N
         torch.cuda.synchronize()
         o_s, o_f = to_np(out_s), to_np(out_f)
         assert np.isfinite(o_f).all(), f"step {t}: unwritten output"
-        assert np.array_equal(o_s.view(np.uint32), o_f.view(np.uint32)), f"step {t}"
+        if flags & DET:
+            assert np.array_equal(o_s.view(np.uint32), o_f.view(np.uint32)), f"step {t}"
+        else:
+            assert row_rel_err(o_f, o_s) <= REPEAT_TOL, f"step {t}"
         if f_fus or t % 9 == 0 or t == S0 + N - 1:
             err = row_rel_err(o_f, oracle.attention(oc, q, scale))
             assert err <= ATTN_TOL, f"step {t}: row-relative error {err:.3e}"

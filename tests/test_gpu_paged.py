@@ -7,7 +7,9 @@ into the oracle's per-sequence layout and compared byte for byte; outputs and
 per-sequence state are checked at every step.  Also: a sequence whose next
 page is not assigned stops at the flush that needs it (KIVI_SEQ_FULL) while
 the others go on; a prefill whose history lacks a page gives
-KIVI_SEQ_BAD_LENGTH; graph replays of paged steps equal eager steps.
+KIVI_SEQ_BAD_LENGTH; graph replays of paged steps equal eager steps (bitwise
+with the deterministic flag, to within 1e-5 row-relative in the default
+launch, whose waves may merge in the order they finish).
 """
 import math
 
@@ -17,7 +19,7 @@ import torch
 
 import oracle
 import synth
-from kivi_testutil import ATTN_TOL, assert_same_cache, bits_to_dev, row_rel_err, to_np
+from kivi_testutil import ATTN_TOL, REPEAT_TOL, assert_same_cache, bits_to_dev, row_rel_err, to_np
 
 kivi = pytest.importorskip("decode_attention_channel_amd.kivi")
 
@@ -183,13 +185,15 @@ def test_paged_missing_pages():
     assert_same_cache(_gather(pc, 0, table, og1, oc0.n_q, oc0.n_res, oc0.res_start), oc0)
 
 
-def test_paged_steps_in_a_graph_replay_like_eager():
+@pytest.mark.parametrize("flags", [0, 1])
+def test_paged_steps_in_a_graph_replay_like_eager(flags):
+    assert kivi.FLAG_DETERMINISTIC == 1
     B, H, QPK, bits, P = 3, 2, 4, 2, 4
     lens = [155, 412, 1000]   # sequences 0 and 1 flush inside the replays
     reps = 6
     w, kb, vb = _inputs(B, H, QPK, 1000 + 2 * reps + 2, bits, 66)
     T = 32 * ((1000 + 2 * reps + 2) // 32 + 1)
-    g = kivi.Geom(B, H, QPK, bits=bits, max_tokens=T)
+    g = kivi.Geom(B, H, QPK, bits=bits, max_tokens=T, flags=flags)
     NG = T // 32
     seq = torch.tensor(lens, dtype=torch.int32, device="cuda")
     caches, states = [], []
@@ -234,7 +238,10 @@ def test_paged_steps_in_a_graph_replay_like_eager():
         outs[1].fill_(float("nan"))
         two_steps(1)
         torch.cuda.synchronize()
-        assert np.array_equal(g_res.view(np.uint32), to_np(outs[1]).view(np.uint32)), i
+        if flags:
+            assert np.array_equal(g_res.view(np.uint32), to_np(outs[1]).view(np.uint32)), i
+        else:
+            assert row_rel_err(g_res, to_np(outs[1])) <= REPEAT_TOL, i
         assert np.array_equal(to_np(states[0][0]), to_np(states[1][0])), i
     og1 = oracle.Geom(1, H, QPK, bits=bits, max_tokens=T)
     ta, tb = caches[0].block_table.cpu().numpy(), caches[1].block_table.cpu().numpy()

@@ -2,11 +2,14 @@
 
 * quantised history (packed codes, scale, zero) and residual: byte-exact;
 * decode attention: max over rows of ||o - o_ref||_inf / ||o_ref||_inf <= 1e-3;
-* outputs are poisoned (NaN) before each launch, and every run is repeated to
-  check that the result is bitwise deterministic.
+* outputs are poisoned (NaN) before each launch; every case runs twice in the
+  default launch (whose waves may merge in the order they finish, so repeats
+  agree to within 1e-5 row-relative) and twice with the deterministic flag
+  (repeats bitwise equal), and each result is checked against the oracle.
 
 Inputs are seeded synthetic K/V/q with outlier key channels (synth.py).
 """
+import dataclasses
 import math
 
 import numpy as np
@@ -15,7 +18,7 @@ import torch
 
 import oracle
 import synth
-from kivi_testutil import ATTN_TOL, assert_same_cache, bits_to_dev, host_cache, row_rel_err, to_np
+from kivi_testutil import ATTN_TOL, REPEAT_TOL, assert_same_cache, bits_to_dev, host_cache, row_rel_err, to_np
 
 kivi = pytest.importorskip("decode_attention_channel_amd.kivi")
 
@@ -39,21 +42,25 @@ def _attend_and_check(kg, gc, oc, q_bits, scale=None, rows_units=None):
     scale = 1.0 / math.sqrt(128) if scale is None else scale
     q = bits_to_dev(q_bits)
     ws = kivi.Workspace(kg)
-    out = torch.full((kg.batch, kg.q_heads, 128), float("nan"), device=DEV)
-    kivi.decode_attention(kg, gc, q, out=out, softmax_scale=scale, ws=ws)
-    out2 = torch.full_like(out, float("nan"))
-    kivi.decode_attention(kg, gc, q, out=out2, softmax_scale=scale, ws=ws)
+    kd = dataclasses.replace(kg, flags=kg.flags | kivi.FLAG_DETERMINISTIC)
+    outs = []
+    for g in (kg, kg, kd, kd):
+        out = torch.full((kg.batch, kg.q_heads, 128), float("nan"), device=DEV)
+        kivi.decode_attention(g, gc, q, out=out, softmax_scale=scale, ws=ws)
+        outs.append(out)
     torch.cuda.synchronize()
-    o1, o2 = to_np(out), to_np(out2)
-    assert np.isfinite(o1).all(), "unwritten or non-finite output"
-    assert np.array_equal(o1.view(np.uint32), o2.view(np.uint32)), "not deterministic"
+    o = [to_np(x) for x in outs]
+    for x in o:
+        assert np.isfinite(x).all(), "unwritten or non-finite output"
+    assert row_rel_err(o[0], o[1]) <= REPEAT_TOL, "default launches disagree"
+    assert np.array_equal(o[2].view(np.uint32), o[3].view(np.uint32)), "not deterministic"
     ref = oracle.attention(oc, q_bits, scale, units=rows_units)
     if rows_units is not None:
         H, QPK = kg.kv_heads, kg.q_per_kv
         rows = [(u // H, (u % H) * QPK + j) for u in rows_units for j in range(QPK)]
-        o1 = np.stack([o1[b, hq] for b, hq in rows])
+        o = [np.stack([x[b, hq] for b, hq in rows]) for x in o]
         ref = np.stack([ref[b, hq] for b, hq in rows])
-    err = row_rel_err(o1, ref)
+    err = max(row_rel_err(o[0], ref), row_rel_err(o[2], ref))
     assert err <= ATTN_TOL, f"attention row-relative error {err:.3e}"
     return err
 

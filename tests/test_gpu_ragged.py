@@ -12,7 +12,9 @@ kivi_ragged_decode_step) against the oracle run on each sequence alone.
   one whose history is full stops taking tokens and keeps its cache.
 * The two launches of a step take the same arguments every step, so a HIP
   graph of two steps (state buffers swapped) replays them; replays are
-  checked bitwise against the same steps run eagerly.
+  checked against the same steps run eagerly, bitwise with the deterministic
+  flag and to within 1e-5 row-relative in the default launch (whose waves may
+  merge in the order they finish).
 """
 import math
 
@@ -22,7 +24,7 @@ import torch
 
 import oracle
 import synth
-from kivi_testutil import ATTN_TOL, assert_same_cache, bits_to_dev, host_cache, row_rel_err, to_np
+from kivi_testutil import ATTN_TOL, REPEAT_TOL, assert_same_cache, bits_to_dev, host_cache, row_rel_err, to_np
 
 kivi = pytest.importorskip("decode_attention_channel_amd.kivi")
 
@@ -46,8 +48,8 @@ def _padded(x, lens, stride):
     return y
 
 
-def _ragged_cache(B, H, QPK, bits, meta, T, lens, kb, vb, stride):
-    kg = kivi.Geom(B, H, QPK, bits=bits, max_tokens=T, meta_format=meta)
+def _ragged_cache(B, H, QPK, bits, meta, T, lens, kb, vb, stride, flags=0):
+    kg = kivi.Geom(B, H, QPK, bits=bits, max_tokens=T, meta_format=meta, flags=flags)
     gc = kivi.Cache(kg)
     seq = torch.tensor(lens, dtype=torch.int32, device="cuda")
     state = kivi.ragged_prefill(kg, gc, bits_to_dev(_padded(kb, lens, stride)),
@@ -162,15 +164,17 @@ def test_ragged_flags():
     _check_seq_cache(gc, kg, 1, oc1)
 
 
-def test_ragged_steps_in_a_graph_replay_like_eager():
+@pytest.mark.parametrize("flags", [0, 1])
+def test_ragged_steps_in_a_graph_replay_like_eager(flags):
+    assert kivi.FLAG_DETERMINISTIC == 1
     B, H, QPK, bits = 3, 2, 4, 2
     lens = [155, 412, 1000]   # sequences 0 and 1 flush inside the replays (steps 4 and 3)
     stride = max(lens)
     reps = 6
     w, kb, vb = _inputs(B, H, QPK, stride, bits, 55, 2 * reps + 2)
     T = 32 * ((stride + 2 * reps + 2) // 32 + 1)
-    kg, g_cache, ga = _ragged_cache(B, H, QPK, bits, 0, T, lens, kb, vb, stride)
-    _, e_cache, ea = _ragged_cache(B, H, QPK, bits, 0, T, lens, kb, vb, stride)
+    kg, g_cache, ga = _ragged_cache(B, H, QPK, bits, 0, T, lens, kb, vb, stride, flags)
+    _, e_cache, ea = _ragged_cache(B, H, QPK, bits, 0, T, lens, kb, vb, stride, flags)
     gb, eb = torch.empty_like(ga), torch.empty_like(ea)
     g_ws, e_ws = kivi.Workspace(kg), kivi.Workspace(kg)
     kn = torch.empty(2, B, H, 128, dtype=torch.bfloat16, device="cuda")
@@ -220,7 +224,10 @@ def test_ragged_steps_in_a_graph_replay_like_eager():
         e_out.fill_(float("nan"))            # eager work between replays
         two_steps(e_cache, ea, eb, e_ws, e_out)
         torch.cuda.synchronize()
-        assert np.array_equal(g_res.view(np.uint32), to_np(e_out).view(np.uint32)), i
+        if flags:
+            assert np.array_equal(g_res.view(np.uint32), to_np(e_out).view(np.uint32)), i
+        else:
+            assert row_rel_err(g_res, to_np(e_out)) <= REPEAT_TOL, i
         assert np.array_equal(to_np(ga), to_np(ea)), i
     # the used part of each sequence's cache (the rest was never written)
     og = oracle.Geom(B, H, QPK, bits=bits, max_tokens=T)
