@@ -41,6 +41,8 @@
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <type_traits>
+
 #include "kivi_internal.h"
 
 namespace kivi {
@@ -945,13 +947,22 @@ __device__ __forceinline__ WorkRange wave_work(const DecodeArgs &a, int u, int s
 template <int BITS, int NHB, int META, bool PAGED, int NW>
 __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeArgs a) {
   constexpr int HMAX = 4 * NHB;
-  __shared__ __align__(16) union {
-    MfmaSmem<NHB, NW> mf;
-    MergeSmem<HMAX, NW> mg;
-  } sm;
   // NW > 4: the workgroup's groups are handed out to its waves one at a
   // time from this counter (the first kPrefetch + 1 of each wave fixed)
   constexpr bool kDyn = NW > 4;
+  // The merge buffer: with one workgroup per compute unit (NW > 4) there is
+  // room for it beside the staging areas, and each wave writes its totals as
+  // soon as it is done; with several workgroups per compute unit (NW == 4) it
+  // aliases the staging areas, and the waves first wait for each other.
+  struct Apart {
+    MfmaSmem<NHB, NW> mf;
+    MergeSmem<HMAX, NW> mg;
+  };
+  union Shared {
+    MfmaSmem<NHB, NW> mf;
+    MergeSmem<HMAX, NW> mg;
+  };
+  __shared__ __align__(16) std::conditional_t<kDyn, Apart, Shared> sm;
   constexpr int C = kPrefetch + 1;
   __shared__ int s_next;
 
@@ -1097,9 +1108,8 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeArgs a) {
   for (int rc = r_begin; rc < r_end; rc += r_step)
     mfma_rchunk<NHB, NW>(a, u, rc, st, sm.mf, wave, lane, n, gq);
 
-  // ---- per-wave totals, then the workgroup merge (the merge buffer aliases
-  // the staging areas of the other waves: wait until every wave is done)
-  __syncthreads();
+  // ---- per-wave totals, then the workgroup merge
+  if constexpr (!kDyn) __syncthreads();
   const int jv = n >> 2, hv = n & 3;
 #pragma unroll
   for (int hb = 0; hb < NHB; ++hb) {
