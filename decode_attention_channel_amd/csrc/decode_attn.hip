@@ -9,10 +9,13 @@
 // Split-K flash decoding.  Grid (unit, split): the workgroups of a unit (as
 // many as fill the resident slots of the chip in one round) take byte shares
 // of its work -- quantised groups of 32 tokens, then the bf16 residual in
-// chunks of 32 -- and each of their 4 waves a quarter of that, with its own
-// online-softmax state, merged in LDS at the end.  Each workgroup writes
-// (m, l, o[128]) per query head; the last workgroup of a unit to finish
-// merges that unit's partials into `out` (arrival counter in the workspace).
+// chunks of 32.  Within a workgroup each wave keeps its own online-softmax
+// state over its part: a fixed quarter of the share (4 waves, several
+// workgroups per compute unit), or groups taken one at a time from an LDS
+// counter (8 or 12 waves, one workgroup per compute unit).  The waves' states
+// are merged in LDS at the end; each workgroup writes (m, l, o[128]) per
+// query head, and the last workgroup of a unit to finish merges that unit's
+// partials into `out` (arrival counter in the workspace).
 //
 // Dequantisation is folded into the products, which is algebraically the
 // same as dequantise-then-dot:
@@ -948,7 +951,8 @@ template <int BITS, int NHB, int META, bool PAGED, int NW>
 __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeArgs a) {
   constexpr int HMAX = 4 * NHB;
   // NW > 4: the workgroup's groups are handed out to its waves one at a
-  // time from this counter (the first kPrefetch + 1 of each wave fixed)
+  // time from the LDS counter s_next (the first kPrefetch + 1 of each wave
+  // fixed)
   constexpr bool kDyn = NW > 4;
   // The merge buffer: with one workgroup per compute unit (NW > 4) there is
   // room for it beside the staging areas, and each wave writes its totals as
@@ -964,7 +968,7 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeArgs a) {
   };
   __shared__ __align__(16) std::conditional_t<kDyn, Apart, Shared> sm;
   constexpr int C = kPrefetch + 1;
-  __shared__ int s_next;
+  __shared__ int s_next;   // kDyn: the next group to hand out
 
   const int u = blockIdx.x, split = blockIdx.y;
   const int4 next_state = a.state_in ? apply_unit_state(a, u) : make_int4(0, 0, 0, 0);
