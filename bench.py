@@ -72,21 +72,32 @@ def prefill_bytes(w, S, n_q, meta_bytes=4):
                                    4 * r * D)
 
 
+def code_hash(path: str) -> str:
+    """sha256 prefix of a source file's code: '//' comments, trailing blanks
+    and empty lines removed, so that editing a comment keeps the hash."""
+    import hashlib
+    import re
+    lines = []
+    for line in open(path).read().splitlines():
+        line = re.sub(r"//.*$", "", line).rstrip()
+        if line:
+            lines.append(line)
+    return hashlib.sha256("\n".join(lines).encode()).hexdigest()[:16]
+
+
 def read_traffic(kernel_tag: str):
     """HBM traffic per launch measured with rocprofv3 counters (committed
-    summary), valid only while the kernel source is unchanged."""
-    import hashlib
+    summary), valid only while the kernel's code is unchanged."""
     path = os.path.join(ROOT, "profiles", f"{kernel_tag}_traffic.txt")
     src = os.path.join(ROOT, "decode_attention_channel_amd", "csrc", "decode_attn.hip")
     if not os.path.exists(path):
         return None
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
     vals = {}
     for line in open(path):
         if ":" in line and not line.startswith("#"):
             key, val = line.split(":", 1)
             vals[key.strip()] = val.strip()
-    if vals.get("kernel_source_sha256_16") != sha:
+    if vals.get("kernel_code_sha256_16") != code_hash(src):
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])
