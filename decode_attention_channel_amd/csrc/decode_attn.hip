@@ -1008,7 +1008,6 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeArgs a) {
     for (int mt = 0; mt < 8; ++mt) st.acc[hb][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     st.m_run[hb] = kNegInf; st.l_run[hb] = 0.f; st.z_run[hb] = 0.f; st.m_ref[hb] = 0.f;
   }
-  const bool has_groups = g_begin < g_end;
   const RecView view = make_rec_view<BITS, META, PAGED>(a, u, lane);
   // register sets of the load pipeline: kPrefetch groups in flight
   GroupRaw<BITS> r[kPrefetch + 1];

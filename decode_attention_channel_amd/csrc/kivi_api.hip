@@ -50,7 +50,7 @@ kivi_status check_geom(const kivi_geom *g) {
   return KIVI_OK;
 }
 
-kivi_status check_cache(const kivi_geom *g, const kivi_cache *c) {
+kivi_status check_cache(const kivi_geom *, const kivi_cache *c) {
   if (!c) return KIVI_E_NULL;
   if (!c->records || !c->k_res || !c->v_res) return KIVI_E_NULL;
   return KIVI_OK;
