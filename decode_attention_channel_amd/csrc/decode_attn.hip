@@ -134,7 +134,9 @@ __device__ __forceinline__ float ld_shared_agent(const float *p) {
 
 // ---------------------------------------------------------------- merge ---
 // Each wave contributes (m, l, o[128]) per head; the workgroup writes one
-// partial per head: M = max m_w, l = sum 2^(m_w - M) l_w, o likewise.
+// partial per head: M = max m_w, l = sum 2^(m_w - M) l_w, o likewise.  A
+// unit's only workgroup (n_split == 1) writes out = o / l itself instead,
+// the value the combine would compute from its one partial (weight 2^0).
 template <int HMAX, int NW>
 struct MergeSmem {
   float m[NW][HMAX];
@@ -144,9 +146,11 @@ struct MergeSmem {
 };
 
 template <int HMAX, int NW>
-__device__ void merge_and_store(MergeSmem<HMAX, NW> &sm, const DecodeArgs &a, int u, int split) {
+__device__ void merge_and_store(MergeSmem<HMAX, NW> &sm, const DecodeArgs &a, int u, int split,
+                                int4 next_state) {
   __syncthreads();
   const int qpk = a.qpk;
+  const bool direct = a.n_split == 1;
   float *part = a.part + ((long long)u * a.n_split + split) * qpk * kPartStride;
   for (int idx = threadIdx.x; idx < qpk * D; idx += 64 * NW) {
     const int hh = idx / D, c = idx % D;
@@ -160,12 +164,19 @@ __device__ void merge_and_store(MergeSmem<HMAX, NW> &sm, const DecodeArgs &a, in
       l += f * sm.l[w][hh];
       o += f * sm.o[w][hh][c];
     }
+    if (direct) {
+      // a unit with no token (a flagged sequence of a mixed-length batch) gets 0
+      a.out[((long long)u * qpk + hh) * D + c] = l > 0.f ? o / l : 0.f;
+      continue;
+    }
     st_shared_agent(part + hh * kPartStride + 4 + c, o);
     if (c == 0) {
       st_shared_agent(part + hh * kPartStride + 0, M);
       st_shared_agent(part + hh * kPartStride + 1, l);
     }
   }
+  if (direct && threadIdx.x == 0 && a.state_out && u % a.kv_heads == 0)
+    reinterpret_cast<int4 *>(a.state_out)[u / a.kv_heads] = next_state;
 }
 
 // ------------------------------------------------------------ combine -----
@@ -1136,8 +1147,8 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeArgs a) {
       sm.mg.l[wave][hb * 4 + gq] = l;
     }
   }
-  merge_and_store<HMAX, NW>(sm.mg, a, u, split);
-  finish_unit<64 * NW>(a, u, &sm.mg.last, next_state);
+  merge_and_store<HMAX, NW>(sm.mg, a, u, split, next_state);
+  if (a.n_split > 1) finish_unit<64 * NW>(a, u, &sm.mg.last, next_state);
 }
 
 }  // namespace
