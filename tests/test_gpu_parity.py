@@ -107,6 +107,28 @@ def test_prefill_and_attention(B, H, QPK, S, bits):
     _attend_and_check(kg, gc, oc, q)
 
 
+@pytest.mark.parametrize("B,H,QPK", [(32, 32, 1), (16, 64, 4)])
+def test_one_workgroup_per_unit(B, H, QPK):
+    """1024 (sequence, kv head) units at 300 tokens: more units than the
+    chip holds at once, so the launch is the static variant with one
+    workgroup per unit, which writes its output directly from its merge (no
+    partial, no combine).  Checked against the oracle in the default launch
+    and with the deterministic flag."""
+    S, bits = 300, 2
+    print(f"one workgroup per unit: B={B} H={H} QPK={QPK} S={S}", flush=True)
+    w = _wl(B, H, QPK, S, bits)
+    seed = 7100 + B + H + QPK
+    k, v = synth.prefill_kv(w, seed)
+    kb, vb = synth.bits_u16(k), synth.bits_u16(v)
+    kg, og = _geoms(w)
+    gc = kivi.Cache(kg)
+    kivi.quantize_prefill(kg, gc, bits_to_dev(kb), bits_to_dev(vb))
+    oc = oracle.prefill(og, kb, vb)
+    torch.cuda.synchronize()
+    q = synth.bits_u16(synth.query(w, seed))
+    _attend_and_check(kg, gc, oc, q)
+
+
 def test_tiny_workload_exact():
     """Tiny single head, S = 256: 4 key groups + 128 residual, 4 fixed outlier
     channels x10, one prefill and one decode step."""
