@@ -308,6 +308,7 @@ def batch_sweep(args):
                          n_q, n_res)
         rows.setdefault(B, {})["kivi"] = {"us_per_layer": t * 1e6, "tokens_s": B / (t * L),
                                           "hbm_gbps": byt / t / 1e9, "layers_resident": n_layers}
+        print(f"batch sweep: KIVI batch {B}: {t * 1e6:.1f} us per layer", file=sys.stderr, flush=True)
         del st, caches, ws, q, out
         torch.cuda.empty_cache()
     for B in batches(bmax_bf16):
@@ -329,6 +330,7 @@ def batch_sweep(args):
         byt = B * w.kv_heads * S * D * 4 + B * w.q_heads * D * 6
         rows.setdefault(B, {})["bf16"] = {"us_per_layer": t * 1e6, "tokens_s": B / (t * L),
                                           "hbm_gbps": byt / t / 1e9, "layers_resident": n_layers}
+        print(f"batch sweep: bf16 batch {B}: {t * 1e6:.1f} us per layer", file=sys.stderr, flush=True)
         del fns, kv, ws, q, out
         torch.cuda.empty_cache()
     best_kivi = max(r["kivi"]["tokens_s"] for r in rows.values() if "kivi" in r)
