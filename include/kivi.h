@@ -52,9 +52,9 @@
  *    Llama-3-8B-shaped batch of 16 at 8K tokens is one) lets the waves of a
  *    workgroup take token groups as they become free; the grouping of the
  *    fp32 online-softmax sums then depends on timing, and two calls on the
- *    same inputs can differ in the last bits (measured: below 1e-5 of the
- *    row's largest output; the bound of the accuracy target, 1e-3, holds
- *    for both).  Quantised codes and scale/zero bytes never depend on it.
+ *    same inputs can differ in the last bits (measured: up to 3.5e-5 of the
+ *    row's largest output at that batch, none at small ones; the bound of
+ *    the accuracy target, 1e-3, holds for both).  Quantised codes and scale/zero bytes never depend on it.
  *  - The whole batch moves in lockstep: one (n_q, n_res, res_start) triple
  *    describes every sequence of the batch.
  *  - Numbers: bf16 tensors are passed as uint16_t bit patterns.  Inputs must

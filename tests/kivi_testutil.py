@@ -12,12 +12,15 @@ import torch
 import oracle
 
 ATTN_TOL = 1e-3
-# Two default launches on the same inputs: the waves of a workgroup may merge
-# their softmax states in the order they finish, a reordering of at most a few
-# dozen fp32 multiply-adds per output (each rounding at 2^-24 relative), so
-# repeats agree far inside this; launches with the deterministic flag repeat
-# bit for bit.
-REPEAT_TOL = 1e-5
+# Two default launches on the same inputs: when the waves of a workgroup take
+# token groups as they become free, the grouping of the fp32 online-softmax
+# sums depends on timing.  Small launches repeat bit for bit; the 8K GQA
+# launch (128 units, 256 groups each) differed by up to 3.5e-5 of the row's
+# largest output over 20 repeats.  The bound leaves a margin over that and
+# stays 5x inside the accuracy target (each result is also checked against
+# the oracle at ATTN_TOL); launches with the deterministic flag repeat bit
+# for bit.
+REPEAT_TOL = 2e-4
 
 
 def to_np(t: torch.Tensor) -> np.ndarray:

@@ -9,7 +9,7 @@ the CPU oracle:
   counters and the cache bytes (the new token's ring slot is written by the
   attention kernel in the fused path), and in every output when launched with
   the deterministic flag (in the default launch, whose waves may merge in the
-  order they finish, to within 1e-5 row-relative);
+  order they finish, to within REPEAT_TOL (2e-4) row-relative);
 * outputs agree with the oracle within the attention tolerance, and the
   final cache equals the oracle's byte for byte.
 

@@ -8,7 +8,7 @@ per-sequence state are checked at every step.  Also: a sequence whose next
 page is not assigned stops at the flush that needs it (KIVI_SEQ_FULL) while
 the others go on; a prefill whose history lacks a page gives
 KIVI_SEQ_BAD_LENGTH; graph replays of paged steps equal eager steps (bitwise
-with the deterministic flag, to within 1e-5 row-relative in the default
+with the deterministic flag, to within REPEAT_TOL (2e-4) row-relative in the default
 launch, whose waves may merge in the order they finish).
 """
 import math

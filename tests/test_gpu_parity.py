@@ -4,7 +4,7 @@
 * decode attention: max over rows of ||o - o_ref||_inf / ||o_ref||_inf <= 1e-3;
 * outputs are poisoned (NaN) before each launch; every case runs twice in the
   default launch (whose waves may merge in the order they finish, so repeats
-  agree to within 1e-5 row-relative) and twice with the deterministic flag
+  agree to within REPEAT_TOL (2e-4) row-relative) and twice with the deterministic flag
   (repeats bitwise equal), and each result is checked against the oracle.
 
 Inputs are seeded synthetic K/V/q with outlier key channels (synth.py).

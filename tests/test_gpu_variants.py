@@ -14,7 +14,7 @@ import torch
 
 import oracle
 import synth
-from kivi_testutil import ATTN_TOL, bits_to_dev, row_rel_err, to_np
+from kivi_testutil import ATTN_TOL, REPEAT_TOL, bits_to_dev, row_rel_err, to_np
 
 kivi = pytest.importorskip("decode_attention_channel_amd.kivi")
 
@@ -54,6 +54,5 @@ def test_static_and_dynamic_launches_match_the_oracle(B, H, S, bits, meta):
             for o in runs[1:]:
                 np.testing.assert_array_equal(o, runs[0])
         outs[flags] = runs[0]
-    # the variants differ only in how fp32 partial sums are grouped: each is
-    # ~1e-5 from the exact result, so the two are within 1e-4 of each other
-    assert row_rel_err(outs[0], outs[kivi.FLAG_DETERMINISTIC]) <= 1e-4
+    # the variants differ only in how fp32 partial sums are grouped
+    assert row_rel_err(outs[0], outs[kivi.FLAG_DETERMINISTIC]) <= REPEAT_TOL

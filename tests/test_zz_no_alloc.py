@@ -2,7 +2,7 @@
 device array) against kivi_decode_step with a caller workspace, through the
 C ABI: two calls in a row, the second on a smaller input, each compared with
 kivi_decode_step on identical inputs (cache bytes exact; outputs bitwise
-equal for deterministic launches, within 1e-4 otherwise) and with the oracle
+equal for deterministic launches, within REPEAT_TOL otherwise) and with the oracle
 (1e-3).  The first call flushes a group, so its launches are the flush and
 the attention with the fused append."""
 import math
@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import synth
-from kivi_testutil import ATTN_TOL, row_rel_err, to_np
+from kivi_testutil import ATTN_TOL, REPEAT_TOL, row_rel_err, to_np
 
 kivi = pytest.importorskip("decode_attention_channel_amd.kivi")
 
@@ -55,7 +55,7 @@ def _one_call(B, H, QPK, S, bits, flags, seed):
     if flags & kivi.FLAG_DETERMINISTIC:
         np.testing.assert_array_equal(go, ro)
     else:
-        assert row_rel_err(go, ro) <= 1e-4
+        assert row_rel_err(go, ro) <= REPEAT_TOL
     og = oracle.Geom(B, H, QPK, bits=bits, max_tokens=T)
     oc = oracle.prefill(og, synth.bits_u16(k), synth.bits_u16(v))
     oracle.append(oc, synth.bits_u16(kn), synth.bits_u16(vn))
