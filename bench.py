@@ -33,7 +33,8 @@ Workload (Llama-3-8B GQA geometry of the catalog record kivi-2bit-llama3-8b-gqa-
   it;
 * cpu_baseline: the CPU oracle (plain C) on a bounded sample of the same
   workload (eight layers' worth of (sequence, kv head) units), threads over
-  units, plus a single-thread rate on a smaller sample.
+  units, plus a single-thread rate on a smaller sample, and one residual
+  flush per layer at the 32K 4-bit geometry (4 sequences x 8 kv heads).
 
 Prints one JSON line.
 """
@@ -200,6 +201,51 @@ def cpu_baseline(w, seed, units_wanted=1024, meta=0, units_1thread=64):
         "cpu_model": _cpu_model(),
         "quantize_gelem_s": 2 * n * n_q * w.head_dim / t_prefill / 1e9,
         "attn_wall_s": t_attn, "prefill_wall_s": t_prefill, "attn_wall_s_1thread": t_attn1,
+        "flush": cpu_flush_baseline(seed, threads, meta),
+    }
+
+
+def cpu_flush_baseline(seed, threads, meta=0, name="llama3-8b-gqa-32k-4bit", layers=32,
+                       steps=4):
+    """Oracle residual flush timed at the 32K 4-bit workload, one flush per
+    layer per decode step: a flush quantises the oldest G ring tokens of every
+    (sequence, kv head) unit into a new group, and its cost does not depend on
+    the history length, so each layer's cache is built from a prefill of
+    R+G-1 tokens and one appended token (n_res = R+G).  `steps` steps' worth
+    of layer caches are flushed threaded over layers, one step's worth on one
+    thread, after one untimed flush."""
+    import oracle
+    import synth
+    w = synth.WORKLOADS[name]
+    og = oracle.Geom(w.batch, w.kv_heads, w.q_per_kv, bits=w.bits, max_tokens=192, meta=meta)
+    S = og.residual + og.group - 1
+
+    def ready(layer):
+        k, v = synth.prefill_kv(w, seed + 4099, layer, seq_len=S)
+        c = oracle.prefill(og, synth.bits_u16(k), synth.bits_u16(v))
+        kn, vn = synth.new_token(w, seed + 4099, layer, 0)
+        oracle.append(c, synth.bits_u16(kn), synth.bits_u16(vn))
+        return c
+
+    base = [ready(layer) for layer in range(layers)]
+    oracle.flush(base[0].copy())
+    caches = [base[i % layers].copy() for i in range(steps * layers)]
+    with concurrent.futures.ThreadPoolExecutor(threads) as ex:
+        t0 = time.perf_counter()
+        flushed = list(ex.map(oracle.flush, caches))
+        t_thr = (time.perf_counter() - t0) / steps
+    t0 = time.perf_counter()
+    flushed += [oracle.flush(c) for c in base]
+    t_one = time.perf_counter() - t0
+    assert all(f == 1 for f in flushed) and all(c.n_q == og.group for c in caches + base)
+    elems = 2 * layers * w.batch * w.kv_heads * og.group * w.head_dim
+    return {
+        "workload": name, "cores": threads,
+        "ms_per_step": t_thr * 1e3, "ms_per_step_1thread": t_one * 1e3,
+        "gelem_s": elems / t_thr / 1e9,
+        "sample": (f"one flush in each of {layers} layers ({w.batch} sequences x {w.kv_heads} "
+                   f"kv heads, {og.group} tokens of K and V each) per step, {steps} steps "
+                   f"threaded over layers, one step on one thread"),
     }
 
 
