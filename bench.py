@@ -632,6 +632,8 @@ def main():
     ap.add_argument("--meta", choices=("fp32", "fp16"), default="fp32",
                     help="scale/zero format: fp32 scale + zero (default), or fp16 scale + "
                          "bf16 zero")
+    ap.add_argument("--deterministic", action="store_true",
+                    help="time the bitwise-repeatable launch (KIVI_FLAG_DETERMINISTIC)")
     ap.add_argument("--no-other", action="store_true",
                     help="skip the whole-step measurement of the other workloads")
     ap.add_argument("--no-ragged", action="store_true",
@@ -680,7 +682,9 @@ def main():
     max_tokens = G * math.ceil((w.seq_len - R + cap_steps + G) / G)
     meta = kivi.META_FP16_BF16 if args.meta == "fp16" else kivi.META_FP32
     geom = kivi.Geom(w.batch, w.kv_heads, w.q_per_kv, bits=w.bits, max_tokens=max_tokens,
-                     meta_format=meta)
+                     meta_format=meta,
+                     flags=kivi.FLAG_DETERMINISTIC if args.deterministic else 0)
+    default_launch = args.meta == "fp32" and not args.deterministic
 
     caches = [kivi.Cache(geom, dev) for _ in range(layers)]
     ws = kivi.Workspace(geom, dev)
@@ -817,6 +821,7 @@ def main():
                    "q_heads": w.q_heads, "head_dim": D, "context": w.seq_len, "bits": w.bits,
                    "group": G, "residual": R, "layers": layers,
                    "scale_zero": "fp16 scale + bf16 zero" if args.meta == "fp16" else "fp32",
+                   "launch": "deterministic" if args.deterministic else "default",
                    "step": "per layer: kivi_decode_step (append + flush-if-full + decode "
                            "attention; one launch, two on flush steps)"},
         "ms_per_step_separate_calls": t_steps_sep / n_timed * 1e3,
@@ -834,13 +839,13 @@ def main():
         "quantize_prefill_ms_per_layer": pre_t / layers * 1e3,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": (read_traffic(f"decode_attn_{w.name}") if args.meta == "fp32"
+                     "traffic": (read_traffic(f"decode_attn_{w.name}") if default_launch
                                  else None)},
         "mixed_length_steps": ragged,
         "paper_context": "2.35x-3.47x decode throughput vs FP16 and 2.6x less peak memory "
                          "(Llama-2-7B, one A100 80GB; not comparable, quoted as context)",
     }
-    if not args.no_other and args.workload == "llama3-8b-gqa-8k" and args.meta == "fp32":
+    if not args.no_other and args.workload == "llama3-8b-gqa-8k" and default_launch:
         # the headline's caches first give way to the others'
         del steppers, caches, ws, new_tok
         torch.cuda.empty_cache()
