@@ -958,13 +958,18 @@ __device__ __forceinline__ WorkRange wave_work(const DecodeArgs &a, int u, int s
 // hardware issues less often take fewer groups and all finish together; the
 // grouping of the online-softmax sums then depends on timing, so results may
 // differ between launches in the last bits.
-template <int BITS, int NHB, int META, bool PAGED, int NW>
+template <int BITS, int NHB, int META, bool PAGED, int NW, bool FIXED>
 __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeArgs a) {
   constexpr int HMAX = 4 * NHB;
-  // NW > 4: the workgroup's groups are handed out to its waves one at a
-  // time from the LDS counter s_next (the first kPrefetch + 1 of each wave
-  // fixed)
+  // NW > 4: one workgroup per compute unit.  Its groups are handed out to
+  // the waves one at a time from the LDS counter s_next (the first
+  // kPrefetch + 1 of each wave fixed), or with FIXED round-robin (wave w
+  // takes groups w, w + NW, ...), which makes every wave's groups, and so the
+  // result, independent of timing.
   constexpr bool kDyn = NW > 4;
+  static_assert(!FIXED || kDyn, "fixed round-robin claims are a form of the one-workgroup launch");
+  // groups between a wave's consecutive claims
+  constexpr int kClaimStride = FIXED ? NW : 1;
   // The merge buffer: with one workgroup per compute unit (NW > 4) there is
   // room for it beside the staging areas, and each wave writes its totals as
   // soon as it is done; with several workgroups per compute unit (NW == 4) it
@@ -996,7 +1001,7 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeArgs a) {
   const WorkRange wr = kDyn ? wave_work(a, u, split, 0, 1, BITS + kMetaBytes<META> / 2, 16)
                             : wave_work(a, u, split, wave, NW, BITS + kMetaBytes<META> / 2, 16);
   const int g_end = wr.g_end;
-  const int g_begin = kDyn ? wr.g_begin + wave * C : wr.g_begin;
+  const int g_begin = kDyn ? wr.g_begin + wave * (FIXED ? 1 : C) : wr.g_begin;
   const int r_begin = kDyn ? wr.r_begin + wave : wr.r_begin;
   const int r_end = wr.r_end;
   constexpr int r_step = kDyn ? NW : 1;
@@ -1024,7 +1029,8 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeArgs a) {
   GroupRaw<BITS> r[kPrefetch + 1];
 #pragma unroll
   for (int i = 0; i < kPrefetch; ++i) {
-    load_group<BITS, META, PAGED>(r[i], view, a, u, g_begin + i, g_begin + i < g_end);
+    const int g = g_begin + i * kClaimStride;
+    load_group<BITS, META, PAGED>(r[i], view, a, u, g, g < g_end);
     // keep the groups' loads in group order, as in the loop, so that the
     // wait counts at the loop head are the steady-state ones
     __builtin_amdgcn_sched_barrier(0);
@@ -1056,10 +1062,11 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeArgs a) {
     // ones, then one claimed per step, claimed a step before it is loaded
     int gk[C];
 #pragma unroll
-    for (int k = 0; k < C; ++k) gk[k] = g_begin + k;
-    int to_load = g_begin + kPrefetch;   // loaded at the next step
-    int claim = 0;
-    if (lane == 0) claim = __hip_atomic_fetch_add(&s_next, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    for (int k = 0; k < C; ++k) gk[k] = g_begin + k * kClaimStride;
+    int to_load = g_begin + kPrefetch * kClaimStride;   // loaded at the next step
+    int claim = g_begin + (kPrefetch + 1) * kClaimStride;
+    if (!FIXED && lane == 0)
+      claim = __hip_atomic_fetch_add(&s_next, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     // the first group's prep; each step then preps the wave's next group
     // (in register set k + 1) while it attends to the current one
     prep_group<NHB, META, NW>(r[0].mw, sm.mf, 0, qv, wave, lane, gq, ch, cm);
@@ -1069,9 +1076,14 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeArgs a) {
         const int slot = (k + kPrefetch) % (kPrefetch + 1);
         gk[slot] = to_load;
         load_group<BITS, META, PAGED>(r[slot], view, a, u, to_load, to_load < g_end);
-        to_load = __builtin_amdgcn_readfirstlane(claim);
-        if (lane == 0)
-          claim = __hip_atomic_fetch_add(&s_next, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if constexpr (FIXED) {
+          to_load = claim;
+          claim += NW;
+        } else {
+          to_load = __builtin_amdgcn_readfirstlane(claim);
+          if (lane == 0)
+            claim = __hip_atomic_fetch_add(&s_next, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
         // issue priority from the live groups still in this wave's register
         // sets: the same for all waves while groups remain to be claimed; at
         // the end the waves with more left are served first, so that the
@@ -1168,21 +1180,28 @@ namespace {
 // spare, and its unpack-once path needs fewer vector instructions per group
 // than fp32 FMAs would.
 constexpr int kDynVariant = 5;
+// 6: the same launch with fixed round-robin claims (bitwise repeatable).
+// 8K GQA on one MI355X: 30.5-30.9 us per launch, against 29.3-30.0 us for 5
+// and 33.5-34.2 us for 1 with its three-per-CU round.
+constexpr int kDynFixedVariant = 6;
 template <int BITS, int META>
 constexpr int kDynWaves = BITS == 2 || META == 1 ? 12 : 8;
 int variant_waves(int bits, int meta, int variant) {
-  if (variant != kDynVariant) return 4;
+  if (variant != kDynVariant && variant != kDynFixedVariant) return 4;
   return bits == 2 || meta == 1 ? 12 : 8;
 }
 
 template <int BITS, int META, bool PAGED>
 void *kernel_fn_t(int variant) {
   switch (variant) {
-    case 1: return (void *)&decode_gqa_kernel<BITS, 1, META, PAGED, 4>;
-    case kDynVariant: return (void *)&decode_gqa_kernel<BITS, 1, META, PAGED, kDynWaves<BITS, META>>;
-    case 2: return (void *)&decode_gqa_kernel<BITS, 2, META, PAGED, 4>;
-    case 3: return (void *)&decode_gqa_kernel<BITS, 3, META, PAGED, 4>;
-    default: return (void *)&decode_gqa_kernel<BITS, 4, META, PAGED, 4>;
+    case 1: return (void *)&decode_gqa_kernel<BITS, 1, META, PAGED, 4, false>;
+    case kDynVariant:
+      return (void *)&decode_gqa_kernel<BITS, 1, META, PAGED, kDynWaves<BITS, META>, false>;
+    case kDynFixedVariant:
+      return (void *)&decode_gqa_kernel<BITS, 1, META, PAGED, kDynWaves<BITS, META>, true>;
+    case 2: return (void *)&decode_gqa_kernel<BITS, 2, META, PAGED, 4, false>;
+    case 3: return (void *)&decode_gqa_kernel<BITS, 3, META, PAGED, 4, false>;
+    default: return (void *)&decode_gqa_kernel<BITS, 4, META, PAGED, 4, false>;
   }
 }
 
@@ -1204,7 +1223,7 @@ struct Residency {
 };
 
 Residency residency(int bits, int meta, int variant, bool paged) {
-  static int cache[16][2][2][2][6][2];   // 0 = not yet queried
+  static int cache[16][2][2][2][7][2];   // 0 = not yet queried
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
   int *slot = cache[dev & 15][bits == 4 ? 1 : 0][meta == 1 ? 1 : 0][paged ? 1 : 0][variant];
@@ -1298,12 +1317,14 @@ hipError_t launch_decode(int bits, int meta, const DecodeArgs &a_in, bool determ
   // Up to 4 query heads per kv head and at most one unit per compute unit:
   // the launch is a single round, whose end the slowest wave sets, so the
   // dynamic variant (one workgroup per compute unit, waves balanced by an
-  // LDS counter) is used, unless the caller asked for bitwise-repeatable
-  // results (its summation order depends on timing).  Longer launches refill
-  // their slots as workgroups finish and keep the static variant.
-  if (variant == 1 && !deterministic) {
-    const Residency rd = residency(bits, meta, kDynVariant, paged);
-    if ((long long)a_in.n_units <= (long long)rd.per_cu * rd.cus) variant = kDynVariant;
+  // LDS counter) is used; a caller that asked for bitwise-repeatable results
+  // gets the same launch with fixed round-robin claims (the counter's order
+  // depends on timing).  Longer launches refill their slots as workgroups
+  // finish and keep the static variant.
+  if (variant == 1) {
+    const int dyn = deterministic ? kDynFixedVariant : kDynVariant;
+    const Residency rd = residency(bits, meta, dyn, paged);
+    if ((long long)a_in.n_units <= (long long)rd.per_cu * rd.cus) variant = dyn;
   }
   const Residency res = residency(bits, meta, variant, paged);
   const int slots = res.per_cu * res.cus;

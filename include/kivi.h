@@ -54,7 +54,10 @@
  *    fp32 online-softmax sums then depends on timing, and two calls on the
  *    same inputs can differ in the last bits (measured: up to 3.5e-5 of the
  *    row's largest output at that batch, none at small ones; the bound of
- *    the accuracy target, 1e-3, holds for both).  Quantised codes and scale/zero bytes never depend on it.
+ *    the accuracy target, 1e-3, holds for both).  With the flag such a
+ *    launch keeps its shape but hands the groups out round-robin (measured
+ *    about 3% slower at that batch).  Quantised codes and scale/zero bytes
+ *    never depend on the flag.
  *  - The whole batch moves in lockstep: one (n_q, n_res, res_start) triple
  *    describes every sequence of the batch.
  *  - Numbers: bf16 tensors are passed as uint16_t bit patterns.  Inputs must

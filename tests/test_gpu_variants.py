@@ -1,11 +1,12 @@
-"""GPU parity of both launch variants of the decode kernel against the oracle:
-the static one (four waves per workgroup, fixed shares; chosen with
-KIVI_FLAG_DETERMINISTIC) and the dynamic one (one workgroup per compute unit
-whose waves take groups from an LDS counter; the default when every
-(sequence, kv head) fits on its own compute unit).  Two shapes: few units at
+"""GPU parity of both launches of the decode kernel against the oracle when
+every (sequence, kv head) fits on its own compute unit (one workgroup per
+compute unit): by default its waves take groups from an LDS counter; with
+KIVI_FLAG_DETERMINISTIC they take them round-robin.  Two shapes: few units at
 a long context (many workgroups per unit) and 256 units (one workgroup per
-unit, so that its waves claim groups to the end of the unit).  The static
-variant must also repeat bitwise."""
+unit, so that its waves claim groups to the end of the unit).  The
+round-robin launch must also repeat bitwise.  (The four-wave static launch,
+used when the units outnumber the compute units, is covered by the
+many-unit cases of test_gpu_parity.py.)"""
 import math
 
 import numpy as np
