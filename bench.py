@@ -31,6 +31,9 @@ Workload (Llama-3-8B GQA geometry of the catalog record kivi-2bit-llama3-8b-gqa-
 * copy bandwidth: a plain 1 GiB device-to-device copy (torch copy_), timed
   with HIP events; the decode kernel's rate is also reported as a fraction of
   it;
+* --deterministic times the same legs with KIVI_FLAG_DETERMINISTIC (the
+  bitwise-repeatable launch); its line carries no traffic figure, which was
+  counted for the default launch;
 * cpu_baseline: the CPU oracle (plain C) on a bounded sample of the same
   workload (eight layers' worth of (sequence, kv head) units), threads over
   units, plus a single-thread rate on a smaller sample, and one residual
