@@ -11,8 +11,9 @@
 // of its work -- quantised groups of 32 tokens, then the bf16 residual in
 // chunks of 32.  Within a workgroup each wave keeps its own online-softmax
 // state over its part: a fixed quarter of the share (4 waves, several
-// workgroups per compute unit), or groups taken one at a time from an LDS
-// counter (8 or 12 waves, one workgroup per compute unit).  The waves' states
+// workgroups per compute unit), or, with one workgroup of 8 or 12 waves per
+// compute unit, groups taken one at a time from an LDS counter (the default)
+// or round-robin (bitwise-repeatable results).  The waves' states
 // are merged in LDS at the end; each workgroup writes (m, l, o[128]) per
 // query head, and the last workgroup of a unit to finish merges that unit's
 // partials into `out` (arrival counter in the workspace).
