@@ -331,7 +331,16 @@ kivi_status kivi_quantize_prefill(const kivi_geom *g, kivi_cache *c, const uint1
   if (n_q > g->max_tokens || r > slots) return KIVI_E_CAPACITY;
   hipStream_t s = (hipStream_t)stream;
   const int U = (int)units_of(g);
+  // the r residual tokens go to ring slots 0.. (r >= 1 since seq_len >= 1)
+  kivi::CopyRowsArgs res{};
+  res.src_k = k; res.src_v = v;
+  res.src_unit_stride = (long long)seq_len * g->head_dim;
+  res.src_tok0 = n_q;
+  res.dst_k = c->k_res; res.dst_v = c->v_res;
+  res.dst_unit_stride = (long long)slots * g->head_dim;
+  res.dst_row0 = 0; res.n_rows = r; res.n_units = U;
   if (n_q > 0) {
+    // one launch: the groups, and the residual rows in extra workgroups
     kivi::QuantizeArgs a{};
     a.src_k = k; a.src_v = v;
     a.src_unit_stride = (long long)seq_len * g->head_dim;
@@ -339,17 +348,10 @@ kivi_status kivi_quantize_prefill(const kivi_geom *g, kivi_cache *c, const uint1
     a.n_groups = n_q / G; a.n_units = U; a.dst_g0 = 0;
     a.max_tokens = g->max_tokens; a.n_groups_cap = g->max_tokens / G;
     a.records = c->records;
-      if ((st = hip_status(kivi::launch_quantize(g->bits, g->meta_format, a, s))) != KIVI_OK) return st;
-  }
-  if (r > 0) {
-    kivi::CopyRowsArgs a{};
-    a.src_k = k; a.src_v = v;
-    a.src_unit_stride = (long long)seq_len * g->head_dim;
-    a.src_tok0 = n_q;
-    a.dst_k = c->k_res; a.dst_v = c->v_res;
-    a.dst_unit_stride = (long long)slots * g->head_dim;
-    a.dst_row0 = 0; a.n_rows = r; a.n_units = U;
-    if ((st = hip_status(kivi::launch_copy_rows(a, s))) != KIVI_OK) return st;
+    a.res = res;
+    if ((st = hip_status(kivi::launch_quantize(g->bits, g->meta_format, a, s))) != KIVI_OK) return st;
+  } else if ((st = hip_status(kivi::launch_copy_rows(res, s))) != KIVI_OK) {
+    return st;
   }
   c->n_q = n_q;
   c->n_res = r;

@@ -107,6 +107,20 @@ __host__ __device__ constexpr int rec_bytes(int bits, int meta) {
   return rec_planes(bits, meta) * kPlaneBytes;
 }
 
+// Copy `n_rows` bf16 rows of D channels per unit (K and V) from
+// src + u*src_unit_stride + (src_tok0 + i)*D to dst + u*dst_unit_stride +
+// (dst_row0 + i)*D.
+struct CopyRowsArgs {
+  const uint16_t *src_k, *src_v;
+  long long src_unit_stride;
+  int src_tok0;
+  uint16_t *dst_k, *dst_v;
+  long long dst_unit_stride;
+  int dst_row0;
+  int n_rows, n_units;
+};
+hipError_t launch_copy_rows(const CopyRowsArgs &a, hipStream_t s);
+
 // One launch of the group quantiser: `n_groups` groups of G tokens for each
 // of `n_units` units.  Source token i of local group gl of unit u is row
 // (src_tok0 + gl*G + i) of a [rows][D] bf16 block starting at
@@ -127,22 +141,11 @@ struct QuantizeArgs {
   const int32_t *seq_lens, *state;
   int kv_heads, residual, slots, stride;
   PageMap pages;   // destination group slots (group_slot)
+  // Prefill: residual rows copied by extra workgroups of the same launch
+  // (res.n_rows 0: none); its unit count and source are those above.
+  CopyRowsArgs res;
 };
 hipError_t launch_quantize(int bits, int meta, const QuantizeArgs &a, hipStream_t s);
-
-// Copy `n_rows` bf16 rows of D channels per unit (K and V) from
-// src + u*src_unit_stride + (src_tok0 + i)*D to dst + u*dst_unit_stride +
-// (dst_row0 + i)*D.
-struct CopyRowsArgs {
-  const uint16_t *src_k, *src_v;
-  long long src_unit_stride;
-  int src_tok0;
-  uint16_t *dst_k, *dst_v;
-  long long dst_unit_stride;
-  int dst_row0;
-  int n_rows, n_units;
-};
-hipError_t launch_copy_rows(const CopyRowsArgs &a, hipStream_t s);
 
 // Mixed-length prefill: copy each sequence's residual tokens into ring slots
 // 0.. and write its state.

@@ -338,7 +338,23 @@ __device__ __forceinline__ void quantize_values(const QuantizeArgs &a, int u, in
   value_group<BITS, META>(a, u, gl1 - 1, nxt, part, lane, tile);
 }
 
-// Grid (ceil(n_groups / gpw), n_units): waves 0-1 take the keys (channel
+// One 16-byte piece of the row copy: piece `idx` of unit u, the K rows'
+// pieces first, then the V rows'.
+__device__ __forceinline__ void copy_row_piece(const CopyRowsArgs &a, int idx, int u) {
+  constexpr int CH = kHeadDim / 8;   // 16-byte pieces per row
+  const int per = a.n_rows * CH;
+  if (idx >= 2 * per) return;
+  const bool is_v = idx >= per;
+  const int i = (idx - (is_v ? per : 0)) / CH, c = idx % CH;
+  const uint16_t *src = is_v ? a.src_v : a.src_k;
+  uint16_t *dst = is_v ? a.dst_v : a.dst_k;
+  const uint4 v = *reinterpret_cast<const uint4 *>(
+      src + (long long)u * a.src_unit_stride + (long long)(a.src_tok0 + i) * kHeadDim + 8 * c);
+  *reinterpret_cast<uint4 *>(dst + (long long)u * a.dst_unit_stride +
+                             (long long)(a.dst_row0 + i) * kHeadDim + 8 * c) = v;
+}
+
+// Grid (ceil(n_groups / gpw) + residual blocks, n_units): waves 0-1 take the keys (channel
 // halves), waves 2-3 the values (token halves) of `gpw` consecutive groups
 // (one by default).  The waves share nothing and never wait for each other.
 template <int BITS, int META>
@@ -347,6 +363,12 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantizeArgs a) {
   __shared__ uint4 s_stage[2][16 * kStageStride];   // value waves' bf16 staging
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int u = blockIdx.y;
+  const int n_gblocks = (a.n_groups + a.gpw - 1) / a.gpw;
+  if ((int)blockIdx.x >= n_gblocks) {
+    // a prefill's residual rows, beside its groups: one piece per thread
+    copy_row_piece(a.res, ((int)blockIdx.x - n_gblocks) * 256 + (int)threadIdx.x, u);
+    return;
+  }
   const int gl0 = blockIdx.x * a.gpw;
   int gl1 = min(gl0 + a.gpw, a.n_groups);
   if (a.seq_lens) {
@@ -373,16 +395,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantizeArgs a) {
 }
 
 __global__ __launch_bounds__(256) void copy_rows_kernel(CopyRowsArgs a) {
-  constexpr int CH = kHeadDim / 8;   // 16-byte chunks per row
-  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= a.n_rows * CH) return;
-  const int i = idx / CH, c = idx % CH, u = blockIdx.y;
-  const uint16_t *src = blockIdx.z == 0 ? a.src_k : a.src_v;
-  uint16_t *dst = blockIdx.z == 0 ? a.dst_k : a.dst_v;
-  const uint4 v = *reinterpret_cast<const uint4 *>(
-      src + (long long)u * a.src_unit_stride + (long long)(a.src_tok0 + i) * kHeadDim + 8 * c);
-  *reinterpret_cast<uint4 *>(dst + (long long)u * a.dst_unit_stride +
-                             (long long)(a.dst_row0 + i) * kHeadDim + 8 * c) = v;
+  copy_row_piece(a, blockIdx.x * blockDim.x + threadIdx.x, blockIdx.y);
 }
 
 __global__ __launch_bounds__(256) void ragged_residual_kernel(RaggedResidualArgs a) {
@@ -437,7 +450,9 @@ hipError_t launch_quantize(int bits, int meta, const QuantizeArgs &a_in, hipStre
     return env ? atoll(env) : 1ll;
   }();
   a.gpw = (int)(gpw < 1 ? 1 : gpw > 8 ? 8 : gpw);
-  const dim3 grid((a.n_groups + a.gpw - 1) / a.gpw, a.n_units), block(256);
+  // workgroups of the residual copy: 2 * n_rows rows of 16 pieces, 256 a block
+  const int res_blocks = a.res.n_rows > 0 ? (2 * a.res.n_rows * (kHeadDim / 8) + 255) / 256 : 0;
+  const dim3 grid((a.n_groups + a.gpw - 1) / a.gpw + res_blocks, a.n_units), block(256);
   if (bits == 2 && meta == 0)
     hipLaunchKernelGGL((quantize_kernel<2, 0>), grid, block, 0, s, a);
   else if (bits == 2)
@@ -451,8 +466,8 @@ hipError_t launch_quantize(int bits, int meta, const QuantizeArgs &a_in, hipStre
 
 hipError_t launch_copy_rows(const CopyRowsArgs &a, hipStream_t s) {
   if (a.n_rows <= 0 || a.n_units <= 0) return hipSuccess;
-  const int chunks = a.n_rows * (kHeadDim / 8);
-  const dim3 grid((chunks + 255) / 256, a.n_units, 2);
+  const int pieces = 2 * a.n_rows * (kHeadDim / 8);   // K rows, then V rows
+  const dim3 grid((pieces + 255) / 256, a.n_units);
   hipLaunchKernelGGL(copy_rows_kernel, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
