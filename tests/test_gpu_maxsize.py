@@ -1,7 +1,8 @@
 """GPU parity at the largest accepted geometry: one (sequence, kv head) whose
 quantised history fills the 2^30-byte record limit of a unit (8,388,608
-tokens at 2-bit, 5,592,384 at 4-bit, fp32 scale/zero; kivi.h, geometry
-limits), plus a full residual of R = 128 bf16 tokens.
+tokens at 2-bit and 5,592,384 at 4-bit with fp32 scale/zero; 11,184,800 and
+6,710,880 with 16-bit scale/zero; kivi.h, geometry limits), plus a full
+residual of R = 128 bf16 tokens.
 
 Every history group but the last holds the same 32 tokens A; the last group
 B (at the largest record offset) and the residual have their keys shifted
@@ -33,18 +34,19 @@ kivi = pytest.importorskip("decode_attention_channel_amd.kivi")
 pytestmark = pytest.mark.gpu
 
 G, R, D, QPK = 32, 128, 128, 4
-MAX_TOKENS = {2: 8_388_608, 4: 5_592_384}
+# (bits, scale/zero format) -> the most tokens whose records fit 2^30 bytes
+MAX_TOKENS = {(2, 0): 8_388_608, (4, 0): 5_592_384, (2, 1): 11_184_800, (4, 1): 6_710_880}
 
 
 def _f(bits):
     return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
-@pytest.mark.parametrize("bits", [2, 4])
-def test_largest_geometry(bits):
-    T = MAX_TOKENS[bits]
+@pytest.mark.parametrize("bits,meta", sorted(MAX_TOKENS))
+def test_largest_geometry(bits, meta):
+    T = MAX_TOKENS[(bits, meta)]
     n = T // G
-    print(f"max size: bits={bits} max_tokens={T} groups={n}", flush=True)
+    print(f"max size: bits={bits} meta={meta} max_tokens={T} groups={n}", flush=True)
     rng = np.random.default_rng(40 + bits)
     qf = rng.standard_normal((QPK, D)).astype(np.float32)
     qb = (qf.view(np.uint32) >> 16).astype(np.uint16)[None]
@@ -61,10 +63,10 @@ def test_largest_geometry(bits):
     kb, vb = small[0].copy(), small[1].copy()
 
     # the 192-token cache: GPU against the oracle, byte for byte
-    og = oracle.Geom(1, 1, QPK, bits=bits, max_tokens=2 * G)
+    og = oracle.Geom(1, 1, QPK, bits=bits, max_tokens=2 * G, meta=meta)
     oc = oracle.prefill(og, kb, vb)
     assert (oc.n_q, oc.n_res) == (2 * G, R)
-    gs_geom = kivi.Geom(1, 1, QPK, bits=bits, max_tokens=2 * G)
+    gs_geom = kivi.Geom(1, 1, QPK, bits=bits, max_tokens=2 * G, meta_format=meta)
     gs = kivi.Cache(gs_geom)
     kivi.quantize_prefill(gs_geom, gs, bits_to_dev(kb), bits_to_dev(vb))
     torch.cuda.synchronize()
@@ -77,7 +79,7 @@ def test_largest_geometry(bits):
     del k_small, v_small
     outs = {}
     for flags in (0, kivi.FLAG_DETERMINISTIC):
-        g = kivi.Geom(1, 1, QPK, bits=bits, max_tokens=T, flags=flags)
+        g = kivi.Geom(1, 1, QPK, bits=bits, max_tokens=T, meta_format=meta, flags=flags)
         gc = kivi.Cache(g)
         kivi.quantize_prefill(g, gc, k, v)
         torch.cuda.synchronize()
