@@ -87,3 +87,11 @@ def test_traffic_voided_by_a_code_change(tmp_path, monkeypatch):
     assert bench.read_traffic("k") == 12345.0
     src.write_text(open(kernel).read() + "\nstatic int unused_marker = 0;\n")
     assert bench.read_traffic("k") is None
+
+
+def test_cpu_flush_baseline_runs_the_oracle_flush():
+    """The flush timing of cpu_baseline at a small sample: every timed flush
+    quantises one group per (sequence, kv head) of the 32K 4-bit geometry."""
+    r = bench.cpu_flush_baseline(seed=5, threads=2, layers=2, steps=1)
+    assert r["workload"] == "llama3-8b-gqa-32k-4bit" and r["cores"] == 2
+    assert r["ms_per_step"] > 0 and r["ms_per_step_1thread"] > 0 and r["gelem_s"] > 0
