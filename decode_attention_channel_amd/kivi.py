@@ -254,6 +254,43 @@ class Cache:
     def nbytes(self) -> int:
         return sum(getattr(self, n).numel() * getattr(self, n).element_size() for n in BUFFERS)
 
+    # geometry fields that fix the buffers' meaning (flags only pick a launch)
+    _STATE_GEOM = ("batch", "kv_heads", "q_per_kv", "head_dim", "bits", "group", "residual",
+                   "meta_format")
+
+    def state_dict(self) -> dict:
+        """Snapshot for checkpointing: host copies of the live group records
+        (the first n_q / G of every unit), the whole residual ring, and the
+        counters, as tensors and ints (loadable with torch.load(...,
+        weights_only=True)).  Enqueued work on the cache must have finished:
+        the copies synchronise with the current stream."""
+        g = self.geom
+        ng = self.n_q // g.group
+        return {"geom": {k: getattr(g, k) for k in self._STATE_GEOM},
+                "n_q": self.n_q, "n_res": self.n_res, "res_start": self.res_start,
+                "records": self.records[:, :, :ng].cpu().contiguous(),
+                "k_res": self.k_res.cpu(), "v_res": self.v_res.cpu()}
+
+    def load_state_dict(self, sd: dict) -> None:
+        """Restore a state_dict() snapshot into this cache (same geometry; its
+        max_tokens may be larger): the stream continues exactly as it would
+        have from the snapshot."""
+        g = self.geom
+        want = {k: getattr(g, k) for k in self._STATE_GEOM}
+        if sd["geom"] != want:
+            raise ValueError(f"snapshot geometry {sd['geom']} does not match {want}")
+        n_q, n_res, res_start = int(sd["n_q"]), int(sd["n_res"]), int(sd["res_start"])
+        ng = n_q // g.group
+        if (n_q % g.group or not 0 <= n_q <= g.max_tokens or not 0 <= n_res <= g.slots or
+                not 0 <= res_start < g.slots or res_start % g.group or
+                tuple(sd["records"].shape) != tuple(self.records.shape[:2]) + (ng, self.records.shape[3]) or
+                sd["k_res"].shape != self.k_res.shape or sd["v_res"].shape != self.v_res.shape):
+            raise ValueError("snapshot counters or buffer shapes do not fit this cache")
+        self.records[:, :, :ng].copy_(sd["records"])
+        self.k_res.copy_(sd["k_res"])
+        self.v_res.copy_(sd["v_res"])
+        self.set_counters(n_q, n_res, res_start)
+
     def history(self) -> dict:
         """Host copy of the quantised history in the per-array layout
         (k_codes [B][H][T][D*b/8], k_scale ..., as numpy arrays) from the
