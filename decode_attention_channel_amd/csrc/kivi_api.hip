@@ -9,6 +9,7 @@
 // decode_attn.hip (decode attention over the mixed cache).
 #include <math.h>
 #include <stdlib.h>
+#include <string.h>
 
 #include <mutex>
 
@@ -282,7 +283,12 @@ kivi_status decode_step_impl(const kivi_geom *g, kivi_cache *c, const uint16_t *
 extern "C" {
 
 const char *kivi_status_string(kivi_status s) {
-  switch (s) {
+  // A C caller may pass any int; C++ gives an enum object only the values of
+  // its enumerators' bit range, so the argument is read as the int it is.
+  static_assert(sizeof(kivi_status) == sizeof(int), "kivi_status is int-sized");
+  int v;
+  memcpy(&v, &s, sizeof v);
+  switch (v) {
     case KIVI_OK: return "ok";
     case KIVI_E_NULL: return "a required pointer is NULL";
     case KIVI_E_GEOMETRY: return "invalid geometry";
