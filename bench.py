@@ -11,7 +11,7 @@ Workload (Llama-3-8B GQA geometry of the catalog record kivi-2bit-llama3-8b-gqa-
 * decode leg (the timed "step"): for each of the 32 layers, one
   kivi_decode_step call -- append one token per sequence, flush a group when
   the residual is full, and decode attention over the whole mixed cache, in
-  one launch (two on flush steps).  value = generated tokens/s (batch / step
+  one launch (a due flush is quantised inside it).  value = tokens/s (batch / step
   time).  The same number of steps is then timed with the three separate
   calls (append, flush, attend) for comparison.  The 32 layer caches (4.5 GB)
   rotate, so the 256 MB MALL cannot serve them;
@@ -24,7 +24,7 @@ Workload (Llama-3-8B GQA geometry of the catalog record kivi-2bit-llama3-8b-gqa-
   shuffled pool) through kivi_paged_decode_step at the lockstep length, then
   the caches themselves through kivi_ragged_decode_step at the lockstep
   length and with lengths drawn uniformly from [S/2, S]; eager launches and
-  HIP graph replays of all layers (two launches per layer) are timed;
+  HIP graph replays of all layers (one launch per layer) are timed;
 * flush-amortised rate: a further window of 32 fused steps, in which every
   layer flushes exactly once (value's window of `steps` steps holds
   floor or ceil of steps/32 flushes);
@@ -466,7 +466,7 @@ def ragged_leg(w, geom, caches, ws, qs, outs, tok, steps, seed, meta_bytes):
     length and with lengths drawn uniformly from [S/2, S] per sequence (the
     cache bytes beyond a sequence's length are not read).  Each case is timed
     as eager launches and as HIP graph replays (one graph per state parity,
-    all layers, two launches per layer).  `steps` is even."""
+    all layers, one launch per layer).  `steps` is even."""
     import numpy as np
     import torch
 
@@ -826,7 +826,7 @@ def main():
                    "scale_zero": "fp16 scale + bf16 zero" if args.meta == "fp16" else "fp32",
                    "launch": "deterministic" if args.deterministic else "default",
                    "step": "per layer: kivi_decode_step (append + flush-if-full + decode "
-                           "attention; one launch, two on flush steps)"},
+                           "attention, the flush quantised inside the launch; one launch)"},
         "ms_per_step_separate_calls": t_steps_sep / n_timed * 1e3,
         "tokens_s_flush_amortised": w.batch * amort_steps / t_amort,
         "ms_per_step_flush_amortised": t_amort / amort_steps * 1e3,

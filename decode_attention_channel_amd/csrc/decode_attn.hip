@@ -48,6 +48,7 @@
 #include <type_traits>
 
 #include "kivi_internal.h"
+#include "quantize_group.h"
 
 namespace kivi {
 namespace {
@@ -261,11 +262,14 @@ __device__ __forceinline__ int4 apply_unit_state(DecodeArgs &a, int u) {
     flags = kSeqBadLength;
   }
   bool append = flags == 0;
+  a.flush_g = -1;
   if (append && n_res + 1 >= a.slots) {
-    // the flush launch quantised the G oldest ring tokens into group n_q / G
-    // iff there is room for it (and, paged, a page)
+    // the G oldest ring tokens go into group n_q / G, quantised in this
+    // launch, iff there is room for it (and, paged, a page)
     if (n_res + 1 == a.slots && n_q + G <= a.max_tokens &&
         (!a.pages.table || group_slot(a.pages, a.kv_heads, 0, u, n_q / G) >= 0)) {
+      a.flush_g = n_q / G;
+      a.flush_src = res_start;
       n_q += G;
       n_res -= G;
       res_start = (res_start + G) % a.slots;
@@ -910,6 +914,44 @@ __device__ __forceinline__ void mfma_rchunk(const DecodeArgs &a, int u, int rc,
   __builtin_amdgcn_wave_barrier();
 }
 
+// A flush folded into a decode launch (DecodeArgs::flush_g): waves 0-3 of
+// the workgroup that holds the group quantise it from the ring, one quarter
+// each (the quantise kernels' per-wave functions: channel halves of the keys,
+// token halves of the values), using their own staging areas in LDS, which
+// hold nothing yet.  Each then waits for its record stores to complete and
+// counts itself in `done`; a wave that loads the group first waits until all
+// four have counted (they wait on nothing, so the wait ends).  The ring
+// tokens read here are neither the ones this launch attends to nor the slot
+// the fused append writes (R >= G), and no other workgroup reads the group.
+template <int BITS, int META>
+__device__ __forceinline__ void fold_flush(const DecodeArgs &a, int u, int wave, int lane,
+                                           uint8_t *stage_area, int *done) {
+  QuantizeArgs q{};
+  q.src_k = a.k_res;
+  q.src_v = a.v_res;
+  q.src_unit_stride = (long long)a.slots * D;
+  q.src_tok0 = a.flush_src;
+  q.dst_g0 = a.flush_g;
+  q.n_groups_cap = a.n_groups_cap;
+  q.records = const_cast<uint8_t *>(a.records);
+  q.kv_heads = a.kv_heads;
+  q.pages = a.pages;
+  if (wave < 2)
+    qgroup::quantize_keys<BITS, META>(q, u, 0, 1, wave, lane, stage_area);
+  else
+    qgroup::quantize_values<BITS, META>(q, u, 0, 1, wave - 2, lane, stage_area,
+                                        reinterpret_cast<uint4 *>(stage_area + 16 * D));
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  if (lane == 0) __hip_atomic_fetch_add(done, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+// Before loading group g: if it is the folded flush's group, wait for it.
+__device__ __forceinline__ void wait_fold(bool owner, int g, int flush_g, const int *done) {
+  if (owner && g == flush_g)
+    while (__hip_atomic_load(const_cast<int *>(done), __ATOMIC_ACQUIRE,
+                             __HIP_MEMORY_SCOPE_WORKGROUP) < 4)
+      __builtin_amdgcn_s_sleep(2);
+}
+
 // Byte range [lo, hi) of the unit's work for wave `wave` of workgroup
 // (u, split): quantised groups cost `cq` units each, then residual chunks of
 // G tokens `cr` each; the workgroup's share is weighted by its co-residency
@@ -1001,6 +1043,20 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeArgs a) {
   // its residual chunks round-robin, wave w the chunks w, w + NW, ...)
   const WorkRange wr = kDyn ? wave_work(a, u, split, 0, 1, BITS + kMetaBytes<META> / 2, 16)
                             : wave_work(a, u, split, wave, NW, BITS + kMetaBytes<META> / 2, 16);
+  // A flush folded into this launch, if this workgroup's share holds its
+  // group (workgroup-uniform)
+  __shared__ int s_fold;   // quarters of the folded flush done
+  bool fold = false;
+  if (a.flush_g >= 0) {
+    const WorkRange wg = kDyn ? wr : wave_work(a, u, split, 0, 1, BITS + kMetaBytes<META> / 2, 16);
+    fold = a.flush_g >= wg.g_begin && a.flush_g < wg.g_end;
+  }
+  if (fold) {
+    if (threadIdx.x == 0) s_fold = 0;
+    __syncthreads();
+    if (wave < 4)
+      fold_flush<BITS, META>(a, u, wave, lane, reinterpret_cast<uint8_t *>(&sm.mf.w[wave]), &s_fold);
+  }
   const int g_end = wr.g_end;
   const int g_begin = kDyn ? wr.g_begin + wave * (FIXED ? 1 : C) : wr.g_begin;
   const int r_begin = kDyn ? wr.r_begin + wave : wr.r_begin;
@@ -1031,6 +1087,7 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeArgs a) {
 #pragma unroll
   for (int i = 0; i < kPrefetch; ++i) {
     const int g = g_begin + i * kClaimStride;
+    wait_fold(fold, g, a.flush_g, &s_fold);
     load_group<BITS, META, PAGED>(r[i], view, a, u, g, g < g_end);
     // keep the groups' loads in group order, as in the loop, so that the
     // wait counts at the loop head are the steady-state ones
@@ -1076,6 +1133,7 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeArgs a) {
       for (int k = 0; k <= kPrefetch; ++k) {
         const int slot = (k + kPrefetch) % (kPrefetch + 1);
         gk[slot] = to_load;
+        wait_fold(fold, to_load, a.flush_g, &s_fold);
         load_group<BITS, META, PAGED>(r[slot], view, a, u, to_load, to_load < g_end);
         if constexpr (FIXED) {
           to_load = claim;
@@ -1119,6 +1177,7 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeArgs a) {
 #pragma unroll
     for (int k = 0; k <= kPrefetch; ++k) {
       const int g = g0 + k;
+      wait_fold(fold, g + kPrefetch, a.flush_g, &s_fold);
       load_group<BITS, META, PAGED>(r[(k + kPrefetch) % (kPrefetch + 1)], view, a, u,
                                     g + kPrefetch, g + kPrefetch < g_end);
       if (g < g_end) {

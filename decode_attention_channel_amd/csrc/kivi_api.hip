@@ -153,9 +153,12 @@ kivi_status enqueue_attend(const kivi_geom *g, const kivi_cache *c, const uint16
                            float softmax_scale, void *ws, size_t ws_bytes, hipStream_t s,
                            int slots = 0,
                            const int32_t *state_in = nullptr, int32_t *state_out = nullptr,
-                           const kivi::PageMap &pages = kivi::PageMap{}) {
+                           const kivi::PageMap &pages = kivi::PageMap{}, int flush_g = -1,
+                           int flush_src = 0) {
   kivi::DecodeArgs a{};
   a.pages = pages;
+  a.flush_g = flush_g;
+  a.flush_src = flush_src;
   a.records = c->records;
   a.k_res = c->k_res; a.v_res = c->v_res;
   a.k_new = k_new; a.v_new = v_new;
@@ -260,21 +263,28 @@ kivi_status decode_step_impl(const kivi_geom *g, kivi_cache *c, const uint16_t *
     if (flushed) *flushed = 1;
     return enqueue_attend(g, c, nullptr, nullptr, q, out, softmax_scale, ws, ws_bytes, s);
   }
-  if (flush) {
-    // With R >= G the G oldest tokens of the full ring exclude the new one
-    // (the newest of R+G), so quantising them before the append leaves the
-    // same state as append-then-flush, and the append can fuse into the
-    // attention launch.
-    if ((st = enqueue_flush(g, c, s)) != KIVI_OK) return st;
-    if (flushed) *flushed = 1;
-  }
-  // attention with the append fused: the new token is logical index n_res
+  // With R >= G the G oldest tokens of the full ring exclude the new one (the
+  // newest of R+G), so quantising them before the append leaves the same
+  // state as append-then-flush: the flush and the append both fold into the
+  // attention launch, which quantises the group before any of its waves
+  // reads it.
   kivi_cache next = *c;
+  int flush_g = -1;
+  if (flush) {
+    flush_g = c->n_q / G;
+    next.n_q += G;
+    next.n_res -= G;
+    next.res_start = (c->res_start + G) % slots;
+  }
+  // the new token is logical index n_res of the ring after the flush
   next.n_res += 1;
-  if ((st = enqueue_attend(g, &next, k_new, v_new, q, out, softmax_scale, ws, ws_bytes, s)) !=
-      KIVI_OK)
+  if ((st = enqueue_attend(g, &next, k_new, v_new, q, out, softmax_scale, ws, ws_bytes, s, 0,
+                           nullptr, nullptr, kivi::PageMap{}, flush_g, c->res_start)) != KIVI_OK)
     return st;
+  c->n_q = next.n_q;
   c->n_res = next.n_res;
+  c->res_start = next.res_start;
+  if (flushed && flush) *flushed = 1;
   return KIVI_OK;
 }
 
@@ -498,20 +508,10 @@ kivi_status ragged_step_impl(const kivi_geom *g, const kivi_cache *c, const kivi
   // kivi_decode_step)
   if (g->residual < g->group) return KIVI_E_UNSUPPORTED;
   const int G = g->group, slots = g->residual + G;
-  // 1. flush: each sequence whose ring fills with this step's append
-  kivi::QuantizeArgs f{};
-  f.src_k = c->k_res; f.src_v = c->v_res;
-  f.src_unit_stride = (long long)slots * g->head_dim;
-  f.n_groups = 1; f.n_units = (int)units_of(g);
-  f.max_tokens = g->max_tokens; f.n_groups_cap = g->max_tokens / G;
-  f.records = c->records;
-  f.state = state_in;
-  f.kv_heads = g->kv_heads; f.residual = g->residual; f.slots = slots;
-  f.pages = pm;
-  if ((st = hip_status(kivi::launch_quantize(g->bits, g->meta_format, f, s))) != KIVI_OK)
-    return st;
-  // 2. attention with the fused append; every sequence's counters come from
-  // state_in, the launch shape from the capacity
+  // One launch: every sequence's counters come from state_in, the launch
+  // shape from the capacity; a sequence whose ring fills with this step's
+  // append has its G oldest ring tokens quantised into its next group inside
+  // the launch (the flush), then takes the fused append.
   kivi_cache bound = *c;
   bound.n_q = g->max_tokens / G * G;
   bound.n_res = slots;

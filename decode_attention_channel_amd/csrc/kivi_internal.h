@@ -188,6 +188,12 @@ struct DecodeArgs {
   // paged history (table == nullptr: contiguous per unit); with pages, a
   // flush also needs a page for the new group
   PageMap pages;
+  // A flush folded into this launch (flush_g -1: none): group flush_g of the
+  // unit is quantised from the G ring tokens that start at slot flush_src,
+  // by four waves of the workgroup whose share holds that group, before any
+  // of its waves loads it.  Mixed-length batches set it per sequence
+  // (from state_in); the counters above already include the flush.
+  int flush_g, flush_src;
   // byte shares: workgroup (unit u, split s) has linear index s*n_units+u
   // and co-residency rank min(index / cus, 3) on its compute unit; its share
   // of the unit's bytes is proportional to rank_w[rank]

@@ -304,16 +304,18 @@ kivi_status kivi_decode_attention(const kivi_geom *geom, const kivi_cache *cache
                                   float softmax_scale, void *ws, size_t ws_bytes,
                                   void *stream);
 
-/* One decode step of one layer in (usually) a single launch: append
+/* One decode step of one layer in a single launch (R >= G): append
  * k_new/v_new, flush iff the ring is then full, and attend with q -- the
  * same cache bytes, counters and `out` as kivi_append_token,
  * kivi_flush_residual and kivi_decode_attention called in that order (the
  * step order of the cache state machine above).
  * How: when the append would fill the ring (n_res == R+G-1) the G oldest
  * tokens are quantised first; with R >= G they cannot include the new
- * token, so the state is the same.  The attention kernel then reads the new
- * token from k_new/v_new and stores it into its ring slot itself.  With
- * R == 0 a flush step runs as three launches.
+ * token, so the state is the same.  The attention launch does both: the
+ * workgroup whose share holds the new group quantises it from the ring
+ * before any of its waves reads it, and the new token is read from
+ * k_new/v_new and stored into its ring slot by the kernel.  With R == 0 a
+ * flush step runs as three launches.
  * k_new, v_new: device bf16 [B][H][D]; q, out, softmax_scale, ws, ws_bytes
  * as for kivi_decode_attention, the workspace sized for the counters after
  * the step (kivi_decode_workspace_bytes(geom, n_q, n_res + 1) serves every
@@ -408,9 +410,10 @@ kivi_status kivi_ragged_prefill(const kivi_geom *geom, const kivi_cache *cache,
 /* One decode step of a mixed-length batch: for every sequence, append
  * k_new/v_new, flush iff its ring is then full, and attend with q -- per
  * sequence the same cache bytes and output as kivi_decode_step on a batch
- * of that sequence alone.  Two launches with fixed arguments: a flush launch
- * in which only the sequences due to flush work, then decode attention with
- * the append fused.  The state is read from state_in and the state after
+ * of that sequence alone.  One launch with fixed arguments: decode
+ * attention in which each sequence due to flush first quantises its G
+ * oldest ring tokens into its next group, and the append is fused.  The
+ * state is read from state_in and the state after
  * the step written to state_out (distinct device int32 [B][4] buffers; the
  * next step reads state_out).  Requires residual >= group.
  * k_new, v_new: device bf16 [B][H][D]; q, out, softmax_scale, ws, ws_bytes
@@ -475,7 +478,7 @@ kivi_status kivi_paged_prefill(const kivi_geom *geom, const kivi_paged_cache *ca
                                const int32_t *seq_lens, int32_t *state, void *stream);
 
 /* kivi_ragged_decode_step over a paged cache (flushes write the new group
- * into its page).  The same two launches with fixed arguments.
+ * into its page).  The same single launch with fixed arguments.
  * Errors: those of kivi_ragged_decode_step and kivi_paged_layout. */
 kivi_status kivi_paged_decode_step(const kivi_geom *geom, const kivi_paged_cache *cache,
                                    const int32_t *state_in, int32_t *state_out,
