@@ -76,32 +76,38 @@ def prefill_bytes(w, S, n_q, meta_bytes=4):
                                    4 * r * D)
 
 
-def code_hash(path: str) -> str:
-    """sha256 prefix of a source file's code: '//' comments, trailing blanks
-    and empty lines removed, so that editing a comment keeps the hash."""
+def code_hash(*paths: str) -> str:
+    """sha256 prefix of source files' code, in order: '//' comments, trailing
+    blanks and empty lines removed, so that editing a comment keeps the hash."""
     import hashlib
     import re
     lines = []
-    for line in open(path).read().splitlines():
-        line = re.sub(r"//.*$", "", line).rstrip()
-        if line:
-            lines.append(line)
+    for path in paths:
+        for line in open(path).read().splitlines():
+            line = re.sub(r"//.*$", "", line).rstrip()
+            if line:
+                lines.append(line)
     return hashlib.sha256("\n".join(lines).encode()).hexdigest()[:16]
+
+
+# the sources of the decode kernel's device code (it folds the per-wave group
+# quantiser in for flushes)
+DECODE_SOURCES = ("decode_attn.hip", "quantize_group.h")
 
 
 def read_traffic(kernel_tag: str):
     """HBM traffic per launch measured with rocprofv3 counters (committed
     summary), valid only while the kernel's code is unchanged."""
     path = os.path.join(ROOT, "profiles", f"{kernel_tag}_traffic.txt")
-    src = os.path.join(ROOT, "decode_attention_channel_amd", "csrc", "decode_attn.hip")
-    if not os.path.exists(path):
+    srcs = [os.path.join(ROOT, "decode_attention_channel_amd", "csrc", f) for f in DECODE_SOURCES]
+    if not os.path.exists(path) or not all(os.path.exists(f) for f in srcs):
         return None
     vals = {}
     for line in open(path):
         if ":" in line and not line.startswith("#"):
             key, val = line.split(":", 1)
             vals[key.strip()] = val.strip()
-    if vals.get("kernel_code_sha256_16") != code_hash(src):
+    if vals.get("kernel_code_sha256_16") != code_hash(*srcs):
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])

@@ -71,22 +71,28 @@ def test_code_hash_ignores_comments_only(tmp_path):
 
 def test_traffic_voided_by_a_code_change(tmp_path, monkeypatch):
     """read_traffic returns the committed figure only while the file's hash
-    equals the current kernel's code hash."""
-    kernel = os.path.join(bench.ROOT, "decode_attention_channel_amd", "csrc", "decode_attn.hip")
+    equals the current code hash of the decode kernel's sources (a change to
+    either voids it)."""
+    csrc = os.path.join(bench.ROOT, "decode_attention_channel_amd", "csrc")
     root = tmp_path / "repo"
     (root / "profiles").mkdir(parents=True)
     (root / "decode_attention_channel_amd" / "csrc").mkdir(parents=True)
-    src = root / "decode_attention_channel_amd" / "csrc" / "decode_attn.hip"
-    src.write_text(open(kernel).read())
-    h = bench.code_hash(str(src))
+    srcs = [root / "decode_attention_channel_amd" / "csrc" / f for f in bench.DECODE_SOURCES]
+    orig = [open(os.path.join(csrc, f)).read() for f in bench.DECODE_SOURCES]
+    for p, text in zip(srcs, orig):
+        p.write_text(text)
+    h = bench.code_hash(*[str(p) for p in srcs])
     prof = root / "profiles" / "k_traffic.txt"
     prof.write_text(f"# comment: 1\nkernel_code_sha256_16: {h}\nhbm_bytes_per_launch: 12345\n")
     monkeypatch.setattr(bench, "ROOT", str(root))
     assert bench.read_traffic("k") == 12345.0
-    src.write_text(open(kernel).read() + "\n// a comment at the end\n")
+    for p, text in zip(srcs, orig):
+        p.write_text(text + "\n// a comment at the end\n")
+        assert bench.read_traffic("k") == 12345.0
+        p.write_text(text + "\nstatic int unused_marker = 0;\n")
+        assert bench.read_traffic("k") is None
+        p.write_text(text)
     assert bench.read_traffic("k") == 12345.0
-    src.write_text(open(kernel).read() + "\nstatic int unused_marker = 0;\n")
-    assert bench.read_traffic("k") is None
 
 
 def test_cpu_flush_baseline_runs_the_oracle_flush():
