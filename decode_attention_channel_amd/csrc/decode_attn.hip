@@ -16,7 +16,9 @@
 // or round-robin (bitwise-repeatable results).  The waves' states
 // are merged in LDS at the end; each workgroup writes (m, l, o[128]) per
 // query head, and the last workgroup of a unit to finish merges that unit's
-// partials into `out` (arrival counter in the workspace).
+// partials into `out` (arrival counter in the workspace).  A decode step
+// whose ring is full also quantises the G oldest ring tokens into the new
+// group inside the same launch (fold_flush), before any wave reads it.
 //
 // Dequantisation is folded into the products, which is algebraically the
 // same as dequantise-then-dot:
