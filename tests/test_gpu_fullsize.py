@@ -143,8 +143,8 @@ def test_streaming_decode_full_size(name, steps, check_every):
 
 @pytest.mark.parametrize("name,steps", [("llama3-8b-gqa-8k", 40), ("llama3-8b-gqa-32k-4bit", 64)])
 def test_fused_decode_step_full_size(name, steps):
-    """The timed call (kivi_decode_step through LayerStepper.step: append fused
-    into the attention launch, flush launched first when the ring fills) at
+    """The timed call (kivi_decode_step through LayerStepper.step: append and,
+    when the ring fills, the flush folded into the attention launch) at
     the full workload size, across flushes: sampled units against the
     oracle at every flush step and at the end (cache bytes exact, attention
     within the bound), and every output against the same steps made of the

@@ -3,8 +3,8 @@ device array) against kivi_decode_step with a caller workspace, through the
 C ABI: two calls in a row, the second on a smaller input, each compared with
 kivi_decode_step on identical inputs (cache bytes exact; outputs bitwise
 equal for deterministic launches, within REPEAT_TOL otherwise) and with the oracle
-(1e-3).  The first call flushes a group, so its launches are the flush and
-the attention with the fused append."""
+(1e-3).  The first call flushes a group, which the attention launch
+quantises itself before attending with the fused append."""
 import math
 
 import numpy as np
